@@ -1,0 +1,470 @@
+"""Pins of the CPU oracle against what the method and the mathematics fix.
+
+Nothing here retypes the oracle's formulas: each test checks a property
+that holds for the method as described on the 1-bit LAMB page (arXiv
+2104.06069) -- a norm identity, an error-feedback identity, a reduction to a
+textbook optimizer, a closed form, an invariance, or a brute force on tiny
+inputs -- chosen so that a dropped term, a wrong sign or a transposed
+operand in the oracle fails at least one of them.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+
+U = 2.0 ** -24
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rng(seed):
+    return np.random.default_rng(seed)
+
+
+def f32(a):
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def hp(**kw):
+    base = dict(beta1=0.9, beta2=0.999, eta=1e-8, lr=1e-3, weight_decay=0.0, c_min=0.01,
+                c_max=10.0, f_min=0.5, f_max=4.0, kappa=0.1)
+    base.update(kw)
+    return oracle.hparams(**base)
+
+
+def chunk_lengths(n, C):
+    return [min(C, n - k * C) for k in range(oracle.num_chunks(n, C))]
+
+
+# ---------------------------------------------------------------------------
+# P1  norm preservation of the 1-bit operator (scale = ||z|| / sqrt(n))
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("n,C", [(4096, 4096), (3 * 4096 + 2816, 4096), (1, 4096), (33, 1024),
+                                 (5000, 1024), (4095, 2048)])
+def test_p1_norm_preserved(n, C):
+    z = f32(rng(1).standard_normal(n) * 0.37)
+    err = np.zeros(n, np.float32)
+    bits, scales = oracle.compress_ef(z, err, C)
+    for k, nk in enumerate(chunk_lengths(n, C)):
+        zk = z[k * C:k * C + nk].astype(np.float64)
+        norm_z = math.sqrt(math.fsum(zk * zk))
+        norm_cz = math.sqrt(nk * float(scales[k]) ** 2)  # ||C[z]|| = s * sqrt(n_k)
+        assert abs(norm_cz - norm_z) <= (math.log2(C) + 3) * U * norm_z
+
+
+def test_p1_zero_padding_not_counted():
+    # The partial last chunk is normalised by its valid length only.
+    C = 4096
+    z = f32(np.full(100, 3.0))
+    _, scales = oracle.compress_ef(z, np.zeros(100, np.float32), C)
+    assert scales[0] == np.float32(3.0)
+
+
+# ---------------------------------------------------------------------------
+# P2  error feedback: z = C[z] + e, and the error is carried forward
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("n,C", [(4096 * 2 + 77, 4096), (3000, 1024)])
+def test_p2_ef_identity_one_step(n, C):
+    z = f32(rng(2).standard_normal(n))
+    err = np.zeros(n, np.float32)          # z = in + 0 exactly
+    bits, scales = oracle.compress_ef(z, err, C)
+    cz = oracle.decompress(bits, scales, n, C).astype(np.float64)
+    e = err.astype(np.float64)
+    resid = np.abs((cz + e) - z.astype(np.float64))
+    half_ulp = np.spacing(np.abs(err)).astype(np.float64) / 2
+    assert np.all(resid <= half_ulp)
+    # Sterbenz range: z - s is exact, so the identity holds exactly
+    s_elem = np.repeat(scales.astype(np.float64), C)[:n]
+    exact = (np.abs(z) >= s_elem / 2) & (np.abs(z) <= 2 * s_elem)
+    assert exact.sum() > n // 4
+    assert np.all(resid[exact] == 0.0)
+
+
+def test_p2_error_carried_forward():
+    # Sum_t C[z_t] + e_T = Sum_t in_t: what is sent tracks what was fed in.
+    n, C, T = 4096 + 1000, 4096, 20
+    err = np.zeros(n, np.float32)
+    sent = np.zeros(n, np.float64)
+    fed = np.zeros(n, np.float64)
+    r = rng(3)
+    for _ in range(T):
+        x = f32(r.standard_normal(n) * r.uniform(0.1, 10))
+        fed += x
+        bits, scales = oracle.compress_ef(x, err, C)
+        sent += oracle.decompress(bits, scales, n, C)
+    gap = np.abs(sent + err - fed)
+    assert np.max(gap) <= 64 * T * U * np.max(np.abs(fed) + np.abs(sent))
+    # and the error stays bounded by the scale (it does not accumulate)
+    assert np.max(np.abs(err)) < 50 * np.max(np.abs(fed)) / math.sqrt(T)
+
+
+# ---------------------------------------------------------------------------
+# P3  identity compressor => textbook momentum SGD
+# ---------------------------------------------------------------------------
+def test_p3_identity_compressor_is_momentum_sgd():
+    numels = [5000, 300]
+    N, W, T = sum(numels), 3, 5
+    h = hp(eta=1.0, lr=1.0, kappa=0.0)
+    r = rng(4)
+    x = np.zeros(N, np.float32)
+    m = f32(r.standard_normal(N) * 1e-2)
+    v0 = np.zeros(N, np.float32)
+    vf = np.zeros(N, np.float32)
+    err_w = [np.zeros(N, np.float32) for _ in range(W)]
+    err_s = np.zeros(N, np.float32)
+    c_avg = np.ones(2, np.float32)
+    f_prev = np.ones(2, np.float32)
+    xd, md = x.astype(np.float64), m.astype(np.float64)
+    for _ in range(T):
+        g = [f32(r.standard_normal(N) * 1e-2) for _ in range(W)]
+        out = oracle.compressed_step(numels, 4096, g, err_w, err_s, x, m, v0, vf, c_avg, f_prev, h,
+                                     compressor=oracle.IDENTITY)
+        gbar = np.mean([gi.astype(np.float64) for gi in g], axis=0)
+        md = 0.9 * md + 0.1 * gbar
+        xd = xd - md
+        assert np.all(out["c"] == 1.0)
+    assert np.max(np.abs(m - md)) <= 1e-5 * np.max(np.abs(md))
+    assert np.max(np.abs(x - xd)) <= 1e-5 * np.max(np.abs(xd))
+    assert all(np.all(e == 0) for e in err_w) and np.all(err_s == 0)
+
+
+# ---------------------------------------------------------------------------
+# P4  the average step is the arithmetic mean
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("W", [1, 2, 3, 5, 8, 16])
+def test_p4_average_is_mean(W):
+    n, C = 4096 + 123, 4096
+    K = oracle.num_chunks(n, C)
+    r = rng(5 + W)
+    bits_w = [r.integers(0, 2 ** 32, size=K * C // 32, dtype=np.uint64).astype(np.uint32)
+              for _ in range(W)]
+    scales_w = [f32(r.uniform(0.5, 2.0, size=K)) for _ in range(W)]
+    a = oracle.average(bits_w, scales_w, n, C).astype(np.float64)
+    vals = []
+    for b, s in zip(bits_w, scales_w):
+        sign = np.unpackbits(b.view(np.uint8), bitorder="little").reshape(K, C)
+        vals.append(np.where(sign, 1.0, -1.0) * s.astype(np.float64)[:, None])
+    mean = (np.sum(vals, axis=0) / W).reshape(-1)[:n]
+    bound = W * U * np.max(np.abs(np.array(vals))) + np.spacing(np.abs(a).astype(np.float32))
+    assert np.all(np.abs(a - mean) <= bound)
+
+
+@pytest.mark.parametrize("W", [2, 4, 8, 16])
+def test_p4_identical_workers_exact(W):
+    n, C = 2 * 4096, 4096
+    z = f32(rng(6).standard_normal(n))
+    bits, scales = oracle.compress_ef(z, np.zeros(n, np.float32), C)
+    err_s = np.zeros(n, np.float32)
+    a = oracle.average([bits] * W, [scales] * W, n, C)
+    assert np.array_equal(a, oracle.decompress(bits, scales, n, C))
+    b2, s2 = oracle.average_packed([bits] * W, [scales] * W, err_s, C)
+    assert np.array_equal(b2, bits) and np.array_equal(s2, scales) and np.all(err_s == 0)
+
+
+# ---------------------------------------------------------------------------
+# P5  trust ratio: the per-tensor step length is gamma * ||x_{t-1}||
+# ---------------------------------------------------------------------------
+def test_p5_trust_ratio_step_length_tiny_tensors():
+    numels = [1, 2, 3, 5, 8, 7]
+    N = sum(numels)
+    r = rng(7)
+    h = hp(lr=0.25, c_min=0.0, c_max=1e30)
+    x0 = f32(r.standard_normal(N))
+    x, m, v = x0.copy(), f32(r.standard_normal(N) * 0.1), f32(r.uniform(0.01, 1, N))
+    c_sum = np.zeros(len(numels), np.float32)
+    g = [f32(r.standard_normal(N)) for _ in range(3)]
+    c = oracle.warmup_step(numels, g, x, m, v, c_sum, h)
+    off = 0
+    for l, nl in enumerate(numels):
+        sl = slice(off, off + nl)
+        xo = x0[sl].astype(np.float64)
+        dx = xo - x[sl].astype(np.float64)
+        assert abs(np.linalg.norm(dx) / np.linalg.norm(xo) - 0.25) <= 4e-7
+        # direction: Adam's m / (sqrt(v) + eta), from the returned moments
+        u = m[sl].astype(np.float64) / (np.sqrt(v[sl].astype(np.float64)) + 1e-8)
+        cos = dx @ u / (np.linalg.norm(dx) * np.linalg.norm(u))
+        assert cos >= 1 - 1e-9
+        # and c is ||x|| / ||u||
+        assert abs(c[l] - np.linalg.norm(xo) / np.linalg.norm(u)) <= 8 * U * c[l]
+        off += nl
+    assert np.array_equal(c_sum, c)
+
+
+def test_p5_clip_applies_to_whole_ratio():
+    numels = [64, 64]
+    N = 128
+    r = rng(8)
+    h = hp(lr=0.5, c_min=0.0, c_max=1e-3)
+    x0 = f32(r.standard_normal(N))
+    x, m, v = x0.copy(), np.zeros(N, np.float32), np.zeros(N, np.float32)
+    g = [f32(r.standard_normal(N))]
+    c = oracle.warmup_step(numels, g, x, m, v, np.zeros(2, np.float32), h)
+    assert np.all(c == np.float32(1e-3))
+    u = m.astype(np.float64) / (np.sqrt(v.astype(np.float64)) + 1e-8)
+    for l in range(2):
+        sl = slice(64 * l, 64 * l + 64)
+        dx = np.linalg.norm(x0[sl].astype(np.float64) - x[sl])
+        assert abs(dx / (0.5 * 1e-3 * np.linalg.norm(u[sl])) - 1) < 1e-4
+
+
+def test_p5_zero_norms_give_ratio_one():
+    numels = [16, 16]
+    h = hp(c_min=0.0, c_max=100.0)
+    x = np.concatenate([np.zeros(16), np.ones(16)]).astype(np.float32)
+    g = [np.concatenate([np.ones(16), np.zeros(16)]).astype(np.float32)]
+    m, v = np.zeros(32, np.float32), np.zeros(32, np.float32)
+    c = oracle.warmup_step(numels, g, x, m, v, np.zeros(2, np.float32), h)
+    assert np.all(c == 1.0)           # x = 0 in tensor 0, update = 0 in tensor 1
+    assert np.all(x[16:] == 1.0)      # no gradient, no move
+
+
+# ---------------------------------------------------------------------------
+# P6  warmup step 1 from m = v = 0: closed form
+# ---------------------------------------------------------------------------
+def test_p6_first_warmup_step_closed_form():
+    numels = [4096, 1000]
+    N, W = sum(numels), 4
+    r = rng(9)
+    h = hp(eta=0.0, c_min=0.0, c_max=1e30)
+    x0 = f32(r.standard_normal(N) * 0.02)
+    x, m, v = x0.copy(), np.zeros(N, np.float32), np.zeros(N, np.float32)
+    g = [f32(r.standard_normal(N) * 1e-3) for _ in range(W)]
+    c = oracle.warmup_step(numels, g, x, m, v, np.zeros(2, np.float32), h)
+    # the hyper-parameters are the fp32 values of 0.9 and 0.999
+    a1 = 1 - float(np.float32(0.9))
+    a2 = 1 - float(np.float32(0.999))
+    G = np.array([gi.astype(np.float64) for gi in g])
+    gbar = G.mean(axis=0)
+    gabs = np.abs(G).mean(axis=0)
+    assert np.all(np.abs(m - a1 * gbar) <= a1 * 4 * U * gabs + 3 * U * np.abs(a1 * gbar))
+    assert np.all(np.abs(v - a2 * gbar ** 2) <= a2 * 10 * U * gabs ** 2 + 4 * U * a2 * gbar ** 2)
+    off = 0
+    for l, nl in enumerate(numels):
+        xn = np.linalg.norm(x0[off:off + nl].astype(np.float64))
+        expect = xn * math.sqrt(a2) / (a1 * math.sqrt(nl))
+        assert abs(c[l] / expect - 1) <= 1e-5
+        off += nl
+
+
+# ---------------------------------------------------------------------------
+# P7  idempotence C[C[z]] = C[z] with zero error, full chunks of 4^k
+# ---------------------------------------------------------------------------
+def test_p7_sqrt_of_rounded_square_is_identity():
+    r = rng(10)
+    s = f32(np.ldexp(r.uniform(1, 2, 10_000_000), r.integers(-60, 60, 10_000_000)))
+    assert np.array_equal(np.sqrt(s * s), s)
+
+
+@pytest.mark.parametrize("C", [1024, 4096, 16384])
+def test_p7_idempotent(C):
+    n = 3 * C
+    z = f32(rng(11).standard_normal(n))
+    bits, scales = oracle.compress_ef(z, np.zeros(n, np.float32), C)
+    cz = oracle.decompress(bits, scales, n, C)
+    err2 = np.zeros(n, np.float32)
+    bits2, scales2 = oracle.compress_ef(cz, err2, C)
+    assert np.array_equal(bits2, bits) and np.array_equal(scales2, scales)
+    assert np.all(err2 == 0)
+
+
+# ---------------------------------------------------------------------------
+# P8  sign packing: brute force on tiny vectors
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("n,C", [(1, 64), (31, 64), (64, 64), (100, 64), (130, 128), (4097, 4096)])
+def test_p8_packing(n, C):
+    r = rng(12 + n)
+    z = f32(r.standard_normal(n))
+    z[::7] = 0.0
+    z[3::11] = -0.0
+    bits, _ = oracle.compress_ef(z, np.zeros(n, np.float32), C)
+    K = oracle.num_chunks(n, C)
+    want = np.zeros(K * C, np.uint8)
+    want[:n] = ~np.signbit(z) | (z == 0)              # z >= 0, with -0 counted as >= 0
+    packed = np.packbits(want, bitorder="little").view(np.uint32)
+    assert np.array_equal(bits, packed)
+    assert int(np.unpackbits(bits.view(np.uint8)).sum()) == int(np.sum(z >= 0))
+
+
+def test_p8_tree_order_against_independent_pairwise():
+    # The chunk sum of squares uses the stride-halving tree t[j] += t[j+h],
+    # h = C/2 .. 1; an independent vectorised evaluation of the same tree.
+    r = rng(13)
+    for C in (64, 1024, 4096):
+        for n in (C, C - 1, C // 2 + 3, 1):
+            z = f32(r.standard_normal(n) * np.exp(r.uniform(-20, 20, n)))
+            t = np.zeros(C, np.float32)
+            t[:n] = z * z
+            while t.size > 1:
+                h = t.size // 2
+                t = t[:h] + t[h:]
+            expect = np.float32(np.sqrt(t[0])) / np.float32(np.sqrt(np.float32(n)))
+            assert oracle.chunk_scale(z, C) == expect
+
+
+# ---------------------------------------------------------------------------
+# P9  identity compressor => reconstructed gradient equals the mean gradient
+# ---------------------------------------------------------------------------
+def test_p9_reconstructed_gradient_identity():
+    numels = [3000]
+    N, W = 3000, 4
+    r = rng(14)
+    x = f32(r.standard_normal(N))
+    m = f32(r.standard_normal(N) * 1e-3)
+    m0 = m.copy()
+    vfz = f32(r.uniform(1e-8, 1e-4, N))
+    vf = vfz.copy()
+    g = [f32(r.standard_normal(N) * 1e-3) for _ in range(W)]
+    oracle.compressed_step(numels, 4096, g, [np.zeros(N, np.float32) for _ in range(W)],
+                           np.zeros(N, np.float32), x, m, vfz, vf, np.ones(1, np.float32),
+                           np.ones(1, np.float32), hp(), compressor=oracle.IDENTITY)
+    gbar = np.mean([gi.astype(np.float64) for gi in g], axis=0)
+    want = 0.999 * vfz.astype(np.float64) + 0.001 * gbar * gbar
+    assert np.max(np.abs(vf - want) / want) < 2e-5
+    assert np.allclose(m, 0.9 * m0.astype(np.float64) + 0.1 * gbar, rtol=0, atol=1e-9)
+
+
+# ---------------------------------------------------------------------------
+# P10 layerwise rescale: closed form with a zero reconstructed gradient, and
+#     the soft-threshold truth table
+# ---------------------------------------------------------------------------
+def _constant_magnitude_state(numels, mus, r):
+    N = sum(numels)
+    sign = np.where(r.random(N) < 0.5, -1.0, 1.0)
+    m = f32(sign * np.repeat(mus, numels))
+    return m
+
+
+def _run_zero_ghat(numels, vfz, vf, f_prev, c_avg, W=4):
+    N = sum(numels)
+    r = rng(15)
+    m = _constant_magnitude_state(numels, r.uniform(1e-4, 1e-2, len(numels)), r)
+    beta1 = np.float32(0.9)
+    mhat_want = beta1 * m
+    x = f32(r.standard_normal(N) * 0.02)
+    g = [np.zeros(N, np.float32)] * W
+    err_w = [np.zeros(N, np.float32) for _ in range(W)]
+    err_s = np.zeros(N, np.float32)
+    out = oracle.compressed_step(numels, 4096, g, err_w, err_s, x, m, vfz, vf, c_avg, f_prev, hp())
+    assert np.array_equal(m, mhat_want)               # mhat = fl(beta1 m) exactly
+    assert all(np.all(e == 0) for e in err_w) and np.all(err_s == 0)
+    return out
+
+
+def test_p10_zero_ghat_closed_form():
+    numels = [4096 * 2, 4096]
+    N = sum(numels)
+    r = rng(16)
+    vfz = f32(r.uniform(1e-8, 1e-4, N))
+    vf = vfz.copy()
+    c_avg = np.array([2.0, 0.5], np.float32)
+    out = _run_zero_ghat(numels, vfz, vf, np.ones(2, np.float32), c_avg)
+    assert np.array_equal(vf, np.float32(0.999) * vfz)  # ghat = 0: only the decay
+    off = 0
+    for l, nl in enumerate(numels):
+        sl = slice(off, off + nl)
+        q = (np.sqrt(vfz[sl].astype(np.float64)) + 1e-8) / (np.sqrt(vf[sl].astype(np.float64)) + 1e-8)
+        rho = q.max()
+        assert abs(rho - 1 / math.sqrt(0.999)) < 1e-6
+        assert abs(out["c"][l] / c_avg[l] - rho) <= 6 * U * rho
+        off += nl
+
+
+def test_p10_soft_threshold_truth_table():
+    rows = [ln.split() for ln in open(os.path.join(GOLDEN, "soft_threshold_cases.txt"))
+            if ln.strip() and not ln.startswith("#")]
+    L = len(rows)
+    numels = [4096] * L
+    N = sum(numels)
+    r = rng(17)
+    vfz = f32(r.uniform(1e-6, 1e-5, N))
+    vf = np.empty(N, np.float32)
+    f_prev = np.empty(L, np.float32)
+    for l, (_, fp, rho_t, _, _) in enumerate(rows):
+        sl = slice(4096 * l, 4096 * l + 4096)
+        # rho = max sqrt(vfz / (beta2 vf)) -> choose vf so that the max is near rho_t
+        vf[sl] = f32(vfz[sl].astype(np.float64) / (0.999 * float(rho_t) ** 2))
+        f_prev[l] = np.float32(float(fp))
+    vfz_c, vf_c = vfz.copy(), vf.copy()
+    out = _run_zero_ghat(numels, vfz, vf, f_prev, np.ones(L, np.float32))
+    for l, (name, _, _, expect, _) in enumerate(rows):
+        if expect == "rho":
+            sl = slice(4096 * l, 4096 * l + 4096)
+            vf_new = np.float32(0.999) * vf_c[sl]
+            rho = np.max((np.sqrt(vfz_c[sl].astype(np.float64)) + 1e-8) /
+                         (np.sqrt(vf_new.astype(np.float64)) + 1e-8))
+            assert abs(out["c"][l] - rho) <= 6 * U * rho, name
+        else:
+            assert out["c"][l] == np.float32(float.fromhex(expect)), name
+    assert np.array_equal(f_prev, out["c"])          # f_prev tracks the new factor (c_avg = 1)
+
+
+# ---------------------------------------------------------------------------
+# P11 power-of-two homogeneity and antisymmetry of the 1-bit operator
+# ---------------------------------------------------------------------------
+def test_p11_homogeneity_and_antisymmetry():
+    n, C = 4096 * 2 + 500, 4096
+    z = f32(rng(18).standard_normal(n))
+    z[z == 0] = 1.0
+    e1 = np.zeros(n, np.float32)
+    b1, s1 = oracle.compress_ef(z, e1, C)
+    e4 = np.zeros(n, np.float32)
+    b4, s4 = oracle.compress_ef(f32(z * 4), e4, C)
+    assert np.array_equal(b4, b1) and np.array_equal(s4, s1 * 4) and np.array_equal(e4, e1 * 4)
+    en = np.zeros(n, np.float32)
+    bn, sn = oracle.compress_ef(f32(-z), en, C)
+    valid = np.zeros(oracle.num_chunks(n, C) * C, bool)
+    valid[:n] = True
+    ub1 = np.unpackbits(b1.view(np.uint8), bitorder="little").astype(bool)
+    ubn = np.unpackbits(bn.view(np.uint8), bitorder="little").astype(bool)
+    assert np.array_equal(ubn[valid], ~ub1[valid]) and not ubn[~valid].any()
+    assert np.array_equal(sn, s1) and np.array_equal(en, -e1)
+
+
+# ---------------------------------------------------------------------------
+# P12 LAMB scale invariance: with eta = 0, g -> 2^k g leaves the update alone
+# ---------------------------------------------------------------------------
+def test_p12_scale_invariance():
+    numels = [2000, 96]
+    N = sum(numels)
+    r = rng(19)
+    h = hp(eta=0.0)
+    x0 = f32(r.standard_normal(N) * 0.02)
+    gs = [[f32(r.standard_normal(N) * 1e-3) for _ in range(2)] for _ in range(3)]
+    res = []
+    for scale in (1.0, 4.0, 0.125):
+        x, m, v = x0.copy(), np.zeros(N, np.float32), np.zeros(N, np.float32)
+        cs = np.zeros(2, np.float32)
+        for g in gs:
+            oracle.warmup_step(numels, [f32(gi * scale) for gi in g], x, m, v, cs, h)
+        res.append((x, cs))
+    for x, cs in res[1:]:
+        assert np.array_equal(x, res[0][0]) and np.array_equal(cs, res[0][1])
+
+
+# ---------------------------------------------------------------------------
+# P13 determinism and freeze bookkeeping
+# ---------------------------------------------------------------------------
+def test_p13_determinism_and_freeze():
+    numels = [4096, 777]
+    N, W = sum(numels), 2
+    r = rng(20)
+    v = f32(r.uniform(1e-8, 1e-4, N))
+    outs = []
+    for _ in range(2):
+        vf = np.empty(N, np.float32)
+        err_w = [f32(r.standard_normal(N)) for _ in range(W)]
+        err_s = f32(r.standard_normal(N))
+        c_avg = np.empty(2, np.float32)
+        f_prev = np.zeros(2, np.float32)
+        oracle.freeze(numels, v, vf, err_w, err_s, np.array([3.0, 1.5], np.float32), 3, c_avg, f_prev)
+        assert np.array_equal(vf, v) and all(np.all(e == 0) for e in err_w) and np.all(err_s == 0)
+        assert np.array_equal(c_avg, [1.0, 0.5]) and np.array_equal(f_prev, [1.0, 1.0])
+        rr = rng(21)
+        x, m = f32(rr.standard_normal(N)), f32(rr.standard_normal(N) * 1e-3)
+        g = [f32(rr.standard_normal(N) * 1e-3) for _ in range(W)]
+        out = oracle.compressed_step(numels, 4096, g, err_w, err_s, x, m, v, vf, c_avg, f_prev, hp())
+        outs.append((x, m, vf, err_s, out["bits_s"], out["scales_s"], out["c"]))
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
