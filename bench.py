@@ -1,0 +1,226 @@
+#!/usr/bin/env python3
+"""Benchmark: one 1-bit LAMB compression-stage step over the BERT-Large
+tensor table (385 fp32 tensors, N = 333,563,904 parameters) with W = 8
+simulated workers on one MI355X.
+
+A step is the whole hot path through the C ABI: every worker's
+error-compensated 1-bit compression of its momentum, the server average
+and recompression, the reconstructed gradient and fresh variance, the
+per-tensor rescale with soft thresholds, and the parameter update.  Inputs
+are synthetic (seeded counter-based generator) and already resident in HBM
+when the timed region starts; the gradient buffers are filled once and
+reused by every step (the optimizer state still evolves step to step).
+
+Prints one JSON line.  `value` is parameters per second for the step;
+`roofline` is the dominant kernel (phase 1: compression, average, rescale
+statistics) timed with HIP events on its stream; `cpu_baseline` is the
+single-threaded CPU oracle on a bounded window of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+METRIC = "params/sec and achieved HBM GB/s (% of peak) per 1-bit LAMB step"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def step_bytes(N, K, C, W):
+    """Algorithmic bytes of the step, every array touched once: momentum
+    read and written, each worker's gradient read and error read and
+    written, the server error read and written, the frozen variance read,
+    the fresh variance and the parameters read and written, and the packed
+    signs and scales of the W workers and the server written."""
+    packed = (W + 1) * K * (C // 8 + 4)
+    return N * (12 * W + 36) + packed
+
+
+def phase1_bytes(N, K, C, W):
+    """Algorithmic bytes of the phase-1 kernel: m read; per worker g read,
+    e read and written; e_s read and written; v_fresh read and written;
+    v_frozen read; (W+1) packed sign arrays and scales written."""
+    packed = (W + 1) * K * (C // 8 + 4)
+    return N * (12 * W + 24) + packed
+
+
+def cpu_baseline(wl, n_chunks):
+    """The oracle (single-threaded C, as it stands) on the window of the
+    first n_chunks chunks of the workload: one compression step."""
+    import numpy as np
+    from tests.harness import HostRun
+    hi = min(wl.N, n_chunks * wl.chunk)
+    h = HostRun(wl, 0, hi)
+    h.fill_grads(0)
+    t0 = time.perf_counter()
+    h.compressed_step(0, fill=False)
+    dt = time.perf_counter() - t0
+    del np
+    return {"value": hi / dt, "unit": "params/s", "cores": 1, "kind": "oracle",
+            "sample": f"one compression step on elements [0, {hi}) of the {wl.name} table "
+                      f"(first {hi // wl.chunk} chunks, W={wl.W}); {dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="bert_large")
+    ap.add_argument("--cpu-chunks", type=int, default=12288,
+                    help="chunks of the workload the CPU oracle baseline runs (0 = skip)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        log(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the W workers are "
+            "simulated as W buffers on one device, so there is no multi-GPU run to measure")
+        sys.exit(2)
+
+    need = [os.path.join(ROOT, "communication_compressed_optimizer_amd", "libonebit.so"),
+            os.path.join(ROOT, "synth", "libsynth_dev.so"), os.path.join(ROOT, "oracle", "liboracle.so")]
+    if not all(os.path.exists(p) for p in need):
+        import __graft_entry__
+        __graft_entry__.build()
+
+    import torch
+    import communication_compressed_optimizer_amd as ob
+    from synth.workloads import HPARAMS, WORKLOADS
+
+    wl = WORKLOADS[args.workload]
+    C, N, W, K, L = wl.chunk, wl.N, wl.W, wl.K, wl.L
+    torch.cuda.set_device(0)
+    dev = "cuda"
+    log(f"[bench] workload {wl.name}: N={N} L={L} K={K} W={W}; allocating state")
+    table = ob.LayerTable(wl.numels, C)
+
+    def f():
+        return torch.empty(N, dtype=torch.float32, device=dev)
+
+    x, m, v, vf = f(), f(), f(), f()
+    err_s = torch.zeros(N, dtype=torch.float32, device=dev)
+    g = [f() for _ in range(W)]
+    e = [torch.zeros(N, dtype=torch.float32, device=dev) for _ in range(W)]
+    words = K * C // 32
+    bits_w = [torch.zeros(words, dtype=torch.int32, device=dev) for _ in range(W)]
+    scales_w = [torch.zeros(K, dtype=torch.float32, device=dev) for _ in range(W)]
+    bits_s = torch.zeros(words, dtype=torch.int32, device=dev)
+    scales_s = torch.zeros(K, dtype=torch.float32, device=dev)
+    c_avg = torch.ones(L, dtype=torch.float32, device=dev)
+    f_prev = torch.ones(L, dtype=torch.float32, device=dev)
+    c_out = torch.zeros(L, dtype=torch.float32, device=dev)
+    ws = torch.empty(table.workspace_size(W), dtype=torch.uint8, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    hp = ob.onebit_hparams(**HPARAMS)
+    wl.fill("x", x)
+    wl.fill("m", m)
+    wl.fill("v", v)
+    vf.copy_(v)
+    for w in range(W):
+        wl.fill("g", g[w], 0, 0, w)
+    torch.cuda.synchronize()
+    log("[bench] inputs resident; warming up")
+
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        ob.onebit_lamb_compress_average(table, W, g, e, err_s, m, v, vf, bits_w, scales_w, bits_s,
+                                        scales_s, hp, ws, status, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        ob.onebit_lamb_rescale_update(table, bits_s, scales_s, x, m, v, c_avg, f_prev, c_out, hp,
+                                      ws, status, stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    st = int(status.item())
+    if st:
+        log(f"[bench] WARNING: status flags {st} (non-finite scale or statistic)")
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    p1 = sorted(a.elapsed_time(b) for a, b, _ in evs)
+    p2 = sorted(b.elapsed_time(c) for _, b, c in evs)
+    p1_ms = sum(p1) / len(p1)
+    p2_ms = sum(p2) / len(p2)
+    log(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step (phase1 {p1_ms:.3f} ms, "
+        f"phase2 {p2_ms:.3f} ms)")
+
+    sbytes = step_bytes(N, K, C, W)
+    abytes = phase1_bytes(N, K, C, W)
+    achieved = abytes / (p1_ms * 1e-3) / 1e9
+    step_gbps = sbytes / (ms_per_step * 1e-3) / 1e9
+    traffic = None
+    prof = os.path.join(ROOT, "profiles", "traffic_compress_average_bert_large.json")
+    if os.path.exists(prof):
+        try:
+            with open(prof) as fh:
+                t = json.load(fh)
+            if t.get("kernel_source_sha") == _kernel_sha():
+                traffic = t.get("bytes_per_launch")
+        except Exception:
+            traffic = None
+
+    cpu = None
+    if args.cpu_chunks > 0:
+        log("[bench] CPU oracle baseline ...")
+        cpu = cpu_baseline(wl, args.cpu_chunks)
+        log(f"[bench] oracle: {cpu['value']:.3e} params/s ({cpu['sample']})")
+
+    out = {
+        "metric": METRIC,
+        "value": N / (ms_per_step * 1e-3),
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: 1-bit LAMB compression-stage step, {L} tensors, "
+                               f"N={N}, W={W} simulated workers, chunk {C}",
+                   "N": N, "W": W, "tensors": L, "chunk": C},
+        "achieved_GBps": step_gbps,
+        "frac_of_peak": step_gbps / PEAK_HBM_GBPS,
+        "step_bytes": sbytes,
+        "phase_ms": {"compress_average": p1_ms, "rescale_update": p2_ms},
+        "roofline": {"bound": "hbm", "kernel": "k_compressed_pass_a<4096>",
+                     "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
+                     "algorithmic_bytes": abytes},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def _kernel_sha():
+    import hashlib
+    h = hashlib.sha256()
+    for p in ("communication_compressed_optimizer_amd/csrc/onebit_kernels.hpp",
+              "communication_compressed_optimizer_amd/csrc/onebit.hip"):
+        with open(os.path.join(ROOT, p), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+if __name__ == "__main__":
+    main()

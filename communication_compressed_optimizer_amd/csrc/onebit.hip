@@ -1,0 +1,540 @@
+// C ABI of libonebit.so (declared in include/onebit.h): argument checks,
+// the tensor-table descriptor, workspace layout and kernel launches.  All
+// arithmetic runs in the kernels of onebit_kernels.hpp.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "onebit.h"
+#include "onebit_kernels.hpp"
+
+using namespace onebit;
+
+struct onebit_layer_table {
+  int32_t L = 0;
+  int32_t chunk = 0;
+  int64_t N = 0;
+  int64_t K = 0;
+  int64_t S = 0;  // (chunk, tensor) segments
+  void* dblock = nullptr;
+  DevTable dev{};
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return ONEBIT_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool chunk_supported(int32_t c) { return c >= 1024 && c <= 16384 && (c & (c - 1)) == 0; }
+
+size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
+
+// Checks a device array pointer argument.
+#define CHECK_PTR(p, name)                                                                   \
+  do {                                                                                       \
+    if (!(p)) return fail(ONEBIT_EINVAL, "%s: %s is NULL", __func__, name);                  \
+    if (!aligned16(p)) return fail(ONEBIT_EALIGN, "%s: %s is not 16-byte aligned", __func__, \
+                                   name);                                                    \
+  } while (0)
+
+#define CHECK_OPT_PTR(p, name)                                                               \
+  do {                                                                                       \
+    if ((p) && !aligned16(p))                                                                \
+      return fail(ONEBIT_EALIGN, "%s: %s is not 16-byte aligned", __func__, name);           \
+  } while (0)
+
+int launch_status(const char* fn) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(ONEBIT_EHIP, "%s: kernel launch failed: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
+Coef make_coef(const onebit_hparams& h) {
+  Coef c;
+  c.beta1 = h.beta1;
+  c.beta2 = h.beta2;
+  c.eta = h.eta;
+  c.lr = h.lr;
+  c.a1 = 1.0f - h.beta1;
+  c.a2 = 1.0f - h.beta2;
+  c.kp = 1.0f + h.kappa;
+  c.km = 1.0f - h.kappa;
+  c.c_min = h.c_min;
+  c.c_max = h.c_max;
+  c.f_min = h.f_min;
+  c.f_max = h.f_max;
+  return c;
+}
+
+int check_hparams(const onebit_hparams* hp, const char* fn) {
+  if (!hp) return fail(ONEBIT_EINVAL, "%s: hp is NULL", fn);
+  if (hp->weight_decay != 0.0f)
+    return fail(ONEBIT_EUNSUPPORTED, "%s: weight_decay must be 0", fn);
+  return ONEBIT_OK;
+}
+
+int check_table(const onebit_layer_table* t, const char* fn) {
+  if (!t || !t->dblock) return fail(ONEBIT_EINVAL, "%s: table is NULL", fn);
+  return ONEBIT_OK;
+}
+
+int check_W(int32_t W, const char* fn) {
+  if (W < 1 || W > kMaxWorkers)
+    return fail(ONEBIT_EUNSUPPORTED, "%s: W = %d outside [1, %d]", fn, W, kMaxWorkers);
+  return ONEBIT_OK;
+}
+
+// Workspace layout: [seg_x: S doubles][seg_u: S doubles][c_layer: L floats];
+// the compression step reuses the first S floats as seg_max.
+struct Ws {
+  double* seg_x;
+  double* seg_u;
+  float* seg_max;
+  float* c_layer;
+};
+
+size_t ws_bytes(const onebit_layer_table* t) {
+  return 2 * round256(sizeof(double) * (size_t)t->S) + round256(sizeof(float) * (size_t)t->L);
+}
+
+Ws ws_view(const onebit_layer_table* t, void* ws) {
+  char* p = static_cast<char*>(ws);
+  Ws w;
+  w.seg_x = reinterpret_cast<double*>(p);
+  w.seg_u = reinterpret_cast<double*>(p + round256(sizeof(double) * (size_t)t->S));
+  w.seg_max = reinterpret_cast<float*>(p);
+  w.c_layer = reinterpret_cast<float*>(p + 2 * round256(sizeof(double) * (size_t)t->S));
+  return w;
+}
+
+// Dispatch a chunk-templated launch on the runtime chunk size.
+template <template <int> class F, typename... A>
+void by_chunk(int32_t chunk, A&&... a) {
+  switch (chunk) {
+    case 1024: F<1024>::run(a...); break;
+    case 2048: F<2048>::run(a...); break;
+    case 4096: F<4096>::run(a...); break;
+    case 8192: F<8192>::run(a...); break;
+    case 16384: F<16384>::run(a...); break;
+    default: break;
+  }
+}
+
+template <int C>
+struct LaunchCompress {
+  static void run(int64_t n, int64_t K, const float* in, float* err, uint32_t* bits, float* scales,
+                  int32_t* status, hipStream_t st) {
+    hipLaunchKernelGGL(k_compress_ef<C>, dim3((unsigned)K), dim3(C / 16), 0, st, n, in, err, bits,
+                       scales, status);
+  }
+};
+
+template <int C>
+struct LaunchAverage {
+  static void run(int64_t n, int64_t K, int W, const PackedIn& pin, float* err_s, uint32_t* bits,
+                  float* scales, int32_t* status, hipStream_t st) {
+    hipLaunchKernelGGL(k_average_packed<C>, dim3((unsigned)K), dim3(C / 16), 0, st, n, W, pin,
+                       err_s, bits, scales, status);
+  }
+};
+
+template <int C>
+struct LaunchDecompress {
+  static void run(int64_t n, int64_t K, const uint32_t* bits, const float* scales, float* out,
+                  hipStream_t st) {
+    hipLaunchKernelGGL(k_decompress<C>, dim3((unsigned)K), dim3(C / 16), 0, st, n, bits, scales,
+                       out);
+  }
+};
+
+template <int C>
+struct LaunchWarmup {
+  static void run(const onebit_layer_table* t, int W, const Workers& wk, float* x, float* m,
+                  float* v, float* c_sum, float* c_out, const Coef& cf, const Ws& ws,
+                  int32_t* status, hipStream_t st) {
+    hipLaunchKernelGGL(k_warmup_pass1<C>, dim3((unsigned)t->K), dim3(C / 16), 0, st, t->dev, W, wk,
+                       x, m, v, ws.seg_x, ws.seg_u, cf);
+    hipLaunchKernelGGL(k_warmup_finalize<256>, dim3((unsigned)t->L), dim3(256), 0, st, t->dev,
+                       ws.seg_x, ws.seg_u, c_sum, ws.c_layer, c_out, cf, status);
+    hipLaunchKernelGGL(k_warmup_pass2<C>, dim3((unsigned)t->K), dim3(C / 16), 0, st, t->dev, m, v,
+                       x, ws.c_layer, cf);
+  }
+};
+
+template <int C>
+struct LaunchFreeze {
+  static void run(const onebit_layer_table* t, int W, const float* v, float* v_fresh,
+                  const Workers& wk, float* err_s, hipStream_t st) {
+    hipLaunchKernelGGL(k_freeze_elems<C>, dim3((unsigned)t->K), dim3(C / 16), 0, st, t->N, W, v,
+                       v_fresh, wk, err_s);
+  }
+};
+
+template <int C>
+struct LaunchPassA {
+  static void run(const onebit_layer_table* t, int W, const Workers& wk, float* err_s,
+                  const float* m, const float* v_frozen, float* v_fresh, uint32_t* bits_s,
+                  float* scales_s, const Coef& cf, const Ws& ws, int32_t* status, hipStream_t st) {
+    hipLaunchKernelGGL(k_compressed_pass_a<C>, dim3((unsigned)t->K), dim3(C / 16), 0, st, t->dev, W,
+                       wk, err_s, m, v_frozen, v_fresh, bits_s, scales_s, ws.seg_max, cf, status);
+  }
+};
+
+template <int C>
+struct LaunchPassB {
+  static void run(const onebit_layer_table* t, const uint32_t* bits_s, const float* scales_s,
+                  float* x, float* m, const float* v_frozen, const float* c_avg, float* f_prev,
+                  float* c_out, const Coef& cf, const Ws& ws, int32_t* status, hipStream_t st) {
+    hipLaunchKernelGGL(k_rescale_finalize<256>, dim3((unsigned)t->L), dim3(256), 0, st, t->dev,
+                       ws.seg_max, c_avg, f_prev, ws.c_layer, c_out, cf, status);
+    hipLaunchKernelGGL(k_compressed_pass_b<C>, dim3((unsigned)t->K), dim3(C / 16), 0, st, t->dev,
+                       bits_s, scales_s, v_frozen, x, m, ws.c_layer, cf);
+  }
+};
+
+// Checks shared by the compressed-step entry points; fills wk.
+int check_phase1(const char* fn, const onebit_layer_table* table, int32_t W,
+                 const float* const* grads, float* const* err_w, float* err_s, const float* m,
+                 const float* v_frozen, float* v_fresh, uint32_t* const* bits_w,
+                 float* const* scales_w, uint32_t* bits_s, float* scales_s,
+                 const onebit_hparams* hp, void* ws, Workers& wk) {
+  if (int rc = check_table(table, fn)) return rc;
+  if (int rc = check_W(W, fn)) return rc;
+  if (int rc = check_hparams(hp, fn)) return rc;
+  if (!grads || !err_w) return fail(ONEBIT_EINVAL, "%s: grads or err_w is NULL", fn);
+  wk = Workers{};
+  for (int w = 0; w < W; ++w) {
+    if (!grads[w] || !err_w[w]) return fail(ONEBIT_EINVAL, "%s: grads[%d] or err_w[%d] is NULL", fn, w, w);
+    if (!aligned16(grads[w]) || !aligned16(err_w[w]))
+      return fail(ONEBIT_EALIGN, "%s: grads[%d] or err_w[%d] is not 16-byte aligned", fn, w, w);
+    wk.g[w] = grads[w];
+    wk.e[w] = err_w[w];
+    if (bits_w) {
+      if (bits_w[w] && !aligned16(bits_w[w]))
+        return fail(ONEBIT_EALIGN, "%s: bits_w[%d] is not 16-byte aligned", fn, w);
+      wk.bits[w] = bits_w[w];
+    }
+    if (scales_w) {
+      if (scales_w[w] && !aligned16(scales_w[w]))
+        return fail(ONEBIT_EALIGN, "%s: scales_w[%d] is not 16-byte aligned", fn, w);
+      wk.scales[w] = scales_w[w];
+    }
+  }
+  const void* req[] = {err_s, m, v_frozen, v_fresh, bits_s, scales_s, ws};
+  const char* names[] = {"err_s", "m", "v_frozen", "v_fresh", "bits_s", "scales_s", "ws"};
+  for (int i = 0; i < 7; ++i) {
+    if (!req[i]) return fail(ONEBIT_EINVAL, "%s: %s is NULL", fn, names[i]);
+    if (!aligned16(req[i])) return fail(ONEBIT_EALIGN, "%s: %s is not 16-byte aligned", fn, names[i]);
+  }
+  return ONEBIT_OK;
+}
+
+int check_phase2(const char* fn, const onebit_layer_table* table, const uint32_t* bits_s,
+                 const float* scales_s, float* x, float* m, const float* v_frozen,
+                 const float* c_avg, float* f_prev, float* c_out, const onebit_hparams* hp,
+                 void* ws) {
+  if (int rc = check_table(table, fn)) return rc;
+  if (int rc = check_hparams(hp, fn)) return rc;
+  const void* req[] = {bits_s, scales_s, x, m, v_frozen, c_avg, f_prev, ws};
+  const char* names[] = {"bits_s", "scales_s", "x", "m", "v_frozen", "c_avg", "f_prev", "ws"};
+  for (int i = 0; i < 8; ++i) {
+    if (!req[i]) return fail(ONEBIT_EINVAL, "%s: %s is NULL", fn, names[i]);
+    if (!aligned16(req[i])) return fail(ONEBIT_EALIGN, "%s: %s is not 16-byte aligned", fn, names[i]);
+  }
+  if (c_out && !aligned16(c_out)) return fail(ONEBIT_EALIGN, "%s: c_out is not 16-byte aligned", fn);
+  return ONEBIT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* onebit_last_error(void) { return g_last_error.c_str(); }
+
+const char* onebit_version(void) { return "onebit 0.1 (gfx950)"; }
+
+int onebit_layer_table_create(const int64_t* numels, int32_t L, int32_t chunk,
+                              onebit_layer_table** out) {
+  if (!numels || !out) return fail(ONEBIT_EINVAL, "%s: NULL argument", __func__);
+  *out = nullptr;
+  if (L < 1) return fail(ONEBIT_EINVAL, "%s: L = %d < 1", __func__, L);
+  if (!chunk_supported(chunk))
+    return fail(ONEBIT_EUNSUPPORTED, "%s: chunk %d is not a power of two in [1024, 16384]",
+                __func__, chunk);
+  std::vector<int64_t> off((size_t)L + 1, 0);
+  for (int32_t l = 0; l < L; ++l) {
+    if (numels[l] < 1) return fail(ONEBIT_EINVAL, "%s: numels[%d] = %lld < 1", __func__, l,
+                                   (long long)numels[l]);
+    off[l + 1] = off[l] + numels[l];
+  }
+  const int64_t N = off[L];
+  const int64_t K = (N + chunk - 1) / chunk;
+  if (K > INT32_MAX / 2) return fail(ONEBIT_EUNSUPPORTED, "%s: too many chunks", __func__);
+  std::vector<int32_t> l0((size_t)K), l1((size_t)K), seg((size_t)K), lseg((size_t)L + 1);
+  int64_t S = 0;
+  int32_t l = 0;
+  for (int64_t k = 0; k < K; ++k) {
+    const int64_t first = k * chunk;
+    const int64_t last = (k + 1) * chunk < N ? (k + 1) * chunk - 1 : N - 1;
+    while (off[l + 1] <= first) ++l;
+    l0[k] = l;
+    int32_t e = l;
+    while (off[e + 1] <= last) ++e;
+    l1[k] = e;
+    seg[k] = (int32_t)S;
+    S += e - l + 1;
+  }
+  if (S > INT32_MAX) return fail(ONEBIT_EUNSUPPORTED, "%s: too many segments", __func__);
+  for (int32_t t = 0; t < L; ++t) {
+    const int64_t k = off[t] / chunk;
+    lseg[t] = seg[k] + (t - l0[k]);
+  }
+  lseg[L] = (int32_t)S;
+
+  onebit_layer_table* t = new (std::nothrow) onebit_layer_table();
+  if (!t) return fail(ONEBIT_ENOMEM, "%s: host allocation failed", __func__);
+  t->L = L;
+  t->chunk = chunk;
+  t->N = N;
+  t->K = K;
+  t->S = S;
+  const size_t b_off = round256(sizeof(int64_t) * ((size_t)L + 1));
+  const size_t b_k = round256(sizeof(int32_t) * (size_t)K);
+  const size_t b_l = round256(sizeof(int32_t) * ((size_t)L + 1));
+  const size_t total = b_off + 3 * b_k + b_l;
+  hipError_t e = hipMalloc(&t->dblock, total);
+  if (e != hipSuccess) {
+    delete t;
+    return fail(e == hipErrorOutOfMemory ? ONEBIT_ENOMEM : ONEBIT_EHIP, "%s: hipMalloc: %s",
+                __func__, hipGetErrorString(e));
+  }
+  char* p = static_cast<char*>(t->dblock);
+  struct Piece {
+    const void* src;
+    size_t bytes;
+    size_t at;
+  } pieces[] = {{off.data(), sizeof(int64_t) * ((size_t)L + 1), 0},
+                {l0.data(), sizeof(int32_t) * (size_t)K, b_off},
+                {l1.data(), sizeof(int32_t) * (size_t)K, b_off + b_k},
+                {seg.data(), sizeof(int32_t) * (size_t)K, b_off + 2 * b_k},
+                {lseg.data(), sizeof(int32_t) * ((size_t)L + 1), b_off + 3 * b_k}};
+  for (const Piece& pc : pieces) {
+    e = hipMemcpy(p + pc.at, pc.src, pc.bytes, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+      (void)hipFree(t->dblock);
+      delete t;
+      return fail(ONEBIT_EHIP, "%s: hipMemcpy: %s", __func__, hipGetErrorString(e));
+    }
+  }
+  t->dev.off = reinterpret_cast<const int64_t*>(p);
+  t->dev.l0 = reinterpret_cast<const int32_t*>(p + b_off);
+  t->dev.l1 = reinterpret_cast<const int32_t*>(p + b_off + b_k);
+  t->dev.seg = reinterpret_cast<const int32_t*>(p + b_off + 2 * b_k);
+  t->dev.lseg = reinterpret_cast<const int32_t*>(p + b_off + 3 * b_k);
+  t->dev.N = N;
+  t->dev.K = K;
+  t->dev.L = L;
+  *out = t;
+  return ok();
+}
+
+int onebit_layer_table_destroy(onebit_layer_table* table) {
+  if (!table) return ok();
+  hipError_t e = hipSuccess;
+  if (table->dblock) e = hipFree(table->dblock);
+  delete table;
+  if (e != hipSuccess) return fail(ONEBIT_EHIP, "%s: hipFree: %s", __func__, hipGetErrorString(e));
+  return ok();
+}
+
+int onebit_layer_table_info(const onebit_layer_table* table, int64_t* N, int64_t* K,
+                            int64_t* n_segments) {
+  if (int rc = check_table(table, __func__)) return rc;
+  if (N) *N = table->N;
+  if (K) *K = table->K;
+  if (n_segments) *n_segments = table->S;
+  return ok();
+}
+
+int onebit_workspace_size(const onebit_layer_table* table, int32_t W, size_t* bytes) {
+  if (int rc = check_table(table, __func__)) return rc;
+  if (int rc = check_W(W, __func__)) return rc;
+  if (!bytes) return fail(ONEBIT_EINVAL, "%s: bytes is NULL", __func__);
+  *bytes = ws_bytes(table);
+  return ok();
+}
+
+int onebit_compress_ef(int64_t n, int32_t chunk, const float* in, float* err, uint32_t* bits,
+                       float* scales, int32_t* status, void* stream) {
+  if (n < 0) return fail(ONEBIT_EINVAL, "%s: n < 0", __func__);
+  if (!chunk_supported(chunk)) return fail(ONEBIT_EUNSUPPORTED, "%s: chunk %d", __func__, chunk);
+  if (n == 0) return ok();
+  CHECK_PTR(in, "in");
+  CHECK_PTR(err, "err");
+  CHECK_PTR(bits, "bits");
+  CHECK_PTR(scales, "scales");
+  const int64_t K = (n + chunk - 1) / chunk;
+  by_chunk<LaunchCompress>(chunk, n, K, in, err, bits, scales, status, (hipStream_t)stream);
+  return launch_status(__func__);
+}
+
+int onebit_average_packed(int64_t n, int32_t chunk, int32_t W, const uint32_t* const* bits_w,
+                          const float* const* scales_w, float* err_s, uint32_t* bits_out,
+                          float* scales_out, int32_t* status, void* stream) {
+  if (n < 0) return fail(ONEBIT_EINVAL, "%s: n < 0", __func__);
+  if (!chunk_supported(chunk)) return fail(ONEBIT_EUNSUPPORTED, "%s: chunk %d", __func__, chunk);
+  if (int rc = check_W(W, __func__)) return rc;
+  if (n == 0) return ok();
+  if (!bits_w || !scales_w) return fail(ONEBIT_EINVAL, "%s: worker arrays are NULL", __func__);
+  PackedIn pin{};
+  for (int w = 0; w < W; ++w) {
+    CHECK_PTR(bits_w[w], "bits_w[w]");
+    CHECK_PTR(scales_w[w], "scales_w[w]");
+    pin.bits[w] = bits_w[w];
+    pin.scales[w] = scales_w[w];
+  }
+  CHECK_PTR(err_s, "err_s");
+  CHECK_PTR(bits_out, "bits_out");
+  CHECK_PTR(scales_out, "scales_out");
+  const int64_t K = (n + chunk - 1) / chunk;
+  by_chunk<LaunchAverage>(chunk, n, K, (int)W, pin, err_s, bits_out, scales_out, status,
+                          (hipStream_t)stream);
+  return launch_status(__func__);
+}
+
+int onebit_decompress(int64_t n, int32_t chunk, const uint32_t* bits, const float* scales,
+                      float* out, void* stream) {
+  if (n < 0) return fail(ONEBIT_EINVAL, "%s: n < 0", __func__);
+  if (!chunk_supported(chunk)) return fail(ONEBIT_EUNSUPPORTED, "%s: chunk %d", __func__, chunk);
+  if (n == 0) return ok();
+  CHECK_PTR(bits, "bits");
+  CHECK_PTR(scales, "scales");
+  CHECK_PTR(out, "out");
+  const int64_t K = (n + chunk - 1) / chunk;
+  by_chunk<LaunchDecompress>(chunk, n, K, bits, scales, out, (hipStream_t)stream);
+  return launch_status(__func__);
+}
+
+int onebit_lamb_warmup_step(const onebit_layer_table* table, int32_t W, const float* const* grads,
+                            float* x, float* m, float* v, float* c_sum, float* c_out,
+                            const onebit_hparams* hp, void* ws, int32_t* status, void* stream) {
+  if (int rc = check_table(table, __func__)) return rc;
+  if (int rc = check_W(W, __func__)) return rc;
+  if (int rc = check_hparams(hp, __func__)) return rc;
+  if (!grads) return fail(ONEBIT_EINVAL, "%s: grads is NULL", __func__);
+  Workers wk{};
+  for (int w = 0; w < W; ++w) {
+    CHECK_PTR(grads[w], "grads[w]");
+    wk.g[w] = grads[w];
+  }
+  CHECK_PTR(x, "x");
+  CHECK_PTR(m, "m");
+  CHECK_PTR(v, "v");
+  CHECK_PTR(c_sum, "c_sum");
+  CHECK_OPT_PTR(c_out, "c_out");
+  CHECK_PTR(ws, "ws");
+  const Coef cf = make_coef(*hp);
+  by_chunk<LaunchWarmup>(table->chunk, table, (int)W, wk, x, m, v, c_sum, c_out, cf,
+                         ws_view(table, ws), status, (hipStream_t)stream);
+  return launch_status(__func__);
+}
+
+int onebit_lamb_freeze(const onebit_layer_table* table, int32_t W, const float* v, float* v_fresh,
+                       float* const* err_w, float* err_s, const float* c_sum, int32_t T_w,
+                       float* c_avg, float* f_prev, void* stream) {
+  if (int rc = check_table(table, __func__)) return rc;
+  if (int rc = check_W(W, __func__)) return rc;
+  if (T_w < 1) return fail(ONEBIT_EINVAL, "%s: T_w = %d < 1", __func__, T_w);
+  if (!err_w) return fail(ONEBIT_EINVAL, "%s: err_w is NULL", __func__);
+  Workers wk{};
+  for (int w = 0; w < W; ++w) {
+    CHECK_PTR(err_w[w], "err_w[w]");
+    wk.e[w] = err_w[w];
+  }
+  CHECK_PTR(v, "v");
+  CHECK_PTR(v_fresh, "v_fresh");
+  CHECK_PTR(err_s, "err_s");
+  CHECK_PTR(c_sum, "c_sum");
+  CHECK_PTR(c_avg, "c_avg");
+  CHECK_PTR(f_prev, "f_prev");
+  hipStream_t st = (hipStream_t)stream;
+  by_chunk<LaunchFreeze>(table->chunk, table, (int)W, v, v_fresh, wk, err_s, st);
+  hipLaunchKernelGGL(k_freeze_tensors, dim3((unsigned)((table->L + 255) / 256)), dim3(256), 0, st,
+                     (int)table->L, c_sum, (float)T_w, c_avg, f_prev);
+  return launch_status(__func__);
+}
+
+int onebit_lamb_compress_average(const onebit_layer_table* table, int32_t W,
+                                 const float* const* grads, float* const* err_w, float* err_s,
+                                 const float* m, const float* v_frozen, float* v_fresh,
+                                 uint32_t* const* bits_w, float* const* scales_w, uint32_t* bits_s,
+                                 float* scales_s, const onebit_hparams* hp, void* ws,
+                                 int32_t* status, void* stream) {
+  Workers wk;
+  if (int rc = check_phase1(__func__, table, W, grads, err_w, err_s, m, v_frozen, v_fresh, bits_w,
+                            scales_w, bits_s, scales_s, hp, ws, wk))
+    return rc;
+  by_chunk<LaunchPassA>(table->chunk, table, (int)W, wk, err_s, m, v_frozen, v_fresh, bits_s,
+                        scales_s, make_coef(*hp), ws_view(table, ws), status, (hipStream_t)stream);
+  return launch_status(__func__);
+}
+
+int onebit_lamb_rescale_update(const onebit_layer_table* table, const uint32_t* bits_s,
+                               const float* scales_s, float* x, float* m, const float* v_frozen,
+                               const float* c_avg, float* f_prev, float* c_out,
+                               const onebit_hparams* hp, void* ws, int32_t* status, void* stream) {
+  if (int rc = check_phase2(__func__, table, bits_s, scales_s, x, m, v_frozen, c_avg, f_prev, c_out,
+                            hp, ws))
+    return rc;
+  by_chunk<LaunchPassB>(table->chunk, table, bits_s, scales_s, x, m, v_frozen, c_avg, f_prev, c_out,
+                        make_coef(*hp), ws_view(table, ws), status, (hipStream_t)stream);
+  return launch_status(__func__);
+}
+
+int onebit_lamb_compressed_step(const onebit_layer_table* table, int32_t W,
+                                const float* const* grads, float* const* err_w, float* err_s,
+                                float* x, float* m, const float* v_frozen, float* v_fresh,
+                                const float* c_avg, float* f_prev, float* c_out,
+                                uint32_t* const* bits_w, float* const* scales_w, uint32_t* bits_s,
+                                float* scales_s, const onebit_hparams* hp, void* ws,
+                                int32_t* status, void* stream) {
+  Workers wk;
+  if (int rc = check_phase1(__func__, table, W, grads, err_w, err_s, m, v_frozen, v_fresh, bits_w,
+                            scales_w, bits_s, scales_s, hp, ws, wk))
+    return rc;
+  if (int rc = check_phase2(__func__, table, bits_s, scales_s, x, m, v_frozen, c_avg, f_prev, c_out,
+                            hp, ws))
+    return rc;
+  const Coef cf = make_coef(*hp);
+  const Ws wsv = ws_view(table, ws);
+  hipStream_t st = (hipStream_t)stream;
+  by_chunk<LaunchPassA>(table->chunk, table, (int)W, wk, err_s, m, v_frozen, v_fresh, bits_s,
+                        scales_s, cf, wsv, status, st);
+  by_chunk<LaunchPassB>(table->chunk, table, bits_s, scales_s, x, m, v_frozen, c_avg, f_prev, c_out,
+                        cf, wsv, status, st);
+  return launch_status(__func__);
+}
+
+}  // extern "C"

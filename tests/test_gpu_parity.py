@@ -1,0 +1,302 @@
+"""GPU parity: the HIP library, called through its C ABI, against the CPU
+oracle on the same seeded inputs.
+
+Signs, scales, errors, moments and the fresh variance must match bit for
+bit; parameters and per-tensor coefficients within rel 1e-5 / abs 1e-7
+(they are bit-exact in the compression stage too, where no order-dependent
+sum is involved, and that is reported).
+"""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("no GPU", allow_module_level=True)
+
+import communication_compressed_optimizer_amd as ob  # noqa: E402
+import oracle  # noqa: E402
+import synth  # noqa: E402
+from synth.workloads import HPARAMS, Workload, WORKLOADS  # noqa: E402
+
+from tests.harness import DevRun, HostRun, assert_parity, compare_state  # noqa: E402
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    return t.cpu().numpy()
+
+
+def u32(t):
+    return t.cpu().numpy().view(np.uint32)
+
+
+def normals(n, stream, std=1.0, seed=0, offset=0):
+    out = np.empty(n, np.float32)
+    return synth.normal_host(out, seed, stream, offset, 0.0, std)
+
+
+# ---------------------------------------------------------------------------
+# the generator itself: device fill == host fill, bit for bit
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("n,offset", [(1, 0), (1000, 7), (3_000_001, 123_456_789_012)])
+def test_synth_device_matches_host(n, offset):
+    t = torch.empty(n, dtype=torch.float32, device="cuda")
+    synth.normal_dev(t, 5, synth.stream_id(synth.G, 3, 2), offset, 0.25, 1e-3)
+    h = np.empty(n, np.float32)
+    synth.normal_host(h, 5, synth.stream_id(synth.G, 3, 2), offset, 0.25, 1e-3)
+    assert np.array_equal(host(t).view(np.uint32), h.view(np.uint32))
+    synth.uniform_dev(t, 5, 77, offset, 1e-8, 1e-4)
+    synth.uniform_host(h, 5, 77, offset, 1e-8, 1e-4)
+    assert np.array_equal(host(t).view(np.uint32), h.view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# codec entry points
+# ---------------------------------------------------------------------------
+CODEC_CASES = [(1, 4096), (4095, 4096), (4097, 4096), (129_792, 4096), (3 * 4096 + 2816, 4096),
+               (1_000_003, 1024), (70_001, 2048), (50_000, 8192), (100_001, 16384),
+               (16 * 1024 * 1024, 4096)]
+
+
+@pytest.mark.parametrize("n,C", CODEC_CASES)
+def test_compress_ef_parity(n, C):
+    K = oracle.num_chunks(n, C)
+    inp = normals(n, 11, 1e-3)
+    err = normals(n, 12, 1e-4)
+    inp[::97] = 0.0
+    inp[5::101] = -0.0
+    d_in, d_err = dev(inp), dev(err)
+    d_bits = torch.full((K * C // 32,), -1, dtype=torch.int32, device="cuda")
+    d_sc = torch.full((K,), float("nan"), dtype=torch.float32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ob.onebit_compress_ef(n, C, d_in, d_err, d_bits, d_sc, status)
+    bits, scales = oracle.compress_ef(inp, err, C)
+    assert np.array_equal(u32(d_bits), bits)
+    assert np.array_equal(host(d_sc).view(np.uint32), scales.view(np.uint32))
+    assert np.array_equal(host(d_err).view(np.uint32), err.view(np.uint32))
+    assert int(status.item()) == 0
+
+
+def test_compress_ef_zero_chunk_and_empty():
+    C = 4096
+    n = 2 * C
+    inp = np.zeros(n, np.float32)
+    inp[C:] = 1.0
+    err = np.zeros(n, np.float32)
+    d_in, d_err = dev(inp), dev(err)
+    d_bits = torch.zeros(n // 32, dtype=torch.int32, device="cuda")
+    d_sc = torch.zeros(2, dtype=torch.float32, device="cuda")
+    ob.onebit_compress_ef(n, C, d_in, d_err, d_bits, d_sc)
+    assert np.all(u32(d_bits) == 0xFFFFFFFF) and host(d_sc).tolist() == [0.0, 1.0]
+    assert np.all(host(d_err) == 0)
+    ob.onebit_compress_ef(0, C, None, None, None, None)  # n = 0 does nothing
+
+
+def test_status_flags_nonfinite():
+    C, n = 4096, 4096 * 2
+    inp = np.ones(n, np.float32)
+    inp[5000] = np.inf
+    d_in, d_err = dev(inp), dev(np.zeros(n, np.float32))
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ob.onebit_compress_ef(n, C, d_in, d_err, torch.zeros(n // 32, dtype=torch.int32, device="cuda"),
+                          torch.zeros(2, dtype=torch.float32, device="cuda"), status)
+    assert int(status.item()) == ob.ONEBIT_STATUS_NONFINITE_WORKER
+
+
+@pytest.mark.parametrize("W", [1, 2, 3, 8, 16])
+@pytest.mark.parametrize("n,C", [(129_792, 4096), (3 * 4096 + 5, 4096), (20_000, 1024)])
+def test_average_packed_parity(W, n, C):
+    K = oracle.num_chunks(n, C)
+    bits_w, scales_w = [], []
+    for w in range(W):
+        b, s = oracle.compress_ef(normals(n, 100 + w, 1e-3), np.zeros(n, np.float32), C)
+        bits_w.append(b)
+        scales_w.append(s)
+    err_s = normals(n, 200, 1e-4)
+    d_err = dev(err_s)
+    d_bits = torch.full((K * C // 32,), -1, dtype=torch.int32, device="cuda")
+    d_sc = torch.zeros(K, dtype=torch.float32, device="cuda")
+    ob.onebit_average_packed(n, C, W, [dev(b.view(np.int32)) for b in bits_w],
+                             [dev(s) for s in scales_w], d_err, d_bits, d_sc)
+    b, s = oracle.average_packed(bits_w, scales_w, err_s, C)
+    assert np.array_equal(u32(d_bits), b)
+    assert np.array_equal(host(d_sc).view(np.uint32), s.view(np.uint32))
+    assert np.array_equal(host(d_err).view(np.uint32), err_s.view(np.uint32))
+
+
+@pytest.mark.parametrize("n,C", [(129_792, 4096), (4097, 4096), (5000, 1024)])
+def test_decompress_parity(n, C):
+    bits, scales = oracle.compress_ef(normals(n, 300), np.zeros(n, np.float32), C)
+    out = torch.empty(n, dtype=torch.float32, device="cuda")
+    ob.onebit_decompress(n, C, dev(bits.view(np.int32)), dev(scales), out)
+    assert np.array_equal(host(out), oracle.decompress(bits, scales, n, C))
+
+
+# ---------------------------------------------------------------------------
+# optimizer steps on ragged tables
+# ---------------------------------------------------------------------------
+RAGGED = [
+    [1, 3, 4095, 4097, 100, 8192, 17],       # chunks straddle up to 4 tensors
+    [4096 * 3],                               # chunk-aligned single tensor
+    [5, 7, 11, 13] * 300 + [2048 * 3 + 1],   # many tiny tensors per chunk
+    [256 * 256, 256, 1000 * 64],              # the three-tensor table
+]
+
+
+def _ragged_workload(numels, W, chunk=4096, init="frozen"):
+    return Workload("ragged", numels, W=W, chunk=chunk, init=init,
+                    grad_std=0.02 if init == "fresh" else 1e-3)
+
+
+@pytest.mark.parametrize("numels", RAGGED)
+@pytest.mark.parametrize("W", [1, 3, 8, 16])
+def test_compressed_step_parity(numels, W):
+    wl = _ragged_workload(numels, W)
+    d, h = DevRun(wl), HostRun(wl)
+    for step in range(2):
+        d.compressed_step(step)
+        h.compressed_step(step)
+        rep = compare_state(d, h)
+        assert_parity(rep, f"step {step}")
+        assert rep["x"]["max_abs"] == 0.0          # no order-dependent sum in this stage
+    assert int(d.status.item()) == 0
+
+
+@pytest.mark.parametrize("chunk", [1024, 2048, 8192, 16384])
+def test_compressed_step_other_chunks(chunk):
+    wl = _ragged_workload(RAGGED[0] + [3 * chunk + 9], 4, chunk=chunk)
+    d, h = DevRun(wl), HostRun(wl)
+    d.compressed_step(0)
+    h.compressed_step(0)
+    assert_parity(compare_state(d, h))
+
+
+@pytest.mark.parametrize("numels", RAGGED)
+@pytest.mark.parametrize("W", [1, 2, 8])
+def test_warmup_step_parity(numels, W):
+    wl = _ragged_workload(numels, W, init="fresh")
+    d, h = DevRun(wl), HostRun(wl)
+    for step in range(3):
+        d.warmup_step(step)
+        h.warmup_step(step)
+        assert_parity(compare_state(d, h, stage="warmup"), f"warmup step {step}")
+
+
+def test_freeze_parity():
+    wl = _ragged_workload(RAGGED[0], 3, init="fresh")
+    d, h = DevRun(wl), HostRun(wl)
+    for step in range(3):
+        d.warmup_step(step)
+        h.warmup_step(step)
+    d.freeze(3)
+    h.freeze(3)
+    assert_parity(compare_state(d, h, stage="warmup"))
+    for w in range(3):
+        assert torch.count_nonzero(d.e[w]).item() == 0
+    assert torch.equal(d.vf, d.v)
+
+
+# ---------------------------------------------------------------------------
+# whole workloads
+# ---------------------------------------------------------------------------
+def test_tiny_trajectory():
+    """The three-tensor workload end to end: 5 warmup steps, freeze, 5
+    compression steps, GPU and oracle each on their own state."""
+    wl = WORKLOADS["tiny"]
+    d, h = DevRun(wl), HostRun(wl)
+    step = 0
+    for _ in range(wl.warmup_steps):
+        d.warmup_step(step)
+        h.warmup_step(step)
+        assert_parity(compare_state(d, h, stage="warmup"), f"warmup {step}")
+        step += 1
+    d.freeze(wl.warmup_steps)
+    h.freeze(wl.warmup_steps)
+    for _ in range(wl.compression_steps):
+        d.compressed_step(step)
+        h.compressed_step(step)
+        assert_parity(compare_state(d, h), f"compression {step}")
+        step += 1
+    assert int(d.status.item()) == 0
+
+
+def test_tiny_strict_per_step():
+    """Each step from an identical state: the oracle adopts the GPU state
+    before every step."""
+    wl = WORKLOADS["tiny"]
+    d, h = DevRun(wl), HostRun(wl)
+    for step in range(3):
+        h.load_from(d.window(0, wl.N))
+        d.warmup_step(step)
+        h.warmup_step(step)
+        assert_parity(compare_state(d, h, stage="warmup"))
+    d.freeze(3)
+    h.freeze(3)
+    for step in range(3, 6):
+        h.load_from(d.window(0, wl.N))
+        d.compressed_step(step)
+        h.compressed_step(step)
+        assert_parity(compare_state(d, h))
+
+
+def test_single_layer_16m():
+    """One 16M-element tensor, W = 4, one compression step, whole buffer."""
+    wl = WORKLOADS["single"]
+    d, h = DevRun(wl), HostRun(wl)
+    d.compressed_step(0)
+    h.compressed_step(0)
+    assert_parity(compare_state(d, h))
+
+
+def test_determinism_and_resume():
+    """Two runs are bitwise identical, and a run resumed from a saved state
+    equals the uninterrupted one (across the warmup -> compression switch)."""
+    wl = _ragged_workload(RAGGED[0], 4, init="fresh")
+    a = DevRun(wl)
+    for s in range(3):
+        a.warmup_step(s)
+    saved = {k: getattr(a, k).clone() for k in ("x", "m", "v", "vf", "c_sum")}
+    a.freeze(3)
+    for s in range(3, 6):
+        a.compressed_step(s)
+    b = DevRun(wl)
+    for k, t in saved.items():
+        getattr(b, k).copy_(t)
+    b.freeze(3)
+    for s in range(3, 6):
+        b.compressed_step(s)
+    for k in ("x", "m", "v", "vf", "err_s", "bits_s", "scales_s", "f_prev", "c_out"):
+        assert torch.equal(getattr(a, k), getattr(b, k)), k
+    for w in range(4):
+        assert torch.equal(a.e[w], b.e[w])
+
+
+def test_two_phase_equals_fused():
+    """onebit_lamb_compress_average + onebit_lamb_rescale_update is
+    onebit_lamb_compressed_step."""
+    wl = _ragged_workload(RAGGED[0], 4)
+    a, b = DevRun(wl), DevRun(wl)
+    for step in range(2):
+        a.compressed_step(step)
+        b.fill_grads(step)
+        ob.onebit_lamb_compress_average(b.table, 4, b.g, b.e, b.err_s, b.m, b.v, b.vf, b.bits_w,
+                                        b.scales_w, b.bits_s, b.scales_s, b.hp, b.ws, b.status)
+        ob.onebit_lamb_rescale_update(b.table, b.bits_s, b.scales_s, b.x, b.m, b.v, b.c_avg,
+                                      b.f_prev, b.c_out, b.hp, b.ws, b.status)
+    for k in ("x", "m", "vf", "err_s", "bits_s", "scales_s", "f_prev", "c_out"):
+        assert torch.equal(getattr(a, k), getattr(b, k)), k
+
+
+def test_worker_packed_outputs_optional():
+    """NULL worker sign/scale arrays skip those stores and change nothing else."""
+    wl = _ragged_workload(RAGGED[3], 2)
+    a, b = DevRun(wl), DevRun(wl, store_worker_bits=False)
+    a.compressed_step(0)
+    b.compressed_step(0)
+    for k in ("x", "m", "vf", "err_s", "bits_s", "scales_s"):
+        assert torch.equal(getattr(a, k), getattr(b, k)), k

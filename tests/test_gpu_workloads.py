@@ -1,0 +1,101 @@
+"""GPU parity on the full-size workloads.
+
+The GPU runs the whole table; the oracle runs windows of it that start on a
+chunk boundary (chunk-local state is exact there; per-tensor values are
+compared for the tensors wholly inside a window).  Inputs of both sides come
+from the same seeded generator (device fill on the GPU, host fill for the
+oracle, bit-identical by construction and by test_synth_device_matches_host).
+"""
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("no GPU", allow_module_level=True)
+
+from synth.workloads import WORKLOADS  # noqa: E402
+
+from tests.harness import DevRun, HostRun, assert_parity, compare_state  # noqa: E402
+
+
+def block_windows(wl, chunks=120):
+    """Windows of `chunks` chunks around the small tensors (bias, LayerNorm)
+    of the first and of the last encoder block (the latter reaching the
+    ragged last chunk), plus the first chunks."""
+    C, K = wl.chunk, wl.K
+    off = wl.offsets
+    first_block = 1 if wl.L % 16 == 1 else 0   # an embedding precedes the blocks
+    i_bo = first_block + 7          # Wo bias of the first block
+    i_b2 = wl.L - 3                 # b2 of the last block
+    wins = [(0, min(K, 64))]
+    for i in (i_bo, i_b2):
+        k = int(off[i]) // C
+        lo = max(0, k - chunks // 2)
+        wins.append((lo, min(K, lo + chunks)))
+    return [(lo * C, min(wl.N, hi * C)) for lo, hi in sorted(set(wins))]
+
+
+def test_bert_large_step():
+    """BERT-Large table, W = 8: two compression steps, windows checked."""
+    wl = WORKLOADS["bert_large"]
+    d = DevRun(wl)
+    hosts = [HostRun(wl, lo, hi) for lo, hi in block_windows(wl)]
+    for step in range(2):
+        d.compressed_step(step)
+        torch.cuda.synchronize()
+        for h in hosts:
+            h.compressed_step(step)
+            assert_parity(compare_state(d, h), f"step {step} window [{h.lo}, {h.hi})")
+    assert int(d.status.item()) == 0
+
+
+def test_mixed_warmup_to_compression():
+    """BERT-Large table with per-tensor gradient scales: 20 LAMB warmup steps,
+    freeze, 20 compression steps, GPU and oracle each on their own state."""
+    wl = WORKLOADS["mixed"]
+    d = DevRun(wl)
+    hosts = [HostRun(wl, lo, hi) for lo, hi in block_windows(wl, chunks=64)]
+    step = 0
+    for _ in range(wl.warmup_steps):
+        d.warmup_step(step)
+        for h in hosts:
+            h.warmup_step(step)
+        step += 1
+    torch.cuda.synchronize()
+    for h in hosts:
+        assert_parity(compare_state(d, h, stage="warmup"), f"after warmup, window [{h.lo}, {h.hi})")
+    d.freeze(wl.warmup_steps)
+    for h in hosts:
+        h.freeze(wl.warmup_steps)
+    for _ in range(wl.compression_steps):
+        d.compressed_step(step)
+        for h in hosts:
+            h.compressed_step(step)
+        step += 1
+    torch.cuda.synchronize()
+    for h in hosts:
+        assert_parity(compare_state(d, h), f"after compression, window [{h.lo}, {h.hi})")
+    assert int(d.status.item()) == 0
+
+
+def test_bert_xl_step():
+    """BERT-XL table (2.83e9 parameters, W = 4, about 150 GB of state): one
+    compression step, windows checked."""
+    torch.cuda.empty_cache()
+    wl = WORKLOADS["bert_xl"]
+    free, _ = torch.cuda.mem_get_info()
+    need = wl.N * 4 * (5 + 2 * wl.W) * 1.02
+    if free < need:
+        pytest.skip(f"needs {need / 2**30:.0f} GiB of device memory, {free / 2**30:.0f} free")
+    d = DevRun(wl, store_worker_bits=False)
+    d.compressed_step(0)
+    torch.cuda.synchronize()
+    for lo, hi in block_windows(wl, chunks=64):
+        h = HostRun(wl, lo, hi)
+        h.compressed_step(0)
+        rep = compare_state(d, h)
+        assert_parity(rep, f"window [{lo}, {hi})")
+    assert int(d.status.item()) == 0
+    del d
+    torch.cuda.empty_cache()
