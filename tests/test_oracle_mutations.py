@@ -1,0 +1,72 @@
+"""The pins must catch a plausible mistake anywhere in the oracle.
+
+Each case plants one mistake in a copy of oracle.c (on the CPU only),
+builds it, and runs the pin tests against the broken build in a fresh
+process: at least one pin has to fail.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "oracle.c")
+
+MUTATIONS = {
+    "scale_without_sqrt_n": ("return sqrtf(t[0]) / sqrtf((float)n);", "return sqrtf(t[0]);"),
+    "scale_counts_padding": ("return sqrtf(t[0]) / sqrtf((float)n);",
+                             "return sqrtf(t[0]) / sqrtf((float)C);"),
+    "adjacent_pair_tree": ("for (int64_t j = 0; j < h; ++j) t[j] = t[j] + t[j + h];",
+                           "for (int64_t j = 0; j < h; ++j) t[j] = t[2 * j] + t[2 * j + 1];"),
+    "sign_strict": ("const int bit = z[j] >= 0.0f;", "const int bit = z[j] > 0.0f;"),
+    "error_sign_flipped": ("z[j] = bit ? z[j] - s : z[j] + s;", "z[j] = bit ? z[j] + s : z[j] - s;"),
+    "msb_first_bits": ("words[j / 32] |= 1u << (j % 32);",
+                       "words[j / 32] |= 0x80000000u >> (j % 32);"),
+    "no_error_feedback": ("z[j] = in[base + j] + err[base + j];", "z[j] = in[base + j];"),
+    "sum_not_mean": ("a[base + j] = acc / (float)W;", "a[base + j] = acc;"),
+    "no_server_error": ("for (int64_t i = 0; i < n; ++i) y[i] = y[i] + err_s[i];", ""),
+    "betas_transposed": ("in[i] = (hp->beta1 * m[i]) + (a1 * grads[w][i]);",
+                         "in[i] = (a1 * m[i]) + (hp->beta1 * grads[w][i]);"),
+    "ghat_without_beta1": ("const float ghat = (mhat[i] - (hp->beta1 * m[i])) / a1;",
+                           "const float ghat = (mhat[i] - m[i]) / a1;"),
+    "vfresh_linear": ("v_fresh[i] = (hp->beta2 * v_fresh[i]) + (a2 * (ghat * ghat));",
+                      "v_fresh[i] = (hp->beta2 * v_fresh[i]) + (a2 * ghat);"),
+    "ratio_inverted": ("const float q = (sqrtf(v_frozen[i]) + hp->eta) / (sqrtf(v_fresh[i]) + hp->eta);",
+                       "const float q = (sqrtf(v_fresh[i]) + hp->eta) / (sqrtf(v_frozen[i]) + hp->eta);"),
+    "no_relative_cap": ("float f = fminf(fminf(rho[l], hp->f_max), kp * f_prev[l]);",
+                        "float f = fminf(rho[l], hp->f_max);"),
+    "no_relative_floor": ("f = fmaxf(fmaxf(f, hp->f_min), km * f_prev[l]);",
+                          "f = fmaxf(f, hp->f_min);"),
+    "update_uses_fresh_variance": ("x[i] = x[i] - (step * (mhat[i] / (sqrtf(v_frozen[i]) + hp->eta)));",
+                                   "x[i] = x[i] - (step * (mhat[i] / (sqrtf(v_fresh[i]) + hp->eta)));"),
+    "trust_ratio_inverted": ("(float)(sqrt(X) / sqrt(U))", "(float)(sqrt(U) / sqrt(X))"),
+    "no_clip": ("c[l] = fminf(fmaxf(r, hp->c_min), hp->c_max);", "c[l] = r;"),
+    "variance_linear": ("v[i] = (hp->beta2 * v[i]) + (a2 * (gbar * gbar));",
+                        "v[i] = (hp->beta2 * v[i]) + (a2 * gbar);"),
+    "gradient_sum_not_mean": ("const float gbar = gsum / (float)W;", "const float gbar = gsum;"),
+    "freeze_keeps_errors": ("for (int64_t i = 0; i < N; ++i) err_s[i] = 0.0f;", ""),
+}
+
+
+@pytest.fixture(scope="module")
+def source():
+    return open(SRC).read()
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_mutation(name, source, tmp_path):
+    old, new = MUTATIONS[name]
+    assert source.count(old) == 1, f"mutation anchor not unique: {old!r}"
+    mutated = source.replace(old, new)
+    src = tmp_path / "oracle.c"
+    src.write_text(mutated)
+    lib = tmp_path / "liboracle_mut.so"
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+                    "-I", os.path.join(ROOT, "oracle"), "-o", str(lib), str(src), "-lm"],
+                   check=True, capture_output=True)
+    env = dict(os.environ, ONEBIT_ORACLE_LIB=str(lib))
+    res = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                          os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                         cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
+    assert res.returncode == 1, f"no pin failed for mutation {name}:\n{res.stdout[-2000:]}"

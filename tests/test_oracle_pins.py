@@ -468,3 +468,25 @@ def test_p13_determinism_and_freeze():
         outs.append((x, m, vf, err_s, out["bits_s"], out["scales_s"], out["c"]))
     for a, b in zip(*outs):
         assert np.array_equal(a, b)
+
+
+def test_p4_server_error_feedback():
+    # The server's packed output plus its new error equals the average plus
+    # its previous error (the server compensates its own compression error).
+    n, C, W = 4096 * 2 + 300, 4096, 3
+    r = rng(22)
+    bits_w, scales_w = [], []
+    for _ in range(W):
+        b, s = oracle.compress_ef(f32(r.standard_normal(n)), np.zeros(n, np.float32), C)
+        bits_w.append(b)
+        scales_w.append(s)
+    e_in = f32(r.standard_normal(n) * 0.1)
+    e_out = e_in.copy()
+    b2, s2 = oracle.average_packed(bits_w, scales_w, e_out, C)
+    a = oracle.average(bits_w, scales_w, n, C).astype(np.float64)
+    lhs = oracle.decompress(b2, s2, n, C).astype(np.float64) + e_out
+    rhs = a + e_in
+    # rounding of y = a + e_in to fp32, and of the new error
+    bound = np.spacing(np.abs(rhs).astype(np.float32)) + np.spacing(np.abs(e_out))
+    assert np.all(np.abs(lhs - rhs) <= bound)
+    assert np.max(np.abs(e_out)) > 0
