@@ -76,7 +76,20 @@ def main():
     ap.add_argument("--workload", default="bert_large")
     ap.add_argument("--cpu-chunks", type=int, default=12288,
                     help="chunks of the workload the CPU oracle baseline runs (0 = skip)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain device copy of 2^28 floats (1 GiB) three times, the "
+                         "reference for scaling HBM byte counters")
     args = ap.parse_args()
+
+    if args.calibrate_copy:
+        import torch
+        a = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log("[bench] copied 3 x 1 GiB")
+        return
 
     if args.gpus != 1:
         log(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the W workers are "
@@ -166,17 +179,7 @@ def main():
     abytes = phase1_bytes(N, K, C, W)
     achieved = abytes / (p1_ms * 1e-3) / 1e9
     step_gbps = sbytes / (ms_per_step * 1e-3) / 1e9
-    traffic = None
-    prof = os.path.join(ROOT, "profiles", "traffic_compress_average_bert_large.json")
-    if os.path.exists(prof):
-        try:
-            with open(prof) as fh:
-                t = json.load(fh)
-            if t.get("kernel_source_sha") == _kernel_sha():
-                traffic = t.get("bytes_per_launch")
-        except Exception:
-            traffic = None
-
+    traffic = _measured_traffic()
     cpu = None
     if args.cpu_chunks > 0:
         log("[bench] CPU oracle baseline ...")
@@ -220,6 +223,26 @@ def _kernel_sha():
         with open(os.path.join(ROOT, p), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+def _measured_traffic():
+    """HBM bytes per phase-1 launch from the committed counter summary, or
+    None if the kernels changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic_compress_average_bert_large.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as fh:
+        for ln in fh:
+            if ":" in ln and not ln.startswith("#"):
+                k, v = ln.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha") != _kernel_sha():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 if __name__ == "__main__":

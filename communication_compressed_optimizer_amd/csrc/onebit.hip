@@ -142,30 +142,49 @@ void by_chunk(int32_t chunk, A&&... a) {
   }
 }
 
+// Launch kfull over the full chunks of an n-element buffer and ktail over
+// its partial last chunk (if any); both take the index of their first chunk
+// as the first argument.
+template <int C, typename KF, typename KT, typename... A>
+void launch_chunks(int64_t n, hipStream_t st, KF kfull, KT ktail, A... args) {
+  const int64_t Kf = n / C;
+  const int64_t K = (n + C - 1) / C;
+  if (Kf > 0) hipLaunchKernelGGL(kfull, dim3((unsigned)Kf), dim3(C / 16), 0, st, (int64_t)0, args...);
+  if (K > Kf) hipLaunchKernelGGL(ktail, dim3(1), dim3(C / 16), 0, st, Kf, args...);
+}
+
+// Tuning of the compression-step kernels, measured on MI355X at the
+// BERT-Large table with W = 8 (phase 1: 7.67 ms plain, 7.39 ms streaming,
+// 7.15-7.25 ms streaming at 6 waves per SIMD; prefetching the next worker
+// costs more registers than the latency it hides).
+constexpr bool kPassA_NT = true;   // streaming loads and stores
+constexpr bool kPassA_PF = false;  // next-worker prefetch
+constexpr int kPassA_WPE = 6;      // minimum waves per SIMD
+constexpr bool kPassB_NT = true;
+
 template <int C>
 struct LaunchCompress {
-  static void run(int64_t n, int64_t K, const float* in, float* err, uint32_t* bits, float* scales,
+  static void run(int64_t n, const float* in, float* err, uint32_t* bits, float* scales,
                   int32_t* status, hipStream_t st) {
-    hipLaunchKernelGGL(k_compress_ef<C>, dim3((unsigned)K), dim3(C / 16), 0, st, n, in, err, bits,
-                       scales, status);
+    launch_chunks<C>(n, st, k_compress_ef<C, false>, k_compress_ef<C, true>, n, in, err, bits,
+                     scales, status);
   }
 };
 
 template <int C>
 struct LaunchAverage {
-  static void run(int64_t n, int64_t K, int W, const PackedIn& pin, float* err_s, uint32_t* bits,
+  static void run(int64_t n, int W, const PackedIn& pin, float* err_s, uint32_t* bits,
                   float* scales, int32_t* status, hipStream_t st) {
-    hipLaunchKernelGGL(k_average_packed<C>, dim3((unsigned)K), dim3(C / 16), 0, st, n, W, pin,
-                       err_s, bits, scales, status);
+    launch_chunks<C>(n, st, k_average_packed<C, false>, k_average_packed<C, true>, n, W, pin,
+                     err_s, bits, scales, status);
   }
 };
 
 template <int C>
 struct LaunchDecompress {
-  static void run(int64_t n, int64_t K, const uint32_t* bits, const float* scales, float* out,
+  static void run(int64_t n, const uint32_t* bits, const float* scales, float* out,
                   hipStream_t st) {
-    hipLaunchKernelGGL(k_decompress<C>, dim3((unsigned)K), dim3(C / 16), 0, st, n, bits, scales,
-                       out);
+    launch_chunks<C>(n, st, k_decompress<C, false>, k_decompress<C, true>, n, bits, scales, out);
   }
 };
 
@@ -174,12 +193,12 @@ struct LaunchWarmup {
   static void run(const onebit_layer_table* t, int W, const Workers& wk, float* x, float* m,
                   float* v, float* c_sum, float* c_out, const Coef& cf, const Ws& ws,
                   int32_t* status, hipStream_t st) {
-    hipLaunchKernelGGL(k_warmup_pass1<C>, dim3((unsigned)t->K), dim3(C / 16), 0, st, t->dev, W, wk,
-                       x, m, v, ws.seg_x, ws.seg_u, cf);
+    launch_chunks<C>(t->N, st, k_warmup_pass1<C, false>, k_warmup_pass1<C, true>, t->dev, W, wk,
+                     (const float*)x, m, v, ws.seg_x, ws.seg_u, cf);
     hipLaunchKernelGGL(k_warmup_finalize<256>, dim3((unsigned)t->L), dim3(256), 0, st, t->dev,
                        ws.seg_x, ws.seg_u, c_sum, ws.c_layer, c_out, cf, status);
-    hipLaunchKernelGGL(k_warmup_pass2<C>, dim3((unsigned)t->K), dim3(C / 16), 0, st, t->dev, m, v,
-                       x, ws.c_layer, cf);
+    launch_chunks<C>(t->N, st, k_warmup_pass2<C, false>, k_warmup_pass2<C, true>, t->dev,
+                     (const float*)m, (const float*)v, x, (const float*)ws.c_layer, cf);
   }
 };
 
@@ -187,8 +206,8 @@ template <int C>
 struct LaunchFreeze {
   static void run(const onebit_layer_table* t, int W, const float* v, float* v_fresh,
                   const Workers& wk, float* err_s, hipStream_t st) {
-    hipLaunchKernelGGL(k_freeze_elems<C>, dim3((unsigned)t->K), dim3(C / 16), 0, st, t->N, W, v,
-                       v_fresh, wk, err_s);
+    launch_chunks<C>(t->N, st, k_freeze_elems<C, false>, k_freeze_elems<C, true>, t->N, W, v,
+                     v_fresh, wk, err_s);
   }
 };
 
@@ -197,8 +216,9 @@ struct LaunchPassA {
   static void run(const onebit_layer_table* t, int W, const Workers& wk, float* err_s,
                   const float* m, const float* v_frozen, float* v_fresh, uint32_t* bits_s,
                   float* scales_s, const Coef& cf, const Ws& ws, int32_t* status, hipStream_t st) {
-    hipLaunchKernelGGL(k_compressed_pass_a<C>, dim3((unsigned)t->K), dim3(C / 16), 0, st, t->dev, W,
-                       wk, err_s, m, v_frozen, v_fresh, bits_s, scales_s, ws.seg_max, cf, status);
+    launch_chunks<C>(t->N, st, k_compressed_pass_a<C, false, kPassA_NT, kPassA_PF, kPassA_WPE>,
+                     k_compressed_pass_a<C, true, kPassA_NT, kPassA_PF, kPassA_WPE>, t->dev, W, wk,
+                     err_s, m, v_frozen, v_fresh, bits_s, scales_s, ws.seg_max, cf, status);
   }
 };
 
@@ -208,9 +228,10 @@ struct LaunchPassB {
                   float* x, float* m, const float* v_frozen, const float* c_avg, float* f_prev,
                   float* c_out, const Coef& cf, const Ws& ws, int32_t* status, hipStream_t st) {
     hipLaunchKernelGGL(k_rescale_finalize<256>, dim3((unsigned)t->L), dim3(256), 0, st, t->dev,
-                       ws.seg_max, c_avg, f_prev, ws.c_layer, c_out, cf, status);
-    hipLaunchKernelGGL(k_compressed_pass_b<C>, dim3((unsigned)t->K), dim3(C / 16), 0, st, t->dev,
-                       bits_s, scales_s, v_frozen, x, m, ws.c_layer, cf);
+                       (const float*)ws.seg_max, c_avg, f_prev, ws.c_layer, c_out, cf, status);
+    launch_chunks<C>(t->N, st, k_compressed_pass_b<C, false, kPassB_NT>,
+                     k_compressed_pass_b<C, true, kPassB_NT>, t->dev, bits_s, scales_s, v_frozen, x,
+                     m, (const float*)ws.c_layer, cf);
   }
 };
 
@@ -395,8 +416,7 @@ int onebit_compress_ef(int64_t n, int32_t chunk, const float* in, float* err, ui
   CHECK_PTR(err, "err");
   CHECK_PTR(bits, "bits");
   CHECK_PTR(scales, "scales");
-  const int64_t K = (n + chunk - 1) / chunk;
-  by_chunk<LaunchCompress>(chunk, n, K, in, err, bits, scales, status, (hipStream_t)stream);
+  by_chunk<LaunchCompress>(chunk, n, in, err, bits, scales, status, (hipStream_t)stream);
   return launch_status(__func__);
 }
 
@@ -418,8 +438,7 @@ int onebit_average_packed(int64_t n, int32_t chunk, int32_t W, const uint32_t* c
   CHECK_PTR(err_s, "err_s");
   CHECK_PTR(bits_out, "bits_out");
   CHECK_PTR(scales_out, "scales_out");
-  const int64_t K = (n + chunk - 1) / chunk;
-  by_chunk<LaunchAverage>(chunk, n, K, (int)W, pin, err_s, bits_out, scales_out, status,
+  by_chunk<LaunchAverage>(chunk, n, (int)W, pin, err_s, bits_out, scales_out, status,
                           (hipStream_t)stream);
   return launch_status(__func__);
 }
@@ -432,8 +451,7 @@ int onebit_decompress(int64_t n, int32_t chunk, const uint32_t* bits, const floa
   CHECK_PTR(bits, "bits");
   CHECK_PTR(scales, "scales");
   CHECK_PTR(out, "out");
-  const int64_t K = (n + chunk - 1) / chunk;
-  by_chunk<LaunchDecompress>(chunk, n, K, bits, scales, out, (hipStream_t)stream);
+  by_chunk<LaunchDecompress>(chunk, n, bits, scales, out, (hipStream_t)stream);
   return launch_status(__func__);
 }
 

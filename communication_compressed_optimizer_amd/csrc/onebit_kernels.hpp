@@ -76,19 +76,52 @@ struct Geo {
 
 using Slots = float[4][4];  // [slot k][component c]
 
+// Chunk of this workgroup.  Every chunk kernel is instantiated twice: for the
+// full chunks (TAIL = false: nk == C at compile time, no guards) and for the
+// one partial last chunk (TAIL = true), launched separately.
+template <int C, bool TAIL>
+struct ChunkAt {
+  int64_t k, base;
+  int nk;
+  __device__ __forceinline__ ChunkAt(int64_t k0, int64_t n) {
+    k = k0 + (int64_t)blockIdx.x;
+    base = k * C;
+    nk = TAIL ? (int)(n - base) : C;
+  }
+};
+
 // ---------------------------------------------------------------------------
 // loads and stores of a chunk in the slot layout
 // ---------------------------------------------------------------------------
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Streaming (nontemporal) or plain 16-byte accesses.
+template <bool NT>
+__device__ __forceinline__ f32x4 ld4(const float* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+  else return *reinterpret_cast<const f32x4*>(p);
+}
+
+template <bool NT>
+__device__ __forceinline__ void st4(float* p, f32x4 v) {
+  if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
+  else *reinterpret_cast<f32x4*>(p) = v;
+}
+
 template <int C>
+__device__ __forceinline__ bool slot_valid(int k, int c, int nk) {
+  return 4 * ((int)threadIdx.x + Geo<C>::T * k) + c < nk;
+}
+
+template <int C, bool TAIL, bool NT = false>
 __device__ __forceinline__ void load_chunk(const float* __restrict__ p, int64_t base, int nk,
                                            Slots& o) {
   constexpr int T = Geo<C>::T;
   const int t = threadIdx.x;
-  if (nk == C) {
-    const float4* q = reinterpret_cast<const float4*>(p + base);
+  if constexpr (!TAIL) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const float4 v = q[t + T * k];
+      const f32x4 v = ld4<NT>(p + base + 4 * (t + T * k));
       o[k][0] = v.x;
       o[k][1] = v.y;
       o[k][2] = v.z;
@@ -98,30 +131,27 @@ __device__ __forceinline__ void load_chunk(const float* __restrict__ p, int64_t 
 #pragma unroll
     for (int k = 0; k < 4; ++k)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int j = 4 * (t + T * k) + c;
-        o[k][c] = j < nk ? p[base + j] : 0.0f;
-      }
+      for (int c = 0; c < 4; ++c) o[k][c] = slot_valid<C>(k, c, nk) ? p[base + 4 * (t + T * k) + c] : 0.0f;
   }
 }
 
-template <int C>
+template <int C, bool TAIL, bool NT = false>
 __device__ __forceinline__ void store_chunk(float* __restrict__ p, int64_t base, int nk,
                                             const Slots& o) {
   constexpr int T = Geo<C>::T;
   const int t = threadIdx.x;
-  if (nk == C) {
-    float4* q = reinterpret_cast<float4*>(p + base);
+  if constexpr (!TAIL) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) q[t + T * k] = make_float4(o[k][0], o[k][1], o[k][2], o[k][3]);
+    for (int k = 0; k < 4; ++k) {
+      const f32x4 v = {o[k][0], o[k][1], o[k][2], o[k][3]};
+      st4<NT>(p + base + 4 * (t + T * k), v);
+    }
   } else {
 #pragma unroll
     for (int k = 0; k < 4; ++k)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int j = 4 * (t + T * k) + c;
-        if (j < nk) p[base + j] = o[k][c];
-      }
+      for (int c = 0; c < 4; ++c)
+        if (slot_valid<C>(k, c, nk)) p[base + 4 * (t + T * k) + c] = o[k][c];
   }
 }
 
@@ -212,19 +242,17 @@ __device__ __forceinline__ void load_sign_nibbles(const uint32_t* __restrict__ w
   for (int k = 0; k < 4; ++k) nib[k] = (words[(t + T * k) >> 3] >> (4 * (t & 7))) & 0xFu;
 }
 
-template <int C>
-__device__ __forceinline__ bool slot_valid(int k, int c, int nk) {
-  return 4 * ((int)threadIdx.x + Geo<C>::T * k) + c < nk;
+__device__ __forceinline__ float signed_scale(const uint32_t (&nib)[4], int k, int c, float s) {
+  return ((nib[k] >> c) & 1u) ? s : -s;
 }
 
 // Error-compensated 1-bit compression of z in place (z becomes the error):
-// returns s; nib receives the sign nibbles; sgn[k][c] = +-s.
-// Slots past the last valid element are cleared first (they count as 0 in
-// the chunk sum and their bits are 0).
-template <int C>
+// returns the chunk scale s; nib receives the sign nibbles (0 past the last
+// valid element, whose slots are cleared first so they count as 0).
+template <int C, bool TAIL>
 __device__ __forceinline__ float compress_slots(Slots& z, int nk, float4* lds, int& parity,
-                                                uint32_t (&nib)[4], Slots& sgn) {
-  if (nk != C) {
+                                                uint32_t (&nib)[4]) {
+  if constexpr (TAIL) {
 #pragma unroll
     for (int k = 0; k < 4; ++k)
 #pragma unroll
@@ -238,9 +266,8 @@ __device__ __forceinline__ float compress_slots(Slots& z, int nk, float4* lds, i
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const bool b = z[k][c] >= 0.0f;
-      nb |= (uint32_t)(b && slot_valid<C>(k, c, nk)) << c;
+      nb |= (uint32_t)(b && (!TAIL || slot_valid<C>(k, c, nk))) << c;
       z[k][c] = b ? z[k][c] - s : z[k][c] + s;
-      sgn[k][c] = b ? s : -s;
     }
     nib[k] = nb;
   }
@@ -302,178 +329,11 @@ __device__ __forceinline__ int tensor_of(const DevTable& tab, int l0, int l1, in
   return l;
 }
 
-// ===========================================================================
-// kernels
-// ===========================================================================
-
-// onebit_compress_ef: z = in + err -> bits, scales, err
+// Per-(chunk, tensor) maximum of q over the chunk's valid elements.
 template <int C>
-__global__ void __launch_bounds__(C / 16)
-k_compress_ef(int64_t n, const float* __restrict__ in, float* __restrict__ err,
-              uint32_t* __restrict__ bits, float* __restrict__ scales, int32_t* status) {
-  __shared__ float4 lds[2 * Geo<C>::T];
-  int parity = 0;
-  const int64_t k = blockIdx.x;
-  const int64_t base = k * C;
-  const int nk = (int)min((int64_t)C, n - base);
-  Slots z, e;
-  load_chunk<C>(in, base, nk, z);
-  load_chunk<C>(err, base, nk, e);
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) z[a][c] = z[a][c] + e[a][c];
-  uint32_t nib[4];
-  Slots sgn;
-  const float s = compress_slots<C>(z, nk, lds, parity, nib, sgn);
-  store_chunk<C>(err, base, nk, z);
-  store_sign_words<C>(bits + k * Geo<C>::WORDS, nib);
-  if (threadIdx.x == 0) {
-    scales[k] = s;
-    if (!__builtin_isfinite(s)) flag(status, 1);
-  }
-}
-
-// onebit_average_packed: y = mean of the workers' +-s, + err_s -> recompress
-template <int C>
-__global__ void __launch_bounds__(C / 16)
-k_average_packed(int64_t n, int W, PackedIn pin, float* __restrict__ err_s,
-                 uint32_t* __restrict__ bits_out, float* __restrict__ scales_out, int32_t* status) {
-  __shared__ float4 lds[2 * Geo<C>::T];
-  int parity = 0;
-  const int64_t k = blockIdx.x;
-  const int64_t base = k * C;
-  const int nk = (int)min((int64_t)C, n - base);
-  Slots acc, y;
-  for (int w = 0; w < W; ++w) {
-    const float s = pin.scales[w][k];
-    uint32_t nib[4];
-    load_sign_nibbles<C>(pin.bits[w] + k * Geo<C>::WORDS, nib);
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const float v = ((nib[a] >> c) & 1u) ? s : -s;
-        acc[a][c] = w == 0 ? v : acc[a][c] + v;
-      }
-  }
-  load_chunk<C>(err_s, base, nk, y);
-  const float fW = (float)W;
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) y[a][c] = (acc[a][c] / fW) + y[a][c];
-  uint32_t nib[4];
-  Slots sgn;
-  const float s = compress_slots<C>(y, nk, lds, parity, nib, sgn);
-  store_chunk<C>(err_s, base, nk, y);
-  store_sign_words<C>(bits_out + k * Geo<C>::WORDS, nib);
-  if (threadIdx.x == 0) {
-    scales_out[k] = s;
-    if (!__builtin_isfinite(s)) flag(status, 2);
-  }
-}
-
-// onebit_decompress
-template <int C>
-__global__ void __launch_bounds__(C / 16)
-k_decompress(int64_t n, const uint32_t* __restrict__ bits, const float* __restrict__ scales,
-             float* __restrict__ out) {
-  const int64_t k = blockIdx.x;
-  const int64_t base = k * C;
-  const int nk = (int)min((int64_t)C, n - base);
-  const float s = scales[k];
-  uint32_t nib[4];
-  load_sign_nibbles<C>(bits + k * Geo<C>::WORDS, nib);
-  Slots o;
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) o[a][c] = ((nib[a] >> c) & 1u) ? s : -s;
-  store_chunk<C>(out, base, nk, o);
-}
-
-// Compression step, pass A: every worker's momentum compression, the server
-// average and recompression, the reconstructed gradient, the fresh variance
-// and the per-(chunk, tensor) maximum of the rescale ratio.
-template <int C>
-__global__ void __launch_bounds__(C / 16)
-k_compressed_pass_a(DevTable tab, int W, Workers wk, float* __restrict__ err_s,
-                    const float* __restrict__ m, const float* __restrict__ v_frozen,
-                    float* __restrict__ v_fresh, uint32_t* __restrict__ bits_s,
-                    float* __restrict__ scales_s, float* __restrict__ seg_max, Coef cf,
-                    int32_t* status) {
+__device__ __forceinline__ void segment_max(const DevTable& tab, int64_t k, int64_t base, int nk,
+                                            const Slots& q, float* red, float* __restrict__ seg_max) {
   constexpr int T = Geo<C>::T;
-  __shared__ float4 lds[2 * T];
-  __shared__ float red[T / 64];
-  int parity = 0;
-  const int64_t k = blockIdx.x;
-  const int64_t base = k * C;
-  const int nk = (int)min((int64_t)C, tab.N - base);
-
-  Slots bm, acc;
-  load_chunk<C>(m, base, nk, bm);
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) bm[a][c] = cf.beta1 * bm[a][c];
-
-  for (int w = 0; w < W; ++w) {
-    Slots z, e;
-    load_chunk<C>(wk.g[w], base, nk, z);
-    load_chunk<C>(wk.e[w], base, nk, e);
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) z[a][c] = (bm[a][c] + (cf.a1 * z[a][c])) + e[a][c];
-    uint32_t nib[4];
-    Slots sgn;
-    const float s = compress_slots<C>(z, nk, lds, parity, nib, sgn);
-    store_chunk<C>(wk.e[w], base, nk, z);
-    if (wk.bits[w]) store_sign_words<C>(wk.bits[w] + k * Geo<C>::WORDS, nib);
-    if (threadIdx.x == 0) {
-      if (wk.scales[w]) wk.scales[w][k] = s;
-      if (!__builtin_isfinite(s)) flag(status, 1);
-    }
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) acc[a][c] = w == 0 ? sgn[a][c] : acc[a][c] + sgn[a][c];
-  }
-
-  // server: average, add its error, recompress
-  Slots y;
-  load_chunk<C>(err_s, base, nk, y);
-  const float fW = (float)W;
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) y[a][c] = (acc[a][c] / fW) + y[a][c];
-  uint32_t nib[4];
-  Slots mhat;
-  const float s2 = compress_slots<C>(y, nk, lds, parity, nib, mhat);
-  store_chunk<C>(err_s, base, nk, y);
-  store_sign_words<C>(bits_s + k * Geo<C>::WORDS, nib);
-  if (threadIdx.x == 0) {
-    scales_s[k] = s2;
-    if (!__builtin_isfinite(s2)) flag(status, 2);
-  }
-
-  // reconstructed gradient, fresh variance, rescale ratio
-  Slots vf, vz;
-  load_chunk<C>(v_fresh, base, nk, vf);
-  load_chunk<C>(v_frozen, base, nk, vz);
-  Slots q;
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const float gh = (mhat[a][c] - bm[a][c]) / cf.a1;
-      vf[a][c] = (cf.beta2 * vf[a][c]) + (cf.a2 * (gh * gh));
-      q[a][c] = (__builtin_sqrtf(vz[a][c]) + cf.eta) / (__builtin_sqrtf(vf[a][c]) + cf.eta);
-    }
-  store_chunk<C>(v_fresh, base, nk, vf);
-
   const int l0 = tab.l0[k];
   const int l1 = tab.l1[k];
   const int sb = tab.seg[k];
@@ -491,6 +351,207 @@ k_compressed_pass_a(DevTable tab, int W, Workers wk, float* __restrict__ err_s,
     mx = block_max<T>(mx, red);
     if (threadIdx.x == 0) seg_max[sb + (l - l0)] = mx;
   }
+}
+
+// ===========================================================================
+// kernels (k0: index of the first chunk of the launch)
+// ===========================================================================
+
+// onebit_compress_ef: z = in + err -> bits, scales, err
+template <int C, bool TAIL>
+__global__ void __launch_bounds__(C / 16)
+k_compress_ef(int64_t k0, int64_t n, const float* __restrict__ in, float* __restrict__ err,
+              uint32_t* __restrict__ bits, float* __restrict__ scales, int32_t* status) {
+  __shared__ float4 lds[2 * Geo<C>::T];
+  int parity = 0;
+  const ChunkAt<C, TAIL> ch(k0, n);
+  Slots z, e;
+  load_chunk<C, TAIL>(in, ch.base, ch.nk, z);
+  load_chunk<C, TAIL>(err, ch.base, ch.nk, e);
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) z[a][c] = z[a][c] + e[a][c];
+  uint32_t nib[4];
+  const float s = compress_slots<C, TAIL>(z, ch.nk, lds, parity, nib);
+  store_chunk<C, TAIL>(err, ch.base, ch.nk, z);
+  store_sign_words<C>(bits + ch.k * Geo<C>::WORDS, nib);
+  if (threadIdx.x == 0) {
+    scales[ch.k] = s;
+    if (!__builtin_isfinite(s)) flag(status, 1);
+  }
+}
+
+// onebit_average_packed: y = mean of the workers' +-s, + err_s -> recompress
+template <int C, bool TAIL>
+__global__ void __launch_bounds__(C / 16)
+k_average_packed(int64_t k0, int64_t n, int W, PackedIn pin, float* __restrict__ err_s,
+                 uint32_t* __restrict__ bits_out, float* __restrict__ scales_out, int32_t* status) {
+  __shared__ float4 lds[2 * Geo<C>::T];
+  int parity = 0;
+  const ChunkAt<C, TAIL> ch(k0, n);
+  Slots acc, y;
+  for (int w = 0; w < W; ++w) {
+    const float s = pin.scales[w][ch.k];
+    uint32_t nib[4];
+    load_sign_nibbles<C>(pin.bits[w] + ch.k * Geo<C>::WORDS, nib);
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float v = signed_scale(nib, a, c, s);
+        acc[a][c] = w == 0 ? v : acc[a][c] + v;
+      }
+  }
+  load_chunk<C, TAIL>(err_s, ch.base, ch.nk, y);
+  const float fW = (float)W;
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) y[a][c] = (acc[a][c] / fW) + y[a][c];
+  uint32_t nib[4];
+  const float s = compress_slots<C, TAIL>(y, ch.nk, lds, parity, nib);
+  store_chunk<C, TAIL>(err_s, ch.base, ch.nk, y);
+  store_sign_words<C>(bits_out + ch.k * Geo<C>::WORDS, nib);
+  if (threadIdx.x == 0) {
+    scales_out[ch.k] = s;
+    if (!__builtin_isfinite(s)) flag(status, 2);
+  }
+}
+
+// onebit_decompress
+template <int C, bool TAIL>
+__global__ void __launch_bounds__(C / 16)
+k_decompress(int64_t k0, int64_t n, const uint32_t* __restrict__ bits,
+             const float* __restrict__ scales, float* __restrict__ out) {
+  const ChunkAt<C, TAIL> ch(k0, n);
+  const float s = scales[ch.k];
+  uint32_t nib[4];
+  load_sign_nibbles<C>(bits + ch.k * Geo<C>::WORDS, nib);
+  Slots o;
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) o[a][c] = signed_scale(nib, a, c, s);
+  store_chunk<C, TAIL>(out, ch.base, ch.nk, o);
+}
+
+// Compression step, pass A: every worker's momentum compression, the server
+// average and recompression, the reconstructed gradient, the fresh variance
+// and the per-(chunk, tensor) maximum of the rescale ratio.
+//
+// The worker loop carries beta1*m, the running sum ((+-s_0 + +-s_1) + ...)
+// of the workers' decompressed values (worker order), and the current
+// worker's values.  The kernel is HBM-bound; occupancy (WPE) is what moves it.
+//   NT:  streaming (nontemporal) loads and stores for the element arrays.
+//   PF:  worker w+1's gradient and error are loaded before worker w's chunk
+//        reduction, so they are in flight across its barrier.
+//   WPE: minimum waves per SIMD the register allocation must allow.
+template <int C, bool TAIL, bool NT = false, bool PF = false, int WPE = 1>
+__global__ void __launch_bounds__(C / 16, WPE)
+k_compressed_pass_a(int64_t k0, DevTable tab, int W, Workers wk, float* __restrict__ err_s,
+                    const float* __restrict__ m, const float* __restrict__ v_frozen,
+                    float* __restrict__ v_fresh, uint32_t* __restrict__ bits_s,
+                    float* __restrict__ scales_s, float* __restrict__ seg_max, Coef cf,
+                    int32_t* status) {
+  constexpr int T = Geo<C>::T;
+  __shared__ float4 lds[2 * T];
+  __shared__ float red[T / 64];
+  int parity = 0;
+  const ChunkAt<C, TAIL> ch(k0, tab.N);
+  const int64_t base = ch.base;
+  const int nk = ch.nk;
+  const int t = threadIdx.x;
+
+  Slots bm, acc;
+  Slots gn, en;  // the next worker's gradient and error (PF)
+  if constexpr (PF) {
+    load_chunk<C, TAIL, NT>(wk.g[0], base, nk, gn);
+    load_chunk<C, TAIL, NT>(wk.e[0], base, nk, en);
+  }
+  load_chunk<C, TAIL, NT>(m, base, nk, bm);
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) bm[a][c] = cf.beta1 * bm[a][c];
+
+  for (int w = 0; w < W; ++w) {
+    Slots z, e;
+    if constexpr (PF) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          z[a][c] = gn[a][c];
+          e[a][c] = en[a][c];
+        }
+      if (w + 1 < W) {
+        load_chunk<C, TAIL, NT>(wk.g[w + 1], base, nk, gn);
+        load_chunk<C, TAIL, NT>(wk.e[w + 1], base, nk, en);
+      }
+    } else {
+      load_chunk<C, TAIL, NT>(wk.g[w], base, nk, z);
+      load_chunk<C, TAIL, NT>(wk.e[w], base, nk, e);
+    }
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) z[a][c] = (bm[a][c] + (cf.a1 * z[a][c])) + e[a][c];
+    uint32_t nib[4];
+    const float s = compress_slots<C, TAIL>(z, nk, lds, parity, nib);
+    store_chunk<C, TAIL, NT>(wk.e[w], base, nk, z);
+    if (wk.bits[w]) store_sign_words<C>(wk.bits[w] + ch.k * Geo<C>::WORDS, nib);
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float sv = signed_scale(nib, a, c, s);
+        acc[a][c] = w == 0 ? sv : acc[a][c] + sv;
+      }
+    if (t == 0) {
+      if (wk.scales[w]) wk.scales[w][ch.k] = s;
+      if (!__builtin_isfinite(s)) flag(status, 1);
+    }
+  }
+
+  // server: average of the workers' values, add its error, recompress
+  Slots y;
+  load_chunk<C, TAIL, NT>(err_s, base, nk, y);
+  const float fW = (float)W;
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) y[a][c] = (acc[a][c] / fW) + y[a][c];
+  Slots vf, vz;
+  if constexpr (PF) {  // in flight across the server's reduction
+    load_chunk<C, TAIL, NT>(v_fresh, base, nk, vf);
+    load_chunk<C, TAIL, NT>(v_frozen, base, nk, vz);
+  }
+  uint32_t nib[4];
+  const float s2 = compress_slots<C, TAIL>(y, nk, lds, parity, nib);
+  store_chunk<C, TAIL, NT>(err_s, base, nk, y);
+  store_sign_words<C>(bits_s + ch.k * Geo<C>::WORDS, nib);
+  if (t == 0) {
+    scales_s[ch.k] = s2;
+    if (!__builtin_isfinite(s2)) flag(status, 2);
+  }
+
+  // reconstructed gradient, fresh variance, rescale ratio
+  if constexpr (!PF) {
+    load_chunk<C, TAIL, NT>(v_fresh, base, nk, vf);
+    load_chunk<C, TAIL, NT>(v_frozen, base, nk, vz);
+  }
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float mh = signed_scale(nib, a, c, s2);
+      const float gh = (mh - bm[a][c]) / cf.a1;
+      vf[a][c] = (cf.beta2 * vf[a][c]) + (cf.a2 * (gh * gh));
+      vz[a][c] = (__builtin_sqrtf(vz[a][c]) + cf.eta) / (__builtin_sqrtf(vf[a][c]) + cf.eta);
+    }
+  store_chunk<C, TAIL, NT>(v_fresh, base, nk, vf);
+  segment_max<C>(tab, ch.k, base, nk, vz, red, seg_max);  // vz now holds the ratio q
 }
 
 // Per tensor: rho = max of its segments, soft thresholds, c.
@@ -518,67 +579,81 @@ k_rescale_finalize(DevTable tab, const float* __restrict__ seg_max, const float*
   }
 }
 
+// Per-element step size lr*c_l for the chunk's elements.
+template <int C, bool TAIL>
+__device__ __forceinline__ void step_sizes(const DevTable& tab, int64_t k, int64_t base,
+                                           const float* __restrict__ c_layer, float lr,
+                                           Slots& st) {
+  constexpr int T = Geo<C>::T;
+  const int l0 = tab.l0[k];
+  const int l1 = tab.l1[k];
+  const float s0 = lr * c_layer[l0];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) st[a][c] = s0;
+  if (l0 != l1) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int64_t gi = base + 4 * ((int)threadIdx.x + T * a) + c;
+        st[a][c] = lr * c_layer[tensor_of(tab, l0, l1, gi)];
+      }
+  }
+}
+
 // Compression step, pass B: x update with the per-tensor c, m = mhat.
-template <int C>
+template <int C, bool TAIL, bool NT = false>
 __global__ void __launch_bounds__(C / 16)
-k_compressed_pass_b(DevTable tab, const uint32_t* __restrict__ bits_s,
+k_compressed_pass_b(int64_t k0, DevTable tab, const uint32_t* __restrict__ bits_s,
                     const float* __restrict__ scales_s, const float* __restrict__ v_frozen,
                     float* __restrict__ x, float* __restrict__ m, const float* __restrict__ c_layer,
                     Coef cf) {
-  constexpr int T = Geo<C>::T;
-  const int64_t k = blockIdx.x;
-  const int64_t base = k * C;
-  const int nk = (int)min((int64_t)C, tab.N - base);
-  const float s = scales_s[k];
+  const ChunkAt<C, TAIL> ch(k0, tab.N);
+  const float s = scales_s[ch.k];
   uint32_t nib[4];
-  load_sign_nibbles<C>(bits_s + k * Geo<C>::WORDS, nib);
-  Slots vz, xx, mh;
-  load_chunk<C>(v_frozen, base, nk, vz);
-  load_chunk<C>(x, base, nk, xx);
-  const int l0 = tab.l0[k];
-  const int l1 = tab.l1[k];
-  const float step0 = cf.lr * c_layer[l0];
+  load_sign_nibbles<C>(bits_s + ch.k * Geo<C>::WORDS, nib);
+  Slots vz, xx, mh, st;
+  load_chunk<C, TAIL, NT>(v_frozen, ch.base, ch.nk, vz);
+  load_chunk<C, TAIL, NT>(x, ch.base, ch.nk, xx);
+  step_sizes<C, TAIL>(tab, ch.k, ch.base, c_layer, cf.lr, st);
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      float step = step0;
-      if (l0 != l1) {
-        const int64_t gi = base + 4 * ((int)threadIdx.x + T * a) + c;
-        step = cf.lr * c_layer[tensor_of(tab, l0, l1, gi)];
-      }
-      mh[a][c] = ((nib[a] >> c) & 1u) ? s : -s;
-      xx[a][c] = xx[a][c] - (step * (mh[a][c] / (__builtin_sqrtf(vz[a][c]) + cf.eta)));
+      mh[a][c] = signed_scale(nib, a, c, s);
+      xx[a][c] = xx[a][c] - (st[a][c] * (mh[a][c] / (__builtin_sqrtf(vz[a][c]) + cf.eta)));
     }
-  store_chunk<C>(x, base, nk, xx);
-  store_chunk<C>(m, base, nk, mh);
+  store_chunk<C, TAIL, NT>(x, ch.base, ch.nk, xx);
+  store_chunk<C, TAIL, NT>(m, ch.base, ch.nk, mh);
 }
 
 // Warmup pass 1: mean gradient, moments, per-(chunk, tensor) sums of x^2 and
 // u^2 in double.
-template <int C>
+template <int C, bool TAIL>
 __global__ void __launch_bounds__(C / 16)
-k_warmup_pass1(DevTable tab, int W, Workers wk, const float* __restrict__ x, float* __restrict__ m,
-               float* __restrict__ v, double* __restrict__ seg_x, double* __restrict__ seg_u,
-               Coef cf) {
+k_warmup_pass1(int64_t k0, DevTable tab, int W, Workers wk, const float* __restrict__ x,
+               float* __restrict__ m, float* __restrict__ v, double* __restrict__ seg_x,
+               double* __restrict__ seg_u, Coef cf) {
   constexpr int T = Geo<C>::T;
   __shared__ double red[2 * (T / 64)];
-  const int64_t k = blockIdx.x;
-  const int64_t base = k * C;
-  const int nk = (int)min((int64_t)C, tab.N - base);
+  const ChunkAt<C, TAIL> ch(k0, tab.N);
+  const int64_t base = ch.base;
+  const int nk = ch.nk;
   Slots gs;
-  load_chunk<C>(wk.g[0], base, nk, gs);
+  load_chunk<C, TAIL>(wk.g[0], base, nk, gs);
   for (int w = 1; w < W; ++w) {
     Slots g;
-    load_chunk<C>(wk.g[w], base, nk, g);
+    load_chunk<C, TAIL>(wk.g[w], base, nk, g);
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
       for (int c = 0; c < 4; ++c) gs[a][c] = gs[a][c] + g[a][c];
   }
   Slots mm, vv, u;
-  load_chunk<C>(m, base, nk, mm);
-  load_chunk<C>(v, base, nk, vv);
+  load_chunk<C, TAIL>(m, base, nk, mm);
+  load_chunk<C, TAIL>(v, base, nk, vv);
   const float fW = (float)W;
 #pragma unroll
   for (int a = 0; a < 4; ++a)
@@ -589,13 +664,13 @@ k_warmup_pass1(DevTable tab, int W, Workers wk, const float* __restrict__ x, flo
       vv[a][c] = (cf.beta2 * vv[a][c]) + (cf.a2 * (gb * gb));
       u[a][c] = mm[a][c] / (__builtin_sqrtf(vv[a][c]) + cf.eta);
     }
-  store_chunk<C>(m, base, nk, mm);
-  store_chunk<C>(v, base, nk, vv);
+  store_chunk<C, TAIL>(m, base, nk, mm);
+  store_chunk<C, TAIL>(v, base, nk, vv);
   Slots xx;
-  load_chunk<C>(x, base, nk, xx);
-  const int l0 = tab.l0[k];
-  const int l1 = tab.l1[k];
-  const int sb = tab.seg[k];
+  load_chunk<C, TAIL>(x, base, nk, xx);
+  const int l0 = tab.l0[ch.k];
+  const int l1 = tab.l1[ch.k];
+  const int sb = tab.seg[ch.k];
   for (int l = l0; l <= l1; ++l) {
     const int64_t lo = tab.off[l] - base;
     const int64_t hi = tab.off[l + 1] - base;
@@ -645,53 +720,41 @@ k_warmup_finalize(DevTable tab, const double* __restrict__ seg_x, const double* 
 }
 
 // Warmup pass 2: x = x - (lr*c_l)*u with u recomputed from the new m, v.
-template <int C>
+template <int C, bool TAIL>
 __global__ void __launch_bounds__(C / 16)
-k_warmup_pass2(DevTable tab, const float* __restrict__ m, const float* __restrict__ v,
+k_warmup_pass2(int64_t k0, DevTable tab, const float* __restrict__ m, const float* __restrict__ v,
                float* __restrict__ x, const float* __restrict__ c_layer, Coef cf) {
-  constexpr int T = Geo<C>::T;
-  const int64_t k = blockIdx.x;
-  const int64_t base = k * C;
-  const int nk = (int)min((int64_t)C, tab.N - base);
-  Slots mm, vv, xx;
-  load_chunk<C>(m, base, nk, mm);
-  load_chunk<C>(v, base, nk, vv);
-  load_chunk<C>(x, base, nk, xx);
-  const int l0 = tab.l0[k];
-  const int l1 = tab.l1[k];
-  const float step0 = cf.lr * c_layer[l0];
+  const ChunkAt<C, TAIL> ch(k0, tab.N);
+  Slots mm, vv, xx, st;
+  load_chunk<C, TAIL>(m, ch.base, ch.nk, mm);
+  load_chunk<C, TAIL>(v, ch.base, ch.nk, vv);
+  load_chunk<C, TAIL>(x, ch.base, ch.nk, xx);
+  step_sizes<C, TAIL>(tab, ch.k, ch.base, c_layer, cf.lr, st);
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      float step = step0;
-      if (l0 != l1) {
-        const int64_t gi = base + 4 * ((int)threadIdx.x + T * a) + c;
-        step = cf.lr * c_layer[tensor_of(tab, l0, l1, gi)];
-      }
       const float u = mm[a][c] / (__builtin_sqrtf(vv[a][c]) + cf.eta);
-      xx[a][c] = xx[a][c] - (step * u);
+      xx[a][c] = xx[a][c] - (st[a][c] * u);
     }
-  store_chunk<C>(x, base, nk, xx);
+  store_chunk<C, TAIL>(x, ch.base, ch.nk, xx);
 }
 
 // Freeze, element part: v_fresh = v, error buffers cleared.
-template <int C>
+template <int C, bool TAIL>
 __global__ void __launch_bounds__(C / 16)
-k_freeze_elems(int64_t n, int W, const float* __restrict__ v, float* __restrict__ v_fresh,
-               Workers wk, float* __restrict__ err_s) {
-  const int64_t k = blockIdx.x;
-  const int64_t base = k * C;
-  const int nk = (int)min((int64_t)C, n - base);
+k_freeze_elems(int64_t k0, int64_t n, int W, const float* __restrict__ v,
+               float* __restrict__ v_fresh, Workers wk, float* __restrict__ err_s) {
+  const ChunkAt<C, TAIL> ch(k0, n);
   Slots vv, zero;
-  load_chunk<C>(v, base, nk, vv);
-  store_chunk<C>(v_fresh, base, nk, vv);
+  load_chunk<C, TAIL>(v, ch.base, ch.nk, vv);
+  store_chunk<C, TAIL>(v_fresh, ch.base, ch.nk, vv);
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int c = 0; c < 4; ++c) zero[a][c] = 0.0f;
-  for (int w = 0; w < W; ++w) store_chunk<C>(wk.e[w], base, nk, zero);
-  store_chunk<C>(err_s, base, nk, zero);
+  for (int w = 0; w < W; ++w) store_chunk<C, TAIL>(wk.e[w], ch.base, ch.nk, zero);
+  store_chunk<C, TAIL>(err_s, ch.base, ch.nk, zero);
 }
 
 // Freeze, tensor part: c_avg = c_sum / T_w, f_prev = 1.
