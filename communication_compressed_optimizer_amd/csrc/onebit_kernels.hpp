@@ -113,6 +113,16 @@ __device__ __forceinline__ bool slot_valid(int k, int c, int nk) {
   return 4 * ((int)threadIdx.x + Geo<C>::T * k) + c < nk;
 }
 
+// A wave-uniform pointer, moved to scalar registers so that loads and stores
+// can use a scalar base plus one per-lane 32-bit offset.
+template <typename P>
+__device__ __forceinline__ P* scalar_ptr(P* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+  return reinterpret_cast<P*>(((uint64_t)hi << 32) | lo);
+}
+
 template <int C, bool TAIL, bool NT = false>
 __device__ __forceinline__ void load_chunk(const float* __restrict__ p, int64_t base, int nk,
                                            Slots& o) {
@@ -121,7 +131,9 @@ __device__ __forceinline__ void load_chunk(const float* __restrict__ p, int64_t 
   if constexpr (!TAIL) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const f32x4 v = ld4<NT>(p + base + 4 * (t + T * k));
+      // uniform slot base plus one per-lane offset shared by every array
+      const char* pk = scalar_ptr(reinterpret_cast<const char*>(p + (base + (int64_t)(4 * T * k))));
+      const f32x4 v = ld4<NT>(reinterpret_cast<const float*>(pk + 16u * threadIdx.x));
       o[k][0] = v.x;
       o[k][1] = v.y;
       o[k][2] = v.z;
@@ -144,7 +156,8 @@ __device__ __forceinline__ void store_chunk(float* __restrict__ p, int64_t base,
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const f32x4 v = {o[k][0], o[k][1], o[k][2], o[k][3]};
-      st4<NT>(p + base + 4 * (t + T * k), v);
+      char* pk = scalar_ptr(reinterpret_cast<char*>(p + (base + (int64_t)(4 * T * k))));
+      st4<NT>(reinterpret_cast<float*>(pk + 16u * threadIdx.x), v);
     }
   } else {
 #pragma unroll
