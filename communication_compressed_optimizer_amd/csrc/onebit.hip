@@ -154,10 +154,10 @@ void launch_chunks(int64_t n, hipStream_t st, KF kfull, KT ktail, A... args) {
 }
 
 // Tuning of the compression-step kernels, measured on MI355X at the
-// BERT-Large table with W = 8 (phase 1, interleaved medians: plain accesses
-// 7.76 ms, streaming 7.38 ms, streaming at 6 waves per SIMD 7.35 ms, at 7
-// waves 7.28 ms; prefetching the next worker costs more registers than the
-// latency it hides).
+// BERT-Large table with W = 8 (phase 1, interleaved medians on one box:
+// plain accesses 7.76 ms, streaming 7.38 ms, streaming at 7 waves per SIMD
+// with global scalar-base addressing 7.19 ms; prefetching the next worker, or
+// keeping beta1*m in LDS to avoid the cap's spills, did not help).
 constexpr bool kPassA_NT = true;   // streaming loads and stores
 constexpr bool kPassA_PF = false;  // next-worker prefetch
 constexpr int kPassA_WPE = 7;      // minimum waves per SIMD

@@ -95,17 +95,24 @@ struct ChunkAt {
 // ---------------------------------------------------------------------------
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// Streaming (nontemporal) or plain 16-byte accesses.
+// Streaming (nontemporal) or plain 16-byte accesses, always issued as
+// global-memory instructions (the pointers are global; an explicit address
+// space keeps the compiler from falling back to flat accesses, which would
+// also count against the LDS wait counter at every barrier).
+typedef __attribute__((address_space(1))) f32x4 gf32x4;
+
 template <bool NT>
 __device__ __forceinline__ f32x4 ld4(const float* p) {
-  if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
-  else return *reinterpret_cast<const f32x4*>(p);
+  const gf32x4* q = (const gf32x4*)p;
+  if constexpr (NT) return __builtin_nontemporal_load(q);
+  else return *q;
 }
 
 template <bool NT>
 __device__ __forceinline__ void st4(float* p, f32x4 v) {
-  if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
-  else *reinterpret_cast<f32x4*>(p) = v;
+  gf32x4* q = (gf32x4*)p;
+  if constexpr (NT) __builtin_nontemporal_store(v, q);
+  else *q = v;
 }
 
 template <int C>
