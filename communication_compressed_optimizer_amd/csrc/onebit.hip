@@ -155,12 +155,14 @@ void launch_chunks(int64_t n, hipStream_t st, KF kfull, KT ktail, A... args) {
 
 // Tuning of the compression-step kernels, measured on MI355X at the
 // BERT-Large table with W = 8 (phase 1, interleaved medians on one box:
-// plain accesses 7.76 ms, streaming 7.38 ms, streaming at 7 waves per SIMD
-// with global scalar-base addressing 7.19 ms; prefetching the next worker, or
-// keeping beta1*m in LDS to avoid the cap's spills, did not help).
+// plain accesses 7.76 ms, streaming 7.38 ms; with the partial chunk folded
+// into the grid, streaming with a 6-wave register cap 7.05 ms, uncapped 7.39,
+// 7-wave cap 7.44, 8-wave cap 7.89 -- the cap's spills are reloaded every
+// worker iteration, so the best cap depends on where they land; prefetching
+// the next worker, or keeping beta1*m in LDS, did not help).
 constexpr bool kPassA_NT = true;   // streaming loads and stores
 constexpr bool kPassA_PF = false;  // next-worker prefetch
-constexpr int kPassA_WPE = 7;      // minimum waves per SIMD
+constexpr int kPassA_WPE = 6;      // minimum waves per SIMD
 constexpr bool kPassB_NT = true;
 
 template <int C>
@@ -217,9 +219,9 @@ struct LaunchPassA {
   static void run(const onebit_layer_table* t, int W, const Workers& wk, float* err_s,
                   const float* m, const float* v_frozen, float* v_fresh, uint32_t* bits_s,
                   float* scales_s, const Coef& cf, const Ws& ws, int32_t* status, hipStream_t st) {
-    launch_chunks<C>(t->N, st, k_compressed_pass_a<C, false, kPassA_NT, kPassA_PF, kPassA_WPE>,
-                     k_compressed_pass_a<C, true, kPassA_NT, kPassA_PF, kPassA_WPE>, t->dev, W, wk,
-                     err_s, m, v_frozen, v_fresh, bits_s, scales_s, ws.seg_max, cf, status);
+    hipLaunchKernelGGL((k_compressed_pass_a<C, kPassA_NT, kPassA_PF, kPassA_WPE>),
+                       dim3((unsigned)t->K), dim3(C / 16), 0, st, t->N / C, t->dev, W, wk, err_s, m,
+                       v_frozen, v_fresh, bits_s, scales_s, ws.seg_max, cf, status);
   }
 };
 
@@ -230,9 +232,9 @@ struct LaunchPassB {
                   float* c_out, const Coef& cf, const Ws& ws, int32_t* status, hipStream_t st) {
     hipLaunchKernelGGL(k_rescale_finalize<256>, dim3((unsigned)t->L), dim3(256), 0, st, t->dev,
                        (const float*)ws.seg_max, c_avg, f_prev, ws.c_layer, c_out, cf, status);
-    launch_chunks<C>(t->N, st, k_compressed_pass_b<C, false, kPassB_NT>,
-                     k_compressed_pass_b<C, true, kPassB_NT>, t->dev, bits_s, scales_s, v_frozen, x,
-                     m, (const float*)ws.c_layer, cf);
+    hipLaunchKernelGGL((k_compressed_pass_b<C, kPassB_NT>), dim3((unsigned)t->K), dim3(C / 16), 0,
+                       st, t->N / C, t->dev, bits_s, scales_s, v_frozen, x, m,
+                       (const float*)ws.c_layer, cf);
   }
 };
 

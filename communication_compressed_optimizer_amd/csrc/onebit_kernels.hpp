@@ -76,15 +76,15 @@ struct Geo {
 
 using Slots = float[4][4];  // [slot k][component c]
 
-// Chunk of this workgroup.  Every chunk kernel is instantiated twice: for the
+// Chunk k of an n-element buffer.  Chunk code is instantiated twice: for the
 // full chunks (TAIL = false: nk == C at compile time, no guards) and for the
-// one partial last chunk (TAIL = true), launched separately.
+// one partial last chunk (TAIL = true).
 template <int C, bool TAIL>
 struct ChunkAt {
   int64_t k, base;
   int nk;
-  __device__ __forceinline__ ChunkAt(int64_t k0, int64_t n) {
-    k = k0 + (int64_t)blockIdx.x;
+  __device__ __forceinline__ ChunkAt(int64_t k_, int64_t n) {
+    k = k_;
     base = k * C;
     nk = TAIL ? (int)(n - base) : C;
   }
@@ -384,7 +384,7 @@ k_compress_ef(int64_t k0, int64_t n, const float* __restrict__ in, float* __rest
               uint32_t* __restrict__ bits, float* __restrict__ scales, int32_t* status) {
   __shared__ float4 lds[2 * Geo<C>::T];
   int parity = 0;
-  const ChunkAt<C, TAIL> ch(k0, n);
+  const ChunkAt<C, TAIL> ch(k0 + (int64_t)blockIdx.x, n);
   Slots z, e;
   load_chunk<C, TAIL>(in, ch.base, ch.nk, z);
   load_chunk<C, TAIL>(err, ch.base, ch.nk, e);
@@ -409,7 +409,7 @@ k_average_packed(int64_t k0, int64_t n, int W, PackedIn pin, float* __restrict__
                  uint32_t* __restrict__ bits_out, float* __restrict__ scales_out, int32_t* status) {
   __shared__ float4 lds[2 * Geo<C>::T];
   int parity = 0;
-  const ChunkAt<C, TAIL> ch(k0, n);
+  const ChunkAt<C, TAIL> ch(k0 + (int64_t)blockIdx.x, n);
   Slots acc, y;
   for (int w = 0; w < W; ++w) {
     const float s = pin.scales[w][ch.k];
@@ -444,7 +444,7 @@ template <int C, bool TAIL>
 __global__ void __launch_bounds__(C / 16)
 k_decompress(int64_t k0, int64_t n, const uint32_t* __restrict__ bits,
              const float* __restrict__ scales, float* __restrict__ out) {
-  const ChunkAt<C, TAIL> ch(k0, n);
+  const ChunkAt<C, TAIL> ch(k0 + (int64_t)blockIdx.x, n);
   const float s = scales[ch.k];
   uint32_t nib[4];
   load_sign_nibbles<C>(bits + ch.k * Geo<C>::WORDS, nib);
@@ -467,18 +467,18 @@ k_decompress(int64_t k0, int64_t n, const uint32_t* __restrict__ bits,
 //   PF:  worker w+1's gradient and error are loaded before worker w's chunk
 //        reduction, so they are in flight across its barrier.
 //   WPE: minimum waves per SIMD the register allocation must allow.
-template <int C, bool TAIL, bool NT = false, bool PF = false, int WPE = 1>
-__global__ void __launch_bounds__(C / 16, WPE)
-k_compressed_pass_a(int64_t k0, DevTable tab, int W, Workers wk, float* __restrict__ err_s,
-                    const float* __restrict__ m, const float* __restrict__ v_frozen,
-                    float* __restrict__ v_fresh, uint32_t* __restrict__ bits_s,
-                    float* __restrict__ scales_s, float* __restrict__ seg_max, Coef cf,
-                    int32_t* status) {
-  constexpr int T = Geo<C>::T;
-  __shared__ float4 lds[2 * T];
-  __shared__ float red[T / 64];
+template <int C, bool TAIL, bool NT, bool PF>
+__device__ __forceinline__ void pass_a_chunk(int64_t kk, const DevTable& tab, int W,
+                                             const Workers& wk, float* __restrict__ err_s,
+                                             const float* __restrict__ m,
+                                             const float* __restrict__ v_frozen,
+                                             float* __restrict__ v_fresh,
+                                             uint32_t* __restrict__ bits_s,
+                                             float* __restrict__ scales_s,
+                                             float* __restrict__ seg_max, const Coef& cf,
+                                             int32_t* status, float4* lds, float* red) {
   int parity = 0;
-  const ChunkAt<C, TAIL> ch(k0, tab.N);
+  const ChunkAt<C, TAIL> ch(kk, tab.N);
   const int64_t base = ch.base;
   const int nk = ch.nk;
   const int t = threadIdx.x;
@@ -574,6 +574,28 @@ k_compressed_pass_a(int64_t k0, DevTable tab, int W, Workers wk, float* __restri
   segment_max<C>(tab, ch.k, base, nk, vz, red, seg_max);  // vz now holds the ratio q
 }
 
+
+// One workgroup per chunk; when the buffer ends in a partial chunk, block 0
+// takes it (its guarded code is slower, so it starts first and overlaps the
+// full chunks instead of trailing them).
+template <int C, bool NT = false, bool PF = false, int WPE = 1>
+__global__ void __launch_bounds__(C / 16, WPE)
+k_compressed_pass_a(int64_t n_full, DevTable tab, int W, Workers wk, float* __restrict__ err_s,
+                    const float* __restrict__ m, const float* __restrict__ v_frozen,
+                    float* __restrict__ v_fresh, uint32_t* __restrict__ bits_s,
+                    float* __restrict__ scales_s, float* __restrict__ seg_max, Coef cf,
+                    int32_t* status) {
+  __shared__ float4 lds[2 * Geo<C>::T];
+  __shared__ float red[Geo<C>::T / 64];
+  const int64_t has_tail = tab.K - n_full;
+  if (has_tail && blockIdx.x == 0)
+    pass_a_chunk<C, true, NT, PF>(n_full, tab, W, wk, err_s, m, v_frozen, v_fresh, bits_s, scales_s,
+                                  seg_max, cf, status, lds, red);
+  else
+    pass_a_chunk<C, false, NT, PF>((int64_t)blockIdx.x - has_tail, tab, W, wk, err_s, m, v_frozen,
+                                   v_fresh, bits_s, scales_s, seg_max, cf, status, lds, red);
+}
+
 // Per tensor: rho = max of its segments, soft thresholds, c.
 template <int TB>
 __global__ void __launch_bounds__(TB)
@@ -624,13 +646,14 @@ __device__ __forceinline__ void step_sizes(const DevTable& tab, int64_t k, int64
 }
 
 // Compression step, pass B: x update with the per-tensor c, m = mhat.
-template <int C, bool TAIL, bool NT = false>
-__global__ void __launch_bounds__(C / 16)
-k_compressed_pass_b(int64_t k0, DevTable tab, const uint32_t* __restrict__ bits_s,
-                    const float* __restrict__ scales_s, const float* __restrict__ v_frozen,
-                    float* __restrict__ x, float* __restrict__ m, const float* __restrict__ c_layer,
-                    Coef cf) {
-  const ChunkAt<C, TAIL> ch(k0, tab.N);
+template <int C, bool TAIL, bool NT>
+__device__ __forceinline__ void pass_b_chunk(int64_t kk, const DevTable& tab,
+                                             const uint32_t* __restrict__ bits_s,
+                                             const float* __restrict__ scales_s,
+                                             const float* __restrict__ v_frozen,
+                                             float* __restrict__ x, float* __restrict__ m,
+                                             const float* __restrict__ c_layer, const Coef& cf) {
+  const ChunkAt<C, TAIL> ch(kk, tab.N);
   const float s = scales_s[ch.k];
   uint32_t nib[4];
   load_sign_nibbles<C>(bits_s + ch.k * Geo<C>::WORDS, nib);
@@ -649,6 +672,20 @@ k_compressed_pass_b(int64_t k0, DevTable tab, const uint32_t* __restrict__ bits_
   store_chunk<C, TAIL, NT>(m, ch.base, ch.nk, mh);
 }
 
+template <int C, bool NT = false>
+__global__ void __launch_bounds__(C / 16)
+k_compressed_pass_b(int64_t n_full, DevTable tab, const uint32_t* __restrict__ bits_s,
+                    const float* __restrict__ scales_s, const float* __restrict__ v_frozen,
+                    float* __restrict__ x, float* __restrict__ m, const float* __restrict__ c_layer,
+                    Coef cf) {
+  const int64_t has_tail = tab.K - n_full;
+  if (has_tail && blockIdx.x == 0)
+    pass_b_chunk<C, true, NT>(n_full, tab, bits_s, scales_s, v_frozen, x, m, c_layer, cf);
+  else
+    pass_b_chunk<C, false, NT>((int64_t)blockIdx.x - has_tail, tab, bits_s, scales_s, v_frozen, x,
+                               m, c_layer, cf);
+}
+
 // Warmup pass 1: mean gradient, moments, per-(chunk, tensor) sums of x^2 and
 // u^2 in double.
 template <int C, bool TAIL>
@@ -658,7 +695,7 @@ k_warmup_pass1(int64_t k0, DevTable tab, int W, Workers wk, const float* __restr
                double* __restrict__ seg_u, Coef cf) {
   constexpr int T = Geo<C>::T;
   __shared__ double red[2 * (T / 64)];
-  const ChunkAt<C, TAIL> ch(k0, tab.N);
+  const ChunkAt<C, TAIL> ch(k0 + (int64_t)blockIdx.x, tab.N);
   const int64_t base = ch.base;
   const int nk = ch.nk;
   Slots gs;
@@ -744,7 +781,7 @@ template <int C, bool TAIL>
 __global__ void __launch_bounds__(C / 16)
 k_warmup_pass2(int64_t k0, DevTable tab, const float* __restrict__ m, const float* __restrict__ v,
                float* __restrict__ x, const float* __restrict__ c_layer, Coef cf) {
-  const ChunkAt<C, TAIL> ch(k0, tab.N);
+  const ChunkAt<C, TAIL> ch(k0 + (int64_t)blockIdx.x, tab.N);
   Slots mm, vv, xx, st;
   load_chunk<C, TAIL>(m, ch.base, ch.nk, mm);
   load_chunk<C, TAIL>(v, ch.base, ch.nk, vv);
@@ -765,7 +802,7 @@ template <int C, bool TAIL>
 __global__ void __launch_bounds__(C / 16)
 k_freeze_elems(int64_t k0, int64_t n, int W, const float* __restrict__ v,
                float* __restrict__ v_fresh, Workers wk, float* __restrict__ err_s) {
-  const ChunkAt<C, TAIL> ch(k0, n);
+  const ChunkAt<C, TAIL> ch(k0 + (int64_t)blockIdx.x, n);
   Slots vv, zero;
   load_chunk<C, TAIL>(v, ch.base, ch.nk, vv);
   store_chunk<C, TAIL>(v_fresh, ch.base, ch.nk, vv);
