@@ -79,3 +79,16 @@ def test_table_checks(ob):
     hp = ob.onebit_hparams(weight_decay=0.01)
     assert lib.onebit_lamb_warmup_step(None, 1, None, None, None, None, None, None,
                                        ctypes.byref(hp), None, None, None) == ob.ONEBIT_EINVAL
+
+
+def test_package_refuses_to_load_without_library(tmp_path):
+    """No fallback: without libonebit.so the package import fails loudly."""
+    import shutil
+    import subprocess
+    import sys
+    pkg = tmp_path / "communication_compressed_optimizer_amd"
+    pkg.mkdir()
+    shutil.copy(os.path.join(ROOT, "communication_compressed_optimizer_amd", "__init__.py"), pkg)
+    res = subprocess.run([sys.executable, "-c", "import communication_compressed_optimizer_amd"],
+                         cwd=tmp_path, capture_output=True, text=True)
+    assert res.returncode != 0 and "is not built" in res.stderr

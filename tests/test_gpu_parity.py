@@ -300,3 +300,105 @@ def test_worker_packed_outputs_optional():
     b.compressed_step(0)
     for k in ("x", "m", "vf", "err_s", "bits_s", "scales_s"):
         assert torch.equal(getattr(a, k), getattr(b, k)), k
+
+
+# ---------------------------------------------------------------------------
+# failure handling and elastic membership (forced from the host)
+# ---------------------------------------------------------------------------
+def test_worker_drop_and_rejoin():
+    """A worker leaves for two steps (the step runs with W-1 workers) and
+    rejoins with its error buffer reset; GPU and oracle agree throughout."""
+    numels = RAGGED[0]
+    wl4 = _ragged_workload(numels, 4)
+    d, h = DevRun(wl4), HostRun(wl4)
+    N = wl4.N
+    hp = d.hp
+    for step in range(5):
+        active = [0, 1, 2] if step in (1, 2) else [0, 1, 2, 3]
+        if step == 3:                           # rejoin: its stale error is dropped
+            d.e[3].zero_()
+            h.e[3][:] = 0
+        d.fill_grads(step)
+        h.fill_grads(step)
+        W = len(active)
+        ob.onebit_lamb_compressed_step(
+            d.table, W, [d.g[w] for w in active], [d.e[w] for w in active], d.err_s, d.x, d.m, d.v,
+            d.vf, d.c_avg, d.f_prev, d.c_out, [d.bits_w[w] for w in active],
+            [d.scales_w[w] for w in active], d.bits_s, d.scales_s, hp, d.ws, d.status)
+        out = oracle.compressed_step(h.numels, wl4.chunk, [h.g[w] for w in active],
+                                     [h.e[w] for w in active], h.err_s, h.x, h.m, h.v, h.vf,
+                                     h.c_avg, h.f_prev, h.hp)
+        torch.cuda.synchronize()
+        for name, a, b in (("x", d.x, h.x), ("m", d.m, h.m), ("vf", d.vf, h.vf),
+                           ("err_s", d.err_s, h.err_s)):
+            assert np.array_equal(host(a).view(np.uint32), b.view(np.uint32)), (step, name)
+        for w in range(4):
+            assert np.array_equal(host(d.e[w]).view(np.uint32), h.e[w].view(np.uint32)), (step, w)
+        assert np.array_equal(u32(d.bits_s), out["bits_s"])
+    assert N > 0 and int(d.status.item()) == 0
+
+
+def test_status_flags_from_steps():
+    """Non-finite gradients set the documented status bits in the warmup and
+    in the compression step; the calls still complete."""
+    wl = _ragged_workload(RAGGED[0], 2, init="fresh")
+    d = DevRun(wl)
+    d.fill_grads(0)
+    d.g[1][5] = float("nan")
+    ob.onebit_lamb_warmup_step(d.table, 2, d.g, d.x, d.m, d.v, d.c_sum, d.c_out, d.hp, d.ws,
+                               d.status)
+    torch.cuda.synchronize()
+    assert int(d.status.item()) & ob.ONEBIT_STATUS_NONFINITE_TRUST
+    wl2 = _ragged_workload(RAGGED[0], 2)
+    d2 = DevRun(wl2)
+    d2.fill_grads(0)
+    d2.g[0][100] = float("inf")
+    ob.onebit_lamb_compressed_step(d2.table, 2, d2.g, d2.e, d2.err_s, d2.x, d2.m, d2.v, d2.vf,
+                                   d2.c_avg, d2.f_prev, d2.c_out, d2.bits_w, d2.scales_w,
+                                   d2.bits_s, d2.scales_s, d2.hp, d2.ws, d2.status)
+    torch.cuda.synchronize()
+    st = int(d2.status.item())
+    assert st & ob.ONEBIT_STATUS_NONFINITE_WORKER and st & ob.ONEBIT_STATUS_NONFINITE_SERVER
+
+
+def test_binding_rejects_bad_arguments():
+    n, C = 4096, 4096
+    a = torch.zeros(n + 4, dtype=torch.float32, device="cuda")
+    bits = torch.zeros(n // 32, dtype=torch.int32, device="cuda")
+    sc = torch.zeros(1, dtype=torch.float32, device="cuda")
+    with pytest.raises(ob.OnebitError) as ei:
+        ob.onebit_compress_ef(n, C, a[1:], a[:n], bits, sc)      # 4-byte offset
+    assert ei.value.code == ob.ONEBIT_EALIGN
+    with pytest.raises(ob.OnebitError) as ei:
+        ob.onebit_compress_ef(n, 3000, a, a, bits, sc)
+    assert ei.value.code == ob.ONEBIT_EUNSUPPORTED
+    with pytest.raises(ob.OnebitError):
+        ob.LayerTable([10, 0, 5])
+    ob.onebit_average_packed(0, C, 2, [bits, bits], [sc, sc], a, bits, sc)   # n = 0: nothing
+    ob.onebit_decompress(0, C, bits, sc, a)
+    assert torch.count_nonzero(a).item() == 0
+
+
+def test_many_workers_trajectory():
+    """W = 16 workers through warmup, freeze and compression on a ragged table."""
+    wl = _ragged_workload(RAGGED[0], 16, init="fresh")
+    d, h = DevRun(wl), HostRun(wl)
+    for step in range(3):
+        d.warmup_step(step)
+        h.warmup_step(step)
+    d.freeze(3)
+    h.freeze(3)
+    for step in range(3, 6):
+        d.compressed_step(step)
+        h.compressed_step(step)
+        assert_parity(compare_state(d, h), f"step {step}")
+
+
+@pytest.mark.parametrize("chunk", [1024, 16384])
+def test_warmup_other_chunks(chunk):
+    wl = _ragged_workload(RAGGED[0] + [2 * chunk + 3], 3, chunk=chunk, init="fresh")
+    d, h = DevRun(wl), HostRun(wl)
+    for step in range(2):
+        d.warmup_step(step)
+        h.warmup_step(step)
+    assert_parity(compare_state(d, h, stage="warmup"))
