@@ -175,6 +175,21 @@ def main():
     log(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step (phase1 {p1_ms:.3f} ms, "
         f"phase2 {p2_ms:.3f} ms)")
 
+    # context: one LAMB warmup step on the same table (after the timed
+    # compression steps; it reuses the same buffers)
+    c_sum = torch.zeros(L, dtype=torch.float32, device=dev)
+    for _ in range(2):
+        ob.onebit_lamb_warmup_step(table, W, g, x, m, v, c_sum, c_out, hp, ws, status, stream)
+    wev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    wsteps = 5
+    wev[0].record(stream)
+    for _ in range(wsteps):
+        ob.onebit_lamb_warmup_step(table, W, g, x, m, v, c_sum, c_out, hp, ws, status, stream)
+    wev[1].record(stream)
+    torch.cuda.synchronize()
+    warm_ms = wev[0].elapsed_time(wev[1]) / wsteps
+    warm_bytes = N * (4 * W + 36)
+
     sbytes = step_bytes(N, K, C, W)
     abytes = phase1_bytes(N, K, C, W)
     achieved = abytes / (p1_ms * 1e-3) / 1e9
@@ -206,6 +221,8 @@ def main():
         "frac_of_peak": step_gbps / PEAK_HBM_GBPS,
         "step_bytes": sbytes,
         "phase_ms": {"compress_average": p1_ms, "rescale_update": p2_ms},
+        "warmup_step": {"ms": warm_ms, "params_per_s": N / (warm_ms * 1e-3),
+                        "GBps": warm_bytes / (warm_ms * 1e-3) / 1e9, "bytes": warm_bytes},
         "roofline": {"bound": "hbm", "kernel": "k_compressed_pass_a<4096>",
                      "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
