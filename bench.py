@@ -194,7 +194,7 @@ def main():
     abytes = phase1_bytes(N, K, C, W)
     achieved = abytes / (p1_ms * 1e-3) / 1e9
     step_gbps = sbytes / (ms_per_step * 1e-3) / 1e9
-    traffic = _measured_traffic()
+    traffic = _measured_traffic() if wl.name == "bert_large" else None
     cpu = None
     if args.cpu_chunks > 0:
         log("[bench] CPU oracle baseline ...")
