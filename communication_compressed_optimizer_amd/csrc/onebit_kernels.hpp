@@ -13,8 +13,8 @@
 // levels h >= 4 act on the float4 slot index p with strides P/2..1
 // (P = C/4) independently per component; strides 2T and T pair a thread's
 // own slots, strides T/2..64 pair waves (through LDS), strides 32..1 pair
-// lanes (cross-lane shuffles), and the last two levels (h = 2, 1) combine
-// the four components: (c0 + c2) + (c1 + c3).
+// lanes (lane swaps and DPP row shifts), and the last two levels (h = 2, 1)
+// combine the four components: (c0 + c2) + (c1 + c3).
 //
 // Packed signs.  Element 4p+c sits in word p/8 at bit 4(p mod 8)+c, so
 // eight consecutive lanes each contribute one nibble to a word; three DPP
@@ -182,6 +182,23 @@ __device__ __forceinline__ float uniform_f32(float v) {
   return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
 }
 
+// Lanes l < s receive v[l] + v[l+s] for s = 32, 16, 8, 4, 2, 1 in turn, so
+// lane 0 ends with the stride-halving tree over the wave's 64 values:
+// strides 32 and 16 use the gfx950 lane swaps (the second result of
+// permlane32_swap(v, v) holds lane l+32 in lanes 0-31, that of
+// permlane16_swap(v, v) lane l+16 in lanes 0-15), strides 8..1 DPP row shifts.
+__device__ __forceinline__ float wave_tree_sum(float v) {
+  v = v + __uint_as_float(__builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                           false, false)[1]);
+  v = v + __uint_as_float(__builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
+                                                           false, false)[1]);
+  v = v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x108, 0xF, 0xF, false));
+  v = v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x104, 0xF, 0xF, false));
+  v = v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x102, 0xF, 0xF, false));
+  v = v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x101, 0xF, 0xF, false));
+  return v;
+}
+
 // lds: 2*T float4 (double-buffered between consecutive calls, so one
 // barrier per call suffices).  Returns the sum in every thread.
 template <int C>
@@ -222,10 +239,8 @@ __device__ __forceinline__ float chunk_sumsq(const Slots& z, float4* __restrict_
     for (int c = 0; c < 4; ++c) p[c] = v[0][c];
   }
 #pragma unroll
-  for (int s = 32; s >= 1; s >>= 1)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) p[c] = p[c] + __shfl_down(p[c], s, 64);  // lane strides 32..1
-  return uniform_f32((p[0] + p[2]) + (p[1] + p[3]));                 // h = 2, then h = 1
+  for (int c = 0; c < 4; ++c) p[c] = wave_tree_sum(p[c]);  // lane strides 32..1
+  return uniform_f32((p[0] + p[2]) + (p[1] + p[3]));  // h = 2, then h = 1
 }
 
 __device__ __forceinline__ float chunk_scale(float S, int nk) {
