@@ -163,6 +163,7 @@ void launch_chunks(int64_t n, hipStream_t st, KF kfull, KT ktail, A... args) {
 constexpr bool kPassA_NT = true;   // streaming loads and stores
 constexpr bool kPassA_PF = false;  // next-worker prefetch
 constexpr int kPassA_WPE = 6;      // minimum waves per SIMD
+constexpr int kPassA_SPT = 4;      // float4 slots per thread (workgroup = C / (4 * SPT))
 constexpr bool kPassB_NT = true;
 
 template <int C>
@@ -219,8 +220,8 @@ struct LaunchPassA {
   static void run(const onebit_layer_table* t, int W, const Workers& wk, float* err_s,
                   const float* m, const float* v_frozen, float* v_fresh, uint32_t* bits_s,
                   float* scales_s, const Coef& cf, const Ws& ws, int32_t* status, hipStream_t st) {
-    hipLaunchKernelGGL((k_compressed_pass_a<C, kPassA_NT, kPassA_PF, kPassA_WPE>),
-                       dim3((unsigned)t->K), dim3(C / 16), 0, st, t->N / C, t->dev, W, wk, err_s, m,
+    hipLaunchKernelGGL((k_compressed_pass_a<C, kPassA_NT, kPassA_PF, kPassA_WPE, kPassA_SPT>),
+                       dim3((unsigned)t->K), dim3(Geo<C, kPassA_SPT>::T), 0, st, t->N / C, t->dev, W, wk, err_s, m,
                        v_frozen, v_fresh, bits_s, scales_s, ws.seg_max, cf, status);
   }
 };

@@ -66,15 +66,20 @@ struct PackedIn {
   const float* scales[kMaxWorkers];
 };
 
-template <int C>
+// C elements per chunk, SPT float4 slots per thread, T = C/(4*SPT) threads.
+template <int C, int SPT = 4>
 struct Geo {
   static_assert(C >= 1024 && C <= 16384 && (C & (C - 1)) == 0, "chunk must be 2^10..2^14");
-  static constexpr int T = C / 16;      // threads per chunk
-  static constexpr int NW = T / 64;     // waves per chunk
-  static constexpr int WORDS = C / 32;  // sign words per chunk
+  static_assert(SPT == 1 || SPT == 2 || SPT == 4, "slots per thread");
+  static constexpr int T = C / (4 * SPT);  // threads per chunk
+  static constexpr int NW = T / 64;        // waves per chunk
+  static constexpr int WORDS = C / 32;     // sign words per chunk
+  static_assert(T >= 64 && T <= 1024, "workgroup size");
 };
 
-using Slots = float[4][4];  // [slot k][component c]
+template <int S>
+using SlotsN = float[S][4];  // [slot k][component c]
+using Slots = SlotsN<4>;
 
 // Chunk k of an n-element buffer.  Chunk code is instantiated twice: for the
 // full chunks (TAIL = false: nk == C at compile time, no guards) and for the
@@ -115,9 +120,9 @@ __device__ __forceinline__ void st4(float* p, f32x4 v) {
   else *q = v;
 }
 
-template <int C>
+template <int C, int SPT = 4>
 __device__ __forceinline__ bool slot_valid(int k, int c, int nk) {
-  return 4 * ((int)threadIdx.x + Geo<C>::T * k) + c < nk;
+  return 4 * ((int)threadIdx.x + Geo<C, SPT>::T * k) + c < nk;
 }
 
 // A wave-uniform pointer, moved to scalar registers so that loads and stores
@@ -130,14 +135,14 @@ __device__ __forceinline__ P* scalar_ptr(P* p) {
   return reinterpret_cast<P*>(((uint64_t)hi << 32) | lo);
 }
 
-template <int C, bool TAIL, bool NT = false>
+template <int C, bool TAIL, bool NT = false, int SPT = 4>
 __device__ __forceinline__ void load_chunk(const float* __restrict__ p, int64_t base, int nk,
-                                           Slots& o) {
-  constexpr int T = Geo<C>::T;
+                                           SlotsN<SPT>& o) {
+  constexpr int T = Geo<C, SPT>::T;
   const int t = threadIdx.x;
   if constexpr (!TAIL) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < SPT; ++k) {
       // uniform slot base plus one per-lane offset shared by every array
       const char* pk = scalar_ptr(reinterpret_cast<const char*>(p + (base + (int64_t)(4 * T * k))));
       const f32x4 v = ld4<NT>(reinterpret_cast<const float*>(pk + 16u * threadIdx.x));
@@ -148,30 +153,30 @@ __device__ __forceinline__ void load_chunk(const float* __restrict__ p, int64_t 
     }
   } else {
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
+    for (int k = 0; k < SPT; ++k)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) o[k][c] = slot_valid<C>(k, c, nk) ? p[base + 4 * (t + T * k) + c] : 0.0f;
+      for (int c = 0; c < 4; ++c) o[k][c] = slot_valid<C, SPT>(k, c, nk) ? p[base + 4 * (t + T * k) + c] : 0.0f;
   }
 }
 
-template <int C, bool TAIL, bool NT = false>
+template <int C, bool TAIL, bool NT = false, int SPT = 4>
 __device__ __forceinline__ void store_chunk(float* __restrict__ p, int64_t base, int nk,
-                                            const Slots& o) {
-  constexpr int T = Geo<C>::T;
+                                            const SlotsN<SPT>& o) {
+  constexpr int T = Geo<C, SPT>::T;
   const int t = threadIdx.x;
   if constexpr (!TAIL) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < SPT; ++k) {
       const f32x4 v = {o[k][0], o[k][1], o[k][2], o[k][3]};
       char* pk = scalar_ptr(reinterpret_cast<char*>(p + (base + (int64_t)(4 * T * k))));
       st4<NT>(reinterpret_cast<float*>(pk + 16u * threadIdx.x), v);
     }
   } else {
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
+    for (int k = 0; k < SPT; ++k)
 #pragma unroll
       for (int c = 0; c < 4; ++c)
-        if (slot_valid<C>(k, c, nk)) p[base + 4 * (t + T * k) + c] = o[k][c];
+        if (slot_valid<C, SPT>(k, c, nk)) p[base + 4 * (t + T * k) + c] = o[k][c];
   }
 }
 
@@ -201,18 +206,21 @@ __device__ __forceinline__ float wave_tree_sum(float v) {
 
 // lds: 2*T float4 (double-buffered between consecutive calls, so one
 // barrier per call suffices).  Returns the sum in every thread.
-template <int C>
-__device__ __forceinline__ float chunk_sumsq(const Slots& z, float4* __restrict__ lds, int& parity) {
-  constexpr int T = Geo<C>::T;
-  constexpr int NW = Geo<C>::NW;
+template <int C, int SPT = 4>
+__device__ __forceinline__ float chunk_sumsq(const SlotsN<SPT>& z, float4* __restrict__ lds, int& parity) {
+  constexpr int T = Geo<C, SPT>::T;
+  constexpr int NW = Geo<C, SPT>::NW;
   float p[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    const float q0 = z[0][c] * z[0][c];
-    const float q1 = z[1][c] * z[1][c];
-    const float q2 = z[2][c] * z[2][c];
-    const float q3 = z[3][c] * z[3][c];
-    p[c] = (q0 + q2) + (q1 + q3);  // slot strides 2T, then T
+    float q[SPT];
+#pragma unroll
+    for (int k = 0; k < SPT; ++k) q[k] = z[k][c] * z[k][c];
+#pragma unroll
+    for (int h = SPT / 2; h >= 1; h /= 2)
+#pragma unroll
+      for (int k = 0; k < h; ++k) q[k] = q[k] + q[k + h];  // slot strides (SPT/2)T .. T
+    p[c] = q[0];
   }
   if constexpr (NW > 1) {
     float4* buf = lds + parity * T;
@@ -258,50 +266,51 @@ __device__ __forceinline__ uint32_t or_group8(uint32_t x) {
 }
 
 // nib[k]: bit c = sign of element 4(t+T*k)+c.  words: the chunk's C/32 words.
-template <int C>
-__device__ __forceinline__ void store_sign_words(uint32_t* __restrict__ words, const uint32_t (&nib)[4]) {
-  constexpr int T = Geo<C>::T;
+template <int C, int SPT = 4>
+__device__ __forceinline__ void store_sign_words(uint32_t* __restrict__ words, const uint32_t (&nib)[SPT]) {
+  constexpr int T = Geo<C, SPT>::T;
   const int t = threadIdx.x;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
+  for (int k = 0; k < SPT; ++k) {
     const uint32_t w = or_group8(nib[k] << (4 * (t & 7)));
     if ((t & 7) == 0) words[(t + T * k) >> 3] = w;
   }
 }
 
-template <int C>
-__device__ __forceinline__ void load_sign_nibbles(const uint32_t* __restrict__ words, uint32_t (&nib)[4]) {
-  constexpr int T = Geo<C>::T;
+template <int C, int SPT = 4>
+__device__ __forceinline__ void load_sign_nibbles(const uint32_t* __restrict__ words, uint32_t (&nib)[SPT]) {
+  constexpr int T = Geo<C, SPT>::T;
   const int t = threadIdx.x;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) nib[k] = (words[(t + T * k) >> 3] >> (4 * (t & 7))) & 0xFu;
+  for (int k = 0; k < SPT; ++k) nib[k] = (words[(t + T * k) >> 3] >> (4 * (t & 7))) & 0xFu;
 }
 
-__device__ __forceinline__ float signed_scale(const uint32_t (&nib)[4], int k, int c, float s) {
+template <int S>
+__device__ __forceinline__ float signed_scale(const uint32_t (&nib)[S], int k, int c, float s) {
   return ((nib[k] >> c) & 1u) ? s : -s;
 }
 
 // Error-compensated 1-bit compression of z in place (z becomes the error):
 // returns the chunk scale s; nib receives the sign nibbles (0 past the last
 // valid element, whose slots are cleared first so they count as 0).
-template <int C, bool TAIL>
-__device__ __forceinline__ float compress_slots(Slots& z, int nk, float4* lds, int& parity,
-                                                uint32_t (&nib)[4]) {
+template <int C, bool TAIL, int SPT = 4>
+__device__ __forceinline__ float compress_slots(SlotsN<SPT>& z, int nk, float4* lds, int& parity,
+                                                uint32_t (&nib)[SPT]) {
   if constexpr (TAIL) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
+    for (int k = 0; k < SPT; ++k)
 #pragma unroll
       for (int c = 0; c < 4; ++c)
-        if (!slot_valid<C>(k, c, nk)) z[k][c] = 0.0f;
+        if (!slot_valid<C, SPT>(k, c, nk)) z[k][c] = 0.0f;
   }
-  const float s = chunk_scale(chunk_sumsq<C>(z, lds, parity), nk);
+  const float s = chunk_scale(chunk_sumsq<C, SPT>(z, lds, parity), nk);
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
+  for (int k = 0; k < SPT; ++k) {
     uint32_t nb = 0;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const bool b = z[k][c] >= 0.0f;
-      nb |= (uint32_t)(b && (!TAIL || slot_valid<C>(k, c, nk))) << c;
+      nb |= (uint32_t)(b && (!TAIL || slot_valid<C, SPT>(k, c, nk))) << c;
       z[k][c] = b ? z[k][c] - s : z[k][c] + s;
     }
     nib[k] = nb;
@@ -365,10 +374,10 @@ __device__ __forceinline__ int tensor_of(const DevTable& tab, int l0, int l1, in
 }
 
 // Per-(chunk, tensor) maximum of q over the chunk's valid elements.
-template <int C>
+template <int C, int SPT = 4>
 __device__ __forceinline__ void segment_max(const DevTable& tab, int64_t k, int64_t base, int nk,
-                                            const Slots& q, float* red, float* __restrict__ seg_max) {
-  constexpr int T = Geo<C>::T;
+                                            const SlotsN<SPT>& q, float* red, float* __restrict__ seg_max) {
+  constexpr int T = Geo<C, SPT>::T;
   const int l0 = tab.l0[k];
   const int l1 = tab.l1[k];
   const int sb = tab.seg[k];
@@ -377,7 +386,7 @@ __device__ __forceinline__ void segment_max(const DevTable& tab, int64_t k, int6
     const int64_t hi = tab.off[l + 1] - base;
     float mx = -__builtin_inff();
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < SPT; ++a)
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int j = 4 * ((int)threadIdx.x + T * a) + c;
@@ -482,7 +491,7 @@ k_decompress(int64_t k0, int64_t n, const uint32_t* __restrict__ bits,
 //   PF:  worker w+1's gradient and error are loaded before worker w's chunk
 //        reduction, so they are in flight across its barrier.
 //   WPE: minimum waves per SIMD the register allocation must allow.
-template <int C, bool TAIL, bool NT, bool PF>
+template <int C, bool TAIL, bool NT, bool PF, int SPT>
 __device__ __forceinline__ void pass_a_chunk(int64_t kk, const DevTable& tab, int W,
                                              const Workers& wk, float* __restrict__ err_s,
                                              const float* __restrict__ m,
@@ -498,46 +507,46 @@ __device__ __forceinline__ void pass_a_chunk(int64_t kk, const DevTable& tab, in
   const int nk = ch.nk;
   const int t = threadIdx.x;
 
-  Slots bm, acc;
-  Slots gn, en;  // the next worker's gradient and error (PF)
+  SlotsN<SPT> bm, acc;
+  SlotsN<SPT> gn, en;  // the next worker's gradient and error (PF)
   if constexpr (PF) {
-    load_chunk<C, TAIL, NT>(wk.g[0], base, nk, gn);
-    load_chunk<C, TAIL, NT>(wk.e[0], base, nk, en);
+    load_chunk<C, TAIL, NT, SPT>(wk.g[0], base, nk, gn);
+    load_chunk<C, TAIL, NT, SPT>(wk.e[0], base, nk, en);
   }
-  load_chunk<C, TAIL, NT>(m, base, nk, bm);
+  load_chunk<C, TAIL, NT, SPT>(m, base, nk, bm);
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < SPT; ++a)
 #pragma unroll
     for (int c = 0; c < 4; ++c) bm[a][c] = cf.beta1 * bm[a][c];
 
   for (int w = 0; w < W; ++w) {
-    Slots z, e;
+    SlotsN<SPT> z, e;
     if constexpr (PF) {
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+      for (int a = 0; a < SPT; ++a)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           z[a][c] = gn[a][c];
           e[a][c] = en[a][c];
         }
       if (w + 1 < W) {
-        load_chunk<C, TAIL, NT>(wk.g[w + 1], base, nk, gn);
-        load_chunk<C, TAIL, NT>(wk.e[w + 1], base, nk, en);
+        load_chunk<C, TAIL, NT, SPT>(wk.g[w + 1], base, nk, gn);
+        load_chunk<C, TAIL, NT, SPT>(wk.e[w + 1], base, nk, en);
       }
     } else {
-      load_chunk<C, TAIL, NT>(wk.g[w], base, nk, z);
-      load_chunk<C, TAIL, NT>(wk.e[w], base, nk, e);
+      load_chunk<C, TAIL, NT, SPT>(wk.g[w], base, nk, z);
+      load_chunk<C, TAIL, NT, SPT>(wk.e[w], base, nk, e);
     }
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < SPT; ++a)
 #pragma unroll
       for (int c = 0; c < 4; ++c) z[a][c] = (bm[a][c] + (cf.a1 * z[a][c])) + e[a][c];
-    uint32_t nib[4];
-    const float s = compress_slots<C, TAIL>(z, nk, lds, parity, nib);
-    store_chunk<C, TAIL, NT>(wk.e[w], base, nk, z);
-    if (wk.bits[w]) store_sign_words<C>(wk.bits[w] + ch.k * Geo<C>::WORDS, nib);
+    uint32_t nib[SPT];
+    const float s = compress_slots<C, TAIL, SPT>(z, nk, lds, parity, nib);
+    store_chunk<C, TAIL, NT, SPT>(wk.e[w], base, nk, z);
+    if (wk.bits[w]) store_sign_words<C, SPT>(wk.bits[w] + ch.k * Geo<C>::WORDS, nib);
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < SPT; ++a)
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const float sv = signed_scale(nib, a, c, s);
@@ -550,22 +559,22 @@ __device__ __forceinline__ void pass_a_chunk(int64_t kk, const DevTable& tab, in
   }
 
   // server: average of the workers' values, add its error, recompress
-  Slots y;
-  load_chunk<C, TAIL, NT>(err_s, base, nk, y);
+  SlotsN<SPT> y;
+  load_chunk<C, TAIL, NT, SPT>(err_s, base, nk, y);
   const float fW = (float)W;
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < SPT; ++a)
 #pragma unroll
     for (int c = 0; c < 4; ++c) y[a][c] = (acc[a][c] / fW) + y[a][c];
-  Slots vf, vz;
+  SlotsN<SPT> vf, vz;
   if constexpr (PF) {  // in flight across the server's reduction
-    load_chunk<C, TAIL, NT>(v_fresh, base, nk, vf);
-    load_chunk<C, TAIL, NT>(v_frozen, base, nk, vz);
+    load_chunk<C, TAIL, NT, SPT>(v_fresh, base, nk, vf);
+    load_chunk<C, TAIL, NT, SPT>(v_frozen, base, nk, vz);
   }
-  uint32_t nib[4];
-  const float s2 = compress_slots<C, TAIL>(y, nk, lds, parity, nib);
-  store_chunk<C, TAIL, NT>(err_s, base, nk, y);
-  store_sign_words<C>(bits_s + ch.k * Geo<C>::WORDS, nib);
+  uint32_t nib[SPT];
+  const float s2 = compress_slots<C, TAIL, SPT>(y, nk, lds, parity, nib);
+  store_chunk<C, TAIL, NT, SPT>(err_s, base, nk, y);
+  store_sign_words<C, SPT>(bits_s + ch.k * Geo<C>::WORDS, nib);
   if (t == 0) {
     scales_s[ch.k] = s2;
     if (!__builtin_isfinite(s2)) flag(status, 2);
@@ -573,11 +582,11 @@ __device__ __forceinline__ void pass_a_chunk(int64_t kk, const DevTable& tab, in
 
   // reconstructed gradient, fresh variance, rescale ratio
   if constexpr (!PF) {
-    load_chunk<C, TAIL, NT>(v_fresh, base, nk, vf);
-    load_chunk<C, TAIL, NT>(v_frozen, base, nk, vz);
+    load_chunk<C, TAIL, NT, SPT>(v_fresh, base, nk, vf);
+    load_chunk<C, TAIL, NT, SPT>(v_frozen, base, nk, vz);
   }
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < SPT; ++a)
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const float mh = signed_scale(nib, a, c, s2);
@@ -585,29 +594,29 @@ __device__ __forceinline__ void pass_a_chunk(int64_t kk, const DevTable& tab, in
       vf[a][c] = (cf.beta2 * vf[a][c]) + (cf.a2 * (gh * gh));
       vz[a][c] = (__builtin_sqrtf(vz[a][c]) + cf.eta) / (__builtin_sqrtf(vf[a][c]) + cf.eta);
     }
-  store_chunk<C, TAIL, NT>(v_fresh, base, nk, vf);
-  segment_max<C>(tab, ch.k, base, nk, vz, red, seg_max);  // vz now holds the ratio q
+  store_chunk<C, TAIL, NT, SPT>(v_fresh, base, nk, vf);
+  segment_max<C, SPT>(tab, ch.k, base, nk, vz, red, seg_max);  // vz now holds the ratio q
 }
 
 
 // One workgroup per chunk; when the buffer ends in a partial chunk, block 0
 // takes it (its guarded code is slower, so it starts first and overlaps the
 // full chunks instead of trailing them).
-template <int C, bool NT = false, bool PF = false, int WPE = 1>
-__global__ void __launch_bounds__(C / 16, WPE)
+template <int C, bool NT = false, bool PF = false, int WPE = 1, int SPT = 4>
+__global__ void __launch_bounds__((Geo<C, SPT>::T), WPE)
 k_compressed_pass_a(int64_t n_full, DevTable tab, int W, Workers wk, float* __restrict__ err_s,
                     const float* __restrict__ m, const float* __restrict__ v_frozen,
                     float* __restrict__ v_fresh, uint32_t* __restrict__ bits_s,
                     float* __restrict__ scales_s, float* __restrict__ seg_max, Coef cf,
                     int32_t* status) {
-  __shared__ float4 lds[2 * Geo<C>::T];
-  __shared__ float red[Geo<C>::T / 64];
+  __shared__ float4 lds[2 * Geo<C, SPT>::T];
+  __shared__ float red[Geo<C, SPT>::T / 64];
   const int64_t has_tail = tab.K - n_full;
   if (has_tail && blockIdx.x == 0)
-    pass_a_chunk<C, true, NT, PF>(n_full, tab, W, wk, err_s, m, v_frozen, v_fresh, bits_s, scales_s,
+    pass_a_chunk<C, true, NT, PF, SPT>(n_full, tab, W, wk, err_s, m, v_frozen, v_fresh, bits_s, scales_s,
                                   seg_max, cf, status, lds, red);
   else
-    pass_a_chunk<C, false, NT, PF>((int64_t)blockIdx.x - has_tail, tab, W, wk, err_s, m, v_frozen,
+    pass_a_chunk<C, false, NT, PF, SPT>((int64_t)blockIdx.x - has_tail, tab, W, wk, err_s, m, v_frozen,
                                    v_fresh, bits_s, scales_s, seg_max, cf, status, lds, red);
 }
 
