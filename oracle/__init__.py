@@ -45,9 +45,13 @@ def lib():
         _lib.oracle_freeze.argtypes = [i32, i64, i32, P, P, P, P, P, i32, P, P]
         _lib.oracle_compressed_step.argtypes = [i32, P, i32, i32, P, P, P, P, P, P, P, P, P, P, P,
                                                 P, P, P, ctypes.POINTER(HParams), i32]
+        _lib.oracle_adam_warmup_step.argtypes = [i64, i32, P, P, P, P, ctypes.POINTER(HParams)]
+        _lib.oracle_adam_compressed_step.argtypes = [i64, i32, i32, P, P, P, P, P, P, P, P, P, P,
+                                                     ctypes.POINTER(HParams), i32]
         for f in ("oracle_compress_ef", "oracle_decompress", "oracle_average",
                   "oracle_average_packed", "oracle_warmup_step", "oracle_freeze",
-                  "oracle_compressed_step"):
+                  "oracle_compressed_step", "oracle_adam_warmup_step",
+                  "oracle_adam_compressed_step"):
             getattr(_lib, f).restype = None
     return _lib
 
@@ -155,3 +159,27 @@ def compressed_step(numels, C, grads, err_w, err_s, x, m, v_frozen, v_fresh, c_a
         ctypes.byref(hp), compressor)
     return {"c": c_out, "bits_w": bits_w, "scales_w": scales_w, "bits_s": bits_s,
             "scales_s": scales_s}
+
+
+def adam_warmup_step(grads, x, m, v, hp):
+    """1-bit Adam's warmup: one Adam step; x, m, v updated in place."""
+    lib().oracle_adam_warmup_step(x.size, len(grads), _ptr_array([_f32(g) for g in grads]),
+                                  _ptr(_f32(x)), _ptr(_f32(m)), _ptr(_f32(v)), ctypes.byref(hp))
+
+
+def adam_compressed_step(C, grads, err_w, err_s, x, m, v_frozen, hp, compressor=ONEBIT):
+    """1-bit Adam's compression-stage step; state updated in place.  Returns
+    the workers' and the server's packed signs and scales."""
+    n = x.size
+    W = len(grads)
+    K = num_chunks(n, C)
+    bits_w = [np.zeros(K * C // 32, np.uint32) for _ in range(W)]
+    scales_w = [np.zeros(K, np.float32) for _ in range(W)]
+    bits_s = np.zeros(K * C // 32, np.uint32)
+    scales_s = np.zeros(K, np.float32)
+    lib().oracle_adam_compressed_step(
+        n, C, W, _ptr_array([_f32(g) for g in grads]), _ptr_array([_f32(e) for e in err_w]),
+        _ptr(_f32(err_s)), _ptr(_f32(x)), _ptr(_f32(m)), _ptr(_f32(v_frozen)),
+        _ptr_array(bits_w), _ptr_array(scales_w), _ptr(bits_s), _ptr(scales_s), ctypes.byref(hp),
+        compressor)
+    return {"bits_w": bits_w, "scales_w": scales_w, "bits_s": bits_s, "scales_s": scales_s}

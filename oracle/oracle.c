@@ -45,6 +45,13 @@
  *       f_prev_l = f; c_l = c_avg_l (*) f          stabilized soft thresholds
  *   C11 x_i = x_i (-) ((gamma (*) c_l) (*) (mhat_i (/) (sqrt(v_frozen,i) (+) eta)));
  *       m_i = mhat_i
+ *
+ * 1-bit Adam (the 1-bit Adam page's abstract; 1-bit LAMB's Related Work):
+ *   warmup  W1-W4 as above, then x_i = x_i (-) (gamma (*) u_i)  (plain Adam,
+ *           no layerwise coefficient)
+ *   compression  C1-C6 as above, then
+ *           x_i = x_i (-) (gamma (*) (mhat_i (/) (sqrt(v_frozen,i) (+) eta)));
+ *           m_i = mhat_i          (frozen variance, no rescale)
  */
 #include "oracle.h"
 
@@ -304,6 +311,87 @@ void oracle_compressed_step(int32_t L, const int64_t* numels, int32_t C, int32_t
 
   free(c);
   free(rho);
+  free(in);
+  free(mhat);
+}
+
+/* ---- 1-bit Adam ------------------------------------------------------ */
+
+void oracle_adam_warmup_step(int64_t n, int32_t W, const float* const* grads, float* x, float* m,
+                             float* v, const oracle_hparams* hp) {
+  const float a1 = 1.0f - hp->beta1;
+  const float a2 = 1.0f - hp->beta2;
+  /* W1-W3 */
+  for (int64_t i = 0; i < n; ++i) {
+    float gsum = grads[0][i];
+    for (int32_t w = 1; w < W; ++w) gsum = gsum + grads[w][i];
+    const float gmean = gsum / (float)W;
+    m[i] = (hp->beta1 * m[i]) + (a1 * gmean);
+    v[i] = (hp->beta2 * v[i]) + (a2 * (gmean * gmean));
+  }
+  /* W4 and the Adam update */
+  for (int64_t i = 0; i < n; ++i) {
+    const float u = m[i] / (sqrtf(v[i]) + hp->eta);
+    x[i] = x[i] - (hp->lr * u);
+  }
+}
+
+void oracle_adam_compressed_step(int64_t n, int32_t C, int32_t W, const float* const* grads,
+                                 float* const* err_w, float* err_s, float* x, float* m,
+                                 const float* v_frozen, uint32_t* const* bits_w,
+                                 float* const* scales_w, uint32_t* bits_s, float* scales_s,
+                                 const oracle_hparams* hp, int32_t compressor) {
+  const float a1 = 1.0f - hp->beta1;
+  const int64_t K = num_chunks(n, C);
+  const size_t nbuf = (size_t)(n > 0 ? n : 1);
+  float* mhat = (float*)xmalloc(sizeof(float) * nbuf);
+  float* in = (float*)xmalloc(sizeof(float) * nbuf);
+
+  if (compressor == ORACLE_IDENTITY) {
+    for (int64_t i = 0; i < n; ++i) {
+      float acc = 0.0f;
+      for (int32_t w = 0; w < W; ++w) {
+        const float z = ((hp->beta1 * m[i]) + (a1 * grads[w][i])) + err_w[w][i];
+        acc = w == 0 ? z : acc + z;
+      }
+      mhat[i] = (acc / (float)W) + err_s[i];
+    }
+  } else {
+    uint32_t** bw = (uint32_t**)xmalloc(sizeof(uint32_t*) * (size_t)W);
+    float** sw = (float**)xmalloc(sizeof(float*) * (size_t)W);
+    for (int32_t w = 0; w < W; ++w) {
+      bw[w] = bits_w && bits_w[w] ? bits_w[w]
+                                  : (uint32_t*)xmalloc(sizeof(uint32_t) * (size_t)(K * C / 32 + 1));
+      sw[w] = scales_w && scales_w[w] ? scales_w[w] : (float*)xmalloc(sizeof(float) * (size_t)(K + 1));
+    }
+    uint32_t* bs = bits_s ? bits_s : (uint32_t*)xmalloc(sizeof(uint32_t) * (size_t)(K * C / 32 + 1));
+    float* ss = scales_s ? scales_s : (float*)xmalloc(sizeof(float) * (size_t)(K + 1));
+
+    /* C1-C4, worker by worker */
+    for (int32_t w = 0; w < W; ++w) {
+      const float* gw = grads[w];
+      for (int64_t i = 0; i < n; ++i) in[i] = (hp->beta1 * m[i]) + (a1 * gw[i]);
+      oracle_compress_ef(n, C, in, err_w[w], bw[w], sw[w]);
+    }
+    /* C5-C6 */
+    oracle_average_packed(n, C, W, (const uint32_t* const*)bw, (const float* const*)sw, err_s, bs, ss);
+    oracle_decompress(n, C, bs, ss, mhat);
+
+    for (int32_t w = 0; w < W; ++w) {
+      if (!(bits_w && bits_w[w])) free(bw[w]);
+      if (!(scales_w && scales_w[w])) free(sw[w]);
+    }
+    if (!bits_s) free(bs);
+    if (!scales_s) free(ss);
+    free(bw);
+    free(sw);
+  }
+
+  /* momentum SGD preconditioned by the frozen variance */
+  for (int64_t i = 0; i < n; ++i) {
+    x[i] = x[i] - (hp->lr * (mhat[i] / (sqrtf(v_frozen[i]) + hp->eta)));
+    m[i] = mhat[i];
+  }
   free(in);
   free(mhat);
 }

@@ -46,6 +46,18 @@ MUTATIONS = {
                         "v[i] = (hp->beta2 * v[i]) + (a2 * gbar);"),
     "gradient_sum_not_mean": ("const float gbar = gsum / (float)W;", "const float gbar = gsum;"),
     "freeze_keeps_errors": ("for (int64_t i = 0; i < N; ++i) err_s[i] = 0.0f;", ""),
+    "adam_momentum_undamped": ("m[i] = (hp->beta1 * m[i]) + (a1 * gmean);",
+                               "m[i] = (hp->beta1 * m[i]) + gmean;"),
+    "adam_variance_linear": ("v[i] = (hp->beta2 * v[i]) + (a2 * (gmean * gmean));",
+                             "v[i] = (hp->beta2 * v[i]) + (a2 * gmean);"),
+    "adam_eta_inside_sqrt": ("const float u = m[i] / (sqrtf(v[i]) + hp->eta);",
+                             "const float u = m[i] / sqrtf(v[i] + hp->eta);"),
+    "adam_worker_input_no_momentum": ("in[i] = (hp->beta1 * m[i]) + (a1 * gw[i]);",
+                                      "in[i] = a1 * gw[i];"),
+    "adam_update_with_old_momentum": (
+        "x[i] = x[i] - (hp->lr * (mhat[i] / (sqrtf(v_frozen[i]) + hp->eta)));",
+        "x[i] = x[i] - (hp->lr * (m[i] / (sqrtf(v_frozen[i]) + hp->eta)));"),
+    "adam_momentum_not_replaced": ("    m[i] = mhat[i];\n  }\n  free(in);", "  }\n  free(in);"),
 }
 
 

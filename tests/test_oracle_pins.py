@@ -490,3 +490,117 @@ def test_p4_server_error_feedback():
     bound = np.spacing(np.abs(rhs).astype(np.float32)) + np.spacing(np.abs(e_out))
     assert np.all(np.abs(lhs - rhs) <= bound)
     assert np.max(np.abs(e_out)) > 0
+
+
+# ---------------------------------------------------------------------------
+# P14 1-bit Adam warmup = textbook Adam (torch.optim.Adam, fp64) with its
+#     bias correction folded into a per-step learning rate and epsilon
+# ---------------------------------------------------------------------------
+def _torch_adam_steps(x0, grads_per_step, b1, b2, lr, eta):
+    import torch
+    p = torch.nn.Parameter(torch.tensor(x0, dtype=torch.float64))
+    opt = torch.optim.Adam([p], lr=lr, betas=(b1, b2), eps=eta, foreach=False)
+    for t, g in enumerate(grads_per_step, start=1):
+        bc1, bc2 = 1 - b1 ** t, 1 - b2 ** t
+        # torch divides by bc1 and sqrt(bc2); undo both so the step is
+        # lr * m / (sqrt(v) + eta) with the raw moments
+        opt.param_groups[0]["lr"] = lr * bc1 / math.sqrt(bc2)
+        opt.param_groups[0]["eps"] = eta / math.sqrt(bc2)
+        p.grad = torch.tensor(g, dtype=torch.float64)
+        opt.step()
+    st = opt.state[p]
+    return p.detach().numpy(), st["exp_avg"].numpy(), st["exp_avg_sq"].numpy()
+
+
+@pytest.mark.parametrize("eta", [1e-8, 1e-5])
+def test_p14_adam_warmup_is_textbook_adam(eta):
+    n, W, T = 6000, 3, 5
+    r = rng(30)
+    h = hp(eta=eta, lr=1e-3)
+    b1, b2 = float(np.float32(0.9)), float(np.float32(0.999))
+    x0 = f32(r.standard_normal(n) * 0.02)
+    x, m, v = x0.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)
+    gbars = []
+    for _ in range(T):
+        g = [f32(r.standard_normal(n) * 1e-3) for _ in range(W)]
+        oracle.adam_warmup_step(g, x, m, v, h)
+        gbars.append(np.mean([gi.astype(np.float64) for gi in g], axis=0))
+    xd, md, vd = _torch_adam_steps(x0.astype(np.float64), gbars, b1, b2, 1e-3, float(np.float32(eta)))
+    assert np.max(np.abs(m - md)) <= 1e-5 * np.max(np.abs(md))
+    assert np.max(np.abs(v - vd)) <= 1e-5 * np.max(np.abs(vd))
+    # parameters: T roundings of x plus a small relative error on each step
+    assert np.all(np.abs(x - xd) <= T * (U * np.abs(xd) + 1e-5 * 1e-3 * 4))
+    assert np.max(np.abs(x - x0)) > 1e-4          # it moved
+
+
+# ---------------------------------------------------------------------------
+# P15 1-bit Adam compression stage with the identity compressor = momentum
+#     SGD under the fixed preconditioner diag(1 / (sqrt(v_frozen) + eta))
+#     (torch.optim.SGD, fp64, in the coordinates m / d, g / d)
+# ---------------------------------------------------------------------------
+def test_p15_adam_identity_compressor_is_preconditioned_momentum_sgd():
+    import torch
+    n, W, T = 5000, 3, 5
+    r = rng(31)
+    h = hp(eta=1e-4, lr=1e-2)
+    b1 = float(np.float32(0.9))
+    a1 = float(np.float32(1) - np.float32(0.9))
+    x = f32(r.standard_normal(n) * 0.02)
+    x0 = x.astype(np.float64)
+    m = f32(r.standard_normal(n) * 1e-3)
+    vfz = f32(r.uniform(1e-8, 1e-5, n))
+    d = np.sqrt(vfz.astype(np.float64)) + float(np.float32(1e-4))
+    err_w = [np.zeros(n, np.float32) for _ in range(W)]
+    err_s = np.zeros(n, np.float32)
+    p = torch.nn.Parameter(torch.tensor(x, dtype=torch.float64))
+    opt = torch.optim.SGD([p], lr=float(np.float32(1e-2)), momentum=b1, dampening=1 - a1,
+                          foreach=False)
+    opt.state[p]["momentum_buffer"] = torch.tensor(m.astype(np.float64) / d)
+    for _ in range(T):
+        g = [f32(r.standard_normal(n) * 1e-3) for _ in range(W)]
+        oracle.adam_compressed_step(4096, g, err_w, err_s, x, m, vfz, h, compressor=oracle.IDENTITY)
+        gbar = np.mean([gi.astype(np.float64) for gi in g], axis=0)
+        p.grad = torch.tensor(gbar / d)
+        opt.step()
+    xd = p.detach().numpy()
+    md = opt.state[p]["momentum_buffer"].numpy() * d
+    assert np.max(np.abs(m - md)) <= 1e-5 * np.max(np.abs(md))
+    # T roundings of x plus a small relative error on the distance moved
+    assert np.all(np.abs(x - xd) <= T * U * np.abs(xd) + 1e-5 * np.max(np.abs(xd - x0)))
+    assert np.max(np.abs(xd - x0)) > 1e-3          # it moved
+    assert all(np.all(e == 0) for e in err_w) and np.all(err_s == 0)
+
+
+# ---------------------------------------------------------------------------
+# P16 1-bit Adam with chunks of constant magnitude (4^k valid elements): the
+#     1-bit operator is exact there (sqrt of a rounded square is the value;
+#     power-of-two sums of equal terms are exact), so the 1-bit step equals
+#     the identity-compressor step bit for bit, with zero errors
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("W", [1, 2])
+@pytest.mark.parametrize("carrier", ["momentum", "gradient"])
+def test_p16_adam_exact_compression_matches_identity(W, carrier):
+    C = 4096
+    n = 2 * C + 1024
+    r = rng(32 + W)
+    mags = f32(np.exp(r.uniform(-8, -3, 3)))
+    signs = np.where(r.random(n) < 0.5, -1.0, 1.0).astype(np.float32)
+    pattern = f32(signs * np.repeat(mags, [C, C, 1024]))
+    h = hp(eta=1e-6, lr=1e-2)
+    vfz = f32(r.uniform(1e-8, 1e-5, n))
+    x0 = f32(r.standard_normal(n) * 0.02)
+    if carrier == "momentum":
+        m0, g = pattern, [np.zeros(n, np.float32) for _ in range(W)]
+    else:
+        m0, g = np.zeros(n, np.float32), [pattern.copy() for _ in range(W)]
+    res = []
+    for comp in (oracle.ONEBIT, oracle.IDENTITY):
+        x, m = x0.copy(), m0.copy()
+        err_w = [np.zeros(n, np.float32) for _ in range(W)]
+        err_s = np.zeros(n, np.float32)
+        oracle.adam_compressed_step(C, g, err_w, err_s, x, m, vfz, h, compressor=comp)
+        res.append((x, m, err_w, err_s))
+    (x1, m1, ew1, es1), (x2, m2, _, _) = res
+    assert np.array_equal(x1, x2) and np.array_equal(m1, m2)
+    assert all(np.all(e == 0) for e in ew1) and np.all(es1 == 0)
+    assert np.max(np.abs(x1 - x0)) > 0
