@@ -51,20 +51,31 @@ def phase1_bytes(N, K, C, W):
     return N * (12 * W + 24) + packed
 
 
-def cpu_baseline(wl, n_chunks):
+def adam_bytes(N, K, C, W):
+    """Algorithmic bytes of the fused 1-bit Adam compression kernel: m read
+    and written; per worker g read, e read and written; e_s read and written;
+    v_frozen read; x read and written; (W+1) packed sign arrays and scales
+    written."""
+    packed = (W + 1) * K * (C // 8 + 4)
+    return N * (12 * W + 28) + packed
+
+
+def cpu_baseline(wl, n_chunks, method="lamb"):
     """The oracle (single-threaded C, as it stands) on the window of the
     first n_chunks chunks of the workload: one compression step."""
-    import numpy as np
     from tests.harness import HostRun
     hi = min(wl.N, n_chunks * wl.chunk)
     h = HostRun(wl, 0, hi)
     h.fill_grads(0)
     t0 = time.perf_counter()
-    h.compressed_step(0, fill=False)
+    if method == "adam":
+        h.adam_compressed_step(0, fill=False)
+    else:
+        h.compressed_step(0, fill=False)
     dt = time.perf_counter() - t0
-    del np
+    what = "1-bit Adam" if method == "adam" else "1-bit LAMB"
     return {"value": hi / dt, "unit": "params/s", "cores": 1, "kind": "oracle",
-            "sample": f"one compression step on elements [0, {hi}) of the {wl.name} table "
+            "sample": f"one {what} compression step on elements [0, {hi}) of the {wl.name} table "
                       f"(first {hi // wl.chunk} chunks, W={wl.W}); {dt:.2f} s"}
 
 
@@ -74,6 +85,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="bert_large")
+    ap.add_argument("--method", choices=("lamb", "adam"), default="lamb",
+                    help="1-bit LAMB (the default) or the 1-bit Adam mode on the same buffers")
     ap.add_argument("--cpu-chunks", type=int, default=12288,
                     help="chunks of the workload the CPU oracle baseline runs (0 = skip)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -142,6 +155,10 @@ def main():
 
     stream = torch.cuda.current_stream()
 
+    if args.method == "adam":
+        return bench_adam(args, wl, ob, torch, hp, g, e, err_s, x, m, v, bits_w, scales_w, bits_s,
+                          scales_s, status, stream)
+
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
@@ -194,7 +211,8 @@ def main():
     abytes = phase1_bytes(N, K, C, W)
     achieved = abytes / (p1_ms * 1e-3) / 1e9
     step_gbps = sbytes / (ms_per_step * 1e-3) / 1e9
-    traffic = _measured_traffic() if wl.name == "bert_large" else None
+    traffic = _measured_traffic("traffic_compress_average_bert_large.txt") \
+        if wl.name == "bert_large" else None
     cpu = None
     if args.cpu_chunks > 0:
         log("[bench] CPU oracle baseline ...")
@@ -232,6 +250,86 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+def bench_adam(args, wl, ob, torch, hp, g, e, err_s, x, m, v, bits_w, scales_w, bits_s, scales_s,
+               status, stream):
+    """The 1-bit Adam mode on the same table, flattened: one fused kernel per
+    compression step (v is the frozen variance)."""
+    C, N, W, K = wl.chunk, wl.N, wl.W, wl.K
+
+    def step():
+        ob.onebit_adam_compressed_step(N, C, W, g, e, err_s, x, m, v, bits_w, scales_w, bits_s,
+                                       scales_s, hp, status, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for _ in range(args.steps):
+        step()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    if int(status.item()):
+        log(f"[bench] WARNING: status flags {int(status.item())}")
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    k_ms = ev[0].elapsed_time(ev[1]) / args.steps
+    log(f"[bench] adam {args.steps} steps: {ms_per_step:.3f} ms/step (kernel {k_ms:.3f} ms)")
+
+    for _ in range(2):
+        ob.onebit_adam_warmup_step(N, W, g, x, m, v, hp, stream)
+    wev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    wsteps = 5
+    wev[0].record(stream)
+    for _ in range(wsteps):
+        ob.onebit_adam_warmup_step(N, W, g, x, m, v, hp, stream)
+    wev[1].record(stream)
+    torch.cuda.synchronize()
+    warm_ms = wev[0].elapsed_time(wev[1]) / wsteps
+    warm_bytes = N * (4 * W + 24)
+
+    abytes = adam_bytes(N, K, C, W)
+    achieved = abytes / (k_ms * 1e-3) / 1e9
+    traffic = _measured_traffic("traffic_adam_compressed_bert_large.txt") \
+        if wl.name == "bert_large" else None
+    cpu = None
+    if args.cpu_chunks > 0:
+        log("[bench] CPU oracle baseline ...")
+        cpu = cpu_baseline(wl, args.cpu_chunks, "adam")
+        log(f"[bench] oracle: {cpu['value']:.3e} params/s ({cpu['sample']})")
+    step_gbps = abytes / (ms_per_step * 1e-3) / 1e9
+    out = {
+        "metric": "params/sec and achieved HBM GB/s (% of peak) per 1-bit Adam step",
+        "value": N / (ms_per_step * 1e-3),
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name} (flattened): 1-bit Adam compression-stage step, "
+                               f"N={N}, W={W} simulated workers, chunk {C}",
+                   "N": N, "W": W, "chunk": C},
+        "achieved_GBps": step_gbps,
+        "frac_of_peak": step_gbps / PEAK_HBM_GBPS,
+        "step_bytes": abytes,
+        "warmup_step": {"ms": warm_ms, "params_per_s": N / (warm_ms * 1e-3),
+                        "GBps": warm_bytes / (warm_ms * 1e-3) / 1e9, "bytes": warm_bytes},
+        "roofline": {"bound": "hbm", "kernel": "k_adam_compressed<4096>",
+                     "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
+                     "algorithmic_bytes": abytes},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def _kernel_sha():
     import hashlib
     h = hashlib.sha256()
@@ -242,10 +340,10 @@ def _kernel_sha():
     return h.hexdigest()[:16]
 
 
-def _measured_traffic():
-    """HBM bytes per phase-1 launch from the committed counter summary, or
-    None if the kernels changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", "traffic_compress_average_bert_large.txt")
+def _measured_traffic(name):
+    """HBM bytes per launch of the dominant kernel from a committed counter
+    summary, or None if the kernels changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     vals = {}

@@ -63,6 +63,10 @@ _lib.onebit_lamb_compress_average.argtypes = [_P, _i32, _P, _P, _P, _P, _P, _P, 
 _lib.onebit_lamb_rescale_update.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P,
                                             ctypes.POINTER(onebit_hparams), _P, _P, _P]
 _lib.onebit_decompress.argtypes = [_i64, _i32, _P, _P, _P, _P]
+_lib.onebit_adam_warmup_step.argtypes = [_i64, _i32, _P, _P, _P, _P, ctypes.POINTER(onebit_hparams),
+                                         _P]
+_lib.onebit_adam_compressed_step.argtypes = [_i64, _i32, _i32, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                             _P, ctypes.POINTER(onebit_hparams), _P, _P]
 _lib.onebit_last_error.restype = ctypes.c_char_p
 _lib.onebit_version.restype = ctypes.c_char_p
 for _f in ("onebit_layer_table_create", "onebit_layer_table_destroy", "onebit_layer_table_info",
@@ -234,3 +238,18 @@ def onebit_lamb_rescale_update(table, bits_s, scales_s, x, m, v_frozen, c_avg, f
 def onebit_decompress(n, chunk, bits, scales, out, stream=None):
     _check(_lib.onebit_decompress(n, chunk, _ptr(bits), _ptr(scales), _ptr(out), _stream(stream)),
            "onebit_decompress")
+
+
+def onebit_adam_warmup_step(n, W, grads, x, m, v, hp, stream=None):
+    _check(_lib.onebit_adam_warmup_step(n, W, _ptr_list(grads), _ptr(x), _ptr(m), _ptr(v),
+                                        ctypes.byref(hp), _stream(stream)),
+           "onebit_adam_warmup_step")
+
+
+def onebit_adam_compressed_step(n, chunk, W, grads, err_w, err_s, x, m, v_frozen, bits_w,
+                                scales_w, bits_s, scales_s, hp, status=None, stream=None):
+    _check(_lib.onebit_adam_compressed_step(
+        n, chunk, W, _ptr_list(grads), _ptr_list(err_w), _ptr(err_s), _ptr(x), _ptr(m),
+        _ptr(v_frozen), _ptr_list(bits_w), _ptr_list(scales_w), _ptr(bits_s), _ptr(scales_s),
+        ctypes.byref(hp), _ptr(status), _stream(stream)),
+        "onebit_adam_compressed_step")

@@ -166,6 +166,16 @@ constexpr int kPassA_WPE = 6;      // minimum waves per SIMD
 constexpr int kPassA_SPT = 4;      // float4 slots per thread (workgroup = C / (4 * SPT))
 constexpr bool kPassB_NT = true;
 
+// The 1-bit Adam compression kernel shares pass A's compressed allreduce and
+// takes the same settings.
+constexpr bool kAdam_NT = true;
+constexpr bool kAdam_PF = false;
+constexpr int kAdam_WPE = 6;
+constexpr int kAdam_SPT = 4;
+// Chunk geometry of the element-wise 1-bit Adam warmup kernel (any chunk
+// gives the same result; this one gives 256-thread workgroups).
+constexpr int kAdamWarmupChunk = 4096;
+
 template <int C>
 struct LaunchCompress {
   static void run(int64_t n, const float* in, float* err, uint32_t* bits, float* scales,
@@ -227,6 +237,18 @@ struct LaunchPassA {
 };
 
 template <int C>
+struct LaunchAdam {
+  static void run(int64_t n, int W, const Workers& wk, float* err_s, float* m, float* x,
+                  const float* v_frozen, uint32_t* bits_s, float* scales_s, const Coef& cf,
+                  int32_t* status, hipStream_t st) {
+    const int64_t K = (n + C - 1) / C;
+    hipLaunchKernelGGL((k_adam_compressed<C, kAdam_NT, kAdam_PF, kAdam_WPE, kAdam_SPT>),
+                       dim3((unsigned)K), dim3(Geo<C, kAdam_SPT>::T), 0, st, n / C, n, K, W, wk,
+                       err_s, m, x, v_frozen, bits_s, scales_s, cf, status);
+  }
+};
+
+template <int C>
 struct LaunchPassB {
   static void run(const onebit_layer_table* t, const uint32_t* bits_s, const float* scales_s,
                   float* x, float* m, const float* v_frozen, const float* c_avg, float* f_prev,
@@ -239,15 +261,9 @@ struct LaunchPassB {
   }
 };
 
-// Checks shared by the compressed-step entry points; fills wk.
-int check_phase1(const char* fn, const onebit_layer_table* table, int32_t W,
-                 const float* const* grads, float* const* err_w, float* err_s, const float* m,
-                 const float* v_frozen, float* v_fresh, uint32_t* const* bits_w,
-                 float* const* scales_w, uint32_t* bits_s, float* scales_s,
-                 const onebit_hparams* hp, void* ws, Workers& wk) {
-  if (int rc = check_table(table, fn)) return rc;
-  if (int rc = check_W(W, fn)) return rc;
-  if (int rc = check_hparams(hp, fn)) return rc;
+// The workers' arrays of a compression step; fills wk.
+int check_workers(const char* fn, int32_t W, const float* const* grads, float* const* err_w,
+                  uint32_t* const* bits_w, float* const* scales_w, Workers& wk) {
   if (!grads || !err_w) return fail(ONEBIT_EINVAL, "%s: grads or err_w is NULL", fn);
   wk = Workers{};
   for (int w = 0; w < W; ++w) {
@@ -267,6 +283,19 @@ int check_phase1(const char* fn, const onebit_layer_table* table, int32_t W,
       wk.scales[w] = scales_w[w];
     }
   }
+  return ONEBIT_OK;
+}
+
+// Checks shared by the 1-bit LAMB compressed-step entry points; fills wk.
+int check_phase1(const char* fn, const onebit_layer_table* table, int32_t W,
+                 const float* const* grads, float* const* err_w, float* err_s, const float* m,
+                 const float* v_frozen, float* v_fresh, uint32_t* const* bits_w,
+                 float* const* scales_w, uint32_t* bits_s, float* scales_s,
+                 const onebit_hparams* hp, void* ws, Workers& wk) {
+  if (int rc = check_table(table, fn)) return rc;
+  if (int rc = check_W(W, fn)) return rc;
+  if (int rc = check_hparams(hp, fn)) return rc;
+  if (int rc = check_workers(fn, W, grads, err_w, bits_w, scales_w, wk)) return rc;
   const void* req[] = {err_s, m, v_frozen, v_fresh, bits_s, scales_s, ws};
   const char* names[] = {"err_s", "m", "v_frozen", "v_fresh", "bits_s", "scales_s", "ws"};
   for (int i = 0; i < 7; ++i) {
@@ -556,6 +585,54 @@ int onebit_lamb_compressed_step(const onebit_layer_table* table, int32_t W,
                         scales_s, cf, wsv, status, st);
   by_chunk<LaunchPassB>(table->chunk, table, bits_s, scales_s, x, m, v_frozen, c_avg, f_prev, c_out,
                         cf, wsv, status, st);
+  return launch_status(__func__);
+}
+
+int onebit_adam_warmup_step(int64_t n, int32_t W, const float* const* grads, float* x, float* m,
+                            float* v, const onebit_hparams* hp, void* stream) {
+  if (n < 0) return fail(ONEBIT_EINVAL, "%s: n < 0", __func__);
+  if (int rc = check_W(W, __func__)) return rc;
+  if (int rc = check_hparams(hp, __func__)) return rc;
+  if ((n + kAdamWarmupChunk - 1) / kAdamWarmupChunk > INT32_MAX / 2)
+    return fail(ONEBIT_EUNSUPPORTED, "%s: n too large", __func__);
+  if (n == 0) return ok();
+  if (!grads) return fail(ONEBIT_EINVAL, "%s: grads is NULL", __func__);
+  Workers wk{};
+  for (int w = 0; w < W; ++w) {
+    CHECK_PTR(grads[w], "grads[w]");
+    wk.g[w] = grads[w];
+  }
+  CHECK_PTR(x, "x");
+  CHECK_PTR(m, "m");
+  CHECK_PTR(v, "v");
+  constexpr int C = kAdamWarmupChunk;
+  launch_chunks<C>(n, (hipStream_t)stream, k_adam_warmup<C, false>, k_adam_warmup<C, true>, n,
+                   (int)W, wk, x, m, v, make_coef(*hp));
+  return launch_status(__func__);
+}
+
+int onebit_adam_compressed_step(int64_t n, int32_t chunk, int32_t W, const float* const* grads,
+                                float* const* err_w, float* err_s, float* x, float* m,
+                                const float* v_frozen, uint32_t* const* bits_w,
+                                float* const* scales_w, uint32_t* bits_s, float* scales_s,
+                                const onebit_hparams* hp, int32_t* status, void* stream) {
+  if (n < 0) return fail(ONEBIT_EINVAL, "%s: n < 0", __func__);
+  if (!chunk_supported(chunk)) return fail(ONEBIT_EUNSUPPORTED, "%s: chunk %d", __func__, chunk);
+  if (int rc = check_W(W, __func__)) return rc;
+  if (int rc = check_hparams(hp, __func__)) return rc;
+  if ((n + chunk - 1) / chunk > INT32_MAX / 2)
+    return fail(ONEBIT_EUNSUPPORTED, "%s: n too large", __func__);
+  if (n == 0) return ok();
+  Workers wk;
+  if (int rc = check_workers(__func__, W, grads, err_w, bits_w, scales_w, wk)) return rc;
+  CHECK_PTR(err_s, "err_s");
+  CHECK_PTR(x, "x");
+  CHECK_PTR(m, "m");
+  CHECK_PTR(v_frozen, "v_frozen");
+  CHECK_PTR(bits_s, "bits_s");
+  CHECK_PTR(scales_s, "scales_s");
+  by_chunk<LaunchAdam>(chunk, n, (int)W, wk, err_s, m, x, v_frozen, bits_s, scales_s,
+                       make_coef(*hp), status, (hipStream_t)stream);
   return launch_status(__func__);
 }
 

@@ -480,34 +480,37 @@ k_decompress(int64_t k0, int64_t n, const uint32_t* __restrict__ bits,
   store_chunk<C, TAIL>(out, ch.base, ch.nk, o);
 }
 
-// Compression step, pass A: every worker's momentum compression, the server
-// average and recompression, the reconstructed gradient, the fresh variance
-// and the per-(chunk, tensor) maximum of the rescale ratio.
+// The compressed allreduce of one chunk's momentum: every worker's
+// error-compensated 1-bit compression of beta1*m + a1*g_w, then the server's
+// average of the W packed chunks and its own error-compensated
+// recompression.  On return bm holds beta1*m and nib the server's sign
+// nibbles; the server's scale is returned.  With PF, the chunk's slices of
+// the two arrays the caller needs next (p0, p1) are loaded into d0, d1 just
+// before the server's chunk reduction, so they are in flight across it.
 //
 // The worker loop carries beta1*m, the running sum ((+-s_0 + +-s_1) + ...)
 // of the workers' decompressed values (worker order), and the current
-// worker's values.  The kernel is HBM-bound; occupancy (WPE) is what moves it.
+// worker's values.  The kernels built on it are HBM-bound; occupancy (WPE)
+// is what moves them.
 //   NT:  streaming (nontemporal) loads and stores for the element arrays.
 //   PF:  worker w+1's gradient and error are loaded before worker w's chunk
 //        reduction, so they are in flight across its barrier.
-//   WPE: minimum waves per SIMD the register allocation must allow.
 template <int C, bool TAIL, bool NT, bool PF, int SPT>
-__device__ __forceinline__ void pass_a_chunk(int64_t kk, const DevTable& tab, int W,
-                                             const Workers& wk, float* __restrict__ err_s,
-                                             const float* __restrict__ m,
-                                             const float* __restrict__ v_frozen,
-                                             float* __restrict__ v_fresh,
-                                             uint32_t* __restrict__ bits_s,
-                                             float* __restrict__ scales_s,
-                                             float* __restrict__ seg_max, const Coef& cf,
-                                             int32_t* status, float4* lds, float* red) {
-  int parity = 0;
-  const ChunkAt<C, TAIL> ch(kk, tab.N);
+__device__ __forceinline__ float workers_and_server(const ChunkAt<C, TAIL> ch, int W,
+                                                    const Workers& wk, float* __restrict__ err_s,
+                                                    const float* __restrict__ m,
+                                                    uint32_t* __restrict__ bits_s,
+                                                    float* __restrict__ scales_s, const Coef& cf,
+                                                    int32_t* status, float4* lds, int& parity,
+                                                    SlotsN<SPT>& bm, uint32_t (&nib)[SPT],
+                                                    const float* __restrict__ p0,
+                                                    const float* __restrict__ p1,
+                                                    SlotsN<SPT>& d0, SlotsN<SPT>& d1) {
   const int64_t base = ch.base;
   const int nk = ch.nk;
   const int t = threadIdx.x;
 
-  SlotsN<SPT> bm, acc;
+  SlotsN<SPT> acc;
   SlotsN<SPT> gn, en;  // the next worker's gradient and error (PF)
   if constexpr (PF) {
     load_chunk<C, TAIL, NT, SPT>(wk.g[0], base, nk, gn);
@@ -541,15 +544,15 @@ __device__ __forceinline__ void pass_a_chunk(int64_t kk, const DevTable& tab, in
     for (int a = 0; a < SPT; ++a)
 #pragma unroll
       for (int c = 0; c < 4; ++c) z[a][c] = (bm[a][c] + (cf.a1 * z[a][c])) + e[a][c];
-    uint32_t nib[SPT];
-    const float s = compress_slots<C, TAIL, SPT>(z, nk, lds, parity, nib);
+    uint32_t wnib[SPT];
+    const float s = compress_slots<C, TAIL, SPT>(z, nk, lds, parity, wnib);
     store_chunk<C, TAIL, NT, SPT>(wk.e[w], base, nk, z);
-    if (wk.bits[w]) store_sign_words<C, SPT>(wk.bits[w] + ch.k * Geo<C>::WORDS, nib);
+    if (wk.bits[w]) store_sign_words<C, SPT>(wk.bits[w] + ch.k * Geo<C>::WORDS, wnib);
 #pragma unroll
     for (int a = 0; a < SPT; ++a)
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const float sv = signed_scale(nib, a, c, s);
+        const float sv = signed_scale(wnib, a, c, s);
         acc[a][c] = w == 0 ? sv : acc[a][c] + sv;
       }
     if (t == 0) {
@@ -566,12 +569,10 @@ __device__ __forceinline__ void pass_a_chunk(int64_t kk, const DevTable& tab, in
   for (int a = 0; a < SPT; ++a)
 #pragma unroll
     for (int c = 0; c < 4; ++c) y[a][c] = (acc[a][c] / fW) + y[a][c];
-  SlotsN<SPT> vf, vz;
-  if constexpr (PF) {  // in flight across the server's reduction
-    load_chunk<C, TAIL, NT, SPT>(v_fresh, base, nk, vf);
-    load_chunk<C, TAIL, NT, SPT>(v_frozen, base, nk, vz);
+  if constexpr (PF) {
+    load_chunk<C, TAIL, NT, SPT>(p0, base, nk, d0);
+    load_chunk<C, TAIL, NT, SPT>(p1, base, nk, d1);
   }
-  uint32_t nib[SPT];
   const float s2 = compress_slots<C, TAIL, SPT>(y, nk, lds, parity, nib);
   store_chunk<C, TAIL, NT, SPT>(err_s, base, nk, y);
   store_sign_words<C, SPT>(bits_s + ch.k * Geo<C>::WORDS, nib);
@@ -579,6 +580,32 @@ __device__ __forceinline__ void pass_a_chunk(int64_t kk, const DevTable& tab, in
     scales_s[ch.k] = s2;
     if (!__builtin_isfinite(s2)) flag(status, 2);
   }
+  return s2;
+}
+
+// 1-bit LAMB compression step, pass A: the compressed allreduce, then the
+// reconstructed gradient, the fresh variance and the per-(chunk, tensor)
+// maximum of the rescale ratio.
+template <int C, bool TAIL, bool NT, bool PF, int SPT>
+__device__ __forceinline__ void pass_a_chunk(int64_t kk, const DevTable& tab, int W,
+                                             const Workers& wk, float* __restrict__ err_s,
+                                             const float* __restrict__ m,
+                                             const float* __restrict__ v_frozen,
+                                             float* __restrict__ v_fresh,
+                                             uint32_t* __restrict__ bits_s,
+                                             float* __restrict__ scales_s,
+                                             float* __restrict__ seg_max, const Coef& cf,
+                                             int32_t* status, float4* lds, float* red) {
+  int parity = 0;
+  const ChunkAt<C, TAIL> ch(kk, tab.N);
+  const int64_t base = ch.base;
+  const int nk = ch.nk;
+
+  SlotsN<SPT> bm, vf, vz;
+  uint32_t nib[SPT];
+  const float s2 = workers_and_server<C, TAIL, NT, PF, SPT>(ch, W, wk, err_s, m, bits_s, scales_s,
+                                                            cf, status, lds, parity, bm, nib,
+                                                            v_fresh, v_frozen, vf, vz);
 
   // reconstructed gradient, fresh variance, rescale ratio
   if constexpr (!PF) {
@@ -618,6 +645,97 @@ k_compressed_pass_a(int64_t n_full, DevTable tab, int W, Workers wk, float* __re
   else
     pass_a_chunk<C, false, NT, PF, SPT>((int64_t)blockIdx.x - has_tail, tab, W, wk, err_s, m, v_frozen,
                                    v_fresh, bits_s, scales_s, seg_max, cf, status, lds, red);
+}
+
+// 1-bit Adam compression step, one pass per chunk: the compressed allreduce,
+// then x = x - lr*(mhat/(sqrt(v_frozen)+eta)) and m = mhat.  There is no
+// layerwise coefficient, so the update follows in the same pass.
+template <int C, bool TAIL, bool NT, bool PF, int SPT>
+__device__ __forceinline__ void adam_chunk(int64_t kk, int64_t n, int W, const Workers& wk,
+                                           float* __restrict__ err_s, float* __restrict__ m,
+                                           float* __restrict__ x,
+                                           const float* __restrict__ v_frozen,
+                                           uint32_t* __restrict__ bits_s,
+                                           float* __restrict__ scales_s, const Coef& cf,
+                                           int32_t* status, float4* lds) {
+  int parity = 0;
+  const ChunkAt<C, TAIL> ch(kk, n);
+  SlotsN<SPT> bm, xx, vz;
+  uint32_t nib[SPT];
+  const float s2 = workers_and_server<C, TAIL, NT, PF, SPT>(ch, W, wk, err_s, m, bits_s, scales_s,
+                                                            cf, status, lds, parity, bm, nib, x,
+                                                            v_frozen, xx, vz);
+  if constexpr (!PF) {
+    load_chunk<C, TAIL, NT, SPT>(x, ch.base, ch.nk, xx);
+    load_chunk<C, TAIL, NT, SPT>(v_frozen, ch.base, ch.nk, vz);
+  }
+#pragma unroll
+  for (int a = 0; a < SPT; ++a)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float mh = signed_scale(nib, a, c, s2);
+      xx[a][c] = xx[a][c] - (cf.lr * (mh / (__builtin_sqrtf(vz[a][c]) + cf.eta)));
+      bm[a][c] = mh;
+    }
+  store_chunk<C, TAIL, NT, SPT>(x, ch.base, ch.nk, xx);
+  store_chunk<C, TAIL, NT, SPT>(m, ch.base, ch.nk, bm);
+}
+
+// One workgroup per chunk of an n-element buffer; block 0 takes the partial
+// last chunk, if any (as in k_compressed_pass_a).
+template <int C, bool NT = false, bool PF = false, int WPE = 1, int SPT = 4>
+__global__ void __launch_bounds__((Geo<C, SPT>::T), WPE)
+k_adam_compressed(int64_t n_full, int64_t n, int64_t K, int W, Workers wk,
+                  float* __restrict__ err_s, float* __restrict__ m, float* __restrict__ x,
+                  const float* __restrict__ v_frozen, uint32_t* __restrict__ bits_s,
+                  float* __restrict__ scales_s, Coef cf, int32_t* status) {
+  __shared__ float4 lds[2 * Geo<C, SPT>::T];
+  const int64_t has_tail = K - n_full;
+  if (has_tail && blockIdx.x == 0)
+    adam_chunk<C, true, NT, PF, SPT>(n_full, n, W, wk, err_s, m, x, v_frozen, bits_s, scales_s, cf,
+                                     status, lds);
+  else
+    adam_chunk<C, false, NT, PF, SPT>((int64_t)blockIdx.x - has_tail, n, W, wk, err_s, m, x,
+                                      v_frozen, bits_s, scales_s, cf, status, lds);
+}
+
+// 1-bit Adam warmup: one Adam step, element-wise in one pass (mean gradient,
+// moments, x = x - lr*(m/(sqrt(v)+eta))).
+template <int C, bool TAIL>
+__global__ void __launch_bounds__(C / 16)
+k_adam_warmup(int64_t k0, int64_t n, int W, Workers wk, float* __restrict__ x,
+              float* __restrict__ m, float* __restrict__ v, Coef cf) {
+  const ChunkAt<C, TAIL> ch(k0 + (int64_t)blockIdx.x, n);
+  const int64_t base = ch.base;
+  const int nk = ch.nk;
+  Slots gs;
+  load_chunk<C, TAIL, true>(wk.g[0], base, nk, gs);
+  for (int w = 1; w < W; ++w) {
+    Slots g;
+    load_chunk<C, TAIL, true>(wk.g[w], base, nk, g);
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) gs[a][c] = gs[a][c] + g[a][c];
+  }
+  Slots mm, vv, xx;
+  load_chunk<C, TAIL, true>(m, base, nk, mm);
+  load_chunk<C, TAIL, true>(v, base, nk, vv);
+  load_chunk<C, TAIL, true>(x, base, nk, xx);
+  const float fW = (float)W;
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float gb = gs[a][c] / fW;
+      mm[a][c] = (cf.beta1 * mm[a][c]) + (cf.a1 * gb);
+      vv[a][c] = (cf.beta2 * vv[a][c]) + (cf.a2 * (gb * gb));
+      const float u = mm[a][c] / (__builtin_sqrtf(vv[a][c]) + cf.eta);
+      xx[a][c] = xx[a][c] - (cf.lr * u);
+    }
+  store_chunk<C, TAIL, true>(m, base, nk, mm);
+  store_chunk<C, TAIL, true>(v, base, nk, vv);
+  store_chunk<C, TAIL, true>(x, base, nk, xx);
 }
 
 // Per tensor: rho = max of its segments, soft thresholds, c.

@@ -81,6 +81,20 @@ class DevRun:
             self.c_avg, self.f_prev, self.c_out, self.bits_w, self.scales_w, self.bits_s,
             self.scales_s, self.hp, self.ws, self.status)
 
+    # -- 1-bit Adam mode: v is the (frozen) variance, vf is not used ------
+    def adam_warmup_step(self, step, fill=True):
+        if fill:
+            self.fill_grads(step)
+        self.ob.onebit_adam_warmup_step(self.wl.N, self.wl.W, self.g, self.x, self.m, self.v,
+                                        self.hp)
+
+    def adam_compressed_step(self, step, fill=True, chunk=None):
+        if fill:
+            self.fill_grads(step)
+        self.ob.onebit_adam_compressed_step(
+            self.wl.N, chunk or self.wl.chunk, self.wl.W, self.g, self.e, self.err_s, self.x, self.m,
+            self.v, self.bits_w, self.scales_w, self.bits_s, self.scales_s, self.hp, self.status)
+
     # -- window download -------------------------------------------------
     def window(self, lo, hi):
         C = self.wl.chunk
@@ -153,6 +167,17 @@ class HostRun:
                                           self.hp)
         self.c = self.out["c"]
 
+    def adam_warmup_step(self, step, fill=True):
+        if fill:
+            self.fill_grads(step)
+        oracle.adam_warmup_step(self.g, self.x, self.m, self.v, self.hp)
+
+    def adam_compressed_step(self, step, fill=True):
+        if fill:
+            self.fill_grads(step)
+        self.out = oracle.adam_compressed_step(self.wl.chunk, self.g, self.e, self.err_s, self.x,
+                                               self.m, self.v, self.hp)
+
     def load_from(self, d):
         """Adopt a downloaded GPU window (strict per-step parity)."""
         for k in ("x", "m", "v", "vf", "err_s"):
@@ -219,6 +244,32 @@ def compare_state(dev, host, d=None, stage="compression"):
     for k, hk in (("c", host.c), ("c_sum", host.c_sum), ("c_avg", host.c_avg),
                   ("f_prev", host.f_prev)):
         close(k, d[k][gl], hk[host.full])
+    return rep
+
+
+def compare_adam(dev, host, d=None):
+    """1-bit Adam: every array of the window bit for bit (there is no
+    per-tensor quantity, so x is exact on every element too)."""
+    if d is None:
+        d = dev.window(host.lo, host.hi)
+    rep = {}
+
+    def exact(name, a, b):
+        a = np.asarray(a)
+        b = np.asarray(b)
+        rep[name] = _entry(a.view(np.uint32) != b.view(np.uint32), a, b, True)
+
+    for k in ("x", "m", "v", "err_s"):
+        exact(k, d[k], getattr(host, k))
+    for w in range(host.wl.W):
+        exact(f"e{w}", d["e"][w], host.e[w])
+    if host.out is not None:
+        exact("bits_s", d["bits_s"], host.out["bits_s"])
+        exact("scales_s", d["scales_s"], host.out["scales_s"])
+        if "bits_w" in d:
+            for w in range(host.wl.W):
+                exact(f"bits_w{w}", d["bits_w"][w], host.out["bits_w"][w])
+                exact(f"scales_w{w}", d["scales_w"][w], host.out["scales_w"][w])
     return rep
 
 

@@ -27,7 +27,8 @@ def test_header_lists_the_entry_points():
     names = declared_functions()
     for fn in ("onebit_layer_table_create", "onebit_layer_table_destroy", "onebit_lamb_warmup_step",
                "onebit_lamb_freeze", "onebit_compress_ef", "onebit_average_packed",
-               "onebit_lamb_compressed_step", "onebit_decompress", "onebit_workspace_size"):
+               "onebit_lamb_compressed_step", "onebit_decompress", "onebit_workspace_size",
+               "onebit_adam_warmup_step", "onebit_adam_compressed_step"):
         assert fn in names
 
 
@@ -79,6 +80,45 @@ def test_table_checks(ob):
     hp = ob.onebit_hparams(weight_decay=0.01)
     assert lib.onebit_lamb_warmup_step(None, 1, None, None, None, None, None, None,
                                        ctypes.byref(hp), None, None, None) == ob.ONEBIT_EINVAL
+
+
+def test_adam_argument_checks(ob):
+    lib = ob._lib
+    P = ctypes.c_void_p
+    hp = ob.onebit_hparams(beta1=0.9, beta2=0.999, eta=1e-8, lr=1e-3)
+    bad_wd = ob.onebit_hparams(beta1=0.9, beta2=0.999, eta=1e-8, lr=1e-3, weight_decay=0.01)
+    g = (P * 2)(4096, 4096)
+    hpr = ctypes.byref(hp)
+    assert lib.onebit_adam_warmup_step(-1, 2, g, P(4096), P(4096), P(4096), hpr, None) == \
+        ob.ONEBIT_EINVAL
+    assert lib.onebit_adam_warmup_step(10, 0, g, P(4096), P(4096), P(4096), hpr, None) == \
+        ob.ONEBIT_EUNSUPPORTED
+    assert lib.onebit_adam_warmup_step(10, 2, g, P(4096), P(4096), P(4096), ctypes.byref(bad_wd),
+                                       None) == ob.ONEBIT_EUNSUPPORTED
+    assert lib.onebit_adam_warmup_step(10, 2, g, P(4100), P(4096), P(4096), hpr, None) == \
+        ob.ONEBIT_EALIGN
+    assert lib.onebit_adam_warmup_step(10, 2, None, P(4096), P(4096), P(4096), hpr, None) == \
+        ob.ONEBIT_EINVAL
+    assert lib.onebit_adam_warmup_step(0, 2, None, None, None, None, hpr, None) == ob.ONEBIT_OK
+    args = [g, g, P(4096), P(4096), P(4096), P(4096), None, None, P(4096), P(4096)]
+    assert lib.onebit_adam_compressed_step(10, 3000, 2, *args, hpr, None, None) == \
+        ob.ONEBIT_EUNSUPPORTED
+    assert lib.onebit_adam_compressed_step(10, 4096, 17, *args, hpr, None, None) == \
+        ob.ONEBIT_EUNSUPPORTED
+    assert lib.onebit_adam_compressed_step(-5, 4096, 2, *args, hpr, None, None) == \
+        ob.ONEBIT_EINVAL
+    bad = list(args)
+    bad[4] = None                     # m
+    assert lib.onebit_adam_compressed_step(10, 4096, 2, *bad, hpr, None, None) == ob.ONEBIT_EINVAL
+    assert "m is NULL" in ob.onebit_last_error()
+    bad = list(args)
+    bad[5] = P(4104)                  # v_frozen misaligned
+    assert lib.onebit_adam_compressed_step(10, 4096, 2, *bad, hpr, None, None) == ob.ONEBIT_EALIGN
+    bad = list(args)
+    bad[1] = (P * 2)(4096, 0)         # err_w[1] NULL
+    assert lib.onebit_adam_compressed_step(10, 4096, 2, *bad, hpr, None, None) == ob.ONEBIT_EINVAL
+    assert lib.onebit_adam_compressed_step(0, 4096, 2, *[None] * 10, hpr, None, None) == \
+        ob.ONEBIT_OK
 
 
 def test_package_refuses_to_load_without_library(tmp_path):
