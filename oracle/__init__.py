@@ -20,7 +20,8 @@ IDENTITY = 1
 class HParams(ctypes.Structure):
     _fields_ = [(name, ctypes.c_float) for name in
                 ("beta1", "beta2", "eta", "lr", "weight_decay", "c_min", "c_max", "f_min", "f_max",
-                 "kappa")]
+                 "kappa")] + [("rho_mode", ctypes.c_int32), ("c_avg_decay", ctypes.c_float),
+                              ("bias_step", ctypes.c_int32)]
 
 
 _lib = None
@@ -42,7 +43,8 @@ def lib():
         _lib.oracle_average.argtypes = [i64, i32, i32, P, P, P]
         _lib.oracle_average_packed.argtypes = [i64, i32, i32, P, P, P, P, P]
         _lib.oracle_warmup_step.argtypes = [i32, P, i32, P, P, P, P, P, P, ctypes.POINTER(HParams)]
-        _lib.oracle_freeze.argtypes = [i32, i64, i32, P, P, P, P, P, i32, P, P]
+        _lib.oracle_freeze.argtypes = [i32, i64, i32, P, P, P, P, P, i32, P, P,
+                                       ctypes.POINTER(HParams)]
         _lib.oracle_compressed_step.argtypes = [i32, P, i32, i32, P, P, P, P, P, P, P, P, P, P, P,
                                                 P, P, P, ctypes.POINTER(HParams), i32]
         _lib.oracle_adam_warmup_step.argtypes = [i64, i32, P, P, P, P, ctypes.POINTER(HParams)]
@@ -129,12 +131,12 @@ def warmup_step(numels, grads, x, m, v, c_sum, hp):
     return c_out
 
 
-def freeze(numels, v, v_fresh, err_w, err_s, c_sum, T_w, c_avg, f_prev):
+def freeze(numels, v, v_fresh, err_w, err_s, c_sum, T_w, c_avg, f_prev, hp=None):
     numels = np.asarray(numels, dtype=np.int64)
     lib().oracle_freeze(numels.size, int(numels.sum()), len(err_w), _ptr(_f32(v)),
                         _ptr(_f32(v_fresh)), _ptr_array([_f32(e) for e in err_w]),
                         _ptr(_f32(err_s)), _ptr(_f32(c_sum)), T_w, _ptr(_f32(c_avg)),
-                        _ptr(_f32(f_prev)))
+                        _ptr(_f32(f_prev)), None if hp is None else ctypes.byref(hp))
 
 
 def compressed_step(numels, C, grads, err_w, err_s, x, m, v_frozen, v_fresh, c_avg, f_prev, hp,

@@ -46,9 +46,28 @@
  *   C11 x_i = x_i (-) ((gamma (*) c_l) (*) (mhat_i (/) (sqrt(v_frozen,i) (+) eta)));
  *       m_i = mhat_i
  *
+ * Variant readings (each off by default; the page leaves these points open):
+ *   bias correction (bias_step = t >= 1; Adam's, which the page does not
+ *       mention): bc1 = fp32(1 - beta1^t), bc2 = fp32(1 - beta2^t), both
+ *       evaluated in double from the fp32 betas;
+ *       W4' u_i = (m_i (/) bc1) (/) (sqrt(v_i (/) bc2) (+) eta)
+ *   weight decay (lambda != 0; footnote 3 omits it; LAMB's usual form):
+ *       W4'' u_i = u_i (+) (lambda (*) x_i)  with x before the update, so it
+ *       enters the trust ratio; in the compression stage
+ *       C11' x_i = x_i (-) ((gamma (*) c_l) (*) ((mhat_i (/) (sqrt(v_frozen,i)
+ *            (+) eta)) (+) (lambda (*) x_i)))
+ *   EMA of the warmup coefficient (c_avg_decay = d in (0,1)):
+ *       W5' c_sum_l = (d (*) c_sum_l) (+) ((1 (-) d) (*) c_l), and at the
+ *       freeze c_avg_l = c_sum_l (/) fp32(1 - d^T_w) (double power)
+ *   norm-ratio factor (rho_mode = 1):
+ *       C9' Qz = sum (sqrt(v_frozen,i) (+) eta)^2, Qf = sum (sqrt(vf_i) (+) eta)^2
+ *       in double, sequential; rho_l = 1 if either is 0, else
+ *       fp32(sqrt(Qz)/sqrt(Qf)) (double)
+ *
  * 1-bit Adam (the 1-bit Adam page's abstract; 1-bit LAMB's Related Work):
- *   warmup  W1-W4 as above, then x_i = x_i (-) (gamma (*) u_i)  (plain Adam,
- *           no layerwise coefficient)
+ *   warmup  W1-W4 (or W4' with bias correction) as above, then
+ *           x_i = x_i (-) (gamma (*) u_i)  (plain Adam, no layerwise
+ *           coefficient; weight decay is not part of this mode)
  *   compression  C1-C6 as above, then
  *           x_i = x_i (-) (gamma (*) (mhat_i (/) (sqrt(v_frozen,i) (+) eta)));
  *           m_i = mhat_i          (frozen variance, no rescale)
@@ -60,6 +79,11 @@
 #include <string.h>
 
 static int64_t num_chunks(int64_t n, int32_t C) { return (n + C - 1) / C; }
+
+/* Bias-correction divisors of warmup step t (1 when t == 0). */
+static float bias_divisor(float beta, int32_t t) {
+  return t >= 1 ? (float)(1.0 - pow((double)beta, (double)t)) : 1.0f;
+}
 
 static void* xmalloc(size_t bytes) {
   void* p = malloc(bytes ? bytes : 1);
@@ -170,9 +194,17 @@ void oracle_warmup_step(int32_t L, const int64_t* numels, int32_t W, const float
     v[i] = (hp->beta2 * v[i]) + (a2 * (gbar * gbar));
   }
 
-  /* W4 */
+  /* W4 (W4' and W4'' when enabled) */
   float* u = (float*)xmalloc(sizeof(float) * (size_t)(N > 0 ? N : 1));
-  for (int64_t i = 0; i < N; ++i) u[i] = m[i] / (sqrtf(v[i]) + hp->eta);
+  const float bc1 = bias_divisor(hp->beta1, hp->bias_step);
+  const float bc2 = bias_divisor(hp->beta2, hp->bias_step);
+  for (int64_t i = 0; i < N; ++i) {
+    if (hp->bias_step >= 1)
+      u[i] = (m[i] / bc1) / (sqrtf(v[i] / bc2) + hp->eta);
+    else
+      u[i] = m[i] / (sqrtf(v[i]) + hp->eta);
+    if (hp->weight_decay != 0.0f) u[i] = u[i] + (hp->weight_decay * x[i]);
+  }
 
   /* W5 */
   float* c = (float*)xmalloc(sizeof(float) * (size_t)L);
@@ -185,7 +217,10 @@ void oracle_warmup_step(int32_t L, const int64_t* numels, int32_t W, const float
     }
     const float r = (X == 0.0 || U == 0.0) ? 1.0f : (float)(sqrt(X) / sqrt(U));
     c[l] = fminf(fmaxf(r, hp->c_min), hp->c_max);
-    c_sum[l] = c_sum[l] + c[l];
+    if (hp->c_avg_decay > 0.0f)
+      c_sum[l] = (hp->c_avg_decay * c_sum[l]) + ((1.0f - hp->c_avg_decay) * c[l]);
+    else
+      c_sum[l] = c_sum[l] + c[l];
     if (c_out) c_out[l] = c[l];
     off += numels[l];
   }
@@ -203,13 +238,15 @@ void oracle_warmup_step(int32_t L, const int64_t* numels, int32_t W, const float
 
 void oracle_freeze(int32_t L, int64_t N, int32_t W, const float* v, float* v_fresh,
                    float* const* err_w, float* err_s, const float* c_sum, int32_t T_w, float* c_avg,
-                   float* f_prev) {
+                   float* f_prev, const oracle_hparams* hp) {
+  const float d = hp ? hp->c_avg_decay : 0.0f;
+  const float den = d > 0.0f ? (float)(1.0 - pow((double)d, (double)T_w)) : (float)T_w;
   for (int64_t i = 0; i < N; ++i) v_fresh[i] = v[i];
   for (int32_t w = 0; w < W; ++w)
     for (int64_t i = 0; i < N; ++i) err_w[w][i] = 0.0f;
   for (int64_t i = 0; i < N; ++i) err_s[i] = 0.0f;
   for (int32_t l = 0; l < L; ++l) {
-    c_avg[l] = c_sum[l] / (float)T_w;
+    c_avg[l] = c_sum[l] / den;
     f_prev[l] = 1.0f;
   }
 }
@@ -273,17 +310,23 @@ void oracle_compressed_step(int32_t L, const int64_t* numels, int32_t C, int32_t
     free(sw);
   }
 
-  /* C7-C9 */
+  /* C7-C9 (C9' when rho_mode = 1) */
   float* rho = (float*)xmalloc(sizeof(float) * (size_t)L);
   int64_t off = 0;
   for (int32_t l = 0; l < L; ++l) {
     float r = 0.0f;
+    double Qz = 0.0, Qf = 0.0;
     for (int64_t i = off; i < off + numels[l]; ++i) {
       const float ghat = (mhat[i] - (hp->beta1 * m[i])) / a1;
       v_fresh[i] = (hp->beta2 * v_fresh[i]) + (a2 * (ghat * ghat));
       const float q = (sqrtf(v_frozen[i]) + hp->eta) / (sqrtf(v_fresh[i]) + hp->eta);
       r = (i == off || q > r) ? q : r;
+      const double dz = (double)(sqrtf(v_frozen[i]) + hp->eta);
+      const double df = (double)(sqrtf(v_fresh[i]) + hp->eta);
+      Qz += dz * dz;
+      Qf += df * df;
     }
+    if (hp->rho_mode == 1) r = (Qz == 0.0 || Qf == 0.0) ? 1.0f : (float)(sqrt(Qz) / sqrt(Qf));
     rho[l] = r;
     off += numels[l];
   }
@@ -303,7 +346,10 @@ void oracle_compressed_step(int32_t L, const int64_t* numels, int32_t C, int32_t
   for (int32_t l = 0; l < L; ++l) {
     const float step = hp->lr * c[l];
     for (int64_t i = off; i < off + numels[l]; ++i) {
-      x[i] = x[i] - (step * (mhat[i] / (sqrtf(v_frozen[i]) + hp->eta)));
+      if (hp->weight_decay != 0.0f)
+        x[i] = x[i] - (step * ((mhat[i] / (sqrtf(v_frozen[i]) + hp->eta)) + (hp->weight_decay * x[i])));
+      else
+        x[i] = x[i] - (step * (mhat[i] / (sqrtf(v_frozen[i]) + hp->eta)));
       m[i] = mhat[i];
     }
     off += numels[l];
@@ -329,9 +375,12 @@ void oracle_adam_warmup_step(int64_t n, int32_t W, const float* const* grads, fl
     m[i] = (hp->beta1 * m[i]) + (a1 * gmean);
     v[i] = (hp->beta2 * v[i]) + (a2 * (gmean * gmean));
   }
-  /* W4 and the Adam update */
+  /* W4 (W4' with bias correction) and the Adam update */
+  const float bc1 = bias_divisor(hp->beta1, hp->bias_step);
+  const float bc2 = bias_divisor(hp->beta2, hp->bias_step);
   for (int64_t i = 0; i < n; ++i) {
-    const float u = m[i] / (sqrtf(v[i]) + hp->eta);
+    const float u = hp->bias_step >= 1 ? (m[i] / bc1) / (sqrtf(v[i] / bc2) + hp->eta)
+                                       : m[i] / (sqrtf(v[i]) + hp->eta);
     x[i] = x[i] - (hp->lr * u);
   }
 }

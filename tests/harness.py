@@ -157,7 +157,7 @@ class HostRun:
 
     def freeze(self, T_w):
         oracle.freeze(self.numels, self.v, self.vf, self.e, self.err_s, self.c_sum, T_w, self.c_avg,
-                      self.f_prev)
+                      self.f_prev, self.hp)
 
     def compressed_step(self, step, fill=True):
         if fill:

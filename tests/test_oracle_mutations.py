@@ -50,14 +50,28 @@ MUTATIONS = {
                                "m[i] = (hp->beta1 * m[i]) + gmean;"),
     "adam_variance_linear": ("v[i] = (hp->beta2 * v[i]) + (a2 * (gmean * gmean));",
                              "v[i] = (hp->beta2 * v[i]) + (a2 * gmean);"),
-    "adam_eta_inside_sqrt": ("const float u = m[i] / (sqrtf(v[i]) + hp->eta);",
-                             "const float u = m[i] / sqrtf(v[i] + hp->eta);"),
+    "adam_eta_inside_sqrt": (": m[i] / (sqrtf(v[i]) + hp->eta);",
+                             ": m[i] / sqrtf(v[i] + hp->eta);"),
     "adam_worker_input_no_momentum": ("in[i] = (hp->beta1 * m[i]) + (a1 * gw[i]);",
                                       "in[i] = a1 * gw[i];"),
     "adam_update_with_old_momentum": (
         "x[i] = x[i] - (hp->lr * (mhat[i] / (sqrtf(v_frozen[i]) + hp->eta)));",
         "x[i] = x[i] - (hp->lr * (m[i] / (sqrtf(v_frozen[i]) + hp->eta)));"),
     "adam_momentum_not_replaced": ("    m[i] = mhat[i];\n  }\n  free(in);", "  }\n  free(in);"),
+    "bias_sqrt_misplaced": ("u[i] = (m[i] / bc1) / (sqrtf(v[i] / bc2) + hp->eta);",
+                            "u[i] = (m[i] / bc1) / ((sqrtf(v[i]) / bc2) + hp->eta);"),
+    "bias_step_off_by_one": ("pow((double)beta, (double)t)", "pow((double)beta, (double)(t + 1))"),
+    "adam_bias_first_moment_only": ("? (m[i] / bc1) / (sqrtf(v[i] / bc2) + hp->eta)",
+                                    "? (m[i] / bc1) / (sqrtf(v[i]) + hp->eta)"),
+    "weight_decay_sign": ("u[i] = u[i] + (hp->weight_decay * x[i]);",
+                          "u[i] = u[i] - (hp->weight_decay * x[i]);"),
+    "weight_decay_dropped_in_compression": (
+        "((mhat[i] / (sqrtf(v_frozen[i]) + hp->eta)) + (hp->weight_decay * x[i]))",
+        "(mhat[i] / (sqrtf(v_frozen[i]) + hp->eta))"),
+    "ema_weights_swapped": ("((1.0f - hp->c_avg_decay) * c[l])", "(hp->c_avg_decay * c[l])"),
+    "ema_not_bias_corrected": ("(float)(1.0 - pow((double)d, (double)T_w))", "1.0f"),
+    "norm_ratio_not_squared": ("Qf += df * df;", "Qf += df;"),
+    "norm_ratio_inverted": ("(float)(sqrt(Qz) / sqrt(Qf))", "(float)(sqrt(Qf) / sqrt(Qz))"),
 }
 
 

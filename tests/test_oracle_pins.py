@@ -604,3 +604,156 @@ def test_p16_adam_exact_compression_matches_identity(W, carrier):
     assert np.array_equal(x1, x2) and np.array_equal(m1, m2)
     assert all(np.all(e == 0) for e in ew1) and np.all(es1 == 0)
     assert np.max(np.abs(x1 - x0)) > 0
+
+
+# ---------------------------------------------------------------------------
+# Variant readings (all off by default)
+# ---------------------------------------------------------------------------
+# P17 bias correction: the 1-bit Adam warmup with bias_step = t is exactly
+#     textbook Adam (torch.optim.Adam, fp64, its own bias correction)
+def test_p17_bias_corrected_adam_warmup_is_torch_adam():
+    import torch
+    n, W, T = 5000, 2, 6
+    r = rng(40)
+    b1, b2 = float(np.float32(0.9)), float(np.float32(0.999))
+    eta = 1e-6
+    x0 = f32(r.standard_normal(n) * 0.02)
+    x, m, v = x0.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)
+    p = torch.nn.Parameter(torch.tensor(x0, dtype=torch.float64))
+    opt = torch.optim.Adam([p], lr=float(np.float32(1e-3)), betas=(b1, b2),
+                           eps=float(np.float32(eta)), foreach=False)
+    for t in range(1, T + 1):
+        g = [f32(r.standard_normal(n) * 1e-3) for _ in range(W)]
+        oracle.adam_warmup_step(g, x, m, v, hp(eta=eta, bias_step=t))
+        p.grad = torch.tensor(np.mean([gi.astype(np.float64) for gi in g], axis=0))
+        opt.step()
+    xd = p.detach().numpy()
+    assert np.all(np.abs(x - xd) <= T * (U * np.abs(xd) + 1e-5 * 1e-3 * 4))
+    assert np.max(np.abs(x - x0)) > 5e-3       # bias-corrected steps are ~lr each
+
+
+# P18 bias correction in the LAMB warmup: step 1 from m = v = 0 has
+#     mhat = gbar and vhat = gbar^2, so u = sign(gbar) (eta = 0) and the trust
+#     ratio is ||x|| / sqrt(n_l) exactly
+def test_p18_bias_corrected_lamb_first_step():
+    numels = [4096, 1000, 7]
+    N, W = sum(numels), 3
+    r = rng(41)
+    h = hp(eta=0.0, c_min=0.0, c_max=1e30, bias_step=1)
+    x0 = f32(r.standard_normal(N) * 0.02)
+    x, m, v = x0.copy(), np.zeros(N, np.float32), np.zeros(N, np.float32)
+    g = [f32(r.standard_normal(N) * 1e-3) for _ in range(W)]
+    c = oracle.warmup_step(numels, g, x, m, v, np.zeros(3, np.float32), h)
+    off = 0
+    for l, nl in enumerate(numels):
+        xn = np.linalg.norm(x0[off:off + nl].astype(np.float64))
+        assert abs(c[l] / (xn / math.sqrt(nl)) - 1) <= 1e-6
+        # the step moves every parameter of the tensor by about lr * c
+        dx = np.abs(x0[off:off + nl].astype(np.float64) - x[off:off + nl])
+        assert np.all(np.abs(dx / (1e-3 * float(c[l])) - 1) <= 1e-3)
+        off += nl
+
+
+# P19 weight decay (LAMB): with zero gradient and momentum the update
+#     direction is lambda*x, so the trust ratio is 1/lambda and the step
+#     scales x by (1 - lr*c*lambda); the same in the compression stage
+@pytest.mark.parametrize("lam,c_expect", [(0.5, 2.0), (0.01, 10.0)])
+def test_p19_weight_decay_closed_form(lam, c_expect):
+    numels = [4096, 333]
+    N = sum(numels)
+    r = rng(42)
+    x0 = f32(r.standard_normal(N) * 0.02)
+    x, m = x0.copy(), np.zeros(N, np.float32)
+    v = f32(r.uniform(1e-8, 1e-4, N))
+    g = [np.zeros(N, np.float32)] * 2
+    h = hp(weight_decay=lam)
+    c = oracle.warmup_step(numels, g, x, m, v, np.zeros(2, np.float32), h)
+    assert np.allclose(c, c_expect, rtol=4 * U, atol=0)      # clipped at c_max = 10 for 0.01
+    want = x0.astype(np.float64) * (1 - 1e-3 * c_expect * lam)
+    assert np.all(np.abs(x - want) <= 4 * U * np.abs(want))
+    # compression stage: m = g = 0 -> mhat = 0, update lr*c*lambda*x
+    x1 = x.copy()
+    vf = v.copy()
+    err_w = [np.zeros(N, np.float32) for _ in range(2)]
+    out = oracle.compressed_step(numels, 4096, g, err_w, np.zeros(N, np.float32), x, m, v, vf,
+                                 np.ones(2, np.float32), np.ones(2, np.float32), h)
+    assert np.all(m == 0)
+    off = 0
+    for l, nl in enumerate(numels):
+        want = x1[off:off + nl].astype(np.float64) * (1 - 1e-3 * float(out["c"][l]) * lam)
+        assert np.all(np.abs(x[off:off + nl] - want) <= 4 * U * np.abs(want))
+        off += nl
+
+
+# P20 EMA of the warmup coefficient: after T warmup steps the frozen c_avg is
+#     the bias-corrected exponential average of the per-step coefficients
+@pytest.mark.parametrize("d", [0.5, 0.9])
+def test_p20_ema_c_avg(d):
+    numels = [4096, 500, 3]
+    N, W, T = sum(numels), 2, 7
+    r = rng(43)
+    h = hp(c_avg_decay=d)
+    x = f32(r.standard_normal(N) * 0.02)
+    m, v = np.zeros(N, np.float32), np.zeros(N, np.float32)
+    c_sum = np.zeros(3, np.float32)
+    cs = []
+    for _ in range(T):
+        g = [f32(r.standard_normal(N) * 10 ** r.uniform(-4, -2)) for _ in range(W)]
+        cs.append(oracle.warmup_step(numels, g, x, m, v, c_sum, h).astype(np.float64))
+    c_avg = np.zeros(3, np.float32)
+    oracle.freeze(numels, v, v.copy(), [np.zeros(N, np.float32)] * W, np.zeros(N, np.float32),
+                  c_sum, T, c_avg, np.zeros(3, np.float32), h)
+    wts = np.array([(1 - d) * d ** (T - 1 - t) for t in range(T)])
+    want = (wts[:, None] * np.array(cs)).sum(axis=0) / wts.sum()
+    assert np.all(np.abs(c_avg - want) <= 4 * T * U * want)
+    # and the mean (default) is the plain average
+    c_avg2 = np.zeros(3, np.float32)
+    oracle.freeze(numels, v, v.copy(), [np.zeros(N, np.float32)] * W, np.zeros(N, np.float32),
+                  f32(np.sum(cs, axis=0)), T, c_avg2, np.zeros(3, np.float32))
+    assert np.all(np.abs(c_avg2 - np.mean(cs, axis=0)) <= 2 * U * np.mean(cs, axis=0))
+
+
+# P21 norm-ratio factor: rho = ||sqrt(v_frozen)+eta|| / ||sqrt(v_fresh)+eta||
+#     is a weighted mean of the element ratios q, so it equals the common q
+#     when they agree, lies between min q and max q, and for two equal halves
+#     with equal denominators is the root mean square of the two ratios
+def _run_zero_ghat_hp(numels, vfz, vf, h):
+    N = sum(numels)
+    r = rng(44)
+    m = _constant_magnitude_state(numels, r.uniform(1e-4, 1e-2, len(numels)), r)
+    x = f32(r.standard_normal(N) * 0.02)
+    g = [np.zeros(N, np.float32)] * 2
+    err_w = [np.zeros(N, np.float32) for _ in range(2)]
+    L = len(numels)
+    return oracle.compressed_step(numels, 4096, g, err_w, np.zeros(N, np.float32), x, m, vfz, vf,
+                                  np.ones(L, np.float32), np.ones(L, np.float32), h)
+
+
+def test_p21_norm_ratio_factor():
+    numels = [4096, 4096, 4096]
+    N = sum(numels)
+    r = rng(45)
+    h = hp(rho_mode=1, eta=0.0, kappa=1000.0, f_min=0.0, f_max=1e30)
+    vfz = np.empty(N, np.float32)
+    vf = np.empty(N, np.float32)
+    vfz[:4096] = 4e-6                             # tensor 0: every q equal
+    vf[:4096] = 1e-6
+    vfz[4096:8192] = f32(r.uniform(1e-8, 1e-4, 4096))   # tensor 1: random
+    vf[4096:8192] = f32(r.uniform(1e-8, 1e-4, 4096))
+    vfz[8192:8192 + 2048] = 9e-6                  # tensor 2: two halves, one denominator
+    vfz[8192 + 2048:] = 1e-6
+    vf[8192:] = 4e-6
+    vfz0, vf0 = vfz.copy(), vf.copy()
+    out = _run_zero_ghat_hp(numels, vfz, vf, h)
+    vf_new = (np.float32(0.999) * vf0).astype(np.float64)
+    q = np.sqrt(vfz0.astype(np.float64)) / np.sqrt(vf_new)
+    c = out["c"].astype(np.float64)
+    assert abs(c[0] / q[0] - 1) <= 8 * U
+    assert q[4096:8192].min() * (1 - 4 * U) <= c[1] <= q[4096:8192].max() * (1 + 4 * U)
+    assert abs(c[1] / q[4096:8192].max() - 1) > 1e-3        # not the max reading
+    rms = math.sqrt((q[8192] ** 2 + q[-1] ** 2) / 2)
+    assert abs(c[2] / rms - 1) <= 8 * U
+    # the default reading on the same state is the max
+    out2 = _run_zero_ghat_hp(numels, vfz0.copy(), vf0.copy(), hp(eta=0.0, kappa=1000.0, f_min=0.0,
+                                                                   f_max=1e30))
+    assert abs(out2["c"][1] / q[4096:8192].max() - 1) <= 8 * U
