@@ -17,7 +17,8 @@ __all__ = [
     "onebit_layer_table_destroy", "onebit_layer_table_info", "onebit_workspace_size",
     "onebit_lamb_warmup_step", "onebit_lamb_freeze", "onebit_compress_ef", "onebit_average_packed",
     "onebit_lamb_compressed_step", "onebit_lamb_compress_average", "onebit_lamb_rescale_update",
-    "onebit_decompress", "onebit_last_error", "onebit_version",
+    "onebit_decompress", "onebit_last_error", "onebit_version", "onebit_adam_warmup_step",
+    "onebit_adam_compressed_step", "ONEBIT_RHO_MAX", "ONEBIT_RHO_NORM_RATIO",
     "LIB_PATH",
 ]
 
@@ -43,7 +44,12 @@ _i64 = ctypes.c_int64
 class onebit_hparams(ctypes.Structure):
     _fields_ = [(name, ctypes.c_float) for name in
                 ("beta1", "beta2", "eta", "lr", "weight_decay", "c_min", "c_max", "f_min", "f_max",
-                 "kappa")]
+                 "kappa")] + [("rho_mode", ctypes.c_int32), ("c_avg_decay", ctypes.c_float),
+                              ("bias_step", ctypes.c_int32)]
+
+
+ONEBIT_RHO_MAX = 0
+ONEBIT_RHO_NORM_RATIO = 1
 
 
 _lib.onebit_layer_table_create.argtypes = [_P, _i32, _i32, ctypes.POINTER(_P)]
@@ -52,7 +58,8 @@ _lib.onebit_layer_table_info.argtypes = [_P, _P, _P, _P]
 _lib.onebit_workspace_size.argtypes = [_P, _i32, ctypes.POINTER(ctypes.c_size_t)]
 _lib.onebit_lamb_warmup_step.argtypes = [_P, _i32, _P, _P, _P, _P, _P, _P,
                                          ctypes.POINTER(onebit_hparams), _P, _P, _P]
-_lib.onebit_lamb_freeze.argtypes = [_P, _i32, _P, _P, _P, _P, _P, _i32, _P, _P, _P]
+_lib.onebit_lamb_freeze.argtypes = [_P, _i32, _P, _P, _P, _P, _P, _i32, _P, _P,
+                                    ctypes.POINTER(onebit_hparams), _P]
 _lib.onebit_compress_ef.argtypes = [_i64, _i32, _P, _P, _P, _P, _P, _P]
 _lib.onebit_average_packed.argtypes = [_i64, _i32, _i32, _P, _P, _P, _P, _P, _P, _P]
 _lib.onebit_lamb_compressed_step.argtypes = [_P, _i32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
@@ -186,10 +193,11 @@ def onebit_lamb_warmup_step(table, W, grads, x, m, v, c_sum, c_out, hp, ws, stat
            "onebit_lamb_warmup_step")
 
 
-def onebit_lamb_freeze(table, W, v, v_fresh, err_w, err_s, c_sum, T_w, c_avg, f_prev, stream=None):
+def onebit_lamb_freeze(table, W, v, v_fresh, err_w, err_s, c_sum, T_w, c_avg, f_prev, hp=None,
+                       stream=None):
     _check(_lib.onebit_lamb_freeze(_h(table), W, _ptr(v), _ptr(v_fresh), _ptr_list(err_w),
                                    _ptr(err_s), _ptr(c_sum), T_w, _ptr(c_avg), _ptr(f_prev),
-                                   _stream(stream)),
+                                   None if hp is None else ctypes.byref(hp), _stream(stream)),
            "onebit_lamb_freeze")
 
 

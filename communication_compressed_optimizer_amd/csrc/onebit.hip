@@ -3,6 +3,7 @@
 // arithmetic runs in the kernels of onebit_kernels.hpp.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -85,13 +86,29 @@ Coef make_coef(const onebit_hparams& h) {
   c.c_max = h.c_max;
   c.f_min = h.f_min;
   c.f_max = h.f_max;
+  c.wd = h.weight_decay;
+  c.bias = h.bias_step >= 1 ? 1 : 0;
+  // 1 - beta^t in double from the fp32 beta, rounded once
+  c.bc1 = c.bias ? (float)(1.0 - std::pow((double)h.beta1, (double)h.bias_step)) : 1.0f;
+  c.bc2 = c.bias ? (float)(1.0 - std::pow((double)h.beta2, (double)h.bias_step)) : 1.0f;
+  c.cd = h.c_avg_decay;
+  c.cd1 = 1.0f - h.c_avg_decay;
   return c;
 }
 
-int check_hparams(const onebit_hparams* hp, const char* fn) {
+// allow_wd: weight decay is a variant of the LAMB entry points only.
+int check_hparams(const onebit_hparams* hp, const char* fn, bool allow_wd = true) {
   if (!hp) return fail(ONEBIT_EINVAL, "%s: hp is NULL", fn);
-  if (hp->weight_decay != 0.0f)
-    return fail(ONEBIT_EUNSUPPORTED, "%s: weight_decay must be 0", fn);
+  if (!std::isfinite(hp->weight_decay) || hp->weight_decay < 0.0f)
+    return fail(ONEBIT_EINVAL, "%s: weight_decay must be finite and >= 0", fn);
+  if (!allow_wd && hp->weight_decay != 0.0f)
+    return fail(ONEBIT_EUNSUPPORTED, "%s: weight_decay must be 0 in the 1-bit Adam mode", fn);
+  if (hp->rho_mode != ONEBIT_RHO_MAX && hp->rho_mode != ONEBIT_RHO_NORM_RATIO)
+    return fail(ONEBIT_EINVAL, "%s: rho_mode %d is not ONEBIT_RHO_MAX or ONEBIT_RHO_NORM_RATIO", fn,
+                hp->rho_mode);
+  if (!(hp->c_avg_decay >= 0.0f && hp->c_avg_decay < 1.0f))
+    return fail(ONEBIT_EINVAL, "%s: c_avg_decay must be in [0, 1)", fn);
+  if (hp->bias_step < 0) return fail(ONEBIT_EINVAL, "%s: bias_step < 0", fn);
   return ONEBIT_OK;
 }
 
@@ -229,10 +246,17 @@ template <int C>
 struct LaunchPassA {
   static void run(const onebit_layer_table* t, int W, const Workers& wk, float* err_s,
                   const float* m, const float* v_frozen, float* v_fresh, uint32_t* bits_s,
-                  float* scales_s, const Coef& cf, const Ws& ws, int32_t* status, hipStream_t st) {
-    hipLaunchKernelGGL((k_compressed_pass_a<C, kPassA_NT, kPassA_PF, kPassA_WPE, kPassA_SPT>),
-                       dim3((unsigned)t->K), dim3(Geo<C, kPassA_SPT>::T), 0, st, t->N / C, t->dev, W, wk, err_s, m,
-                       v_frozen, v_fresh, bits_s, scales_s, ws.seg_max, cf, status);
+                  float* scales_s, const Coef& cf, bool rho_norm, const Ws& ws, int32_t* status,
+                  hipStream_t st) {
+    const dim3 grid((unsigned)t->K), block(Geo<C, kPassA_SPT>::T);
+    if (rho_norm)
+      hipLaunchKernelGGL((k_compressed_pass_a<C, kPassA_NT, kPassA_PF, kPassA_WPE, kPassA_SPT, true>),
+                         grid, block, 0, st, t->N / C, t->dev, W, wk, err_s, m, v_frozen, v_fresh,
+                         bits_s, scales_s, ws.seg_max, ws.seg_x, ws.seg_u, cf, status);
+    else
+      hipLaunchKernelGGL((k_compressed_pass_a<C, kPassA_NT, kPassA_PF, kPassA_WPE, kPassA_SPT>),
+                         grid, block, 0, st, t->N / C, t->dev, W, wk, err_s, m, v_frozen, v_fresh,
+                         bits_s, scales_s, ws.seg_max, ws.seg_x, ws.seg_u, cf, status);
   }
 };
 
@@ -252,9 +276,16 @@ template <int C>
 struct LaunchPassB {
   static void run(const onebit_layer_table* t, const uint32_t* bits_s, const float* scales_s,
                   float* x, float* m, const float* v_frozen, const float* c_avg, float* f_prev,
-                  float* c_out, const Coef& cf, const Ws& ws, int32_t* status, hipStream_t st) {
-    hipLaunchKernelGGL(k_rescale_finalize<256>, dim3((unsigned)t->L), dim3(256), 0, st, t->dev,
-                       (const float*)ws.seg_max, c_avg, f_prev, ws.c_layer, c_out, cf, status);
+                  float* c_out, const Coef& cf, bool rho_norm, const Ws& ws, int32_t* status,
+                  hipStream_t st) {
+    if (rho_norm)
+      hipLaunchKernelGGL((k_rescale_finalize<256, true>), dim3((unsigned)t->L), dim3(256), 0, st,
+                         t->dev, (const float*)ws.seg_max, (const double*)ws.seg_x,
+                         (const double*)ws.seg_u, c_avg, f_prev, ws.c_layer, c_out, cf, status);
+    else
+      hipLaunchKernelGGL((k_rescale_finalize<256>), dim3((unsigned)t->L), dim3(256), 0, st,
+                         t->dev, (const float*)ws.seg_max, (const double*)ws.seg_x,
+                         (const double*)ws.seg_u, c_avg, f_prev, ws.c_layer, c_out, cf, status);
     hipLaunchKernelGGL((k_compressed_pass_b<C, kPassB_NT>), dim3((unsigned)t->K), dim3(C / 16), 0,
                        st, t->N / C, t->dev, bits_s, scales_s, v_frozen, x, m,
                        (const float*)ws.c_layer, cf);
@@ -514,10 +545,15 @@ int onebit_lamb_warmup_step(const onebit_layer_table* table, int32_t W, const fl
 
 int onebit_lamb_freeze(const onebit_layer_table* table, int32_t W, const float* v, float* v_fresh,
                        float* const* err_w, float* err_s, const float* c_sum, int32_t T_w,
-                       float* c_avg, float* f_prev, void* stream) {
+                       float* c_avg, float* f_prev, const onebit_hparams* hp, void* stream) {
   if (int rc = check_table(table, __func__)) return rc;
   if (int rc = check_W(W, __func__)) return rc;
   if (T_w < 1) return fail(ONEBIT_EINVAL, "%s: T_w = %d < 1", __func__, T_w);
+  if (hp)
+    if (int rc = check_hparams(hp, __func__)) return rc;
+  // mean of the warmup coefficients, or the bias correction of their EMA
+  const double d = hp ? (double)hp->c_avg_decay : 0.0;
+  const float den = d > 0.0 ? (float)(1.0 - std::pow(d, (double)T_w)) : (float)T_w;
   if (!err_w) return fail(ONEBIT_EINVAL, "%s: err_w is NULL", __func__);
   Workers wk{};
   for (int w = 0; w < W; ++w) {
@@ -533,7 +569,7 @@ int onebit_lamb_freeze(const onebit_layer_table* table, int32_t W, const float* 
   hipStream_t st = (hipStream_t)stream;
   by_chunk<LaunchFreeze>(table->chunk, table, (int)W, v, v_fresh, wk, err_s, st);
   hipLaunchKernelGGL(k_freeze_tensors, dim3((unsigned)((table->L + 255) / 256)), dim3(256), 0, st,
-                     (int)table->L, c_sum, (float)T_w, c_avg, f_prev);
+                     (int)table->L, c_sum, den, c_avg, f_prev);
   return launch_status(__func__);
 }
 
@@ -548,7 +584,8 @@ int onebit_lamb_compress_average(const onebit_layer_table* table, int32_t W,
                             scales_w, bits_s, scales_s, hp, ws, wk))
     return rc;
   by_chunk<LaunchPassA>(table->chunk, table, (int)W, wk, err_s, m, v_frozen, v_fresh, bits_s,
-                        scales_s, make_coef(*hp), ws_view(table, ws), status, (hipStream_t)stream);
+                        scales_s, make_coef(*hp), hp->rho_mode == ONEBIT_RHO_NORM_RATIO,
+                        ws_view(table, ws), status, (hipStream_t)stream);
   return launch_status(__func__);
 }
 
@@ -560,7 +597,8 @@ int onebit_lamb_rescale_update(const onebit_layer_table* table, const uint32_t* 
                             hp, ws))
     return rc;
   by_chunk<LaunchPassB>(table->chunk, table, bits_s, scales_s, x, m, v_frozen, c_avg, f_prev, c_out,
-                        make_coef(*hp), ws_view(table, ws), status, (hipStream_t)stream);
+                        make_coef(*hp), hp->rho_mode == ONEBIT_RHO_NORM_RATIO, ws_view(table, ws),
+                        status, (hipStream_t)stream);
   return launch_status(__func__);
 }
 
@@ -579,12 +617,13 @@ int onebit_lamb_compressed_step(const onebit_layer_table* table, int32_t W,
                             hp, ws))
     return rc;
   const Coef cf = make_coef(*hp);
+  const bool rn = hp->rho_mode == ONEBIT_RHO_NORM_RATIO;
   const Ws wsv = ws_view(table, ws);
   hipStream_t st = (hipStream_t)stream;
   by_chunk<LaunchPassA>(table->chunk, table, (int)W, wk, err_s, m, v_frozen, v_fresh, bits_s,
-                        scales_s, cf, wsv, status, st);
+                        scales_s, cf, rn, wsv, status, st);
   by_chunk<LaunchPassB>(table->chunk, table, bits_s, scales_s, x, m, v_frozen, c_avg, f_prev, c_out,
-                        cf, wsv, status, st);
+                        cf, rn, wsv, status, st);
   return launch_status(__func__);
 }
 
@@ -592,7 +631,7 @@ int onebit_adam_warmup_step(int64_t n, int32_t W, const float* const* grads, flo
                             float* v, const onebit_hparams* hp, void* stream) {
   if (n < 0) return fail(ONEBIT_EINVAL, "%s: n < 0", __func__);
   if (int rc = check_W(W, __func__)) return rc;
-  if (int rc = check_hparams(hp, __func__)) return rc;
+  if (int rc = check_hparams(hp, __func__, false)) return rc;
   if ((n + kAdamWarmupChunk - 1) / kAdamWarmupChunk > INT32_MAX / 2)
     return fail(ONEBIT_EUNSUPPORTED, "%s: n too large", __func__);
   if (n == 0) return ok();
@@ -619,7 +658,7 @@ int onebit_adam_compressed_step(int64_t n, int32_t chunk, int32_t W, const float
   if (n < 0) return fail(ONEBIT_EINVAL, "%s: n < 0", __func__);
   if (!chunk_supported(chunk)) return fail(ONEBIT_EUNSUPPORTED, "%s: chunk %d", __func__, chunk);
   if (int rc = check_W(W, __func__)) return rc;
-  if (int rc = check_hparams(hp, __func__)) return rc;
+  if (int rc = check_hparams(hp, __func__, false)) return rc;
   if ((n + chunk - 1) / chunk > INT32_MAX / 2)
     return fail(ONEBIT_EUNSUPPORTED, "%s: n too large", __func__);
   if (n == 0) return ok();

@@ -36,10 +36,25 @@ namespace onebit {
 constexpr int kMaxWorkers = 16;
 
 // Hyper-parameters and their fp32-derived constants (computed on the host in
-// fp32: a1 = 1-beta1, a2 = 1-beta2, kp = 1+kappa, km = 1-kappa).
+// fp32: a1 = 1-beta1, a2 = 1-beta2, kp = 1+kappa, km = 1-kappa), and the
+// variant readings: wd = weight decay lambda (0: off); bias = 1 when the
+// warmup direction is bias-corrected by the divisors bc1 = 1-beta1^t and
+// bc2 = 1-beta2^t (evaluated in double on the host, rounded once); cd = decay
+// of the EMA of the warmup coefficient (0: plain sum) and cd1 = 1-cd.
 struct Coef {
   float beta1, beta2, eta, lr, a1, a2, kp, km, c_min, c_max, f_min, f_max;
+  float wd, bc1, bc2, cd, cd1;
+  int bias;
 };
+
+// Warmup direction u = m/(sqrt(v)+eta), or with bias correction
+// (m/bc1)/(sqrt(v/bc2)+eta); plus lambda*x with weight decay.
+__device__ __forceinline__ float warmup_dir(float m, float v, float x, const Coef& cf) {
+  float u = cf.bias ? (m / cf.bc1) / (__builtin_sqrtf(v / cf.bc2) + cf.eta)
+                    : m / (__builtin_sqrtf(v) + cf.eta);
+  if (cf.wd != 0.0f) u = u + (cf.wd * x);
+  return u;
+}
 
 // Device view of the tensor table.
 struct DevTable {
@@ -397,6 +412,39 @@ __device__ __forceinline__ void segment_max(const DevTable& tab, int64_t k, int6
   }
 }
 
+// Per-(chunk, tensor) double sums of a^2 and b^2 over the chunk's valid
+// elements (fixed order: per thread, then the wave and block tree).
+template <int C, int SPT = 4>
+__device__ __forceinline__ void segment_sums(const DevTable& tab, int64_t k, int64_t base, int nk,
+                                             const SlotsN<SPT>& a_, const SlotsN<SPT>& b_,
+                                             double* red, double* __restrict__ seg_a,
+                                             double* __restrict__ seg_b) {
+  constexpr int T = Geo<C, SPT>::T;
+  const int l0 = tab.l0[k];
+  const int l1 = tab.l1[k];
+  const int sb = tab.seg[k];
+  for (int l = l0; l <= l1; ++l) {
+    const int64_t lo = tab.off[l] - base;
+    const int64_t hi = tab.off[l + 1] - base;
+    double sa = 0.0, sb2 = 0.0;
+#pragma unroll
+    for (int a = 0; a < SPT; ++a)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int j = 4 * ((int)threadIdx.x + T * a) + c;
+        if (j < nk && j >= lo && j < hi) {
+          sa += (double)a_[a][c] * (double)a_[a][c];
+          sb2 += (double)b_[a][c] * (double)b_[a][c];
+        }
+      }
+    block_sum2<T>(sa, sb2, red);
+    if (threadIdx.x == 0) {
+      seg_a[sb + (l - l0)] = sa;
+      seg_b[sb + (l - l0)] = sb2;
+    }
+  }
+}
+
 // ===========================================================================
 // kernels (k0: index of the first chunk of the launch)
 // ===========================================================================
@@ -585,8 +633,10 @@ __device__ __forceinline__ float workers_and_server(const ChunkAt<C, TAIL> ch, i
 
 // 1-bit LAMB compression step, pass A: the compressed allreduce, then the
 // reconstructed gradient, the fresh variance and the per-(chunk, tensor)
-// maximum of the rescale ratio.
-template <int C, bool TAIL, bool NT, bool PF, int SPT>
+// statistic of the rescale: the maximum of the ratio q, or (RN, the
+// norm-ratio variant) the double sums of (sqrt(v_frozen)+eta)^2 and
+// (sqrt(v_fresh)+eta)^2.
+template <int C, bool TAIL, bool NT, bool PF, int SPT, bool RN>
 __device__ __forceinline__ void pass_a_chunk(int64_t kk, const DevTable& tab, int W,
                                              const Workers& wk, float* __restrict__ err_s,
                                              const float* __restrict__ m,
@@ -594,8 +644,11 @@ __device__ __forceinline__ void pass_a_chunk(int64_t kk, const DevTable& tab, in
                                              float* __restrict__ v_fresh,
                                              uint32_t* __restrict__ bits_s,
                                              float* __restrict__ scales_s,
-                                             float* __restrict__ seg_max, const Coef& cf,
-                                             int32_t* status, float4* lds, float* red) {
+                                             float* __restrict__ seg_max,
+                                             double* __restrict__ seg_z,
+                                             double* __restrict__ seg_f, const Coef& cf,
+                                             int32_t* status, float4* lds, float* red,
+                                             double* dred) {
   int parity = 0;
   const ChunkAt<C, TAIL> ch(kk, tab.N);
   const int64_t base = ch.base;
@@ -619,32 +672,51 @@ __device__ __forceinline__ void pass_a_chunk(int64_t kk, const DevTable& tab, in
       const float mh = signed_scale(nib, a, c, s2);
       const float gh = (mh - bm[a][c]) / cf.a1;
       vf[a][c] = (cf.beta2 * vf[a][c]) + (cf.a2 * (gh * gh));
-      vz[a][c] = (__builtin_sqrtf(vz[a][c]) + cf.eta) / (__builtin_sqrtf(vf[a][c]) + cf.eta);
     }
   store_chunk<C, TAIL, NT, SPT>(v_fresh, base, nk, vf);
-  segment_max<C, SPT>(tab, ch.k, base, nk, vz, red, seg_max);  // vz now holds the ratio q
+  if constexpr (RN) {
+#pragma unroll
+    for (int a = 0; a < SPT; ++a)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        vz[a][c] = __builtin_sqrtf(vz[a][c]) + cf.eta;
+        vf[a][c] = __builtin_sqrtf(vf[a][c]) + cf.eta;
+      }
+    segment_sums<C, SPT>(tab, ch.k, base, nk, vz, vf, dred, seg_z, seg_f);
+  } else {
+#pragma unroll
+    for (int a = 0; a < SPT; ++a)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        vz[a][c] = (__builtin_sqrtf(vz[a][c]) + cf.eta) / (__builtin_sqrtf(vf[a][c]) + cf.eta);
+    segment_max<C, SPT>(tab, ch.k, base, nk, vz, red, seg_max);  // vz now holds the ratio q
+  }
 }
 
 
 // One workgroup per chunk; when the buffer ends in a partial chunk, block 0
 // takes it (its guarded code is slower, so it starts first and overlaps the
 // full chunks instead of trailing them).
-template <int C, bool NT = false, bool PF = false, int WPE = 1, int SPT = 4>
+template <int C, bool NT = false, bool PF = false, int WPE = 1, int SPT = 4, bool RN = false>
 __global__ void __launch_bounds__((Geo<C, SPT>::T), WPE)
 k_compressed_pass_a(int64_t n_full, DevTable tab, int W, Workers wk, float* __restrict__ err_s,
                     const float* __restrict__ m, const float* __restrict__ v_frozen,
                     float* __restrict__ v_fresh, uint32_t* __restrict__ bits_s,
-                    float* __restrict__ scales_s, float* __restrict__ seg_max, Coef cf,
+                    float* __restrict__ scales_s, float* __restrict__ seg_max,
+                    double* __restrict__ seg_z, double* __restrict__ seg_f, Coef cf,
                     int32_t* status) {
   __shared__ float4 lds[2 * Geo<C, SPT>::T];
   __shared__ float red[Geo<C, SPT>::T / 64];
+  __shared__ double dred[RN ? 2 * (Geo<C, SPT>::T / 64) : 1];
   const int64_t has_tail = tab.K - n_full;
   if (has_tail && blockIdx.x == 0)
-    pass_a_chunk<C, true, NT, PF, SPT>(n_full, tab, W, wk, err_s, m, v_frozen, v_fresh, bits_s, scales_s,
-                                  seg_max, cf, status, lds, red);
+    pass_a_chunk<C, true, NT, PF, SPT, RN>(n_full, tab, W, wk, err_s, m, v_frozen, v_fresh, bits_s,
+                                           scales_s, seg_max, seg_z, seg_f, cf, status, lds, red,
+                                           dred);
   else
-    pass_a_chunk<C, false, NT, PF, SPT>((int64_t)blockIdx.x - has_tail, tab, W, wk, err_s, m, v_frozen,
-                                   v_fresh, bits_s, scales_s, seg_max, cf, status, lds, red);
+    pass_a_chunk<C, false, NT, PF, SPT, RN>((int64_t)blockIdx.x - has_tail, tab, W, wk, err_s, m,
+                                            v_frozen, v_fresh, bits_s, scales_s, seg_max, seg_z,
+                                            seg_f, cf, status, lds, red, dred);
 }
 
 // 1-bit Adam compression step, one pass per chunk: the compressed allreduce,
@@ -730,7 +802,7 @@ k_adam_warmup(int64_t k0, int64_t n, int W, Workers wk, float* __restrict__ x,
       const float gb = gs[a][c] / fW;
       mm[a][c] = (cf.beta1 * mm[a][c]) + (cf.a1 * gb);
       vv[a][c] = (cf.beta2 * vv[a][c]) + (cf.a2 * (gb * gb));
-      const float u = mm[a][c] / (__builtin_sqrtf(vv[a][c]) + cf.eta);
+      const float u = warmup_dir(mm[a][c], vv[a][c], xx[a][c], cf);
       xx[a][c] = xx[a][c] - (cf.lr * u);
     }
   store_chunk<C, TAIL, true>(m, base, nk, mm);
@@ -738,19 +810,33 @@ k_adam_warmup(int64_t k0, int64_t n, int W, Workers wk, float* __restrict__ x,
   store_chunk<C, TAIL, true>(x, base, nk, xx);
 }
 
-// Per tensor: rho = max of its segments, soft thresholds, c.
-template <int TB>
+// Per tensor: rho = max of its segments (or, RN, the ratio of the norms from
+// the segments' double sums), soft thresholds, c.
+template <int TB, bool RN = false>
 __global__ void __launch_bounds__(TB)
-k_rescale_finalize(DevTable tab, const float* __restrict__ seg_max, const float* __restrict__ c_avg,
+k_rescale_finalize(DevTable tab, const float* __restrict__ seg_max, const double* __restrict__ seg_z,
+                   const double* __restrict__ seg_f, const float* __restrict__ c_avg,
                    float* __restrict__ f_prev, float* __restrict__ c_layer, float* __restrict__ c_out,
                    Coef cf, int32_t* status) {
   __shared__ float red[TB / 64];
+  __shared__ double dred[2 * (TB / 64)];
   const int l = blockIdx.x;
   const int lo = tab.lseg[l];
   const int hi = tab.lseg[l + 1];
-  float mx = -__builtin_inff();
-  for (int i = lo + (int)threadIdx.x; i < hi; i += TB) mx = fmaxf(mx, seg_max[i]);
-  mx = block_max<TB>(mx, red);
+  float mx;
+  if constexpr (RN) {
+    double Z = 0.0, F = 0.0;
+    for (int i = lo + (int)threadIdx.x; i < hi; i += TB) {
+      Z += seg_z[i];
+      F += seg_f[i];
+    }
+    block_sum2<TB>(Z, F, dred);
+    mx = (Z == 0.0 || F == 0.0) ? 1.0f : (float)(__builtin_sqrt(Z) / __builtin_sqrt(F));
+  } else {
+    mx = -__builtin_inff();
+    for (int i = lo + (int)threadIdx.x; i < hi; i += TB) mx = fmaxf(mx, seg_max[i]);
+    mx = block_max<TB>(mx, red);
+  }
   if (threadIdx.x == 0) {
     const float fp = f_prev[l];
     float f = fminf(fminf(mx, cf.f_max), cf.kp * fp);
@@ -808,7 +894,9 @@ __device__ __forceinline__ void pass_b_chunk(int64_t kk, const DevTable& tab,
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       mh[a][c] = signed_scale(nib, a, c, s);
-      xx[a][c] = xx[a][c] - (st[a][c] * (mh[a][c] / (__builtin_sqrtf(vz[a][c]) + cf.eta)));
+      const float d = mh[a][c] / (__builtin_sqrtf(vz[a][c]) + cf.eta);
+      xx[a][c] = cf.wd != 0.0f ? xx[a][c] - (st[a][c] * (d + (cf.wd * xx[a][c])))
+                               : xx[a][c] - (st[a][c] * d);
     }
   store_chunk<C, TAIL, NT>(x, ch.base, ch.nk, xx);
   store_chunk<C, TAIL, NT>(m, ch.base, ch.nk, mh);
@@ -850,9 +938,10 @@ k_warmup_pass1(int64_t k0, DevTable tab, int W, Workers wk, const float* __restr
 #pragma unroll
       for (int c = 0; c < 4; ++c) gs[a][c] = gs[a][c] + g[a][c];
   }
-  Slots mm, vv, u;
+  Slots mm, vv, u, xx;
   load_chunk<C, TAIL>(m, base, nk, mm);
   load_chunk<C, TAIL>(v, base, nk, vv);
+  load_chunk<C, TAIL>(x, base, nk, xx);
   const float fW = (float)W;
 #pragma unroll
   for (int a = 0; a < 4; ++a)
@@ -861,12 +950,10 @@ k_warmup_pass1(int64_t k0, DevTable tab, int W, Workers wk, const float* __restr
       const float gb = gs[a][c] / fW;
       mm[a][c] = (cf.beta1 * mm[a][c]) + (cf.a1 * gb);
       vv[a][c] = (cf.beta2 * vv[a][c]) + (cf.a2 * (gb * gb));
-      u[a][c] = mm[a][c] / (__builtin_sqrtf(vv[a][c]) + cf.eta);
+      u[a][c] = warmup_dir(mm[a][c], vv[a][c], xx[a][c], cf);
     }
   store_chunk<C, TAIL>(m, base, nk, mm);
   store_chunk<C, TAIL>(v, base, nk, vv);
-  Slots xx;
-  load_chunk<C, TAIL>(x, base, nk, xx);
   const int l0 = tab.l0[ch.k];
   const int l1 = tab.l1[ch.k];
   const int sb = tab.seg[ch.k];
@@ -911,7 +998,7 @@ k_warmup_finalize(DevTable tab, const double* __restrict__ seg_x, const double* 
   if (threadIdx.x == 0) {
     const float r = (X == 0.0 || U == 0.0) ? 1.0f : (float)(__builtin_sqrt(X) / __builtin_sqrt(U));
     const float c = fminf(fmaxf(r, cf.c_min), cf.c_max);
-    c_sum[l] = c_sum[l] + c;
+    c_sum[l] = cf.cd > 0.0f ? (cf.cd * c_sum[l]) + (cf.cd1 * c) : c_sum[l] + c;
     c_layer[l] = c;
     if (c_out) c_out[l] = c;
     if (!__builtin_isfinite(X) || !__builtin_isfinite(U)) flag(status, 4);
@@ -933,7 +1020,7 @@ k_warmup_pass2(int64_t k0, DevTable tab, const float* __restrict__ m, const floa
   for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const float u = mm[a][c] / (__builtin_sqrtf(vv[a][c]) + cf.eta);
+      const float u = warmup_dir(mm[a][c], vv[a][c], xx[a][c], cf);
       xx[a][c] = xx[a][c] - (st[a][c] * u);
     }
   store_chunk<C, TAIL>(x, ch.base, ch.nk, xx);
@@ -956,7 +1043,8 @@ k_freeze_elems(int64_t k0, int64_t n, int W, const float* __restrict__ v,
   store_chunk<C, TAIL>(err_s, ch.base, ch.nk, zero);
 }
 
-// Freeze, tensor part: c_avg = c_sum / T_w, f_prev = 1.
+// Freeze, tensor part: c_avg = c_sum / den (den = T_w, or 1-d^T_w for the
+// EMA variant), f_prev = 1.
 __global__ void __launch_bounds__(256)
 k_freeze_tensors(int L, const float* __restrict__ c_sum, float Tw, float* __restrict__ c_avg,
                  float* __restrict__ f_prev) {

@@ -71,7 +71,7 @@ class DevRun:
 
     def freeze(self, T_w):
         self.ob.onebit_lamb_freeze(self.table, self.wl.W, self.v, self.vf, self.e, self.err_s,
-                                   self.c_sum, T_w, self.c_avg, self.f_prev)
+                                   self.c_sum, T_w, self.c_avg, self.f_prev, self.hp)
 
     def compressed_step(self, step, fill=True):
         if fill:
