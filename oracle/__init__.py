@@ -50,10 +50,12 @@ def lib():
         _lib.oracle_adam_warmup_step.argtypes = [i64, i32, P, P, P, P, ctypes.POINTER(HParams)]
         _lib.oracle_adam_compressed_step.argtypes = [i64, i32, i32, P, P, P, P, P, P, P, P, P, P,
                                                      ctypes.POINTER(HParams), i32]
+        _lib.oracle_sparse_step.argtypes = [i32, P, i32, i32, i32, P, P, P, P, P, P, P, P, P, P,
+                                            ctypes.POINTER(HParams)]
         for f in ("oracle_compress_ef", "oracle_decompress", "oracle_average",
                   "oracle_average_packed", "oracle_warmup_step", "oracle_freeze",
                   "oracle_compressed_step", "oracle_adam_warmup_step",
-                  "oracle_adam_compressed_step"):
+                  "oracle_adam_compressed_step", "oracle_sparse_step"):
             getattr(_lib, f).restype = None
     return _lib
 
@@ -185,3 +187,23 @@ def adam_compressed_step(C, grads, err_w, err_s, x, m, v_frozen, hp, compressor=
         _ptr_array(bits_w), _ptr_array(scales_w), _ptr(bits_s), _ptr(scales_s), ctypes.byref(hp),
         compressor)
     return {"bits_w": bits_w, "scales_w": scales_w, "bits_s": bits_s, "scales_s": scales_s}
+
+
+def sparse_step(numels, C, nsel, sel, grads, err_w, x, m, v_frozen, v_fresh, c_avg, hp):
+    """SLAMB-style sparse compression step; state updated in place.  Returns
+    the workers' transmitted values and the server's averages (nsel*64 per
+    chunk)."""
+    numels = np.asarray(numels, dtype=np.int64)
+    N = int(numels.sum())
+    K = num_chunks(N, C)
+    W = len(grads)
+    sel = np.ascontiguousarray(sel, dtype=np.int32)
+    assert sel.size == K
+    vals_w = [np.zeros(K * nsel * 64, np.float32) for _ in range(W)]
+    vals_s = np.zeros(K * nsel * 64, np.float32)
+    lib().oracle_sparse_step(
+        numels.size, numels.ctypes.data, C, W, nsel, sel.ctypes.data,
+        _ptr_array([_f32(g) for g in grads]), _ptr_array([_f32(e) for e in err_w]), _ptr(_f32(x)),
+        _ptr(_f32(m)), _ptr(_f32(v_frozen)), _ptr(_f32(v_fresh)), _ptr(_f32(c_avg)),
+        _ptr_array(vals_w), _ptr(vals_s), ctypes.byref(hp))
+    return {"vals_w": vals_w, "vals_s": vals_s}

@@ -444,3 +444,75 @@ void oracle_adam_compressed_step(int64_t n, int32_t C, int32_t W, const float* c
   free(in);
   free(mhat);
 }
+
+/* ---- SLAMB-style sparse compression stage ----------------------------- */
+
+/* Position of element j of a chunk among the transmitted values, or -1. */
+static int64_t sparse_slot(int64_t j, int32_t C, int32_t nsel, int32_t first_block) {
+  const int64_t nb = C / 64;
+  const int64_t rel = ((j / 64) - first_block + nb) % nb;
+  return rel < nsel ? rel * 64 + j % 64 : -1;
+}
+
+void oracle_sparse_step(int32_t L, const int64_t* numels, int32_t C, int32_t W, int32_t nsel,
+                        const int32_t* sel, const float* const* grads, float* const* err_w,
+                        float* x, float* m, const float* v_frozen, float* v_fresh,
+                        const float* c_avg, float* const* vals_w, float* vals_s,
+                        const oracle_hparams* hp) {
+  const float a1 = 1.0f - hp->beta1;
+  const float a2 = 1.0f - hp->beta2;
+  int64_t N = 0;
+  for (int32_t l = 0; l < L; ++l) N += numels[l];
+  const int64_t K = num_chunks(N, C);
+  const int64_t per = (int64_t)nsel * 64;
+  float* mhat = (float*)xmalloc(sizeof(float) * (size_t)(N > 0 ? N : 1));
+
+  /* the transmitted arrays start at 0 (positions past the buffer's end) */
+  for (int64_t q = 0; q < K * per; ++q) vals_s[q] = 0.0f;
+  for (int32_t w = 0; w < W; ++w)
+    if (vals_w && vals_w[w])
+      for (int64_t q = 0; q < K * per; ++q) vals_w[w][q] = 0.0f;
+
+  /* S1-S4, element by element, workers in order */
+  for (int64_t i = 0; i < N; ++i) {
+    const int64_t k = i / C;
+    const int64_t slot = sparse_slot(i - k * C, C, nsel, sel[k]);
+    float acc = 0.0f;
+    for (int32_t w = 0; w < W; ++w) {
+      const float z = ((hp->beta1 * m[i]) + (a1 * grads[w][i])) + err_w[w][i];
+      if (slot >= 0) {
+        if (vals_w && vals_w[w]) vals_w[w][k * per + slot] = z;
+        acc = w == 0 ? z : acc + z;
+        err_w[w][i] = 0.0f;
+      } else {
+        err_w[w][i] = z;
+      }
+    }
+    if (slot >= 0) {
+      mhat[i] = acc / (float)W;
+      vals_s[k * per + slot] = mhat[i];
+    } else {
+      mhat[i] = 0.0f;
+    }
+  }
+
+  /* S5-S6 */
+  int64_t off = 0;
+  for (int32_t l = 0; l < L; ++l) {
+    const float step = hp->lr * c_avg[l];
+    for (int64_t i = off; i < off + numels[l]; ++i) {
+      const int64_t k = i / C;
+      if (sparse_slot(i - k * C, C, nsel, sel[k]) >= 0) {
+        const float gh = (mhat[i] - (hp->beta1 * m[i])) / a1;
+        v_fresh[i] = (hp->beta2 * v_fresh[i]) + (a2 * (gh * gh));
+        const float dz = sqrtf(v_frozen[i]) + hp->eta;
+        const float q = dz / (sqrtf(v_fresh[i]) + hp->eta);
+        const float r = fminf(fmaxf(q, hp->f_min), hp->f_max);
+        x[i] = x[i] - (step * (r * (mhat[i] / dz)));
+      }
+      m[i] = mhat[i];
+    }
+    off += numels[l];
+  }
+  free(mhat);
+}

@@ -15,7 +15,7 @@ _host = None
 _dev = None
 
 # array ids used in the stream number
-X, M, V, G, LAYER_SCALE = 1, 2, 3, 4, 5
+X, M, V, G, LAYER_SCALE, SEL = 1, 2, 3, 4, 5, 6
 
 
 def stream_id(array, step=0, worker=0):
@@ -36,6 +36,7 @@ def host_lib():
         _host.synth_fill_uniform.argtypes = [u64, u64, i64, i64, d, d, P]
         _host.synth_normal_f64.argtypes = [u64, u64, i64, i64, P]
         _host.synth_layer_log_scales.argtypes = [u64, u64, i32, d, d, P]
+        _host.synth_fill_index.argtypes = [u64, u64, i64, i64, i32, P]
         _host.synth_ln_unit_host.argtypes = [u64]
         _host.synth_ln_unit_host.restype = d
         _host.synth_sqrt_host.argtypes = [d]
@@ -103,4 +104,11 @@ def layer_log_scales(seed, L, lo_exp10, hi_exp10):
     out = np.empty(L, np.float64)
     host_lib().synth_layer_log_scales(seed, stream_id(LAYER_SCALE), L, lo_exp10, hi_exp10,
                                       out.ctypes.data)
+    return out
+
+
+def index_host(out, seed, stream, offset, nb):
+    """Fill the int32 array `out` with uniform integers in [0, nb)."""
+    assert out.dtype == np.int32 and out.flags.c_contiguous
+    host_lib().synth_fill_index(seed, stream, offset, out.size, nb, out.ctypes.data)
     return out

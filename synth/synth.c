@@ -45,6 +45,17 @@ void synth_layer_log_scales(uint64_t seed, uint64_t stream, int32_t L, double lo
     out[l] = pow(10.0, lo_exp10 + (hi_exp10 - lo_exp10) * synth_uniform(key, (uint64_t)l));
 }
 
+/* out[j] = uniform integer in [0, nb) number offset+j of the stream: the top
+ * 32 bits of the keyed draw, scaled to the range by a multiply and shift. */
+void synth_fill_index(uint64_t seed, uint64_t stream, int64_t offset, int64_t n, int32_t nb,
+                      int32_t* out) {
+  const uint64_t key = synth_key(seed, stream);
+  for (int64_t j = 0; j < n; ++j) {
+    const uint64_t x = synth_mix64(key + (2 * (uint64_t)(offset + j) + 1) * SYNTH_GAMMA);
+    out[j] = (int32_t)(((x >> 32) * (uint64_t)nb) >> 32);
+  }
+}
+
 /* Scalar reference pieces of the generator, exposed for its own tests. */
 double synth_ln_unit_host(uint64_t M) { return synth_ln_unit(M); }
 double synth_sqrt_host(double a) { return synth_sqrt(a); }

@@ -72,6 +72,18 @@ MUTATIONS = {
     "ema_not_bias_corrected": ("(float)(1.0 - pow((double)d, (double)T_w))", "1.0f"),
     "norm_ratio_not_squared": ("Qf += df * df;", "Qf += df;"),
     "norm_ratio_inverted": ("(float)(sqrt(Qz) / sqrt(Qf))", "(float)(sqrt(Qf) / sqrt(Qz))"),
+    "sparse_one_block_too_many": ("return rel < nsel ? rel * 64 + j % 64 : -1;",
+                                  "return rel <= nsel ? rel * 64 + j % 64 : -1;"),
+    "sparse_blocks_not_cyclic": ("const int64_t rel = ((j / 64) - first_block + nb) % nb;",
+                                 "const int64_t rel = (j / 64) - first_block;"),
+    "sparse_error_not_cleared": ("        err_w[w][i] = 0.0f;\n      } else {",
+                                 "        err_w[w][i] = z;\n      } else {"),
+    "sparse_no_local_error": ("        err_w[w][i] = z;\n      }", "        err_w[w][i] = 0.0f;\n      }"),
+    "sparse_momentum_not_masked": ("      mhat[i] = 0.0f;\n", "      mhat[i] = hp->beta1 * m[i];\n"),
+    "sparse_no_clamp": ("const float r = fminf(fmaxf(q, hp->f_min), hp->f_max);", "const float r = q;"),
+    "sparse_update_fresh_variance": ("x[i] = x[i] - (step * (r * (mhat[i] / dz)));",
+                                     "x[i] = x[i] - (step * (r * (mhat[i] / (sqrtf(v_fresh[i]) + hp->eta))));"),
+    "sparse_sum_not_mean": ("      mhat[i] = acc / (float)W;", "      mhat[i] = acc;"),
 }
 
 

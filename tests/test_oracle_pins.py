@@ -757,3 +757,138 @@ def test_p21_norm_ratio_factor():
     out2 = _run_zero_ghat_hp(numels, vfz0.copy(), vf0.copy(), hp(eta=0.0, kappa=1000.0, f_min=0.0,
                                                                    f_max=1e30))
     assert abs(out2["c"][1] / q[4096:8192].max() - 1) <= 8 * U
+
+
+# ---------------------------------------------------------------------------
+# SLAMB-style sparse compression stage
+# ---------------------------------------------------------------------------
+def _selected_mask(N, C, nsel, sel):
+    """Independent enumeration of the transmitted positions: blocks
+    sel[k], sel[k]+1, ... (nsel of them, modulo C/64) of every chunk."""
+    mask = np.zeros(N, bool)
+    nb = C // 64
+    for k, b0 in enumerate(sel):
+        for j in range(nsel):
+            b = (b0 + j) % nb
+            lo = k * C + b * 64
+            mask[lo:min(lo + 64, N)] = True
+    return mask
+
+
+def _sparse_state(numels, W, seed, m_std=1e-3):
+    N = sum(numels)
+    r = rng(seed)
+    return dict(x=f32(r.standard_normal(N) * 0.02), m=f32(r.standard_normal(N) * m_std),
+                vfz=f32(r.uniform(1e-8, 1e-4, N)), vf=f32(r.uniform(1e-8, 1e-4, N)),
+                e=[f32(r.standard_normal(N) * 1e-4) for _ in range(W)],
+                g=[f32(r.standard_normal(N) * 1e-3) for _ in range(W)], r=r)
+
+
+# P22 selection, masking and local error compensation: exactly the chosen
+#     blocks are transmitted (in cyclic block order), the momentum is zero
+#     elsewhere, nothing outside moves, and transmitted + kept = accumulated
+@pytest.mark.parametrize("nsel", [1, 3])
+def test_p22_sparse_selection_masking_and_ef(nsel):
+    numels = [4096 * 2 + 1000, 700]
+    N, C, W = sum(numels), 4096, 3
+    st = _sparse_state(numels, W, 50)
+    K = oracle.num_chunks(N, C)
+    sel = st["r"].integers(0, C // 64, K).astype(np.int32)
+    sel[-1] = 27 - (nsel - 1)            # the partial chunk's blocks straddle its end
+    mask = _selected_mask(N, C, nsel, sel)
+    x0, m0, vf0 = st["x"].copy(), st["m"].copy(), st["vf"].copy()
+    e0 = [e.copy() for e in st["e"]]
+    out = oracle.sparse_step(numels, C, nsel, sel, st["g"], st["e"], st["x"], st["m"], st["vfz"],
+                             st["vf"], np.ones(2, np.float32), hp())
+    assert np.all(st["m"][~mask] == 0) and np.all(st["x"][~mask] == x0[~mask])
+    assert np.all(st["vf"][~mask] == vf0[~mask])
+    assert np.all(st["m"][mask] != 0) and np.all(st["x"][mask] != x0[mask])
+    for w in range(W):
+        assert np.all(st["e"][w][mask] == 0)
+        # transmitted value + kept error = the worker's accumulated momentum
+        sent = np.zeros(N, np.float64)
+        pos = np.flatnonzero(mask)
+        sent[pos] = _gather(out["vals_w"][w], pos, C, nsel, sel)
+        b1 = float(np.float32(0.9))
+        a1 = float(np.float32(1) - np.float32(0.9))
+        t1, t2 = b1 * m0.astype(np.float64), a1 * st["g"][w].astype(np.float64)
+        acc = t1 + t2 + e0[w]
+        bound = 4 * U * (np.abs(t1) + np.abs(t2) + np.abs(e0[w]))
+        assert np.all(np.abs(sent + st["e"][w] - acc) <= bound)
+    # the server's values are the workers' mean, in the same order
+    vw = np.array([v.astype(np.float64) for v in out["vals_w"]])
+    mean = vw.mean(axis=0)
+    bound = W * U * np.abs(vw).mean(axis=0) + U * np.abs(mean)
+    assert np.all(np.abs(out["vals_s"] - mean) <= bound)
+    # per full chunk exactly nsel*64 values; past the buffer's end zeros
+    per = nsel * 64
+    assert np.count_nonzero(out["vals_s"][:per * (K - 1)]) == per * (K - 1)
+    assert np.count_nonzero(out["vals_s"][per * (K - 1):]) == int(mask[(K - 1) * C:].sum())
+
+
+def _gather(vals, pos, C, nsel, sel):
+    """Values at flat positions `pos` from a transmitted array laid out as
+    nsel*64 per chunk, blocks in cyclic order from sel[k]."""
+    nb = C // 64
+    k = pos // C
+    j = pos - k * C
+    rel = ((j // 64) - sel[k]) % nb
+    return vals[k * nsel * 64 + rel * 64 + j % 64].astype(np.float64)
+
+
+# P23 every block selected and the rescale pinned to 1: the sparse stage is
+#     the 1-bit LAMB stage with the identity compressor (and f = 1), which
+#     P3 pins to textbook momentum SGD
+def test_p23_sparse_dense_limit_is_identity_compressor():
+    numels = [4096 + 300, 4096]
+    N, C, W = sum(numels), 4096, 2
+    h = hp(f_min=1.0, f_max=1.0, kappa=1e6)
+    a = _sparse_state(numels, W, 51)
+    b = {k: ([e.copy() for e in v] if isinstance(v, list) else v.copy()) for k, v in a.items()
+         if k != "r"}
+    for e in a["e"] + b["e"]:
+        e[:] = 0
+    K = oracle.num_chunks(N, C)
+    c_avg = np.array([1.5, 0.75], np.float32)
+    for step in range(3):
+        sel = a["r"].integers(0, C // 64, K).astype(np.int32)
+        oracle.sparse_step(numels, C, C // 64, sel, a["g"], a["e"], a["x"], a["m"], a["vfz"],
+                           a["vf"], c_avg, h)
+        oracle.compressed_step(numels, C, b["g"], b["e"], np.zeros(N, np.float32), b["x"], b["m"],
+                               b["vfz"], b["vf"], c_avg, np.ones(2, np.float32), h,
+                               compressor=oracle.IDENTITY)
+        for k in ("x", "m", "vf"):
+            assert np.array_equal(a[k], b[k]), (step, k)
+        assert all(np.all(e == 0) for e in a["e"])
+
+
+# P24 element-wise rescale in closed form: with zero gradients, zero errors
+#     and identical workers the average is beta1*m exactly, the reconstructed
+#     gradient is 0, v_fresh decays by beta2, and each selected element moves
+#     by lr*c*clamp(q)*mhat/(sqrt(v_frozen)+eta) with q from the decayed v_fresh
+def test_p24_sparse_elementwise_rescale_closed_form():
+    numels = [4096 * 2]
+    N, C, W = sum(numels), 4096, 2
+    r = rng(52)
+    m = f32(np.where(r.random(N) < 0.5, -1.0, 1.0) * 3e-3)
+    vfz = f32(r.uniform(1e-6, 1e-5, N))
+    vf = f32(vfz.astype(np.float64) * r.uniform(0.01, 100.0, N))   # q from 0.1 to 10
+    x = f32(r.standard_normal(N) * 0.02)
+    x0, vf0, m0 = x.copy(), vf.copy(), m.copy()
+    g = [np.zeros(N, np.float32)] * W
+    e = [np.zeros(N, np.float32) for _ in range(W)]
+    sel = np.array([5, 60], np.int32)
+    nsel = 16
+    mask = _selected_mask(N, C, nsel, sel)
+    h = hp(eta=0.0)
+    oracle.sparse_step(numels, C, nsel, sel, g, e, x, m, vfz, vf, np.array([2.0], np.float32), h)
+    mhat = (np.float32(0.9) * m0).astype(np.float64)
+    assert np.array_equal(m[mask], mhat[mask].astype(np.float32))
+    vf_new = (np.float32(0.999) * vf0)
+    assert np.array_equal(vf[mask], vf_new[mask])
+    q = np.sqrt(vfz.astype(np.float64)) / np.sqrt(vf_new.astype(np.float64))
+    rr = np.clip(q, 0.5, 4.0)
+    assert np.any(q[mask] < 0.5) and np.any(q[mask] > 4.0)      # both clamps bind
+    want = x0.astype(np.float64) - 1e-3 * 2.0 * rr * mhat / np.sqrt(vfz.astype(np.float64))
+    assert np.all(np.abs(x[mask] - want[mask]) <= 2 * U * np.abs(want[mask]) + 8 * U * 1e-3 * 2.0 *
+                  np.abs(rr * mhat / np.sqrt(vfz.astype(np.float64)))[mask])
