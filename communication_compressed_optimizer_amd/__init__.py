@@ -18,7 +18,8 @@ __all__ = [
     "onebit_lamb_warmup_step", "onebit_lamb_freeze", "onebit_compress_ef", "onebit_average_packed",
     "onebit_lamb_compressed_step", "onebit_lamb_compress_average", "onebit_lamb_rescale_update",
     "onebit_decompress", "onebit_last_error", "onebit_version", "onebit_adam_warmup_step",
-    "onebit_adam_compressed_step", "ONEBIT_RHO_MAX", "ONEBIT_RHO_NORM_RATIO",
+    "onebit_adam_compressed_step", "onebit_sparse_compressed_step", "ONEBIT_RHO_MAX",
+    "ONEBIT_RHO_NORM_RATIO",
     "LIB_PATH",
 ]
 
@@ -74,6 +75,8 @@ _lib.onebit_adam_warmup_step.argtypes = [_i64, _i32, _P, _P, _P, _P, ctypes.POIN
                                          _P]
 _lib.onebit_adam_compressed_step.argtypes = [_i64, _i32, _i32, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                              _P, ctypes.POINTER(onebit_hparams), _P, _P]
+_lib.onebit_sparse_compressed_step.argtypes = [_P, _i32, _i32, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                               _P, ctypes.POINTER(onebit_hparams), _P, _P]
 _lib.onebit_last_error.restype = ctypes.c_char_p
 _lib.onebit_version.restype = ctypes.c_char_p
 for _f in ("onebit_layer_table_create", "onebit_layer_table_destroy", "onebit_layer_table_info",
@@ -261,3 +264,12 @@ def onebit_adam_compressed_step(n, chunk, W, grads, err_w, err_s, x, m, v_frozen
         _ptr(v_frozen), _ptr_list(bits_w), _ptr_list(scales_w), _ptr(bits_s), _ptr(scales_s),
         ctypes.byref(hp), _ptr(status), _stream(stream)),
         "onebit_adam_compressed_step")
+
+
+def onebit_sparse_compressed_step(table, W, nsel, sel, grads, err_w, x, m, v_frozen, v_fresh,
+                                  c_avg, vals_w, vals_s, hp, status=None, stream=None):
+    _check(_lib.onebit_sparse_compressed_step(
+        _h(table), W, nsel, _ptr(sel), _ptr_list(grads), _ptr_list(err_w), _ptr(x), _ptr(m),
+        _ptr(v_frozen), _ptr(v_fresh), _ptr(c_avg), _ptr_list(vals_w), _ptr(vals_s),
+        ctypes.byref(hp), _ptr(status), _stream(stream)),
+        "onebit_sparse_compressed_step")

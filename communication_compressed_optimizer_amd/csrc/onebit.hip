@@ -189,6 +189,8 @@ constexpr bool kAdam_NT = true;
 constexpr bool kAdam_PF = false;
 constexpr int kAdam_WPE = 6;
 constexpr int kAdam_SPT = 4;
+// Streaming accesses in the sparse-stage kernel.
+constexpr bool kSparse_NT = true;
 // Chunk geometry of the element-wise 1-bit Adam warmup kernel (any chunk
 // gives the same result; this one gives 256-thread workgroups).
 constexpr int kAdamWarmupChunk = 4096;
@@ -269,6 +271,18 @@ struct LaunchAdam {
     hipLaunchKernelGGL((k_adam_compressed<C, kAdam_NT, kAdam_PF, kAdam_WPE, kAdam_SPT>),
                        dim3((unsigned)K), dim3(Geo<C, kAdam_SPT>::T), 0, st, n / C, n, K, W, wk,
                        err_s, m, x, v_frozen, bits_s, scales_s, cf, status);
+  }
+};
+
+template <int C>
+struct LaunchSparse {
+  static void run(const onebit_layer_table* t, int W, int nsel, const int32_t* sel,
+                  const Workers& wk, const WorkerVals& wv, float* x, float* m, const float* v_frozen,
+                  float* v_fresh, const float* c_avg, float* vals_s, const Coef& cf, int32_t* status,
+                  hipStream_t st) {
+    hipLaunchKernelGGL((k_sparse_step<C, kSparse_NT>), dim3((unsigned)t->K), dim3(C / 16), 0, st,
+                       t->N / C, t->dev, W, nsel, sel, wk, wv, x, m, v_frozen, v_fresh, c_avg,
+                       vals_s, cf, status);
   }
 };
 
@@ -672,6 +686,38 @@ int onebit_adam_compressed_step(int64_t n, int32_t chunk, int32_t W, const float
   CHECK_PTR(scales_s, "scales_s");
   by_chunk<LaunchAdam>(chunk, n, (int)W, wk, err_s, m, x, v_frozen, bits_s, scales_s,
                        make_coef(*hp), status, (hipStream_t)stream);
+  return launch_status(__func__);
+}
+
+int onebit_sparse_compressed_step(const onebit_layer_table* table, int32_t W, int32_t nsel,
+                                  const int32_t* sel, const float* const* grads,
+                                  float* const* err_w, float* x, float* m, const float* v_frozen,
+                                  float* v_fresh, const float* c_avg, float* const* vals_w,
+                                  float* vals_s, const onebit_hparams* hp, int32_t* status,
+                                  void* stream) {
+  if (int rc = check_table(table, __func__)) return rc;
+  if (int rc = check_W(W, __func__)) return rc;
+  if (int rc = check_hparams(hp, __func__, false)) return rc;
+  if (nsel < 1 || nsel > table->chunk / 64)
+    return fail(ONEBIT_EINVAL, "%s: nsel = %d outside [1, chunk/64 = %d]", __func__, nsel,
+                table->chunk / 64);
+  if (!sel) return fail(ONEBIT_EINVAL, "%s: sel is NULL", __func__);
+  Workers wk;
+  if (int rc = check_workers(__func__, W, grads, err_w, nullptr, nullptr, wk)) return rc;
+  WorkerVals wv{};
+  if (vals_w)
+    for (int w = 0; w < W; ++w) {
+      CHECK_OPT_PTR(vals_w[w], "vals_w[w]");
+      wv.v[w] = vals_w[w];
+    }
+  CHECK_PTR(x, "x");
+  CHECK_PTR(m, "m");
+  CHECK_PTR(v_frozen, "v_frozen");
+  CHECK_PTR(v_fresh, "v_fresh");
+  CHECK_PTR(c_avg, "c_avg");
+  CHECK_PTR(vals_s, "vals_s");
+  by_chunk<LaunchSparse>(table->chunk, table, (int)W, (int)nsel, sel, wk, wv, x, m, v_frozen,
+                         v_fresh, c_avg, vals_s, make_coef(*hp), status, (hipStream_t)stream);
   return launch_status(__func__);
 }
 

@@ -81,6 +81,11 @@ struct PackedIn {
   const float* scales[kMaxWorkers];
 };
 
+// Per-worker transmitted values of the sparse stage (entries may be NULL).
+struct WorkerVals {
+  float* v[kMaxWorkers];
+};
+
 // C elements per chunk, SPT float4 slots per thread, T = C/(4*SPT) threads.
 template <int C, int SPT = 4>
 struct Geo {
@@ -808,6 +813,155 @@ k_adam_warmup(int64_t k0, int64_t n, int W, Workers wk, float* __restrict__ x,
   store_chunk<C, TAIL, true>(m, base, nk, mm);
   store_chunk<C, TAIL, true>(v, base, nk, vv);
   store_chunk<C, TAIL, true>(x, base, nk, xx);
+}
+
+// SLAMB-style sparse compression stage, one pass per chunk.  The chunk's
+// C/64 blocks of 64 elements are transmitted in nsel consecutive blocks from
+// block sel[k] (cyclically); thread t's slot k covers block (t + T*k)/16, so
+// 16 consecutive lanes share one block and its selection.  Workers' values
+// are error-compensated on the unselected blocks and averaged on the
+// selected ones; the momentum is masked to the selected blocks, where the
+// fresh variance, the clamped element-wise ratio and the update follow.
+template <int C, bool TAIL, bool NT>
+__device__ __forceinline__ void sparse_chunk(int64_t kk, const DevTable& tab, int W, int nsel,
+                                             const int32_t* __restrict__ sel, const Workers& wk,
+                                             const WorkerVals& vals_w, float* __restrict__ x,
+                                             float* __restrict__ m,
+                                             const float* __restrict__ v_frozen,
+                                             float* __restrict__ v_fresh,
+                                             const float* __restrict__ c_avg,
+                                             float* __restrict__ vals_s, const Coef& cf,
+                                             int32_t* status) {
+  constexpr int T = Geo<C>::T;
+  constexpr int NB = C / 64;
+  const ChunkAt<C, TAIL> ch(kk, tab.N);
+  const int64_t base = ch.base;
+  const int nk = ch.nk;
+  const int t = threadIdx.x;
+  const int b0 = ((sel[ch.k] % NB) + NB) % NB;
+  const int64_t per = (int64_t)nsel * 64;
+  // per slot: transmitted position within the chunk's values, or -1
+  int pos[4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const int p = t + T * a;                    // float4 slot; block p/16
+    const int rel = ((p / 16) - b0 + NB) % NB;
+    pos[a] = rel < nsel ? rel * 64 + 4 * (p % 16) : -1;
+  }
+
+  Slots bm, acc;
+  load_chunk<C, TAIL, NT>(m, base, nk, bm);
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) bm[a][c] = cf.beta1 * bm[a][c];
+
+  for (int w = 0; w < W; ++w) {
+    Slots z, e;
+    load_chunk<C, TAIL, NT>(wk.g[w], base, nk, z);
+    load_chunk<C, TAIL, NT>(wk.e[w], base, nk, e);
+    float* vw = vals_w.v[w];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        z[a][c] = (bm[a][c] + (cf.a1 * z[a][c])) + e[a][c];
+        if (pos[a] >= 0) {
+          acc[a][c] = w == 0 ? z[a][c] : acc[a][c] + z[a][c];
+          e[a][c] = 0.0f;
+        } else {
+          e[a][c] = z[a][c];
+        }
+      }
+      if (vw && pos[a] >= 0) {
+        float* q = vw + ch.k * per + pos[a];
+        if constexpr (TAIL) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) q[c] = slot_valid<C>(a, c, nk) ? z[a][c] : 0.0f;
+        } else {
+          st4<NT>(q, f32x4{z[a][0], z[a][1], z[a][2], z[a][3]});
+        }
+      }
+    }
+    store_chunk<C, TAIL, NT>(wk.e[w], base, nk, e);
+  }
+
+  // server average, masked momentum
+  const float fW = (float)W;
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[a][c] = pos[a] >= 0 ? acc[a][c] / fW : 0.0f;
+
+  // element-wise rescale and update on the transmitted blocks
+  const int l0 = tab.l0[ch.k];
+  const int l1 = tab.l1[ch.k];
+  const float st0 = cf.lr * c_avg[l0];
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    if (pos[a] < 0) continue;
+    const int64_t e0 = base + 4 * (t + T * a);
+    float xs[4], vz[4], vf[4];
+    if constexpr (TAIL) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const bool ok = slot_valid<C>(a, c, nk);
+        xs[c] = ok ? x[e0 + c] : 0.0f;
+        vz[c] = ok ? v_frozen[e0 + c] : 0.0f;
+        vf[c] = ok ? v_fresh[e0 + c] : 0.0f;
+      }
+    } else {
+      const f32x4 xv = ld4<NT>(x + e0), zv = ld4<NT>(v_frozen + e0), fv = ld4<NT>(v_fresh + e0);
+      xs[0] = xv.x; xs[1] = xv.y; xs[2] = xv.z; xs[3] = xv.w;
+      vz[0] = zv.x; vz[1] = zv.y; vz[2] = zv.z; vz[3] = zv.w;
+      vf[0] = fv.x; vf[1] = fv.y; vf[2] = fv.z; vf[3] = fv.w;
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float mh = acc[a][c];
+      const float gh = (mh - bm[a][c]) / cf.a1;
+      vf[c] = (cf.beta2 * vf[c]) + (cf.a2 * (gh * gh));
+      const float dz = __builtin_sqrtf(vz[c]) + cf.eta;
+      const float q = dz / (__builtin_sqrtf(vf[c]) + cf.eta);
+      const float r = fminf(fmaxf(q, cf.f_min), cf.f_max);
+      const float stp = l0 == l1 ? st0 : cf.lr * c_avg[tensor_of(tab, l0, l1, e0 + c)];
+      xs[c] = xs[c] - (stp * (r * (mh / dz)));
+      if (!__builtin_isfinite(mh)) flag(status, 2);
+    }
+    float* q = vals_s + ch.k * per + pos[a];
+    if constexpr (TAIL) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if (slot_valid<C>(a, c, nk)) {
+          x[e0 + c] = xs[c];
+          v_fresh[e0 + c] = vf[c];
+        }
+        q[c] = slot_valid<C>(a, c, nk) ? acc[a][c] : 0.0f;
+      }
+    } else {
+      st4<NT>(x + e0, f32x4{xs[0], xs[1], xs[2], xs[3]});
+      st4<NT>(v_fresh + e0, f32x4{vf[0], vf[1], vf[2], vf[3]});
+      st4<NT>(q, f32x4{acc[a][0], acc[a][1], acc[a][2], acc[a][3]});
+    }
+  }
+  store_chunk<C, TAIL, NT>(m, base, nk, acc);
+}
+
+// One workgroup per chunk; block 0 takes the partial last chunk, if any.
+template <int C, bool NT = true>
+__global__ void __launch_bounds__(C / 16)
+k_sparse_step(int64_t n_full, DevTable tab, int W, int nsel, const int32_t* __restrict__ sel,
+              Workers wk, WorkerVals vals_w, float* __restrict__ x, float* __restrict__ m,
+              const float* __restrict__ v_frozen, float* __restrict__ v_fresh,
+              const float* __restrict__ c_avg, float* __restrict__ vals_s, Coef cf,
+              int32_t* status) {
+  const int64_t has_tail = tab.K - n_full;
+  if (has_tail && blockIdx.x == 0)
+    sparse_chunk<C, true, NT>(n_full, tab, W, nsel, sel, wk, vals_w, x, m, v_frozen, v_fresh,
+                              c_avg, vals_s, cf, status);
+  else
+    sparse_chunk<C, false, NT>((int64_t)blockIdx.x - has_tail, tab, W, nsel, sel, wk, vals_w, x, m,
+                               v_frozen, v_fresh, c_avg, vals_s, cf, status);
 }
 
 // Per tensor: rho = max of its segments (or, RN, the ratio of the norms from

@@ -15,8 +15,8 @@ import dataclasses
 
 import numpy as np
 
-from . import G, M, V, X, layer_log_scales, normal_dev, normal_host, stream_id, uniform_dev, \
-    uniform_host
+from . import G, M, SEL, V, X, index_host, layer_log_scales, normal_dev, normal_host, stream_id, \
+    uniform_dev, uniform_host
 
 HPARAMS = dict(beta1=0.9, beta2=0.999, eta=1e-8, lr=1e-3, weight_decay=0.0, c_min=0.01, c_max=10.0,
                f_min=0.5, f_max=4.0, kappa=0.1)
@@ -119,6 +119,14 @@ class Workload:
         else:
             raise ValueError(array)
         return out
+
+    def selection(self, step, k0=0, k1=None):
+        """First transmitted 64-element block of chunks [k0, k1) for the
+        sparse stage at `step`: uniform in [0, chunk/64), shared by all
+        workers."""
+        k1 = self.K if k1 is None else k1
+        out = np.empty(k1 - k0, np.int32)
+        return index_host(out, self.seed, stream_id(SEL, step), k0, self.chunk // 64)
 
     def window_table(self, lo, hi):
         """Tensor sizes of [lo, hi) clipped to the window, and the index of

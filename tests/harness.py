@@ -95,6 +95,31 @@ class DevRun:
             self.wl.N, chunk or self.wl.chunk, self.wl.W, self.g, self.e, self.err_s, self.x, self.m,
             self.v, self.bits_w, self.scales_w, self.bits_s, self.scales_s, self.hp, self.status)
 
+    # -- SLAMB-style sparse stage ----------------------------------------
+    def sparse_step(self, step, nsel, fill=True):
+        torch = self.torch
+        if fill:
+            self.fill_grads(step)
+        K, W = self.wl.K, self.wl.W
+        if getattr(self, "_nsel", None) != nsel:
+            self._nsel = nsel
+            self.vals_s = torch.zeros(K * nsel * 64, dtype=torch.float32, device="cuda")
+            self.vals_w = [torch.zeros(K * nsel * 64, dtype=torch.float32, device="cuda")
+                           for _ in range(W)] if self.bits_w is not None else None
+        self.sel = torch.from_numpy(self.wl.selection(step)).cuda()
+        self.ob.onebit_sparse_compressed_step(
+            self.table, W, nsel, self.sel, self.g, self.e, self.x, self.m, self.v, self.vf,
+            self.c_avg, self.vals_w, self.vals_s, self.hp, self.status)
+
+    def sparse_window(self, lo, hi):
+        C, per = self.wl.chunk, self._nsel * 64
+        k0, k1 = lo // C, -(-hi // C)
+        d = self.window(lo, hi)
+        d["vals_s"] = self.vals_s[k0 * per:k1 * per].cpu().numpy()
+        if self.vals_w is not None:
+            d["vals_w"] = [v[k0 * per:k1 * per].cpu().numpy() for v in self.vals_w]
+        return d
+
     # -- window download -------------------------------------------------
     def window(self, lo, hi):
         C = self.wl.chunk
@@ -177,6 +202,14 @@ class HostRun:
             self.fill_grads(step)
         self.out = oracle.adam_compressed_step(self.wl.chunk, self.g, self.e, self.err_s, self.x,
                                                self.m, self.v, self.hp)
+
+    def sparse_step(self, step, nsel, fill=True):
+        if fill:
+            self.fill_grads(step)
+        C = self.wl.chunk
+        sel = self.wl.selection(step, self.lo // C, -(-self.hi // C))
+        self.out = oracle.sparse_step(self.numels, C, nsel, sel, self.g, self.e, self.x, self.m,
+                                      self.v, self.vf, self.c_avg, self.hp)
 
     def load_from(self, d):
         """Adopt a downloaded GPU window (strict per-step parity)."""
@@ -270,6 +303,33 @@ def compare_adam(dev, host, d=None):
             for w in range(host.wl.W):
                 exact(f"bits_w{w}", d["bits_w"][w], host.out["bits_w"][w])
                 exact(f"scales_w{w}", d["scales_w"][w], host.out["scales_w"][w])
+    return rep
+
+
+def compare_sparse(dev, host):
+    """Sparse stage: every array of the window bit for bit (all of it is
+    element-wise)."""
+    d = dev.sparse_window(host.lo, host.hi)
+    rep = {}
+
+    def exact(name, a, b):
+        a = np.asarray(a)
+        b = np.asarray(b)
+        rep[name] = _entry(a.view(np.uint32) != b.view(np.uint32), a, b, True)
+
+    for k in ("m", "v", "vf"):
+        exact(k, d[k], getattr(host, k))
+    # x on the tensors wholly inside the window (c_avg is per tensor)
+    off_w = np.concatenate([[0], np.cumsum(host.numels)])
+    idx = np.concatenate([np.arange(off_w[i], off_w[i + 1]) for i in host.full]) \
+        if host.full.size else np.zeros(0, np.int64)
+    exact("x", d["x"][idx], host.x[idx])
+    for w in range(host.wl.W):
+        exact(f"e{w}", d["e"][w], host.e[w])
+    exact("vals_s", d["vals_s"], host.out["vals_s"])
+    if "vals_w" in d:
+        for w in range(host.wl.W):
+            exact(f"vals_w{w}", d["vals_w"][w], host.out["vals_w"][w])
     return rep
 
 
