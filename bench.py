@@ -60,7 +60,16 @@ def adam_bytes(N, K, C, W):
     return N * (12 * W + 28) + packed
 
 
-def cpu_baseline(wl, n_chunks, method="lamb"):
+def sparse_bytes(N, K, C, W, nsel):
+    """Algorithmic bytes of the sparse-stage kernel: m read and written; per
+    worker g read, e read and written; on the transmitted fraction
+    f = nsel*64/C: x and v_fresh read and written, v_frozen read, W + 1
+    transmitted values written; the selection read."""
+    f = nsel * 64 / C
+    return int(N * (12 * W + 8) + N * f * (20 + 4 * (W + 1)) + 4 * K)
+
+
+def cpu_baseline(wl, n_chunks, method="lamb", nsel=1):
     """The oracle (single-threaded C, as it stands) on the window of the
     first n_chunks chunks of the workload: one compression step."""
     from tests.harness import HostRun
@@ -70,10 +79,13 @@ def cpu_baseline(wl, n_chunks, method="lamb"):
     t0 = time.perf_counter()
     if method == "adam":
         h.adam_compressed_step(0, fill=False)
+    elif method == "sparse":
+        h.sparse_step(0, nsel, fill=False)
     else:
         h.compressed_step(0, fill=False)
     dt = time.perf_counter() - t0
-    what = "1-bit Adam" if method == "adam" else "1-bit LAMB"
+    what = {"adam": "1-bit Adam", "sparse": f"sparse ({nsel} block(s) of 64 per chunk)"}.get(
+        method, "1-bit LAMB")
     return {"value": hi / dt, "unit": "params/s", "cores": 1, "kind": "oracle",
             "sample": f"one {what} compression step on elements [0, {hi}) of the {wl.name} table "
                       f"(first {hi // wl.chunk} chunks, W={wl.W}); {dt:.2f} s"}
@@ -85,8 +97,11 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="bert_large")
-    ap.add_argument("--method", choices=("lamb", "adam"), default="lamb",
-                    help="1-bit LAMB (the default) or the 1-bit Adam mode on the same buffers")
+    ap.add_argument("--method", choices=("lamb", "adam", "sparse"), default="lamb",
+                    help="1-bit LAMB (the default), the 1-bit Adam mode, or the SLAMB-style "
+                         "sparse stage, on the same buffers")
+    ap.add_argument("--nsel", type=int, default=1,
+                    help="sparse stage: transmitted 64-element blocks per chunk")
     ap.add_argument("--cpu-chunks", type=int, default=12288,
                     help="chunks of the workload the CPU oracle baseline runs (0 = skip)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -158,6 +173,9 @@ def main():
     if args.method == "adam":
         return bench_adam(args, wl, ob, torch, hp, g, e, err_s, x, m, v, bits_w, scales_w, bits_s,
                           scales_s, status, stream)
+    if args.method == "sparse":
+        return bench_sparse(args, wl, ob, torch, table, hp, g, e, x, m, v, vf, c_avg, status,
+                            stream)
 
     def step(ev=None):
         if ev is not None:
@@ -324,6 +342,77 @@ def bench_adam(args, wl, ob, torch, hp, g, e, err_s, x, m, v, bits_w, scales_w, 
         "roofline": {"bound": "hbm", "kernel": "k_adam_compressed<4096>",
                      "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
+                     "algorithmic_bytes": abytes},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def bench_sparse(args, wl, ob, torch, table, hp, g, e, x, m, v, vf, c_avg, status, stream):
+    """The SLAMB-style sparse stage on the same table: one fused kernel per
+    step, a fresh seeded block selection per step (uploaded before timing)."""
+    C, N, W, K, L = wl.chunk, wl.N, wl.W, wl.K, wl.L
+    nsel = args.nsel
+    per = nsel * 64
+    vals_w = [torch.zeros(K * per, dtype=torch.float32, device="cuda") for _ in range(W)]
+    vals_s = torch.zeros(K * per, dtype=torch.float32, device="cuda")
+    total = args.warmup + args.steps
+    sels = [torch.from_numpy(wl.selection(i)).cuda() for i in range(total)]
+    torch.cuda.synchronize()
+
+    def step(i):
+        ob.onebit_sparse_compressed_step(table, W, nsel, sels[i], g, e, x, m, v, vf, c_avg, vals_w,
+                                         vals_s, hp, status, stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(args.warmup, total):
+        step(i)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    if int(status.item()):
+        log(f"[bench] WARNING: status flags {int(status.item())}")
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    k_ms = ev[0].elapsed_time(ev[1]) / args.steps
+    log(f"[bench] sparse {args.steps} steps: {ms_per_step:.3f} ms/step (kernel {k_ms:.3f} ms)")
+    abytes = sparse_bytes(N, K, C, W, nsel)
+    achieved = abytes / (k_ms * 1e-3) / 1e9
+    cpu = None
+    if args.cpu_chunks > 0:
+        log("[bench] CPU oracle baseline ...")
+        cpu = cpu_baseline(wl, args.cpu_chunks, "sparse", nsel)
+        log(f"[bench] oracle: {cpu['value']:.3e} params/s ({cpu['sample']})")
+    step_gbps = abytes / (ms_per_step * 1e-3) / 1e9
+    out = {
+        "metric": "params/sec and achieved HBM GB/s (% of peak) per sparse-stage step",
+        "value": N / (ms_per_step * 1e-3),
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: SLAMB-style sparse compression step, {L} tensors, "
+                               f"N={N}, W={W} simulated workers, chunk {C}, {nsel} of {C // 64} "
+                               f"blocks transmitted",
+                   "N": N, "W": W, "tensors": L, "chunk": C, "nsel": nsel},
+        "achieved_GBps": step_gbps,
+        "frac_of_peak": step_gbps / PEAK_HBM_GBPS,
+        "step_bytes": abytes,
+        "roofline": {"bound": "hbm", "kernel": "k_sparse_step<4096>",
+                     "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBPS,
+                     "traffic": _measured_traffic("traffic_sparse_step_bert_large.txt")
+                     if wl.name == "bert_large" and nsel == 1 else None,
                      "algorithmic_bytes": abytes},
         "cpu_baseline": cpu,
     }
