@@ -102,7 +102,7 @@ def main():
                          "sparse stage, on the same buffers")
     ap.add_argument("--nsel", type=int, default=1,
                     help="sparse stage: transmitted 64-element blocks per chunk")
-    ap.add_argument("--cpu-chunks", type=int, default=12288,
+    ap.add_argument("--cpu-chunks", type=int, default=40960,
                     help="chunks of the workload the CPU oracle baseline runs (0 = skip)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of 2^28 floats (1 GiB) three times, the "
