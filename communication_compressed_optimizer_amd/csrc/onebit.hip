@@ -250,15 +250,24 @@ struct LaunchPassA {
                   const float* m, const float* v_frozen, float* v_fresh, uint32_t* bits_s,
                   float* scales_s, const Coef& cf, bool rho_norm, const Ws& ws, int32_t* status,
                   hipStream_t st) {
-    const dim3 grid((unsigned)t->K), block(Geo<C, kPassA_SPT>::T);
-    if (rho_norm)
-      hipLaunchKernelGGL((k_compressed_pass_a<C, kPassA_NT, kPassA_PF, kPassA_WPE, kPassA_SPT, true>),
-                         grid, block, 0, st, t->N / C, t->dev, W, wk, err_s, m, v_frozen, v_fresh,
-                         bits_s, scales_s, ws.seg_max, ws.seg_x, ws.seg_u, cf, status);
+    const bool pm = m == nullptr;
+    if (rho_norm && pm)
+      go<true, true>(t, W, wk, err_s, m, v_frozen, v_fresh, bits_s, scales_s, cf, ws, status, st);
+    else if (rho_norm)
+      go<true, false>(t, W, wk, err_s, m, v_frozen, v_fresh, bits_s, scales_s, cf, ws, status, st);
+    else if (pm)
+      go<false, true>(t, W, wk, err_s, m, v_frozen, v_fresh, bits_s, scales_s, cf, ws, status, st);
     else
-      hipLaunchKernelGGL((k_compressed_pass_a<C, kPassA_NT, kPassA_PF, kPassA_WPE, kPassA_SPT>),
-                         grid, block, 0, st, t->N / C, t->dev, W, wk, err_s, m, v_frozen, v_fresh,
-                         bits_s, scales_s, ws.seg_max, ws.seg_x, ws.seg_u, cf, status);
+      go<false, false>(t, W, wk, err_s, m, v_frozen, v_fresh, bits_s, scales_s, cf, ws, status, st);
+  }
+  template <bool RN, bool PM>
+  static void go(const onebit_layer_table* t, int W, const Workers& wk, float* err_s,
+                 const float* m, const float* v_frozen, float* v_fresh, uint32_t* bits_s,
+                 float* scales_s, const Coef& cf, const Ws& ws, int32_t* status, hipStream_t st) {
+    hipLaunchKernelGGL(
+        (k_compressed_pass_a<C, kPassA_NT, kPassA_PF, kPassA_WPE, kPassA_SPT, RN, PM>),
+        dim3((unsigned)t->K), dim3(Geo<C, kPassA_SPT>::T), 0, st, t->N / C, t->dev, W, wk, err_s, m,
+        v_frozen, v_fresh, bits_s, scales_s, ws.seg_max, ws.seg_x, ws.seg_u, cf, status);
   }
 };
 
@@ -268,9 +277,14 @@ struct LaunchAdam {
                   const float* v_frozen, uint32_t* bits_s, float* scales_s, const Coef& cf,
                   int32_t* status, hipStream_t st) {
     const int64_t K = (n + C - 1) / C;
-    hipLaunchKernelGGL((k_adam_compressed<C, kAdam_NT, kAdam_PF, kAdam_WPE, kAdam_SPT>),
-                       dim3((unsigned)K), dim3(Geo<C, kAdam_SPT>::T), 0, st, n / C, n, K, W, wk,
-                       err_s, m, x, v_frozen, bits_s, scales_s, cf, status);
+    if (m)
+      hipLaunchKernelGGL((k_adam_compressed<C, kAdam_NT, kAdam_PF, kAdam_WPE, kAdam_SPT>),
+                         dim3((unsigned)K), dim3(Geo<C, kAdam_SPT>::T), 0, st, n / C, n, K, W, wk,
+                         err_s, m, x, v_frozen, bits_s, scales_s, cf, status);
+    else
+      hipLaunchKernelGGL((k_adam_compressed<C, kAdam_NT, kAdam_PF, kAdam_WPE, kAdam_SPT, true>),
+                         dim3((unsigned)K), dim3(Geo<C, kAdam_SPT>::T), 0, st, n / C, n, K, W, wk,
+                         err_s, m, x, v_frozen, bits_s, scales_s, cf, status);
   }
 };
 
@@ -341,12 +355,13 @@ int check_phase1(const char* fn, const onebit_layer_table* table, int32_t W,
   if (int rc = check_W(W, fn)) return rc;
   if (int rc = check_hparams(hp, fn)) return rc;
   if (int rc = check_workers(fn, W, grads, err_w, bits_w, scales_w, wk)) return rc;
-  const void* req[] = {err_s, m, v_frozen, v_fresh, bits_s, scales_s, ws};
-  const char* names[] = {"err_s", "m", "v_frozen", "v_fresh", "bits_s", "scales_s", "ws"};
-  for (int i = 0; i < 7; ++i) {
+  const void* req[] = {err_s, v_frozen, v_fresh, bits_s, scales_s, ws};
+  const char* names[] = {"err_s", "v_frozen", "v_fresh", "bits_s", "scales_s", "ws"};
+  for (int i = 0; i < 6; ++i) {
     if (!req[i]) return fail(ONEBIT_EINVAL, "%s: %s is NULL", fn, names[i]);
     if (!aligned16(req[i])) return fail(ONEBIT_EALIGN, "%s: %s is not 16-byte aligned", fn, names[i]);
   }
+  if (m && !aligned16(m)) return fail(ONEBIT_EALIGN, "%s: m is not 16-byte aligned", fn);
   return ONEBIT_OK;
 }
 
@@ -356,12 +371,13 @@ int check_phase2(const char* fn, const onebit_layer_table* table, const uint32_t
                  void* ws) {
   if (int rc = check_table(table, fn)) return rc;
   if (int rc = check_hparams(hp, fn)) return rc;
-  const void* req[] = {bits_s, scales_s, x, m, v_frozen, c_avg, f_prev, ws};
-  const char* names[] = {"bits_s", "scales_s", "x", "m", "v_frozen", "c_avg", "f_prev", "ws"};
-  for (int i = 0; i < 8; ++i) {
+  const void* req[] = {bits_s, scales_s, x, v_frozen, c_avg, f_prev, ws};
+  const char* names[] = {"bits_s", "scales_s", "x", "v_frozen", "c_avg", "f_prev", "ws"};
+  for (int i = 0; i < 7; ++i) {
     if (!req[i]) return fail(ONEBIT_EINVAL, "%s: %s is NULL", fn, names[i]);
     if (!aligned16(req[i])) return fail(ONEBIT_EALIGN, "%s: %s is not 16-byte aligned", fn, names[i]);
   }
+  if (m && !aligned16(m)) return fail(ONEBIT_EALIGN, "%s: m is not 16-byte aligned", fn);
   if (c_out && !aligned16(c_out)) return fail(ONEBIT_EALIGN, "%s: c_out is not 16-byte aligned", fn);
   return ONEBIT_OK;
 }
@@ -680,7 +696,7 @@ int onebit_adam_compressed_step(int64_t n, int32_t chunk, int32_t W, const float
   if (int rc = check_workers(__func__, W, grads, err_w, bits_w, scales_w, wk)) return rc;
   CHECK_PTR(err_s, "err_s");
   CHECK_PTR(x, "x");
-  CHECK_PTR(m, "m");
+  CHECK_OPT_PTR(m, "m");
   CHECK_PTR(v_frozen, "v_frozen");
   CHECK_PTR(bits_s, "bits_s");
   CHECK_PTR(scales_s, "scales_s");

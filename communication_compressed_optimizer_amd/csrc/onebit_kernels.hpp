@@ -537,7 +537,10 @@ k_decompress(int64_t k0, int64_t n, const uint32_t* __restrict__ bits,
 // error-compensated 1-bit compression of beta1*m + a1*g_w, then the server's
 // average of the W packed chunks and its own error-compensated
 // recompression.  On return bm holds beta1*m and nib the server's sign
-// nibbles; the server's scale is returned.  With PF, the chunk's slices of
+// nibbles; the server's scale is returned.  With PM (packed momentum) m is
+// not read: the momentum is the previous step's server output, which
+// bits_s/scales_s hold on entry (chunk k's words and scale are read by this
+// workgroup before its first barrier and rewritten after its last one).  With PF, the chunk's slices of
 // the two arrays the caller needs next (p0, p1) are loaded into d0, d1 just
 // before the server's chunk reduction, so they are in flight across it.
 //
@@ -548,7 +551,7 @@ k_decompress(int64_t k0, int64_t n, const uint32_t* __restrict__ bits,
 //   NT:  streaming (nontemporal) loads and stores for the element arrays.
 //   PF:  worker w+1's gradient and error are loaded before worker w's chunk
 //        reduction, so they are in flight across its barrier.
-template <int C, bool TAIL, bool NT, bool PF, int SPT>
+template <int C, bool TAIL, bool NT, bool PF, int SPT, bool PM>
 __device__ __forceinline__ float workers_and_server(const ChunkAt<C, TAIL> ch, int W,
                                                     const Workers& wk, float* __restrict__ err_s,
                                                     const float* __restrict__ m,
@@ -569,11 +572,21 @@ __device__ __forceinline__ float workers_and_server(const ChunkAt<C, TAIL> ch, i
     load_chunk<C, TAIL, NT, SPT>(wk.g[0], base, nk, gn);
     load_chunk<C, TAIL, NT, SPT>(wk.e[0], base, nk, en);
   }
-  load_chunk<C, TAIL, NT, SPT>(m, base, nk, bm);
+  if constexpr (PM) {
+    uint32_t pn[SPT];
+    load_sign_nibbles<C, SPT>(bits_s + ch.k * Geo<C>::WORDS, pn);
+    const float sp = scales_s[ch.k];
 #pragma unroll
-  for (int a = 0; a < SPT; ++a)
+    for (int a = 0; a < SPT; ++a)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) bm[a][c] = cf.beta1 * bm[a][c];
+      for (int c = 0; c < 4; ++c) bm[a][c] = cf.beta1 * signed_scale(pn, a, c, sp);
+  } else {
+    load_chunk<C, TAIL, NT, SPT>(m, base, nk, bm);
+#pragma unroll
+    for (int a = 0; a < SPT; ++a)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) bm[a][c] = cf.beta1 * bm[a][c];
+  }
 
   for (int w = 0; w < W; ++w) {
     SlotsN<SPT> z, e;
@@ -641,7 +654,7 @@ __device__ __forceinline__ float workers_and_server(const ChunkAt<C, TAIL> ch, i
 // statistic of the rescale: the maximum of the ratio q, or (RN, the
 // norm-ratio variant) the double sums of (sqrt(v_frozen)+eta)^2 and
 // (sqrt(v_fresh)+eta)^2.
-template <int C, bool TAIL, bool NT, bool PF, int SPT, bool RN>
+template <int C, bool TAIL, bool NT, bool PF, int SPT, bool RN, bool PM>
 __device__ __forceinline__ void pass_a_chunk(int64_t kk, const DevTable& tab, int W,
                                              const Workers& wk, float* __restrict__ err_s,
                                              const float* __restrict__ m,
@@ -661,9 +674,9 @@ __device__ __forceinline__ void pass_a_chunk(int64_t kk, const DevTable& tab, in
 
   SlotsN<SPT> bm, vf, vz;
   uint32_t nib[SPT];
-  const float s2 = workers_and_server<C, TAIL, NT, PF, SPT>(ch, W, wk, err_s, m, bits_s, scales_s,
-                                                            cf, status, lds, parity, bm, nib,
-                                                            v_fresh, v_frozen, vf, vz);
+  const float s2 = workers_and_server<C, TAIL, NT, PF, SPT, PM>(ch, W, wk, err_s, m, bits_s,
+                                                                scales_s, cf, status, lds, parity,
+                                                                bm, nib, v_fresh, v_frozen, vf, vz);
 
   // reconstructed gradient, fresh variance, rescale ratio
   if constexpr (!PF) {
@@ -702,7 +715,8 @@ __device__ __forceinline__ void pass_a_chunk(int64_t kk, const DevTable& tab, in
 // One workgroup per chunk; when the buffer ends in a partial chunk, block 0
 // takes it (its guarded code is slower, so it starts first and overlaps the
 // full chunks instead of trailing them).
-template <int C, bool NT = false, bool PF = false, int WPE = 1, int SPT = 4, bool RN = false>
+template <int C, bool NT = false, bool PF = false, int WPE = 1, int SPT = 4, bool RN = false,
+          bool PM = false>
 __global__ void __launch_bounds__((Geo<C, SPT>::T), WPE)
 k_compressed_pass_a(int64_t n_full, DevTable tab, int W, Workers wk, float* __restrict__ err_s,
                     const float* __restrict__ m, const float* __restrict__ v_frozen,
@@ -715,11 +729,11 @@ k_compressed_pass_a(int64_t n_full, DevTable tab, int W, Workers wk, float* __re
   __shared__ double dred[RN ? 2 * (Geo<C, SPT>::T / 64) : 1];
   const int64_t has_tail = tab.K - n_full;
   if (has_tail && blockIdx.x == 0)
-    pass_a_chunk<C, true, NT, PF, SPT, RN>(n_full, tab, W, wk, err_s, m, v_frozen, v_fresh, bits_s,
+    pass_a_chunk<C, true, NT, PF, SPT, RN, PM>(n_full, tab, W, wk, err_s, m, v_frozen, v_fresh, bits_s,
                                            scales_s, seg_max, seg_z, seg_f, cf, status, lds, red,
                                            dred);
   else
-    pass_a_chunk<C, false, NT, PF, SPT, RN>((int64_t)blockIdx.x - has_tail, tab, W, wk, err_s, m,
+    pass_a_chunk<C, false, NT, PF, SPT, RN, PM>((int64_t)blockIdx.x - has_tail, tab, W, wk, err_s, m,
                                             v_frozen, v_fresh, bits_s, scales_s, seg_max, seg_z,
                                             seg_f, cf, status, lds, red, dred);
 }
@@ -727,7 +741,7 @@ k_compressed_pass_a(int64_t n_full, DevTable tab, int W, Workers wk, float* __re
 // 1-bit Adam compression step, one pass per chunk: the compressed allreduce,
 // then x = x - lr*(mhat/(sqrt(v_frozen)+eta)) and m = mhat.  There is no
 // layerwise coefficient, so the update follows in the same pass.
-template <int C, bool TAIL, bool NT, bool PF, int SPT>
+template <int C, bool TAIL, bool NT, bool PF, int SPT, bool PM>
 __device__ __forceinline__ void adam_chunk(int64_t kk, int64_t n, int W, const Workers& wk,
                                            float* __restrict__ err_s, float* __restrict__ m,
                                            float* __restrict__ x,
@@ -739,9 +753,9 @@ __device__ __forceinline__ void adam_chunk(int64_t kk, int64_t n, int W, const W
   const ChunkAt<C, TAIL> ch(kk, n);
   SlotsN<SPT> bm, xx, vz;
   uint32_t nib[SPT];
-  const float s2 = workers_and_server<C, TAIL, NT, PF, SPT>(ch, W, wk, err_s, m, bits_s, scales_s,
-                                                            cf, status, lds, parity, bm, nib, x,
-                                                            v_frozen, xx, vz);
+  const float s2 = workers_and_server<C, TAIL, NT, PF, SPT, PM>(ch, W, wk, err_s, m, bits_s,
+                                                                scales_s, cf, status, lds, parity,
+                                                                bm, nib, x, v_frozen, xx, vz);
   if constexpr (!PF) {
     load_chunk<C, TAIL, NT, SPT>(x, ch.base, ch.nk, xx);
     load_chunk<C, TAIL, NT, SPT>(v_frozen, ch.base, ch.nk, vz);
@@ -755,12 +769,12 @@ __device__ __forceinline__ void adam_chunk(int64_t kk, int64_t n, int W, const W
       bm[a][c] = mh;
     }
   store_chunk<C, TAIL, NT, SPT>(x, ch.base, ch.nk, xx);
-  store_chunk<C, TAIL, NT, SPT>(m, ch.base, ch.nk, bm);
+  if constexpr (!PM) store_chunk<C, TAIL, NT, SPT>(m, ch.base, ch.nk, bm);
 }
 
 // One workgroup per chunk of an n-element buffer; block 0 takes the partial
 // last chunk, if any (as in k_compressed_pass_a).
-template <int C, bool NT = false, bool PF = false, int WPE = 1, int SPT = 4>
+template <int C, bool NT = false, bool PF = false, int WPE = 1, int SPT = 4, bool PM = false>
 __global__ void __launch_bounds__((Geo<C, SPT>::T), WPE)
 k_adam_compressed(int64_t n_full, int64_t n, int64_t K, int W, Workers wk,
                   float* __restrict__ err_s, float* __restrict__ m, float* __restrict__ x,
@@ -769,11 +783,11 @@ k_adam_compressed(int64_t n_full, int64_t n, int64_t K, int W, Workers wk,
   __shared__ float4 lds[2 * Geo<C, SPT>::T];
   const int64_t has_tail = K - n_full;
   if (has_tail && blockIdx.x == 0)
-    adam_chunk<C, true, NT, PF, SPT>(n_full, n, W, wk, err_s, m, x, v_frozen, bits_s, scales_s, cf,
-                                     status, lds);
+    adam_chunk<C, true, NT, PF, SPT, PM>(n_full, n, W, wk, err_s, m, x, v_frozen, bits_s, scales_s,
+                                         cf, status, lds);
   else
-    adam_chunk<C, false, NT, PF, SPT>((int64_t)blockIdx.x - has_tail, n, W, wk, err_s, m, x,
-                                      v_frozen, bits_s, scales_s, cf, status, lds);
+    adam_chunk<C, false, NT, PF, SPT, PM>((int64_t)blockIdx.x - has_tail, n, W, wk, err_s, m, x,
+                                          v_frozen, bits_s, scales_s, cf, status, lds);
 }
 
 // 1-bit Adam warmup: one Adam step, element-wise in one pass (mean gradient,
@@ -1027,7 +1041,8 @@ __device__ __forceinline__ void step_sizes(const DevTable& tab, int64_t k, int64
   }
 }
 
-// Compression step, pass B: x update with the per-tensor c, m = mhat.
+// Compression step, pass B: x update with the per-tensor c, m = mhat (m may
+// be NULL: packed momentum, the server's packed chunk is the state).
 template <int C, bool TAIL, bool NT>
 __device__ __forceinline__ void pass_b_chunk(int64_t kk, const DevTable& tab,
                                              const uint32_t* __restrict__ bits_s,
@@ -1053,7 +1068,7 @@ __device__ __forceinline__ void pass_b_chunk(int64_t kk, const DevTable& tab,
                                : xx[a][c] - (st[a][c] * d);
     }
   store_chunk<C, TAIL, NT>(x, ch.base, ch.nk, xx);
-  store_chunk<C, TAIL, NT>(m, ch.base, ch.nk, mh);
+  if (m) store_chunk<C, TAIL, NT>(m, ch.base, ch.nk, mh);  // NULL: packed momentum
 }
 
 template <int C, bool NT = false>

@@ -73,11 +73,14 @@ class DevRun:
         self.ob.onebit_lamb_freeze(self.table, self.wl.W, self.v, self.vf, self.e, self.err_s,
                                    self.c_sum, T_w, self.c_avg, self.f_prev, self.hp)
 
-    def compressed_step(self, step, fill=True):
+    def compressed_step(self, step, fill=True, packed=False):
+        """packed: the momentum is the previous step's server output
+        (bits_s, scales_s) and self.m is neither read nor written."""
         if fill:
             self.fill_grads(step)
         self.ob.onebit_lamb_compressed_step(
-            self.table, self.wl.W, self.g, self.e, self.err_s, self.x, self.m, self.v, self.vf,
+            self.table, self.wl.W, self.g, self.e, self.err_s, self.x,
+            None if packed else self.m, self.v, self.vf,
             self.c_avg, self.f_prev, self.c_out, self.bits_w, self.scales_w, self.bits_s,
             self.scales_s, self.hp, self.ws, self.status)
 
@@ -88,12 +91,19 @@ class DevRun:
         self.ob.onebit_adam_warmup_step(self.wl.N, self.wl.W, self.g, self.x, self.m, self.v,
                                         self.hp)
 
-    def adam_compressed_step(self, step, fill=True, chunk=None):
+    def adam_compressed_step(self, step, fill=True, chunk=None, packed=False):
         if fill:
             self.fill_grads(step)
         self.ob.onebit_adam_compressed_step(
-            self.wl.N, chunk or self.wl.chunk, self.wl.W, self.g, self.e, self.err_s, self.x, self.m,
-            self.v, self.bits_w, self.scales_w, self.bits_s, self.scales_s, self.hp, self.status)
+            self.wl.N, chunk or self.wl.chunk, self.wl.W, self.g, self.e, self.err_s, self.x,
+            None if packed else self.m, self.v, self.bits_w, self.scales_w, self.bits_s,
+            self.scales_s, self.hp, self.status)
+
+    def momentum_from_packed(self):
+        """The packed momentum (the server's last output) as fp32."""
+        out = self.torch.empty_like(self.m)
+        self.ob.onebit_decompress(self.wl.N, self.wl.chunk, self.bits_s, self.scales_s, out)
+        return out
 
     # -- SLAMB-style sparse stage ----------------------------------------
     def sparse_step(self, step, nsel, fill=True):

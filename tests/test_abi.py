@@ -108,9 +108,12 @@ def test_adam_argument_checks(ob):
     assert lib.onebit_adam_compressed_step(-5, 4096, 2, *args, hpr, None, None) == \
         ob.ONEBIT_EINVAL
     bad = list(args)
-    bad[4] = None                     # m
+    bad[3] = None                     # x (m may be NULL: packed momentum)
     assert lib.onebit_adam_compressed_step(10, 4096, 2, *bad, hpr, None, None) == ob.ONEBIT_EINVAL
-    assert "m is NULL" in ob.onebit_last_error()
+    assert "x is NULL" in ob.onebit_last_error()
+    bad = list(args)
+    bad[4] = P(4100)                  # m misaligned
+    assert lib.onebit_adam_compressed_step(10, 4096, 2, *bad, hpr, None, None) == ob.ONEBIT_EALIGN
     bad = list(args)
     bad[5] = P(4104)                  # v_frozen misaligned
     assert lib.onebit_adam_compressed_step(10, 4096, 2, *bad, hpr, None, None) == ob.ONEBIT_EALIGN
