@@ -43,6 +43,13 @@ def step_bytes(N, K, C, W):
     return N * (12 * W + 36) + packed
 
 
+def step_bytes_packed(N, K, C, W):
+    """The same step with packed momentum: the momentum is read as the
+    previous server signs and scales instead of fp32, and not written."""
+    packed = (W + 1) * K * (C // 8 + 4)
+    return N * (12 * W + 28) + packed + K * (C // 8 + 4)
+
+
 def phase1_bytes(N, K, C, W):
     """Algorithmic bytes of the phase-1 kernel: m read; per worker g read,
     e read and written; e_s read and written; v_fresh read and written;
@@ -177,38 +184,44 @@ def main():
         return bench_sparse(args, wl, ob, torch, table, hp, g, e, x, m, v, vf, c_avg, status,
                             stream)
 
-    def step(ev=None):
+    def step(ev=None, mm=m):
         if ev is not None:
             ev[0].record(stream)
-        ob.onebit_lamb_compress_average(table, W, g, e, err_s, m, v, vf, bits_w, scales_w, bits_s,
+        ob.onebit_lamb_compress_average(table, W, g, e, err_s, mm, v, vf, bits_w, scales_w, bits_s,
                                         scales_s, hp, ws, status, stream)
         if ev is not None:
             ev[1].record(stream)
-        ob.onebit_lamb_rescale_update(table, bits_s, scales_s, x, m, v, c_avg, f_prev, c_out, hp,
+        ob.onebit_lamb_rescale_update(table, bits_s, scales_s, x, mm, v, c_avg, f_prev, c_out, hp,
                                       ws, status, stream)
         if ev is not None:
             ev[2].record(stream)
 
+    def timed(mm):
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(evs[i], mm)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        p1 = [a.elapsed_time(b) for a, b, _ in evs]
+        p2 = [b.elapsed_time(c) for _, b, c in evs]
+        return (t1 - t0) * 1e3 / args.steps, sum(p1) / len(p1), sum(p2) / len(p2)
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    ms_per_step, p1_ms, p2_ms = timed(m)
     st = int(status.item())
     if st:
         log(f"[bench] WARNING: status flags {st} (non-finite scale or statistic)")
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    p1 = sorted(a.elapsed_time(b) for a, b, _ in evs)
-    p2 = sorted(b.elapsed_time(c) for _, b, c in evs)
-    p1_ms = sum(p1) / len(p1)
-    p2_ms = sum(p2) / len(p2)
     log(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step (phase1 {p1_ms:.3f} ms, "
         f"phase2 {p2_ms:.3f} ms)")
+    # context: the same steps with packed momentum (m = NULL: the momentum is
+    # the previous server output, bit-identical results, no fp32 copy)
+    pm_ms, pm_p1, pm_p2 = timed(None)
+    log(f"[bench] packed momentum {args.steps} steps: {pm_ms:.3f} ms/step (phase1 {pm_p1:.3f} ms, "
+        f"phase2 {pm_p2:.3f} ms)")
 
     # context: one LAMB warmup step on the same table (after the timed
     # compression steps; it reuses the same buffers)
@@ -226,6 +239,7 @@ def main():
     warm_bytes = N * (4 * W + 36)
 
     sbytes = step_bytes(N, K, C, W)
+    pm_bytes = step_bytes_packed(N, K, C, W)
     abytes = phase1_bytes(N, K, C, W)
     achieved = abytes / (p1_ms * 1e-3) / 1e9
     step_gbps = sbytes / (ms_per_step * 1e-3) / 1e9
@@ -259,6 +273,12 @@ def main():
         "phase_ms": {"compress_average": p1_ms, "rescale_update": p2_ms},
         "warmup_step": {"ms": warm_ms, "params_per_s": N / (warm_ms * 1e-3),
                         "GBps": warm_bytes / (warm_ms * 1e-3) / 1e9, "bytes": warm_bytes},
+        "packed_momentum": {
+            "ms_per_step": pm_ms, "params_per_s": N / (pm_ms * 1e-3),
+            "phase_ms": {"compress_average": pm_p1, "rescale_update": pm_p2},
+            "step_bytes": pm_bytes, "GBps": pm_bytes / (pm_ms * 1e-3) / 1e9,
+            "note": "same step with m = NULL: the momentum is the previous server output "
+                    "(bits_s, scales_s), outputs bit-identical to the fp32-momentum step"},
         "roofline": {"bound": "hbm", "kernel": "k_compressed_pass_a<4096>",
                      "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
@@ -274,27 +294,33 @@ def bench_adam(args, wl, ob, torch, hp, g, e, err_s, x, m, v, bits_w, scales_w, 
     compression step (v is the frozen variance)."""
     C, N, W, K = wl.chunk, wl.N, wl.W, wl.K
 
-    def step():
-        ob.onebit_adam_compressed_step(N, C, W, g, e, err_s, x, m, v, bits_w, scales_w, bits_s,
+    def step(mm=m):
+        ob.onebit_adam_compressed_step(N, C, W, g, e, err_s, x, mm, v, bits_w, scales_w, bits_s,
                                        scales_s, hp, status, stream)
+
+    def timed(mm):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev[0].record(stream)
+        for _ in range(args.steps):
+            step(mm)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        return (t1 - t0) * 1e3 / args.steps, ev[0].elapsed_time(ev[1]) / args.steps
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev[0].record(stream)
-    for _ in range(args.steps):
-        step()
-    ev[1].record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    ms_per_step, k_ms = timed(m)
     if int(status.item()):
         log(f"[bench] WARNING: status flags {int(status.item())}")
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    k_ms = ev[0].elapsed_time(ev[1]) / args.steps
     log(f"[bench] adam {args.steps} steps: {ms_per_step:.3f} ms/step (kernel {k_ms:.3f} ms)")
+    pm_ms, pm_k = timed(None)
+    log(f"[bench] adam packed momentum {args.steps} steps: {pm_ms:.3f} ms/step "
+        f"(kernel {pm_k:.3f} ms)")
+    pm_bytes = adam_bytes(N, K, C, W) - 8 * N + K * (C // 8 + 4)
 
     for _ in range(2):
         ob.onebit_adam_warmup_step(N, W, g, x, m, v, hp, stream)
@@ -339,6 +365,11 @@ def bench_adam(args, wl, ob, torch, hp, g, e, err_s, x, m, v, bits_w, scales_w, 
         "step_bytes": abytes,
         "warmup_step": {"ms": warm_ms, "params_per_s": N / (warm_ms * 1e-3),
                         "GBps": warm_bytes / (warm_ms * 1e-3) / 1e9, "bytes": warm_bytes},
+        "packed_momentum": {
+            "ms_per_step": pm_ms, "params_per_s": N / (pm_ms * 1e-3), "kernel_ms": pm_k,
+            "step_bytes": pm_bytes, "GBps": pm_bytes / (pm_k * 1e-3) / 1e9,
+            "note": "same step with m = NULL: the momentum is the previous server output, "
+                    "outputs bit-identical"},
         "roofline": {"bound": "hbm", "kernel": "k_adam_compressed<4096>",
                      "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
