@@ -182,6 +182,11 @@ constexpr bool kPassA_PF = false;  // next-worker prefetch
 constexpr int kPassA_WPE = 6;      // minimum waves per SIMD
 constexpr int kPassA_SPT = 4;      // float4 slots per thread (workgroup = C / (4 * SPT))
 constexpr bool kPassB_NT = true;
+// LAMB warmup passes (BERT-Large, W = 8, interleaved on one box): streaming
+// accesses take pass 1 from 3.30 to 2.95 ms and pass 2 from 0.97 to 0.87 ms;
+// a 5- or 6-wave register cap on pass 1 is slower (3.07, 3.44 ms) and one on
+// the 1-bit Adam warmup changes nothing (3.19-3.22 against 3.20 ms).
+constexpr bool kWarm_NT = true;
 
 // The 1-bit Adam compression kernel shares pass A's compressed allreduce and
 // takes the same settings.
@@ -226,11 +231,13 @@ struct LaunchWarmup {
   static void run(const onebit_layer_table* t, int W, const Workers& wk, float* x, float* m,
                   float* v, float* c_sum, float* c_out, const Coef& cf, const Ws& ws,
                   int32_t* status, hipStream_t st) {
-    launch_chunks<C>(t->N, st, k_warmup_pass1<C, false>, k_warmup_pass1<C, true>, t->dev, W, wk,
+    launch_chunks<C>(t->N, st, k_warmup_pass1<C, false, kWarm_NT>, k_warmup_pass1<C, true, kWarm_NT>,
+                     t->dev, W, wk,
                      (const float*)x, m, v, ws.seg_x, ws.seg_u, cf);
     hipLaunchKernelGGL(k_warmup_finalize<256>, dim3((unsigned)t->L), dim3(256), 0, st, t->dev,
                        ws.seg_x, ws.seg_u, c_sum, ws.c_layer, c_out, cf, status);
-    launch_chunks<C>(t->N, st, k_warmup_pass2<C, false>, k_warmup_pass2<C, true>, t->dev,
+    launch_chunks<C>(t->N, st, k_warmup_pass2<C, false, kWarm_NT>, k_warmup_pass2<C, true, kWarm_NT>,
+                     t->dev,
                      (const float*)m, (const float*)v, x, (const float*)ws.c_layer, cf);
   }
 };

@@ -792,8 +792,8 @@ k_adam_compressed(int64_t n_full, int64_t n, int64_t K, int W, Workers wk,
 
 // 1-bit Adam warmup: one Adam step, element-wise in one pass (mean gradient,
 // moments, x = x - lr*(m/(sqrt(v)+eta))).
-template <int C, bool TAIL>
-__global__ void __launch_bounds__(C / 16)
+template <int C, bool TAIL, int WPE = 1>
+__global__ void __launch_bounds__(C / 16, WPE)
 k_adam_warmup(int64_t k0, int64_t n, int W, Workers wk, float* __restrict__ x,
               float* __restrict__ m, float* __restrict__ v, Coef cf) {
   const ChunkAt<C, TAIL> ch(k0 + (int64_t)blockIdx.x, n);
@@ -1086,9 +1086,9 @@ k_compressed_pass_b(int64_t n_full, DevTable tab, const uint32_t* __restrict__ b
 }
 
 // Warmup pass 1: mean gradient, moments, per-(chunk, tensor) sums of x^2 and
-// u^2 in double.
-template <int C, bool TAIL>
-__global__ void __launch_bounds__(C / 16)
+// u^2 in double.  NT: streaming accesses; WPE: minimum waves per SIMD.
+template <int C, bool TAIL, bool NT = false, int WPE = 1>
+__global__ void __launch_bounds__(C / 16, WPE)
 k_warmup_pass1(int64_t k0, DevTable tab, int W, Workers wk, const float* __restrict__ x,
                float* __restrict__ m, float* __restrict__ v, double* __restrict__ seg_x,
                double* __restrict__ seg_u, Coef cf) {
@@ -1098,19 +1098,19 @@ k_warmup_pass1(int64_t k0, DevTable tab, int W, Workers wk, const float* __restr
   const int64_t base = ch.base;
   const int nk = ch.nk;
   Slots gs;
-  load_chunk<C, TAIL>(wk.g[0], base, nk, gs);
+  load_chunk<C, TAIL, NT>(wk.g[0], base, nk, gs);
   for (int w = 1; w < W; ++w) {
     Slots g;
-    load_chunk<C, TAIL>(wk.g[w], base, nk, g);
+    load_chunk<C, TAIL, NT>(wk.g[w], base, nk, g);
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
       for (int c = 0; c < 4; ++c) gs[a][c] = gs[a][c] + g[a][c];
   }
   Slots mm, vv, u, xx;
-  load_chunk<C, TAIL>(m, base, nk, mm);
-  load_chunk<C, TAIL>(v, base, nk, vv);
-  load_chunk<C, TAIL>(x, base, nk, xx);
+  load_chunk<C, TAIL, NT>(m, base, nk, mm);
+  load_chunk<C, TAIL, NT>(v, base, nk, vv);
+  load_chunk<C, TAIL, NT>(x, base, nk, xx);
   const float fW = (float)W;
 #pragma unroll
   for (int a = 0; a < 4; ++a)
@@ -1121,8 +1121,8 @@ k_warmup_pass1(int64_t k0, DevTable tab, int W, Workers wk, const float* __restr
       vv[a][c] = (cf.beta2 * vv[a][c]) + (cf.a2 * (gb * gb));
       u[a][c] = warmup_dir(mm[a][c], vv[a][c], xx[a][c], cf);
     }
-  store_chunk<C, TAIL>(m, base, nk, mm);
-  store_chunk<C, TAIL>(v, base, nk, vv);
+  store_chunk<C, TAIL, NT>(m, base, nk, mm);
+  store_chunk<C, TAIL, NT>(v, base, nk, vv);
   const int l0 = tab.l0[ch.k];
   const int l1 = tab.l1[ch.k];
   const int sb = tab.seg[ch.k];
@@ -1175,15 +1175,15 @@ k_warmup_finalize(DevTable tab, const double* __restrict__ seg_x, const double* 
 }
 
 // Warmup pass 2: x = x - (lr*c_l)*u with u recomputed from the new m, v.
-template <int C, bool TAIL>
+template <int C, bool TAIL, bool NT = false>
 __global__ void __launch_bounds__(C / 16)
 k_warmup_pass2(int64_t k0, DevTable tab, const float* __restrict__ m, const float* __restrict__ v,
                float* __restrict__ x, const float* __restrict__ c_layer, Coef cf) {
   const ChunkAt<C, TAIL> ch(k0 + (int64_t)blockIdx.x, tab.N);
   Slots mm, vv, xx, st;
-  load_chunk<C, TAIL>(m, ch.base, ch.nk, mm);
-  load_chunk<C, TAIL>(v, ch.base, ch.nk, vv);
-  load_chunk<C, TAIL>(x, ch.base, ch.nk, xx);
+  load_chunk<C, TAIL, NT>(m, ch.base, ch.nk, mm);
+  load_chunk<C, TAIL, NT>(v, ch.base, ch.nk, vv);
+  load_chunk<C, TAIL, NT>(x, ch.base, ch.nk, xx);
   step_sizes<C, TAIL>(tab, ch.k, ch.base, c_layer, cf.lr, st);
 #pragma unroll
   for (int a = 0; a < 4; ++a)
@@ -1192,7 +1192,7 @@ k_warmup_pass2(int64_t k0, DevTable tab, const float* __restrict__ m, const floa
       const float u = warmup_dir(mm[a][c], vv[a][c], xx[a][c], cf);
       xx[a][c] = xx[a][c] - (st[a][c] * u);
     }
-  store_chunk<C, TAIL>(x, ch.base, ch.nk, xx);
+  store_chunk<C, TAIL, NT>(x, ch.base, ch.nk, xx);
 }
 
 // Freeze, element part: v_fresh = v, error buffers cleared.
