@@ -145,6 +145,8 @@ RAGGED = [
     [4096 * 3],                               # chunk-aligned single tensor
     [5, 7, 11, 13] * 300 + [2048 * 3 + 1],   # many tiny tensors per chunk
     [256 * 256, 256, 1000 * 64],              # the three-tensor table
+    [10, 20, 30],                             # the whole table inside one partial chunk
+    [1],                                      # a single element
 ]
 
 
