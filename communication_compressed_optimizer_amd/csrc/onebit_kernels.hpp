@@ -455,7 +455,7 @@ __device__ __forceinline__ void segment_sums(const DevTable& tab, int64_t k, int
 // ===========================================================================
 
 // onebit_compress_ef: z = in + err -> bits, scales, err
-template <int C, bool TAIL>
+template <int C, bool TAIL, bool NT = false>
 __global__ void __launch_bounds__(C / 16)
 k_compress_ef(int64_t k0, int64_t n, const float* __restrict__ in, float* __restrict__ err,
               uint32_t* __restrict__ bits, float* __restrict__ scales, int32_t* status) {
@@ -463,15 +463,15 @@ k_compress_ef(int64_t k0, int64_t n, const float* __restrict__ in, float* __rest
   int parity = 0;
   const ChunkAt<C, TAIL> ch(k0 + (int64_t)blockIdx.x, n);
   Slots z, e;
-  load_chunk<C, TAIL>(in, ch.base, ch.nk, z);
-  load_chunk<C, TAIL>(err, ch.base, ch.nk, e);
+  load_chunk<C, TAIL, NT>(in, ch.base, ch.nk, z);
+  load_chunk<C, TAIL, NT>(err, ch.base, ch.nk, e);
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int c = 0; c < 4; ++c) z[a][c] = z[a][c] + e[a][c];
   uint32_t nib[4];
   const float s = compress_slots<C, TAIL>(z, ch.nk, lds, parity, nib);
-  store_chunk<C, TAIL>(err, ch.base, ch.nk, z);
+  store_chunk<C, TAIL, NT>(err, ch.base, ch.nk, z);
   store_sign_words<C>(bits + ch.k * Geo<C>::WORDS, nib);
   if (threadIdx.x == 0) {
     scales[ch.k] = s;
@@ -480,7 +480,7 @@ k_compress_ef(int64_t k0, int64_t n, const float* __restrict__ in, float* __rest
 }
 
 // onebit_average_packed: y = mean of the workers' +-s, + err_s -> recompress
-template <int C, bool TAIL>
+template <int C, bool TAIL, bool NT = false>
 __global__ void __launch_bounds__(C / 16)
 k_average_packed(int64_t k0, int64_t n, int W, PackedIn pin, float* __restrict__ err_s,
                  uint32_t* __restrict__ bits_out, float* __restrict__ scales_out, int32_t* status) {
@@ -500,7 +500,7 @@ k_average_packed(int64_t k0, int64_t n, int W, PackedIn pin, float* __restrict__
         acc[a][c] = w == 0 ? v : acc[a][c] + v;
       }
   }
-  load_chunk<C, TAIL>(err_s, ch.base, ch.nk, y);
+  load_chunk<C, TAIL, NT>(err_s, ch.base, ch.nk, y);
   const float fW = (float)W;
 #pragma unroll
   for (int a = 0; a < 4; ++a)
@@ -508,7 +508,7 @@ k_average_packed(int64_t k0, int64_t n, int W, PackedIn pin, float* __restrict__
     for (int c = 0; c < 4; ++c) y[a][c] = (acc[a][c] / fW) + y[a][c];
   uint32_t nib[4];
   const float s = compress_slots<C, TAIL>(y, ch.nk, lds, parity, nib);
-  store_chunk<C, TAIL>(err_s, ch.base, ch.nk, y);
+  store_chunk<C, TAIL, NT>(err_s, ch.base, ch.nk, y);
   store_sign_words<C>(bits_out + ch.k * Geo<C>::WORDS, nib);
   if (threadIdx.x == 0) {
     scales_out[ch.k] = s;
@@ -517,7 +517,7 @@ k_average_packed(int64_t k0, int64_t n, int W, PackedIn pin, float* __restrict__
 }
 
 // onebit_decompress
-template <int C, bool TAIL>
+template <int C, bool TAIL, bool NT = false>
 __global__ void __launch_bounds__(C / 16)
 k_decompress(int64_t k0, int64_t n, const uint32_t* __restrict__ bits,
              const float* __restrict__ scales, float* __restrict__ out) {
@@ -530,7 +530,7 @@ k_decompress(int64_t k0, int64_t n, const uint32_t* __restrict__ bits,
   for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int c = 0; c < 4; ++c) o[a][c] = signed_scale(nib, a, c, s);
-  store_chunk<C, TAIL>(out, ch.base, ch.nk, o);
+  store_chunk<C, TAIL, NT>(out, ch.base, ch.nk, o);
 }
 
 // The compressed allreduce of one chunk's momentum: every worker's
