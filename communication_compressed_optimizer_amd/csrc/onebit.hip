@@ -198,7 +198,9 @@ constexpr bool kAdam_NT = true;
 constexpr bool kAdam_PF = false;
 constexpr int kAdam_WPE = 6;
 constexpr int kAdam_SPT = 4;
-// Streaming accesses in the sparse-stage kernel.
+// Sparse-stage kernel (BERT-Large, W = 8, 1 of 64 blocks, interleaved):
+// streaming accesses 6.36 ms against 6.66 ms plain; a 5- or 6-wave register
+// cap changes nothing (6.38 ms), so it runs uncapped (104 VGPRs, no spills).
 constexpr bool kSparse_NT = true;
 // Chunk geometry of the element-wise 1-bit Adam warmup kernel (any chunk
 // gives the same result; this one gives 256-thread workgroups).

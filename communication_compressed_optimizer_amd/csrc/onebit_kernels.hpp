@@ -962,8 +962,8 @@ __device__ __forceinline__ void sparse_chunk(int64_t kk, const DevTable& tab, in
 }
 
 // One workgroup per chunk; block 0 takes the partial last chunk, if any.
-template <int C, bool NT = true>
-__global__ void __launch_bounds__(C / 16)
+template <int C, bool NT = true, int WPE = 1>
+__global__ void __launch_bounds__(C / 16, WPE)
 k_sparse_step(int64_t n_full, DevTable tab, int W, int nsel, const int32_t* __restrict__ sel,
               Workers wk, WorkerVals vals_w, float* __restrict__ x, float* __restrict__ m,
               const float* __restrict__ v_frozen, float* __restrict__ v_fresh,
