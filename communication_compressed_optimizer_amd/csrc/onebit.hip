@@ -123,8 +123,10 @@ int check_W(int32_t W, const char* fn) {
   return ONEBIT_OK;
 }
 
-// Workspace layout: [seg_x: S doubles][seg_u: S doubles][c_layer: L floats];
-// the compression step reuses the first S floats as seg_max.
+// Workspace layout: [seg_x: S doubles][seg_u: S doubles][c_layer: L floats].
+// The warmup keeps the per-segment sums of x^2 and u^2 there; the
+// compression step reuses the first S floats as seg_max, or (norm-ratio
+// rescale) seg_x and seg_u for the sums of (sqrt(v)+eta)^2.
 struct Ws {
   double* seg_x;
   double* seg_u;
@@ -176,7 +178,8 @@ void launch_chunks(int64_t n, hipStream_t st, KF kfull, KT ktail, A... args) {
 // into the grid, streaming with a 6-wave register cap 7.05 ms, uncapped 7.39,
 // 7-wave cap 7.44, 8-wave cap 7.89 -- the cap's spills are reloaded every
 // worker iteration, so the best cap depends on where they land; prefetching
-// the next worker, or keeping beta1*m in LDS, did not help).
+// the next worker, keeping beta1*m in LDS, or keeping the workers' signs in
+// LDS and summing after the loop (no spills, 3.5% slower) did not help).
 constexpr bool kPassA_NT = true;   // streaming loads and stores
 constexpr bool kPassA_PF = false;  // next-worker prefetch
 constexpr int kPassA_WPE = 6;      // minimum waves per SIMD

@@ -1,10 +1,13 @@
-// HIP kernels of the 1-bit LAMB step for gfx950 (CDNA4, 64-wide waves).
+// HIP kernels of the 1-bit LAMB step for gfx950 (CDNA4, 64-wide waves), and
+// of the 1-bit Adam mode and the SLAMB-style sparse stage built on the same
+// pieces.
 //
 // Every kernel that touches chunks runs one workgroup per chunk of C
-// elements with T = C/16 threads; thread t owns the four float4 slots
-// p = t + T*k (k = 0..3) of its chunk, i.e. chunk elements 4p..4p+3.  The
-// loads and stores of a wave are therefore 64 consecutive float4 (1 KiB) per
-// slot: fully coalesced dwordx4 traffic.
+// elements with T = C/(4*SPT) threads (SPT = 4 float4 slots per thread unless
+// a kernel says otherwise: T = C/16); thread t owns the slots p = t + T*k
+// (k = 0..SPT-1) of its chunk, i.e. chunk elements 4p..4p+3.  The loads and
+// stores of a wave are therefore 64 consecutive float4 (1 KiB) per slot:
+// fully coalesced dwordx4 traffic.
 //
 // Chunk scale.  The sum of squares of a chunk is the stride-halving tree
 // t[j] += t[j+h], h = C/2, ..., 1 (zero past the last valid element), which
