@@ -1,0 +1,191 @@
+"""Bounds and coverage of every entry point's writes, on the GPU.
+
+Every device argument lives inside a larger allocation with canary words on
+both sides; after the calls, every canary must be intact (no write outside
+an argument).  Outputs that the entry point must write in full (packed signs
+and scales, transmitted values, per-tensor coefficients) are filled with a
+poison pattern first; afterwards no poison may remain inside them.  Sizes are
+ragged and small, so chunk tails, one-chunk and one-element tables are all
+exercised.
+"""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("no GPU", allow_module_level=True)
+
+import communication_compressed_optimizer_amd as ob  # noqa: E402
+from synth.workloads import HPARAMS, Workload  # noqa: E402
+
+PAD = 64                       # canary words on each side (keeps 16-byte alignment)
+CANARY = 0x5A5AA5A5
+POISON = 0x7FC0DEAD            # a NaN pattern for floats
+
+
+class Arena:
+    """Device arrays with canary words around each."""
+
+    def __init__(self):
+        self.blocks = []
+
+    def take(self, n, dtype=torch.float32, fill=None):
+        n = max(int(n), 1)
+        full = torch.full((n + 2 * PAD,), CANARY, dtype=torch.int32, device="cuda")
+        if fill is not None:
+            full[PAD:PAD + n] = fill
+        self.blocks.append((full, n))
+        return full[PAD:PAD + n].view(dtype)
+
+    def check(self):
+        torch.cuda.synchronize()
+        for i, (full, n) in enumerate(self.blocks):
+            head = full[:PAD].cpu().numpy()
+            tail = full[PAD + n:].cpu().numpy()
+            assert np.all(head == CANARY) and np.all(tail == CANARY), f"canary {i} (n={n}) overwritten"
+
+
+def poisoned(t):
+    return t.view(torch.int32)
+
+
+def no_poison(t):
+    return not bool((t.view(torch.int32) == POISON).any().item())
+
+
+def fill_normal(t, seed, std):
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    t.copy_(torch.randn(t.numel(), generator=g, device="cuda") * std)
+
+
+TABLES = [[1], [10, 20, 30], [4096 * 2 + 7, 3, 1000], [1, 3, 4095, 4097, 100, 8192, 17]]
+
+
+@pytest.mark.parametrize("numels", TABLES)
+@pytest.mark.parametrize("chunk", [1024, 4096])
+@pytest.mark.parametrize("W", [1, 3])
+def test_lamb_entry_points_stay_in_bounds(numels, chunk, W):
+    table = ob.LayerTable(numels, chunk)
+    N, K, L = table.N, table.K, len(numels)
+    words = K * chunk // 32
+    A = Arena()
+    f = lambda: A.take(N)                               # noqa: E731
+    x, m, v, vf, err_s = f(), f(), f(), f(), A.take(N, fill=0)
+    g = [f() for _ in range(W)]
+    e = [A.take(N, fill=0) for _ in range(W)]
+    for i, t in enumerate([x, m] + g):
+        fill_normal(t, i, 0.02)
+    v.copy_(torch.rand(N, device="cuda") * 1e-4)
+    m.zero_()
+    bits_w = [A.take(words, torch.int32, POISON) for _ in range(W)]
+    scales_w = [A.take(K, torch.float32, POISON) for _ in range(W)]
+    bits_s = A.take(words, torch.int32, POISON)
+    scales_s = A.take(K, torch.float32, POISON)
+    c_sum = A.take(L, fill=0)
+    c_avg, f_prev = A.take(L), A.take(L)
+    c_out = A.take(L, torch.float32, POISON)
+    ws = A.take((table.workspace_size(W) + 3) // 4, torch.int32).view(torch.uint8)
+    status = A.take(1, torch.int32, 0)
+    hp = ob.onebit_hparams(**HPARAMS)
+    for _ in range(2):
+        ob.onebit_lamb_warmup_step(table, W, g, x, m, v, c_sum, c_out, hp, ws, status)
+    torch.cuda.synchronize()
+    assert no_poison(c_out)
+    c_out.view(torch.int32).fill_(POISON)
+    ob.onebit_lamb_freeze(table, W, v, vf, e, err_s, c_sum, 2, c_avg, f_prev, hp)
+    for mm in (m, None, None):                          # fp32, then packed momentum
+        ob.onebit_lamb_compressed_step(table, W, g, e, err_s, x, mm, v, vf, c_avg, f_prev, c_out,
+                                       bits_w, scales_w, bits_s, scales_s, hp, ws, status)
+        torch.cuda.synchronize()
+        for t in bits_w + scales_w + [bits_s, scales_s, c_out]:
+            assert no_poison(t)
+        for t in bits_w + scales_w + [c_out]:
+            poisoned(t).fill_(POISON)
+    hp.rho_mode = ob.ONEBIT_RHO_NORM_RATIO
+    ob.onebit_lamb_compressed_step(table, W, g, e, err_s, x, m, v, vf, c_avg, f_prev, c_out,
+                                   bits_w, scales_w, bits_s, scales_s, hp, ws, status)
+    torch.cuda.synchronize()
+    assert no_poison(c_out)
+    # the codec entry points on the same buffers
+    bits_o = A.take(words, torch.int32, POISON)
+    scales_o = A.take(K, torch.float32, POISON)
+    ob.onebit_compress_ef(N, chunk, x, err_s, bits_o, scales_o, status)
+    torch.cuda.synchronize()
+    assert no_poison(bits_o) and no_poison(scales_o)
+    poisoned(bits_o).fill_(POISON)
+    poisoned(scales_o).fill_(POISON)
+    ob.onebit_average_packed(N, chunk, W, bits_w, scales_w, err_s, bits_o, scales_o, status)
+    out = A.take(N, torch.float32, POISON)
+    ob.onebit_decompress(N, chunk, bits_o, scales_o, out)
+    torch.cuda.synchronize()
+    assert no_poison(bits_o) and no_poison(scales_o) and no_poison(out)
+    A.check()
+
+
+@pytest.mark.parametrize("n", [1, 1000, 3 * 4096 + 5])
+@pytest.mark.parametrize("W", [1, 4])
+def test_adam_entry_points_stay_in_bounds(n, W):
+    chunk = 4096
+    K = (n + chunk - 1) // chunk
+    words = K * chunk // 32
+    A = Arena()
+    x, m, v = A.take(n), A.take(n, fill=0), A.take(n, fill=0)
+    err_s = A.take(n, fill=0)
+    g = [A.take(n) for _ in range(W)]
+    e = [A.take(n, fill=0) for _ in range(W)]
+    for i, t in enumerate([x] + g):
+        fill_normal(t, 10 + i, 0.02)
+    bits_w = [A.take(words, torch.int32, POISON) for _ in range(W)]
+    scales_w = [A.take(K, torch.float32, POISON) for _ in range(W)]
+    bits_s = A.take(words, torch.int32, POISON)
+    scales_s = A.take(K, torch.float32, POISON)
+    status = A.take(1, torch.int32, 0)
+    hp = ob.onebit_hparams(**HPARAMS)
+    hp.bias_step = 1
+    ob.onebit_adam_warmup_step(n, W, g, x, m, v, hp)
+    hp.bias_step = 0
+    for mm in (m, None):
+        ob.onebit_adam_compressed_step(n, chunk, W, g, e, err_s, x, mm, v, bits_w, scales_w,
+                                       bits_s, scales_s, hp, status)
+        torch.cuda.synchronize()
+        for t in bits_w + scales_w + [bits_s, scales_s]:
+            assert no_poison(t)
+        for t in bits_w + scales_w:
+            poisoned(t).fill_(POISON)
+    A.check()
+
+
+@pytest.mark.parametrize("numels", TABLES)
+@pytest.mark.parametrize("nsel", [1, 3])
+def test_sparse_entry_point_stays_in_bounds(numels, nsel):
+    W, chunk = 3, 4096
+    table = ob.LayerTable(numels, chunk)
+    N, K, L = table.N, table.K, len(numels)
+    wl = Workload("bounds", numels, W=W, chunk=chunk)
+    A = Arena()
+    x, m, v, vf = A.take(N), A.take(N), A.take(N), A.take(N)
+    g = [A.take(N) for _ in range(W)]
+    e = [A.take(N, fill=0) for _ in range(W)]
+    for i, t in enumerate([x, m] + g):
+        fill_normal(t, 20 + i, 0.02)
+    v.copy_(torch.rand(N, device="cuda") * 1e-4)
+    vf.copy_(v)
+    c_avg = A.take(L)
+    c_avg.fill_(1.0)
+    per = nsel * 64
+    vals_w = [A.take(K * per, torch.float32, POISON) for _ in range(W)]
+    vals_s = A.take(K * per, torch.float32, POISON)
+    sel = A.take(K, torch.int32)
+    status = A.take(1, torch.int32, 0)
+    hp = ob.onebit_hparams(**HPARAMS)
+    for step in range(2):
+        sel.copy_(torch.from_numpy(wl.selection(step)).cuda())
+        ob.onebit_sparse_compressed_step(table, W, nsel, sel, g, e, x, m, v, vf, c_avg, vals_w,
+                                         vals_s, hp, status)
+        torch.cuda.synchronize()
+        for t in vals_w + [vals_s]:
+            assert no_poison(t)
+            poisoned(t).fill_(POISON)
+    A.check()
