@@ -11,10 +11,14 @@ are synthetic (seeded counter-based generator) and already resident in HBM
 when the timed region starts; the gradient buffers are filled once and
 reused by every step (the optimizer state still evolves step to step).
 
-Prints one JSON line.  `value` is parameters per second for the step;
-`roofline` is the dominant kernel (phase 1: compression, average, rescale
-statistics) timed with HIP events on its stream; `cpu_baseline` is the
-single-threaded CPU oracle on a bounded window of the same workload.
+Prints one JSON line.  `value` is parameters per second for the step with
+fp32 momentum; `packed_momentum` times the same step with the momentum kept
+as the server's packed output (bit-identical results); `roofline` is the
+dominant kernel (phase 1: compression, average, rescale statistics) timed
+with HIP events on its stream; `cpu_baseline` is the single-threaded CPU
+oracle on a bounded window of the same workload.  `--method adam` and
+`--method sparse` time the 1-bit Adam mode and the SLAMB-style sparse stage
+on the same buffers instead.
 """
 import argparse
 import json
