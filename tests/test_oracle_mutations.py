@@ -2,11 +2,12 @@
 
 Each case plants one mistake in a copy of oracle.c (on the CPU only),
 builds it, and runs the pin tests against the broken build in a fresh
-process: at least one pin has to fail.
+process: at least one pin has to fail.  The cases run several at a time.
 """
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import pytest
 
@@ -87,24 +88,41 @@ MUTATIONS = {
 }
 
 
+def _run_mutation(name, source, workdir):
+    """Builds oracle.c with one planted mistake and runs the pins against it
+    in a fresh process; returns (pytest exit code, tail of its output)."""
+    old, new = MUTATIONS[name]
+    assert source.count(old) == 1, f"mutation anchor not unique: {old!r}"
+    os.makedirs(workdir, exist_ok=True)
+    src = os.path.join(workdir, "oracle.c")
+    with open(src, "w") as f:
+        f.write(source.replace(old, new))
+    lib = os.path.join(workdir, "liboracle_mut.so")
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+                    "-I", os.path.join(ROOT, "oracle"), "-o", lib, src, "-lm"],
+                   check=True, capture_output=True)
+    env = dict(os.environ, ONEBIT_ORACLE_LIB=lib, OMP_NUM_THREADS="1")
+    res = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                          os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                         cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    return res.returncode, res.stdout[-2000:]
+
+
 @pytest.fixture(scope="module")
-def source():
-    return open(SRC).read()
+def outcomes(request, tmp_path_factory):
+    """Runs every selected mutation, several at a time (each in its own
+    process), the first time a case asks for it."""
+    selected = [it.callspec.params["name"] for it in request.session.items
+                if it.module is request.module and hasattr(it, "callspec")]
+    source = open(SRC).read()
+    base = tmp_path_factory.mktemp("mutants")
+    workers = max(1, min(6, (os.cpu_count() or 2) - 2))
+    with ThreadPoolExecutor(max_workers=workers) as pool:
+        futs = {n: pool.submit(_run_mutation, n, source, str(base / n)) for n in selected}
+        return {n: f.result() for n, f in futs.items()}
 
 
 @pytest.mark.parametrize("name", sorted(MUTATIONS))
-def test_pins_catch_mutation(name, source, tmp_path):
-    old, new = MUTATIONS[name]
-    assert source.count(old) == 1, f"mutation anchor not unique: {old!r}"
-    mutated = source.replace(old, new)
-    src = tmp_path / "oracle.c"
-    src.write_text(mutated)
-    lib = tmp_path / "liboracle_mut.so"
-    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
-                    "-I", os.path.join(ROOT, "oracle"), "-o", str(lib), str(src), "-lm"],
-                   check=True, capture_output=True)
-    env = dict(os.environ, ONEBIT_ORACLE_LIB=str(lib))
-    res = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
-                          os.path.join(ROOT, "tests", "test_oracle_pins.py")],
-                         cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
-    assert res.returncode == 1, f"no pin failed for mutation {name}:\n{res.stdout[-2000:]}"
+def test_pins_catch_mutation(name, outcomes):
+    rc, out = outcomes[name]
+    assert rc == 1, f"no pin failed for mutation {name}:\n{out}"
