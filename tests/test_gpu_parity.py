@@ -255,6 +255,59 @@ def test_single_layer_16m():
     assert_parity(compare_state(d, h))
 
 
+def test_degenerate_tensors():
+    """The method's special cases through 2 LAMB warmup steps, the freeze
+    and 3 compression steps, GPU against oracle: a tensor of zero
+    parameters (||x|| = 0, so the trust ratio is 1), a tensor whose
+    gradients and moments are all zero (||u|| = 0, ratio 1; then whole
+    chunks of zeros: scale 0, every sign bit set, errors 0, q = 1), a
+    one-element tensor, a one-chunk tensor whose gradients are all
+    positive, and gradients of -0.0."""
+    C = 4096
+    numels = [C, 2 * C, 1, C, 2 * C + 11]
+    wl = Workload("degenerate", numels, W=3, chunk=C, init="fresh", grad_std=0.02)
+    d, h = DevRun(wl), HostRun(wl)
+    off = wl.offsets
+    t = [slice(int(off[i]), int(off[i + 1])) for i in range(len(numels))]
+    h.x[t[0]] = 0.0
+    for a in (h.m, h.v):
+        a[t[1]] = 0.0
+    for name in ("x", "m", "v"):
+        getattr(d, name).copy_(dev(getattr(h, name)))
+    d.vf.copy_(d.v)
+    h.vf[:] = h.v
+
+    def grads(step):
+        h.fill_grads(step)
+        for w in range(wl.W):
+            g = h.g[w]
+            g[t[1]] = 0.0
+            g[t[3]] = np.abs(g[t[3]])
+            g[t[4]][::7] = -0.0
+            d.g[w].copy_(dev(g))
+
+    for step in range(2):
+        grads(step)
+        d.warmup_step(step, fill=False)
+        h.warmup_step(step, fill=False)
+        assert_parity(compare_state(d, h, stage="warmup"), f"warmup {step}")
+        if step == 0:
+            c = host(d.c_out)
+            assert c[0] == 1.0 and c[1] == 1.0, c     # ||x|| = 0 and ||u|| = 0
+    d.freeze(2)
+    h.freeze(2)
+    for step in range(2, 5):
+        grads(step)
+        d.compressed_step(step, fill=False)
+        h.compressed_step(step, fill=False)
+        assert_parity(compare_state(d, h), f"compression {step}")
+        # chunks 1 and 2 hold tensor 1 alone: all zeros
+        assert np.all(host(d.scales_s)[1:3] == 0.0)
+        assert np.all(u32(d.bits_s)[C // 32:3 * C // 32] == 0xFFFFFFFF)
+        assert not torch.any(d.err_s[t[1]] != 0)
+    assert int(d.status.item()) == 0
+
+
 def test_determinism_and_resume():
     """Two runs are bitwise identical, and a run resumed from a saved state
     equals the uninterrupted one (across the warmup -> compression switch)."""
