@@ -161,15 +161,13 @@ void by_chunk(int32_t chunk, A&&... a) {
   }
 }
 
-// Launch kfull over the full chunks of an n-element buffer and ktail over
-// its partial last chunk (if any); both take the index of their first chunk
-// as the first argument.
-template <int C, typename KF, typename KT, typename... A>
-void launch_chunks(int64_t n, hipStream_t st, KF kfull, KT ktail, A... args) {
-  const int64_t Kf = n / C;
+// Launch k with one workgroup of C/16 threads per chunk of an n-element
+// buffer; k takes the number of full chunks first (block 0 takes the
+// partial last chunk, if any).
+template <int C, typename KF, typename... A>
+void launch_chunks(int64_t n, hipStream_t st, KF k, A... args) {
   const int64_t K = (n + C - 1) / C;
-  if (Kf > 0) hipLaunchKernelGGL(kfull, dim3((unsigned)Kf), dim3(C / 16), 0, st, (int64_t)0, args...);
-  if (K > Kf) hipLaunchKernelGGL(ktail, dim3(1), dim3(C / 16), 0, st, Kf, args...);
+  if (K > 0) hipLaunchKernelGGL(k, dim3((unsigned)K), dim3(C / 16), 0, st, n / C, args...);
 }
 
 // Tuning of the compression-step kernels, measured on MI355X at the
@@ -213,8 +211,7 @@ template <int C>
 struct LaunchCompress {
   static void run(int64_t n, const float* in, float* err, uint32_t* bits, float* scales,
                   int32_t* status, hipStream_t st) {
-    launch_chunks<C>(n, st, k_compress_ef<C, false, kCodec_NT>, k_compress_ef<C, true, kCodec_NT>, n,
-                     in, err, bits, scales, status);
+    launch_chunks<C>(n, st, k_compress_ef<C, kCodec_NT>, n, in, err, bits, scales, status);
   }
 };
 
@@ -222,8 +219,8 @@ template <int C>
 struct LaunchAverage {
   static void run(int64_t n, int W, const PackedIn& pin, float* err_s, uint32_t* bits,
                   float* scales, int32_t* status, hipStream_t st) {
-    launch_chunks<C>(n, st, k_average_packed<C, false, kCodec_NT>,
-                     k_average_packed<C, true, kCodec_NT>, n, W, pin, err_s, bits, scales, status);
+    launch_chunks<C>(n, st, k_average_packed<C, kCodec_NT>, n, W, pin, err_s, bits, scales,
+                     status);
   }
 };
 
@@ -231,8 +228,7 @@ template <int C>
 struct LaunchDecompress {
   static void run(int64_t n, const uint32_t* bits, const float* scales, float* out,
                   hipStream_t st) {
-    launch_chunks<C>(n, st, k_decompress<C, false, kCodec_NT>, k_decompress<C, true, kCodec_NT>, n,
-                     bits, scales, out);
+    launch_chunks<C>(n, st, k_decompress<C, kCodec_NT>, n, bits, scales, out);
   }
 };
 
@@ -241,14 +237,12 @@ struct LaunchWarmup {
   static void run(const onebit_layer_table* t, int W, const Workers& wk, float* x, float* m,
                   float* v, float* c_sum, float* c_out, const Coef& cf, const Ws& ws,
                   int32_t* status, hipStream_t st) {
-    launch_chunks<C>(t->N, st, k_warmup_pass1<C, false, kWarm_NT>, k_warmup_pass1<C, true, kWarm_NT>,
-                     t->dev, W, wk,
-                     (const float*)x, m, v, ws.seg_x, ws.seg_u, cf);
+    launch_chunks<C>(t->N, st, k_warmup_pass1<C, kWarm_NT>, t->dev, W, wk, (const float*)x, m, v,
+                     ws.seg_x, ws.seg_u, cf);
     hipLaunchKernelGGL(k_warmup_finalize<256>, dim3((unsigned)t->L), dim3(256), 0, st, t->dev,
                        ws.seg_x, ws.seg_u, c_sum, ws.c_layer, c_out, cf, status);
-    launch_chunks<C>(t->N, st, k_warmup_pass2<C, false, kWarm_NT>, k_warmup_pass2<C, true, kWarm_NT>,
-                     t->dev,
-                     (const float*)m, (const float*)v, x, (const float*)ws.c_layer, cf);
+    launch_chunks<C>(t->N, st, k_warmup_pass2<C, kWarm_NT>, t->dev, (const float*)m,
+                     (const float*)v, x, (const float*)ws.c_layer, cf);
   }
 };
 
@@ -256,8 +250,7 @@ template <int C>
 struct LaunchFreeze {
   static void run(const onebit_layer_table* t, int W, const float* v, float* v_fresh,
                   const Workers& wk, float* err_s, hipStream_t st) {
-    launch_chunks<C>(t->N, st, k_freeze_elems<C, false>, k_freeze_elems<C, true>, t->N, W, v,
-                     v_fresh, wk, err_s);
+    launch_chunks<C>(t->N, st, k_freeze_elems<C>, t->N, W, v, v_fresh, wk, err_s);
   }
 };
 
@@ -692,8 +685,8 @@ int onebit_adam_warmup_step(int64_t n, int32_t W, const float* const* grads, flo
   CHECK_PTR(m, "m");
   CHECK_PTR(v, "v");
   constexpr int C = kAdamWarmupChunk;
-  launch_chunks<C>(n, (hipStream_t)stream, k_adam_warmup<C, false>, k_adam_warmup<C, true>, n,
-                   (int)W, wk, x, m, v, make_coef(*hp));
+  launch_chunks<C>(n, (hipStream_t)stream, k_adam_warmup<C>, n, (int)W, wk, x, m, v,
+                   make_coef(*hp));
   return launch_status(__func__);
 }
 

@@ -454,17 +454,29 @@ __device__ __forceinline__ void segment_sums(const DevTable& tab, int64_t k, int
 }
 
 // ===========================================================================
-// kernels (k0: index of the first chunk of the launch)
+// kernels
 // ===========================================================================
 
+// Launch shape of the element-wise and codec kernels below: one workgroup
+// per chunk of an n-element buffer, n_full = n / C full chunks; when the
+// buffer ends in a partial chunk, block 0 takes it (its guarded code starts
+// first and overlaps the full chunks) and block b > 0 takes full chunk b-1.
+// The count is formed with integer division rather than a 64-bit compare,
+// which would leave the chunk index in vector registers.
+template <int C>
+__device__ __forceinline__ int64_t partial_chunks(int64_t n_full, int64_t n) {
+  return (n + (C - 1)) / C - n_full;  // 1 if the buffer ends in a partial chunk, else 0
+}
+
 // onebit_compress_ef: z = in + err -> bits, scales, err
-template <int C, bool TAIL, bool NT = false>
-__global__ void __launch_bounds__(C / 16)
-k_compress_ef(int64_t k0, int64_t n, const float* __restrict__ in, float* __restrict__ err,
-              uint32_t* __restrict__ bits, float* __restrict__ scales, int32_t* status) {
-  __shared__ float4 lds[2 * Geo<C>::T];
+template <int C, bool TAIL, bool NT>
+__device__ __forceinline__ void compress_ef_chunk(int64_t k, int64_t n, const float* __restrict__ in,
+                                                  float* __restrict__ err,
+                                                  uint32_t* __restrict__ bits,
+                                                  float* __restrict__ scales, int32_t* status,
+                                                  float4* lds) {
   int parity = 0;
-  const ChunkAt<C, TAIL> ch(k0 + (int64_t)blockIdx.x, n);
+  const ChunkAt<C, TAIL> ch(k, n);
   Slots z, e;
   load_chunk<C, TAIL, NT>(in, ch.base, ch.nk, z);
   load_chunk<C, TAIL, NT>(err, ch.base, ch.nk, e);
@@ -482,14 +494,28 @@ k_compress_ef(int64_t k0, int64_t n, const float* __restrict__ in, float* __rest
   }
 }
 
-// onebit_average_packed: y = mean of the workers' +-s, + err_s -> recompress
-template <int C, bool TAIL, bool NT = false>
+template <int C, bool NT = false>
 __global__ void __launch_bounds__(C / 16)
-k_average_packed(int64_t k0, int64_t n, int W, PackedIn pin, float* __restrict__ err_s,
-                 uint32_t* __restrict__ bits_out, float* __restrict__ scales_out, int32_t* status) {
+k_compress_ef(int64_t n_full, int64_t n, const float* __restrict__ in, float* __restrict__ err,
+              uint32_t* __restrict__ bits, float* __restrict__ scales, int32_t* status) {
   __shared__ float4 lds[2 * Geo<C>::T];
+  const int64_t has_tail = partial_chunks<C>(n_full, n);
+  if (has_tail && blockIdx.x == 0)
+    compress_ef_chunk<C, true, NT>(n_full, n, in, err, bits, scales, status, lds);
+  else
+    compress_ef_chunk<C, false, NT>((int64_t)blockIdx.x - has_tail, n, in, err, bits, scales,
+                                    status, lds);
+}
+
+// onebit_average_packed: y = mean of the workers' +-s, + err_s -> recompress
+template <int C, bool TAIL, bool NT>
+__device__ __forceinline__ void average_packed_chunk(int64_t k, int64_t n, int W, const PackedIn& pin,
+                                                     float* __restrict__ err_s,
+                                                     uint32_t* __restrict__ bits_out,
+                                                     float* __restrict__ scales_out,
+                                                     int32_t* status, float4* lds) {
   int parity = 0;
-  const ChunkAt<C, TAIL> ch(k0 + (int64_t)blockIdx.x, n);
+  const ChunkAt<C, TAIL> ch(k, n);
   Slots acc, y;
   for (int w = 0; w < W; ++w) {
     const float s = pin.scales[w][ch.k];
@@ -519,12 +545,25 @@ k_average_packed(int64_t k0, int64_t n, int W, PackedIn pin, float* __restrict__
   }
 }
 
-// onebit_decompress
-template <int C, bool TAIL, bool NT = false>
+template <int C, bool NT = false>
 __global__ void __launch_bounds__(C / 16)
-k_decompress(int64_t k0, int64_t n, const uint32_t* __restrict__ bits,
-             const float* __restrict__ scales, float* __restrict__ out) {
-  const ChunkAt<C, TAIL> ch(k0 + (int64_t)blockIdx.x, n);
+k_average_packed(int64_t n_full, int64_t n, int W, PackedIn pin, float* __restrict__ err_s,
+                 uint32_t* __restrict__ bits_out, float* __restrict__ scales_out, int32_t* status) {
+  __shared__ float4 lds[2 * Geo<C>::T];
+  const int64_t has_tail = partial_chunks<C>(n_full, n);
+  if (has_tail && blockIdx.x == 0)
+    average_packed_chunk<C, true, NT>(n_full, n, W, pin, err_s, bits_out, scales_out, status, lds);
+  else
+    average_packed_chunk<C, false, NT>((int64_t)blockIdx.x - has_tail, n, W, pin, err_s,
+                                       bits_out, scales_out, status, lds);
+}
+
+// onebit_decompress
+template <int C, bool TAIL, bool NT>
+__device__ __forceinline__ void decompress_chunk(int64_t k, int64_t n, const uint32_t* __restrict__ bits,
+                                                 const float* __restrict__ scales,
+                                                 float* __restrict__ out) {
+  const ChunkAt<C, TAIL> ch(k, n);
   const float s = scales[ch.k];
   uint32_t nib[4];
   load_sign_nibbles<C>(bits + ch.k * Geo<C>::WORDS, nib);
@@ -534,6 +573,17 @@ k_decompress(int64_t k0, int64_t n, const uint32_t* __restrict__ bits,
 #pragma unroll
     for (int c = 0; c < 4; ++c) o[a][c] = signed_scale(nib, a, c, s);
   store_chunk<C, TAIL, NT>(out, ch.base, ch.nk, o);
+}
+
+template <int C, bool NT = false>
+__global__ void __launch_bounds__(C / 16)
+k_decompress(int64_t n_full, int64_t n, const uint32_t* __restrict__ bits,
+             const float* __restrict__ scales, float* __restrict__ out) {
+  const int64_t has_tail = partial_chunks<C>(n_full, n);
+  if (has_tail && blockIdx.x == 0)
+    decompress_chunk<C, true, NT>(n_full, n, bits, scales, out);
+  else
+    decompress_chunk<C, false, NT>((int64_t)blockIdx.x - has_tail, n, bits, scales, out);
 }
 
 // The compressed allreduce of one chunk's momentum: every worker's
@@ -795,11 +845,11 @@ k_adam_compressed(int64_t n_full, int64_t n, int64_t K, int W, Workers wk,
 
 // 1-bit Adam warmup: one Adam step, element-wise in one pass (mean gradient,
 // moments, x = x - lr*(m/(sqrt(v)+eta))).
-template <int C, bool TAIL, int WPE = 1>
-__global__ void __launch_bounds__(C / 16, WPE)
-k_adam_warmup(int64_t k0, int64_t n, int W, Workers wk, float* __restrict__ x,
-              float* __restrict__ m, float* __restrict__ v, Coef cf) {
-  const ChunkAt<C, TAIL> ch(k0 + (int64_t)blockIdx.x, n);
+template <int C, bool TAIL>
+__device__ __forceinline__ void adam_warmup_chunk(int64_t k, int64_t n, int W, const Workers& wk,
+                                                  float* __restrict__ x, float* __restrict__ m,
+                                                  float* __restrict__ v, const Coef& cf) {
+  const ChunkAt<C, TAIL> ch(k, n);
   const int64_t base = ch.base;
   const int nk = ch.nk;
   Slots gs;
@@ -830,6 +880,17 @@ k_adam_warmup(int64_t k0, int64_t n, int W, Workers wk, float* __restrict__ x,
   store_chunk<C, TAIL, true>(m, base, nk, mm);
   store_chunk<C, TAIL, true>(v, base, nk, vv);
   store_chunk<C, TAIL, true>(x, base, nk, xx);
+}
+
+template <int C, int WPE = 1>
+__global__ void __launch_bounds__(C / 16, WPE)
+k_adam_warmup(int64_t n_full, int64_t n, int W, Workers wk, float* __restrict__ x,
+              float* __restrict__ m, float* __restrict__ v, Coef cf) {
+  const int64_t has_tail = partial_chunks<C>(n_full, n);
+  if (has_tail && blockIdx.x == 0)
+    adam_warmup_chunk<C, true>(n_full, n, W, wk, x, m, v, cf);
+  else
+    adam_warmup_chunk<C, false>((int64_t)blockIdx.x - has_tail, n, W, wk, x, m, v, cf);
 }
 
 // SLAMB-style sparse compression stage, one pass per chunk.  The chunk's
@@ -1090,14 +1151,15 @@ k_compressed_pass_b(int64_t n_full, DevTable tab, const uint32_t* __restrict__ b
 
 // Warmup pass 1: mean gradient, moments, per-(chunk, tensor) sums of x^2 and
 // u^2 in double.  NT: streaming accesses; WPE: minimum waves per SIMD.
-template <int C, bool TAIL, bool NT = false, int WPE = 1>
-__global__ void __launch_bounds__(C / 16, WPE)
-k_warmup_pass1(int64_t k0, DevTable tab, int W, Workers wk, const float* __restrict__ x,
-               float* __restrict__ m, float* __restrict__ v, double* __restrict__ seg_x,
-               double* __restrict__ seg_u, Coef cf) {
+template <int C, bool TAIL, bool NT>
+__device__ __forceinline__ void warmup_pass1_chunk(int64_t k, const DevTable& tab, int W,
+                                                   const Workers& wk, const float* __restrict__ x,
+                                                   float* __restrict__ m, float* __restrict__ v,
+                                                   double* __restrict__ seg_x,
+                                                   double* __restrict__ seg_u, const Coef& cf,
+                                                   double* red) {
   constexpr int T = Geo<C>::T;
-  __shared__ double red[2 * (T / 64)];
-  const ChunkAt<C, TAIL> ch(k0 + (int64_t)blockIdx.x, tab.N);
+  const ChunkAt<C, TAIL> ch(k, tab.N);
   const int64_t base = ch.base;
   const int nk = ch.nk;
   Slots gs;
@@ -1151,6 +1213,20 @@ k_warmup_pass1(int64_t k0, DevTable tab, int W, Workers wk, const float* __restr
   }
 }
 
+template <int C, bool NT = false, int WPE = 1>
+__global__ void __launch_bounds__(C / 16, WPE)
+k_warmup_pass1(int64_t n_full, DevTable tab, int W, Workers wk, const float* __restrict__ x,
+               float* __restrict__ m, float* __restrict__ v, double* __restrict__ seg_x,
+               double* __restrict__ seg_u, Coef cf) {
+  __shared__ double red[2 * (Geo<C>::T / 64)];
+  const int64_t has_tail = tab.K - n_full;
+  if (has_tail && blockIdx.x == 0)
+    warmup_pass1_chunk<C, true, NT>(n_full, tab, W, wk, x, m, v, seg_x, seg_u, cf, red);
+  else
+    warmup_pass1_chunk<C, false, NT>((int64_t)blockIdx.x - has_tail, tab, W, wk, x, m, v,
+                                     seg_x, seg_u, cf, red);
+}
+
 // Per tensor: norms, trust ratio, clip, c_sum.
 template <int TB>
 __global__ void __launch_bounds__(TB)
@@ -1178,11 +1254,14 @@ k_warmup_finalize(DevTable tab, const double* __restrict__ seg_x, const double* 
 }
 
 // Warmup pass 2: x = x - (lr*c_l)*u with u recomputed from the new m, v.
-template <int C, bool TAIL, bool NT = false>
-__global__ void __launch_bounds__(C / 16)
-k_warmup_pass2(int64_t k0, DevTable tab, const float* __restrict__ m, const float* __restrict__ v,
-               float* __restrict__ x, const float* __restrict__ c_layer, Coef cf) {
-  const ChunkAt<C, TAIL> ch(k0 + (int64_t)blockIdx.x, tab.N);
+template <int C, bool TAIL, bool NT>
+__device__ __forceinline__ void warmup_pass2_chunk(int64_t k, const DevTable& tab,
+                                                   const float* __restrict__ m,
+                                                   const float* __restrict__ v,
+                                                   float* __restrict__ x,
+                                                   const float* __restrict__ c_layer,
+                                                   const Coef& cf) {
+  const ChunkAt<C, TAIL> ch(k, tab.N);
   Slots mm, vv, xx, st;
   load_chunk<C, TAIL, NT>(m, ch.base, ch.nk, mm);
   load_chunk<C, TAIL, NT>(v, ch.base, ch.nk, vv);
@@ -1198,12 +1277,25 @@ k_warmup_pass2(int64_t k0, DevTable tab, const float* __restrict__ m, const floa
   store_chunk<C, TAIL, NT>(x, ch.base, ch.nk, xx);
 }
 
+template <int C, bool NT = false>
+__global__ void __launch_bounds__(C / 16)
+k_warmup_pass2(int64_t n_full, DevTable tab, const float* __restrict__ m, const float* __restrict__ v,
+               float* __restrict__ x, const float* __restrict__ c_layer, Coef cf) {
+  const int64_t has_tail = tab.K - n_full;
+  if (has_tail && blockIdx.x == 0)
+    warmup_pass2_chunk<C, true, NT>(n_full, tab, m, v, x, c_layer, cf);
+  else
+    warmup_pass2_chunk<C, false, NT>((int64_t)blockIdx.x - has_tail, tab, m, v, x, c_layer,
+                                     cf);
+}
+
 // Freeze, element part: v_fresh = v, error buffers cleared.
 template <int C, bool TAIL>
-__global__ void __launch_bounds__(C / 16)
-k_freeze_elems(int64_t k0, int64_t n, int W, const float* __restrict__ v,
-               float* __restrict__ v_fresh, Workers wk, float* __restrict__ err_s) {
-  const ChunkAt<C, TAIL> ch(k0 + (int64_t)blockIdx.x, n);
+__device__ __forceinline__ void freeze_elems_chunk(int64_t k, int64_t n, int W,
+                                                   const float* __restrict__ v,
+                                                   float* __restrict__ v_fresh, const Workers& wk,
+                                                   float* __restrict__ err_s) {
+  const ChunkAt<C, TAIL> ch(k, n);
   Slots vv, zero;
   load_chunk<C, TAIL>(v, ch.base, ch.nk, vv);
   store_chunk<C, TAIL>(v_fresh, ch.base, ch.nk, vv);
@@ -1213,6 +1305,17 @@ k_freeze_elems(int64_t k0, int64_t n, int W, const float* __restrict__ v,
     for (int c = 0; c < 4; ++c) zero[a][c] = 0.0f;
   for (int w = 0; w < W; ++w) store_chunk<C, TAIL>(wk.e[w], ch.base, ch.nk, zero);
   store_chunk<C, TAIL>(err_s, ch.base, ch.nk, zero);
+}
+
+template <int C>
+__global__ void __launch_bounds__(C / 16)
+k_freeze_elems(int64_t n_full, int64_t n, int W, const float* __restrict__ v,
+               float* __restrict__ v_fresh, Workers wk, float* __restrict__ err_s) {
+  const int64_t has_tail = partial_chunks<C>(n_full, n);
+  if (has_tail && blockIdx.x == 0)
+    freeze_elems_chunk<C, true>(n_full, n, W, v, v_fresh, wk, err_s);
+  else
+    freeze_elems_chunk<C, false>((int64_t)blockIdx.x - has_tail, n, W, v, v_fresh, wk, err_s);
 }
 
 // Freeze, tensor part: c_avg = c_sum / den (den = T_w, or 1-d^T_w for the
