@@ -7,6 +7,14 @@ order of its C counterpart in include/onebit.h; array arguments are CUDA
 lists stand for the host arrays of worker pointers, `stream` defaults to
 torch's current stream.  Every step of the path runs in the library's HIP
 kernels; if the library is not built, importing this package raises.
+
+Before a call reaches the library, tensors are checked for what the C side
+cannot see: that they live on the GPU, are contiguous, have the documented
+dtype and hold at least the bytes the call touches, and that a list holds
+at least W worker entries (OnebitError with ONEBIT_EINVAL otherwise).  When
+a scalar argument (n, chunk, W, nsel) is itself invalid, the sizes are not
+checked and the library reports the error.  Raw integer addresses are
+passed through unchecked.
 """
 import ctypes
 import os
@@ -97,19 +105,74 @@ def _check(rc, fn):
         raise OnebitError(rc, fn, onebit_last_error())
 
 
-def _ptr(a):
-    """Device address of a tensor, an int address, or None (NULL)."""
+_F32, _WORDS, _ANY = "f32", "words", "any"
+
+
+def _chunk_ok(chunk):
+    return isinstance(chunk, int) and 1024 <= chunk <= 16384 and chunk & (chunk - 1) == 0
+
+
+def _W_ok(W):
+    return isinstance(W, int) and 1 <= W <= ONEBIT_MAX_WORKERS
+
+
+def _bad(fn, msg):
+    return OnebitError(ONEBIT_EINVAL, fn, "binding: " + msg)
+
+
+def _ptr(a, fn="", name="", nbytes=None, kind=_ANY):
+    """Device address of a tensor, an int address, or None (NULL).  A
+    tensor must be on the GPU, contiguous, of the kind's dtype, and hold at
+    least nbytes (when given)."""
     if a is None:
         return None
     if isinstance(a, int):
         return a
+    import torch
+    if not a.is_cuda:
+        raise _bad(fn, f"{name} is not a GPU tensor")
+    if not a.is_contiguous():
+        raise _bad(fn, f"{name} is not contiguous")
+    if kind == _F32 and a.dtype != torch.float32:
+        raise _bad(fn, f"{name} has dtype {a.dtype}, float32 expected")
+    if kind == _WORDS and a.dtype not in (torch.int32, getattr(torch, "uint32", torch.int32)):
+        raise _bad(fn, f"{name} has dtype {a.dtype}, 32-bit words expected")
+    if nbytes is not None and a.numel() * a.element_size() < nbytes:
+        raise _bad(fn, f"{name} holds {a.numel() * a.element_size()} bytes, the call touches "
+                       f"{nbytes}")
     return a.data_ptr()
 
 
-def _ptr_list(items):
+def _ptr_list(items, fn="", name="", W=None, nbytes=None, kind=_ANY):
+    """Host array of the entries' device addresses; at least W entries."""
     if items is None:
         return None
-    return (ctypes.c_void_p * len(items))(*[_ptr(a) for a in items])
+    if W is not None and _W_ok(W) and len(items) < W:
+        raise _bad(fn, f"{name} has {len(items)} entries, W = {W}")
+    return (ctypes.c_void_p * len(items))(
+        *[_ptr(a, fn, f"{name}[{i}]", nbytes, kind) for i, a in enumerate(items)])
+
+
+class _Sizes:
+    """Bytes an entry point touches per kind of array, or None where the
+    scalar arguments are invalid (the library then reports the error)."""
+
+    def __init__(self, n=None, chunk=None, L=None, ws=None):
+        ok = n is not None and n >= 0 and _chunk_ok(chunk)
+        K = -(-n // chunk) if ok else None
+        self.elems = 4 * n if ok else None             # one fp32 per element
+        self.words = 4 * (K * chunk // 32) if ok else None
+        self.scales = 4 * K if ok else None
+        self.tensors = 4 * L if L is not None else None
+        self.ws = ws
+        self.K = K
+
+
+def _table_sizes(table, W=None):
+    if isinstance(table, LayerTable):
+        ws = table.workspace_size(W) if W is not None and _W_ok(W) else None
+        return _Sizes(table.N, table.chunk, table.L, ws)
+    return _Sizes()                                     # raw handle: sizes unknown here
 
 
 def _stream(stream):
@@ -190,86 +253,132 @@ def _h(table):
 
 def onebit_lamb_warmup_step(table, W, grads, x, m, v, c_sum, c_out, hp, ws, status=None,
                             stream=None):
-    _check(_lib.onebit_lamb_warmup_step(_h(table), W, _ptr_list(grads), _ptr(x), _ptr(m), _ptr(v),
-                                        _ptr(c_sum), _ptr(c_out), ctypes.byref(hp), _ptr(ws),
-                                        _ptr(status), _stream(stream)),
-           "onebit_lamb_warmup_step")
+    fn, z = "onebit_lamb_warmup_step", _table_sizes(table, W)
+    e = lambda a, nm: _ptr(a, fn, nm, z.elems, _F32)  # noqa: E731
+    t = lambda a, nm: _ptr(a, fn, nm, z.tensors, _F32)  # noqa: E731
+    _check(_lib.onebit_lamb_warmup_step(_h(table), W, _ptr_list(grads, fn, "grads", W, z.elems, _F32),
+                                        e(x, "x"), e(m, "m"), e(v, "v"), t(c_sum, "c_sum"),
+                                        t(c_out, "c_out"), ctypes.byref(hp),
+                                        _ptr(ws, fn, "ws", z.ws), _ptr(status, fn, "status", 4),
+                                        _stream(stream)), fn)
 
 
 def onebit_lamb_freeze(table, W, v, v_fresh, err_w, err_s, c_sum, T_w, c_avg, f_prev, hp=None,
                        stream=None):
-    _check(_lib.onebit_lamb_freeze(_h(table), W, _ptr(v), _ptr(v_fresh), _ptr_list(err_w),
-                                   _ptr(err_s), _ptr(c_sum), T_w, _ptr(c_avg), _ptr(f_prev),
-                                   None if hp is None else ctypes.byref(hp), _stream(stream)),
-           "onebit_lamb_freeze")
+    fn, z = "onebit_lamb_freeze", _table_sizes(table)
+    e = lambda a, nm: _ptr(a, fn, nm, z.elems, _F32)  # noqa: E731
+    t = lambda a, nm: _ptr(a, fn, nm, z.tensors, _F32)  # noqa: E731
+    _check(_lib.onebit_lamb_freeze(_h(table), W, e(v, "v"), e(v_fresh, "v_fresh"),
+                                   _ptr_list(err_w, fn, "err_w", W, z.elems, _F32),
+                                   e(err_s, "err_s"), t(c_sum, "c_sum"), T_w, t(c_avg, "c_avg"),
+                                   t(f_prev, "f_prev"), None if hp is None else ctypes.byref(hp),
+                                   _stream(stream)), fn)
 
 
 def onebit_compress_ef(n, chunk, inp, err, bits, scales, status=None, stream=None):
-    _check(_lib.onebit_compress_ef(n, chunk, _ptr(inp), _ptr(err), _ptr(bits), _ptr(scales),
-                                   _ptr(status), _stream(stream)),
-           "onebit_compress_ef")
+    fn, z = "onebit_compress_ef", _Sizes(n, chunk)
+    _check(_lib.onebit_compress_ef(n, chunk, _ptr(inp, fn, "in", z.elems, _F32),
+                                   _ptr(err, fn, "err", z.elems, _F32),
+                                   _ptr(bits, fn, "bits", z.words, _WORDS),
+                                   _ptr(scales, fn, "scales", z.scales, _F32),
+                                   _ptr(status, fn, "status", 4), _stream(stream)), fn)
 
 
 def onebit_average_packed(n, chunk, W, bits_w, scales_w, err_s, bits_out, scales_out, status=None,
                           stream=None):
-    _check(_lib.onebit_average_packed(n, chunk, W, _ptr_list(bits_w), _ptr_list(scales_w),
-                                      _ptr(err_s), _ptr(bits_out), _ptr(scales_out), _ptr(status),
-                                      _stream(stream)),
-           "onebit_average_packed")
+    fn, z = "onebit_average_packed", _Sizes(n, chunk)
+    _check(_lib.onebit_average_packed(n, chunk, W, _ptr_list(bits_w, fn, "bits_w", W, z.words, _WORDS),
+                                      _ptr_list(scales_w, fn, "scales_w", W, z.scales, _F32),
+                                      _ptr(err_s, fn, "err_s", z.elems, _F32),
+                                      _ptr(bits_out, fn, "bits_out", z.words, _WORDS),
+                                      _ptr(scales_out, fn, "scales_out", z.scales, _F32),
+                                      _ptr(status, fn, "status", 4), _stream(stream)), fn)
 
 
 def onebit_lamb_compressed_step(table, W, grads, err_w, err_s, x, m, v_frozen, v_fresh, c_avg,
                                 f_prev, c_out, bits_w, scales_w, bits_s, scales_s, hp, ws,
                                 status=None, stream=None):
+    fn, z = "onebit_lamb_compressed_step", _table_sizes(table, W)
+    e = lambda a, nm: _ptr(a, fn, nm, z.elems, _F32)  # noqa: E731
+    t = lambda a, nm: _ptr(a, fn, nm, z.tensors, _F32)  # noqa: E731
     _check(_lib.onebit_lamb_compressed_step(
-        _h(table), W, _ptr_list(grads), _ptr_list(err_w), _ptr(err_s), _ptr(x), _ptr(m),
-        _ptr(v_frozen), _ptr(v_fresh), _ptr(c_avg), _ptr(f_prev), _ptr(c_out), _ptr_list(bits_w),
-        _ptr_list(scales_w), _ptr(bits_s), _ptr(scales_s), ctypes.byref(hp), _ptr(ws),
-        _ptr(status), _stream(stream)),
-        "onebit_lamb_compressed_step")
+        _h(table), W, _ptr_list(grads, fn, "grads", W, z.elems, _F32),
+        _ptr_list(err_w, fn, "err_w", W, z.elems, _F32), e(err_s, "err_s"), e(x, "x"), e(m, "m"),
+        e(v_frozen, "v_frozen"), e(v_fresh, "v_fresh"), t(c_avg, "c_avg"), t(f_prev, "f_prev"),
+        t(c_out, "c_out"), _ptr_list(bits_w, fn, "bits_w", W, z.words, _WORDS),
+        _ptr_list(scales_w, fn, "scales_w", W, z.scales, _F32),
+        _ptr(bits_s, fn, "bits_s", z.words, _WORDS), _ptr(scales_s, fn, "scales_s", z.scales, _F32),
+        ctypes.byref(hp), _ptr(ws, fn, "ws", z.ws), _ptr(status, fn, "status", 4),
+        _stream(stream)), fn)
 
 
 def onebit_lamb_compress_average(table, W, grads, err_w, err_s, m, v_frozen, v_fresh, bits_w,
                                  scales_w, bits_s, scales_s, hp, ws, status=None, stream=None):
+    fn, z = "onebit_lamb_compress_average", _table_sizes(table, W)
+    e = lambda a, nm: _ptr(a, fn, nm, z.elems, _F32)  # noqa: E731
     _check(_lib.onebit_lamb_compress_average(
-        _h(table), W, _ptr_list(grads), _ptr_list(err_w), _ptr(err_s), _ptr(m), _ptr(v_frozen),
-        _ptr(v_fresh), _ptr_list(bits_w), _ptr_list(scales_w), _ptr(bits_s), _ptr(scales_s),
-        ctypes.byref(hp), _ptr(ws), _ptr(status), _stream(stream)),
-        "onebit_lamb_compress_average")
+        _h(table), W, _ptr_list(grads, fn, "grads", W, z.elems, _F32),
+        _ptr_list(err_w, fn, "err_w", W, z.elems, _F32), e(err_s, "err_s"), e(m, "m"),
+        e(v_frozen, "v_frozen"), e(v_fresh, "v_fresh"),
+        _ptr_list(bits_w, fn, "bits_w", W, z.words, _WORDS),
+        _ptr_list(scales_w, fn, "scales_w", W, z.scales, _F32),
+        _ptr(bits_s, fn, "bits_s", z.words, _WORDS), _ptr(scales_s, fn, "scales_s", z.scales, _F32),
+        ctypes.byref(hp), _ptr(ws, fn, "ws", z.ws), _ptr(status, fn, "status", 4),
+        _stream(stream)), fn)
 
 
 def onebit_lamb_rescale_update(table, bits_s, scales_s, x, m, v_frozen, c_avg, f_prev, c_out, hp,
                                ws, status=None, stream=None):
+    fn, z = "onebit_lamb_rescale_update", _table_sizes(table, 1)
+    e = lambda a, nm: _ptr(a, fn, nm, z.elems, _F32)  # noqa: E731
+    t = lambda a, nm: _ptr(a, fn, nm, z.tensors, _F32)  # noqa: E731
     _check(_lib.onebit_lamb_rescale_update(
-        _h(table), _ptr(bits_s), _ptr(scales_s), _ptr(x), _ptr(m), _ptr(v_frozen), _ptr(c_avg),
-        _ptr(f_prev), _ptr(c_out), ctypes.byref(hp), _ptr(ws), _ptr(status), _stream(stream)),
-        "onebit_lamb_rescale_update")
+        _h(table), _ptr(bits_s, fn, "bits_s", z.words, _WORDS),
+        _ptr(scales_s, fn, "scales_s", z.scales, _F32), e(x, "x"), e(m, "m"),
+        e(v_frozen, "v_frozen"), t(c_avg, "c_avg"), t(f_prev, "f_prev"), t(c_out, "c_out"),
+        ctypes.byref(hp), _ptr(ws, fn, "ws", z.ws), _ptr(status, fn, "status", 4),
+        _stream(stream)), fn)
 
 
 def onebit_decompress(n, chunk, bits, scales, out, stream=None):
-    _check(_lib.onebit_decompress(n, chunk, _ptr(bits), _ptr(scales), _ptr(out), _stream(stream)),
-           "onebit_decompress")
+    fn, z = "onebit_decompress", _Sizes(n, chunk)
+    _check(_lib.onebit_decompress(n, chunk, _ptr(bits, fn, "bits", z.words, _WORDS),
+                                  _ptr(scales, fn, "scales", z.scales, _F32),
+                                  _ptr(out, fn, "out", z.elems, _F32), _stream(stream)), fn)
 
 
 def onebit_adam_warmup_step(n, W, grads, x, m, v, hp, stream=None):
-    _check(_lib.onebit_adam_warmup_step(n, W, _ptr_list(grads), _ptr(x), _ptr(m), _ptr(v),
-                                        ctypes.byref(hp), _stream(stream)),
-           "onebit_adam_warmup_step")
+    fn = "onebit_adam_warmup_step"
+    nb = 4 * n if isinstance(n, int) and n >= 0 else None
+    e = lambda a, nm: _ptr(a, fn, nm, nb, _F32)  # noqa: E731
+    _check(_lib.onebit_adam_warmup_step(n, W, _ptr_list(grads, fn, "grads", W, nb, _F32),
+                                        e(x, "x"), e(m, "m"), e(v, "v"), ctypes.byref(hp),
+                                        _stream(stream)), fn)
 
 
 def onebit_adam_compressed_step(n, chunk, W, grads, err_w, err_s, x, m, v_frozen, bits_w,
                                 scales_w, bits_s, scales_s, hp, status=None, stream=None):
+    fn, z = "onebit_adam_compressed_step", _Sizes(n, chunk)
+    e = lambda a, nm: _ptr(a, fn, nm, z.elems, _F32)  # noqa: E731
     _check(_lib.onebit_adam_compressed_step(
-        n, chunk, W, _ptr_list(grads), _ptr_list(err_w), _ptr(err_s), _ptr(x), _ptr(m),
-        _ptr(v_frozen), _ptr_list(bits_w), _ptr_list(scales_w), _ptr(bits_s), _ptr(scales_s),
-        ctypes.byref(hp), _ptr(status), _stream(stream)),
-        "onebit_adam_compressed_step")
+        n, chunk, W, _ptr_list(grads, fn, "grads", W, z.elems, _F32),
+        _ptr_list(err_w, fn, "err_w", W, z.elems, _F32), e(err_s, "err_s"), e(x, "x"), e(m, "m"),
+        e(v_frozen, "v_frozen"), _ptr_list(bits_w, fn, "bits_w", W, z.words, _WORDS),
+        _ptr_list(scales_w, fn, "scales_w", W, z.scales, _F32),
+        _ptr(bits_s, fn, "bits_s", z.words, _WORDS), _ptr(scales_s, fn, "scales_s", z.scales, _F32),
+        ctypes.byref(hp), _ptr(status, fn, "status", 4), _stream(stream)), fn)
 
 
 def onebit_sparse_compressed_step(table, W, nsel, sel, grads, err_w, x, m, v_frozen, v_fresh,
                                   c_avg, vals_w, vals_s, hp, status=None, stream=None):
+    fn, z = "onebit_sparse_compressed_step", _table_sizes(table)
+    e = lambda a, nm: _ptr(a, fn, nm, z.elems, _F32)  # noqa: E731
+    nsel_ok = z.K is not None and isinstance(nsel, int) and 1 <= nsel <= table.chunk // 64
+    per = 4 * z.K * nsel * 64 if nsel_ok else None
     _check(_lib.onebit_sparse_compressed_step(
-        _h(table), W, nsel, _ptr(sel), _ptr_list(grads), _ptr_list(err_w), _ptr(x), _ptr(m),
-        _ptr(v_frozen), _ptr(v_fresh), _ptr(c_avg), _ptr_list(vals_w), _ptr(vals_s),
-        ctypes.byref(hp), _ptr(status), _stream(stream)),
-        "onebit_sparse_compressed_step")
+        _h(table), W, nsel, _ptr(sel, fn, "sel", z.scales, _WORDS),
+        _ptr_list(grads, fn, "grads", W, z.elems, _F32),
+        _ptr_list(err_w, fn, "err_w", W, z.elems, _F32), e(x, "x"), e(m, "m"),
+        e(v_frozen, "v_frozen"), e(v_fresh, "v_fresh"), _ptr(c_avg, fn, "c_avg", z.tensors, _F32),
+        _ptr_list(vals_w, fn, "vals_w", W, per, _F32), _ptr(vals_s, fn, "vals_s", per, _F32),
+        ctypes.byref(hp), _ptr(status, fn, "status", 4), _stream(stream)), fn)

@@ -135,3 +135,22 @@ def test_package_refuses_to_load_without_library(tmp_path):
     res = subprocess.run([sys.executable, "-c", "import communication_compressed_optimizer_amd"],
                          cwd=tmp_path, capture_output=True, text=True)
     assert res.returncode != 0 and "is not built" in res.stderr
+
+
+def test_binding_checks_tensors_before_the_library(ob):
+    """Host tensors and short worker lists are rejected by the binding
+    itself (a host address or a missing worker pointer would reach the
+    GPU otherwise)."""
+    import torch
+    host = torch.zeros(4096, dtype=torch.float32)
+    with pytest.raises(ob.OnebitError) as ei:
+        ob.onebit_compress_ef(4096, 4096, host, host, None, None)
+    assert ei.value.code == ob.ONEBIT_EINVAL and "not a GPU tensor" in str(ei.value)
+    hp = ob.onebit_hparams(beta1=0.9, beta2=0.999, eta=1e-8, lr=1e-3)
+    with pytest.raises(ob.OnebitError) as ei:
+        ob.onebit_adam_warmup_step(4096, 4, [None] * 3, None, None, None, hp)
+    assert ei.value.code == ob.ONEBIT_EINVAL and "3 entries, W = 4" in str(ei.value)
+    # invalid scalars are left to the library, which names them
+    assert ob._Sizes(10, 3000).elems is None and ob._Sizes(-1, 4096).elems is None
+    z = ob._Sizes(4097, 4096)
+    assert (z.K, z.elems, z.words, z.scales) == (2, 4 * 4097, 4 * 2 * 128, 8)

@@ -432,6 +432,18 @@ def test_binding_rejects_bad_arguments():
     ob.onebit_average_packed(0, C, 2, [bits, bits], [sc, sc], a, bits, sc)   # n = 0: nothing
     ob.onebit_decompress(0, C, bits, sc, a)
     assert torch.count_nonzero(a).item() == 0
+    # the binding's own checks, before the library: dtype, layout, size, worker count
+    strided = torch.zeros(2 * n, dtype=torch.float32, device="cuda")[::2]
+    for call in (lambda: ob.onebit_compress_ef(n, C, a.double()[:n], a[:n], bits, sc),
+                 lambda: ob.onebit_compress_ef(n, C, strided, a[:n], bits, sc),
+                 lambda: ob.onebit_compress_ef(n, C, a[:n - 1], a[:n], bits, sc),
+                 lambda: ob.onebit_compress_ef(n, C, a[:n], a[:n], bits.float(), sc),
+                 lambda: ob.onebit_compress_ef(n, C, a[:n], a[:n], bits[:-1], sc),
+                 lambda: ob.onebit_average_packed(n, C, 2, [bits], [sc, sc], a, bits, sc)):
+        with pytest.raises(ob.OnebitError) as ei:
+            call()
+        assert ei.value.code == ob.ONEBIT_EINVAL and "binding:" in str(ei.value)
+    assert torch.count_nonzero(a).item() == 0 and torch.count_nonzero(bits).item() == 0
 
 
 def test_many_workers_trajectory():
