@@ -15,8 +15,10 @@ Prints one JSON line.  `value` is parameters per second for the step with
 fp32 momentum; `packed_momentum` times the same step with the momentum kept
 as the server's packed output (bit-identical results); `roofline` is the
 dominant kernel (phase 1: compression, average, rescale statistics) timed
-with HIP events on its stream; `cpu_baseline` is the single-threaded CPU
-oracle on a bounded window of the same workload.  `--method adam` and
+with HIP events on its stream; `runtime_copy` is the runtime's own 1 GiB
+device-to-device copy timed on the same box, as a reference rate;
+`cpu_baseline` is the single-threaded CPU oracle on a bounded window of the
+same workload.  `--method adam` and
 `--method sparse` time the 1-bit Adam mode and the SLAMB-style sparse stage
 on the same buffers instead.
 """
@@ -78,6 +80,35 @@ def sparse_bytes(N, K, C, W, nsel):
     transmitted values written; the selection read."""
     f = nsel * 64 / C
     return int(N * (12 * W + 8) + N * f * (20 + 4 * (W + 1)) + 4 * K)
+
+
+def copy_ceiling(torch, stream, nbytes=1 << 30, reps=10):
+    """torch's device-to-device copy of nbytes on the same stream, timed with
+    HIP events: a reference rate of this machine, reported beside the 8 TB/s
+    peak.  Returns GB/s counting the bytes read and written."""
+    a = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(reps):
+        b.copy_(a)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / reps
+    del a, b
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
+def _ceiling(torch, stream, achieved):
+    copy_gbps = copy_ceiling(torch, stream)
+    log(f"[bench] copy ceiling {copy_gbps:.0f} GB/s")
+    return {"copy_GBps": copy_gbps, "copy_frac_of_peak": copy_gbps / PEAK_HBM_GBPS,
+            "kernel_frac_of_copy": achieved / copy_gbps,
+            "note": "1 GiB device-to-device copy by the runtime (torch copy_) on the same stream "
+                    "after the timed steps, read plus written bytes; a reference rate of the box, "
+                    "not an upper bound (a tuned streaming copy runs faster)"}
 
 
 def cpu_baseline(wl, n_chunks, method="lamb", nsel=1):
@@ -210,12 +241,14 @@ def main():
         t1 = time.perf_counter()
         p1 = [a.elapsed_time(b) for a, b, _ in evs]
         p2 = [b.elapsed_time(c) for _, b, c in evs]
+        timed.p1 = sorted(p1)
         return (t1 - t0) * 1e3 / args.steps, sum(p1) / len(p1), sum(p2) / len(p2)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     ms_per_step, p1_ms, p2_ms = timed(m)
+    p1_sorted = timed.p1
     st = int(status.item())
     if st:
         log(f"[bench] WARNING: status flags {st} (non-finite scale or statistic)")
@@ -275,6 +308,8 @@ def main():
         "frac_of_peak": step_gbps / PEAK_HBM_GBPS,
         "step_bytes": sbytes,
         "phase_ms": {"compress_average": p1_ms, "rescale_update": p2_ms},
+        "phase1_ms_per_step": {"min": p1_sorted[0], "median": p1_sorted[len(p1_sorted) // 2],
+                               "max": p1_sorted[-1]},
         "warmup_step": {"ms": warm_ms, "params_per_s": N / (warm_ms * 1e-3),
                         "GBps": warm_bytes / (warm_ms * 1e-3) / 1e9, "bytes": warm_bytes},
         "packed_momentum": {
@@ -287,6 +322,7 @@ def main():
                      "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
                      "algorithmic_bytes": abytes},
+        "runtime_copy": _ceiling(torch, stream, achieved),
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
@@ -378,6 +414,7 @@ def bench_adam(args, wl, ob, torch, hp, g, e, err_s, x, m, v, bits_w, scales_w, 
                      "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
                      "algorithmic_bytes": abytes},
+        "runtime_copy": _ceiling(torch, stream, achieved),
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
@@ -449,6 +486,7 @@ def bench_sparse(args, wl, ob, torch, table, hp, g, e, x, m, v, vf, c_avg, statu
                      "traffic": _measured_traffic("traffic_sparse_step_bert_large.txt")
                      if wl.name == "bert_large" and nsel == 1 else None,
                      "algorithmic_bytes": abytes},
+        "runtime_copy": _ceiling(torch, stream, achieved),
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
