@@ -103,7 +103,7 @@ def copy_ceiling(torch, stream, nbytes=1 << 30, reps=10):
 
 def _ceiling(torch, stream, achieved):
     copy_gbps = copy_ceiling(torch, stream)
-    log(f"[bench] copy ceiling {copy_gbps:.0f} GB/s")
+    log(f"[bench] runtime copy {copy_gbps:.0f} GB/s")
     return {"copy_GBps": copy_gbps, "copy_frac_of_peak": copy_gbps / PEAK_HBM_GBPS,
             "kernel_frac_of_copy": achieved / copy_gbps,
             "note": "1 GiB device-to-device copy by the runtime (torch copy_) on the same stream "
