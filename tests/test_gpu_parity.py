@@ -308,6 +308,46 @@ def test_degenerate_tensors():
     assert int(d.status.item()) == 0
 
 
+def test_independent_calls_on_two_streams():
+    """Two tables, each with its own state and workspace, stepped on two
+    streams at once (LAMB compression steps on one, 1-bit Adam steps on the
+    other) give bit for bit what each gives alone: the library keeps no
+    state between calls beyond the caller's arrays."""
+    wa = Workload("streams_a", [4096 * 5 + 3, 100, 4096], W=3, init="frozen")
+    wb = Workload("streams_b", [7, 4096 * 2, 999], W=5, init="frozen", seed=1)
+    keys = ("x", "m", "v", "vf", "err_s", "bits_s", "scales_s", "c")
+
+    def run(d, wl, step):
+        if wl is wa:
+            d.compressed_step(step)
+        else:
+            d.adam_compressed_step(step)
+
+    ref = {}
+    for wl in (wa, wb):
+        d = DevRun(wl)
+        for step in range(3):
+            run(d, wl, step)
+        torch.cuda.synchronize()
+        ref[wl.name] = d.window(0, wl.N)
+    da, db = DevRun(wa), DevRun(wb)
+    torch.cuda.synchronize()
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    for step in range(3):
+        with torch.cuda.stream(sa):
+            run(da, wa, step)
+        with torch.cuda.stream(sb):
+            run(db, wb, step)
+    torch.cuda.synchronize()
+    for d, wl in ((da, wa), (db, wb)):
+        got = d.window(0, wl.N)
+        for k in keys:
+            assert np.array_equal(np.asarray(got[k]).view(np.uint32),
+                                  np.asarray(ref[wl.name][k]).view(np.uint32)), (wl.name, k)
+        for w in range(wl.W):
+            assert np.array_equal(got["e"][w].view(np.uint32), ref[wl.name]["e"][w].view(np.uint32))
+
+
 def test_determinism_and_resume():
     """Two runs are bitwise identical, and a run resumed from a saved state
     equals the uninterrupted one (across the warmup -> compression switch)."""
