@@ -85,6 +85,22 @@ MUTATIONS = {
     "sparse_update_fresh_variance": ("x[i] = x[i] - (step * (r * (mhat[i] / dz)));",
                                      "x[i] = x[i] - (step * (r * (mhat[i] / (sqrtf(v_fresh[i]) + hp->eta))));"),
     "sparse_sum_not_mean": ("      mhat[i] = acc / (float)W;", "      mhat[i] = acc;"),
+    "sparse_step_drops_c_avg": ("const float step = hp->lr * c_avg[l];", "const float step = hp->lr;"),
+    "c_drops_c_avg": ("c[l] = c_avg[l] * f;", "c[l] = f;"),
+    "c_drops_factor": ("c[l] = c_avg[l] * f;", "c[l] = c_avg[l];"),
+    "cap_uses_km": ("float f = fminf(fminf(rho[l], hp->f_max), kp * f_prev[l]);",
+                    "float f = fminf(fminf(rho[l], hp->f_max), km * f_prev[l]);"),
+    "floor_uses_kp": ("f = fmaxf(fmaxf(f, hp->f_min), km * f_prev[l]);",
+                      "f = fmaxf(fmaxf(f, hp->f_min), kp * f_prev[l]);"),
+    "f_prev_not_updated": ("    f_prev[l] = f;\n", ""),
+    "rho_min_not_max": ("r = (i == off || q > r) ? q : r;", "r = (i == off || q < r) ? q : r;"),
+    "norm_ratio_zero_guard": ("r = (Qz == 0.0 || Qf == 0.0) ? 1.0f :", "r = (Qz == 0.0 || Qf == 0.0) ? 0.0f :"),
+    "decompress_sign_inverted": (
+        "out[base + j] = sign_bit(bits, C, k, j) ? scales[k] : -scales[k];",
+        "out[base + j] = sign_bit(bits, C, k, j) ? -scales[k] : scales[k];"),
+    "warmup_c_sum_replaced": ("c_sum[l] = c_sum[l] + c[l];", "c_sum[l] = c[l];"),
+    "freeze_f_prev_not_one": ("    f_prev[l] = 1.0f;\n  }\n}", "    f_prev[l] = 0.5f;\n  }\n}"),
+    "freeze_c_avg_not_divided": ("c_avg[l] = c_sum[l] / den;", "c_avg[l] = c_sum[l];"),
 }
 
 

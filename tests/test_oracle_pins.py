@@ -892,3 +892,51 @@ def test_p24_sparse_elementwise_rescale_closed_form():
     want = x0.astype(np.float64) - 1e-3 * 2.0 * rr * mhat / np.sqrt(vfz.astype(np.float64))
     assert np.all(np.abs(x[mask] - want[mask]) <= 2 * U * np.abs(want[mask]) + 8 * U * 1e-3 * 2.0 *
                   np.abs(rr * mhat / np.sqrt(vfz.astype(np.float64)))[mask])
+
+
+# P25 the warmup coefficients accumulate: after T warmup steps (default
+#     reading) c_sum is the sum of the T per-step coefficients the steps
+#     returned, and the freeze makes c_avg their mean
+def test_p25_warmup_coefficients_accumulate():
+    numels = [4096, 500, 3]
+    N, W, T = sum(numels), 2, 6
+    r = rng(53)
+    h = hp(c_min=1e-4)                                        # no coefficient at a clip bound
+    x = f32(r.standard_normal(N) * 0.1)
+    m, v = np.zeros(N, np.float32), np.zeros(N, np.float32)
+    c_sum = np.zeros(3, np.float32)
+    cs = []
+    for _ in range(T):
+        g = [f32(r.standard_normal(N) * 10 ** r.uniform(-4, -2)) for _ in range(W)]
+        cs.append(oracle.warmup_step(numels, g, x, m, v, c_sum, h).astype(np.float64))
+    total = np.sum(cs, axis=0)
+    assert len(set(map(tuple, cs))) == T and np.all(np.array(cs) > 1e-4)   # they vary, unclipped
+    assert np.all(np.abs(c_sum - total) <= T * U * total)
+    c_avg = np.zeros(3, np.float32)
+    oracle.freeze(numels, v, v.copy(), [np.zeros(N, np.float32)] * W, np.zeros(N, np.float32),
+                  c_sum, T, c_avg, np.zeros(3, np.float32), h)
+    assert np.all(np.abs(c_avg - total / T) <= (T + 1) * U * total / T)
+
+
+# P26 norm-ratio factor of a tensor whose sums vanish (eta = 0, zero
+#     variances and momentum): the ratio is taken as 1, as for the trust
+#     ratio, so f = 1 and c = c_avg; the other tensor is unaffected
+def test_p26_norm_ratio_zero_sums():
+    numels = [4096, 4096]
+    N = sum(numels)
+    r = rng(54)
+    h = hp(rho_mode=1, eta=0.0)
+    vfz = np.zeros(N, np.float32)
+    vfz[4096:] = f32(r.uniform(1e-8, 1e-4, 4096))
+    vf = vfz.copy()
+    m = np.zeros(N, np.float32)
+    m[4096:] = f32(r.standard_normal(4096) * 1e-3)
+    x = f32(r.standard_normal(N) * 0.02)
+    g = [np.zeros(N, np.float32)] * 2
+    err_w = [np.zeros(N, np.float32) for _ in range(2)]
+    c_avg = np.array([0.75, 0.75], np.float32)
+    with np.errstate(invalid="ignore"):
+        out = oracle.compressed_step(numels, 4096, g, err_w, np.zeros(N, np.float32), x, m, vfz, vf,
+                                     c_avg, np.ones(2, np.float32), h)
+    assert out["c"][0] == np.float32(0.75)
+    assert np.isfinite(out["c"][1]) and np.all(np.isfinite(x[4096:]))
