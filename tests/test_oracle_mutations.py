@@ -101,6 +101,12 @@ MUTATIONS = {
     "warmup_c_sum_replaced": ("c_sum[l] = c_sum[l] + c[l];", "c_sum[l] = c[l];"),
     "freeze_f_prev_not_one": ("    f_prev[l] = 1.0f;\n  }\n}", "    f_prev[l] = 0.5f;\n  }\n}"),
     "freeze_c_avg_not_divided": ("c_avg[l] = c_sum[l] / den;", "c_avg[l] = c_sum[l];"),
+    "sign_words_not_cleared": ("  for (int64_t q = 0; q < C / 32; ++q) words[q] = 0u;\n", ""),
+    "clip_bounds_swapped": ("c[l] = fminf(fmaxf(r, hp->c_min), hp->c_max);",
+                            "c[l] = fmaxf(fminf(r, hp->c_min), hp->c_max);"),
+    "trust_ratio_on_updated_x": ("X += (double)x[i] * (double)x[i];",
+                                 "X += (double)(x[i] - hp->lr * u[i]) * (double)(x[i] - hp->lr * u[i]);"),
+    "padding_slots_not_zeroed": ("t[j] = j < n ? z[j] * z[j] : 0.0f;", "t[j] = j < n ? z[j] * z[j] : t[j];"),
 }
 
 

@@ -285,6 +285,12 @@ def test_p8_packing(n, C):
     packed = np.packbits(want, bitorder="little").view(np.uint32)
     assert np.array_equal(bits, packed)
     assert int(np.unpackbits(bits.view(np.uint8)).sum()) == int(np.sum(z >= 0))
+    # every sign word is written in full: what the output held before does not leak
+    dirty = np.full(K * C // 32, 0xFFFFFFFF, np.uint32)
+    err0, sc = np.zeros(n, np.float32), np.zeros(K, np.float32)      # kept alive across the call
+    oracle.lib().oracle_compress_ef(n, C, oracle._ptr(z), oracle._ptr(err0), oracle._ptr(dirty),
+                                    oracle._ptr(sc))
+    assert np.array_equal(dirty, packed)
 
 
 def test_p8_tree_order_against_independent_pairwise():
