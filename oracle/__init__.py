@@ -74,6 +74,17 @@ def _ptr_array(arrays):
     return arr
 
 
+def _words_out(n):
+    """An output array of sign words, all ones until the oracle writes it
+    (so a word it failed to write shows)."""
+    return np.full(n, 0xFFFFFFFF, np.uint32)
+
+
+def _f32_out(n):
+    """An fp32 output array, NaN until the oracle writes it."""
+    return np.full(n, np.nan, np.float32)
+
+
 def num_chunks(n, C):
     return (n + C - 1) // C
 
@@ -92,8 +103,8 @@ def compress_ef(inp, err, C):
     """err is updated in place; returns (bits uint32[K*C/32], scales f32[K])."""
     n = inp.size
     K = num_chunks(n, C)
-    bits = np.zeros(K * C // 32, np.uint32)
-    scales = np.zeros(K, np.float32)
+    bits = _words_out(K * C // 32)
+    scales = _f32_out(K)
     lib().oracle_compress_ef(n, C, _ptr(_f32(inp)), _ptr(_f32(err)), _ptr(bits), _ptr(scales))
     return bits, scales
 
@@ -115,8 +126,8 @@ def average_packed(bits_w, scales_w, err_s, C):
     n = err_s.size
     K = num_chunks(n, C)
     W = len(bits_w)
-    bits = np.zeros(K * C // 32, np.uint32)
-    scales = np.zeros(K, np.float32)
+    bits = _words_out(K * C // 32)
+    scales = _f32_out(K)
     lib().oracle_average_packed(n, C, W, _ptr_array(bits_w), _ptr_array(scales_w),
                                 _ptr(_f32(err_s)), _ptr(bits), _ptr(scales))
     return bits, scales
@@ -151,10 +162,10 @@ def compressed_step(numels, C, grads, err_w, err_s, x, m, v_frozen, v_fresh, c_a
     W = len(grads)
     K = num_chunks(N, C)
     c_out = np.empty(L, np.float32)
-    bits_w = [np.zeros(K * C // 32, np.uint32) for _ in range(W)]
-    scales_w = [np.zeros(K, np.float32) for _ in range(W)]
-    bits_s = np.zeros(K * C // 32, np.uint32)
-    scales_s = np.zeros(K, np.float32)
+    bits_w = [_words_out(K * C // 32) for _ in range(W)]
+    scales_w = [_f32_out(K) for _ in range(W)]
+    bits_s = _words_out(K * C // 32)
+    scales_s = _f32_out(K)
     lib().oracle_compressed_step(
         L, _ptr(numels), C, W, _ptr_array([_f32(g) for g in grads]),
         _ptr_array([_f32(e) for e in err_w]), _ptr(_f32(err_s)), _ptr(_f32(x)), _ptr(_f32(m)),
@@ -177,10 +188,10 @@ def adam_compressed_step(C, grads, err_w, err_s, x, m, v_frozen, hp, compressor=
     n = x.size
     W = len(grads)
     K = num_chunks(n, C)
-    bits_w = [np.zeros(K * C // 32, np.uint32) for _ in range(W)]
-    scales_w = [np.zeros(K, np.float32) for _ in range(W)]
-    bits_s = np.zeros(K * C // 32, np.uint32)
-    scales_s = np.zeros(K, np.float32)
+    bits_w = [_words_out(K * C // 32) for _ in range(W)]
+    scales_w = [_f32_out(K) for _ in range(W)]
+    bits_s = _words_out(K * C // 32)
+    scales_s = _f32_out(K)
     lib().oracle_adam_compressed_step(
         n, C, W, _ptr_array([_f32(g) for g in grads]), _ptr_array([_f32(e) for e in err_w]),
         _ptr(_f32(err_s)), _ptr(_f32(x)), _ptr(_f32(m)), _ptr(_f32(v_frozen)),
@@ -199,8 +210,8 @@ def sparse_step(numels, C, nsel, sel, grads, err_w, x, m, v_frozen, v_fresh, c_a
     W = len(grads)
     sel = np.ascontiguousarray(sel, dtype=np.int32)
     assert sel.size == K
-    vals_w = [np.zeros(K * nsel * 64, np.float32) for _ in range(W)]
-    vals_s = np.zeros(K * nsel * 64, np.float32)
+    vals_w = [_f32_out(K * nsel * 64) for _ in range(W)]
+    vals_s = _f32_out(K * nsel * 64)
     lib().oracle_sparse_step(
         numels.size, numels.ctypes.data, C, W, nsel, sel.ctypes.data,
         _ptr_array([_f32(g) for g in grads]), _ptr_array([_f32(e) for e in err_w]), _ptr(_f32(x)),

@@ -107,6 +107,10 @@ MUTATIONS = {
     "trust_ratio_on_updated_x": ("X += (double)x[i] * (double)x[i];",
                                  "X += (double)(x[i] - hp->lr * u[i]) * (double)(x[i] - hp->lr * u[i]);"),
     "padding_slots_not_zeroed": ("t[j] = j < n ? z[j] * z[j] : 0.0f;", "t[j] = j < n ? z[j] * z[j] : t[j];"),
+    "sparse_values_not_cleared": ("  for (int64_t q = 0; q < K * per; ++q) vals_s[q] = 0.0f;\n", ""),
+    "sparse_worker_values_wrong_slot": (
+        "if (vals_w && vals_w[w]) vals_w[w][k * per + slot] = z;",
+        "if (vals_w && vals_w[w]) vals_w[w][k * per + (slot ^ 1)] = z;"),
 }
 
 
