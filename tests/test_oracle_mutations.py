@@ -111,6 +111,16 @@ MUTATIONS = {
     "sparse_worker_values_wrong_slot": (
         "if (vals_w && vals_w[w]) vals_w[w][k * per + slot] = z;",
         "if (vals_w && vals_w[w]) vals_w[w][k * per + (slot ^ 1)] = z;"),
+    "sparse_momentum_not_replaced": (
+        "        x[i] = x[i] - (step * (r * (mhat[i] / dz)));\n      }\n      m[i] = mhat[i];\n",
+        "        x[i] = x[i] - (step * (r * (mhat[i] / dz)));\n      }\n"),
+    "momentum_not_replaced": (
+        "        x[i] = x[i] - (step * (mhat[i] / (sqrtf(v_frozen[i]) + hp->eta)));\n      m[i] = mhat[i];\n",
+        "        x[i] = x[i] - (step * (mhat[i] / (sqrtf(v_frozen[i]) + hp->eta)));\n"),
+    "update_with_old_momentum": (
+        "        x[i] = x[i] - (step * (mhat[i] / (sqrtf(v_frozen[i]) + hp->eta)));\n      m[i] = mhat[i];\n",
+        "        x[i] = x[i] - (step * (m[i] / (sqrtf(v_frozen[i]) + hp->eta)));\n      m[i] = mhat[i];\n"),
+    "freeze_v_fresh_not_copied": ("  for (int64_t i = 0; i < N; ++i) v_fresh[i] = v[i];\n", ""),
 }
 
 
