@@ -26,7 +26,8 @@ __all__ = [
     "onebit_lamb_warmup_step", "onebit_lamb_freeze", "onebit_compress_ef", "onebit_average_packed",
     "onebit_lamb_compressed_step", "onebit_lamb_compress_average", "onebit_lamb_rescale_update",
     "onebit_decompress", "onebit_last_error", "onebit_version", "onebit_adam_warmup_step",
-    "onebit_adam_compressed_step", "onebit_sparse_compressed_step", "ONEBIT_RHO_MAX",
+    "onebit_adam_compressed_step", "onebit_sparse_compressed_step", "onebit_worker_compress",
+    "onebit_lamb_rescale_stats", "ONEBIT_RHO_MAX",
     "ONEBIT_RHO_NORM_RATIO",
     "LIB_PATH",
 ]
@@ -85,6 +86,10 @@ _lib.onebit_adam_compressed_step.argtypes = [_i64, _i32, _i32, _P, _P, _P, _P, _
                                              _P, ctypes.POINTER(onebit_hparams), _P, _P]
 _lib.onebit_sparse_compressed_step.argtypes = [_P, _i32, _i32, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                                _P, ctypes.POINTER(onebit_hparams), _P, _P]
+_lib.onebit_worker_compress.argtypes = [_i64, _i32, _P, _P, _P, _P, _P, _P, _P,
+                                        ctypes.POINTER(onebit_hparams), _P, _P]
+_lib.onebit_lamb_rescale_stats.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P,
+                                           ctypes.POINTER(onebit_hparams), _P, _P]
 _lib.onebit_last_error.restype = ctypes.c_char_p
 _lib.onebit_version.restype = ctypes.c_char_p
 for _f in ("onebit_layer_table_create", "onebit_layer_table_destroy", "onebit_layer_table_info",
@@ -382,3 +387,26 @@ def onebit_sparse_compressed_step(table, W, nsel, sel, grads, err_w, x, m, v_fro
         e(v_frozen, "v_frozen"), e(v_fresh, "v_fresh"), _ptr(c_avg, fn, "c_avg", z.tensors, _F32),
         _ptr_list(vals_w, fn, "vals_w", W, per, _F32), _ptr(vals_s, fn, "vals_s", per, _F32),
         ctypes.byref(hp), _ptr(status, fn, "status", 4), _stream(stream)), fn)
+
+
+def onebit_worker_compress(n, chunk, grad, err_w, m, bits_m, scales_m, bits_w, scales_w, hp,
+                           status=None, stream=None):
+    fn, z = "onebit_worker_compress", _Sizes(n, chunk)
+    e = lambda a, nm: _ptr(a, fn, nm, z.elems, _F32)  # noqa: E731
+    _check(_lib.onebit_worker_compress(
+        n, chunk, e(grad, "grad"), e(err_w, "err_w"), e(m, "m"),
+        _ptr(bits_m, fn, "bits_m", z.words, _WORDS), _ptr(scales_m, fn, "scales_m", z.scales, _F32),
+        _ptr(bits_w, fn, "bits_w", z.words, _WORDS), _ptr(scales_w, fn, "scales_w", z.scales, _F32),
+        ctypes.byref(hp), _ptr(status, fn, "status", 4), _stream(stream)), fn)
+
+
+def onebit_lamb_rescale_stats(table, bits_s, scales_s, m, bits_m, scales_m, v_frozen, v_fresh, hp,
+                              ws, stream=None):
+    fn, z = "onebit_lamb_rescale_stats", _table_sizes(table, 1)
+    e = lambda a, nm: _ptr(a, fn, nm, z.elems, _F32)  # noqa: E731
+    _check(_lib.onebit_lamb_rescale_stats(
+        _h(table), _ptr(bits_s, fn, "bits_s", z.words, _WORDS),
+        _ptr(scales_s, fn, "scales_s", z.scales, _F32), e(m, "m"),
+        _ptr(bits_m, fn, "bits_m", z.words, _WORDS), _ptr(scales_m, fn, "scales_m", z.scales, _F32),
+        e(v_frozen, "v_frozen"), e(v_fresh, "v_fresh"), ctypes.byref(hp), _ptr(ws, fn, "ws", z.ws),
+        _stream(stream)), fn)

@@ -47,6 +47,7 @@ int ok() {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 bool chunk_supported(int32_t c) { return c >= 1024 && c <= 16384 && (c & (c - 1)) == 0; }
 
@@ -58,6 +59,14 @@ size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
     if (!(p)) return fail(ONEBIT_EINVAL, "%s: %s is NULL", __func__, name);                  \
     if (!aligned16(p)) return fail(ONEBIT_EALIGN, "%s: %s is not 16-byte aligned", __func__, \
                                    name);                                                    \
+  } while (0)
+
+// Sign-word and scale arrays are read and written one 32-bit word at a time.
+#define CHECK_WORDS(p, name)                                                                 \
+  do {                                                                                       \
+    if (!(p)) return fail(ONEBIT_EINVAL, "%s: %s is NULL", __func__, name);                  \
+    if (!aligned4(p)) return fail(ONEBIT_EALIGN, "%s: %s is not 4-byte aligned", __func__,   \
+                                  name);                                                     \
   } while (0)
 
 #define CHECK_OPT_PTR(p, name)                                                               \
@@ -203,6 +212,9 @@ constexpr int kAdam_SPT = 4;
 // streaming accesses 6.36 ms against 6.66 ms plain; a 5- or 6-wave register
 // cap changes nothing (6.38 ms), so it runs uncapped (104 VGPRs, no spills).
 constexpr bool kSparse_NT = true;
+// One GPU's share of a W-GPU step: the worker compression and the receiver
+// statistics stream like the codec kernels.
+constexpr bool kShare_NT = true;
 // Chunk geometry of the element-wise 1-bit Adam warmup kernel (any chunk
 // gives the same result; this one gives 256-thread workgroups).
 constexpr int kAdamWarmupChunk = 4096;
@@ -311,6 +323,45 @@ struct LaunchSparse {
 };
 
 template <int C>
+struct LaunchWorker {
+  static void run(int64_t n, const float* g, float* e, const float* m, const uint32_t* bits_m,
+                  const float* scales_m, uint32_t* bits_w, float* scales_w, const Coef& cf,
+                  int32_t* status, hipStream_t st) {
+    if (m)
+      launch_chunks<C>(n, st, k_worker_compress<C, kShare_NT, false>, n, g, e, m, bits_m, scales_m,
+                       bits_w, scales_w, cf, status);
+    else
+      launch_chunks<C>(n, st, k_worker_compress<C, kShare_NT, true>, n, g, e, m, bits_m, scales_m,
+                       bits_w, scales_w, cf, status);
+  }
+};
+
+template <int C>
+struct LaunchStats {
+  static void run(const onebit_layer_table* t, const uint32_t* bits_s, const float* scales_s,
+                  const float* m, const uint32_t* bits_m, const float* scales_m,
+                  const float* v_frozen, float* v_fresh, const Coef& cf, bool rn, const Ws& ws,
+                  hipStream_t st) {
+    if (rn && !m)
+      go<true, true>(t, bits_s, scales_s, m, bits_m, scales_m, v_frozen, v_fresh, cf, ws, st);
+    else if (rn)
+      go<true, false>(t, bits_s, scales_s, m, bits_m, scales_m, v_frozen, v_fresh, cf, ws, st);
+    else if (!m)
+      go<false, true>(t, bits_s, scales_s, m, bits_m, scales_m, v_frozen, v_fresh, cf, ws, st);
+    else
+      go<false, false>(t, bits_s, scales_s, m, bits_m, scales_m, v_frozen, v_fresh, cf, ws, st);
+  }
+  template <bool RN, bool PM>
+  static void go(const onebit_layer_table* t, const uint32_t* bits_s, const float* scales_s,
+                 const float* m, const uint32_t* bits_m, const float* scales_m,
+                 const float* v_frozen, float* v_fresh, const Coef& cf, const Ws& ws,
+                 hipStream_t st) {
+    launch_chunks<C>(t->N, st, k_rescale_stats<C, kShare_NT, RN, PM>, t->dev, bits_s, scales_s, m,
+                     bits_m, scales_m, v_frozen, v_fresh, ws.seg_max, ws.seg_x, ws.seg_u, cf);
+  }
+};
+
+template <int C>
 struct LaunchPassB {
   static void run(const onebit_layer_table* t, const uint32_t* bits_s, const float* scales_s,
                   float* x, float* m, const float* v_frozen, const float* c_avg, float* f_prev,
@@ -342,13 +393,13 @@ int check_workers(const char* fn, int32_t W, const float* const* grads, float* c
     wk.g[w] = grads[w];
     wk.e[w] = err_w[w];
     if (bits_w) {
-      if (bits_w[w] && !aligned16(bits_w[w]))
-        return fail(ONEBIT_EALIGN, "%s: bits_w[%d] is not 16-byte aligned", fn, w);
+      if (bits_w[w] && !aligned4(bits_w[w]))
+        return fail(ONEBIT_EALIGN, "%s: bits_w[%d] is not 4-byte aligned", fn, w);
       wk.bits[w] = bits_w[w];
     }
     if (scales_w) {
-      if (scales_w[w] && !aligned16(scales_w[w]))
-        return fail(ONEBIT_EALIGN, "%s: scales_w[%d] is not 16-byte aligned", fn, w);
+      if (scales_w[w] && !aligned4(scales_w[w]))
+        return fail(ONEBIT_EALIGN, "%s: scales_w[%d] is not 4-byte aligned", fn, w);
       wk.scales[w] = scales_w[w];
     }
   }
@@ -367,9 +418,11 @@ int check_phase1(const char* fn, const onebit_layer_table* table, int32_t W,
   if (int rc = check_workers(fn, W, grads, err_w, bits_w, scales_w, wk)) return rc;
   const void* req[] = {err_s, v_frozen, v_fresh, bits_s, scales_s, ws};
   const char* names[] = {"err_s", "v_frozen", "v_fresh", "bits_s", "scales_s", "ws"};
+  const int align[] = {16, 16, 16, 4, 4, 16};
   for (int i = 0; i < 6; ++i) {
     if (!req[i]) return fail(ONEBIT_EINVAL, "%s: %s is NULL", fn, names[i]);
-    if (!aligned16(req[i])) return fail(ONEBIT_EALIGN, "%s: %s is not 16-byte aligned", fn, names[i]);
+    if (reinterpret_cast<uintptr_t>(req[i]) % align[i])
+      return fail(ONEBIT_EALIGN, "%s: %s is not %d-byte aligned", fn, names[i], align[i]);
   }
   if (m && !aligned16(m)) return fail(ONEBIT_EALIGN, "%s: m is not 16-byte aligned", fn);
   return ONEBIT_OK;
@@ -383,9 +436,11 @@ int check_phase2(const char* fn, const onebit_layer_table* table, const uint32_t
   if (int rc = check_hparams(hp, fn)) return rc;
   const void* req[] = {bits_s, scales_s, x, v_frozen, c_avg, f_prev, ws};
   const char* names[] = {"bits_s", "scales_s", "x", "v_frozen", "c_avg", "f_prev", "ws"};
+  const int align[] = {4, 4, 16, 16, 16, 16, 16};
   for (int i = 0; i < 7; ++i) {
     if (!req[i]) return fail(ONEBIT_EINVAL, "%s: %s is NULL", fn, names[i]);
-    if (!aligned16(req[i])) return fail(ONEBIT_EALIGN, "%s: %s is not 16-byte aligned", fn, names[i]);
+    if (reinterpret_cast<uintptr_t>(req[i]) % align[i])
+      return fail(ONEBIT_EALIGN, "%s: %s is not %d-byte aligned", fn, names[i], align[i]);
   }
   if (m && !aligned16(m)) return fail(ONEBIT_EALIGN, "%s: m is not 16-byte aligned", fn);
   if (c_out && !aligned16(c_out)) return fail(ONEBIT_EALIGN, "%s: c_out is not 16-byte aligned", fn);
@@ -518,8 +573,8 @@ int onebit_compress_ef(int64_t n, int32_t chunk, const float* in, float* err, ui
   if (n == 0) return ok();
   CHECK_PTR(in, "in");
   CHECK_PTR(err, "err");
-  CHECK_PTR(bits, "bits");
-  CHECK_PTR(scales, "scales");
+  CHECK_WORDS(bits, "bits");
+  CHECK_WORDS(scales, "scales");
   by_chunk<LaunchCompress>(chunk, n, in, err, bits, scales, status, (hipStream_t)stream);
   return launch_status(__func__);
 }
@@ -534,14 +589,14 @@ int onebit_average_packed(int64_t n, int32_t chunk, int32_t W, const uint32_t* c
   if (!bits_w || !scales_w) return fail(ONEBIT_EINVAL, "%s: worker arrays are NULL", __func__);
   PackedIn pin{};
   for (int w = 0; w < W; ++w) {
-    CHECK_PTR(bits_w[w], "bits_w[w]");
-    CHECK_PTR(scales_w[w], "scales_w[w]");
+    CHECK_WORDS(bits_w[w], "bits_w[w]");
+    CHECK_WORDS(scales_w[w], "scales_w[w]");
     pin.bits[w] = bits_w[w];
     pin.scales[w] = scales_w[w];
   }
   CHECK_PTR(err_s, "err_s");
-  CHECK_PTR(bits_out, "bits_out");
-  CHECK_PTR(scales_out, "scales_out");
+  CHECK_WORDS(bits_out, "bits_out");
+  CHECK_WORDS(scales_out, "scales_out");
   by_chunk<LaunchAverage>(chunk, n, (int)W, pin, err_s, bits_out, scales_out, status,
                           (hipStream_t)stream);
   return launch_status(__func__);
@@ -552,8 +607,8 @@ int onebit_decompress(int64_t n, int32_t chunk, const uint32_t* bits, const floa
   if (n < 0) return fail(ONEBIT_EINVAL, "%s: n < 0", __func__);
   if (!chunk_supported(chunk)) return fail(ONEBIT_EUNSUPPORTED, "%s: chunk %d", __func__, chunk);
   if (n == 0) return ok();
-  CHECK_PTR(bits, "bits");
-  CHECK_PTR(scales, "scales");
+  CHECK_WORDS(bits, "bits");
+  CHECK_WORDS(scales, "scales");
   CHECK_PTR(out, "out");
   by_chunk<LaunchDecompress>(chunk, n, bits, scales, out, (hipStream_t)stream);
   return launch_status(__func__);
@@ -667,6 +722,58 @@ int onebit_lamb_compressed_step(const onebit_layer_table* table, int32_t W,
   return launch_status(__func__);
 }
 
+int onebit_worker_compress(int64_t n, int32_t chunk, const float* grad, float* err_w,
+                           const float* m, const uint32_t* bits_m, const float* scales_m,
+                           uint32_t* bits_w, float* scales_w, const onebit_hparams* hp,
+                           int32_t* status, void* stream) {
+  if (n < 0) return fail(ONEBIT_EINVAL, "%s: n < 0", __func__);
+  if (!chunk_supported(chunk)) return fail(ONEBIT_EUNSUPPORTED, "%s: chunk %d", __func__, chunk);
+  if (int rc = check_hparams(hp, __func__)) return rc;
+  if ((n + chunk - 1) / chunk > INT32_MAX / 2)
+    return fail(ONEBIT_EUNSUPPORTED, "%s: n too large", __func__);
+  if (n == 0) return ok();
+  CHECK_PTR(grad, "grad");
+  CHECK_PTR(err_w, "err_w");
+  CHECK_WORDS(bits_w, "bits_w");
+  CHECK_WORDS(scales_w, "scales_w");
+  if (m) {
+    CHECK_PTR(m, "m");
+  } else {
+    if (!bits_m || !scales_m)
+      return fail(ONEBIT_EINVAL, "%s: m is NULL and bits_m/scales_m do not give it", __func__);
+    CHECK_WORDS(bits_m, "bits_m");
+    CHECK_WORDS(scales_m, "scales_m");
+  }
+  by_chunk<LaunchWorker>(chunk, n, grad, err_w, m, bits_m, scales_m, bits_w, scales_w,
+                         make_coef(*hp), status, (hipStream_t)stream);
+  return launch_status(__func__);
+}
+
+int onebit_lamb_rescale_stats(const onebit_layer_table* table, const uint32_t* bits_s,
+                              const float* scales_s, const float* m, const uint32_t* bits_m,
+                              const float* scales_m, const float* v_frozen, float* v_fresh,
+                              const onebit_hparams* hp, void* ws, void* stream) {
+  if (int rc = check_table(table, __func__)) return rc;
+  if (int rc = check_hparams(hp, __func__)) return rc;
+  CHECK_WORDS(bits_s, "bits_s");
+  CHECK_WORDS(scales_s, "scales_s");
+  CHECK_PTR(v_frozen, "v_frozen");
+  CHECK_PTR(v_fresh, "v_fresh");
+  CHECK_PTR(ws, "ws");
+  if (m) {
+    CHECK_PTR(m, "m");
+  } else {
+    if (!bits_m || !scales_m)
+      return fail(ONEBIT_EINVAL, "%s: m is NULL and bits_m/scales_m do not give it", __func__);
+    CHECK_WORDS(bits_m, "bits_m");
+    CHECK_WORDS(scales_m, "scales_m");
+  }
+  by_chunk<LaunchStats>(table->chunk, table, bits_s, scales_s, m, bits_m, scales_m, v_frozen,
+                        v_fresh, make_coef(*hp), hp->rho_mode == ONEBIT_RHO_NORM_RATIO,
+                        ws_view(table, ws), (hipStream_t)stream);
+  return launch_status(__func__);
+}
+
 int onebit_adam_warmup_step(int64_t n, int32_t W, const float* const* grads, float* x, float* m,
                             float* v, const onebit_hparams* hp, void* stream) {
   if (n < 0) return fail(ONEBIT_EINVAL, "%s: n < 0", __func__);
@@ -708,8 +815,8 @@ int onebit_adam_compressed_step(int64_t n, int32_t chunk, int32_t W, const float
   CHECK_PTR(x, "x");
   CHECK_OPT_PTR(m, "m");
   CHECK_PTR(v_frozen, "v_frozen");
-  CHECK_PTR(bits_s, "bits_s");
-  CHECK_PTR(scales_s, "scales_s");
+  CHECK_WORDS(bits_s, "bits_s");
+  CHECK_WORDS(scales_s, "scales_s");
   by_chunk<LaunchAdam>(chunk, n, (int)W, wk, err_s, m, x, v_frozen, bits_s, scales_s,
                        make_coef(*hp), status, (hipStream_t)stream);
   return launch_status(__func__);

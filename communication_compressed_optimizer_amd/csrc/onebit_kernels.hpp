@@ -843,6 +843,163 @@ k_adam_compressed(int64_t n_full, int64_t n, int64_t K, int W, Workers wk,
                                           v_frozen, bits_s, scales_s, cf, status, lds);
 }
 
+// ---------------------------------------------------------------------------
+// One GPU's share of a compression step on W GPUs.  Each GPU compresses its
+// own worker's momentum over the whole buffer (k_worker_compress), averages
+// and recompresses the chunks it serves, 1/W of them (k_average_packed on
+// that range), and, once every GPU holds the server's packed output, forms
+// the rescale statistics (k_rescale_stats) and updates its replica
+// (k_rescale_finalize, k_compressed_pass_b).  The arithmetic is that of the
+// fused k_compressed_pass_a, element for element, so both give the same
+// bits.
+// ---------------------------------------------------------------------------
+
+// beta1*m for one chunk: from the fp32 momentum or (PM) from the previous
+// server output (bits_m, scales_m), whose decompressed value is the momentum.
+template <int C, bool TAIL, bool NT, bool PM>
+__device__ __forceinline__ void beta1_momentum(const ChunkAt<C, TAIL>& ch,
+                                               const float* __restrict__ m,
+                                               const uint32_t* __restrict__ bits_m,
+                                               const float* __restrict__ scales_m, const Coef& cf,
+                                               Slots& bm) {
+  if constexpr (PM) {
+    uint32_t pn[4];
+    load_sign_nibbles<C>(bits_m + ch.k * Geo<C>::WORDS, pn);
+    const float sp = scales_m[ch.k];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) bm[a][c] = cf.beta1 * signed_scale(pn, a, c, sp);
+  } else {
+    load_chunk<C, TAIL, NT>(m, ch.base, ch.nk, bm);
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) bm[a][c] = cf.beta1 * bm[a][c];
+  }
+}
+
+// One worker: z = (beta1*m + a1*g) + e, error-compensated 1-bit compression.
+template <int C, bool TAIL, bool NT, bool PM>
+__device__ __forceinline__ void worker_compress_chunk(int64_t k, int64_t n, const float* __restrict__ g,
+                                                      float* __restrict__ e,
+                                                      const float* __restrict__ m,
+                                                      const uint32_t* __restrict__ bits_m,
+                                                      const float* __restrict__ scales_m,
+                                                      uint32_t* __restrict__ bits_w,
+                                                      float* __restrict__ scales_w, const Coef& cf,
+                                                      int32_t* status, float4* lds) {
+  int parity = 0;
+  const ChunkAt<C, TAIL> ch(k, n);
+  Slots z, gg, ee;
+  beta1_momentum<C, TAIL, NT, PM>(ch, m, bits_m, scales_m, cf, z);
+  load_chunk<C, TAIL, NT>(g, ch.base, ch.nk, gg);
+  load_chunk<C, TAIL, NT>(e, ch.base, ch.nk, ee);
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) z[a][c] = (z[a][c] + (cf.a1 * gg[a][c])) + ee[a][c];
+  uint32_t nib[4];
+  const float s = compress_slots<C, TAIL>(z, ch.nk, lds, parity, nib);
+  store_chunk<C, TAIL, NT>(e, ch.base, ch.nk, z);
+  store_sign_words<C>(bits_w + ch.k * Geo<C>::WORDS, nib);
+  if (threadIdx.x == 0) {
+    scales_w[ch.k] = s;
+    if (!__builtin_isfinite(s)) flag(status, 1);
+  }
+}
+
+template <int C, bool NT = true, bool PM = false>
+__global__ void __launch_bounds__(C / 16)
+k_worker_compress(int64_t n_full, int64_t n, const float* __restrict__ g, float* __restrict__ e,
+                  const float* __restrict__ m, const uint32_t* __restrict__ bits_m,
+                  const float* __restrict__ scales_m, uint32_t* __restrict__ bits_w,
+                  float* __restrict__ scales_w, Coef cf, int32_t* status) {
+  __shared__ float4 lds[2 * Geo<C>::T];
+  const int64_t has_tail = partial_chunks<C>(n_full, n);
+  if (has_tail && blockIdx.x == 0)
+    worker_compress_chunk<C, true, NT, PM>(n_full, n, g, e, m, bits_m, scales_m, bits_w, scales_w,
+                                           cf, status, lds);
+  else
+    worker_compress_chunk<C, false, NT, PM>((int64_t)blockIdx.x - has_tail, n, g, e, m, bits_m,
+                                            scales_m, bits_w, scales_w, cf, status, lds);
+}
+
+// The receiver side of the rescale: mhat from the server's packed output,
+// the reconstructed gradient, the fresh variance, and the per-(chunk,
+// tensor) statistic of the rescale (as the second half of pass A).
+template <int C, bool TAIL, bool NT, bool RN, bool PM>
+__device__ __forceinline__ void rescale_stats_chunk(int64_t kk, const DevTable& tab,
+                                                    const uint32_t* __restrict__ bits_s,
+                                                    const float* __restrict__ scales_s,
+                                                    const float* __restrict__ m,
+                                                    const uint32_t* __restrict__ bits_m,
+                                                    const float* __restrict__ scales_m,
+                                                    const float* __restrict__ v_frozen,
+                                                    float* __restrict__ v_fresh,
+                                                    float* __restrict__ seg_max,
+                                                    double* __restrict__ seg_z,
+                                                    double* __restrict__ seg_f, const Coef& cf,
+                                                    float* red, double* dred) {
+  const ChunkAt<C, TAIL> ch(kk, tab.N);
+  const int64_t base = ch.base;
+  const int nk = ch.nk;
+  uint32_t nib[4];
+  load_sign_nibbles<C>(bits_s + ch.k * Geo<C>::WORDS, nib);
+  const float s2 = scales_s[ch.k];
+  Slots bm, vf, vz;
+  beta1_momentum<C, TAIL, NT, PM>(ch, m, bits_m, scales_m, cf, bm);
+  load_chunk<C, TAIL, NT>(v_fresh, base, nk, vf);
+  load_chunk<C, TAIL, NT>(v_frozen, base, nk, vz);
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float mh = signed_scale(nib, a, c, s2);
+      const float gh = (mh - bm[a][c]) / cf.a1;
+      vf[a][c] = (cf.beta2 * vf[a][c]) + (cf.a2 * (gh * gh));
+    }
+  store_chunk<C, TAIL, NT>(v_fresh, base, nk, vf);
+  if constexpr (RN) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        vz[a][c] = __builtin_sqrtf(vz[a][c]) + cf.eta;
+        vf[a][c] = __builtin_sqrtf(vf[a][c]) + cf.eta;
+      }
+    segment_sums<C>(tab, ch.k, base, nk, vz, vf, dred, seg_z, seg_f);
+  } else {
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        vz[a][c] = (__builtin_sqrtf(vz[a][c]) + cf.eta) / (__builtin_sqrtf(vf[a][c]) + cf.eta);
+    segment_max<C>(tab, ch.k, base, nk, vz, red, seg_max);
+  }
+}
+
+template <int C, bool NT = true, bool RN = false, bool PM = false>
+__global__ void __launch_bounds__(C / 16)
+k_rescale_stats(int64_t n_full, DevTable tab, const uint32_t* __restrict__ bits_s,
+                const float* __restrict__ scales_s, const float* __restrict__ m,
+                const uint32_t* __restrict__ bits_m, const float* __restrict__ scales_m,
+                const float* __restrict__ v_frozen, float* __restrict__ v_fresh,
+                float* __restrict__ seg_max, double* __restrict__ seg_z,
+                double* __restrict__ seg_f, Coef cf) {
+  __shared__ float red[Geo<C>::T / 64];
+  __shared__ double dred[RN ? 2 * (Geo<C>::T / 64) : 1];
+  const int64_t has_tail = tab.K - n_full;
+  if (has_tail && blockIdx.x == 0)
+    rescale_stats_chunk<C, true, NT, RN, PM>(n_full, tab, bits_s, scales_s, m, bits_m, scales_m,
+                                             v_frozen, v_fresh, seg_max, seg_z, seg_f, cf, red,
+                                             dred);
+  else
+    rescale_stats_chunk<C, false, NT, RN, PM>((int64_t)blockIdx.x - has_tail, tab, bits_s,
+                                              scales_s, m, bits_m, scales_m, v_frozen, v_fresh,
+                                              seg_max, seg_z, seg_f, cf, red, dred);
+}
+
 // 1-bit Adam warmup: one Adam step, element-wise in one pass (mean gradient,
 // moments, x = x - lr*(m/(sqrt(v)+eta))).
 template <int C, bool TAIL>

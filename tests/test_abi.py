@@ -154,3 +154,30 @@ def test_binding_checks_tensors_before_the_library(ob):
     assert ob._Sizes(10, 3000).elems is None and ob._Sizes(-1, 4096).elems is None
     z = ob._Sizes(4097, 4096)
     assert (z.K, z.elems, z.words, z.scales) == (2, 4 * 4097, 4 * 2 * 128, 8)
+
+
+def test_share_entry_point_checks(ob):
+    """One GPU's share: argument errors come back as codes without a GPU."""
+    lib = ob._lib
+    P = ctypes.c_void_p
+    hp = ob.onebit_hparams(beta1=0.9, beta2=0.999, eta=1e-8, lr=1e-3)
+    hpr = ctypes.byref(hp)
+    args = [P(4096), P(4096), P(4096), None, None, P(4096), P(4096)]
+    assert lib.onebit_worker_compress(10, 3000, *args, hpr, None, None) == ob.ONEBIT_EUNSUPPORTED
+    assert lib.onebit_worker_compress(-1, 4096, *args, hpr, None, None) == ob.ONEBIT_EINVAL
+    assert lib.onebit_worker_compress(0, 4096, *[None] * 7, hpr, None, None) == ob.ONEBIT_OK
+    bad = list(args)
+    bad[2] = None                     # no fp32 momentum and no packed one
+    assert lib.onebit_worker_compress(10, 4096, *bad, hpr, None, None) == ob.ONEBIT_EINVAL
+    assert "m is NULL" in ob.onebit_last_error()
+    bad = list(args)
+    bad[0] = P(4100)                  # grad misaligned
+    assert lib.onebit_worker_compress(10, 4096, *bad, hpr, None, None) == ob.ONEBIT_EALIGN
+    bad = list(args)
+    bad[5] = P(4100)                  # sign words may start at any 4-byte boundary
+    bad[6] = P(4098)                  # but not at 2 bytes
+    assert lib.onebit_worker_compress(10, 4096, *bad, hpr, None, None) == ob.ONEBIT_EALIGN
+    assert "scales_w is not 4-byte aligned" in ob.onebit_last_error()
+    assert lib.onebit_lamb_rescale_stats(None, P(4096), P(4096), P(4096), None, None, P(4096),
+                                         P(4096), hpr, P(4096), None) == ob.ONEBIT_EINVAL
+

@@ -1,0 +1,217 @@
+"""One GPU's share of a W-GPU compression step, on one GPU.
+
+W simulated GPUs step through the per-GPU entry points: each compresses its
+own worker's momentum over the whole buffer (onebit_worker_compress), serves
+1/W of the chunks as the server (onebit_average_packed on its chunk range),
+and, with the server's packed output in hand, updates its own replica
+(onebit_lamb_rescale_stats, onebit_lamb_rescale_update).  The all-to-all and
+the all-gather are pointer hand-offs here.  Every replica must equal the
+fused onebit_lamb_compressed_step bit for bit, and the oracle within the
+parity bar.
+"""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("no GPU", allow_module_level=True)
+
+import communication_compressed_optimizer_amd as ob  # noqa: E402
+from synth.workloads import WORKLOADS, Workload  # noqa: E402
+
+from tests.harness import DevRun, HostRun, assert_parity, compare_state  # noqa: E402
+
+
+def chunk_ranges(K, W):
+    """The chunks GPU p serves: [K*p // W, K*(p+1) // W)."""
+    return [(K * p // W, K * (p + 1) // W) for p in range(W)]
+
+
+class Sharded:
+    """W simulated GPUs.  Replicated state (x, m, v_fresh, f_prev, c) is kept
+    for the GPUs in `replicas`; the workers' errors and the server's error
+    (split by chunk range) are each GPU's own."""
+
+    def __init__(self, d, replicas=None):
+        self.d = d
+        W, L = d.wl.W, d.wl.L
+        self.replicas = list(range(W)) if replicas is None else list(replicas)
+        self.x = {p: d.x.clone() for p in self.replicas}
+        self.m = {p: d.m.clone() for p in self.replicas}
+        self.vf = {p: d.vf.clone() for p in self.replicas}
+        self.f_prev = {p: d.f_prev.clone() for p in self.replicas}
+        self.c_out = {p: torch.zeros(L, dtype=torch.float32, device="cuda") for p in self.replicas}
+        self.ws = {p: torch.empty_like(d.ws) for p in self.replicas}
+        self.e = [t.clone() for t in d.e]
+        self.err_s = d.err_s.clone()
+        self.bits_w = [torch.zeros_like(d.bits_s) for _ in range(W)]
+        self.scales_w = [torch.zeros_like(d.scales_s) for _ in range(W)]
+        self.bits_s, self.scales_s = d.bits_s.clone(), d.scales_s.clone()
+        self.bits_prev, self.scales_prev = d.bits_s.clone(), d.scales_s.clone()
+
+    def step(self, packed=False):
+        d, wl = self.d, self.d.wl
+        W, C, N, K = wl.W, wl.chunk, wl.N, wl.K
+        p0 = self.replicas[0]
+        # 1. every GPU compresses its own worker's momentum (the replicas'
+        #    momentum is the same on every GPU)
+        for p in range(W):
+            ob.onebit_worker_compress(N, C, d.g[p], self.e[p], None if packed else self.m[p0],
+                                      self.bits_s if packed else None,
+                                      self.scales_s if packed else None, self.bits_w[p],
+                                      self.scales_w[p], d.hp, d.status)
+        self.bits_prev.copy_(self.bits_s)          # the previous momentum, packed
+        self.scales_prev.copy_(self.scales_s)
+        # 2-3. all-to-all, then GPU p averages and recompresses its chunks
+        for k0, k1 in chunk_ranges(K, W):
+            if k1 == k0:
+                continue
+            lo, hi, w0, w1 = k0 * C, min(k1 * C, N), k0 * C // 32, k1 * C // 32
+            ob.onebit_average_packed(hi - lo, C, W, [b[w0:w1] for b in self.bits_w],
+                                     [s[k0:k1] for s in self.scales_w], self.err_s[lo:hi],
+                                     self.bits_s[w0:w1], self.scales_s[k0:k1], d.status)
+        # 4-5. all-gather, then every GPU updates its replica
+        for p in self.replicas:
+            ob.onebit_lamb_rescale_stats(d.table, self.bits_s, self.scales_s,
+                                         None if packed else self.m[p],
+                                         self.bits_prev if packed else None,
+                                         self.scales_prev if packed else None, d.v, self.vf[p],
+                                         d.hp, self.ws[p])
+            ob.onebit_lamb_rescale_update(d.table, self.bits_s, self.scales_s, self.x[p],
+                                          None if packed else self.m[p], d.v, d.c_avg,
+                                          self.f_prev[p], self.c_out[p], d.hp, self.ws[p],
+                                          d.status)
+
+    def window(self, p):
+        """GPU p's replica as compare_state expects it (whole buffer)."""
+        h = lambda t: t.cpu().numpy()  # noqa: E731
+        return {"x": h(self.x[p]), "m": h(self.m[p]), "v": h(self.d.v), "vf": h(self.vf[p]),
+                "err_s": h(self.err_s), "e": [h(t) for t in self.e],
+                "bits_s": h(self.bits_s).view(np.uint32), "scales_s": h(self.scales_s),
+                "bits_w": [h(b).view(np.uint32) for b in self.bits_w],
+                "scales_w": [h(s) for s in self.scales_w], "c_sum": h(self.d.c_sum),
+                "c_avg": h(self.d.c_avg), "f_prev": h(self.f_prev[p]), "c": h(self.c_out[p])}
+
+
+def _same(a, b, what):
+    assert np.array_equal(np.asarray(a).view(np.uint32), np.asarray(b).view(np.uint32)), what
+
+
+def _assert_equals_fused(sh, f, packed):
+    got_f = f.window(0, f.wl.N)
+    for p in sh.replicas:
+        got = sh.window(p)
+        for k in ("x", "vf", "err_s", "bits_s", "scales_s", "f_prev", "c") + (() if packed else ("m",)):
+            _same(got[k], got_f[k], f"GPU {p}: {k}")
+        for w in range(f.wl.W):
+            _same(got["e"][w], got_f["e"][w], f"e{w}")
+            _same(got["bits_w"][w], got_f["bits_w"][w], f"bits_w{w}")
+            _same(got["scales_w"][w], got_f["scales_w"][w], f"scales_w{w}")
+
+
+RAGGED = [[1, 3, 4095, 4097, 100, 8192, 17], [4096 * 3], [10, 20, 30]]
+
+
+@pytest.mark.parametrize("numels", RAGGED)
+@pytest.mark.parametrize("W", [1, 3, 8])
+@pytest.mark.parametrize("rho_mode", [0, 1])
+def test_sharded_step_equals_fused(numels, W, rho_mode):
+    """Three steps (fp32 momentum, then packed momentum) from a frozen
+    state: every replica equals the fused step bit for bit."""
+    wl = Workload("sharded", numels, W=W, init="frozen")
+    f, s = DevRun(wl), DevRun(wl)
+    for r in (f, s):
+        r.hp.rho_mode = rho_mode
+    sh = Sharded(s)
+    for step in range(3):
+        packed = step > 0
+        f.fill_grads(step)
+        s.fill_grads(step)
+        f.compressed_step(step, fill=False, packed=packed)
+        sh.step(packed=packed)
+        torch.cuda.synchronize()
+        _assert_equals_fused(sh, f, packed)
+    assert int(s.status.item()) == 0
+
+
+def test_sharded_step_matches_oracle():
+    """The three-tensor table after a LAMB warmup: the per-GPU path against
+    the oracle (W = 2), three compression steps."""
+    wl = WORKLOADS["tiny"]
+    s, h = DevRun(wl), HostRun(wl)
+    for step in range(3):
+        s.warmup_step(step)
+        h.warmup_step(step)
+    s.freeze(3)
+    h.freeze(3)
+    sh = Sharded(s)
+    for step in range(3, 6):
+        s.fill_grads(step)
+        sh.step()
+        h.compressed_step(step)
+        torch.cuda.synchronize()
+        for p in sh.replicas:
+            rep = compare_state(None, h, d=sh.window(p))
+            assert_parity(rep, f"GPU {p}, step {step}")
+            assert rep["x"]["max_abs"] == 0.0
+
+
+def test_worker_compress_matches_compress_ef():
+    """The fused worker momentum and compression equals onebit_compress_ef of
+    beta1*m + a1*g (formed by the same two fp32 operations)."""
+    n, C = 3 * 4096 + 77, 4096
+    wl = Workload("worker", [n], W=1, init="frozen")
+    d = DevRun(wl)
+    d.fill_grads(0)
+    hp = d.hp
+    a1 = np.float32(1.0) - np.float32(hp.beta1)
+    inp = (np.float32(hp.beta1) * d.m.cpu().numpy()) + (a1 * d.g[0].cpu().numpy())
+    e0 = (np.random.default_rng(0).standard_normal(n) * 1e-4).astype(np.float32)
+    err_a, err_b = torch.from_numpy(e0).cuda(), torch.from_numpy(e0).cuda()
+    K = wl.K
+    ba, bb = (torch.zeros(K * C // 32, dtype=torch.int32, device="cuda") for _ in range(2))
+    sa, sb = (torch.zeros(K, device="cuda") for _ in range(2))
+    ob.onebit_worker_compress(n, C, d.g[0], err_a, d.m, None, None, ba, sa, hp)
+    ob.onebit_compress_ef(n, C, torch.from_numpy(inp).cuda(), err_b, bb, sb)
+    torch.cuda.synchronize()
+    for a, b, k in ((err_a, err_b, "err"), (ba, bb, "bits"), (sa, sb, "scales")):
+        assert torch.equal(a, b), k
+
+
+def test_share_argument_checks():
+    wl = Workload("worker", [4096], W=1, init="frozen")
+    d = DevRun(wl)
+    with pytest.raises(ob.OnebitError) as ei:
+        ob.onebit_worker_compress(4096, 4096, d.g[0], d.e[0], None, None, None, d.bits_s,
+                                  d.scales_s, d.hp)
+    assert ei.value.code == ob.ONEBIT_EINVAL
+    with pytest.raises(ob.OnebitError) as ei:
+        ob.onebit_worker_compress(4096, 3000, d.g[0], d.e[0], d.m, None, None, d.bits_s,
+                                  d.scales_s, d.hp)
+    assert ei.value.code == ob.ONEBIT_EUNSUPPORTED
+    with pytest.raises(ob.OnebitError) as ei:
+        ob.onebit_lamb_rescale_stats(d.table, d.bits_s, d.scales_s, None, None, d.scales_s, d.v,
+                                     d.vf, d.hp, d.ws)
+    assert ei.value.code == ob.ONEBIT_EINVAL
+    ob.onebit_worker_compress(0, 4096, None, None, None, None, None, None, None, d.hp)   # n = 0
+
+
+def test_sharded_bert_large_equals_fused():
+    """The BERT-Large table, W = 8: one fp32-momentum and one packed step;
+    the replicas of GPU 0 and GPU 7 equal the fused step bit for bit."""
+    wl = WORKLOADS["bert_large"]
+    f = DevRun(wl, store_worker_bits=True)
+    s = DevRun(wl, store_worker_bits=False)
+    sh = Sharded(s, replicas=[0, wl.W - 1])
+    for step in range(2):
+        f.fill_grads(step)
+        s.fill_grads(step)
+        f.compressed_step(step, fill=False, packed=step > 0)
+        sh.step(packed=step > 0)
+        torch.cuda.synchronize()
+        _assert_equals_fused(sh, f, step > 0)
+    assert int(s.status.item()) == 0
+    del f, s, sh
+    torch.cuda.empty_cache()
