@@ -139,9 +139,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="bert_large")
-    ap.add_argument("--method", choices=("lamb", "adam", "sparse"), default="lamb",
-                    help="1-bit LAMB (the default), the 1-bit Adam mode, or the SLAMB-style "
-                         "sparse stage, on the same buffers")
+    ap.add_argument("--method", choices=("lamb", "adam", "sparse", "share"), default="lamb",
+                    help="1-bit LAMB (the default), the 1-bit Adam mode, the SLAMB-style "
+                         "sparse stage, or one GPU's share of a W-GPU 1-bit LAMB step, on the "
+                         "same buffers")
     ap.add_argument("--nsel", type=int, default=1,
                     help="sparse stage: transmitted 64-element blocks per chunk")
     ap.add_argument("--cpu-chunks", type=int, default=40960,
@@ -218,6 +219,9 @@ def main():
     if args.method == "sparse":
         return bench_sparse(args, wl, ob, torch, table, hp, g, e, x, m, v, vf, c_avg, status,
                             stream)
+    if args.method == "share":
+        return bench_share(args, wl, ob, torch, table, hp, g, e, err_s, x, m, v, vf, bits_w,
+                           scales_w, bits_s, scales_s, c_avg, f_prev, c_out, ws, status, stream)
 
     def step(ev=None, mm=m):
         if ev is not None:
@@ -416,6 +420,112 @@ def bench_adam(args, wl, ob, torch, hp, g, e, err_s, x, m, v, bits_w, scales_w, 
                      "algorithmic_bytes": abytes},
         "runtime_copy": _ceiling(torch, stream, achieved),
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def share_bytes(N, K, C, W):
+    """Algorithmic bytes of one GPU's share of a W-GPU step, per kernel:
+    worker compression (g read, e read and written, m read, signs and
+    scales written), serving 1/W of the chunks (W workers' signs and scales
+    read, server error read and written, signs and scales written),
+    receiver statistics (signs and scales, m and v_frozen read, v_fresh read
+    and written) and the update (signs and scales, v_frozen read, x read and
+    written, m written)."""
+    pk = K * (C // 8 + 4)
+    ks = -(-K // W)
+    n_s = min(ks * C, N)
+    pk_s = ks * (C // 8 + 4)
+    return {"worker": 16 * N + pk, "server": (W + 1) * pk_s + 8 * n_s,
+            "stats": 16 * N + pk, "update": 16 * N + pk}
+
+
+def bench_share(args, wl, ob, torch, table, hp, g, e, err_s, x, m, v, vf, bits_w, scales_w,
+                bits_s, scales_s, c_avg, f_prev, c_out, ws, status, stream):
+    """One GPU's share of a W-GPU 1-bit LAMB compression step at its real
+    shape, the exchange left out: this GPU's worker compresses its momentum
+    over the whole buffer, serves the first 1/W of the chunks (the other
+    workers' packed chunks, as the all-to-all would deliver them, are the
+    simulated workers' arrays), then forms the rescale statistics and
+    updates its replica."""
+    C, N, W, K = wl.chunk, wl.N, wl.W, wl.K
+    ks = -(-K // W)                       # chunks this GPU serves: [0, ks)
+    n_s = min(ks * C, N)
+    wq = ks * C // 32
+    # the other workers' packed chunks for this range, filled once
+    for w in range(1, W):
+        ob.onebit_worker_compress(N, C, g[w], e[w], m, None, None, bits_w[w], scales_w[w], hp,
+                                  status, stream)
+    names = ("worker", "server", "stats", "update")
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record(stream)
+        mark(0)
+        ob.onebit_worker_compress(N, C, g[0], e[0], m, None, None, bits_w[0], scales_w[0], hp,
+                                  status, stream)
+        mark(1)
+        ob.onebit_average_packed(n_s, C, W, [b[:wq] for b in bits_w], [s[:ks] for s in scales_w],
+                                 err_s[:n_s], bits_s[:wq], scales_s[:ks], status, stream)
+        mark(2)
+        ob.onebit_lamb_rescale_stats(table, bits_s, scales_s, m, None, None, v, vf, hp, ws, stream)
+        mark(3)
+        ob.onebit_lamb_rescale_update(table, bits_s, scales_s, x, m, v, c_avg, f_prev, c_out, hp,
+                                      ws, status, stream)
+        mark(4)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    if int(status.item()):
+        log(f"[bench] WARNING: status flags {int(status.item())}")
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    k_ms = {nm: sum(ev[j].elapsed_time(ev[j + 1]) for ev in evs) / args.steps
+            for j, nm in enumerate(names)}
+    log(f"[bench] share {args.steps} steps: {ms_per_step:.3f} ms/step (" +
+        ", ".join(f"{nm} {k_ms[nm]:.3f}" for nm in names) + " ms)")
+    by = share_bytes(N, K, C, W)
+    sbytes = sum(by.values())
+    achieved = by["worker"] / (k_ms["worker"] * 1e-3) / 1e9
+    step_gbps = sbytes / (ms_per_step * 1e-3) / 1e9
+    traffic = _measured_traffic("traffic_worker_compress_bert_large.txt") \
+        if wl.name == "bert_large" else None
+    out = {
+        "metric": "params/sec and achieved HBM GB/s (% of peak) per GPU for one GPU's share of a "
+                  "W-GPU 1-bit LAMB step (the exchange left out)",
+        "value": N / (ms_per_step * 1e-3),
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: one GPU's share of a {W}-GPU 1-bit LAMB compression "
+                               f"step (its worker, 1/{W} of the chunks as server, its replica's "
+                               f"update), N={N}, chunk {C}",
+                   "N": N, "W": W, "chunk": C},
+        "achieved_GBps": step_gbps,
+        "frac_of_peak": step_gbps / PEAK_HBM_GBPS,
+        "step_bytes": sbytes,
+        "kernel_ms": k_ms,
+        "kernel_bytes": by,
+        "roofline": {"bound": "hbm", "kernel": "k_worker_compress<4096>",
+                     "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
+                     "algorithmic_bytes": by["worker"]},
+        "runtime_copy": _ceiling(torch, stream, achieved),
+        "cpu_baseline": None,
     }
     print(json.dumps(out), flush=True)
 
