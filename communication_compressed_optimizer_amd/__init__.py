@@ -27,7 +27,7 @@ __all__ = [
     "onebit_lamb_compressed_step", "onebit_lamb_compress_average", "onebit_lamb_rescale_update",
     "onebit_decompress", "onebit_last_error", "onebit_version", "onebit_adam_warmup_step",
     "onebit_adam_compressed_step", "onebit_sparse_compressed_step", "onebit_worker_compress",
-    "onebit_lamb_rescale_stats", "ONEBIT_RHO_MAX",
+    "onebit_lamb_rescale_stats", "onebit_adam_update", "ONEBIT_RHO_MAX",
     "ONEBIT_RHO_NORM_RATIO",
     "LIB_PATH",
 ]
@@ -90,6 +90,8 @@ _lib.onebit_worker_compress.argtypes = [_i64, _i32, _P, _P, _P, _P, _P, _P, _P,
                                         ctypes.POINTER(onebit_hparams), _P, _P]
 _lib.onebit_lamb_rescale_stats.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P,
                                            ctypes.POINTER(onebit_hparams), _P, _P]
+_lib.onebit_adam_update.argtypes = [_i64, _i32, _P, _P, _P, _P, _P, ctypes.POINTER(onebit_hparams),
+                                    _P]
 _lib.onebit_last_error.restype = ctypes.c_char_p
 _lib.onebit_version.restype = ctypes.c_char_p
 for _f in ("onebit_layer_table_create", "onebit_layer_table_destroy", "onebit_layer_table_info",
@@ -410,3 +412,12 @@ def onebit_lamb_rescale_stats(table, bits_s, scales_s, m, bits_m, scales_m, v_fr
         _ptr(bits_m, fn, "bits_m", z.words, _WORDS), _ptr(scales_m, fn, "scales_m", z.scales, _F32),
         e(v_frozen, "v_frozen"), e(v_fresh, "v_fresh"), ctypes.byref(hp), _ptr(ws, fn, "ws", z.ws),
         _stream(stream)), fn)
+
+
+def onebit_adam_update(n, chunk, bits_s, scales_s, x, m, v_frozen, hp, stream=None):
+    fn, z = "onebit_adam_update", _Sizes(n, chunk)
+    e = lambda a, nm: _ptr(a, fn, nm, z.elems, _F32)  # noqa: E731
+    _check(_lib.onebit_adam_update(
+        n, chunk, _ptr(bits_s, fn, "bits_s", z.words, _WORDS),
+        _ptr(scales_s, fn, "scales_s", z.scales, _F32), e(x, "x"), e(m, "m"), e(v_frozen, "v_frozen"),
+        ctypes.byref(hp), _stream(stream)), fn)

@@ -362,6 +362,14 @@ struct LaunchStats {
 };
 
 template <int C>
+struct LaunchAdamUpdate {
+  static void run(int64_t n, const uint32_t* bits_s, const float* scales_s, const float* v_frozen,
+                  float* x, float* m, const Coef& cf, hipStream_t st) {
+    launch_chunks<C>(n, st, k_adam_update<C, kShare_NT>, n, bits_s, scales_s, v_frozen, x, m, cf);
+  }
+};
+
+template <int C>
 struct LaunchPassB {
   static void run(const onebit_layer_table* t, const uint32_t* bits_s, const float* scales_s,
                   float* x, float* m, const float* v_frozen, const float* c_avg, float* f_prev,
@@ -771,6 +779,25 @@ int onebit_lamb_rescale_stats(const onebit_layer_table* table, const uint32_t* b
   by_chunk<LaunchStats>(table->chunk, table, bits_s, scales_s, m, bits_m, scales_m, v_frozen,
                         v_fresh, make_coef(*hp), hp->rho_mode == ONEBIT_RHO_NORM_RATIO,
                         ws_view(table, ws), (hipStream_t)stream);
+  return launch_status(__func__);
+}
+
+int onebit_adam_update(int64_t n, int32_t chunk, const uint32_t* bits_s, const float* scales_s,
+                       float* x, float* m, const float* v_frozen, const onebit_hparams* hp,
+                       void* stream) {
+  if (n < 0) return fail(ONEBIT_EINVAL, "%s: n < 0", __func__);
+  if (!chunk_supported(chunk)) return fail(ONEBIT_EUNSUPPORTED, "%s: chunk %d", __func__, chunk);
+  if (int rc = check_hparams(hp, __func__, false)) return rc;
+  if ((n + chunk - 1) / chunk > INT32_MAX / 2)
+    return fail(ONEBIT_EUNSUPPORTED, "%s: n too large", __func__);
+  if (n == 0) return ok();
+  CHECK_WORDS(bits_s, "bits_s");
+  CHECK_WORDS(scales_s, "scales_s");
+  CHECK_PTR(x, "x");
+  CHECK_OPT_PTR(m, "m");
+  CHECK_PTR(v_frozen, "v_frozen");
+  by_chunk<LaunchAdamUpdate>(chunk, n, bits_s, scales_s, v_frozen, x, m, make_coef(*hp),
+                             (hipStream_t)stream);
   return launch_status(__func__);
 }
 

@@ -1000,6 +1000,47 @@ k_rescale_stats(int64_t n_full, DevTable tab, const uint32_t* __restrict__ bits_
                                               seg_max, seg_z, seg_f, cf, red, dred);
 }
 
+// 1-bit Adam on a receiver: x = x - lr*(mhat/(sqrt(v_frozen)+eta)) and
+// m = mhat (m NULL: packed momentum), mhat from the server's packed output
+// (the update half of k_adam_compressed).
+template <int C, bool TAIL, bool NT>
+__device__ __forceinline__ void adam_update_chunk(int64_t k, int64_t n,
+                                                  const uint32_t* __restrict__ bits_s,
+                                                  const float* __restrict__ scales_s,
+                                                  const float* __restrict__ v_frozen,
+                                                  float* __restrict__ x, float* __restrict__ m,
+                                                  const Coef& cf) {
+  const ChunkAt<C, TAIL> ch(k, n);
+  uint32_t nib[4];
+  load_sign_nibbles<C>(bits_s + ch.k * Geo<C>::WORDS, nib);
+  const float s2 = scales_s[ch.k];
+  Slots xx, vz, mh;
+  load_chunk<C, TAIL, NT>(x, ch.base, ch.nk, xx);
+  load_chunk<C, TAIL, NT>(v_frozen, ch.base, ch.nk, vz);
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      mh[a][c] = signed_scale(nib, a, c, s2);
+      xx[a][c] = xx[a][c] - (cf.lr * (mh[a][c] / (__builtin_sqrtf(vz[a][c]) + cf.eta)));
+    }
+  store_chunk<C, TAIL, NT>(x, ch.base, ch.nk, xx);
+  if (m) store_chunk<C, TAIL, NT>(m, ch.base, ch.nk, mh);
+}
+
+template <int C, bool NT = true>
+__global__ void __launch_bounds__(C / 16)
+k_adam_update(int64_t n_full, int64_t n, const uint32_t* __restrict__ bits_s,
+              const float* __restrict__ scales_s, const float* __restrict__ v_frozen,
+              float* __restrict__ x, float* __restrict__ m, Coef cf) {
+  const int64_t has_tail = partial_chunks<C>(n_full, n);
+  if (has_tail && blockIdx.x == 0)
+    adam_update_chunk<C, true, NT>(n_full, n, bits_s, scales_s, v_frozen, x, m, cf);
+  else
+    adam_update_chunk<C, false, NT>((int64_t)blockIdx.x - has_tail, n, bits_s, scales_s, v_frozen,
+                                    x, m, cf);
+}
+
 // 1-bit Adam warmup: one Adam step, element-wise in one pass (mean gradient,
 // moments, x = x - lr*(m/(sqrt(v)+eta))).
 template <int C, bool TAIL>

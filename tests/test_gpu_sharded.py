@@ -158,6 +158,53 @@ def test_sharded_step_matches_oracle():
             assert rep["x"]["max_abs"] == 0.0
 
 
+@pytest.mark.parametrize("n", [3 * 4096 + 777, 5 * 4096, 1000])
+@pytest.mark.parametrize("W", [1, 3, 8])
+def test_sharded_adam_equals_fused(n, W):
+    """1-bit Adam: each GPU's worker compression, its chunk range as server,
+    then onebit_adam_update of its replica, for three steps (fp32, then
+    packed momentum), equal the fused onebit_adam_compressed_step bit for
+    bit."""
+    wl = Workload("sharded_adam", [n], W=W, init="frozen")
+    f, s = DevRun(wl), DevRun(wl)
+    C, K = wl.chunk, wl.K
+    x = [s.x.clone() for _ in range(2)]                     # two replicas
+    m = [s.m.clone() for _ in range(2)]
+    e = [t.clone() for t in s.e]
+    err_s = s.err_s.clone()
+    bits_w = [torch.zeros_like(s.bits_s) for _ in range(W)]
+    scales_w = [torch.zeros_like(s.scales_s) for _ in range(W)]
+    bits_s, scales_s = s.bits_s.clone(), s.scales_s.clone()
+    for step in range(3):
+        packed = step > 0
+        f.fill_grads(step)
+        s.fill_grads(step)
+        f.adam_compressed_step(step, fill=False, packed=packed)
+        for p_ in range(W):
+            ob.onebit_worker_compress(n, C, s.g[p_], e[p_], None if packed else m[0],
+                                      bits_s if packed else None, scales_s if packed else None,
+                                      bits_w[p_], scales_w[p_], s.hp, s.status)
+        for k0, k1 in chunk_ranges(K, W):
+            if k1 > k0:
+                lo, hi, w0, w1 = k0 * C, min(k1 * C, n), k0 * C // 32, k1 * C // 32
+                ob.onebit_average_packed(hi - lo, C, W, [b[w0:w1] for b in bits_w],
+                                         [t[k0:k1] for t in scales_w], err_s[lo:hi],
+                                         bits_s[w0:w1], scales_s[k0:k1], s.status)
+        for r in range(2):
+            ob.onebit_adam_update(n, C, bits_s, scales_s, x[r], None if packed else m[r], s.v,
+                                  s.hp)
+        torch.cuda.synchronize()
+        for r in range(2):
+            assert torch.equal(x[r], f.x), f"x, replica {r}, step {step}"
+            if not packed:
+                assert torch.equal(m[r], f.m), f"m, replica {r}, step {step}"
+        assert torch.equal(err_s, f.err_s) and torch.equal(bits_s, f.bits_s)
+        assert torch.equal(scales_s, f.scales_s)
+        for w in range(W):
+            assert torch.equal(e[w], f.e[w]) and torch.equal(bits_w[w], f.bits_w[w])
+    assert int(s.status.item()) == 0
+
+
 def test_worker_compress_matches_compress_ef():
     """The fused worker momentum and compression equals onebit_compress_ef of
     beta1*m + a1*g (formed by the same two fp32 operations)."""
