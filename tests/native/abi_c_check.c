@@ -4,10 +4,14 @@
  * table, runs two 1-bit LAMB compression-stage steps and one 1-bit Adam
  * compression step on the GPU through the C entry points, runs the CPU
  * oracle on the same seeded inputs, and compares every output bit for bit
- * (this stage has no order-dependent sum, so x and c are exact too).  It
- * also checks a few argument errors.  Test infrastructure: it links the
- * library, the oracle and the host input generator; prints PASS and
- * returns 0, or names the first mismatch and returns 1.
+ * (this stage has no order-dependent sum, so x and c are exact too).  Then
+ * it runs one more LAMB step as W simulated GPUs would, through the per-GPU
+ * entry points (each worker's compression, each GPU's chunk range as server,
+ * one replica's statistics and update), and checks it against the fused
+ * step on a copy of the state.  It also checks a few argument errors.
+ * Test infrastructure: it links the library, the oracle and the host input
+ * generator; prints PASS and returns 0, or names the first mismatch and
+ * returns 1.
  */
 #include <hip/hip_runtime_api.h>
 #include <stdint.h>
@@ -63,7 +67,7 @@ static void* down(const void* d, size_t bytes) {
   return h;
 }
 
-/* Bitwise comparison of a device array with the host oracle's. */
+/* Bitwise comparison of a device array with the expected host copy. */
 static void same(const char* name, const void* d, const void* h, size_t bytes) {
   void* g = down(d, bytes);
   if (memcmp(g, h, bytes) != 0) {
@@ -71,7 +75,8 @@ static void same(const char* name, const void* d, const void* h, size_t bytes) {
     const uint32_t* b = (const uint32_t*)h;
     size_t i = 0;
     while (i < bytes / 4 && a[i] == b[i]) ++i;
-    printf("abi_c_check: %s differs at word %zu (gpu 0x%08x, oracle 0x%08x)\n", name, i, a[i], b[i]);
+    printf("abi_c_check: %s differs at word %zu (got 0x%08x, expected 0x%08x)\n", name, i, a[i],
+           b[i]);
     ++failures;
   }
   free(g);
@@ -171,6 +176,68 @@ int main(void) {
   same("adam x", dx, x, fb); same("adam m", dm, m, fb); same("adam err_s", des, es, fb);
   same("adam bits_s", dbs, bs, wb); same("adam scales_s", dss, ss, sb);
 
+  /* one GPU's share, W simulated GPUs: the same step through the per-GPU
+   * entry points on copies of the state, against the fused step */
+  {
+    float *sx = dev_alloc(fb), *sm = dev_alloc(fb), *svf = dev_alloc(fb), *ses = dev_alloc(fb),
+          *sfp = dev_alloc(lb), *sco = dev_alloc(lb), *se[W], *ssw[W], *sss = dev_alloc(sb);
+    uint32_t *sbw[W], *sbs = dev_alloc(wb);
+    void* sws = dev_alloc(wsb);
+    hip_ok(hipMemcpy(sx, dx, fb, hipMemcpyDeviceToDevice), "copy");
+    hip_ok(hipMemcpy(sm, dm, fb, hipMemcpyDeviceToDevice), "copy");
+    hip_ok(hipMemcpy(svf, dvf, fb, hipMemcpyDeviceToDevice), "copy");
+    hip_ok(hipMemcpy(ses, des, fb, hipMemcpyDeviceToDevice), "copy");
+    hip_ok(hipMemcpy(sfp, dfprev, lb, hipMemcpyDeviceToDevice), "copy");
+    for (int w = 0; w < W; ++w) {
+      se[w] = dev_alloc(fb); sbw[w] = dev_alloc(wb); ssw[w] = dev_alloc(sb);
+      hip_ok(hipMemcpy(se[w], de[w], fb, hipMemcpyDeviceToDevice), "copy");
+      synth_fill_normal(0, stream_id(4, 9, (uint64_t)w), 0, N, 0.0, 1e-3, g[w]);
+      up(dg[w], g[w], fb);
+    }
+    /* the fused step on the original state */
+    rc_ok(onebit_lamb_compressed_step(table, W, (const float* const*)dg, de, des, dx, dm, dvz, dvf,
+                                      dcavg, dfprev, dcout, dbw, dsw, dbs, dss, &hp, dws, dstatus,
+                                      NULL),
+          "onebit_lamb_compressed_step (fused)");
+    /* 1. every GPU compresses its own worker's momentum */
+    for (int w = 0; w < W; ++w)
+      rc_ok(onebit_worker_compress(N, C, dg[w], se[w], sm, NULL, NULL, sbw[w], ssw[w], &hp, dstatus,
+                                   NULL),
+            "onebit_worker_compress");
+    /* 3. GPU p serves chunks [K*p/W, K*(p+1)/W) */
+    for (int p = 0; p < W; ++p) {
+      const int64_t k0 = K * p / W, k1 = K * (p + 1) / W;
+      if (k1 == k0) continue;
+      const int64_t lo = k0 * C, hi = k1 * C < N ? k1 * C : N;
+      const uint32_t* rb[W];
+      const float* rs[W];
+      for (int w = 0; w < W; ++w) { rb[w] = sbw[w] + k0 * C / 32; rs[w] = ssw[w] + k0; }
+      rc_ok(onebit_average_packed(hi - lo, C, W, rb, rs, ses + lo, sbs + k0 * C / 32, sss + k0,
+                                  dstatus, NULL),
+            "onebit_average_packed (range)");
+    }
+    /* 5. one replica: statistics, then the update */
+    rc_ok(onebit_lamb_rescale_stats(table, sbs, sss, sm, NULL, NULL, dvz, svf, &hp, sws, NULL),
+          "onebit_lamb_rescale_stats");
+    rc_ok(onebit_lamb_rescale_update(table, sbs, sss, sx, sm, dvz, dcavg, sfp, sco, &hp, sws,
+                                     dstatus, NULL),
+          "onebit_lamb_rescale_update");
+    hip_ok(hipDeviceSynchronize(), "hipDeviceSynchronize");
+    void* h;
+#define SAME_DEV(name, a, b, bytes)                     \
+    h = down(b, bytes);                                 \
+    same(name, a, h, bytes);                            \
+    free(h)
+    SAME_DEV("share x", sx, dx, fb); SAME_DEV("share m", sm, dm, fb);
+    SAME_DEV("share v_fresh", svf, dvf, fb); SAME_DEV("share err_s", ses, des, fb);
+    SAME_DEV("share bits_s", sbs, dbs, wb); SAME_DEV("share scales_s", sss, dss, sb);
+    SAME_DEV("share f_prev", sfp, dfprev, lb); SAME_DEV("share c", sco, dcout, lb);
+    for (int w = 0; w < W; ++w) {
+      SAME_DEV("share err_w", se[w], de[w], fb); SAME_DEV("share bits_w", sbw[w], dbw[w], wb);
+    }
+#undef SAME_DEV
+  }
+
   int32_t status = -1;
   hip_ok(hipMemcpy(&status, dstatus, 4, hipMemcpyDeviceToHost), "status");
   if (status != 0) { printf("abi_c_check: status %d\n", status); ++failures; }
@@ -189,7 +256,8 @@ int main(void) {
   if (onebit_last_error()[0] == '\0') { printf("abi_c_check: empty error message\n"); ++failures; }
 
   rc_ok(onebit_layer_table_destroy(table), "onebit_layer_table_destroy");
-  printf("abi_c_check: %s (N = %lld, K = %lld, W = %d, %d LAMB steps and one Adam step)\n",
+  printf("abi_c_check: %s (N = %lld, K = %lld, W = %d, %d LAMB steps, one Adam step, one "
+         "LAMB step through the per-GPU entry points)\n",
          failures ? "FAIL" : "PASS", (long long)N, (long long)K, W, STEPS);
   return failures ? 1 : 0;
 }
