@@ -189,3 +189,70 @@ def test_sparse_entry_point_stays_in_bounds(numels, nsel):
             assert no_poison(t)
             poisoned(t).fill_(POISON)
     A.check()
+
+
+@pytest.mark.parametrize("numels", TABLES)
+@pytest.mark.parametrize("W", [1, 3])
+def test_share_entry_points_stay_in_bounds(numels, W):
+    """The per-GPU entry points (worker compression, a chunk range served,
+    receiver statistics and update, the Adam receiver update) touch only
+    their arguments, and write their packed outputs in full."""
+    chunk = 4096
+    table = ob.LayerTable(numels, chunk)
+    N, K, L = table.N, table.K, len(numels)
+    words = K * chunk // 32
+    A = Arena()
+    x, m, v, vf = A.take(N), A.take(N), A.take(N), A.take(N)
+    g, e = A.take(N), A.take(N, fill=0)
+    for i, t in enumerate([x, m, g]):
+        fill_normal(t, 30 + i, 0.02)
+    v.copy_(torch.rand(N, device="cuda") * 1e-4)
+    vf.copy_(v)
+    bits_w = [A.take(words, torch.int32, POISON) for _ in range(W)]
+    scales_w = [A.take(K, torch.float32, POISON) for _ in range(W)]
+    err_s = A.take(N, fill=0)
+    bits_s = A.take(words, torch.int32, POISON)
+    scales_s = A.take(K, torch.float32, POISON)
+    c_avg, f_prev = A.take(L), A.take(L)
+    c_avg.fill_(1.0)
+    f_prev.fill_(1.0)
+    c_out = A.take(L, torch.float32, POISON)
+    ws = A.take((table.workspace_size(W) + 3) // 4, torch.int32).view(torch.uint8)
+    status = A.take(1, torch.int32, 0)
+    hp = ob.onebit_hparams(**HPARAMS)
+    for w in range(W):
+        ob.onebit_worker_compress(N, chunk, g, e, m, None, None, bits_w[w], scales_w[w], hp, status)
+    torch.cuda.synchronize()
+    for t in bits_w + scales_w:
+        assert no_poison(t)
+    for p in range(W):                                  # each GPU's chunk range
+        k0, k1 = K * p // W, K * (p + 1) // W
+        if k1 == k0:
+            continue
+        lo, hi, w0, w1 = k0 * chunk, min(k1 * chunk, N), k0 * chunk // 32, k1 * chunk // 32
+        ob.onebit_average_packed(hi - lo, chunk, W, [b[w0:w1] for b in bits_w],
+                                 [s[k0:k1] for s in scales_w], err_s[lo:hi], bits_s[w0:w1],
+                                 scales_s[k0:k1], status)
+    torch.cuda.synchronize()
+    assert no_poison(bits_s) and no_poison(scales_s)
+    ob.onebit_lamb_rescale_stats(table, bits_s, scales_s, m, None, None, v, vf, hp, ws)
+    ob.onebit_lamb_rescale_update(table, bits_s, scales_s, x, m, v, c_avg, f_prev, c_out, hp, ws,
+                                  status)
+    torch.cuda.synchronize()
+    assert no_poison(c_out)
+    # packed momentum: the previous server output stands in for m
+    bits_p, scales_p = A.take(words, torch.int32), A.take(K, torch.float32)
+    bits_p.copy_(bits_s)
+    scales_p.copy_(scales_s)
+    for w in range(W):
+        poisoned(bits_w[w]).fill_(POISON)
+        poisoned(scales_w[w]).fill_(POISON)
+        ob.onebit_worker_compress(N, chunk, g, e, None, bits_p, scales_p, bits_w[w], scales_w[w],
+                                  hp, status)
+    ob.onebit_lamb_rescale_stats(table, bits_s, scales_s, None, bits_p, scales_p, v, vf, hp, ws)
+    ob.onebit_adam_update(N, chunk, bits_s, scales_s, x, m, v, hp)
+    ob.onebit_adam_update(N, chunk, bits_s, scales_s, x, None, v, hp)
+    torch.cuda.synchronize()
+    for t in bits_w + scales_w:
+        assert no_poison(t)
+    A.check()

@@ -14,6 +14,7 @@ if not torch.cuda.is_available():  # pragma: no cover - CPU container
 from synth.workloads import Workload  # noqa: E402
 
 from tests.harness import DevRun  # noqa: E402
+from tests.test_gpu_sharded import Sharded  # noqa: E402
 
 TABLE = [4096 * 3 + 100, 1, 777, 2 * 4096, 5000, 3]
 STATE = ("x", "m", "v", "vf", "err_s", "bits_s", "scales_s", "c_sum", "c_avg", "f_prev", "c_out")
@@ -86,3 +87,27 @@ def test_adam_and_sparse_steps_replay_as_eager():
                                            c.c_avg, c.vals_w, c.vals_s, c.hp, c.status)
         gs.replay()
         _same(c, d, extra=("vals_s",))
+
+
+def test_share_steps_replay_as_eager():
+    """One GPU's share (worker compressions, the served chunk ranges, the
+    replicas' statistics and updates) captured once and replayed."""
+    wl = Workload("graph", TABLE, W=3, init="frozen")
+    a, b = DevRun(wl), DevRun(wl)
+    for r in (a, b):
+        r.fill_grads(0)
+    sa, sb = Sharded(a), Sharded(b)
+    g = _capture(lambda: sb.step())
+    for _ in range(3):
+        sa.step()
+        g.replay()
+        torch.cuda.synchronize()
+        for p in sa.replicas:
+            for k in ("x", "m", "vf", "f_prev", "c_out"):
+                assert torch.equal(getattr(sa, k)[p], getattr(sb, k)[p]), (p, k)
+        for k in ("err_s", "bits_s", "scales_s"):
+            assert torch.equal(getattr(sa, k), getattr(sb, k)), k
+        for w in range(wl.W):
+            assert torch.equal(sa.e[w], sb.e[w]) and torch.equal(sa.bits_w[w], sb.bits_w[w])
+        a.x.add_(0.0)                       # eager work between the replays
+

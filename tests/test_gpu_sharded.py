@@ -62,8 +62,9 @@ class Sharded:
                                       self.bits_s if packed else None,
                                       self.scales_s if packed else None, self.bits_w[p],
                                       self.scales_w[p], d.hp, d.status)
-        self.bits_prev.copy_(self.bits_s)          # the previous momentum, packed
-        self.scales_prev.copy_(self.scales_s)
+        if packed:                                 # the previous momentum, packed
+            self.bits_prev.copy_(self.bits_s)
+            self.scales_prev.copy_(self.scales_s)
         # 2-3. all-to-all, then GPU p averages and recompresses its chunks
         for k0, k1 in chunk_ranges(K, W):
             if k1 == k0:
