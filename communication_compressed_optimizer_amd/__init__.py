@@ -27,7 +27,8 @@ __all__ = [
     "onebit_lamb_compressed_step", "onebit_lamb_compress_average", "onebit_lamb_rescale_update",
     "onebit_decompress", "onebit_last_error", "onebit_version", "onebit_adam_warmup_step",
     "onebit_adam_compressed_step", "onebit_sparse_compressed_step", "onebit_worker_compress",
-    "onebit_lamb_rescale_stats", "onebit_adam_update", "ONEBIT_RHO_MAX",
+    "onebit_lamb_rescale_stats", "onebit_adam_update", "onebit_sparse_worker",
+    "onebit_sparse_average", "onebit_sparse_update", "ONEBIT_RHO_MAX",
     "ONEBIT_RHO_NORM_RATIO",
     "LIB_PATH",
 ]
@@ -92,6 +93,11 @@ _lib.onebit_lamb_rescale_stats.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P,
                                            ctypes.POINTER(onebit_hparams), _P, _P]
 _lib.onebit_adam_update.argtypes = [_i64, _i32, _P, _P, _P, _P, _P, ctypes.POINTER(onebit_hparams),
                                     _P]
+_lib.onebit_sparse_worker.argtypes = [_i64, _i32, _i32, _P, _P, _P, _P, _P,
+                                      ctypes.POINTER(onebit_hparams), _P]
+_lib.onebit_sparse_average.argtypes = [_i64, _i32, _P, _P, _P]
+_lib.onebit_sparse_update.argtypes = [_P, _i32, _P, _P, _P, _P, _P, _P, _P,
+                                      ctypes.POINTER(onebit_hparams), _P, _P]
 _lib.onebit_last_error.restype = ctypes.c_char_p
 _lib.onebit_version.restype = ctypes.c_char_p
 for _f in ("onebit_layer_table_create", "onebit_layer_table_destroy", "onebit_layer_table_info",
@@ -421,3 +427,33 @@ def onebit_adam_update(n, chunk, bits_s, scales_s, x, m, v_frozen, hp, stream=No
         n, chunk, _ptr(bits_s, fn, "bits_s", z.words, _WORDS),
         _ptr(scales_s, fn, "scales_s", z.scales, _F32), e(x, "x"), e(m, "m"), e(v_frozen, "v_frozen"),
         ctypes.byref(hp), _stream(stream)), fn)
+
+
+def onebit_sparse_worker(n, chunk, nsel, sel, grad, err_w, m, vals_w, hp, stream=None):
+    fn, z = "onebit_sparse_worker", _Sizes(n, chunk)
+    e = lambda a, nm: _ptr(a, fn, nm, z.elems, _F32)  # noqa: E731
+    ok = z.K is not None and isinstance(nsel, int) and 1 <= nsel <= chunk // 64
+    per = 4 * z.K * nsel * 64 if ok else None
+    _check(_lib.onebit_sparse_worker(
+        n, chunk, nsel, _ptr(sel, fn, "sel", z.scales, _WORDS), e(grad, "grad"), e(err_w, "err_w"),
+        e(m, "m"), _ptr(vals_w, fn, "vals_w", per, _F32), ctypes.byref(hp), _stream(stream)), fn)
+
+
+def onebit_sparse_average(count, W, vals_w, vals_s, stream=None):
+    fn = "onebit_sparse_average"
+    nb = 4 * count if isinstance(count, int) and count >= 0 else None
+    _check(_lib.onebit_sparse_average(count, W, _ptr_list(vals_w, fn, "vals_w", W, nb, _F32),
+                                      _ptr(vals_s, fn, "vals_s", nb, _F32), _stream(stream)), fn)
+
+
+def onebit_sparse_update(table, nsel, sel, vals_s, x, m, v_frozen, v_fresh, c_avg, hp, status=None,
+                         stream=None):
+    fn, z = "onebit_sparse_update", _table_sizes(table)
+    e = lambda a, nm: _ptr(a, fn, nm, z.elems, _F32)  # noqa: E731
+    ok = z.K is not None and isinstance(nsel, int) and 1 <= nsel <= table.chunk // 64
+    per = 4 * z.K * nsel * 64 if ok else None
+    _check(_lib.onebit_sparse_update(
+        _h(table), nsel, _ptr(sel, fn, "sel", z.scales, _WORDS), _ptr(vals_s, fn, "vals_s", per, _F32),
+        e(x, "x"), e(m, "m"), e(v_frozen, "v_frozen"), e(v_fresh, "v_fresh"),
+        _ptr(c_avg, fn, "c_avg", z.tensors, _F32), ctypes.byref(hp), _ptr(status, fn, "status", 4),
+        _stream(stream)), fn)

@@ -370,6 +370,24 @@ struct LaunchAdamUpdate {
 };
 
 template <int C>
+struct LaunchSparseWorker {
+  static void run(int64_t n, int nsel, const int32_t* sel, const float* g, float* e,
+                  const float* m, float* vals, const Coef& cf, hipStream_t st) {
+    launch_chunks<C>(n, st, k_sparse_worker<C, kShare_NT>, n, nsel, sel, g, e, m, vals, cf);
+  }
+};
+
+template <int C>
+struct LaunchSparseUpdate {
+  static void run(const onebit_layer_table* t, int nsel, const int32_t* sel, const float* vals_s,
+                  float* x, float* m, const float* v_frozen, float* v_fresh, const float* c_avg,
+                  const Coef& cf, int32_t* status, hipStream_t st) {
+    launch_chunks<C>(t->N, st, k_sparse_update<C, kShare_NT>, t->dev, nsel, sel, vals_s, x, m,
+                     v_frozen, v_fresh, c_avg, cf, status);
+  }
+};
+
+template <int C>
 struct LaunchPassB {
   static void run(const onebit_layer_table* t, const uint32_t* bits_s, const float* scales_s,
                   float* x, float* m, const float* v_frozen, const float* c_avg, float* f_prev,
@@ -798,6 +816,69 @@ int onebit_adam_update(int64_t n, int32_t chunk, const uint32_t* bits_s, const f
   CHECK_PTR(v_frozen, "v_frozen");
   by_chunk<LaunchAdamUpdate>(chunk, n, bits_s, scales_s, v_frozen, x, m, make_coef(*hp),
                              (hipStream_t)stream);
+  return launch_status(__func__);
+}
+
+int onebit_sparse_worker(int64_t n, int32_t chunk, int32_t nsel, const int32_t* sel,
+                         const float* grad, float* err_w, const float* m, float* vals_w,
+                         const onebit_hparams* hp, void* stream) {
+  if (n < 0) return fail(ONEBIT_EINVAL, "%s: n < 0", __func__);
+  if (!chunk_supported(chunk)) return fail(ONEBIT_EUNSUPPORTED, "%s: chunk %d", __func__, chunk);
+  if (int rc = check_hparams(hp, __func__, false)) return rc;
+  if (nsel < 1 || nsel > chunk / 64)
+    return fail(ONEBIT_EINVAL, "%s: nsel = %d outside [1, chunk/64 = %d]", __func__, nsel,
+                chunk / 64);
+  if ((n + chunk - 1) / chunk > INT32_MAX / 2)
+    return fail(ONEBIT_EUNSUPPORTED, "%s: n too large", __func__);
+  if (n == 0) return ok();
+  CHECK_WORDS(sel, "sel");
+  CHECK_PTR(grad, "grad");
+  CHECK_PTR(err_w, "err_w");
+  CHECK_PTR(m, "m");
+  CHECK_PTR(vals_w, "vals_w");
+  by_chunk<LaunchSparseWorker>(chunk, n, (int)nsel, sel, grad, err_w, m, vals_w, make_coef(*hp),
+                               (hipStream_t)stream);
+  return launch_status(__func__);
+}
+
+int onebit_sparse_average(int64_t count, int32_t W, const float* const* vals_w, float* vals_s,
+                          void* stream) {
+  if (count < 0 || count % 4) return fail(ONEBIT_EINVAL, "%s: count %lld is not a multiple of 4 >= 0",
+                                          __func__, (long long)count);
+  if (int rc = check_W(W, __func__)) return rc;
+  if (count == 0) return ok();
+  if (!vals_w) return fail(ONEBIT_EINVAL, "%s: vals_w is NULL", __func__);
+  WorkerVals wv{};
+  for (int w = 0; w < W; ++w) {
+    CHECK_PTR(vals_w[w], "vals_w[w]");
+    wv.v[w] = const_cast<float*>(vals_w[w]);
+  }
+  CHECK_PTR(vals_s, "vals_s");
+  const int64_t count4 = count / 4;
+  const int64_t blocks = (count4 + 255) / 256 < 65536 ? (count4 + 255) / 256 : 65536;
+  hipLaunchKernelGGL(k_mean_values<kShare_NT>, dim3((unsigned)blocks), dim3(256), 0,
+                     (hipStream_t)stream, count4, (int)W, wv, vals_s);
+  return launch_status(__func__);
+}
+
+int onebit_sparse_update(const onebit_layer_table* table, int32_t nsel, const int32_t* sel,
+                         const float* vals_s, float* x, float* m, const float* v_frozen,
+                         float* v_fresh, const float* c_avg, const onebit_hparams* hp,
+                         int32_t* status, void* stream) {
+  if (int rc = check_table(table, __func__)) return rc;
+  if (int rc = check_hparams(hp, __func__, false)) return rc;
+  if (nsel < 1 || nsel > table->chunk / 64)
+    return fail(ONEBIT_EINVAL, "%s: nsel = %d outside [1, chunk/64 = %d]", __func__, nsel,
+                table->chunk / 64);
+  CHECK_WORDS(sel, "sel");
+  CHECK_PTR(vals_s, "vals_s");
+  CHECK_PTR(x, "x");
+  CHECK_PTR(m, "m");
+  CHECK_PTR(v_frozen, "v_frozen");
+  CHECK_PTR(v_fresh, "v_fresh");
+  CHECK_PTR(c_avg, "c_avg");
+  by_chunk<LaunchSparseUpdate>(table->chunk, table, (int)nsel, sel, vals_s, x, m, v_frozen, v_fresh,
+                               c_avg, make_coef(*hp), status, (hipStream_t)stream);
   return launch_status(__func__);
 }
 

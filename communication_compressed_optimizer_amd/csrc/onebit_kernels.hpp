@@ -1223,6 +1223,190 @@ __device__ __forceinline__ void sparse_chunk(int64_t kk, const DevTable& tab, in
   store_chunk<C, TAIL, NT>(m, base, nk, acc);
 }
 
+// ---------------------------------------------------------------------------
+// One GPU's share of a W-GPU sparse step: its worker's transmitted values
+// and local error (k_sparse_worker), the mean of the W workers' values on the
+// chunks it serves (k_mean_values), and, with every chunk's mean in hand,
+// the masked momentum, fresh variance and update of its replica
+// (k_sparse_update).  Same arithmetic as sparse_chunk, element for element.
+// ---------------------------------------------------------------------------
+
+// Transmitted position of thread t's slots within the chunk's values, or -1.
+template <int C>
+__device__ __forceinline__ void sparse_positions(int32_t sel_k, int nsel, int (&pos)[4]) {
+  constexpr int T = Geo<C>::T;
+  constexpr int NB = C / 64;
+  const int b0 = ((sel_k % NB) + NB) % NB;
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const int p = (int)threadIdx.x + T * a;
+    const int rel = ((p / 16) - b0 + NB) % NB;
+    pos[a] = rel < nsel ? rel * 64 + 4 * (p % 16) : -1;
+  }
+}
+
+template <int C, bool TAIL, bool NT>
+__device__ __forceinline__ void sparse_worker_chunk(int64_t k, int64_t n, int nsel,
+                                                    const int32_t* __restrict__ sel,
+                                                    const float* __restrict__ g,
+                                                    float* __restrict__ e,
+                                                    const float* __restrict__ m,
+                                                    float* __restrict__ vals, const Coef& cf) {
+  const ChunkAt<C, TAIL> ch(k, n);
+  const int64_t per = (int64_t)nsel * 64;
+  int pos[4];
+  sparse_positions<C>(sel[ch.k], nsel, pos);
+  Slots z, gg, ee;
+  load_chunk<C, TAIL, NT>(m, ch.base, ch.nk, z);
+  load_chunk<C, TAIL, NT>(g, ch.base, ch.nk, gg);
+  load_chunk<C, TAIL, NT>(e, ch.base, ch.nk, ee);
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      z[a][c] = ((cf.beta1 * z[a][c]) + (cf.a1 * gg[a][c])) + ee[a][c];
+      ee[a][c] = pos[a] >= 0 ? 0.0f : z[a][c];
+    }
+    if (pos[a] >= 0) {
+      float* q = vals + ch.k * per + pos[a];
+      if constexpr (TAIL) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) q[c] = slot_valid<C>(a, c, ch.nk) ? z[a][c] : 0.0f;
+      } else {
+        st4<NT>(q, f32x4{z[a][0], z[a][1], z[a][2], z[a][3]});
+      }
+    }
+  }
+  store_chunk<C, TAIL, NT>(e, ch.base, ch.nk, ee);
+}
+
+template <int C, bool NT = true>
+__global__ void __launch_bounds__(C / 16)
+k_sparse_worker(int64_t n_full, int64_t n, int nsel, const int32_t* __restrict__ sel,
+                const float* __restrict__ g, float* __restrict__ e, const float* __restrict__ m,
+                float* __restrict__ vals, Coef cf) {
+  const int64_t has_tail = partial_chunks<C>(n_full, n);
+  if (has_tail && blockIdx.x == 0)
+    sparse_worker_chunk<C, true, NT>(n_full, n, nsel, sel, g, e, m, vals, cf);
+  else
+    sparse_worker_chunk<C, false, NT>((int64_t)blockIdx.x - has_tail, n, nsel, sel, g, e, m, vals,
+                                      cf);
+}
+
+// out[i] = ((v_0[i] + v_1[i]) + ...) / W over count4 float4 groups.
+template <bool NT = true>
+__global__ void __launch_bounds__(256)
+k_mean_values(int64_t count4, int W, WorkerVals vals_w, float* __restrict__ out) {
+  const float fW = (float)W;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < count4;
+       i += (int64_t)gridDim.x * 256) {
+    f32x4 acc = ld4<NT>(vals_w.v[0] + 4 * i);
+    for (int w = 1; w < W; ++w) {
+      const f32x4 v = ld4<NT>(vals_w.v[w] + 4 * i);
+      acc.x = acc.x + v.x;
+      acc.y = acc.y + v.y;
+      acc.z = acc.z + v.z;
+      acc.w = acc.w + v.w;
+    }
+    st4<NT>(out + 4 * i, f32x4{acc.x / fW, acc.y / fW, acc.z / fW, acc.w / fW});
+  }
+}
+
+template <int C, bool TAIL, bool NT>
+__device__ __forceinline__ void sparse_update_chunk(int64_t kk, const DevTable& tab, int nsel,
+                                                    const int32_t* __restrict__ sel,
+                                                    const float* __restrict__ vals_s,
+                                                    float* __restrict__ x, float* __restrict__ m,
+                                                    const float* __restrict__ v_frozen,
+                                                    float* __restrict__ v_fresh,
+                                                    const float* __restrict__ c_avg,
+                                                    const Coef& cf, int32_t* status) {
+  constexpr int T = Geo<C>::T;
+  const ChunkAt<C, TAIL> ch(kk, tab.N);
+  const int64_t base = ch.base;
+  const int nk = ch.nk;
+  const int t = threadIdx.x;
+  const int64_t per = (int64_t)nsel * 64;
+  int pos[4];
+  sparse_positions<C>(sel[ch.k], nsel, pos);
+  Slots bm, mh;
+  load_chunk<C, TAIL, NT>(m, base, nk, bm);
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    if (pos[a] >= 0) {
+      const float* q = vals_s + ch.k * per + pos[a];
+      const f32x4 v = ld4<NT>(q);
+      mh[a][0] = v.x; mh[a][1] = v.y; mh[a][2] = v.z; mh[a][3] = v.w;
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) mh[a][c] = 0.0f;
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) bm[a][c] = cf.beta1 * bm[a][c];
+  }
+  const int l0 = tab.l0[ch.k];
+  const int l1 = tab.l1[ch.k];
+  const float st0 = cf.lr * c_avg[l0];
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    if (pos[a] < 0) continue;
+    const int64_t e0 = base + 4 * (t + T * a);
+    float xs[4], vz[4], vf[4];
+    if constexpr (TAIL) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const bool ok = slot_valid<C>(a, c, nk);
+        xs[c] = ok ? x[e0 + c] : 0.0f;
+        vz[c] = ok ? v_frozen[e0 + c] : 0.0f;
+        vf[c] = ok ? v_fresh[e0 + c] : 0.0f;
+      }
+    } else {
+      const f32x4 xv = ld4<NT>(x + e0), zv = ld4<NT>(v_frozen + e0), fv = ld4<NT>(v_fresh + e0);
+      xs[0] = xv.x; xs[1] = xv.y; xs[2] = xv.z; xs[3] = xv.w;
+      vz[0] = zv.x; vz[1] = zv.y; vz[2] = zv.z; vz[3] = zv.w;
+      vf[0] = fv.x; vf[1] = fv.y; vf[2] = fv.z; vf[3] = fv.w;
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float gh = (mh[a][c] - bm[a][c]) / cf.a1;
+      vf[c] = (cf.beta2 * vf[c]) + (cf.a2 * (gh * gh));
+      const float dz = __builtin_sqrtf(vz[c]) + cf.eta;
+      const float q = dz / (__builtin_sqrtf(vf[c]) + cf.eta);
+      const float r = fminf(fmaxf(q, cf.f_min), cf.f_max);
+      const float stp = l0 == l1 ? st0 : cf.lr * c_avg[tensor_of(tab, l0, l1, e0 + c)];
+      xs[c] = xs[c] - (stp * (r * (mh[a][c] / dz)));
+      if (!__builtin_isfinite(mh[a][c])) flag(status, 2);
+    }
+    if constexpr (TAIL) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (slot_valid<C>(a, c, nk)) {
+          x[e0 + c] = xs[c];
+          v_fresh[e0 + c] = vf[c];
+        }
+    } else {
+      st4<NT>(x + e0, f32x4{xs[0], xs[1], xs[2], xs[3]});
+      st4<NT>(v_fresh + e0, f32x4{vf[0], vf[1], vf[2], vf[3]});
+    }
+  }
+  store_chunk<C, TAIL, NT>(m, base, nk, mh);
+}
+
+template <int C, bool NT = true>
+__global__ void __launch_bounds__(C / 16)
+k_sparse_update(int64_t n_full, DevTable tab, int nsel, const int32_t* __restrict__ sel,
+                const float* __restrict__ vals_s, float* __restrict__ x, float* __restrict__ m,
+                const float* __restrict__ v_frozen, float* __restrict__ v_fresh,
+                const float* __restrict__ c_avg, Coef cf, int32_t* status) {
+  const int64_t has_tail = tab.K - n_full;
+  if (has_tail && blockIdx.x == 0)
+    sparse_update_chunk<C, true, NT>(n_full, tab, nsel, sel, vals_s, x, m, v_frozen, v_fresh,
+                                     c_avg, cf, status);
+  else
+    sparse_update_chunk<C, false, NT>((int64_t)blockIdx.x - has_tail, tab, nsel, sel, vals_s, x, m,
+                                      v_frozen, v_fresh, c_avg, cf, status);
+}
+
 // One workgroup per chunk; block 0 takes the partial last chunk, if any.
 template <int C, bool NT = true, int WPE = 1>
 __global__ void __launch_bounds__(C / 16, WPE)

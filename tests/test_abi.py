@@ -180,4 +180,16 @@ def test_share_entry_point_checks(ob):
     assert "scales_w is not 4-byte aligned" in ob.onebit_last_error()
     assert lib.onebit_lamb_rescale_stats(None, P(4096), P(4096), P(4096), None, None, P(4096),
                                          P(4096), hpr, P(4096), None) == ob.ONEBIT_EINVAL
+    # sparse stage
+    assert lib.onebit_sparse_worker(10, 4096, 0, P(4096), P(4096), P(4096), P(4096), P(4096), hpr,
+                                    None) == ob.ONEBIT_EINVAL                  # nsel = 0
+    assert lib.onebit_sparse_worker(10, 4096, 65, P(4096), P(4096), P(4096), P(4096), P(4096), hpr,
+                                    None) == ob.ONEBIT_EINVAL                  # nsel > chunk/64
+    assert lib.onebit_sparse_worker(10, 4096, 1, P(4096), P(4096), P(4096), None, P(4096), hpr,
+                                    None) == ob.ONEBIT_EINVAL                  # m NULL
+    assert lib.onebit_sparse_average(6, 2, None, P(4096), None) == ob.ONEBIT_EINVAL   # 6 % 4
+    assert lib.onebit_sparse_average(8, 17, None, P(4096), None) == ob.ONEBIT_EUNSUPPORTED
+    assert lib.onebit_sparse_average(0, 2, None, None, None) == ob.ONEBIT_OK
+    assert lib.onebit_sparse_update(None, 1, P(4096), P(4096), P(4096), P(4096), P(4096), P(4096),
+                                    P(4096), hpr, None, None) == ob.ONEBIT_EINVAL
 

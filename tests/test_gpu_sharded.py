@@ -206,6 +206,48 @@ def test_sharded_adam_equals_fused(n, W):
     assert int(s.status.item()) == 0
 
 
+@pytest.mark.parametrize("numels", RAGGED)
+@pytest.mark.parametrize("W", [1, 3, 8])
+@pytest.mark.parametrize("nsel", [1, 5])
+def test_sharded_sparse_equals_fused(numels, W, nsel):
+    """The sparse stage: each GPU's worker values and local error, the mean
+    of the W workers' values on its chunks, then the update of its replica,
+    for three steps, equal the fused onebit_sparse_compressed_step bit for
+    bit (two replicas checked)."""
+    wl = Workload("sharded_sparse", numels, W=W, init="frozen")
+    f, s = DevRun(wl), DevRun(wl)
+    C, K, N = wl.chunk, wl.K, wl.N
+    per = nsel * 64
+    x = [s.x.clone() for _ in range(2)]
+    m = [s.m.clone() for _ in range(2)]
+    vf = [s.vf.clone() for _ in range(2)]
+    e = [t.clone() for t in s.e]
+    vals_w = [torch.zeros(K * per, dtype=torch.float32, device="cuda") for _ in range(W)]
+    vals_s = torch.zeros(K * per, dtype=torch.float32, device="cuda")
+    for step in range(3):
+        f.sparse_step(step, nsel)
+        s.fill_grads(step)
+        sel = torch.from_numpy(wl.selection(step)).cuda()
+        for p_ in range(W):
+            ob.onebit_sparse_worker(N, C, nsel, sel, s.g[p_], e[p_], m[0], vals_w[p_], s.hp)
+        for k0, k1 in chunk_ranges(K, W):
+            if k1 > k0:
+                ob.onebit_sparse_average((k1 - k0) * per, W,
+                                         [v[k0 * per:k1 * per] for v in vals_w],
+                                         vals_s[k0 * per:k1 * per])
+        for r in range(2):
+            ob.onebit_sparse_update(s.table, nsel, sel, vals_s, x[r], m[r], s.v, vf[r], s.c_avg,
+                                    s.hp, s.status)
+        torch.cuda.synchronize()
+        for r in range(2):
+            for k, a, b in (("x", x[r], f.x), ("m", m[r], f.m), ("vf", vf[r], f.vf)):
+                assert torch.equal(a, b), f"{k}, replica {r}, step {step}"
+        assert torch.equal(vals_s, f.vals_s)
+        for w in range(W):
+            assert torch.equal(e[w], f.e[w]) and torch.equal(vals_w[w], f.vals_w[w])
+    assert int(s.status.item()) == 0
+
+
 def test_worker_compress_matches_compress_ef():
     """The fused worker momentum and compression equals onebit_compress_ef of
     beta1*m + a1*g (formed by the same two fp32 operations)."""
