@@ -256,3 +256,42 @@ def test_share_entry_points_stay_in_bounds(numels, W):
     for t in bits_w + scales_w:
         assert no_poison(t)
     A.check()
+
+
+@pytest.mark.parametrize("numels", TABLES)
+@pytest.mark.parametrize("nsel", [1, 3])
+def test_sparse_share_entry_points_stay_in_bounds(numels, nsel):
+    """The sparse stage's per-GPU entry points touch only their arguments
+    and write the transmitted values and their means in full."""
+    W, chunk = 3, 4096
+    table = ob.LayerTable(numels, chunk)
+    N, K, L = table.N, table.K, len(numels)
+    wl = Workload("bounds", numels, W=W, chunk=chunk)
+    per = nsel * 64
+    A = Arena()
+    x, m, v, vf, g, e = (A.take(N) for _ in range(6))
+    for i, t in enumerate([x, m, g]):
+        fill_normal(t, 40 + i, 0.02)
+    e.zero_()
+    v.copy_(torch.rand(N, device="cuda") * 1e-4)
+    vf.copy_(v)
+    c_avg = A.take(L)
+    c_avg.fill_(1.0)
+    sel = A.take(K, torch.int32)
+    sel.copy_(torch.from_numpy(wl.selection(0)).cuda())
+    vals_w = [A.take(K * per, torch.float32, POISON) for _ in range(W)]
+    vals_s = A.take(K * per, torch.float32, POISON)
+    status = A.take(1, torch.int32, 0)
+    hp = ob.onebit_hparams(**HPARAMS)
+    for w in range(W):
+        ob.onebit_sparse_worker(N, chunk, nsel, sel, g, e, m, vals_w[w], hp)
+    for p in range(W):
+        k0, k1 = K * p // W, K * (p + 1) // W
+        if k1 > k0:
+            ob.onebit_sparse_average((k1 - k0) * per, W, [t[k0 * per:k1 * per] for t in vals_w],
+                                     vals_s[k0 * per:k1 * per])
+    ob.onebit_sparse_update(table, nsel, sel, vals_s, x, m, v, vf, c_avg, hp, status)
+    torch.cuda.synchronize()
+    for t in vals_w + [vals_s]:
+        assert no_poison(t)
+    A.check()
