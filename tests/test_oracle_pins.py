@@ -253,8 +253,15 @@ def test_p6_first_warmup_step_closed_form():
 # ---------------------------------------------------------------------------
 def test_p7_sqrt_of_rounded_square_is_identity():
     r = rng(10)
-    s = f32(np.ldexp(r.uniform(1, 2, 10_000_000), r.integers(-60, 60, 10_000_000)))
-    assert np.array_equal(np.sqrt(s * s), s)
+    n = 10_000_000
+    t = np.empty(n, np.float32)
+    for _ in range(10):                                   # 10^8 floats in 10 slices
+        # random 23-bit mantissas with exponents 2^-60 .. 2^59
+        bits = (r.integers(67, 187, n, dtype=np.uint32) << 23) | r.integers(0, 1 << 23, n, dtype=np.uint32)
+        s = bits.view(np.float32)
+        np.multiply(s, s, out=t)
+        np.sqrt(t, out=t)
+        assert np.array_equal(t, s)
 
 
 @pytest.mark.parametrize("C", [1024, 4096, 16384])
