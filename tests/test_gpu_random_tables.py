@@ -1,7 +1,8 @@
 """Seeded random tables against the oracle: tensor counts, sizes (including
 ones that end exactly on a chunk boundary), chunk sizes, worker counts,
-modes and variant readings drawn from a fixed seed, a short trajectory
-each.  The bar is the one of the other parity tests."""
+modes (1-bit LAMB, 1-bit Adam, the sparse stage, and one GPU's share of a
+W-GPU LAMB step) and variant readings drawn from a fixed seed, a short
+trajectory each.  The bar is the one of the other parity tests."""
 import numpy as np
 import pytest
 
@@ -16,6 +17,7 @@ from synth.workloads import Workload  # noqa: E402
 
 from tests.harness import (DevRun, HostRun, assert_parity, compare_adam,  # noqa: E402
                            compare_sparse, compare_state)
+from tests.test_gpu_sharded import Sharded  # noqa: E402
 
 
 def _table(r, chunk):
@@ -32,13 +34,13 @@ def _table(r, chunk):
     return sizes
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", range(40))
 def test_random_table(seed):
     r = np.random.default_rng(1000 + seed)
     chunk = int(r.choice([1024, 2048, 4096, 8192, 16384]))
     W = int(r.integers(1, 17))
     numels = _table(r, chunk)
-    mode = ["lamb", "lamb", "adam", "sparse"][seed % 4]
+    mode = ["lamb", "lamb", "adam", "sparse", "share"][seed % 5]
     wl = Workload("random", numels, W=W, chunk=chunk, init="fresh", grad_std=0.02,
                   layer_scaled=bool(r.random() < 0.5), seed=seed)
     d, h = DevRun(wl), HostRun(wl)
@@ -73,6 +75,19 @@ def test_random_table(seed):
             d.adam_compressed_step(step)
             h.adam_compressed_step(step)
             assert_parity(compare_adam(d, h), f"seed {seed} adam {step} (n={n})")
+    elif mode == "share":
+        # one GPU's share on W simulated GPUs against the oracle, from a frozen state
+        wlf = Workload("random", numels, W=W, chunk=chunk, init="frozen", grad_std=1e-3,
+                       layer_scaled=bool(r.random() < 0.5), seed=seed)
+        d, h = DevRun(wlf), HostRun(wlf)
+        d.hp.rho_mode = h.hp.rho_mode = int(r.integers(0, 2))
+        sh = Sharded(d, replicas=sorted({0, W - 1}))
+        for step in range(3):
+            d.fill_grads(step)
+            sh.step()
+            h.compressed_step(step)
+            for p in sh.replicas:
+                assert_parity(compare_state(None, h, d=sh.window(p)), f"seed {seed} share {step}")
     else:
         nsel = int(r.integers(1, chunk // 64 + 1))
         for step in range(2):

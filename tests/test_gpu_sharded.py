@@ -37,7 +37,7 @@ class Sharded:
     def __init__(self, d, replicas=None):
         self.d = d
         W, L = d.wl.W, d.wl.L
-        self.replicas = list(range(W)) if replicas is None else list(replicas)
+        self.replicas = list(range(W)) if replicas is None else sorted(set(replicas))
         self.x = {p: d.x.clone() for p in self.replicas}
         self.m = {p: d.m.clone() for p in self.replicas}
         self.vf = {p: d.vf.clone() for p in self.replicas}
