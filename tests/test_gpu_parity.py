@@ -97,6 +97,56 @@ def test_compress_ef_zero_chunk_and_empty():
     ob.onebit_compress_ef(0, C, None, None, None, None)  # n = 0 does nothing
 
 
+def test_compress_ef_subnormal_values():
+    """fp32 subnormals are kept on both sides (no flush to zero): chunks of
+    subnormal inputs, of values whose squares underflow, of huge values whose
+    squares overflow the sum, and normal chunks, bit for bit."""
+    C = 4096
+    n = 5 * C + 123
+    r = np.random.default_rng(7)
+    inp = f32(r.standard_normal(n))
+    inp[:C] *= np.float32(1e-39)                 # subnormal inputs
+    inp[C:2 * C] *= np.float32(1e-25)            # squares underflow to subnormal or zero
+    inp[2 * C:3 * C] *= np.float32(3e18)         # squares near the top of the range
+    inp[3 * C:3 * C + 7] = np.float32(1.4e-45)   # the smallest subnormal
+    err = f32(r.standard_normal(n) * 1e-41)
+    K = oracle.num_chunks(n, C)
+    d_in, d_err = dev(inp), dev(err)
+    d_bits = torch.zeros(K * C // 32, dtype=torch.int32, device="cuda")
+    d_sc = torch.zeros(K, dtype=torch.float32, device="cuda")
+    ob.onebit_compress_ef(n, C, d_in, d_err, d_bits, d_sc)
+    bits, scales = oracle.compress_ef(inp, err, C)
+    assert np.array_equal(u32(d_bits), bits)
+    assert np.array_equal(host(d_sc).view(np.uint32), scales.view(np.uint32))
+    assert np.array_equal(host(d_err).view(np.uint32), err.view(np.uint32))
+    # squares of subnormals underflow to 0, so that chunk's scale is 0 and its
+    # errors carry the subnormal sums in + err, kept (not flushed) on both sides
+    assert scales[0] == 0.0 and np.count_nonzero(err[:C]) > C // 2
+
+
+def test_compressed_step_tiny_state():
+    """A compression step whose momentum, gradients and variances are tiny
+    (subnormal products along the way), bit for bit against the oracle."""
+    numels = [4096 * 2 + 5, 777]
+    wl = Workload("tiny_state", numels, W=3, init="frozen")
+    d, h = DevRun(wl), HostRun(wl)
+    for t_d, a_h, sc in ((d.m, h.m, 1e-36), (d.v, h.v, 1e-30), (d.vf, h.vf, 1e-30)):
+        a_h *= np.float32(sc)
+        t_d.copy_(dev(a_h))
+    for step in range(2):
+        h.fill_grads(step)
+        for w in range(wl.W):
+            h.g[w] *= np.float32(1e-35)
+            d.g[w].copy_(dev(h.g[w]))
+        d.compressed_step(step, fill=False)
+        h.compressed_step(step, fill=False)
+        assert_parity(compare_state(d, h), f"step {step}")
+
+
+def f32(a):
+    return np.asarray(a, dtype=np.float32)
+
+
 def test_status_flags_nonfinite():
     C, n = 4096, 4096 * 2
     inp = np.ones(n, np.float32)
