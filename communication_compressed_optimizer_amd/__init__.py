@@ -9,7 +9,7 @@ torch's current stream.  Every step of the path runs in the library's HIP
 kernels; if the library is not built, importing this package raises.
 
 Before a call reaches the library, tensors are checked for what the C side
-cannot see: that they live on the GPU, are contiguous, have the documented
+cannot see: that they live on the current GPU, are contiguous, have the documented
 dtype and hold at least the bytes the call touches, and that a list holds
 at least W worker entries (OnebitError with ONEBIT_EINVAL otherwise).  When
 a scalar argument (n, chunk, W, nsel) is itself invalid, the sizes are not
@@ -144,6 +144,9 @@ def _ptr(a, fn="", name="", nbytes=None, kind=_ANY):
     import torch
     if not a.is_cuda:
         raise _bad(fn, f"{name} is not a GPU tensor")
+    if a.device.index != torch.cuda.current_device():
+        raise _bad(fn, f"{name} is on {a.device}, the current device is "
+                       f"cuda:{torch.cuda.current_device()}")
     if not a.is_contiguous():
         raise _bad(fn, f"{name} is not contiguous")
     if kind == _F32 and a.dtype != torch.float32:

@@ -23,6 +23,7 @@ struct onebit_layer_table {
   int64_t N = 0;
   int64_t K = 0;
   int64_t S = 0;  // (chunk, tensor) segments
+  int device = -1;  // the device that holds dblock
   void* dblock = nullptr;
   DevTable dev{};
 };
@@ -67,6 +68,13 @@ size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
     if (!(p)) return fail(ONEBIT_EINVAL, "%s: %s is NULL", __func__, name);                  \
     if (!aligned4(p)) return fail(ONEBIT_EALIGN, "%s: %s is not 4-byte aligned", __func__,   \
                                   name);                                                     \
+  } while (0)
+
+// The optional status word takes 32-bit atomics.
+#define CHECK_OPT_WORDS(p, name)                                                             \
+  do {                                                                                       \
+    if ((p) && !aligned4(p))                                                                 \
+      return fail(ONEBIT_EALIGN, "%s: %s is not 4-byte aligned", __func__, name);            \
   } while (0)
 
 #define CHECK_OPT_PTR(p, name)                                                               \
@@ -121,8 +129,25 @@ int check_hparams(const onebit_hparams* hp, const char* fn, bool allow_wd = true
   return ONEBIT_OK;
 }
 
+// A table's device block lives on one device; a call made with another
+// device current would hand its kernels a foreign address.
 int check_table(const onebit_layer_table* t, const char* fn) {
   if (!t || !t->dblock) return fail(ONEBIT_EINVAL, "%s: table is NULL", fn);
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(ONEBIT_EHIP, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+  if (dev != t->device)
+    return fail(ONEBIT_EINVAL, "%s: table was created on device %d, current device is %d", fn,
+                t->device, dev);
+  return ONEBIT_OK;
+}
+
+// Chunk counts beyond this are refused (launch grids are 32-bit).
+constexpr int64_t kMaxChunks = INT32_MAX / 2;
+
+int check_n(int64_t n, int64_t chunk, const char* fn) {
+  if (n < 0) return fail(ONEBIT_EINVAL, "%s: n < 0", fn);
+  if ((n + chunk - 1) / chunk > kMaxChunks) return fail(ONEBIT_EUNSUPPORTED, "%s: n too large", fn);
   return ONEBIT_OK;
 }
 
@@ -490,14 +515,20 @@ int onebit_layer_table_create(const int64_t* numels, int32_t L, int32_t chunk,
     return fail(ONEBIT_EUNSUPPORTED, "%s: chunk %d is not a power of two in [1024, 16384]",
                 __func__, chunk);
   std::vector<int64_t> off((size_t)L + 1, 0);
+  const int64_t max_n = kMaxChunks * chunk;
   for (int32_t l = 0; l < L; ++l) {
     if (numels[l] < 1) return fail(ONEBIT_EINVAL, "%s: numels[%d] = %lld < 1", __func__, l,
                                    (long long)numels[l]);
+    // bounded before the add, so the running sum cannot overflow
+    if (numels[l] > max_n - off[l])
+      return fail(ONEBIT_EUNSUPPORTED, "%s: too many chunks", __func__);
     off[l + 1] = off[l] + numels[l];
   }
   const int64_t N = off[L];
   const int64_t K = (N + chunk - 1) / chunk;
-  if (K > INT32_MAX / 2) return fail(ONEBIT_EUNSUPPORTED, "%s: too many chunks", __func__);
+  int device = -1;
+  if (hipError_t e = hipGetDevice(&device); e != hipSuccess)
+    return fail(ONEBIT_EHIP, "%s: hipGetDevice: %s", __func__, hipGetErrorString(e));
   std::vector<int32_t> l0((size_t)K), l1((size_t)K), seg((size_t)K), lseg((size_t)L + 1);
   int64_t S = 0;
   int32_t l = 0;
@@ -526,6 +557,7 @@ int onebit_layer_table_create(const int64_t* numels, int32_t L, int32_t chunk,
   t->N = N;
   t->K = K;
   t->S = S;
+  t->device = device;
   const size_t b_off = round256(sizeof(int64_t) * ((size_t)L + 1));
   const size_t b_k = round256(sizeof(int32_t) * (size_t)K);
   const size_t b_l = round256(sizeof(int32_t) * ((size_t)L + 1));
@@ -594,8 +626,9 @@ int onebit_workspace_size(const onebit_layer_table* table, int32_t W, size_t* by
 
 int onebit_compress_ef(int64_t n, int32_t chunk, const float* in, float* err, uint32_t* bits,
                        float* scales, int32_t* status, void* stream) {
-  if (n < 0) return fail(ONEBIT_EINVAL, "%s: n < 0", __func__);
+  CHECK_OPT_WORDS(status, "status");
   if (!chunk_supported(chunk)) return fail(ONEBIT_EUNSUPPORTED, "%s: chunk %d", __func__, chunk);
+  if (int rc = check_n(n, chunk, __func__)) return rc;
   if (n == 0) return ok();
   CHECK_PTR(in, "in");
   CHECK_PTR(err, "err");
@@ -608,8 +641,9 @@ int onebit_compress_ef(int64_t n, int32_t chunk, const float* in, float* err, ui
 int onebit_average_packed(int64_t n, int32_t chunk, int32_t W, const uint32_t* const* bits_w,
                           const float* const* scales_w, float* err_s, uint32_t* bits_out,
                           float* scales_out, int32_t* status, void* stream) {
-  if (n < 0) return fail(ONEBIT_EINVAL, "%s: n < 0", __func__);
+  CHECK_OPT_WORDS(status, "status");
   if (!chunk_supported(chunk)) return fail(ONEBIT_EUNSUPPORTED, "%s: chunk %d", __func__, chunk);
+  if (int rc = check_n(n, chunk, __func__)) return rc;
   if (int rc = check_W(W, __func__)) return rc;
   if (n == 0) return ok();
   if (!bits_w || !scales_w) return fail(ONEBIT_EINVAL, "%s: worker arrays are NULL", __func__);
@@ -630,8 +664,8 @@ int onebit_average_packed(int64_t n, int32_t chunk, int32_t W, const uint32_t* c
 
 int onebit_decompress(int64_t n, int32_t chunk, const uint32_t* bits, const float* scales,
                       float* out, void* stream) {
-  if (n < 0) return fail(ONEBIT_EINVAL, "%s: n < 0", __func__);
   if (!chunk_supported(chunk)) return fail(ONEBIT_EUNSUPPORTED, "%s: chunk %d", __func__, chunk);
+  if (int rc = check_n(n, chunk, __func__)) return rc;
   if (n == 0) return ok();
   CHECK_WORDS(bits, "bits");
   CHECK_WORDS(scales, "scales");
@@ -643,6 +677,7 @@ int onebit_decompress(int64_t n, int32_t chunk, const uint32_t* bits, const floa
 int onebit_lamb_warmup_step(const onebit_layer_table* table, int32_t W, const float* const* grads,
                             float* x, float* m, float* v, float* c_sum, float* c_out,
                             const onebit_hparams* hp, void* ws, int32_t* status, void* stream) {
+  CHECK_OPT_WORDS(status, "status");
   if (int rc = check_table(table, __func__)) return rc;
   if (int rc = check_W(W, __func__)) return rc;
   if (int rc = check_hparams(hp, __func__)) return rc;
@@ -700,6 +735,7 @@ int onebit_lamb_compress_average(const onebit_layer_table* table, int32_t W,
                                  uint32_t* const* bits_w, float* const* scales_w, uint32_t* bits_s,
                                  float* scales_s, const onebit_hparams* hp, void* ws,
                                  int32_t* status, void* stream) {
+  CHECK_OPT_WORDS(status, "status");
   Workers wk;
   if (int rc = check_phase1(__func__, table, W, grads, err_w, err_s, m, v_frozen, v_fresh, bits_w,
                             scales_w, bits_s, scales_s, hp, ws, wk))
@@ -714,6 +750,7 @@ int onebit_lamb_rescale_update(const onebit_layer_table* table, const uint32_t* 
                                const float* scales_s, float* x, float* m, const float* v_frozen,
                                const float* c_avg, float* f_prev, float* c_out,
                                const onebit_hparams* hp, void* ws, int32_t* status, void* stream) {
+  CHECK_OPT_WORDS(status, "status");
   if (int rc = check_phase2(__func__, table, bits_s, scales_s, x, m, v_frozen, c_avg, f_prev, c_out,
                             hp, ws))
     return rc;
@@ -730,6 +767,7 @@ int onebit_lamb_compressed_step(const onebit_layer_table* table, int32_t W,
                                 uint32_t* const* bits_w, float* const* scales_w, uint32_t* bits_s,
                                 float* scales_s, const onebit_hparams* hp, void* ws,
                                 int32_t* status, void* stream) {
+  CHECK_OPT_WORDS(status, "status");
   Workers wk;
   if (int rc = check_phase1(__func__, table, W, grads, err_w, err_s, m, v_frozen, v_fresh, bits_w,
                             scales_w, bits_s, scales_s, hp, ws, wk))
@@ -752,11 +790,11 @@ int onebit_worker_compress(int64_t n, int32_t chunk, const float* grad, float* e
                            const float* m, const uint32_t* bits_m, const float* scales_m,
                            uint32_t* bits_w, float* scales_w, const onebit_hparams* hp,
                            int32_t* status, void* stream) {
+  CHECK_OPT_WORDS(status, "status");
   if (n < 0) return fail(ONEBIT_EINVAL, "%s: n < 0", __func__);
   if (!chunk_supported(chunk)) return fail(ONEBIT_EUNSUPPORTED, "%s: chunk %d", __func__, chunk);
   if (int rc = check_hparams(hp, __func__)) return rc;
-  if ((n + chunk - 1) / chunk > INT32_MAX / 2)
-    return fail(ONEBIT_EUNSUPPORTED, "%s: n too large", __func__);
+  if (int rc = check_n(n, chunk, __func__)) return rc;
   if (n == 0) return ok();
   CHECK_PTR(grad, "grad");
   CHECK_PTR(err_w, "err_w");
@@ -806,8 +844,7 @@ int onebit_adam_update(int64_t n, int32_t chunk, const uint32_t* bits_s, const f
   if (n < 0) return fail(ONEBIT_EINVAL, "%s: n < 0", __func__);
   if (!chunk_supported(chunk)) return fail(ONEBIT_EUNSUPPORTED, "%s: chunk %d", __func__, chunk);
   if (int rc = check_hparams(hp, __func__, false)) return rc;
-  if ((n + chunk - 1) / chunk > INT32_MAX / 2)
-    return fail(ONEBIT_EUNSUPPORTED, "%s: n too large", __func__);
+  if (int rc = check_n(n, chunk, __func__)) return rc;
   if (n == 0) return ok();
   CHECK_WORDS(bits_s, "bits_s");
   CHECK_WORDS(scales_s, "scales_s");
@@ -828,8 +865,7 @@ int onebit_sparse_worker(int64_t n, int32_t chunk, int32_t nsel, const int32_t* 
   if (nsel < 1 || nsel > chunk / 64)
     return fail(ONEBIT_EINVAL, "%s: nsel = %d outside [1, chunk/64 = %d]", __func__, nsel,
                 chunk / 64);
-  if ((n + chunk - 1) / chunk > INT32_MAX / 2)
-    return fail(ONEBIT_EUNSUPPORTED, "%s: n too large", __func__);
+  if (int rc = check_n(n, chunk, __func__)) return rc;
   if (n == 0) return ok();
   CHECK_WORDS(sel, "sel");
   CHECK_PTR(grad, "grad");
@@ -865,6 +901,7 @@ int onebit_sparse_update(const onebit_layer_table* table, int32_t nsel, const in
                          const float* vals_s, float* x, float* m, const float* v_frozen,
                          float* v_fresh, const float* c_avg, const onebit_hparams* hp,
                          int32_t* status, void* stream) {
+  CHECK_OPT_WORDS(status, "status");
   if (int rc = check_table(table, __func__)) return rc;
   if (int rc = check_hparams(hp, __func__, false)) return rc;
   if (nsel < 1 || nsel > table->chunk / 64)
@@ -887,8 +924,7 @@ int onebit_adam_warmup_step(int64_t n, int32_t W, const float* const* grads, flo
   if (n < 0) return fail(ONEBIT_EINVAL, "%s: n < 0", __func__);
   if (int rc = check_W(W, __func__)) return rc;
   if (int rc = check_hparams(hp, __func__, false)) return rc;
-  if ((n + kAdamWarmupChunk - 1) / kAdamWarmupChunk > INT32_MAX / 2)
-    return fail(ONEBIT_EUNSUPPORTED, "%s: n too large", __func__);
+  if (int rc = check_n(n, kAdamWarmupChunk, __func__)) return rc;
   if (n == 0) return ok();
   if (!grads) return fail(ONEBIT_EINVAL, "%s: grads is NULL", __func__);
   Workers wk{};
@@ -910,12 +946,12 @@ int onebit_adam_compressed_step(int64_t n, int32_t chunk, int32_t W, const float
                                 const float* v_frozen, uint32_t* const* bits_w,
                                 float* const* scales_w, uint32_t* bits_s, float* scales_s,
                                 const onebit_hparams* hp, int32_t* status, void* stream) {
+  CHECK_OPT_WORDS(status, "status");
   if (n < 0) return fail(ONEBIT_EINVAL, "%s: n < 0", __func__);
   if (!chunk_supported(chunk)) return fail(ONEBIT_EUNSUPPORTED, "%s: chunk %d", __func__, chunk);
   if (int rc = check_W(W, __func__)) return rc;
   if (int rc = check_hparams(hp, __func__, false)) return rc;
-  if ((n + chunk - 1) / chunk > INT32_MAX / 2)
-    return fail(ONEBIT_EUNSUPPORTED, "%s: n too large", __func__);
+  if (int rc = check_n(n, chunk, __func__)) return rc;
   if (n == 0) return ok();
   Workers wk;
   if (int rc = check_workers(__func__, W, grads, err_w, bits_w, scales_w, wk)) return rc;
@@ -936,13 +972,14 @@ int onebit_sparse_compressed_step(const onebit_layer_table* table, int32_t W, in
                                   float* v_fresh, const float* c_avg, float* const* vals_w,
                                   float* vals_s, const onebit_hparams* hp, int32_t* status,
                                   void* stream) {
+  CHECK_OPT_WORDS(status, "status");
   if (int rc = check_table(table, __func__)) return rc;
   if (int rc = check_W(W, __func__)) return rc;
   if (int rc = check_hparams(hp, __func__, false)) return rc;
   if (nsel < 1 || nsel > table->chunk / 64)
     return fail(ONEBIT_EINVAL, "%s: nsel = %d outside [1, chunk/64 = %d]", __func__, nsel,
                 table->chunk / 64);
-  if (!sel) return fail(ONEBIT_EINVAL, "%s: sel is NULL", __func__);
+  CHECK_WORDS(sel, "sel");
   Workers wk;
   if (int rc = check_workers(__func__, W, grads, err_w, nullptr, nullptr, wk)) return rc;
   WorkerVals wv{};

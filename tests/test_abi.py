@@ -59,12 +59,25 @@ def test_argument_checks(ob):
     assert lib.onebit_compress_ef(10, 4096, P(4100), P(4096), P(4096), P(4096), None, None) == \
         ob.ONEBIT_EALIGN
     assert lib.onebit_compress_ef(0, 4096, None, None, None, None, None, None) == ob.ONEBIT_OK
+    # the status word takes 32-bit atomics
+    assert lib.onebit_compress_ef(10, 4096, P(4096), P(4096), P(4096), P(4096), P(4098), None) == \
+        ob.ONEBIT_EALIGN
+    assert "status is not 4-byte aligned" in ob.onebit_last_error()
     arr2 = (P * 2)(4096, 4096)
     assert lib.onebit_average_packed(10, 4096, 0, arr2, arr2, P(4096), P(4096), P(4096), None,
                                      None) == ob.ONEBIT_EUNSUPPORTED
     assert lib.onebit_average_packed(10, 4096, 17, arr2, arr2, P(4096), P(4096), P(4096), None,
                                      None) == ob.ONEBIT_EUNSUPPORTED
     assert lib.onebit_decompress(5, 4096, P(4096), P(4096), P(4098), None) == ob.ONEBIT_EALIGN
+    # at most 2^30 - 1 chunks per buffer, refused before any pointer is read
+    big = (1 << 30) * 1024
+    assert lib.onebit_compress_ef(big, 1024, *[P(4096)] * 4, None, None) == \
+        ob.ONEBIT_EUNSUPPORTED
+    assert "n too large" in ob.onebit_last_error()
+    assert lib.onebit_average_packed(big, 1024, 2, arr2, arr2, P(4096), P(4096), P(4096), None,
+                                     None) == ob.ONEBIT_EUNSUPPORTED
+    assert lib.onebit_decompress(big, 1024, P(4096), P(4096), P(4096), None) == \
+        ob.ONEBIT_EUNSUPPORTED
 
 
 def test_table_checks(ob):
@@ -77,6 +90,16 @@ def test_table_checks(ob):
     assert lib.onebit_layer_table_create(numels, 1, 3000, ctypes.byref(out)) == \
         ob.ONEBIT_EUNSUPPORTED
     assert lib.onebit_layer_table_destroy(None) == ob.ONEBIT_OK
+    # sizes whose sum would overflow int64, or that exceed 2^30 - 1 chunks,
+    # are refused before anything is allocated
+    numels = (ctypes.c_int64 * 3)(1 << 62, 1 << 62, 1 << 62)
+    assert lib.onebit_layer_table_create(numels, 3, 4096, ctypes.byref(out)) == \
+        ob.ONEBIT_EUNSUPPORTED
+    assert "too many chunks" in ob.onebit_last_error()
+    numels = (ctypes.c_int64 * 2)((1 << 29) * 4096, (1 << 29) * 4096)
+    assert lib.onebit_layer_table_create(numels, 2, 4096, ctypes.byref(out)) == \
+        ob.ONEBIT_EUNSUPPORTED
+    assert not out.value
     hp = ob.onebit_hparams(weight_decay=0.01)
     assert lib.onebit_lamb_warmup_step(None, 1, None, None, None, None, None, None,
                                        ctypes.byref(hp), None, None, None) == ob.ONEBIT_EINVAL
