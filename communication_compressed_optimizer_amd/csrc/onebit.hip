@@ -157,6 +157,64 @@ int check_W(int32_t W, const char* fn) {
   return ONEBIT_OK;
 }
 
+// Byte ranges of one call's device arrays.  The kernels access them through
+// restrict-qualified pointers, so an array the call writes must not overlap
+// any other array of the call; read-only arrays may overlap each other (one
+// gradient buffer passed for several workers, say).
+class Spans {
+ public:
+  void add(const void* p, int64_t bytes, bool written, const char* name, int idx = -1) {
+    if (!p || bytes <= 0 || n_ == kCap) return;
+    s_[n_++] = {reinterpret_cast<uintptr_t>(p), (uintptr_t)bytes, written, name, idx};
+  }
+  // Every array of W workers, given as a host array of pointers (or NULL).
+  template <typename T>
+  void add_workers(T const* arr, int W, int64_t bytes, bool written, const char* name) {
+    if (arr)
+      for (int w = 0; w < W; ++w) add(arr[w], bytes, written, name, w);
+  }
+  int check(const char* fn) const {
+    for (int i = 0; i < n_; ++i)
+      for (int j = i + 1; j < n_; ++j) {
+        const S& a = s_[i];
+        const S& b = s_[j];
+        if ((a.w || b.w) && a.p < b.p + b.bytes && b.p < a.p + a.bytes) {
+          const S& wr = b.w ? b : a;  // the written one is named first
+          const S& other = b.w ? a : b;
+          return fail(ONEBIT_EINVAL, "%s: %s overlaps %s", fn, label(wr).c_str(),
+                      label(other).c_str());
+        }
+      }
+    return ONEBIT_OK;
+  }
+
+ private:
+  struct S {
+    uintptr_t p, bytes;
+    bool w;
+    const char* name;
+    int idx;
+  };
+  static std::string label(const S& s) {
+    return s.idx < 0 ? std::string(s.name) : std::string(s.name) + "[" + std::to_string(s.idx) + "]";
+  }
+  // four worker arrays of up to kMaxWorkers entries plus a dozen others
+  static constexpr int kCap = 4 * kMaxWorkers + 16;
+  S s_[kCap];
+  int n_ = 0;
+};
+
+// Bytes of a buffer's arrays: n elements in chunks of `chunk`.
+struct Bytes {
+  int64_t elems, words, scales;
+  Bytes(int64_t n, int64_t chunk) {
+    const int64_t K = (n + chunk - 1) / chunk;
+    elems = 4 * n;
+    words = 4 * (K * chunk / 32);
+    scales = 4 * K;
+  }
+};
+
 // Workspace layout: [seg_x: S doubles][seg_u: S doubles][c_layer: L floats].
 // The warmup keeps the per-segment sums of x^2 and u^2 there; the
 // compression step reuses the first S floats as seg_max, or (norm-ratio
@@ -634,6 +692,14 @@ int onebit_compress_ef(int64_t n, int32_t chunk, const float* in, float* err, ui
   CHECK_PTR(err, "err");
   CHECK_WORDS(bits, "bits");
   CHECK_WORDS(scales, "scales");
+  const Bytes b(n, chunk);
+  Spans sp;
+  sp.add(in, b.elems, false, "in");
+  sp.add(err, b.elems, true, "err");
+  sp.add(bits, b.words, true, "bits");
+  sp.add(scales, b.scales, true, "scales");
+  sp.add(status, 4, true, "status");
+  if (int rc = sp.check(__func__)) return rc;
   by_chunk<LaunchCompress>(chunk, n, in, err, bits, scales, status, (hipStream_t)stream);
   return launch_status(__func__);
 }
@@ -657,6 +723,15 @@ int onebit_average_packed(int64_t n, int32_t chunk, int32_t W, const uint32_t* c
   CHECK_PTR(err_s, "err_s");
   CHECK_WORDS(bits_out, "bits_out");
   CHECK_WORDS(scales_out, "scales_out");
+  const Bytes b(n, chunk);
+  Spans sp;
+  sp.add_workers(bits_w, W, b.words, false, "bits_w");
+  sp.add_workers(scales_w, W, b.scales, false, "scales_w");
+  sp.add(err_s, b.elems, true, "err_s");
+  sp.add(bits_out, b.words, true, "bits_out");
+  sp.add(scales_out, b.scales, true, "scales_out");
+  sp.add(status, 4, true, "status");
+  if (int rc = sp.check(__func__)) return rc;
   by_chunk<LaunchAverage>(chunk, n, (int)W, pin, err_s, bits_out, scales_out, status,
                           (hipStream_t)stream);
   return launch_status(__func__);
@@ -670,6 +745,12 @@ int onebit_decompress(int64_t n, int32_t chunk, const uint32_t* bits, const floa
   CHECK_WORDS(bits, "bits");
   CHECK_WORDS(scales, "scales");
   CHECK_PTR(out, "out");
+  const Bytes b(n, chunk);
+  Spans sp;
+  sp.add(bits, b.words, false, "bits");
+  sp.add(scales, b.scales, false, "scales");
+  sp.add(out, b.elems, true, "out");
+  if (int rc = sp.check(__func__)) return rc;
   by_chunk<LaunchDecompress>(chunk, n, bits, scales, out, (hipStream_t)stream);
   return launch_status(__func__);
 }
@@ -693,6 +774,17 @@ int onebit_lamb_warmup_step(const onebit_layer_table* table, int32_t W, const fl
   CHECK_PTR(c_sum, "c_sum");
   CHECK_OPT_PTR(c_out, "c_out");
   CHECK_PTR(ws, "ws");
+  const Bytes b(table->N, table->chunk);
+  Spans sp;
+  sp.add_workers(grads, W, b.elems, false, "grads");
+  sp.add(x, b.elems, true, "x");
+  sp.add(m, b.elems, true, "m");
+  sp.add(v, b.elems, true, "v");
+  sp.add(c_sum, 4 * (int64_t)table->L, true, "c_sum");
+  sp.add(c_out, 4 * (int64_t)table->L, true, "c_out");
+  sp.add(ws, (int64_t)ws_bytes(table), true, "ws");
+  sp.add(status, 4, true, "status");
+  if (int rc = sp.check(__func__)) return rc;
   const Coef cf = make_coef(*hp);
   by_chunk<LaunchWarmup>(table->chunk, table, (int)W, wk, x, m, v, c_sum, c_out, cf,
                          ws_view(table, ws), status, (hipStream_t)stream);
@@ -722,6 +814,17 @@ int onebit_lamb_freeze(const onebit_layer_table* table, int32_t W, const float* 
   CHECK_PTR(c_sum, "c_sum");
   CHECK_PTR(c_avg, "c_avg");
   CHECK_PTR(f_prev, "f_prev");
+  const Bytes b(table->N, table->chunk);
+  const int64_t tl = 4 * (int64_t)table->L;
+  Spans sp;
+  sp.add(v, b.elems, false, "v");
+  sp.add(v_fresh, b.elems, true, "v_fresh");
+  sp.add_workers(err_w, W, b.elems, true, "err_w");
+  sp.add(err_s, b.elems, true, "err_s");
+  sp.add(c_sum, tl, false, "c_sum");
+  sp.add(c_avg, tl, true, "c_avg");
+  sp.add(f_prev, tl, true, "f_prev");
+  if (int rc = sp.check(__func__)) return rc;
   hipStream_t st = (hipStream_t)stream;
   by_chunk<LaunchFreeze>(table->chunk, table, (int)W, v, v_fresh, wk, err_s, st);
   hipLaunchKernelGGL(k_freeze_tensors, dim3((unsigned)((table->L + 255) / 256)), dim3(256), 0, st,
@@ -740,6 +843,21 @@ int onebit_lamb_compress_average(const onebit_layer_table* table, int32_t W,
   if (int rc = check_phase1(__func__, table, W, grads, err_w, err_s, m, v_frozen, v_fresh, bits_w,
                             scales_w, bits_s, scales_s, hp, ws, wk))
     return rc;
+  const Bytes b(table->N, table->chunk);
+  Spans sp;
+  sp.add_workers(grads, W, b.elems, false, "grads");
+  sp.add_workers(err_w, W, b.elems, true, "err_w");
+  sp.add_workers(bits_w, W, b.words, true, "bits_w");
+  sp.add_workers(scales_w, W, b.scales, true, "scales_w");
+  sp.add(err_s, b.elems, true, "err_s");
+  sp.add(m, b.elems, false, "m");
+  sp.add(v_frozen, b.elems, false, "v_frozen");
+  sp.add(v_fresh, b.elems, true, "v_fresh");
+  sp.add(bits_s, b.words, true, "bits_s");
+  sp.add(scales_s, b.scales, true, "scales_s");
+  sp.add(ws, (int64_t)ws_bytes(table), true, "ws");
+  sp.add(status, 4, true, "status");
+  if (int rc = sp.check(__func__)) return rc;
   by_chunk<LaunchPassA>(table->chunk, table, (int)W, wk, err_s, m, v_frozen, v_fresh, bits_s,
                         scales_s, make_coef(*hp), hp->rho_mode == ONEBIT_RHO_NORM_RATIO,
                         ws_view(table, ws), status, (hipStream_t)stream);
@@ -754,6 +872,20 @@ int onebit_lamb_rescale_update(const onebit_layer_table* table, const uint32_t* 
   if (int rc = check_phase2(__func__, table, bits_s, scales_s, x, m, v_frozen, c_avg, f_prev, c_out,
                             hp, ws))
     return rc;
+  const Bytes b(table->N, table->chunk);
+  const int64_t tl = 4 * (int64_t)table->L;
+  Spans sp;
+  sp.add(bits_s, b.words, false, "bits_s");
+  sp.add(scales_s, b.scales, false, "scales_s");
+  sp.add(x, b.elems, true, "x");
+  sp.add(m, b.elems, true, "m");
+  sp.add(v_frozen, b.elems, false, "v_frozen");
+  sp.add(c_avg, tl, false, "c_avg");
+  sp.add(f_prev, tl, true, "f_prev");
+  sp.add(c_out, tl, true, "c_out");
+  sp.add(ws, (int64_t)ws_bytes(table), true, "ws");
+  sp.add(status, 4, true, "status");
+  if (int rc = sp.check(__func__)) return rc;
   by_chunk<LaunchPassB>(table->chunk, table, bits_s, scales_s, x, m, v_frozen, c_avg, f_prev, c_out,
                         make_coef(*hp), hp->rho_mode == ONEBIT_RHO_NORM_RATIO, ws_view(table, ws),
                         status, (hipStream_t)stream);
@@ -775,6 +907,26 @@ int onebit_lamb_compressed_step(const onebit_layer_table* table, int32_t W,
   if (int rc = check_phase2(__func__, table, bits_s, scales_s, x, m, v_frozen, c_avg, f_prev, c_out,
                             hp, ws))
     return rc;
+  const Bytes b(table->N, table->chunk);
+  const int64_t tl = 4 * (int64_t)table->L;
+  Spans sp;
+  sp.add_workers(grads, W, b.elems, false, "grads");
+  sp.add_workers(err_w, W, b.elems, true, "err_w");
+  sp.add_workers(bits_w, W, b.words, true, "bits_w");
+  sp.add_workers(scales_w, W, b.scales, true, "scales_w");
+  sp.add(err_s, b.elems, true, "err_s");
+  sp.add(x, b.elems, true, "x");
+  sp.add(m, b.elems, true, "m");
+  sp.add(v_frozen, b.elems, false, "v_frozen");
+  sp.add(v_fresh, b.elems, true, "v_fresh");
+  sp.add(c_avg, tl, false, "c_avg");
+  sp.add(f_prev, tl, true, "f_prev");
+  sp.add(c_out, tl, true, "c_out");
+  sp.add(bits_s, b.words, true, "bits_s");
+  sp.add(scales_s, b.scales, true, "scales_s");
+  sp.add(ws, (int64_t)ws_bytes(table), true, "ws");
+  sp.add(status, 4, true, "status");
+  if (int rc = sp.check(__func__)) return rc;
   const Coef cf = make_coef(*hp);
   const bool rn = hp->rho_mode == ONEBIT_RHO_NORM_RATIO;
   const Ws wsv = ws_view(table, ws);
@@ -808,6 +960,17 @@ int onebit_worker_compress(int64_t n, int32_t chunk, const float* grad, float* e
     CHECK_WORDS(bits_m, "bits_m");
     CHECK_WORDS(scales_m, "scales_m");
   }
+  const Bytes b(n, chunk);
+  Spans sp;
+  sp.add(grad, b.elems, false, "grad");
+  sp.add(err_w, b.elems, true, "err_w");
+  sp.add(m, b.elems, false, "m");
+  sp.add(bits_m, b.words, false, "bits_m");
+  sp.add(scales_m, b.scales, false, "scales_m");
+  sp.add(bits_w, b.words, true, "bits_w");
+  sp.add(scales_w, b.scales, true, "scales_w");
+  sp.add(status, 4, true, "status");
+  if (int rc = sp.check(__func__)) return rc;
   by_chunk<LaunchWorker>(chunk, n, grad, err_w, m, bits_m, scales_m, bits_w, scales_w,
                          make_coef(*hp), status, (hipStream_t)stream);
   return launch_status(__func__);
@@ -832,6 +995,17 @@ int onebit_lamb_rescale_stats(const onebit_layer_table* table, const uint32_t* b
     CHECK_WORDS(bits_m, "bits_m");
     CHECK_WORDS(scales_m, "scales_m");
   }
+  const Bytes b(table->N, table->chunk);
+  Spans sp;
+  sp.add(bits_s, b.words, false, "bits_s");
+  sp.add(scales_s, b.scales, false, "scales_s");
+  sp.add(m, b.elems, false, "m");
+  sp.add(bits_m, b.words, false, "bits_m");
+  sp.add(scales_m, b.scales, false, "scales_m");
+  sp.add(v_frozen, b.elems, false, "v_frozen");
+  sp.add(v_fresh, b.elems, true, "v_fresh");
+  sp.add(ws, (int64_t)ws_bytes(table), true, "ws");
+  if (int rc = sp.check(__func__)) return rc;
   by_chunk<LaunchStats>(table->chunk, table, bits_s, scales_s, m, bits_m, scales_m, v_frozen,
                         v_fresh, make_coef(*hp), hp->rho_mode == ONEBIT_RHO_NORM_RATIO,
                         ws_view(table, ws), (hipStream_t)stream);
@@ -851,6 +1025,14 @@ int onebit_adam_update(int64_t n, int32_t chunk, const uint32_t* bits_s, const f
   CHECK_PTR(x, "x");
   CHECK_OPT_PTR(m, "m");
   CHECK_PTR(v_frozen, "v_frozen");
+  const Bytes b(n, chunk);
+  Spans sp;
+  sp.add(bits_s, b.words, false, "bits_s");
+  sp.add(scales_s, b.scales, false, "scales_s");
+  sp.add(x, b.elems, true, "x");
+  sp.add(m, b.elems, true, "m");
+  sp.add(v_frozen, b.elems, false, "v_frozen");
+  if (int rc = sp.check(__func__)) return rc;
   by_chunk<LaunchAdamUpdate>(chunk, n, bits_s, scales_s, v_frozen, x, m, make_coef(*hp),
                              (hipStream_t)stream);
   return launch_status(__func__);
@@ -872,6 +1054,15 @@ int onebit_sparse_worker(int64_t n, int32_t chunk, int32_t nsel, const int32_t* 
   CHECK_PTR(err_w, "err_w");
   CHECK_PTR(m, "m");
   CHECK_PTR(vals_w, "vals_w");
+  const Bytes b(n, chunk);
+  const int64_t K = (n + chunk - 1) / chunk;
+  Spans sp;
+  sp.add(sel, 4 * K, false, "sel");
+  sp.add(grad, b.elems, false, "grad");
+  sp.add(err_w, b.elems, true, "err_w");
+  sp.add(m, b.elems, false, "m");
+  sp.add(vals_w, 4 * K * nsel * 64, true, "vals_w");
+  if (int rc = sp.check(__func__)) return rc;
   by_chunk<LaunchSparseWorker>(chunk, n, (int)nsel, sel, grad, err_w, m, vals_w, make_coef(*hp),
                                (hipStream_t)stream);
   return launch_status(__func__);
@@ -890,6 +1081,10 @@ int onebit_sparse_average(int64_t count, int32_t W, const float* const* vals_w, 
     wv.v[w] = const_cast<float*>(vals_w[w]);
   }
   CHECK_PTR(vals_s, "vals_s");
+  Spans sp;
+  sp.add_workers(vals_w, W, 4 * count, false, "vals_w");
+  sp.add(vals_s, 4 * count, true, "vals_s");
+  if (int rc = sp.check(__func__)) return rc;
   const int64_t count4 = count / 4;
   const int64_t blocks = (count4 + 255) / 256 < 65536 ? (count4 + 255) / 256 : 65536;
   hipLaunchKernelGGL(k_mean_values<kShare_NT>, dim3((unsigned)blocks), dim3(256), 0,
@@ -914,6 +1109,17 @@ int onebit_sparse_update(const onebit_layer_table* table, int32_t nsel, const in
   CHECK_PTR(v_frozen, "v_frozen");
   CHECK_PTR(v_fresh, "v_fresh");
   CHECK_PTR(c_avg, "c_avg");
+  const Bytes b(table->N, table->chunk);
+  Spans sp;
+  sp.add(sel, 4 * table->K, false, "sel");
+  sp.add(vals_s, 4 * table->K * nsel * 64, false, "vals_s");
+  sp.add(x, b.elems, true, "x");
+  sp.add(m, b.elems, true, "m");
+  sp.add(v_frozen, b.elems, false, "v_frozen");
+  sp.add(v_fresh, b.elems, true, "v_fresh");
+  sp.add(c_avg, 4 * (int64_t)table->L, false, "c_avg");
+  sp.add(status, 4, true, "status");
+  if (int rc = sp.check(__func__)) return rc;
   by_chunk<LaunchSparseUpdate>(table->chunk, table, (int)nsel, sel, vals_s, x, m, v_frozen, v_fresh,
                                c_avg, make_coef(*hp), status, (hipStream_t)stream);
   return launch_status(__func__);
@@ -935,6 +1141,12 @@ int onebit_adam_warmup_step(int64_t n, int32_t W, const float* const* grads, flo
   CHECK_PTR(x, "x");
   CHECK_PTR(m, "m");
   CHECK_PTR(v, "v");
+  Spans sp;
+  sp.add_workers(grads, W, 4 * n, false, "grads");
+  sp.add(x, 4 * n, true, "x");
+  sp.add(m, 4 * n, true, "m");
+  sp.add(v, 4 * n, true, "v");
+  if (int rc = sp.check(__func__)) return rc;
   constexpr int C = kAdamWarmupChunk;
   launch_chunks<C>(n, (hipStream_t)stream, k_adam_warmup<C>, n, (int)W, wk, x, m, v,
                    make_coef(*hp));
@@ -961,6 +1173,20 @@ int onebit_adam_compressed_step(int64_t n, int32_t chunk, int32_t W, const float
   CHECK_PTR(v_frozen, "v_frozen");
   CHECK_WORDS(bits_s, "bits_s");
   CHECK_WORDS(scales_s, "scales_s");
+  const Bytes b(n, chunk);
+  Spans sp;
+  sp.add_workers(grads, W, b.elems, false, "grads");
+  sp.add_workers(err_w, W, b.elems, true, "err_w");
+  sp.add_workers(bits_w, W, b.words, true, "bits_w");
+  sp.add_workers(scales_w, W, b.scales, true, "scales_w");
+  sp.add(err_s, b.elems, true, "err_s");
+  sp.add(x, b.elems, true, "x");
+  sp.add(m, b.elems, true, "m");
+  sp.add(v_frozen, b.elems, false, "v_frozen");
+  sp.add(bits_s, b.words, true, "bits_s");
+  sp.add(scales_s, b.scales, true, "scales_s");
+  sp.add(status, 4, true, "status");
+  if (int rc = sp.check(__func__)) return rc;
   by_chunk<LaunchAdam>(chunk, n, (int)W, wk, err_s, m, x, v_frozen, bits_s, scales_s,
                        make_coef(*hp), status, (hipStream_t)stream);
   return launch_status(__func__);
@@ -994,6 +1220,21 @@ int onebit_sparse_compressed_step(const onebit_layer_table* table, int32_t W, in
   CHECK_PTR(v_fresh, "v_fresh");
   CHECK_PTR(c_avg, "c_avg");
   CHECK_PTR(vals_s, "vals_s");
+  const Bytes b(table->N, table->chunk);
+  const int64_t vals = 4 * table->K * nsel * 64;
+  Spans sp;
+  sp.add(sel, 4 * table->K, false, "sel");
+  sp.add_workers(grads, W, b.elems, false, "grads");
+  sp.add_workers(err_w, W, b.elems, true, "err_w");
+  sp.add_workers(vals_w, W, vals, true, "vals_w");
+  sp.add(x, b.elems, true, "x");
+  sp.add(m, b.elems, true, "m");
+  sp.add(v_frozen, b.elems, false, "v_frozen");
+  sp.add(v_fresh, b.elems, true, "v_fresh");
+  sp.add(c_avg, 4 * (int64_t)table->L, false, "c_avg");
+  sp.add(vals_s, vals, true, "vals_s");
+  sp.add(status, 4, true, "status");
+  if (int rc = sp.check(__func__)) return rc;
   by_chunk<LaunchSparse>(table->chunk, table, (int)W, (int)nsel, sel, wk, wv, x, m, v_frozen,
                          v_fresh, c_avg, vals_s, make_coef(*hp), status, (hipStream_t)stream);
   return launch_status(__func__);

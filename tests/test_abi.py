@@ -216,3 +216,45 @@ def test_share_entry_point_checks(ob):
     assert lib.onebit_sparse_update(None, 1, P(4096), P(4096), P(4096), P(4096), P(4096), P(4096),
                                     P(4096), hpr, None, None) == ob.ONEBIT_EINVAL
 
+
+
+def test_written_arrays_may_not_overlap(ob):
+    """A written array that overlaps another argument of the call is refused
+    before any launch; read-only arrays may overlap each other."""
+    lib = ob._lib
+    P = ctypes.c_void_p
+    n, C = 8192, 4096                       # 32 KiB of fp32, 2 chunks: 1 KiB of words, 8 B of scales
+    base = 1 << 20
+    inp, err, bits, scales = base, base + 32768, base + 65536, base + 65536 + 1024
+    assert lib.onebit_compress_ef(n, C, P(inp), P(inp + 16384), P(bits), P(scales), None,
+                                  None) == ob.ONEBIT_EINVAL
+    assert "err overlaps in" in ob.onebit_last_error()
+    assert lib.onebit_compress_ef(n, C, P(inp), P(err), P(err + 1020), P(scales), None,
+                                  None) == ob.ONEBIT_EINVAL      # bits starts inside err
+    assert lib.onebit_compress_ef(n, C, P(inp), P(err), P(bits), P(bits + 1020), None,
+                                  None) == ob.ONEBIT_EINVAL      # scales inside bits
+    assert lib.onebit_compress_ef(n, C, P(inp), P(err), P(bits), P(scales), P(scales + 4),
+                                  None) == ob.ONEBIT_EINVAL      # status inside scales
+    assert "status overlaps scales" in ob.onebit_last_error()
+    hp = ob.onebit_hparams(beta1=0.9, beta2=0.999, eta=1e-8, lr=1e-3)
+    hpr = ctypes.byref(hp)
+    # two workers reading one gradient buffer is allowed; writing one error
+    # buffer from both is not
+    g = (P * 2)(inp, inp)
+    e = (P * 2)(err, err)
+    x, m, v = base + 4 * 32768, base + 5 * 32768, base + 6 * 32768
+    assert lib.onebit_adam_warmup_step(n, 2, g, P(x), P(inp), P(v), hpr, None) == \
+        ob.ONEBIT_EINVAL                                          # m is a gradient buffer
+    assert "overlaps grads[0]" in ob.onebit_last_error()
+    args = [g, e, P(base + 7 * 32768), P(x), P(m), P(v), None, None, P(bits), P(scales)]
+    assert lib.onebit_adam_compressed_step(n, C, 2, *args, hpr, None, None) == ob.ONEBIT_EINVAL
+    assert "err_w[1] overlaps err_w[0]" in ob.onebit_last_error()
+    arr = (P * 2)(bits, bits)
+    sc = (P * 2)(scales, scales)
+    assert lib.onebit_average_packed(n, C, 2, arr, sc, P(err), P(bits), P(base + 3 * 32768),
+                                     None, None) == ob.ONEBIT_EINVAL   # output over an input
+    assert "bits_out overlaps bits_w[0]" in ob.onebit_last_error()
+    assert lib.onebit_decompress(n, C, P(bits), P(scales), P(bits - 16), None) == \
+        ob.ONEBIT_EINVAL
+    assert lib.onebit_sparse_average(64, 2, (P * 2)(inp, inp), P(inp + 128), None) == \
+        ob.ONEBIT_EINVAL
