@@ -1,10 +1,12 @@
 """Entry points on a flat buffer of more than 2^31 elements (64-bit element,
 word and chunk indexing): the codec (compress_ef, decompress,
-average_packed), the fused 1-bit Adam step, and one GPU's share of it
-(worker_compress, average_packed, adam_update), each checked against the
-oracle on windows of chunks at the start, across element 2^31 and at the
-ragged end.  Every value compared is chunk-local or element-wise, so the
-oracle computes each window exactly from the same seeded inputs."""
+average_packed), the fused 1-bit Adam step and one GPU's share of it
+(worker_compress, average_packed, adam_update), and the sparse stage fused
+and shared (sparse_worker, sparse_average, sparse_update), each checked
+against the oracle on windows of chunks at the start, across element 2^31
+and at the ragged end.  Every value compared is chunk-local or element-wise
+(the sparse stage's per-tensor coefficient is an input), so the oracle
+computes each window exactly from the same seeded inputs."""
 import numpy as np
 import pytest
 
@@ -186,6 +188,94 @@ def test_adam_fused_and_share_past_2_31():
     ob.onebit_average_packed(N, C, s.W, s.bits_w, s.scales_w, s.err_s, s.bits_s, s.scales_s,
                              s.status)
     ob.onebit_adam_update(N, C, s.bits_s, s.scales_s, s.x, s.m, s.vf, hp)
+    s.check(refs)
+    del s
+    torch.cuda.empty_cache()
+
+
+NSEL = 2                                       # two 64-element blocks per chunk
+
+
+class SparseState:
+    """The sparse stage's state on one tensor of N elements, W = 2, from
+    the seeded generator; the block selection is drawn on the host."""
+    W = 2
+    C_AVG = 1.25
+
+    def __init__(self):
+        self.table = ob.LayerTable([N], C)
+        self.g = [f32() for _ in range(self.W)]
+        self.e = [f32() for _ in range(self.W)]
+        self.x, self.m, self.vf, self.vr = f32(), f32(), f32(), f32()
+        self.vals_w = [f32(K * NSEL * 64) for _ in range(self.W)]
+        self.vals_s = f32(K * NSEL * 64)
+        self.c_avg = torch.full((1,), self.C_AVG, dtype=torch.float32, device="cuda")
+        self.status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        self.sel_h = synth.index_host(np.empty(K, np.int32), SEED, synth.stream_id(synth.SEL), 0,
+                                      C // 64)
+        self.sel = torch.from_numpy(self.sel_h).cuda()
+
+    def fill(self):
+        for w in range(self.W):
+            fill_dev(self.g[w], synth.G, w, 1e-3)
+            fill_dev(self.e[w], synth.G, w, 1e-4, step=1)
+        fill_dev(self.x, synth.X, 0, 0.02)
+        fill_dev(self.m, synth.M, 0, 1e-3)
+        fill_dev(self.vf, synth.V, 0, 0, uniform=True)
+        fill_dev(self.vr, synth.V, 0, 0, step=1, uniform=True)
+
+    def oracle_window(self, k0, k1):
+        lo, hi = span(k0, k1)
+        g = [fill_host(lo, hi, synth.G, w, 1e-3) for w in range(self.W)]
+        e = [fill_host(lo, hi, synth.G, w, 1e-4, step=1) for w in range(self.W)]
+        x = fill_host(lo, hi, synth.X, 0, 0.02)
+        m = fill_host(lo, hi, synth.M, 0, 1e-3)
+        vf = fill_host(lo, hi, synth.V, 0, 0, uniform=True)
+        vr = fill_host(lo, hi, synth.V, 0, 0, step=1, uniform=True)
+        out = oracle.sparse_step([hi - lo], C, NSEL, self.sel_h[k0:k1], g, e, x, m, vf, vr,
+                                 np.array([self.C_AVG], np.float32),
+                                 oracle.hparams(**HPARAMS))
+        out.update(e=e, x=x, m=m, vr=vr)
+        return out
+
+    def check(self, refs):
+        torch.cuda.synchronize()
+        assert int(self.status.item()) == 0
+        per = NSEL * 64
+        for (k0, k1), r in refs.items():
+            lo, hi = span(k0, k1)
+            where = f"chunks [{k0}, {k1})"
+            for w in range(self.W):
+                assert np.array_equal(h(self.vals_w[w], k0 * per, k1 * per).view(np.uint32),
+                                      r["vals_w"][w].view(np.uint32)), where
+                assert np.array_equal(h(self.e[w], lo, hi).view(np.uint32),
+                                      r["e"][w].view(np.uint32)), where
+            assert np.array_equal(h(self.vals_s, k0 * per, k1 * per).view(np.uint32),
+                                  r["vals_s"].view(np.uint32)), where
+            for name in ("x", "m", "vr"):
+                assert np.array_equal(h(getattr(self, name), lo, hi).view(np.uint32),
+                                      r[name].view(np.uint32)), (name, where)
+
+
+def test_sparse_fused_and_share_past_2_31():
+    """The fused sparse step on one tensor of N elements, then the same step
+    rebuilt from the seeds and taken through one GPU's share entry points
+    (each worker's selection, the mean over all transmitted values, the
+    replica's update)."""
+    need_gib(8.4)
+    hp = ob.onebit_hparams(**HPARAMS)
+    s = SparseState()
+    refs = {w: s.oracle_window(*w) for w in WINDOWS}
+    s.fill()
+    ob.onebit_sparse_compressed_step(s.table, s.W, NSEL, s.sel, s.g, s.e, s.x, s.m, s.vf, s.vr,
+                                     s.c_avg, s.vals_w, s.vals_s, hp, s.status)
+    s.check(refs)
+    s.fill()
+    for w in range(s.W):
+        ob.onebit_sparse_worker(N, C, NSEL, s.sel, s.g[w], s.e[w], s.m, s.vals_w[w], hp)
+    ob.onebit_sparse_average(K * NSEL * 64, s.W, s.vals_w, s.vals_s)
+    ob.onebit_sparse_update(s.table, NSEL, s.sel, s.vals_s, s.x, s.m, s.vf, s.vr, s.c_avg, hp,
+                            s.status)
     s.check(refs)
     del s
     torch.cuda.empty_cache()
