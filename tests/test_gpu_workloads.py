@@ -99,3 +99,48 @@ def test_bert_xl_step():
     assert int(d.status.item()) == 0
     del d
     torch.cuda.empty_cache()
+
+
+def test_bert_xl_share_step():
+    """BERT-XL table (2.83e9 parameters, W = 4): one compression step through
+    one GPU's share entry points instead of the fused step -- each worker's
+    compression, the W chunk ranges as server, then one replica's statistics
+    and update, in place on one state -- windows checked against the oracle
+    like the fused step (the windows around the last block lie past element
+    2^31)."""
+    import communication_compressed_optimizer_amd as ob
+    torch.cuda.empty_cache()
+    wl = WORKLOADS["bert_xl"]
+    C, N, K, W = wl.chunk, wl.N, wl.K, wl.W
+    words = K * C // 32
+    free, _ = torch.cuda.mem_get_info()
+    need = wl.N * 4 * (5 + 2 * wl.W) * 1.02 + W * 4 * (words + K)
+    if free < need:
+        pytest.skip(f"needs {need / 2**30:.0f} GiB of device memory, {free / 2**30:.0f} free")
+    d = DevRun(wl, store_worker_bits=False)
+    bits_w = [torch.empty(words, dtype=torch.int32, device="cuda") for _ in range(W)]
+    scales_w = [torch.empty(K, dtype=torch.float32, device="cuda") for _ in range(W)]
+    d.fill_grads(0)
+    for p in range(W):
+        ob.onebit_worker_compress(N, C, d.g[p], d.e[p], d.m, None, None, bits_w[p], scales_w[p],
+                                  d.hp, d.status)
+    for p in range(W):
+        k0, k1 = K * p // W, K * (p + 1) // W
+        lo, hi, w0, w1 = k0 * C, min(k1 * C, N), k0 * C // 32, k1 * C // 32
+        ob.onebit_average_packed(hi - lo, C, W, [b[w0:w1] for b in bits_w],
+                                 [s[k0:k1] for s in scales_w], d.err_s[lo:hi], d.bits_s[w0:w1],
+                                 d.scales_s[k0:k1], d.status)
+    ob.onebit_lamb_rescale_stats(d.table, d.bits_s, d.scales_s, d.m, None, None, d.v, d.vf, d.hp,
+                                 d.ws)
+    ob.onebit_lamb_rescale_update(d.table, d.bits_s, d.scales_s, d.x, d.m, d.v, d.c_avg, d.f_prev,
+                                  d.c_out, d.hp, d.ws, d.status)
+    torch.cuda.synchronize()
+    wins = block_windows(wl, chunks=64)
+    assert wins[-1][1] > 2**31
+    for lo, hi in wins:
+        h = HostRun(wl, lo, hi)
+        h.compressed_step(0)
+        assert_parity(compare_state(d, h), f"window [{lo}, {hi})")
+    assert int(d.status.item()) == 0
+    del d, bits_w, scales_w
+    torch.cuda.empty_cache()
