@@ -65,12 +65,13 @@ def phase1_bytes(N, K, C, W):
 
 
 def adam_bytes(N, K, C, W):
-    """Algorithmic bytes of the fused 1-bit Adam compression kernel: m read
-    and written; per worker g read, e read and written; e_s read and written;
-    v_frozen read; x read and written; (W+1) packed sign arrays and scales
-    written."""
-    packed = (W + 1) * K * (C // 8 + 4)
-    return N * (12 * W + 28) + packed
+    """Algorithmic bytes of one 1-bit Adam compression step, both kernels:
+    the allreduce (m read; per worker g read, e read and written; e_s read
+    and written; (W+1) packed sign arrays and scales written), then the
+    update (the server's packed output read back; x read and written;
+    v_frozen read; m written)."""
+    packed = K * (C // 8 + 4)
+    return N * (12 * W + 12) + (W + 1) * packed + N * 16 + packed
 
 
 def sparse_bytes(N, K, C, W, nsel):
@@ -334,8 +335,9 @@ def main():
 
 def bench_adam(args, wl, ob, torch, hp, g, e, err_s, x, m, v, bits_w, scales_w, bits_s, scales_s,
                status, stream):
-    """The 1-bit Adam mode on the same table, flattened: one fused kernel per
-    compression step (v is the frozen variance)."""
+    """The 1-bit Adam mode on the same table, flattened: one
+    onebit_adam_compressed_step per compression step, i.e. the allreduce
+    kernel and the update kernel (v is the frozen variance)."""
     C, N, W, K = wl.chunk, wl.N, wl.W, wl.K
 
     def step(mm=m):
@@ -360,10 +362,10 @@ def bench_adam(args, wl, ob, torch, hp, g, e, err_s, x, m, v, bits_w, scales_w, 
     ms_per_step, k_ms = timed(m)
     if int(status.item()):
         log(f"[bench] WARNING: status flags {int(status.item())}")
-    log(f"[bench] adam {args.steps} steps: {ms_per_step:.3f} ms/step (kernel {k_ms:.3f} ms)")
+    log(f"[bench] adam {args.steps} steps: {ms_per_step:.3f} ms/step (kernels {k_ms:.3f} ms)")
     pm_ms, pm_k = timed(None)
     log(f"[bench] adam packed momentum {args.steps} steps: {pm_ms:.3f} ms/step "
-        f"(kernel {pm_k:.3f} ms)")
+        f"(kernels {pm_k:.3f} ms)")
     pm_bytes = adam_bytes(N, K, C, W) - 8 * N + K * (C // 8 + 4)
 
     for _ in range(2):
@@ -380,7 +382,7 @@ def bench_adam(args, wl, ob, torch, hp, g, e, err_s, x, m, v, bits_w, scales_w, 
 
     abytes = adam_bytes(N, K, C, W)
     achieved = abytes / (k_ms * 1e-3) / 1e9
-    traffic = _measured_traffic("traffic_adam_compressed_bert_large.txt") \
+    traffic = _measured_traffic("traffic_adam_step_bert_large.txt") \
         if wl.name == "bert_large" else None
     cpu = None
     if args.cpu_chunks > 0:
@@ -414,7 +416,8 @@ def bench_adam(args, wl, ob, torch, hp, g, e, err_s, x, m, v, bits_w, scales_w, 
             "step_bytes": pm_bytes, "GBps": pm_bytes / (pm_k * 1e-3) / 1e9,
             "note": "same step with m = NULL: the momentum is the previous server output, "
                     "outputs bit-identical"},
-        "roofline": {"bound": "hbm", "kernel": "k_adam_compressed<4096>",
+        "roofline": {"bound": "hbm",
+                     "kernel": "k_adam_allreduce<4096> + k_adam_update<4096> (one call)",
                      "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
                      "algorithmic_bytes": abytes},

@@ -285,8 +285,8 @@ constexpr bool kWarm_NT = true;
 // average_packed from 0.554 to 0.535 ms and decompress from 0.247 to 0.240 ms.
 constexpr bool kCodec_NT = true;
 
-// The 1-bit Adam compression kernel shares pass A's compressed allreduce and
-// takes the same settings.
+// The 1-bit Adam allreduce kernel is pass A's compressed allreduce without
+// the rescale statistics and takes the same settings.
 constexpr bool kAdam_NT = true;
 constexpr bool kAdam_PF = false;
 constexpr int kAdam_WPE = 6;
@@ -376,6 +376,8 @@ struct LaunchPassA {
   }
 };
 
+// The 1-bit Adam step: the compressed allreduce, then the update from the
+// server's packed output (the same update kernel as one GPU's share).
 template <int C>
 struct LaunchAdam {
   static void run(int64_t n, int W, const Workers& wk, float* err_s, float* m, float* x,
@@ -383,13 +385,15 @@ struct LaunchAdam {
                   int32_t* status, hipStream_t st) {
     const int64_t K = (n + C - 1) / C;
     if (m)
-      hipLaunchKernelGGL((k_adam_compressed<C, kAdam_NT, kAdam_PF, kAdam_WPE, kAdam_SPT>),
+      hipLaunchKernelGGL((k_adam_allreduce<C, kAdam_NT, kAdam_PF, kAdam_WPE, kAdam_SPT>),
                          dim3((unsigned)K), dim3(Geo<C, kAdam_SPT>::T), 0, st, n / C, n, K, W, wk,
-                         err_s, m, x, v_frozen, bits_s, scales_s, cf, status);
+                         err_s, (const float*)m, bits_s, scales_s, cf, status);
     else
-      hipLaunchKernelGGL((k_adam_compressed<C, kAdam_NT, kAdam_PF, kAdam_WPE, kAdam_SPT, true>),
+      hipLaunchKernelGGL((k_adam_allreduce<C, kAdam_NT, kAdam_PF, kAdam_WPE, kAdam_SPT, true>),
                          dim3((unsigned)K), dim3(Geo<C, kAdam_SPT>::T), 0, st, n / C, n, K, W, wk,
-                         err_s, m, x, v_frozen, bits_s, scales_s, cf, status);
+                         err_s, (const float*)m, bits_s, scales_s, cf, status);
+    launch_chunks<C>(n, st, k_adam_update<C, kAdam_NT>, n, (const uint32_t*)bits_s,
+                     (const float*)scales_s, v_frozen, x, m, cf);
   }
 };
 

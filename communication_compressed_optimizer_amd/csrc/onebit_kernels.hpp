@@ -791,56 +791,46 @@ k_compressed_pass_a(int64_t n_full, DevTable tab, int W, Workers wk, float* __re
                                             seg_f, cf, status, lds, red, dred);
 }
 
-// 1-bit Adam compression step, one pass per chunk: the compressed allreduce,
-// then x = x - lr*(mhat/(sqrt(v_frozen)+eta)) and m = mhat.  There is no
-// layerwise coefficient, so the update follows in the same pass.
+// 1-bit Adam compression step, first pass: the compressed allreduce of each
+// chunk's momentum (every worker, then the server), leaving the server's
+// packed output in bits_s/scales_s.  The update x = x - lr*(mhat/(sqrt(
+// v_frozen)+eta)), m = mhat follows in k_adam_update, which reads that
+// packed output back (C/8 + 4 bytes per chunk).  Interleaved at the
+// BERT-Large size, W = 8, the two passes took 7.50 ms against 7.60 ms for
+// one pass that also updated x and m (7.02 against 7.15 ms with packed
+// momentum), with identical outputs: the single pass held four more
+// streams open per chunk.
 template <int C, bool TAIL, bool NT, bool PF, int SPT, bool PM>
-__device__ __forceinline__ void adam_chunk(int64_t kk, int64_t n, int W, const Workers& wk,
-                                           float* __restrict__ err_s, float* __restrict__ m,
-                                           float* __restrict__ x,
-                                           const float* __restrict__ v_frozen,
-                                           uint32_t* __restrict__ bits_s,
-                                           float* __restrict__ scales_s, const Coef& cf,
-                                           int32_t* status, float4* lds) {
+__device__ __forceinline__ void adam_allreduce_chunk(int64_t kk, int64_t n, int W,
+                                                     const Workers& wk, float* __restrict__ err_s,
+                                                     const float* __restrict__ m,
+                                                     uint32_t* __restrict__ bits_s,
+                                                     float* __restrict__ scales_s, const Coef& cf,
+                                                     int32_t* status, float4* lds) {
   int parity = 0;
   const ChunkAt<C, TAIL> ch(kk, n);
-  SlotsN<SPT> bm, xx, vz;
+  SlotsN<SPT> bm, d0, d1;
   uint32_t nib[SPT];
-  const float s2 = workers_and_server<C, TAIL, NT, PF, SPT, PM>(ch, W, wk, err_s, m, bits_s,
-                                                                scales_s, cf, status, lds, parity,
-                                                                bm, nib, x, v_frozen, xx, vz);
-  if constexpr (!PF) {
-    load_chunk<C, TAIL, NT, SPT>(x, ch.base, ch.nk, xx);
-    load_chunk<C, TAIL, NT, SPT>(v_frozen, ch.base, ch.nk, vz);
-  }
-#pragma unroll
-  for (int a = 0; a < SPT; ++a)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const float mh = signed_scale(nib, a, c, s2);
-      xx[a][c] = xx[a][c] - (cf.lr * (mh / (__builtin_sqrtf(vz[a][c]) + cf.eta)));
-      bm[a][c] = mh;
-    }
-  store_chunk<C, TAIL, NT, SPT>(x, ch.base, ch.nk, xx);
-  if constexpr (!PM) store_chunk<C, TAIL, NT, SPT>(m, ch.base, ch.nk, bm);
+  workers_and_server<C, TAIL, NT, PF, SPT, PM>(ch, W, wk, err_s, m, bits_s, scales_s, cf, status,
+                                               lds, parity, bm, nib, nullptr, nullptr, d0, d1);
 }
 
 // One workgroup per chunk of an n-element buffer; block 0 takes the partial
 // last chunk, if any (as in k_compressed_pass_a).
 template <int C, bool NT = false, bool PF = false, int WPE = 1, int SPT = 4, bool PM = false>
 __global__ void __launch_bounds__((Geo<C, SPT>::T), WPE)
-k_adam_compressed(int64_t n_full, int64_t n, int64_t K, int W, Workers wk,
-                  float* __restrict__ err_s, float* __restrict__ m, float* __restrict__ x,
-                  const float* __restrict__ v_frozen, uint32_t* __restrict__ bits_s,
-                  float* __restrict__ scales_s, Coef cf, int32_t* status) {
+k_adam_allreduce(int64_t n_full, int64_t n, int64_t K, int W, Workers wk,
+                 float* __restrict__ err_s, const float* __restrict__ m,
+                 uint32_t* __restrict__ bits_s, float* __restrict__ scales_s, Coef cf,
+                 int32_t* status) {
   __shared__ float4 lds[2 * Geo<C, SPT>::T];
   const int64_t has_tail = K - n_full;
   if (has_tail && blockIdx.x == 0)
-    adam_chunk<C, true, NT, PF, SPT, PM>(n_full, n, W, wk, err_s, m, x, v_frozen, bits_s, scales_s,
-                                         cf, status, lds);
+    adam_allreduce_chunk<C, true, NT, PF, SPT, PM>(n_full, n, W, wk, err_s, m, bits_s, scales_s,
+                                                   cf, status, lds);
   else
-    adam_chunk<C, false, NT, PF, SPT, PM>((int64_t)blockIdx.x - has_tail, n, W, wk, err_s, m, x,
-                                          v_frozen, bits_s, scales_s, cf, status, lds);
+    adam_allreduce_chunk<C, false, NT, PF, SPT, PM>((int64_t)blockIdx.x - has_tail, n, W, wk,
+                                                    err_s, m, bits_s, scales_s, cf, status, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -1002,7 +992,7 @@ k_rescale_stats(int64_t n_full, DevTable tab, const uint32_t* __restrict__ bits_
 
 // 1-bit Adam on a receiver: x = x - lr*(mhat/(sqrt(v_frozen)+eta)) and
 // m = mhat (m NULL: packed momentum), mhat from the server's packed output
-// (the update half of k_adam_compressed).
+// (the second pass of the 1-bit Adam step, after k_adam_allreduce).
 template <int C, bool TAIL, bool NT>
 __device__ __forceinline__ void adam_update_chunk(int64_t k, int64_t n,
                                                   const uint32_t* __restrict__ bits_s,
