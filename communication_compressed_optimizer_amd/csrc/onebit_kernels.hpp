@@ -1319,20 +1319,29 @@ __device__ __forceinline__ void sparse_update_chunk(int64_t kk, const DevTable& 
   const int64_t per = (int64_t)nsel * 64;
   int pos[4];
   sparse_positions<C>(sel[ch.k], nsel, pos);
+  // mhat: the server's mean on the selection, 0 elsewhere.  The previous
+  // momentum enters only through ghat on the selection, so m is read there
+  // alone (elsewhere it is overwritten with 0 unread).
   Slots bm, mh;
-  load_chunk<C, TAIL, NT>(m, base, nk, bm);
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
     if (pos[a] >= 0) {
-      const float* q = vals_s + ch.k * per + pos[a];
-      const f32x4 v = ld4<NT>(q);
+      const f32x4 v = ld4<NT>(vals_s + ch.k * per + pos[a]);
       mh[a][0] = v.x; mh[a][1] = v.y; mh[a][2] = v.z; mh[a][3] = v.w;
+      const int64_t e0 = base + 4 * (t + T * a);
+      if constexpr (TAIL) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          bm[a][c] = cf.beta1 * (slot_valid<C>(a, c, nk) ? m[e0 + c] : 0.0f);
+      } else {
+        const f32x4 mv = ld4<NT>(m + e0);
+        bm[a][0] = cf.beta1 * mv.x; bm[a][1] = cf.beta1 * mv.y;
+        bm[a][2] = cf.beta1 * mv.z; bm[a][3] = cf.beta1 * mv.w;
+      }
     } else {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) mh[a][c] = 0.0f;
+      for (int c = 0; c < 4; ++c) mh[a][c] = bm[a][c] = 0.0f;
     }
-#pragma unroll
-    for (int c = 0; c < 4; ++c) bm[a][c] = cf.beta1 * bm[a][c];
   }
   const int l0 = tab.l0[ch.k];
   const int l1 = tab.l1[ch.k];
