@@ -443,6 +443,73 @@ def share_bytes(N, K, C, W):
             "stats": 16 * N + pk, "update": 16 * N + pk}
 
 
+def _time_calls(torch, stream, fns, reps):
+    """Average HIP-event time of each call in fns, run in order reps times
+    (after two untimed rounds)."""
+    for _ in range(2):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(reps)]
+    for ev in evs:
+        ev[0].record(stream)
+        for j, f in enumerate(fns):
+            f()
+            ev[j + 1].record(stream)
+    torch.cuda.synchronize()
+    return [sum(ev[j].elapsed_time(ev[j + 1]) for ev in evs) / reps for j in range(len(fns))]
+
+
+def _other_shares(wl, ob, torch, table, hp, g, e, err_s, x, m, v, vf, bits_w, scales_w, bits_s,
+                  scales_s, c_avg, status, stream, reps):
+    """Context for the share bench: one GPU's share of a W-GPU 1-bit Adam
+    step (its worker, 1/W of the chunks as server, onebit_adam_update) and
+    of a sparse-stage step (onebit_sparse_worker, onebit_sparse_average on
+    its range of transmitted values, onebit_sparse_update; one 64-element
+    block of 64 per chunk), on the same buffers."""
+    C, N, W, K = wl.chunk, wl.N, wl.W, wl.K
+    ks = -(-K // W)
+    n_s = min(ks * C, N)
+    wq = ks * C // 32
+    pk = K * (C // 8 + 4)
+    pk_s = ks * (C // 8 + 4)
+    worker = lambda: ob.onebit_worker_compress(N, C, g[0], e[0], m, None, None, bits_w[0],  # noqa
+                                               scales_w[0], hp, status, stream)
+    server = lambda: ob.onebit_average_packed(n_s, C, W, [b[:wq] for b in bits_w],  # noqa
+                                              [s_[:ks] for s_ in scales_w], err_s[:n_s],
+                                              bits_s[:wq], scales_s[:ks], status, stream)
+    update = lambda: ob.onebit_adam_update(N, C, bits_s, scales_s, x, m, v, hp, stream)  # noqa
+    t = _time_calls(torch, stream, [worker, server, update], reps)
+    a_by = {"worker": 16 * N + pk, "server": (W + 1) * pk_s + 8 * n_s, "update": 16 * N + pk}
+    a_ms = dict(zip(("worker", "server", "update"), t))
+    adam = {"ms_per_step": sum(t), "kernel_ms": a_ms, "kernel_bytes": a_by,
+            "GBps": sum(a_by.values()) / (sum(t) * 1e-3) / 1e9}
+    log(f"[bench] adam share: {sum(t):.3f} ms/step (" +
+        ", ".join(f"{k} {a_ms[k]:.3f}" for k in a_ms) + " ms)")
+    per = 64                                  # one block of 64 transmitted per chunk
+    sel = torch.from_numpy(wl.selection(0)).cuda()
+    vals_w = [torch.zeros(K * per, dtype=torch.float32, device="cuda") for _ in range(W)]
+    vals_s = torch.zeros(K * per, dtype=torch.float32, device="cuda")
+    for w in range(1, W):                     # the other workers' values, filled once
+        ob.onebit_sparse_worker(N, C, 1, sel, g[w], e[w], m, vals_w[w], hp, stream)
+    s_worker = lambda: ob.onebit_sparse_worker(N, C, 1, sel, g[0], e[0], m, vals_w[0], hp,  # noqa
+                                               stream)
+    s_server = lambda: ob.onebit_sparse_average(ks * per, W, [t_[:ks * per] for t_ in vals_w],  # noqa
+                                                vals_s[:ks * per], stream)
+    s_update = lambda: ob.onebit_sparse_update(table, 1, sel, vals_s, x, m, v, vf, c_avg, hp,  # noqa
+                                               status, stream)
+    t = _time_calls(torch, stream, [s_worker, s_server, s_update], reps)
+    f = per / C
+    s_by = {"worker": int(16 * N + 4 * f * N + 4 * K), "server": 4 * (W + 1) * ks * per,
+            "update": int(4 * N + 28 * f * N + 4 * K)}
+    s_ms = dict(zip(("worker", "server", "update"), t))
+    sparse = {"ms_per_step": sum(t), "kernel_ms": s_ms, "kernel_bytes": s_by,
+              "GBps": sum(s_by.values()) / (sum(t) * 1e-3) / 1e9}
+    log(f"[bench] sparse share: {sum(t):.3f} ms/step (" +
+        ", ".join(f"{k} {s_ms[k]:.3f}" for k in s_ms) + " ms)")
+    return adam, sparse
+
+
 def bench_share(args, wl, ob, torch, table, hp, g, e, err_s, x, m, v, vf, bits_w, scales_w,
                 bits_s, scales_s, c_avg, f_prev, c_out, ws, status, stream):
     """One GPU's share of a W-GPU 1-bit LAMB compression step at its real
@@ -496,6 +563,9 @@ def bench_share(args, wl, ob, torch, table, hp, g, e, err_s, x, m, v, vf, bits_w
         ", ".join(f"{nm} {k_ms[nm]:.3f}" for nm in names) + " ms)")
     by = share_bytes(N, K, C, W)
     sbytes = sum(by.values())
+    adam_share, sparse_share = _other_shares(wl, ob, torch, table, hp, g, e, err_s, x, m, v, vf,
+                                             bits_w, scales_w, bits_s, scales_s, c_avg, status,
+                                             stream, args.steps)
     achieved = by["worker"] / (k_ms["worker"] * 1e-3) / 1e9
     step_gbps = sbytes / (ms_per_step * 1e-3) / 1e9
     traffic = _measured_traffic("traffic_worker_compress_bert_large.txt") \
@@ -523,6 +593,8 @@ def bench_share(args, wl, ob, torch, table, hp, g, e, err_s, x, m, v, vf, bits_w
         "step_bytes": sbytes,
         "kernel_ms": k_ms,
         "kernel_bytes": by,
+        "adam_share": adam_share,
+        "sparse_share": sparse_share,
         "roofline": {"bound": "hbm", "kernel": "k_worker_compress<4096>",
                      "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
