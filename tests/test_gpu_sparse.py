@@ -104,3 +104,36 @@ def test_sparse_bert_large_windows():
             assert_parity(compare_sparse(d, h), f"step {step} window [{h.lo}, {h.hi})")
     del d
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("nsel", [1, 7])
+def test_sparse_update_reads_momentum_on_the_selection_only(nsel):
+    """onebit_sparse_update needs the previous momentum only where a block
+    was transmitted: with m set to NaN everywhere else, every output is the
+    same bit for bit (m ends 0 there either way)."""
+    wl = Workload("sparse", RAGGED, W=2, init="frozen")
+    C, K, N = wl.chunk, wl.K, wl.N
+    d = DevRun(wl)
+    sel_h = wl.selection(0)
+    sel = torch.from_numpy(sel_h).cuda()
+    vals = torch.randn(K * nsel * 64, device="cuda") * 1e-3
+    on = np.zeros(K * C, bool)                       # the selection, chunk by chunk
+    for k in range(K):
+        b0 = int(sel_h[k]) % (C // 64)
+        for j in range(nsel):
+            b = (b0 + j) % (C // 64)
+            on[k * C + b * 64:k * C + (b + 1) * 64] = True
+    on = torch.from_numpy(on[:N]).cuda()
+    outs = []
+    for poison in (False, True):
+        x, m, vf = d.x.clone(), d.m.clone(), d.vf.clone()
+        if poison:
+            m[~on] = float("nan")
+        status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        ob.onebit_sparse_update(d.table, nsel, sel, vals, x, m, d.v, vf, d.c_avg, d.hp, status)
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0
+        outs.append((x, m, vf))
+    for a, b in zip(*outs):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    assert not torch.any(outs[1][1][~on])                 # m is 0 off the selection
