@@ -270,13 +270,9 @@ void launch_chunks(int64_t n, hipStream_t st, KF k, A... args) {
 // worker iteration, so the best cap depends on where they land; prefetching
 // the next worker, keeping beta1*m in LDS, or keeping the workers' signs in
 // LDS and summing after the loop (no spills, 3.5% slower) did not help).
-// Re-swept later (caps 6 and 7, three boxes, interleaved): with fp32
-// momentum the 7-wave cap was ahead on every box (by 1.1%, 0.1% and 0.4%),
-// with packed momentum the 6-wave cap on two of three.
 constexpr bool kPassA_NT = true;   // streaming loads and stores
 constexpr bool kPassA_PF = false;  // next-worker prefetch
-constexpr int kPassA_WPE = 7;      // minimum waves per SIMD, fp32 momentum
-constexpr int kPassA_WPE_PM = 6;   // the same, packed momentum
+constexpr int kPassA_WPE = 6;      // minimum waves per SIMD
 constexpr int kPassA_SPT = 4;      // float4 slots per thread (workgroup = C / (4 * SPT))
 constexpr bool kPassB_NT = true;
 // LAMB warmup passes (BERT-Large, W = 8, interleaved on one box): streaming
@@ -374,8 +370,7 @@ struct LaunchPassA {
                  const float* m, const float* v_frozen, float* v_fresh, uint32_t* bits_s,
                  float* scales_s, const Coef& cf, const Ws& ws, int32_t* status, hipStream_t st) {
     hipLaunchKernelGGL(
-        (k_compressed_pass_a<C, kPassA_NT, kPassA_PF, PM ? kPassA_WPE_PM : kPassA_WPE, kPassA_SPT,
-                             RN, PM>),
+        (k_compressed_pass_a<C, kPassA_NT, kPassA_PF, kPassA_WPE, kPassA_SPT, RN, PM>),
         dim3((unsigned)t->K), dim3(Geo<C, kPassA_SPT>::T), 0, st, t->N / C, t->dev, W, wk, err_s, m,
         v_frozen, v_fresh, bits_s, scales_s, ws.seg_max, ws.seg_x, ws.seg_u, cf, status);
   }
