@@ -13,9 +13,12 @@
 #include <vector>
 
 #include "onebit.h"
+#include "onebit_host.hpp"
 #include "onebit_kernels.hpp"
 
 using namespace onebit;
+
+static_assert(onebit::kMaxWorkers == onebit_host::kMaxWorkers, "one worker bound");
 
 struct onebit_layer_table {
   int32_t L = 0;
@@ -30,29 +33,17 @@ struct onebit_layer_table {
 
 namespace {
 
-thread_local std::string g_last_error;
-
-int fail(int code, const char* fmt, ...) {
-  char buf[512];
-  va_list ap;
-  va_start(ap, fmt);
-  vsnprintf(buf, sizeof buf, fmt, ap);
-  va_end(ap);
-  g_last_error = buf;
-  return code;
-}
-
-int ok() {
-  g_last_error.clear();
-  return ONEBIT_OK;
-}
-
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
-
-bool chunk_supported(int32_t c) { return c >= 1024 && c <= 16384 && (c & (c - 1)) == 0; }
-
-size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
+using onebit_host::aligned16;
+using onebit_host::aligned4;
+using onebit_host::Bytes;
+using onebit_host::check_hparams;
+using onebit_host::check_n;
+using onebit_host::check_W;
+using onebit_host::chunk_supported;
+using onebit_host::fail;
+using onebit_host::kMaxChunks;
+using onebit_host::ok;
+using onebit_host::Spans;
 
 // Checks a device array pointer argument.
 #define CHECK_PTR(p, name)                                                                   \
@@ -113,22 +104,6 @@ Coef make_coef(const onebit_hparams& h) {
   return c;
 }
 
-// allow_wd: weight decay is a variant of the LAMB entry points only.
-int check_hparams(const onebit_hparams* hp, const char* fn, bool allow_wd = true) {
-  if (!hp) return fail(ONEBIT_EINVAL, "%s: hp is NULL", fn);
-  if (!std::isfinite(hp->weight_decay) || hp->weight_decay < 0.0f)
-    return fail(ONEBIT_EINVAL, "%s: weight_decay must be finite and >= 0", fn);
-  if (!allow_wd && hp->weight_decay != 0.0f)
-    return fail(ONEBIT_EUNSUPPORTED, "%s: weight_decay must be 0 in the 1-bit Adam mode", fn);
-  if (hp->rho_mode != ONEBIT_RHO_MAX && hp->rho_mode != ONEBIT_RHO_NORM_RATIO)
-    return fail(ONEBIT_EINVAL, "%s: rho_mode %d is not ONEBIT_RHO_MAX or ONEBIT_RHO_NORM_RATIO", fn,
-                hp->rho_mode);
-  if (!(hp->c_avg_decay >= 0.0f && hp->c_avg_decay < 1.0f))
-    return fail(ONEBIT_EINVAL, "%s: c_avg_decay must be in [0, 1)", fn);
-  if (hp->bias_step < 0) return fail(ONEBIT_EINVAL, "%s: bias_step < 0", fn);
-  return ONEBIT_OK;
-}
-
 // A table's device block lives on one device; a call made with another
 // device current would hand its kernels a foreign address.
 int check_table(const onebit_layer_table* t, const char* fn) {
@@ -142,83 +117,7 @@ int check_table(const onebit_layer_table* t, const char* fn) {
   return ONEBIT_OK;
 }
 
-// Chunk counts beyond this are refused (launch grids are 32-bit).
-constexpr int64_t kMaxChunks = INT32_MAX / 2;
-
-int check_n(int64_t n, int64_t chunk, const char* fn) {
-  if (n < 0) return fail(ONEBIT_EINVAL, "%s: n < 0", fn);
-  if ((n + chunk - 1) / chunk > kMaxChunks) return fail(ONEBIT_EUNSUPPORTED, "%s: n too large", fn);
-  return ONEBIT_OK;
-}
-
-int check_W(int32_t W, const char* fn) {
-  if (W < 1 || W > kMaxWorkers)
-    return fail(ONEBIT_EUNSUPPORTED, "%s: W = %d outside [1, %d]", fn, W, kMaxWorkers);
-  return ONEBIT_OK;
-}
-
-// Byte ranges of one call's device arrays.  The kernels access them through
-// restrict-qualified pointers, so an array the call writes must not overlap
-// any other array of the call; read-only arrays may overlap each other (one
-// gradient buffer passed for several workers, say).
-class Spans {
- public:
-  void add(const void* p, int64_t bytes, bool written, const char* name, int idx = -1) {
-    if (!p || bytes <= 0 || n_ == kCap) return;
-    s_[n_++] = {reinterpret_cast<uintptr_t>(p), (uintptr_t)bytes, written, name, idx};
-  }
-  // Every array of W workers, given as a host array of pointers (or NULL).
-  template <typename T>
-  void add_workers(T const* arr, int W, int64_t bytes, bool written, const char* name) {
-    if (arr)
-      for (int w = 0; w < W; ++w) add(arr[w], bytes, written, name, w);
-  }
-  int check(const char* fn) const {
-    for (int i = 0; i < n_; ++i)
-      for (int j = i + 1; j < n_; ++j) {
-        const S& a = s_[i];
-        const S& b = s_[j];
-        if ((a.w || b.w) && a.p < b.p + b.bytes && b.p < a.p + a.bytes) {
-          const S& wr = b.w ? b : a;  // the written one is named first
-          const S& other = b.w ? a : b;
-          return fail(ONEBIT_EINVAL, "%s: %s overlaps %s", fn, label(wr).c_str(),
-                      label(other).c_str());
-        }
-      }
-    return ONEBIT_OK;
-  }
-
- private:
-  struct S {
-    uintptr_t p, bytes;
-    bool w;
-    const char* name;
-    int idx;
-  };
-  static std::string label(const S& s) {
-    return s.idx < 0 ? std::string(s.name) : std::string(s.name) + "[" + std::to_string(s.idx) + "]";
-  }
-  // four worker arrays of up to kMaxWorkers entries plus a dozen others
-  static constexpr int kCap = 4 * kMaxWorkers + 16;
-  S s_[kCap];
-  int n_ = 0;
-};
-
-// Bytes of a buffer's arrays: n elements in chunks of `chunk`.
-struct Bytes {
-  int64_t elems, words, scales;
-  Bytes(int64_t n, int64_t chunk) {
-    const int64_t K = (n + chunk - 1) / chunk;
-    elems = 4 * n;
-    words = 4 * (K * chunk / 32);
-    scales = 4 * K;
-  }
-};
-
-// Workspace layout: [seg_x: S doubles][seg_u: S doubles][c_layer: L floats].
-// The warmup keeps the per-segment sums of x^2 and u^2 there; the
-// compression step reuses the first S floats as seg_max, or (norm-ratio
-// rescale) seg_x and seg_u for the sums of (sqrt(v)+eta)^2.
+// Device views of the workspace (layout in onebit_host::ws_offsets).
 struct Ws {
   double* seg_x;
   double* seg_u;
@@ -226,17 +125,16 @@ struct Ws {
   float* c_layer;
 };
 
-size_t ws_bytes(const onebit_layer_table* t) {
-  return 2 * round256(sizeof(double) * (size_t)t->S) + round256(sizeof(float) * (size_t)t->L);
-}
+size_t ws_bytes(const onebit_layer_table* t) { return onebit_host::ws_bytes(t->S, t->L); }
 
 Ws ws_view(const onebit_layer_table* t, void* ws) {
   char* p = static_cast<char*>(ws);
+  const onebit_host::WsOffsets o = onebit_host::ws_offsets(t->S);
   Ws w;
-  w.seg_x = reinterpret_cast<double*>(p);
-  w.seg_u = reinterpret_cast<double*>(p + round256(sizeof(double) * (size_t)t->S));
-  w.seg_max = reinterpret_cast<float*>(p);
-  w.c_layer = reinterpret_cast<float*>(p + 2 * round256(sizeof(double) * (size_t)t->S));
+  w.seg_x = reinterpret_cast<double*>(p + o.seg_x);
+  w.seg_u = reinterpret_cast<double*>(p + o.seg_u);
+  w.seg_max = reinterpret_cast<float*>(p + o.seg_max);
+  w.c_layer = reinterpret_cast<float*>(p + o.c_layer);
   return w;
 }
 
@@ -564,7 +462,7 @@ int check_phase2(const char* fn, const onebit_layer_table* table, const uint32_t
 
 extern "C" {
 
-const char* onebit_last_error(void) { return g_last_error.c_str(); }
+const char* onebit_last_error(void) { return onebit_host::last_error_slot().c_str(); }
 
 const char* onebit_version(void) { return "onebit 0.1 (gfx950)"; }
 
@@ -572,45 +470,19 @@ int onebit_layer_table_create(const int64_t* numels, int32_t L, int32_t chunk,
                               onebit_layer_table** out) {
   if (!numels || !out) return fail(ONEBIT_EINVAL, "%s: NULL argument", __func__);
   *out = nullptr;
-  if (L < 1) return fail(ONEBIT_EINVAL, "%s: L = %d < 1", __func__, L);
-  if (!chunk_supported(chunk))
-    return fail(ONEBIT_EUNSUPPORTED, "%s: chunk %d is not a power of two in [1024, 16384]",
-                __func__, chunk);
-  std::vector<int64_t> off((size_t)L + 1, 0);
-  const int64_t max_n = kMaxChunks * chunk;
-  for (int32_t l = 0; l < L; ++l) {
-    if (numels[l] < 1) return fail(ONEBIT_EINVAL, "%s: numels[%d] = %lld < 1", __func__, l,
-                                   (long long)numels[l]);
-    // bounded before the add, so the running sum cannot overflow
-    if (numels[l] > max_n - off[l])
-      return fail(ONEBIT_EUNSUPPORTED, "%s: too many chunks", __func__);
-    off[l + 1] = off[l] + numels[l];
-  }
-  const int64_t N = off[L];
-  const int64_t K = (N + chunk - 1) / chunk;
+  int64_t N = 0, K = 0;
+  if (int rc = onebit_host::table_sizes(numels, L, chunk, &N, &K, __func__)) return rc;
   int device = -1;
   if (hipError_t e = hipGetDevice(&device); e != hipSuccess)
     return fail(ONEBIT_EHIP, "%s: hipGetDevice: %s", __func__, hipGetErrorString(e));
-  std::vector<int32_t> l0((size_t)K), l1((size_t)K), seg((size_t)K), lseg((size_t)L + 1);
-  int64_t S = 0;
-  int32_t l = 0;
-  for (int64_t k = 0; k < K; ++k) {
-    const int64_t first = k * chunk;
-    const int64_t last = (k + 1) * chunk < N ? (k + 1) * chunk - 1 : N - 1;
-    while (off[l + 1] <= first) ++l;
-    l0[k] = l;
-    int32_t e = l;
-    while (off[e + 1] <= last) ++e;
-    l1[k] = e;
-    seg[k] = (int32_t)S;
-    S += e - l + 1;
-  }
-  if (S > INT32_MAX) return fail(ONEBIT_EUNSUPPORTED, "%s: too many segments", __func__);
-  for (int32_t t = 0; t < L; ++t) {
-    const int64_t k = off[t] / chunk;
-    lseg[t] = seg[k] + (t - l0[k]);
-  }
-  lseg[L] = (int32_t)S;
+  onebit_host::HostTable ht;
+  if (int rc = onebit_host::build_table(numels, L, chunk, ht, __func__)) return rc;
+  const std::vector<int64_t>& off = ht.off;
+  const std::vector<int32_t>& l0 = ht.l0;
+  const std::vector<int32_t>& l1 = ht.l1;
+  const std::vector<int32_t>& seg = ht.seg;
+  const std::vector<int32_t>& lseg = ht.lseg;
+  const int64_t S = ht.S;
 
   onebit_layer_table* t = new (std::nothrow) onebit_layer_table();
   if (!t) return fail(ONEBIT_ENOMEM, "%s: host allocation failed", __func__);
@@ -620,6 +492,7 @@ int onebit_layer_table_create(const int64_t* numels, int32_t L, int32_t chunk,
   t->K = K;
   t->S = S;
   t->device = device;
+  using onebit_host::round256;
   const size_t b_off = round256(sizeof(int64_t) * ((size_t)L + 1));
   const size_t b_k = round256(sizeof(int32_t) * (size_t)K);
   const size_t b_l = round256(sizeof(int32_t) * ((size_t)L + 1));

@@ -344,10 +344,18 @@ __device__ __forceinline__ float compress_slots(SlotsN<SPT>& z, int nk, float4* 
 // ---------------------------------------------------------------------------
 // block reductions for per-tensor statistics (fixed order: deterministic)
 // ---------------------------------------------------------------------------
+// Maximum that propagates NaN: the result is NaN when either operand is,
+// else the larger one.  Commutative and associative, so every reduction
+// order gives the same value (a rescale ratio that is NaN anywhere in a
+// tensor makes its factor NaN, and the status bit reports it).
+__device__ __forceinline__ float max_nan(float a, float b) {
+  return (a != a) ? a : ((b != b) ? b : fmaxf(a, b));
+}
+
 template <int T>
 __device__ __forceinline__ float block_max(float v, float* red) {
 #pragma unroll
-  for (int s = 32; s >= 1; s >>= 1) v = fmaxf(v, __shfl_xor(v, s, 64));
+  for (int s = 32; s >= 1; s >>= 1) v = max_nan(v, __shfl_xor(v, s, 64));
   if constexpr (T / 64 == 1) {
     return v;
   } else {
@@ -355,7 +363,7 @@ __device__ __forceinline__ float block_max(float v, float* red) {
     __syncthreads();
     float r = red[0];
 #pragma unroll
-    for (int w = 1; w < T / 64; ++w) r = fmaxf(r, red[w]);
+    for (int w = 1; w < T / 64; ++w) r = max_nan(r, red[w]);
     __syncthreads();
     return r;
   }
@@ -396,7 +404,8 @@ __device__ __forceinline__ int tensor_of(const DevTable& tab, int l0, int l1, in
   return l;
 }
 
-// Per-(chunk, tensor) maximum of q over the chunk's valid elements.
+// Per-(chunk, tensor) maximum of q over the chunk's valid elements (NaN if
+// any of them is NaN).
 template <int C, int SPT = 4>
 __device__ __forceinline__ void segment_max(const DevTable& tab, int64_t k, int64_t base, int nk,
                                             const SlotsN<SPT>& q, float* red, float* __restrict__ seg_max) {
@@ -413,7 +422,7 @@ __device__ __forceinline__ void segment_max(const DevTable& tab, int64_t k, int6
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int j = 4 * ((int)threadIdx.x + T * a) + c;
-        if (j < nk && j >= lo && j < hi) mx = fmaxf(mx, q[a][c]);
+        if (j < nk && j >= lo && j < hi) mx = max_nan(mx, q[a][c]);
       }
     mx = block_max<T>(mx, red);
     if (threadIdx.x == 0) seg_max[sb + (l - l0)] = mx;
@@ -1447,7 +1456,7 @@ k_rescale_finalize(DevTable tab, const float* __restrict__ seg_max, const double
     mx = (Z == 0.0 || F == 0.0) ? 1.0f : (float)(__builtin_sqrt(Z) / __builtin_sqrt(F));
   } else {
     mx = -__builtin_inff();
-    for (int i = lo + (int)threadIdx.x; i < hi; i += TB) mx = fmaxf(mx, seg_max[i]);
+    for (int i = lo + (int)threadIdx.x; i < hi; i += TB) mx = max_nan(mx, seg_max[i]);
     mx = block_max<TB>(mx, red);
   }
   if (threadIdx.x == 0) {

@@ -40,7 +40,10 @@
  *   C7  ghat_i = (mhat_i (-) (beta1 (*) m_i)) (/) a1     reconstructed gradient
  *   C8  vf_i = (beta2 (*) vf_i) (+) (a2 (*) (ghat_i (*) ghat_i))
  *   C9  q_i = (sqrt(v_frozen,i) (+) eta) (/) (sqrt(vf_i) (+) eta);
- *       rho_l = max over the tensor's elements of q_i
+ *       rho_l = max over the tensor's elements of q_i (NaN if any q_i is
+ *       NaN: a sign cannot encode an undefined value, so such a tensor has
+ *       no defined factor; C10's fminf then drops it and f is clamped by
+ *       f_max and kp (*) f_prev alone)
  *   C10 f = min(rho_l, f_max, kp (*) f_prev_l); f = max(f, f_min, km (*) f_prev_l);
  *       f_prev_l = f; c_l = c_avg_l (*) f          stabilized soft thresholds
  *   C11 x_i = x_i (-) ((gamma (*) c_l) (*) (mhat_i (/) (sqrt(v_frozen,i) (+) eta)));
@@ -320,7 +323,10 @@ void oracle_compressed_step(int32_t L, const int64_t* numels, int32_t C, int32_t
       const float ghat = (mhat[i] - (hp->beta1 * m[i])) / a1;
       v_fresh[i] = (hp->beta2 * v_fresh[i]) + (a2 * (ghat * ghat));
       const float q = (sqrtf(v_frozen[i]) + hp->eta) / (sqrtf(v_fresh[i]) + hp->eta);
-      r = (i == off || q > r) ? q : r;
+      /* the maximum of a set holding an undefined ratio is undefined: one
+       * NaN anywhere in the tensor makes rho_l NaN (q > NaN is false, so
+       * once r is NaN it stays NaN) */
+      r = (i == off || isnan(q) || q > r) ? q : r;
       const double dz = (double)(sqrtf(v_frozen[i]) + hp->eta);
       const double df = (double)(sqrtf(v_fresh[i]) + hp->eta);
       Qz += dz * dz;

@@ -506,6 +506,43 @@ def test_status_flags_from_steps():
     assert st & ob.ONEBIT_STATUS_NONFINITE_WORKER and st & ob.ONEBIT_STATUS_NONFINITE_SERVER
 
 
+def test_nan_ratio_rule_matches_oracle():
+    """A NaN rescale ratio (here a NaN frozen variance) at a tensor's first
+    element, in the middle of another and at the last element of a third.
+    Both sides make those tensors' rho NaN (one NaN anywhere, reading R13),
+    so their f is clamped from f_prev alone (kp); the other tensors keep
+    f = rho = their maximum ratio, below kp here because v_frozen = v_fresh
+    = 1 puts every ratio near 1/sqrt(beta2).  The status bit is set, x is
+    NaN at exactly those elements, and every other value meets the bar."""
+    numels = RAGGED[0]
+    wl = _ragged_workload(numels, 3)
+    d, h = DevRun(wl), HostRun(wl)
+    for run in (d, h):
+        run.v[:] = 1.0
+        run.vf[:] = 1.0
+    off = wl.offsets
+    idx = [int(off[2]), int(off[3]) + numels[3] // 2, int(off[6]) - 1]
+    for i in idx:
+        d.v[i] = float("nan")
+        h.v[i] = np.nan
+    d.compressed_step(0)
+    h.compressed_step(0)
+    torch.cuda.synchronize()
+    dd = d.window(0, wl.N)
+    nan_d, nan_h = np.isnan(dd["x"]), np.isnan(h.x)
+    assert np.array_equal(nan_d, nan_h) and sorted(np.flatnonzero(nan_h)) == idx
+    dd["x"] = np.where(nan_d, np.float32(0), dd["x"]).astype(np.float32)
+    h.x[nan_h] = 0.0
+    assert_parity(compare_state(d, h, dd), "NaN ratios")
+    kp = np.float32(1) + np.float32(HPARAMS["kappa"])
+    for l in range(len(numels)):
+        if l in (2, 3, 5):
+            assert dd["f_prev"][l] == kp and h.f_prev[l] == kp, l
+        else:
+            assert 1.0 < dd["f_prev"][l] < kp, (l, dd["f_prev"][l])
+    assert int(d.status.item()) & ob.ONEBIT_STATUS_NONFINITE_RHO
+
+
 def test_binding_rejects_bad_arguments():
     n, C = 4096, 4096
     a = torch.zeros(n + 4, dtype=torch.float32, device="cuda")

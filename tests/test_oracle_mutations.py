@@ -93,7 +93,8 @@ MUTATIONS = {
     "floor_uses_kp": ("f = fmaxf(fmaxf(f, hp->f_min), km * f_prev[l]);",
                       "f = fmaxf(fmaxf(f, hp->f_min), kp * f_prev[l]);"),
     "f_prev_not_updated": ("    f_prev[l] = f;\n", ""),
-    "rho_min_not_max": ("r = (i == off || q > r) ? q : r;", "r = (i == off || q < r) ? q : r;"),
+    "rho_min_not_max": ("r = (i == off || isnan(q) || q > r) ? q : r;",
+                        "r = (i == off || isnan(q) || q < r) ? q : r;"),
     "norm_ratio_zero_guard": ("r = (Qz == 0.0 || Qf == 0.0) ? 1.0f :", "r = (Qz == 0.0 || Qf == 0.0) ? 0.0f :"),
     "decompress_sign_inverted": (
         "out[base + j] = sign_bit(bits, C, k, j) ? scales[k] : -scales[k];",
@@ -121,6 +122,10 @@ MUTATIONS = {
         "        x[i] = x[i] - (step * (mhat[i] / (sqrtf(v_frozen[i]) + hp->eta)));\n      m[i] = mhat[i];\n",
         "        x[i] = x[i] - (step * (m[i] / (sqrtf(v_frozen[i]) + hp->eta)));\n      m[i] = mhat[i];\n"),
     "freeze_v_fresh_not_copied": ("  for (int64_t i = 0; i < N; ++i) v_fresh[i] = v[i];\n", ""),
+    "rho_drops_later_nan": ("r = (i == off || isnan(q) || q > r) ? q : r;",
+                            "r = (i == off || q > r) ? q : r;"),
+    "rho_drops_every_nan": ("r = (i == off || isnan(q) || q > r) ? q : r;",
+                            "r = (i == off || q > r || isnan(r)) ? q : r;"),
 }
 
 

@@ -772,6 +772,26 @@ def test_p21_norm_ratio_factor():
     assert abs(out2["c"][1] / q[4096:8192].max() - 1) <= 8 * U
 
 
+# P27 a NaN rescale ratio anywhere in a tensor makes rho_l NaN (reading R13:
+#     one sign bit cannot encode an undefined value, so the tensor has no
+#     defined factor).  C10's fminf then drops it, so f is the clamp of
+#     f_prev alone: max(min(f_max, kp*f_prev), f_min, km*f_prev) = kp here.
+#     A tensor without NaN keeps f = rho = its exact maximum ratio.
+@pytest.mark.parametrize("where", [0, 1, 1234, 4094, 4095])
+def test_p27_nan_ratio_makes_rho_nan(where):
+    numels = [4096, 4096]
+    N = sum(numels)
+    vfz = np.full(N, 1e-6, np.float32)
+    vf = np.full(N, 1e-6, np.float32)
+    vfz[where] = np.nan                            # q is NaN at one element of tensor 0
+    out = _run_zero_ghat_hp(numels, vfz, vf, hp(eta=0.0))
+    kp = np.float32(1.0) + np.float32(0.1)
+    assert out["c"][0] == kp                       # c_avg = f_prev = 1
+    # tensor 1: every q = sqrt(1e-6) / sqrt(0.999 * 1e-6) in fp32, inside the thresholds
+    q = np.sqrt(np.float32(1e-6)) / np.sqrt(np.float32(0.999) * np.float32(1e-6))
+    assert 1.0 < q < kp and out["c"][1] == q
+
+
 # ---------------------------------------------------------------------------
 # SLAMB-style sparse compression stage
 # ---------------------------------------------------------------------------
