@@ -112,9 +112,80 @@ def _ceiling(torch, stream, achieved):
                     "not an upper bound (a tuned streaming copy runs faster)"}
 
 
-def cpu_baseline(wl, n_chunks, method="lamb", nsel=1):
+def _ceiling_lib():
+    import ctypes
+    path = os.path.join(ROOT, "communication_compressed_optimizer_amd", "libonebit_ceiling.so")
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    lib.onebit_ceiling_read.argtypes = [ctypes.c_int64, P, P, P]
+    lib.onebit_ceiling_copy.argtypes = [ctypes.c_int64, P, P, P]
+    lib.onebit_ceiling_phase1.argtypes = [ctypes.c_int64, ctypes.c_int32, P, P, P, P, P, P, P, P,
+                                          ctypes.c_uint32, P]
+    return lib
+
+
+def pattern_ceiling(torch, stream, wl, g, e, err_s, m, v, vf, bits_w, bits_s, achieved,
+                    reps=10):
+    """The box's practical ceiling, measured in the same run on the step's own
+    buffers by pure-traffic kernels with the step's loads, stores and launch
+    shape (libonebit_ceiling.so): phase 1's exact stream set (m read; per
+    worker g and e read, e and the sign words written, a workgroup barrier per
+    worker; e_s read and written; v_fresh and v_frozen read, v_fresh written;
+    the server's sign words written), a streaming read and a streaming copy.
+    The written arrays get their own bits back, so the state is unchanged.
+    Returns the rates (GB/s of bytes read plus written) and phase 1's
+    fraction of its own pattern's rate."""
+    import ctypes
+    lib = _ceiling_lib()
+    C, N, W = wl.chunk, wl.N, wl.W
+    n = (N // C) * C                               # whole chunks only
+    P = ctypes.c_void_p
+    ga = (P * W)(*[t.data_ptr() for t in g])
+    ea = (P * W)(*[t.data_ptr() for t in e])
+    ba = (P * W)(*[t.data_ptr() for t in bits_w])
+    tmp = torch.empty(N, dtype=torch.float32, device="cuda")
+    sink = torch.empty(N // C + 1, dtype=torch.float32, device="cuda")
+    st = stream.cuda_stream
+    calls = {
+        "phase1_pattern": (lambda: lib.onebit_ceiling_phase1(
+            n, W, m.data_ptr(), ga, ea, ba, err_s.data_ptr(), v.data_ptr(), vf.data_ptr(),
+            bits_s.data_ptr(), 0, st), n * (12 * W + 24) + (W + 1) * n // 8),
+        "stream_read": (lambda: lib.onebit_ceiling_read(n, g[0].data_ptr(), sink.data_ptr(), st),
+                        4 * n),
+        "stream_copy": (lambda: lib.onebit_ceiling_copy(n, g[0].data_ptr(), tmp.data_ptr(), st),
+                        8 * n),
+    }
+    out = {}
+    for name, (fn, nbytes) in calls.items():
+        for _ in range(2):
+            assert fn() == 0, name
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(reps):
+            fn()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_time(ev[1]) / reps
+        out[name + "_GBps"] = nbytes / (ms * 1e-3) / 1e9
+    del tmp, sink
+    out["phase1_frac_of_pattern"] = achieved / out["phase1_pattern_GBps"]
+    out["note"] = ("pure-traffic kernels on the step's own buffers after the timed steps "
+                   "(libonebit_ceiling.so): phase 1's stream set with its barriers and no "
+                   "arithmetic, a streaming read, a streaming copy; bytes read plus written")
+    log("[bench] ceiling: " + ", ".join(f"{k} {v:.0f}" for k, v in out.items()
+                                        if k.endswith("GBps")) +
+        f" GB/s; phase 1 at {out['phase1_frac_of_pattern']:.3f} of its pattern")
+    return out
+
+
+def cpu_baseline(wl, n_chunks, method="lamb", nsel=1, by_step=None):
     """The oracle (single-threaded C, as it stands) on the window of the
-    first n_chunks chunks of the workload: one compression step."""
+    first n_chunks chunks of the workload: one compression step.  With
+    by_step (a dict, LAMB only), the same window's other step types are
+    timed into it too: the LAMB warmup step, the workers' compression
+    (onebit_compress_ef's rule, one worker) and the server's average and
+    recompression (onebit_average_packed's rule, W workers)."""
+    import oracle
     from tests.harness import HostRun
     hi = min(wl.N, n_chunks * wl.chunk)
     h = HostRun(wl, 0, hi)
@@ -129,9 +200,27 @@ def cpu_baseline(wl, n_chunks, method="lamb", nsel=1):
     dt = time.perf_counter() - t0
     what = {"adam": "1-bit Adam", "sparse": f"sparse ({nsel} block(s) of 64 per chunk)"}.get(
         method, "1-bit LAMB")
+    sample = (f"elements [0, {hi}) of the {wl.name} table (first {-(-hi // wl.chunk)} chunks, "
+              f"W={wl.W})")
+    if by_step is not None and method == "lamb":
+        def timed(fn):
+            t = time.perf_counter()
+            fn()
+            return time.perf_counter() - t
+        out = h.out
+        h.fill_grads(1)                       # untimed, like the compression step's
+        steps = {
+            "compressed_step": dt,
+            "compress_ef": timed(lambda: oracle.compress_ef(h.g[0], h.e[0], wl.chunk)),
+            "average_packed": timed(lambda: oracle.average_packed(out["bits_w"], out["scales_w"],
+                                                                  h.err_s, wl.chunk)),
+            "warmup_step": timed(lambda: h.warmup_step(1, fill=False)),
+        }
+        for k, t in steps.items():
+            by_step[k] = {"value": hi / t, "unit": "params/s", "seconds": t, "cores": 1,
+                          "kind": "oracle", "sample": sample}
     return {"value": hi / dt, "unit": "params/s", "cores": 1, "kind": "oracle",
-            "sample": f"one {what} compression step on elements [0, {hi}) of the {wl.name} table "
-                      f"(first {hi // wl.chunk} chunks, W={wl.W}); {dt:.2f} s"}
+            "sample": f"one {what} compression step on {sample}; {dt:.2f} s"}
 
 
 def main():
@@ -169,6 +258,7 @@ def main():
         sys.exit(2)
 
     need = [os.path.join(ROOT, "communication_compressed_optimizer_amd", "libonebit.so"),
+            os.path.join(ROOT, "communication_compressed_optimizer_amd", "libonebit_ceiling.so"),
             os.path.join(ROOT, "synth", "libsynth_dev.so"), os.path.join(ROOT, "oracle", "liboracle.so")]
     if not all(os.path.exists(p) for p in need):
         import __graft_entry__
@@ -265,20 +355,25 @@ def main():
     log(f"[bench] packed momentum {args.steps} steps: {pm_ms:.3f} ms/step (phase1 {pm_p1:.3f} ms, "
         f"phase2 {pm_p2:.3f} ms)")
 
-    # context: one LAMB warmup step on the same table (after the timed
-    # compression steps; it reuses the same buffers)
+    # context: the LAMB warmup step on the same table (after the timed
+    # compression steps; it reuses the same buffers), carrying the
+    # parameters' squared norm from step to step as a warmup loop would
     c_sum = torch.zeros(L, dtype=torch.float32, device=dev)
-    for _ in range(2):
-        ob.onebit_lamb_warmup_step(table, W, g, x, m, v, c_sum, c_out, hp, ws, status, stream)
+    x_sq = torch.zeros(table.n_segments, dtype=torch.float64, device=dev)
+    for i in range(2):
+        ob.onebit_lamb_warmup_step_carry(table, W, g, x, m, v, c_sum, c_out, x_sq, int(i > 0), hp,
+                                         ws, status, stream)
     wev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     wsteps = 5
     wev[0].record(stream)
     for _ in range(wsteps):
-        ob.onebit_lamb_warmup_step(table, W, g, x, m, v, c_sum, c_out, hp, ws, status, stream)
+        ob.onebit_lamb_warmup_step_carry(table, W, g, x, m, v, c_sum, c_out, x_sq, 1, hp, ws,
+                                         status, stream)
     wev[1].record(stream)
     torch.cuda.synchronize()
     warm_ms = wev[0].elapsed_time(wev[1]) / wsteps
-    warm_bytes = N * (4 * W + 36)
+    warm_bytes = N * (4 * W + 24)          # each array once: the algorithmic count
+    warm_moved = N * (4 * W + 32)          # the two passes: m, v and x read again by the update
 
     sbytes = step_bytes(N, K, C, W)
     pm_bytes = step_bytes_packed(N, K, C, W)
@@ -288,10 +383,13 @@ def main():
     traffic = _measured_traffic("traffic_compress_average_bert_large.txt") \
         if wl.name == "bert_large" else None
     cpu = None
+    cpu_by_step = {}
     if args.cpu_chunks > 0:
         log("[bench] CPU oracle baseline ...")
-        cpu = cpu_baseline(wl, args.cpu_chunks)
+        cpu = cpu_baseline(wl, args.cpu_chunks, by_step=cpu_by_step)
         log(f"[bench] oracle: {cpu['value']:.3e} params/s ({cpu['sample']})")
+        log("[bench] oracle by step: " + ", ".join(f"{k} {v['value']:.3e} params/s"
+                                                   for k, v in cpu_by_step.items()))
 
     out = {
         "metric": METRIC,
@@ -316,7 +414,13 @@ def main():
         "phase1_ms_per_step": {"min": p1_sorted[0], "median": p1_sorted[len(p1_sorted) // 2],
                                "max": p1_sorted[-1]},
         "warmup_step": {"ms": warm_ms, "params_per_s": N / (warm_ms * 1e-3),
-                        "GBps": warm_bytes / (warm_ms * 1e-3) / 1e9, "bytes": warm_bytes},
+                        "GBps": warm_bytes / (warm_ms * 1e-3) / 1e9,
+                        "frac_of_peak": warm_bytes / (warm_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                        "bytes": warm_bytes, "moved_bytes": warm_moved,
+                        "moved_GBps": warm_moved / (warm_ms * 1e-3) / 1e9,
+                        "note": "onebit_lamb_warmup_step_carry, norm carried; GBps counts each "
+                                "array once (4W+24 B/elem), moved_GBps the two passes' traffic "
+                                "(4W+32: the update rereads m, v and x)"},
         "packed_momentum": {
             "ms_per_step": pm_ms, "params_per_s": N / (pm_ms * 1e-3),
             "phase_ms": {"compress_average": pm_p1, "rescale_update": pm_p2},
@@ -327,8 +431,11 @@ def main():
                      "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
                      "algorithmic_bytes": abytes},
+        "ceiling": pattern_ceiling(torch, stream, wl, g, e, err_s, m, v, vf, bits_w, bits_s,
+                                   achieved),
         "runtime_copy": _ceiling(torch, stream, achieved),
         "cpu_baseline": cpu,
+        "cpu_baseline_by_step": cpu_by_step or None,
     }
     print(json.dumps(out), flush=True)
 

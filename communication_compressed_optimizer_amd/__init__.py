@@ -23,7 +23,8 @@ __all__ = [
     "ONEBIT_OK", "ONEBIT_EINVAL", "ONEBIT_EALIGN", "ONEBIT_EUNSUPPORTED", "ONEBIT_EHIP",
     "ONEBIT_ENOMEM", "OnebitError", "onebit_hparams", "LayerTable", "onebit_layer_table_create",
     "onebit_layer_table_destroy", "onebit_layer_table_info", "onebit_workspace_size",
-    "onebit_lamb_warmup_step", "onebit_lamb_freeze", "onebit_compress_ef", "onebit_average_packed",
+    "onebit_lamb_warmup_step", "onebit_lamb_warmup_step_carry", "onebit_lamb_freeze",
+    "onebit_compress_ef", "onebit_average_packed",
     "onebit_lamb_compressed_step", "onebit_lamb_compress_average", "onebit_lamb_rescale_update",
     "onebit_decompress", "onebit_last_error", "onebit_version", "onebit_adam_warmup_step",
     "onebit_adam_compressed_step", "onebit_sparse_compressed_step", "onebit_worker_compress",
@@ -69,6 +70,8 @@ _lib.onebit_layer_table_info.argtypes = [_P, _P, _P, _P]
 _lib.onebit_workspace_size.argtypes = [_P, _i32, ctypes.POINTER(ctypes.c_size_t)]
 _lib.onebit_lamb_warmup_step.argtypes = [_P, _i32, _P, _P, _P, _P, _P, _P,
                                          ctypes.POINTER(onebit_hparams), _P, _P, _P]
+_lib.onebit_lamb_warmup_step_carry.argtypes = [_P, _i32, _P, _P, _P, _P, _P, _P, _P, _i32,
+                                               ctypes.POINTER(onebit_hparams), _P, _P, _P]
 _lib.onebit_lamb_freeze.argtypes = [_P, _i32, _P, _P, _P, _P, _P, _i32, _P, _P,
                                     ctypes.POINTER(onebit_hparams), _P]
 _lib.onebit_compress_ef.argtypes = [_i64, _i32, _P, _P, _P, _P, _P, _P]
@@ -101,7 +104,8 @@ _lib.onebit_sparse_update.argtypes = [_P, _i32, _P, _P, _P, _P, _P, _P, _P,
 _lib.onebit_last_error.restype = ctypes.c_char_p
 _lib.onebit_version.restype = ctypes.c_char_p
 for _f in ("onebit_layer_table_create", "onebit_layer_table_destroy", "onebit_layer_table_info",
-           "onebit_workspace_size", "onebit_lamb_warmup_step", "onebit_lamb_freeze",
+           "onebit_workspace_size", "onebit_lamb_warmup_step", "onebit_lamb_warmup_step_carry",
+           "onebit_lamb_freeze",
            "onebit_compress_ef", "onebit_average_packed", "onebit_lamb_compressed_step",
            "onebit_lamb_compress_average", "onebit_lamb_rescale_update", "onebit_decompress"):
     getattr(_lib, _f).restype = ctypes.c_int
@@ -277,6 +281,23 @@ def onebit_lamb_warmup_step(table, W, grads, x, m, v, c_sum, c_out, hp, ws, stat
                                         t(c_out, "c_out"), ctypes.byref(hp),
                                         _ptr(ws, fn, "ws", z.ws), _ptr(status, fn, "status", 4),
                                         _stream(stream)), fn)
+
+
+def onebit_lamb_warmup_step_carry(table, W, grads, x, m, v, c_sum, c_out, x_sq, x_sq_valid, hp,
+                                  ws, status=None, stream=None):
+    fn, z = "onebit_lamb_warmup_step_carry", _table_sizes(table, W)
+    e = lambda a, nm: _ptr(a, fn, nm, z.elems, _F32)  # noqa: E731
+    t = lambda a, nm: _ptr(a, fn, nm, z.tensors, _F32)  # noqa: E731
+    segs = 8 * table.n_segments if isinstance(table, LayerTable) else None
+    if x_sq is not None and not isinstance(x_sq, int):
+        import torch
+        if x_sq.dtype != torch.float64:
+            raise _bad(fn, f"x_sq has dtype {x_sq.dtype}, float64 expected")
+    _check(_lib.onebit_lamb_warmup_step_carry(
+        _h(table), W, _ptr_list(grads, fn, "grads", W, z.elems, _F32), e(x, "x"), e(m, "m"),
+        e(v, "v"), t(c_sum, "c_sum"), t(c_out, "c_out"), _ptr(x_sq, fn, "x_sq", segs), x_sq_valid,
+        ctypes.byref(hp), _ptr(ws, fn, "ws", z.ws), _ptr(status, fn, "status", 4),
+        _stream(stream)), fn)
 
 
 def onebit_lamb_freeze(table, W, v, v_fresh, err_w, err_s, c_sum, T_w, c_avg, f_prev, hp=None,

@@ -225,17 +225,29 @@ struct LaunchDecompress {
   }
 };
 
+// x_sq: NULL (x read in pass 1, nothing carried), or the per-segment sums
+// of x^2 carried between steps: read in place of x when x_in is true,
+// rewritten for the updated x by pass 2.
 template <int C>
 struct LaunchWarmup {
   static void run(const onebit_layer_table* t, int W, const Workers& wk, float* x, float* m,
-                  float* v, float* c_sum, float* c_out, const Coef& cf, const Ws& ws,
-                  int32_t* status, hipStream_t st) {
-    launch_chunks<C>(t->N, st, k_warmup_pass1<C, kWarm_NT>, t->dev, W, wk, (const float*)x, m, v,
-                     ws.seg_x, ws.seg_u, cf);
+                  float* v, float* c_sum, float* c_out, double* x_sq, bool x_in, const Coef& cf,
+                  const Ws& ws, int32_t* status, hipStream_t st) {
+    if (x_in)
+      launch_chunks<C>(t->N, st, k_warmup_pass1<C, kWarm_NT, 1, true>, t->dev, W, wk,
+                       (const float*)x, m, v, ws.seg_x, ws.seg_u, cf);
+    else
+      launch_chunks<C>(t->N, st, k_warmup_pass1<C, kWarm_NT, 1, false>, t->dev, W, wk,
+                       (const float*)x, m, v, ws.seg_x, ws.seg_u, cf);
     hipLaunchKernelGGL(k_warmup_finalize<256>, dim3((unsigned)t->L), dim3(256), 0, st, t->dev,
-                       ws.seg_x, ws.seg_u, c_sum, ws.c_layer, c_out, cf, status);
-    launch_chunks<C>(t->N, st, k_warmup_pass2<C, kWarm_NT>, t->dev, (const float*)m,
-                     (const float*)v, x, (const float*)ws.c_layer, cf);
+                       (const double*)(x_in ? x_sq : ws.seg_x), (const double*)ws.seg_u, c_sum,
+                       ws.c_layer, c_out, cf, status);
+    if (x_sq)
+      launch_chunks<C>(t->N, st, k_warmup_pass2<C, kWarm_NT, true>, t->dev, (const float*)m,
+                       (const float*)v, x, (const float*)ws.c_layer, x_sq, cf);
+    else
+      launch_chunks<C>(t->N, st, k_warmup_pass2<C, kWarm_NT, false>, t->dev, (const float*)m,
+                       (const float*)v, x, (const float*)ws.c_layer, x_sq, cf);
   }
 };
 
@@ -458,6 +470,52 @@ int check_phase2(const char* fn, const onebit_layer_table* table, const uint32_t
   return ONEBIT_OK;
 }
 
+// Both warmup entry points: x_sq NULL carries nothing.
+int warmup_step(const char* fn, const onebit_layer_table* table, int32_t W,
+                const float* const* grads, float* x, float* m, float* v, float* c_sum,
+                float* c_out, double* x_sq, int32_t x_sq_valid, const onebit_hparams* hp, void* ws,
+                int32_t* status, void* stream) {
+  CHECK_OPT_WORDS(status, "status");
+  if (int rc = check_table(table, fn)) return rc;
+  if (int rc = check_W(W, fn)) return rc;
+  if (int rc = check_hparams(hp, fn)) return rc;
+  if (x_sq_valid != 0 && x_sq_valid != 1)
+    return fail(ONEBIT_EINVAL, "%s: x_sq_valid = %d is not 0 or 1", fn, x_sq_valid);
+  if (!grads) return fail(ONEBIT_EINVAL, "%s: grads is NULL", fn);
+  Workers wk{};
+  for (int w = 0; w < W; ++w) {
+    if (!grads[w]) return fail(ONEBIT_EINVAL, "%s: grads[%d] is NULL", fn, w);
+    if (!aligned16(grads[w])) return fail(ONEBIT_EALIGN, "%s: grads[%d] is not 16-byte aligned", fn, w);
+    wk.g[w] = grads[w];
+  }
+  const void* req[] = {x, m, v, c_sum, ws};
+  const char* names[] = {"x", "m", "v", "c_sum", "ws"};
+  for (int i = 0; i < 5; ++i) {
+    if (!req[i]) return fail(ONEBIT_EINVAL, "%s: %s is NULL", fn, names[i]);
+    if (!aligned16(req[i])) return fail(ONEBIT_EALIGN, "%s: %s is not 16-byte aligned", fn, names[i]);
+  }
+  if (c_out && !aligned16(c_out)) return fail(ONEBIT_EALIGN, "%s: c_out is not 16-byte aligned", fn);
+  if (x_sq && !aligned16(x_sq)) return fail(ONEBIT_EALIGN, "%s: x_sq is not 16-byte aligned", fn);
+  const Bytes b(table->N, table->chunk);
+  Spans sp;
+  sp.add_workers(grads, W, b.elems, false, "grads");
+  sp.add(x, b.elems, true, "x");
+  sp.add(m, b.elems, true, "m");
+  sp.add(v, b.elems, true, "v");
+  sp.add(c_sum, 4 * (int64_t)table->L, true, "c_sum");
+  sp.add(c_out, 4 * (int64_t)table->L, true, "c_out");
+  sp.add(x_sq, 8 * table->S, true, "x_sq");
+  sp.add(ws, (int64_t)ws_bytes(table), true, "ws");
+  sp.add(status, 4, true, "status");
+  if (int rc = sp.check(fn)) return rc;
+  // With weight decay the direction needs x itself, so pass 1 reads it and
+  // forms its norm as well (the carried value would be the same bits).
+  const bool x_in = x_sq && x_sq_valid == 1 && hp->weight_decay == 0.0f;
+  by_chunk<LaunchWarmup>(table->chunk, table, (int)W, wk, x, m, v, c_sum, c_out, x_sq, x_in,
+                         make_coef(*hp), ws_view(table, ws), status, (hipStream_t)stream);
+  return launch_status(fn);
+}
+
 }  // namespace
 
 extern "C" {
@@ -635,37 +693,18 @@ int onebit_decompress(int64_t n, int32_t chunk, const uint32_t* bits, const floa
 int onebit_lamb_warmup_step(const onebit_layer_table* table, int32_t W, const float* const* grads,
                             float* x, float* m, float* v, float* c_sum, float* c_out,
                             const onebit_hparams* hp, void* ws, int32_t* status, void* stream) {
-  CHECK_OPT_WORDS(status, "status");
-  if (int rc = check_table(table, __func__)) return rc;
-  if (int rc = check_W(W, __func__)) return rc;
-  if (int rc = check_hparams(hp, __func__)) return rc;
-  if (!grads) return fail(ONEBIT_EINVAL, "%s: grads is NULL", __func__);
-  Workers wk{};
-  for (int w = 0; w < W; ++w) {
-    CHECK_PTR(grads[w], "grads[w]");
-    wk.g[w] = grads[w];
-  }
-  CHECK_PTR(x, "x");
-  CHECK_PTR(m, "m");
-  CHECK_PTR(v, "v");
-  CHECK_PTR(c_sum, "c_sum");
-  CHECK_OPT_PTR(c_out, "c_out");
-  CHECK_PTR(ws, "ws");
-  const Bytes b(table->N, table->chunk);
-  Spans sp;
-  sp.add_workers(grads, W, b.elems, false, "grads");
-  sp.add(x, b.elems, true, "x");
-  sp.add(m, b.elems, true, "m");
-  sp.add(v, b.elems, true, "v");
-  sp.add(c_sum, 4 * (int64_t)table->L, true, "c_sum");
-  sp.add(c_out, 4 * (int64_t)table->L, true, "c_out");
-  sp.add(ws, (int64_t)ws_bytes(table), true, "ws");
-  sp.add(status, 4, true, "status");
-  if (int rc = sp.check(__func__)) return rc;
-  const Coef cf = make_coef(*hp);
-  by_chunk<LaunchWarmup>(table->chunk, table, (int)W, wk, x, m, v, c_sum, c_out, cf,
-                         ws_view(table, ws), status, (hipStream_t)stream);
-  return launch_status(__func__);
+  return warmup_step(__func__, table, W, grads, x, m, v, c_sum, c_out, nullptr, 0, hp, ws, status,
+                     stream);
+}
+
+int onebit_lamb_warmup_step_carry(const onebit_layer_table* table, int32_t W,
+                                  const float* const* grads, float* x, float* m, float* v,
+                                  float* c_sum, float* c_out, double* x_sq, int32_t x_sq_valid,
+                                  const onebit_hparams* hp, void* ws, int32_t* status,
+                                  void* stream) {
+  if (!x_sq) return fail(ONEBIT_EINVAL, "%s: x_sq is NULL", __func__);
+  return warmup_step(__func__, table, W, grads, x, m, v, c_sum, c_out, x_sq, x_sq_valid, hp, ws,
+                     status, stream);
 }
 
 int onebit_lamb_freeze(const onebit_layer_table* table, int32_t W, const float* v, float* v_fresh,

@@ -430,8 +430,13 @@ __device__ __forceinline__ void segment_max(const DevTable& tab, int64_t k, int6
 }
 
 // Per-(chunk, tensor) double sums of a^2 and b^2 over the chunk's valid
-// elements (fixed order: per thread, then the wave and block tree).
-template <int C, int SPT = 4>
+// elements (fixed order: per thread, then the wave and block tree).  The two
+// sums are reduced independently, so a sum's value does not depend on
+// whether the other is formed: HA / HB = false leaves that sum out (its array
+// is neither read nor written).  The warmup's two passes both call this, so
+// the sum of x^2 that pass 2 carries over for the updated parameters is, bit
+// for bit, the one the next step's pass 1 would form from them.
+template <int C, int SPT = 4, bool HA = true, bool HB = true>
 __device__ __forceinline__ void segment_sums(const DevTable& tab, int64_t k, int64_t base, int nk,
                                              const SlotsN<SPT>& a_, const SlotsN<SPT>& b_,
                                              double* red, double* __restrict__ seg_a,
@@ -450,14 +455,14 @@ __device__ __forceinline__ void segment_sums(const DevTable& tab, int64_t k, int
       for (int c = 0; c < 4; ++c) {
         const int j = 4 * ((int)threadIdx.x + T * a) + c;
         if (j < nk && j >= lo && j < hi) {
-          sa += (double)a_[a][c] * (double)a_[a][c];
-          sb2 += (double)b_[a][c] * (double)b_[a][c];
+          if constexpr (HA) sa += (double)a_[a][c] * (double)a_[a][c];
+          if constexpr (HB) sb2 += (double)b_[a][c] * (double)b_[a][c];
         }
       }
     block_sum2<T>(sa, sb2, red);
     if (threadIdx.x == 0) {
-      seg_a[sb + (l - l0)] = sa;
-      seg_b[sb + (l - l0)] = sb2;
+      if constexpr (HA) seg_a[sb + (l - l0)] = sa;
+      if constexpr (HB) seg_b[sb + (l - l0)] = sb2;
     }
   }
 }
@@ -1540,15 +1545,17 @@ k_compressed_pass_b(int64_t n_full, DevTable tab, const uint32_t* __restrict__ b
 }
 
 // Warmup pass 1: mean gradient, moments, per-(chunk, tensor) sums of x^2 and
-// u^2 in double.  NT: streaming accesses; WPE: minimum waves per SIMD.
-template <int C, bool TAIL, bool NT>
+// u^2 in double.  NT: streaming accesses; WPE: minimum waves per SIMD.  XS:
+// the sums of x^2 are carried over from the previous step's pass 2 (x_sq),
+// so x is not read and only the sums of u^2 are formed (the host selects it
+// only without weight decay, where u does not depend on x).
+template <int C, bool TAIL, bool NT, bool XS>
 __device__ __forceinline__ void warmup_pass1_chunk(int64_t k, const DevTable& tab, int W,
                                                    const Workers& wk, const float* __restrict__ x,
                                                    float* __restrict__ m, float* __restrict__ v,
                                                    double* __restrict__ seg_x,
                                                    double* __restrict__ seg_u, const Coef& cf,
                                                    double* red) {
-  constexpr int T = Geo<C>::T;
   const ChunkAt<C, TAIL> ch(k, tab.N);
   const int64_t base = ch.base;
   const int nk = ch.nk;
@@ -1565,7 +1572,14 @@ __device__ __forceinline__ void warmup_pass1_chunk(int64_t k, const DevTable& ta
   Slots mm, vv, u, xx;
   load_chunk<C, TAIL, NT>(m, base, nk, mm);
   load_chunk<C, TAIL, NT>(v, base, nk, vv);
-  load_chunk<C, TAIL, NT>(x, base, nk, xx);
+  if constexpr (XS) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) xx[a][c] = 0.0f;  // not read: weight decay is 0 here
+  } else {
+    load_chunk<C, TAIL, NT>(x, base, nk, xx);
+  }
   const float fW = (float)W;
 #pragma unroll
   for (int a = 0; a < 4; ++a)
@@ -1578,32 +1592,10 @@ __device__ __forceinline__ void warmup_pass1_chunk(int64_t k, const DevTable& ta
     }
   store_chunk<C, TAIL, NT>(m, base, nk, mm);
   store_chunk<C, TAIL, NT>(v, base, nk, vv);
-  const int l0 = tab.l0[ch.k];
-  const int l1 = tab.l1[ch.k];
-  const int sb = tab.seg[ch.k];
-  for (int l = l0; l <= l1; ++l) {
-    const int64_t lo = tab.off[l] - base;
-    const int64_t hi = tab.off[l + 1] - base;
-    double sx = 0.0, su = 0.0;
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int j = 4 * ((int)threadIdx.x + T * a) + c;
-        if (j < nk && j >= lo && j < hi) {
-          sx += (double)xx[a][c] * (double)xx[a][c];
-          su += (double)u[a][c] * (double)u[a][c];
-        }
-      }
-    block_sum2<T>(sx, su, red);
-    if (threadIdx.x == 0) {
-      seg_x[sb + (l - l0)] = sx;
-      seg_u[sb + (l - l0)] = su;
-    }
-  }
+  segment_sums<C, 4, !XS, true>(tab, ch.k, base, nk, xx, u, red, seg_x, seg_u);
 }
 
-template <int C, bool NT = false, int WPE = 1>
+template <int C, bool NT = false, int WPE = 1, bool XS = false>
 __global__ void __launch_bounds__(C / 16, WPE)
 k_warmup_pass1(int64_t n_full, DevTable tab, int W, Workers wk, const float* __restrict__ x,
                float* __restrict__ m, float* __restrict__ v, double* __restrict__ seg_x,
@@ -1611,10 +1603,10 @@ k_warmup_pass1(int64_t n_full, DevTable tab, int W, Workers wk, const float* __r
   __shared__ double red[2 * (Geo<C>::T / 64)];
   const int64_t has_tail = tab.K - n_full;
   if (has_tail && blockIdx.x == 0)
-    warmup_pass1_chunk<C, true, NT>(n_full, tab, W, wk, x, m, v, seg_x, seg_u, cf, red);
+    warmup_pass1_chunk<C, true, NT, XS>(n_full, tab, W, wk, x, m, v, seg_x, seg_u, cf, red);
   else
-    warmup_pass1_chunk<C, false, NT>((int64_t)blockIdx.x - has_tail, tab, W, wk, x, m, v,
-                                     seg_x, seg_u, cf, red);
+    warmup_pass1_chunk<C, false, NT, XS>((int64_t)blockIdx.x - has_tail, tab, W, wk, x, m, v,
+                                         seg_x, seg_u, cf, red);
 }
 
 // Per tensor: norms, trust ratio, clip, c_sum.
@@ -1644,13 +1636,17 @@ k_warmup_finalize(DevTable tab, const double* __restrict__ seg_x, const double* 
 }
 
 // Warmup pass 2: x = x - (lr*c_l)*u with u recomputed from the new m, v.
-template <int C, bool TAIL, bool NT>
+// XO: also the per-(chunk, tensor) sums of the updated x^2 into x_sq, by the
+// reduction pass 1 uses, for the next step's pass 1 to take instead of
+// reading x.
+template <int C, bool TAIL, bool NT, bool XO>
 __device__ __forceinline__ void warmup_pass2_chunk(int64_t k, const DevTable& tab,
                                                    const float* __restrict__ m,
                                                    const float* __restrict__ v,
                                                    float* __restrict__ x,
                                                    const float* __restrict__ c_layer,
-                                                   const Coef& cf) {
+                                                   double* __restrict__ x_sq, const Coef& cf,
+                                                   double* red) {
   const ChunkAt<C, TAIL> ch(k, tab.N);
   Slots mm, vv, xx, st;
   load_chunk<C, TAIL, NT>(m, ch.base, ch.nk, mm);
@@ -1665,18 +1661,22 @@ __device__ __forceinline__ void warmup_pass2_chunk(int64_t k, const DevTable& ta
       xx[a][c] = xx[a][c] - (st[a][c] * u);
     }
   store_chunk<C, TAIL, NT>(x, ch.base, ch.nk, xx);
+  if constexpr (XO) segment_sums<C, 4, true, false>(tab, ch.k, ch.base, ch.nk, xx, xx, red, x_sq,
+                                                    nullptr);
 }
 
-template <int C, bool NT = false>
+template <int C, bool NT = false, bool XO = false>
 __global__ void __launch_bounds__(C / 16)
 k_warmup_pass2(int64_t n_full, DevTable tab, const float* __restrict__ m, const float* __restrict__ v,
-               float* __restrict__ x, const float* __restrict__ c_layer, Coef cf) {
+               float* __restrict__ x, const float* __restrict__ c_layer, double* __restrict__ x_sq,
+               Coef cf) {
+  __shared__ double red[XO ? 2 * (Geo<C>::T / 64) : 1];
   const int64_t has_tail = tab.K - n_full;
   if (has_tail && blockIdx.x == 0)
-    warmup_pass2_chunk<C, true, NT>(n_full, tab, m, v, x, c_layer, cf);
+    warmup_pass2_chunk<C, true, NT, XO>(n_full, tab, m, v, x, c_layer, x_sq, cf, red);
   else
-    warmup_pass2_chunk<C, false, NT>((int64_t)blockIdx.x - has_tail, tab, m, v, x, c_layer,
-                                     cf);
+    warmup_pass2_chunk<C, false, NT, XO>((int64_t)blockIdx.x - has_tail, tab, m, v, x, c_layer,
+                                         x_sq, cf, red);
 }
 
 // Freeze, element part: v_fresh = v, error buffers cleared.

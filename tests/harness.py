@@ -21,7 +21,10 @@ ATOL = 1e-7
 class DevRun:
     """Full-size state on the GPU, stepped through the C ABI."""
 
-    def __init__(self, wl, store_worker_bits=True):
+    def __init__(self, wl, store_worker_bits=True, carry_norm=False):
+        """carry_norm: run the warmup through onebit_lamb_warmup_step_carry,
+        which carries the per-segment sums of x^2 from one warmup step to the
+        next (every step but the first then skips reading x for its norm)."""
         import torch
         import communication_compressed_optimizer_amd as ob
         self.ob = ob
@@ -58,6 +61,9 @@ class DevRun:
         wl.fill("m", self.m)
         wl.fill("v", self.v)
         self.vf.copy_(self.v)
+        self.carry_norm = carry_norm
+        self.x_sq = torch.zeros(self.table.n_segments, dtype=torch.float64, device=dev)
+        self.x_sq_valid = 0          # x_sq does not describe x until a carried step wrote it
 
     def fill_grads(self, step):
         for w in range(self.wl.W):
@@ -66,8 +72,14 @@ class DevRun:
     def warmup_step(self, step, fill=True):
         if fill:
             self.fill_grads(step)
-        self.ob.onebit_lamb_warmup_step(self.table, self.wl.W, self.g, self.x, self.m, self.v,
-                                        self.c_sum, self.c_out, self.hp, self.ws, self.status)
+        if self.carry_norm:
+            self.ob.onebit_lamb_warmup_step_carry(self.table, self.wl.W, self.g, self.x, self.m,
+                                                  self.v, self.c_sum, self.c_out, self.x_sq,
+                                                  self.x_sq_valid, self.hp, self.ws, self.status)
+            self.x_sq_valid = 1
+        else:
+            self.ob.onebit_lamb_warmup_step(self.table, self.wl.W, self.g, self.x, self.m, self.v,
+                                            self.c_sum, self.c_out, self.hp, self.ws, self.status)
 
     def freeze(self, T_w):
         self.ob.onebit_lamb_freeze(self.table, self.wl.W, self.v, self.vf, self.e, self.err_s,
@@ -76,6 +88,7 @@ class DevRun:
     def compressed_step(self, step, fill=True, packed=False):
         """packed: the momentum is the previous step's server output
         (bits_s, scales_s) and self.m is neither read nor written."""
+        self.x_sq_valid = 0
         if fill:
             self.fill_grads(step)
         self.ob.onebit_lamb_compressed_step(
@@ -86,12 +99,14 @@ class DevRun:
 
     # -- 1-bit Adam mode: v is the (frozen) variance, vf is not used ------
     def adam_warmup_step(self, step, fill=True):
+        self.x_sq_valid = 0
         if fill:
             self.fill_grads(step)
         self.ob.onebit_adam_warmup_step(self.wl.N, self.wl.W, self.g, self.x, self.m, self.v,
                                         self.hp)
 
     def adam_compressed_step(self, step, fill=True, chunk=None, packed=False):
+        self.x_sq_valid = 0
         if fill:
             self.fill_grads(step)
         self.ob.onebit_adam_compressed_step(
@@ -107,6 +122,7 @@ class DevRun:
 
     # -- SLAMB-style sparse stage ----------------------------------------
     def sparse_step(self, step, nsel, fill=True):
+        self.x_sq_valid = 0
         torch = self.torch
         if fill:
             self.fill_grads(step)

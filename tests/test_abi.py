@@ -349,3 +349,14 @@ def test_ceiling_library_loads_without_a_gpu():
                                      0, None) == 1                         # W > 16
     assert lib.onebit_ceiling_phase1(4095, 2, P(16), arr, arr, None, P(16), P(16), P(16), P(16),
                                      0, None) == 0
+
+
+def test_warmup_carry_argument_checks(ob):
+    """The carried warmup needs its x_sq array: NULL is refused before the
+    table is looked at (no GPU needed)."""
+    lib = ob._lib
+    P = ctypes.c_void_p
+    hp = _hp(ob)
+    assert lib.onebit_lamb_warmup_step_carry(P(16), 2, None, None, None, None, None, None, None, 0,
+                                             ctypes.byref(hp), None, None, None) == ob.ONEBIT_EINVAL
+    assert "x_sq is NULL" in ob.onebit_last_error()

@@ -239,6 +239,54 @@ def test_warmup_step_parity(numels, W):
         assert_parity(compare_state(d, h, stage="warmup"), f"warmup step {step}")
 
 
+def _segment_sums_host(wl, x):
+    """Per-(chunk, tensor) sums of x^2 in float64, segments numbered chunk by
+    chunk and within a chunk tensor by tensor (an independent enumeration)."""
+    C, N = wl.chunk, wl.N
+    off = wl.offsets
+    x = x.astype(np.float64)
+    out = []
+    for k in range(wl.K):
+        lo, hi = k * C, min((k + 1) * C, N)
+        for l in range(len(off) - 1):
+            a, b = max(lo, int(off[l])), min(hi, int(off[l + 1]))
+            if a < b:
+                out.append(float(np.sum(x[a:b] * x[a:b])))
+    return np.array(out)
+
+
+@pytest.mark.parametrize("numels", RAGGED)
+@pytest.mark.parametrize("variant", ["plain", "bias", "weight_decay"])
+def test_warmup_norm_carry_is_bit_identical(numels, variant):
+    """onebit_lamb_warmup_step_carry (x's squared norm carried from one step's
+    update pass to the next step) against onebit_lamb_warmup_step (x read in
+    every step): four steps, then an outside change to x announced with
+    x_sq_valid = 0, then two more steps.  Every output is equal bit for bit,
+    and after each carried step x_sq holds the per-segment sums of the
+    updated x^2 (float64 sums on the host, to the rounding of the order)."""
+    wl = _ragged_workload(numels, 3, init="fresh")
+    a, b = DevRun(wl), DevRun(wl, carry_norm=True)
+    assert b.x_sq.numel() == b.table.n_segments
+    if variant == "weight_decay":
+        a.hp.weight_decay = b.hp.weight_decay = 0.01
+    for step in range(7):
+        if step == 4:                         # x changed outside the warmup
+            for r in (a, b):
+                r.x.mul_(-0.5)
+            b.x_sq_valid = 0
+        for r in (a, b):
+            if variant == "bias":
+                r.hp.bias_step = step + 1
+            r.warmup_step(step)
+        torch.cuda.synchronize()
+        for name in ("x", "m", "v", "c_sum", "c_out"):
+            assert torch.equal(getattr(a, name).view(torch.int32), getattr(b, name).view(torch.int32)), \
+                (name, step)
+        want = _segment_sums_host(wl, host(b.x))
+        got = host(b.x_sq)
+        assert np.allclose(got, want, rtol=1e-11, atol=0), step
+
+
 def test_freeze_parity():
     wl = _ragged_workload(RAGGED[0], 3, init="fresh")
     d, h = DevRun(wl), HostRun(wl)

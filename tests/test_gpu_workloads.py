@@ -6,6 +6,7 @@ compared for the tensors wholly inside a window).  Inputs of both sides come
 from the same seeded generator (device fill on the GPU, host fill for the
 oracle, bit-identical by construction and by test_synth_device_matches_host).
 """
+import numpy as np
 import pytest
 
 pytestmark = pytest.mark.gpu
@@ -37,11 +38,12 @@ def block_windows(wl, chunks=120):
 
 
 def test_bert_large_step():
-    """BERT-Large table, W = 8: two compression steps, windows checked."""
+    """BERT-Large table, W = 8: the configuration's 10 compression steps, GPU
+    and oracle each on their own state, windows checked after every step."""
     wl = WORKLOADS["bert_large"]
     d = DevRun(wl)
     hosts = [HostRun(wl, lo, hi) for lo, hi in block_windows(wl)]
-    for step in range(2):
+    for step in range(wl.compression_steps):
         d.compressed_step(step)
         torch.cuda.synchronize()
         for h in hosts:
@@ -50,11 +52,65 @@ def test_bert_large_step():
     assert int(d.status.item()) == 0
 
 
-def test_mixed_warmup_to_compression():
-    """BERT-Large table with per-tensor gradient scales: 20 LAMB warmup steps,
-    freeze, 20 compression steps, GPU and oracle each on their own state."""
-    wl = WORKLOADS["mixed"]
+def covering_windows(wl, chunks=16384):
+    """Chunk-aligned windows of at most `chunks` chunks that together cover
+    every chunk, each starting at the first chunk of the first tensor the
+    previous window does not hold whole, so that every tensor lies wholly
+    inside some window (tensors are shorter than a window)."""
+    C, K, N = wl.chunk, wl.K, wl.N
+    off = wl.offsets
+    wins, lo = [], 0
+    while True:
+        hi = min(K, lo + chunks)
+        wins.append((lo, hi))
+        if hi == K:
+            break
+        l = int(np.searchsorted(off, hi * C, side="right")) - 1   # tensor holding element hi*C
+        lo = int(off[l]) // C
+    return [(lo * C, min(N, hi * C)) for lo, hi in wins]
+
+
+@pytest.mark.timeout(900)
+def test_bert_large_whole_buffer():
+    """BERT-Large table, W = 8, one compression step, compared against the
+    oracle over the WHOLE buffer: every chunk's signs, scales and errors of
+    all eight workers and of the server, m, v_fresh, and the parameters and
+    per-tensor coefficients of every tensor (the oracle runs consecutive
+    windows so host memory stays bounded).  Under error feedback a wrong sign
+    anywhere is carried into every later step ("1-bit LAMB" page, Related
+    work), so no chunk is left to sampling."""
+    wl = WORKLOADS["bert_large"]
+    wins = covering_windows(wl)
+    C, off = wl.chunk, wl.offsets
+    covered = np.zeros(wl.K, bool)
+    whole = np.zeros(wl.L, bool)
+    for lo, hi in wins:
+        covered[lo // C:-(-hi // C)] = True
+        whole |= (off[:-1] >= lo) & (off[1:] <= hi)
+    assert covered.all() and whole.all()
     d = DevRun(wl)
+    d.compressed_step(0)
+    torch.cuda.synchronize()
+    assert int(d.status.item()) == 0
+    n_chunks = n_tensors = 0
+    for lo, hi in wins:
+        h = HostRun(wl, lo, hi)
+        h.compressed_step(0)
+        rep = compare_state(d, h)
+        assert_parity(rep, f"window [{lo}, {hi})")
+        assert rep["bits_w7"]["n"] == (-(-hi // C) - lo // C) * C // 32
+        n_chunks += -(-hi // C) - lo // C
+        n_tensors += h.full.size
+        del h
+    assert n_chunks >= wl.K and n_tensors >= wl.L
+
+
+def test_mixed_warmup_to_compression():
+    """BERT-Large table with per-tensor gradient scales: 20 LAMB warmup steps
+    (the parameters' squared norm carried from step to step), freeze, 20
+    compression steps, GPU and oracle each on their own state."""
+    wl = WORKLOADS["mixed"]
+    d = DevRun(wl, carry_norm=True)         # every warmup step after the first skips reading x
     hosts = [HostRun(wl, lo, hi) for lo, hi in block_windows(wl, chunks=64)]
     step = 0
     for _ in range(wl.warmup_steps):
