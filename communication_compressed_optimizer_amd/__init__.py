@@ -25,7 +25,8 @@ __all__ = [
     "onebit_layer_table_destroy", "onebit_layer_table_info", "onebit_workspace_size",
     "onebit_lamb_warmup_step", "onebit_lamb_warmup_step_carry", "onebit_lamb_freeze",
     "onebit_compress_ef", "onebit_average_packed",
-    "onebit_lamb_compressed_step", "onebit_lamb_compress_average", "onebit_lamb_rescale_update",
+    "onebit_lamb_compressed_step", "onebit_lamb_compressed_step_noalloc",
+    "onebit_lamb_compress_average", "onebit_lamb_rescale_update",
     "onebit_decompress", "onebit_last_error", "onebit_version", "onebit_adam_warmup_step",
     "onebit_adam_compressed_step", "onebit_sparse_compressed_step", "onebit_worker_compress",
     "onebit_lamb_rescale_stats", "onebit_adam_update", "onebit_sparse_worker",
@@ -79,6 +80,9 @@ _lib.onebit_average_packed.argtypes = [_i64, _i32, _i32, _P, _P, _P, _P, _P, _P,
 _lib.onebit_lamb_compressed_step.argtypes = [_P, _i32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                              _P, _P, _P, _P, ctypes.POINTER(onebit_hparams), _P,
                                              _P, _P]
+_lib.onebit_lamb_compressed_step_noalloc.argtypes = [_P, _i32, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                                     _P, _P, _P, _P, _P,
+                                                     ctypes.POINTER(onebit_hparams), _P, _P]
 _lib.onebit_lamb_compress_average.argtypes = [_P, _i32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                               ctypes.POINTER(onebit_hparams), _P, _P, _P]
 _lib.onebit_lamb_rescale_update.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P,
@@ -347,6 +351,24 @@ def onebit_lamb_compressed_step(table, W, grads, err_w, err_s, x, m, v_frozen, v
         _ptr(bits_s, fn, "bits_s", z.words, _WORDS), _ptr(scales_s, fn, "scales_s", z.scales, _F32),
         ctypes.byref(hp), _ptr(ws, fn, "ws", z.ws), _ptr(status, fn, "status", 4),
         _stream(stream)), fn)
+
+
+def onebit_lamb_compressed_step_noalloc(table, W, grads, err_w, err_s, x, m, v_frozen, v_fresh,
+                                        c_avg, f_prev, c_out, bits_w, scales_w, bits_s, scales_s,
+                                        hp, status=None, stream=None):
+    """onebit_lamb_compressed_step with the library's static scratch in place
+    of a workspace: the call allocates nothing (see include/onebit.h)."""
+    fn, z = "onebit_lamb_compressed_step_noalloc", _table_sizes(table, W)
+    e = lambda a, nm: _ptr(a, fn, nm, z.elems, _F32)  # noqa: E731
+    t = lambda a, nm: _ptr(a, fn, nm, z.tensors, _F32)  # noqa: E731
+    _check(_lib.onebit_lamb_compressed_step_noalloc(
+        _h(table), W, _ptr_list(grads, fn, "grads", W, z.elems, _F32),
+        _ptr_list(err_w, fn, "err_w", W, z.elems, _F32), e(err_s, "err_s"), e(x, "x"), e(m, "m"),
+        e(v_frozen, "v_frozen"), e(v_fresh, "v_fresh"), t(c_avg, "c_avg"), t(f_prev, "f_prev"),
+        t(c_out, "c_out"), _ptr_list(bits_w, fn, "bits_w", W, z.words, _WORDS),
+        _ptr_list(scales_w, fn, "scales_w", W, z.scales, _F32),
+        _ptr(bits_s, fn, "bits_s", z.words, _WORDS), _ptr(scales_s, fn, "scales_s", z.scales, _F32),
+        ctypes.byref(hp), _ptr(status, fn, "status", 4), _stream(stream)), fn)
 
 
 def onebit_lamb_compress_average(table, W, grads, err_w, err_s, m, v_frozen, v_fresh, bits_w,

@@ -8,6 +8,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -516,6 +517,89 @@ int warmup_step(const char* fn, const onebit_layer_table* table, int32_t W,
   return launch_status(fn);
 }
 
+// The fused compression step of both entry points (ws: the caller's
+// workspace, or this device's static scratch).
+int compressed_step(const char* fn, const onebit_layer_table* table, int32_t W,
+                    const float* const* grads, float* const* err_w, float* err_s, float* x,
+                    float* m, const float* v_frozen, float* v_fresh, const float* c_avg,
+                    float* f_prev, float* c_out, uint32_t* const* bits_w, float* const* scales_w,
+                    uint32_t* bits_s, float* scales_s, const onebit_hparams* hp, void* ws,
+                    int32_t* status, void* stream) {
+  CHECK_OPT_WORDS(status, "status");
+  Workers wk;
+  if (int rc = check_phase1(fn, table, W, grads, err_w, err_s, m, v_frozen, v_fresh, bits_w,
+                            scales_w, bits_s, scales_s, hp, ws, wk))
+    return rc;
+  if (int rc = check_phase2(fn, table, bits_s, scales_s, x, m, v_frozen, c_avg, f_prev, c_out, hp,
+                            ws))
+    return rc;
+  const Bytes b(table->N, table->chunk);
+  const int64_t tl = 4 * (int64_t)table->L;
+  Spans sp;
+  sp.add_workers(grads, W, b.elems, false, "grads");
+  sp.add_workers(err_w, W, b.elems, true, "err_w");
+  sp.add_workers(bits_w, W, b.words, true, "bits_w");
+  sp.add_workers(scales_w, W, b.scales, true, "scales_w");
+  sp.add(err_s, b.elems, true, "err_s");
+  sp.add(x, b.elems, true, "x");
+  sp.add(m, b.elems, true, "m");
+  sp.add(v_frozen, b.elems, false, "v_frozen");
+  sp.add(v_fresh, b.elems, true, "v_fresh");
+  sp.add(c_avg, tl, false, "c_avg");
+  sp.add(f_prev, tl, true, "f_prev");
+  sp.add(c_out, tl, true, "c_out");
+  sp.add(bits_s, b.words, true, "bits_s");
+  sp.add(scales_s, b.scales, true, "scales_s");
+  sp.add(ws, (int64_t)ws_bytes(table), true, "ws");
+  sp.add(status, 4, true, "status");
+  if (int rc = sp.check(fn)) return rc;
+  const Coef cf = make_coef(*hp);
+  const bool rn = hp->rho_mode == ONEBIT_RHO_NORM_RATIO;
+  const Ws wsv = ws_view(table, ws);
+  hipStream_t st = (hipStream_t)stream;
+  by_chunk<LaunchPassA>(table->chunk, table, (int)W, wk, err_s, m, v_frozen, v_fresh, bits_s,
+                        scales_s, cf, rn, wsv, status, st);
+  by_chunk<LaunchPassB>(table->chunk, table, bits_s, scales_s, x, m, v_frozen, c_avg, f_prev, c_out,
+                        cf, rn, wsv, status, st);
+  return launch_status(fn);
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of onebit_lamb_compressed_step_noalloc, for callers that cannot
+// allocate device memory: the same workspace (per-segment statistics and
+// per-tensor coefficients) in a file-scope device array instead of the
+// caller's buffer.  Every GPU the library runs on holds its own copy for the
+// life of the process.  In host code `scratch` only names the variable:
+// its device address on the current device comes from hipGetSymbolAddress,
+// looked up once per device and kept here, and only that address is ever
+// handed to a kernel.  Every word the step reads from it is written earlier
+// in the same step, so nothing needs clearing between calls.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_address(void** out, const char* fn) {
+  int dev = -1;
+  if (hipError_t e = hipGetDevice(&dev); e != hipSuccess)
+    return fail(ONEBIT_EHIP, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(ONEBIT_EUNSUPPORTED, "%s: device %d beyond the %d this entry point serves", fn, dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(ONEBIT_EHIP, "%s: hipGetSymbolAddress(scratch): %s", fn, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ONEBIT_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -815,43 +899,28 @@ int onebit_lamb_compressed_step(const onebit_layer_table* table, int32_t W,
                                 uint32_t* const* bits_w, float* const* scales_w, uint32_t* bits_s,
                                 float* scales_s, const onebit_hparams* hp, void* ws,
                                 int32_t* status, void* stream) {
-  CHECK_OPT_WORDS(status, "status");
-  Workers wk;
-  if (int rc = check_phase1(__func__, table, W, grads, err_w, err_s, m, v_frozen, v_fresh, bits_w,
-                            scales_w, bits_s, scales_s, hp, ws, wk))
-    return rc;
-  if (int rc = check_phase2(__func__, table, bits_s, scales_s, x, m, v_frozen, c_avg, f_prev, c_out,
-                            hp, ws))
-    return rc;
-  const Bytes b(table->N, table->chunk);
-  const int64_t tl = 4 * (int64_t)table->L;
-  Spans sp;
-  sp.add_workers(grads, W, b.elems, false, "grads");
-  sp.add_workers(err_w, W, b.elems, true, "err_w");
-  sp.add_workers(bits_w, W, b.words, true, "bits_w");
-  sp.add_workers(scales_w, W, b.scales, true, "scales_w");
-  sp.add(err_s, b.elems, true, "err_s");
-  sp.add(x, b.elems, true, "x");
-  sp.add(m, b.elems, true, "m");
-  sp.add(v_frozen, b.elems, false, "v_frozen");
-  sp.add(v_fresh, b.elems, true, "v_fresh");
-  sp.add(c_avg, tl, false, "c_avg");
-  sp.add(f_prev, tl, true, "f_prev");
-  sp.add(c_out, tl, true, "c_out");
-  sp.add(bits_s, b.words, true, "bits_s");
-  sp.add(scales_s, b.scales, true, "scales_s");
-  sp.add(ws, (int64_t)ws_bytes(table), true, "ws");
-  sp.add(status, 4, true, "status");
-  if (int rc = sp.check(__func__)) return rc;
-  const Coef cf = make_coef(*hp);
-  const bool rn = hp->rho_mode == ONEBIT_RHO_NORM_RATIO;
-  const Ws wsv = ws_view(table, ws);
-  hipStream_t st = (hipStream_t)stream;
-  by_chunk<LaunchPassA>(table->chunk, table, (int)W, wk, err_s, m, v_frozen, v_fresh, bits_s,
-                        scales_s, cf, rn, wsv, status, st);
-  by_chunk<LaunchPassB>(table->chunk, table, bits_s, scales_s, x, m, v_frozen, c_avg, f_prev, c_out,
-                        cf, rn, wsv, status, st);
-  return launch_status(__func__);
+  return compressed_step(__func__, table, W, grads, err_w, err_s, x, m, v_frozen, v_fresh, c_avg,
+                         f_prev, c_out, bits_w, scales_w, bits_s, scales_s, hp, ws, status, stream);
+}
+
+int onebit_lamb_compressed_step_noalloc(const onebit_layer_table* table, int32_t W,
+                                        const float* const* grads, float* const* err_w,
+                                        float* err_s, float* x, float* m, const float* v_frozen,
+                                        float* v_fresh, const float* c_avg, float* f_prev,
+                                        float* c_out, uint32_t* const* bits_w,
+                                        float* const* scales_w, uint32_t* bits_s, float* scales_s,
+                                        const onebit_hparams* hp, int32_t* status, void* stream) {
+  if (int rc = check_table(table, __func__)) return rc;
+  const size_t need = ws_bytes(table);
+  if (need > kScratchBytes)
+    return fail(ONEBIT_EUNSUPPORTED,
+                "%s: the table needs %zu bytes of scratch, more than the %zu this entry point "
+                "holds per device (use onebit_lamb_compressed_step with a workspace)",
+                __func__, need, kScratchBytes);
+  void* ws = nullptr;
+  if (int rc = scratch_address(&ws, __func__)) return rc;
+  return compressed_step(__func__, table, W, grads, err_w, err_s, x, m, v_frozen, v_fresh, c_avg,
+                         f_prev, c_out, bits_w, scales_w, bits_s, scales_s, hp, ws, status, stream);
 }
 
 int onebit_worker_compress(int64_t n, int32_t chunk, const float* grad, float* err_w,
