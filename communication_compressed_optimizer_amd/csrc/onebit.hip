@@ -571,7 +571,8 @@ int compressed_step(const char* fn, const onebit_layer_table* table, int32_t W,
 // caller's buffer.  Every GPU the library runs on holds its own copy for the
 // life of the process.  In host code `scratch` only names the variable:
 // its device address on the current device comes from hipGetSymbolAddress,
-// looked up once per device and kept here, and only that address is ever
+// looked up once per device (when a layer table is made there, else at the
+// entry point's first call) and kept here, and only that address is ever
 // handed to a kernel.  Every word the step reads from it is written earlier
 // in the same step, so nothing needs clearing between calls.
 constexpr size_t kScratchBytes = size_t(16) << 20;
@@ -617,6 +618,14 @@ int onebit_layer_table_create(const int64_t* numels, int32_t L, int32_t chunk,
   int device = -1;
   if (hipError_t e = hipGetDevice(&device); e != hipSuccess)
     return fail(ONEBIT_EHIP, "%s: hipGetDevice: %s", __func__, hipGetErrorString(e));
+  // Set-up for onebit_lamb_compressed_step_noalloc on this device: its
+  // scratch address is looked up here, outside any stream capture, since
+  // every call of it takes a table made on its device.  A failure is left
+  // for that entry point to report.
+  {
+    void* p = nullptr;
+    (void)scratch_address(&p, __func__);
+  }
   onebit_host::HostTable ht;
   if (int rc = onebit_host::build_table(numels, L, chunk, ht, __func__)) return rc;
   const std::vector<int64_t>& off = ht.off;

@@ -64,6 +64,23 @@ def test_lamb_steps_replay_as_eager():
         torch.cuda.synchronize()
 
 
+def test_carried_warmup_replays_as_eager():
+    """The warmup step with the parameters' squared norm carried: after one
+    eager step has written x_sq, the carried step is captured and replayed
+    three times against the eager carried step."""
+    wl = Workload("graph", TABLE, W=3, init="fresh", grad_std=0.02)
+    a, b = DevRun(wl, carry_norm=True), DevRun(wl, carry_norm=True)
+    for r in (a, b):
+        r.fill_grads(0)
+        r.warmup_step(0, fill=False)        # x_sq written; later steps skip reading x
+    g = _capture(lambda: b.warmup_step(1, fill=False))
+    for _ in range(3):
+        a.warmup_step(1, fill=False)
+        g.replay()
+        _same(a, b, extra=("x_sq",))
+        a.x.add_(0.0)
+
+
 def test_adam_and_sparse_steps_replay_as_eager():
     wl = Workload("graph", [5 * 4096 + 17], W=3, init="frozen")
     a, b = DevRun(wl), DevRun(wl)

@@ -87,3 +87,28 @@ def test_noalloc_refuses_a_table_beyond_its_scratch():
         ctypes.c_void_p(table.handle), 2, *[None] * 14, ctypes.byref(hp), None, None)
     assert rc == ob.ONEBIT_EUNSUPPORTED
     assert "scratch" in ob.onebit_last_error()
+
+
+def test_noalloc_step_replays_from_a_graph():
+    """The callers it is for: captured once in a HIP graph (the scratch
+    address was looked up when the table was made, so the capture holds
+    kernel launches only) and replayed three times, with eager work and
+    synchronizations between the replays; every replay equals an eager
+    workspace step bit for bit."""
+    wl = Workload("noalloc", SMALL, W=3, init="frozen")
+    a, b = DevRun(wl), DevRun(wl)
+    for r in (a, b):
+        r.fill_grads(0)
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        ob.onebit_lamb_compressed_step_noalloc(b.table, 3, b.g, b.e, b.err_s, b.x, b.m, b.v,
+                                               b.vf, b.c_avg, b.f_prev, b.c_out, b.bits_w,
+                                               b.scales_w, b.bits_s, b.scales_s, b.hp, b.status)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        a.compressed_step(0, fill=False)
+        g.replay()
+        torch.cuda.synchronize()
+        _same(a, b)
+        a.x.add_(0.0)                       # eager work between the replays
