@@ -120,7 +120,7 @@ def _ceiling_lib():
     lib.onebit_ceiling_read.argtypes = [ctypes.c_int64, P, P, P]
     lib.onebit_ceiling_copy.argtypes = [ctypes.c_int64, P, P, P]
     lib.onebit_ceiling_phase1.argtypes = [ctypes.c_int64, ctypes.c_int32, P, P, P, P, P, P, P, P,
-                                          ctypes.c_uint32, P]
+                                          ctypes.c_uint32, ctypes.c_int32, ctypes.c_int32, P]
     return lib
 
 
@@ -149,7 +149,7 @@ def pattern_ceiling(torch, stream, wl, g, e, err_s, m, v, vf, bits_w, bits_s, ac
     calls = {
         "phase1_pattern": (lambda: lib.onebit_ceiling_phase1(
             n, W, m.data_ptr(), ga, ea, ba, err_s.data_ptr(), v.data_ptr(), vf.data_ptr(),
-            bits_s.data_ptr(), 0, st), n * (12 * W + 24) + (W + 1) * n // 8),
+            bits_s.data_ptr(), 0, 0, 0, st), n * (12 * W + 24) + (W + 1) * n // 8),
         "stream_read": (lambda: lib.onebit_ceiling_read(n, g[0].data_ptr(), sink.data_ptr(), st),
                         4 * n),
         "stream_copy": (lambda: lib.onebit_ceiling_copy(n, g[0].data_ptr(), tmp.data_ptr(), st),
@@ -237,6 +237,10 @@ def main():
                     help="sparse stage: transmitted 64-element blocks per chunk")
     ap.add_argument("--cpu-chunks", type=int, default=40960,
                     help="chunks of the workload the CPU oracle baseline runs (0 = skip)")
+    ap.add_argument("--ceiling-sweep", action="store_true",
+                    help="time the real phase 1 against the pure-traffic kernel of its stream "
+                         "pattern at several caps on the workgroups per CU, and the pattern's "
+                         "loads alone and stores alone (overwrites the state; one JSON line)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of 2^28 floats (1 GiB) three times, the "
                          "reference for scaling HBM byte counters")
@@ -304,6 +308,9 @@ def main():
 
     stream = torch.cuda.current_stream()
 
+    if args.ceiling_sweep:
+        return ceiling_sweep(args, wl, ob, torch, table, hp, g, e, err_s, m, v, vf, bits_w,
+                             scales_w, bits_s, scales_s, ws, status, stream)
     if args.method == "adam":
         return bench_adam(args, wl, ob, torch, hp, g, e, err_s, x, m, v, bits_w, scales_w, bits_s,
                           scales_s, status, stream)
@@ -437,6 +444,88 @@ def main():
         "cpu_baseline": cpu,
         "cpu_baseline_by_step": cpu_by_step or None,
     }
+    print(json.dumps(out), flush=True)
+
+
+# Dynamic LDS per workgroup that caps the workgroups resident on a CU (160 KiB
+# of LDS per CU; the pattern kernel's own 2 KiB added): 1, 2, 3, 4 per CU.
+_LDS_CAPS = {1: 84 * 1024, 2: 56 * 1024, 3: 44 * 1024, 4: 36 * 1024}
+
+
+def ceiling_sweep(args, wl, ob, torch, table, hp, g, e, err_s, m, v, vf, bits_w, scales_w,
+                  bits_s, scales_s, ws, status, stream, reps=8, rounds=3):
+    """What the phase-1 access pattern costs on this machine, from committed
+    kernels only: the real phase-1 kernel, interleaved with the pure-traffic
+    kernel of its stream set (libonebit_ceiling.so) uncapped and at 1-4
+    workgroups per CU, then that pattern's loads alone and its stores alone,
+    a streaming read and a streaming copy.  Medians over `rounds` rounds of
+    `reps` launches.  The stores-only kernel overwrites the state, so it
+    runs last."""
+    import ctypes
+    lib = _ceiling_lib()
+    C, N, W = wl.chunk, wl.N, wl.W
+    n = (N // C) * C
+    P = ctypes.c_void_p
+    ga = (P * W)(*[t.data_ptr() for t in g])
+    ea = (P * W)(*[t.data_ptr() for t in e])
+    ba = (P * W)(*[t.data_ptr() for t in bits_w])
+    st = stream.cuda_stream
+    pbytes = n * (12 * W + 24) + (W + 1) * n // 8
+
+    def pattern(mode, lds):
+        return lambda: lib.onebit_ceiling_phase1(n, W, m.data_ptr(), ga, ea, ba, err_s.data_ptr(),
+                                                 v.data_ptr(), vf.data_ptr(), bits_s.data_ptr(), 0,
+                                                 mode, lds, st)
+
+    def phase1():
+        ob.onebit_lamb_compress_average(table, W, g, e, err_s, m, v, vf, bits_w, scales_w, bits_s,
+                                        scales_s, hp, ws, status, stream)
+
+    tmp = torch.empty(N, dtype=torch.float32, device="cuda")
+    sink = torch.empty(N // C + 1, dtype=torch.float32, device="cuda")
+    cases = {"phase1_kernel": (phase1, phase1_bytes(wl.N, wl.K, C, W)),
+             "pattern": (pattern(0, 0), pbytes)}
+    for per_cu, lds in _LDS_CAPS.items():
+        cases[f"pattern_{per_cu}_per_cu"] = (pattern(0, lds), pbytes)
+    cases["pattern_loads_only"] = (pattern(1, 0), n * (8 * W + 16))
+    cases["stream_read"] = (lambda: lib.onebit_ceiling_read(n, g[0].data_ptr(), sink.data_ptr(), st),
+                            4 * n)
+    cases["stream_copy"] = (lambda: lib.onebit_ceiling_copy(n, g[0].data_ptr(), tmp.data_ptr(), st),
+                            8 * n)
+    times = {k: [] for k in cases}
+    for _ in range(rounds):
+        for name, (fn, _) in cases.items():
+            fn()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+            for i in range(reps):
+                ev[i].record(stream)
+                fn()
+            ev[reps].record(stream)
+            torch.cuda.synchronize()
+            times[name] += [ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]
+    # last: the stores alone (they overwrite the state)
+    fn = pattern(2, 0)
+    fn()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    for i in range(reps):
+        ev[i].record(stream)
+        fn()
+    ev[reps].record(stream)
+    torch.cuda.synchronize()
+    times["pattern_stores_only"] = [ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]
+    sbytes = n * (4 * W + 8) + (W + 1) * n // 8
+    out = {"metric": "phase-1 access pattern on this box (pure-traffic kernels)",
+           "workload": f"{wl.name}: N={N}, W={W}, chunk {C}", "unit": "ms, GB/s",
+           "note": "medians; *_per_cu caps the resident workgroups per CU with dynamic LDS; "
+                   "loads_only/stores_only are the pattern's reads or writes alone"}
+    for name, ts in times.items():
+        nbytes = cases[name][1] if name in cases else sbytes
+        med = sorted(ts)[len(ts) // 2]
+        out[name] = {"ms": med, "GBps": nbytes / (med * 1e-3) / 1e9}
+        log(f"[sweep] {name:28s} {med:8.3f} ms  {nbytes / (med * 1e-3) / 1e9:7.0f} GB/s")
+    out["mix_penalty"] = out["pattern"]["ms"] / (out["pattern_loads_only"]["ms"] +
+                                                out["pattern_stores_only"]["ms"])
+    out["phase1_frac_of_pattern"] = out["pattern"]["ms"] / out["phase1_kernel"]["ms"]
     print(json.dumps(out), flush=True)
 
 

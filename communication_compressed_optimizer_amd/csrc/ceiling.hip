@@ -15,7 +15,10 @@
 //       and the error read, the error written back, the sign words written,
 //       with one workgroup barrier per worker; the server error read and
 //       written with a barrier; v_fresh and v_frozen read and v_fresh
-//       written; the server's sign words written.
+//       written; the server's sign words written.  Its loads alone, or its
+//       stores alone, and a cap on the workgroups per CU, can be asked for,
+//       to see what the mix of reads and writes and the number of chunks in
+//       flight cost.
 // The written element arrays receive their own bits XOR `key`: with key = 0
 // every state array keeps its value bit for bit, so the kernels can run on
 // a step's real buffers (only the sign words, outputs of every step, are
@@ -90,6 +93,33 @@ struct PatternArgs {
   uint32_t* bits[kMaxWorkers];
 };
 
+// MODE 0: the full stream set; 1: its loads only (the stores are kept out
+// by a practically never true condition); 2: its stores only (the values
+// come from the chunk index, not from memory, so the written arrays do NOT
+// keep their contents).
+template <int MODE>
+__device__ __forceinline__ void pattern_load(const float* __restrict__ p, int64_t base, Slots& s,
+                                             float salt) {
+  if constexpr (MODE == 2) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) s[a][c] = salt + (float)(a * 4 + c);
+  } else {
+    load_chunk<C, false, true>(p, base, C, s);
+  }
+}
+
+template <int MODE>
+__device__ __forceinline__ void pattern_store(float* __restrict__ p, int64_t base, const Slots& s) {
+  if constexpr (MODE == 1) {
+    if (s[0][0] == 1.2345f && s[3][3] == -1.2345f) p[base] = s[1][1];
+  } else {
+    store_chunk<C, false, true>(p, base, C, s);
+  }
+}
+
+template <int MODE>
 __global__ void __launch_bounds__(T, 6)
 k_ceiling_phase1(int W, PatternArgs pa, const float* __restrict__ m, float* __restrict__ err_s,
                  const float* __restrict__ v_frozen, float* __restrict__ v_fresh,
@@ -98,31 +128,42 @@ k_ceiling_phase1(int W, PatternArgs pa, const float* __restrict__ m, float* __re
   int parity = 0;
   const int64_t k = blockIdx.x;
   const int64_t base = k * C;
+  const float salt = (float)(k & 1023);
   Slots mm;
-  load_chunk<C, false, true>(m, base, C, mm);
+  pattern_load<MODE>(m, base, mm, salt);
   float acc = slot_sum(mm);
   for (int w = 0; w < W; ++w) {
     Slots g, e;
-    load_chunk<C, false, true>(pa.g[w], base, C, g);
-    load_chunk<C, false, true>(pa.e[w], base, C, e);
+    pattern_load<MODE>(pa.g[w], base, g, salt + (float)w);
+    pattern_load<MODE>(pa.e[w], base, e, salt - (float)w);
     const float r = exchange(slot_sum(g) + slot_sum(e), lds, parity);
     acc = acc + r;
     xor_slots(e, key);
-    store_chunk<C, false, true>(pa.e[w], base, C, e);
-    if (pa.bits[w]) store_words(pa.bits[w], k, r);
+    pattern_store<MODE>(pa.e[w], base, e);
+    if (pa.bits[w]) {
+      if constexpr (MODE == 1) {
+        if (r == 1.2345f) pa.bits[w][k] = 1u;
+      } else {
+        store_words(pa.bits[w], k, r);
+      }
+    }
   }
   Slots y;
-  load_chunk<C, false, true>(err_s, base, C, y);
+  pattern_load<MODE>(err_s, base, y, salt * 0.5f);
   acc = acc + exchange(slot_sum(y), lds, parity);
   xor_slots(y, key);
-  store_chunk<C, false, true>(err_s, base, C, y);
-  store_words(bits_s, k, acc);
+  pattern_store<MODE>(err_s, base, y);
+  if constexpr (MODE == 1) {
+    if (acc == 1.2345f) bits_s[k] = 1u;
+  } else {
+    store_words(bits_s, k, acc);
+  }
   Slots vf, vz;
-  load_chunk<C, false, true>(v_fresh, base, C, vf);
-  load_chunk<C, false, true>(v_frozen, base, C, vz);
+  pattern_load<MODE>(v_fresh, base, vf, salt * 0.25f);
+  pattern_load<MODE>(v_frozen, base, vz, salt * 0.125f);
   const float q = slot_sum(vz);
   xor_slots(vf, key ^ (q == 1.2345f ? 1u : 0u));  // depends on v_frozen
-  store_chunk<C, false, true>(v_fresh, base, C, vf);
+  pattern_store<MODE>(v_fresh, base, vf);
 }
 
 int launched() { return hipGetLastError() == hipSuccess ? 0 : 4; }
@@ -158,12 +199,16 @@ int onebit_ceiling_copy(int64_t n, const float* in, float* out, void* stream) {
 // host array of W device pointers to n/32 words, or NULL (or NULL entries);
 // m, v_frozen: n floats read; err_s, v_fresh: n floats read and written
 // back XOR key; bits_s: n/32 words written.
+// mode 0: the full set; 1: its loads only; 2: its stores only, with values
+// made up from the chunk index (the written arrays then lose their
+// contents).  lds_bytes > 0 gives every workgroup that much dynamic LDS,
+// which caps how many run on a CU at once (160 KiB per CU).
 int onebit_ceiling_phase1(int64_t n, int32_t W, const float* m, const float* const* g,
                           float* const* e, uint32_t* const* bits_w, float* err_s,
                           const float* v_frozen, float* v_fresh, uint32_t* bits_s, uint32_t key,
-                          void* stream) {
+                          int32_t mode, int32_t lds_bytes, void* stream) {
   if (n < 0 || W < 1 || W > kMaxWorkers || !m || !g || !e || !err_s || !v_frozen || !v_fresh ||
-      !bits_s)
+      !bits_s || mode < 0 || mode > 2 || lds_bytes < 0 || lds_bytes > 150 * 1024)
     return 1;
   PatternArgs pa{};
   for (int w = 0; w < W; ++w) {
@@ -175,8 +220,17 @@ int onebit_ceiling_phase1(int64_t n, int32_t W, const float* m, const float* con
   const int64_t K = n / C;
   if (K == 0) return 0;
   if (K > INT32_MAX / 2) return 1;
-  hipLaunchKernelGGL(k_ceiling_phase1, dim3((unsigned)K), dim3(T), 0, (hipStream_t)stream, (int)W,
-                     pa, m, err_s, v_frozen, v_fresh, bits_s, key);
+  hipStream_t st = (hipStream_t)stream;
+  const dim3 grid((unsigned)K), block(T);
+  if (mode == 0)
+    hipLaunchKernelGGL(k_ceiling_phase1<0>, grid, block, lds_bytes, st, (int)W, pa, m, err_s,
+                       v_frozen, v_fresh, bits_s, key);
+  else if (mode == 1)
+    hipLaunchKernelGGL(k_ceiling_phase1<1>, grid, block, lds_bytes, st, (int)W, pa, m, err_s,
+                       v_frozen, v_fresh, bits_s, key);
+  else
+    hipLaunchKernelGGL(k_ceiling_phase1<2>, grid, block, lds_bytes, st, (int)W, pa, m, err_s,
+                       v_frozen, v_fresh, bits_s, key);
   return launched();
 }
 

@@ -340,15 +340,19 @@ def test_ceiling_library_loads_without_a_gpu():
     lib.onebit_ceiling_read.argtypes = [ctypes.c_int64, P, P, P]
     lib.onebit_ceiling_copy.argtypes = [ctypes.c_int64, P, P, P]
     lib.onebit_ceiling_phase1.argtypes = [ctypes.c_int64, ctypes.c_int32, P, P, P, P, P, P, P, P,
-                                          ctypes.c_uint32, P]
+                                          ctypes.c_uint32, ctypes.c_int32, ctypes.c_int32, P]
     assert lib.onebit_ceiling_read(-1, P(16), P(16), None) == 1
     assert lib.onebit_ceiling_read(4095, P(16), P(16), None) == 0       # no whole chunk
     assert lib.onebit_ceiling_copy(100, None, P(16), None) == 1
     arr = (P * 2)(16, 16)
     assert lib.onebit_ceiling_phase1(4096, 17, P(16), arr, arr, None, P(16), P(16), P(16), P(16),
-                                     0, None) == 1                         # W > 16
+                                     0, 0, 0, None) == 1                   # W > 16
+    assert lib.onebit_ceiling_phase1(4096, 2, P(16), arr, arr, None, P(16), P(16), P(16), P(16),
+                                     0, 3, 0, None) == 1                   # mode 3
+    assert lib.onebit_ceiling_phase1(4096, 2, P(16), arr, arr, None, P(16), P(16), P(16), P(16),
+                                     0, 0, 200000, None) == 1              # more LDS than a CU has
     assert lib.onebit_ceiling_phase1(4095, 2, P(16), arr, arr, None, P(16), P(16), P(16), P(16),
-                                     0, None) == 0
+                                     0, 0, 0, None) == 0
 
 
 def test_warmup_carry_argument_checks(ob):
