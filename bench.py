@@ -223,6 +223,38 @@ def cpu_baseline(wl, n_chunks, method="lamb", nsel=1, by_step=None):
             "sample": f"one {what} compression step on {sample}; {dt:.2f} s"}
 
 
+def cpu_baseline_by_config(max_chunks=8192):
+    """The oracle (as it stands, one core) on each configuration of the
+    workload set: the whole table where it is small (Tiny, Single), else its
+    first max_chunks chunks (Mixed, BERT-XL; BERT-Large is the main
+    baseline's window).  Configurations that start with a warmup time one
+    warmup step, then (after the freeze) one compression step; the others
+    one compression step.  Gradients are filled before each timed call."""
+    from synth.workloads import WORKLOADS
+    from tests.harness import HostRun
+    out = {}
+    for name in ("tiny", "single", "mixed", "bert_xl"):
+        wl = WORKLOADS[name]
+        hi = min(wl.N, max_chunks * wl.chunk)
+        h = HostRun(wl, 0, hi)
+        entry = {"elements": hi, "W": wl.W, "cores": 1, "kind": "oracle",
+                 "sample": f"elements [0, {hi}) of the {name} table"
+                           + (" (whole)" if hi == wl.N else f" (first {-(-hi // wl.chunk)} chunks)")}
+        if wl.init == "fresh":
+            h.fill_grads(0)
+            t0 = time.perf_counter()
+            h.warmup_step(0, fill=False)
+            entry["warmup_step_params_per_s"] = hi / (time.perf_counter() - t0)
+            h.freeze(1)
+        h.fill_grads(1)
+        t0 = time.perf_counter()
+        h.compressed_step(1, fill=False)
+        entry["compressed_step_params_per_s"] = hi / (time.perf_counter() - t0)
+        out[name] = entry
+        del h
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -391,12 +423,16 @@ def main():
         if wl.name == "bert_large" else None
     cpu = None
     cpu_by_step = {}
+    cpu_by_config = None
     if args.cpu_chunks > 0:
         log("[bench] CPU oracle baseline ...")
         cpu = cpu_baseline(wl, args.cpu_chunks, by_step=cpu_by_step)
         log(f"[bench] oracle: {cpu['value']:.3e} params/s ({cpu['sample']})")
         log("[bench] oracle by step: " + ", ".join(f"{k} {v['value']:.3e} params/s"
                                                    for k, v in cpu_by_step.items()))
+        cpu_by_config = cpu_baseline_by_config()
+        log("[bench] oracle by config: " + ", ".join(
+            f"{k} {v['compressed_step_params_per_s']:.3e}" for k, v in cpu_by_config.items()))
 
     out = {
         "metric": METRIC,
@@ -443,6 +479,7 @@ def main():
         "runtime_copy": _ceiling(torch, stream, achieved),
         "cpu_baseline": cpu,
         "cpu_baseline_by_step": cpu_by_step or None,
+        "cpu_baseline_by_config": cpu_by_config,
     }
     print(json.dumps(out), flush=True)
 
