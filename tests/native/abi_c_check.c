@@ -8,7 +8,10 @@
  * it runs one more LAMB step as W simulated GPUs would, through the per-GPU
  * entry points (each worker's compression, each GPU's chunk range as server,
  * one replica's statistics and update), and checks it against the fused
- * step on a copy of the state.  It also checks a few argument errors.
+ * step on a copy of the state; then one step through the allocation-free
+ * entry point against the fused step with a workspace, and three warmup
+ * steps with the parameters' squared norm carried against three that read
+ * x.  It also checks a few argument errors.
  * Test infrastructure: it links the library, the oracle and the host input
  * generator; prints PASS and returns 0, or names the first mismatch and
  * returns 1.
@@ -238,6 +241,76 @@ int main(void) {
 #undef SAME_DEV
   }
 
+  /* the allocation-free step on a copy of the state, against the fused step
+   * with a workspace on the original */
+  {
+    float *ax = dev_alloc(fb), *am = dev_alloc(fb), *avf = dev_alloc(fb), *aes = dev_alloc(fb),
+          *afp = dev_alloc(lb), *aco = dev_alloc(lb), *ae[W], *asw[W], *ass = dev_alloc(sb);
+    uint32_t *abw[W], *abs_ = dev_alloc(wb);
+    hip_ok(hipMemcpy(ax, dx, fb, hipMemcpyDeviceToDevice), "copy");
+    hip_ok(hipMemcpy(am, dm, fb, hipMemcpyDeviceToDevice), "copy");
+    hip_ok(hipMemcpy(avf, dvf, fb, hipMemcpyDeviceToDevice), "copy");
+    hip_ok(hipMemcpy(aes, des, fb, hipMemcpyDeviceToDevice), "copy");
+    hip_ok(hipMemcpy(afp, dfprev, lb, hipMemcpyDeviceToDevice), "copy");
+    for (int w = 0; w < W; ++w) {
+      ae[w] = dev_alloc(fb); abw[w] = dev_alloc(wb); asw[w] = dev_alloc(sb);
+      hip_ok(hipMemcpy(ae[w], de[w], fb, hipMemcpyDeviceToDevice), "copy");
+      synth_fill_normal(0, stream_id(4, 11, (uint64_t)w), 0, N, 0.0, 1e-3, g[w]);
+      up(dg[w], g[w], fb);
+    }
+    rc_ok(onebit_lamb_compressed_step(table, W, (const float* const*)dg, de, des, dx, dm, dvz, dvf,
+                                      dcavg, dfprev, dcout, dbw, dsw, dbs, dss, &hp, dws, dstatus,
+                                      NULL),
+          "onebit_lamb_compressed_step (workspace)");
+    rc_ok(onebit_lamb_compressed_step_noalloc(table, W, (const float* const*)dg, ae, aes, ax, am,
+                                              dvz, avf, dcavg, afp, aco, abw, asw, abs_, ass, &hp,
+                                              dstatus, NULL),
+          "onebit_lamb_compressed_step_noalloc");
+    hip_ok(hipDeviceSynchronize(), "hipDeviceSynchronize");
+    void* h;
+#define SAME_DEV(name, a, b, bytes)                     \
+    h = down(b, bytes);                                 \
+    same(name, a, h, bytes);                            \
+    free(h)
+    SAME_DEV("noalloc x", ax, dx, fb); SAME_DEV("noalloc m", am, dm, fb);
+    SAME_DEV("noalloc v_fresh", avf, dvf, fb); SAME_DEV("noalloc err_s", aes, des, fb);
+    SAME_DEV("noalloc bits_s", abs_, dbs, wb); SAME_DEV("noalloc scales_s", ass, dss, sb);
+    SAME_DEV("noalloc f_prev", afp, dfprev, lb); SAME_DEV("noalloc c", aco, dcout, lb);
+    for (int w = 0; w < W; ++w) {
+      SAME_DEV("noalloc err_w", ae[w], de[w], fb); SAME_DEV("noalloc bits_w", abw[w], dbw[w], wb);
+    }
+  }
+
+  /* the warmup with the parameters' squared norm carried between steps,
+   * against the warmup that reads x every step: three steps from m = v = 0 */
+  {
+    float *wx = dev_alloc(fb), *wm = dev_alloc(fb), *wv = dev_alloc(fb), *wcs = dev_alloc(lb),
+          *wco = dev_alloc(lb);
+    float *qx = dev_alloc(fb), *qm = dev_alloc(fb), *qv = dev_alloc(fb), *qcs = dev_alloc(lb),
+          *qco = dev_alloc(lb);
+    double* x_sq = dev_alloc((size_t)tS * 8);
+    up(wx, x, fb);
+    up(qx, x, fb);
+    for (int step = 0; step < 3; ++step) {
+      for (int w = 0; w < W; ++w) {
+        synth_fill_normal(0, stream_id(4, 20 + (uint64_t)step, (uint64_t)w), 0, N, 0.0, 0.02, g[w]);
+        up(dg[w], g[w], fb);
+      }
+      rc_ok(onebit_lamb_warmup_step(table, W, (const float* const*)dg, wx, wm, wv, wcs, wco, &hp,
+                                    dws, dstatus, NULL),
+            "onebit_lamb_warmup_step");
+      rc_ok(onebit_lamb_warmup_step_carry(table, W, (const float* const*)dg, qx, qm, qv, qcs, qco,
+                                          x_sq, step > 0, &hp, dws, dstatus, NULL),
+            "onebit_lamb_warmup_step_carry");
+    }
+    hip_ok(hipDeviceSynchronize(), "hipDeviceSynchronize");
+    void* h;
+    SAME_DEV("carry x", qx, wx, fb); SAME_DEV("carry m", qm, wm, fb);
+    SAME_DEV("carry v", qv, wv, fb); SAME_DEV("carry c_sum", qcs, wcs, lb);
+    SAME_DEV("carry c", qco, wco, lb);
+#undef SAME_DEV
+  }
+
   int32_t status = -1;
   hip_ok(hipMemcpy(&status, dstatus, 4, hipMemcpyDeviceToHost), "status");
   if (status != 0) { printf("abi_c_check: status %d\n", status); ++failures; }
@@ -257,7 +330,8 @@ int main(void) {
 
   rc_ok(onebit_layer_table_destroy(table), "onebit_layer_table_destroy");
   printf("abi_c_check: %s (N = %lld, K = %lld, W = %d, %d LAMB steps, one Adam step, one "
-         "LAMB step through the per-GPU entry points)\n",
+         "LAMB step through the per-GPU entry points, one allocation-free step, three carried "
+         "warmup steps)\n",
          failures ? "FAIL" : "PASS", (long long)N, (long long)K, W, STEPS);
   return failures ? 1 : 0;
 }
