@@ -143,6 +143,10 @@ Ws ws_view(const onebit_layer_table* t, void* ws) {
 template <template <int> class F, typename... A>
 void by_chunk(int32_t chunk, A&&... a) {
   switch (chunk) {
+    case 64: F<64>::run(a...); break;
+    case 128: F<128>::run(a...); break;
+    case 256: F<256>::run(a...); break;
+    case 512: F<512>::run(a...); break;
     case 1024: F<1024>::run(a...); break;
     case 2048: F<2048>::run(a...); break;
     case 4096: F<4096>::run(a...); break;
@@ -152,13 +156,13 @@ void by_chunk(int32_t chunk, A&&... a) {
   }
 }
 
-// Launch k with one workgroup of C/16 threads per chunk of an n-element
-// buffer; k takes the number of full chunks first (block 0 takes the
-// partial last chunk, if any).
+// Launch k with one workgroup of Geo<C>::T threads (C/16, and 64 for chunks
+// shorter than 1024) per chunk of an n-element buffer; k takes the number
+// of full chunks first (block 0 takes the partial last chunk, if any).
 template <int C, typename KF, typename... A>
 void launch_chunks(int64_t n, hipStream_t st, KF k, A... args) {
   const int64_t K = (n + C - 1) / C;
-  if (K > 0) hipLaunchKernelGGL(k, dim3((unsigned)K), dim3(C / 16), 0, st, n / C, args...);
+  if (K > 0) hipLaunchKernelGGL(k, dim3((unsigned)K), dim3(Geo<C>::T), 0, st, n / C, args...);
 }
 
 // Tuning of the compression-step kernels, measured on MI355X at the
@@ -314,7 +318,7 @@ struct LaunchSparse {
                   const Workers& wk, const WorkerVals& wv, float* x, float* m, const float* v_frozen,
                   float* v_fresh, const float* c_avg, float* vals_s, const Coef& cf, int32_t* status,
                   hipStream_t st) {
-    hipLaunchKernelGGL((k_sparse_step<C, kSparse_NT>), dim3((unsigned)t->K), dim3(C / 16), 0, st,
+    hipLaunchKernelGGL((k_sparse_step<C, kSparse_NT>), dim3((unsigned)t->K), dim3(Geo<C>::T), 0, st,
                        t->N / C, t->dev, W, nsel, sel, wk, wv, x, m, v_frozen, v_fresh, c_avg,
                        vals_s, cf, status);
   }
@@ -399,7 +403,7 @@ struct LaunchPassB {
       hipLaunchKernelGGL((k_rescale_finalize<256>), dim3((unsigned)t->L), dim3(256), 0, st,
                          t->dev, (const float*)ws.seg_max, (const double*)ws.seg_x,
                          (const double*)ws.seg_u, c_avg, f_prev, ws.c_layer, c_out, cf, status);
-    hipLaunchKernelGGL((k_compressed_pass_b<C, kPassB_NT>), dim3((unsigned)t->K), dim3(C / 16), 0,
+    hipLaunchKernelGGL((k_compressed_pass_b<C, kPassB_NT>), dim3((unsigned)t->K), dim3(Geo<C>::T), 0,
                        st, t->N / C, t->dev, bits_s, scales_s, v_frozen, x, m,
                        (const float*)ws.c_layer, cf);
   }

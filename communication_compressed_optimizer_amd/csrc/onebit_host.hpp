@@ -51,7 +51,7 @@ inline int ok() {
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
-inline bool chunk_supported(int32_t c) { return c >= 1024 && c <= 16384 && (c & (c - 1)) == 0; }
+inline bool chunk_supported(int32_t c) { return c >= 64 && c <= 16384 && (c & (c - 1)) == 0; }
 
 inline size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
 
@@ -217,7 +217,7 @@ struct HostTable {
 
 // Checks the sizes and returns N and K without building anything: EINVAL for
 // a NULL array, L < 1 or a tensor of fewer than 1 element; EUNSUPPORTED for a
-// chunk that is not a power of two in [1024, 16384] or more than 2^30 - 1
+// chunk that is not a power of two in [64, 16384] or more than 2^30 - 1
 // chunks in all.  The running sum is bounded before each add, so it cannot
 // overflow.
 inline int table_sizes(const int64_t* numels, int32_t L, int32_t chunk, int64_t* N, int64_t* K,
@@ -225,7 +225,7 @@ inline int table_sizes(const int64_t* numels, int32_t L, int32_t chunk, int64_t*
   if (!numels) return fail(ONEBIT_EINVAL, "%s: NULL argument", fn);
   if (L < 1) return fail(ONEBIT_EINVAL, "%s: L = %d < 1", fn, L);
   if (!chunk_supported(chunk))
-    return fail(ONEBIT_EUNSUPPORTED, "%s: chunk %d is not a power of two in [1024, 16384]", fn,
+    return fail(ONEBIT_EUNSUPPORTED, "%s: chunk %d is not a power of two in [64, 16384]", fn,
                 chunk);
   const int64_t max_n = kMaxChunks * chunk;
   int64_t n = 0;

@@ -89,16 +89,30 @@ struct WorkerVals {
   float* v[kMaxWorkers];
 };
 
-// C elements per chunk, SPT float4 slots per thread, T = C/(4*SPT) threads.
+// C elements per chunk, SPT float4 slots per thread, T = G/(4*SPT) threads,
+// where G = max(C, 1024) is the workgroup's geometry.  A chunk shorter than
+// 1024 elements (SMALL) keeps the 1024-element geometry of one 64-wide wave
+// and lies in its first C/4 slots: every access is then guarded by the
+// chunk's length, as for a partial chunk, and the slots past it are zero.
+// The canonical tree over the padded geometry gives the chunk's own tree
+// bit for bit: its extra top levels only add +0 to sums of squares, which
+// are >= +0.
 template <int C, int SPT = 4>
 struct Geo {
-  static_assert(C >= 1024 && C <= 16384 && (C & (C - 1)) == 0, "chunk must be 2^10..2^14");
+  static_assert(C >= 64 && C <= 16384 && (C & (C - 1)) == 0, "chunk must be 2^6..2^14");
   static_assert(SPT == 1 || SPT == 2 || SPT == 4, "slots per thread");
-  static constexpr int T = C / (4 * SPT);  // threads per chunk
-  static constexpr int NW = T / 64;        // waves per chunk
-  static constexpr int WORDS = C / 32;     // sign words per chunk
+  static constexpr bool SMALL = C < 1024;
+  static constexpr int G = SMALL ? 1024 : C;  // elements a workgroup lays out
+  static constexpr int T = G / (4 * SPT);     // threads per chunk
+  static constexpr int NW = T / 64;           // waves per chunk
+  static constexpr int WORDS = C / 32 > 0 ? C / 32 : 1;  // sign words per chunk
   static_assert(T >= 64 && T <= 1024, "workgroup size");
 };
+
+// Whether a chunk takes the guarded path: the partial last chunk (block 0
+// of a launch), and every chunk shorter than the workgroup's geometry.
+template <int C>
+constexpr bool kSmall = Geo<C>::SMALL;
 
 template <int S>
 using SlotsN = float[S][4];  // [slot k][component c]
@@ -114,7 +128,10 @@ struct ChunkAt {
   __device__ __forceinline__ ChunkAt(int64_t k_, int64_t n) {
     k = k_;
     base = k * C;
-    nk = TAIL ? (int)(n - base) : C;
+    // a guarded chunk is the partial last chunk (n - base < C), or any
+    // chunk shorter than the geometry
+    if constexpr (TAIL && Geo<C>::SMALL) nk = (int)(n - base < C ? n - base : C);
+    else nk = TAIL ? (int)(n - base) : C;
   }
 };
 
@@ -289,6 +306,8 @@ __device__ __forceinline__ uint32_t or_group8(uint32_t x) {
 }
 
 // nib[k]: bit c = sign of element 4(t+T*k)+c.  words: the chunk's C/32 words.
+// A chunk shorter than the geometry owns only its first WORDS words; the
+// groups of lanes past them neither store nor load.
 template <int C, int SPT = 4>
 __device__ __forceinline__ void store_sign_words(uint32_t* __restrict__ words, const uint32_t (&nib)[SPT]) {
   constexpr int T = Geo<C, SPT>::T;
@@ -296,7 +315,8 @@ __device__ __forceinline__ void store_sign_words(uint32_t* __restrict__ words, c
 #pragma unroll
   for (int k = 0; k < SPT; ++k) {
     const uint32_t w = or_group8(nib[k] << (4 * (t & 7)));
-    if ((t & 7) == 0) words[(t + T * k) >> 3] = w;
+    const int q = (t + T * k) >> 3;
+    if ((t & 7) == 0 && (!Geo<C, SPT>::SMALL || q < Geo<C, SPT>::WORDS)) words[q] = w;
   }
 }
 
@@ -305,7 +325,11 @@ __device__ __forceinline__ void load_sign_nibbles(const uint32_t* __restrict__ w
   constexpr int T = Geo<C, SPT>::T;
   const int t = threadIdx.x;
 #pragma unroll
-  for (int k = 0; k < SPT; ++k) nib[k] = (words[(t + T * k) >> 3] >> (4 * (t & 7))) & 0xFu;
+  for (int k = 0; k < SPT; ++k) {
+    const int q = (t + T * k) >> 3;
+    nib[k] = (!Geo<C, SPT>::SMALL || q < Geo<C, SPT>::WORDS) ? (words[q] >> (4 * (t & 7))) & 0xFu
+                                                              : 0u;
+  }
 }
 
 template <int S>
@@ -509,7 +533,7 @@ __device__ __forceinline__ void compress_ef_chunk(int64_t k, int64_t n, const fl
 }
 
 template <int C, bool NT = false>
-__global__ void __launch_bounds__(C / 16)
+__global__ void __launch_bounds__(Geo<C>::T)
 k_compress_ef(int64_t n_full, int64_t n, const float* __restrict__ in, float* __restrict__ err,
               uint32_t* __restrict__ bits, float* __restrict__ scales, int32_t* status) {
   __shared__ float4 lds[2 * Geo<C>::T];
@@ -517,7 +541,7 @@ k_compress_ef(int64_t n_full, int64_t n, const float* __restrict__ in, float* __
   if (has_tail && blockIdx.x == 0)
     compress_ef_chunk<C, true, NT>(n_full, n, in, err, bits, scales, status, lds);
   else
-    compress_ef_chunk<C, false, NT>((int64_t)blockIdx.x - has_tail, n, in, err, bits, scales,
+    compress_ef_chunk<C, kSmall<C>, NT>((int64_t)blockIdx.x - has_tail, n, in, err, bits, scales,
                                     status, lds);
 }
 
@@ -560,7 +584,7 @@ __device__ __forceinline__ void average_packed_chunk(int64_t k, int64_t n, int W
 }
 
 template <int C, bool NT = false>
-__global__ void __launch_bounds__(C / 16)
+__global__ void __launch_bounds__(Geo<C>::T)
 k_average_packed(int64_t n_full, int64_t n, int W, PackedIn pin, float* __restrict__ err_s,
                  uint32_t* __restrict__ bits_out, float* __restrict__ scales_out, int32_t* status) {
   __shared__ float4 lds[2 * Geo<C>::T];
@@ -568,7 +592,7 @@ k_average_packed(int64_t n_full, int64_t n, int W, PackedIn pin, float* __restri
   if (has_tail && blockIdx.x == 0)
     average_packed_chunk<C, true, NT>(n_full, n, W, pin, err_s, bits_out, scales_out, status, lds);
   else
-    average_packed_chunk<C, false, NT>((int64_t)blockIdx.x - has_tail, n, W, pin, err_s,
+    average_packed_chunk<C, kSmall<C>, NT>((int64_t)blockIdx.x - has_tail, n, W, pin, err_s,
                                        bits_out, scales_out, status, lds);
 }
 
@@ -590,14 +614,14 @@ __device__ __forceinline__ void decompress_chunk(int64_t k, int64_t n, const uin
 }
 
 template <int C, bool NT = false>
-__global__ void __launch_bounds__(C / 16)
+__global__ void __launch_bounds__(Geo<C>::T)
 k_decompress(int64_t n_full, int64_t n, const uint32_t* __restrict__ bits,
              const float* __restrict__ scales, float* __restrict__ out) {
   const int64_t has_tail = partial_chunks<C>(n_full, n);
   if (has_tail && blockIdx.x == 0)
     decompress_chunk<C, true, NT>(n_full, n, bits, scales, out);
   else
-    decompress_chunk<C, false, NT>((int64_t)blockIdx.x - has_tail, n, bits, scales, out);
+    decompress_chunk<C, kSmall<C>, NT>((int64_t)blockIdx.x - has_tail, n, bits, scales, out);
 }
 
 // The compressed allreduce of one chunk's momentum: every worker's
@@ -800,7 +824,7 @@ k_compressed_pass_a(int64_t n_full, DevTable tab, int W, Workers wk, float* __re
                                            scales_s, seg_max, seg_z, seg_f, cf, status, lds, red,
                                            dred);
   else
-    pass_a_chunk<C, false, NT, PF, SPT, RN, PM>((int64_t)blockIdx.x - has_tail, tab, W, wk, err_s, m,
+    pass_a_chunk<C, kSmall<C>, NT, PF, SPT, RN, PM>((int64_t)blockIdx.x - has_tail, tab, W, wk, err_s, m,
                                             v_frozen, v_fresh, bits_s, scales_s, seg_max, seg_z,
                                             seg_f, cf, status, lds, red, dred);
 }
@@ -843,7 +867,7 @@ k_adam_allreduce(int64_t n_full, int64_t n, int64_t K, int W, Workers wk,
     adam_allreduce_chunk<C, true, NT, PF, SPT, PM>(n_full, n, W, wk, err_s, m, bits_s, scales_s,
                                                    cf, status, lds);
   else
-    adam_allreduce_chunk<C, false, NT, PF, SPT, PM>((int64_t)blockIdx.x - has_tail, n, W, wk,
+    adam_allreduce_chunk<C, kSmall<C>, NT, PF, SPT, PM>((int64_t)blockIdx.x - has_tail, n, W, wk,
                                                     err_s, m, bits_s, scales_s, cf, status, lds);
 }
 
@@ -914,7 +938,7 @@ __device__ __forceinline__ void worker_compress_chunk(int64_t k, int64_t n, cons
 }
 
 template <int C, bool NT = true, bool PM = false>
-__global__ void __launch_bounds__(C / 16)
+__global__ void __launch_bounds__(Geo<C>::T)
 k_worker_compress(int64_t n_full, int64_t n, const float* __restrict__ g, float* __restrict__ e,
                   const float* __restrict__ m, const uint32_t* __restrict__ bits_m,
                   const float* __restrict__ scales_m, uint32_t* __restrict__ bits_w,
@@ -925,7 +949,7 @@ k_worker_compress(int64_t n_full, int64_t n, const float* __restrict__ g, float*
     worker_compress_chunk<C, true, NT, PM>(n_full, n, g, e, m, bits_m, scales_m, bits_w, scales_w,
                                            cf, status, lds);
   else
-    worker_compress_chunk<C, false, NT, PM>((int64_t)blockIdx.x - has_tail, n, g, e, m, bits_m,
+    worker_compress_chunk<C, kSmall<C>, NT, PM>((int64_t)blockIdx.x - has_tail, n, g, e, m, bits_m,
                                             scales_m, bits_w, scales_w, cf, status, lds);
 }
 
@@ -984,7 +1008,7 @@ __device__ __forceinline__ void rescale_stats_chunk(int64_t kk, const DevTable& 
 }
 
 template <int C, bool NT = true, bool RN = false, bool PM = false>
-__global__ void __launch_bounds__(C / 16)
+__global__ void __launch_bounds__(Geo<C>::T)
 k_rescale_stats(int64_t n_full, DevTable tab, const uint32_t* __restrict__ bits_s,
                 const float* __restrict__ scales_s, const float* __restrict__ m,
                 const uint32_t* __restrict__ bits_m, const float* __restrict__ scales_m,
@@ -999,7 +1023,7 @@ k_rescale_stats(int64_t n_full, DevTable tab, const uint32_t* __restrict__ bits_
                                              v_frozen, v_fresh, seg_max, seg_z, seg_f, cf, red,
                                              dred);
   else
-    rescale_stats_chunk<C, false, NT, RN, PM>((int64_t)blockIdx.x - has_tail, tab, bits_s,
+    rescale_stats_chunk<C, kSmall<C>, NT, RN, PM>((int64_t)blockIdx.x - has_tail, tab, bits_s,
                                               scales_s, m, bits_m, scales_m, v_frozen, v_fresh,
                                               seg_max, seg_z, seg_f, cf, red, dred);
 }
@@ -1033,7 +1057,7 @@ __device__ __forceinline__ void adam_update_chunk(int64_t k, int64_t n,
 }
 
 template <int C, bool NT = true>
-__global__ void __launch_bounds__(C / 16)
+__global__ void __launch_bounds__(Geo<C>::T)
 k_adam_update(int64_t n_full, int64_t n, const uint32_t* __restrict__ bits_s,
               const float* __restrict__ scales_s, const float* __restrict__ v_frozen,
               float* __restrict__ x, float* __restrict__ m, Coef cf) {
@@ -1041,7 +1065,7 @@ k_adam_update(int64_t n_full, int64_t n, const uint32_t* __restrict__ bits_s,
   if (has_tail && blockIdx.x == 0)
     adam_update_chunk<C, true, NT>(n_full, n, bits_s, scales_s, v_frozen, x, m, cf);
   else
-    adam_update_chunk<C, false, NT>((int64_t)blockIdx.x - has_tail, n, bits_s, scales_s, v_frozen,
+    adam_update_chunk<C, kSmall<C>, NT>((int64_t)blockIdx.x - has_tail, n, bits_s, scales_s, v_frozen,
                                     x, m, cf);
 }
 
@@ -1085,14 +1109,14 @@ __device__ __forceinline__ void adam_warmup_chunk(int64_t k, int64_t n, int W, c
 }
 
 template <int C, int WPE = 1>
-__global__ void __launch_bounds__(C / 16, WPE)
+__global__ void __launch_bounds__(Geo<C>::T, WPE)
 k_adam_warmup(int64_t n_full, int64_t n, int W, Workers wk, float* __restrict__ x,
               float* __restrict__ m, float* __restrict__ v, Coef cf) {
   const int64_t has_tail = partial_chunks<C>(n_full, n);
   if (has_tail && blockIdx.x == 0)
     adam_warmup_chunk<C, true>(n_full, n, W, wk, x, m, v, cf);
   else
-    adam_warmup_chunk<C, false>((int64_t)blockIdx.x - has_tail, n, W, wk, x, m, v, cf);
+    adam_warmup_chunk<C, kSmall<C>>((int64_t)blockIdx.x - has_tail, n, W, wk, x, m, v, cf);
 }
 
 // SLAMB-style sparse compression stage, one pass per chunk.  The chunk's
@@ -1126,7 +1150,7 @@ __device__ __forceinline__ void sparse_chunk(int64_t kk, const DevTable& tab, in
   for (int a = 0; a < 4; ++a) {
     const int p = t + T * a;                    // float4 slot; block p/16
     const int rel = ((p / 16) - b0 + NB) % NB;
-    pos[a] = rel < nsel ? rel * 64 + 4 * (p % 16) : -1;
+    pos[a] = ((!Geo<C>::SMALL || p < C / 4) && rel < nsel) ? rel * 64 + 4 * (p % 16) : -1;
   }
 
   Slots bm, acc;
@@ -1245,7 +1269,7 @@ __device__ __forceinline__ void sparse_positions(int32_t sel_k, int nsel, int (&
   for (int a = 0; a < 4; ++a) {
     const int p = (int)threadIdx.x + T * a;
     const int rel = ((p / 16) - b0 + NB) % NB;
-    pos[a] = rel < nsel ? rel * 64 + 4 * (p % 16) : -1;
+    pos[a] = ((!Geo<C>::SMALL || p < C / 4) && rel < nsel) ? rel * 64 + 4 * (p % 16) : -1;
   }
 }
 
@@ -1285,7 +1309,7 @@ __device__ __forceinline__ void sparse_worker_chunk(int64_t k, int64_t n, int ns
 }
 
 template <int C, bool NT = true>
-__global__ void __launch_bounds__(C / 16)
+__global__ void __launch_bounds__(Geo<C>::T)
 k_sparse_worker(int64_t n_full, int64_t n, int nsel, const int32_t* __restrict__ sel,
                 const float* __restrict__ g, float* __restrict__ e, const float* __restrict__ m,
                 float* __restrict__ vals, Coef cf) {
@@ -1293,7 +1317,7 @@ k_sparse_worker(int64_t n_full, int64_t n, int nsel, const int32_t* __restrict__
   if (has_tail && blockIdx.x == 0)
     sparse_worker_chunk<C, true, NT>(n_full, n, nsel, sel, g, e, m, vals, cf);
   else
-    sparse_worker_chunk<C, false, NT>((int64_t)blockIdx.x - has_tail, n, nsel, sel, g, e, m, vals,
+    sparse_worker_chunk<C, kSmall<C>, NT>((int64_t)blockIdx.x - has_tail, n, nsel, sel, g, e, m, vals,
                                       cf);
 }
 
@@ -1406,7 +1430,7 @@ __device__ __forceinline__ void sparse_update_chunk(int64_t kk, const DevTable& 
 }
 
 template <int C, bool NT = true>
-__global__ void __launch_bounds__(C / 16)
+__global__ void __launch_bounds__(Geo<C>::T)
 k_sparse_update(int64_t n_full, DevTable tab, int nsel, const int32_t* __restrict__ sel,
                 const float* __restrict__ vals_s, float* __restrict__ x, float* __restrict__ m,
                 const float* __restrict__ v_frozen, float* __restrict__ v_fresh,
@@ -1416,13 +1440,13 @@ k_sparse_update(int64_t n_full, DevTable tab, int nsel, const int32_t* __restric
     sparse_update_chunk<C, true, NT>(n_full, tab, nsel, sel, vals_s, x, m, v_frozen, v_fresh,
                                      c_avg, cf, status);
   else
-    sparse_update_chunk<C, false, NT>((int64_t)blockIdx.x - has_tail, tab, nsel, sel, vals_s, x, m,
+    sparse_update_chunk<C, kSmall<C>, NT>((int64_t)blockIdx.x - has_tail, tab, nsel, sel, vals_s, x, m,
                                       v_frozen, v_fresh, c_avg, cf, status);
 }
 
 // One workgroup per chunk; block 0 takes the partial last chunk, if any.
 template <int C, bool NT = true, int WPE = 1>
-__global__ void __launch_bounds__(C / 16, WPE)
+__global__ void __launch_bounds__(Geo<C>::T, WPE)
 k_sparse_step(int64_t n_full, DevTable tab, int W, int nsel, const int32_t* __restrict__ sel,
               Workers wk, WorkerVals vals_w, float* __restrict__ x, float* __restrict__ m,
               const float* __restrict__ v_frozen, float* __restrict__ v_fresh,
@@ -1433,7 +1457,7 @@ k_sparse_step(int64_t n_full, DevTable tab, int W, int nsel, const int32_t* __re
     sparse_chunk<C, true, NT>(n_full, tab, W, nsel, sel, wk, vals_w, x, m, v_frozen, v_fresh,
                               c_avg, vals_s, cf, status);
   else
-    sparse_chunk<C, false, NT>((int64_t)blockIdx.x - has_tail, tab, W, nsel, sel, wk, vals_w, x, m,
+    sparse_chunk<C, kSmall<C>, NT>((int64_t)blockIdx.x - has_tail, tab, W, nsel, sel, wk, vals_w, x, m,
                                v_frozen, v_fresh, c_avg, vals_s, cf, status);
 }
 
@@ -1531,7 +1555,7 @@ __device__ __forceinline__ void pass_b_chunk(int64_t kk, const DevTable& tab,
 }
 
 template <int C, bool NT = false>
-__global__ void __launch_bounds__(C / 16)
+__global__ void __launch_bounds__(Geo<C>::T)
 k_compressed_pass_b(int64_t n_full, DevTable tab, const uint32_t* __restrict__ bits_s,
                     const float* __restrict__ scales_s, const float* __restrict__ v_frozen,
                     float* __restrict__ x, float* __restrict__ m, const float* __restrict__ c_layer,
@@ -1540,7 +1564,7 @@ k_compressed_pass_b(int64_t n_full, DevTable tab, const uint32_t* __restrict__ b
   if (has_tail && blockIdx.x == 0)
     pass_b_chunk<C, true, NT>(n_full, tab, bits_s, scales_s, v_frozen, x, m, c_layer, cf);
   else
-    pass_b_chunk<C, false, NT>((int64_t)blockIdx.x - has_tail, tab, bits_s, scales_s, v_frozen, x,
+    pass_b_chunk<C, kSmall<C>, NT>((int64_t)blockIdx.x - has_tail, tab, bits_s, scales_s, v_frozen, x,
                                m, c_layer, cf);
 }
 
@@ -1596,7 +1620,7 @@ __device__ __forceinline__ void warmup_pass1_chunk(int64_t k, const DevTable& ta
 }
 
 template <int C, bool NT = false, int WPE = 1, bool XS = false>
-__global__ void __launch_bounds__(C / 16, WPE)
+__global__ void __launch_bounds__(Geo<C>::T, WPE)
 k_warmup_pass1(int64_t n_full, DevTable tab, int W, Workers wk, const float* __restrict__ x,
                float* __restrict__ m, float* __restrict__ v, double* __restrict__ seg_x,
                double* __restrict__ seg_u, Coef cf) {
@@ -1605,7 +1629,7 @@ k_warmup_pass1(int64_t n_full, DevTable tab, int W, Workers wk, const float* __r
   if (has_tail && blockIdx.x == 0)
     warmup_pass1_chunk<C, true, NT, XS>(n_full, tab, W, wk, x, m, v, seg_x, seg_u, cf, red);
   else
-    warmup_pass1_chunk<C, false, NT, XS>((int64_t)blockIdx.x - has_tail, tab, W, wk, x, m, v,
+    warmup_pass1_chunk<C, kSmall<C>, NT, XS>((int64_t)blockIdx.x - has_tail, tab, W, wk, x, m, v,
                                          seg_x, seg_u, cf, red);
 }
 
@@ -1666,7 +1690,7 @@ __device__ __forceinline__ void warmup_pass2_chunk(int64_t k, const DevTable& ta
 }
 
 template <int C, bool NT = false, bool XO = false>
-__global__ void __launch_bounds__(C / 16)
+__global__ void __launch_bounds__(Geo<C>::T)
 k_warmup_pass2(int64_t n_full, DevTable tab, const float* __restrict__ m, const float* __restrict__ v,
                float* __restrict__ x, const float* __restrict__ c_layer, double* __restrict__ x_sq,
                Coef cf) {
@@ -1675,7 +1699,7 @@ k_warmup_pass2(int64_t n_full, DevTable tab, const float* __restrict__ m, const 
   if (has_tail && blockIdx.x == 0)
     warmup_pass2_chunk<C, true, NT, XO>(n_full, tab, m, v, x, c_layer, x_sq, cf, red);
   else
-    warmup_pass2_chunk<C, false, NT, XO>((int64_t)blockIdx.x - has_tail, tab, m, v, x, c_layer,
+    warmup_pass2_chunk<C, kSmall<C>, NT, XO>((int64_t)blockIdx.x - has_tail, tab, m, v, x, c_layer,
                                          x_sq, cf, red);
 }
 
@@ -1698,14 +1722,14 @@ __device__ __forceinline__ void freeze_elems_chunk(int64_t k, int64_t n, int W,
 }
 
 template <int C>
-__global__ void __launch_bounds__(C / 16)
+__global__ void __launch_bounds__(Geo<C>::T)
 k_freeze_elems(int64_t n_full, int64_t n, int W, const float* __restrict__ v,
                float* __restrict__ v_fresh, Workers wk, float* __restrict__ err_s) {
   const int64_t has_tail = partial_chunks<C>(n_full, n);
   if (has_tail && blockIdx.x == 0)
     freeze_elems_chunk<C, true>(n_full, n, W, v, v_fresh, wk, err_s);
   else
-    freeze_elems_chunk<C, false>((int64_t)blockIdx.x - has_tail, n, W, v, v_fresh, wk, err_s);
+    freeze_elems_chunk<C, kSmall<C>>((int64_t)blockIdx.x - has_tail, n, W, v, v_fresh, wk, err_s);
 }
 
 // Freeze, tensor part: c_avg = c_sum / den (den = T_w, or 1-d^T_w for the

@@ -33,7 +33,8 @@ static int g_fail = 0;
     }                                                       \
   } while (0)
 
-static const int32_t kChunks[] = {1024, 2048, 4096, 8192, 16384};
+static const int32_t kChunks[] = {64, 128, 256, 512, 1024, 2048, 4096, 8192, 16384};
+static const int kNChunks = sizeof kChunks / sizeof kChunks[0];
 
 // ---------------------------------------------------------------------------
 // tables
@@ -111,7 +112,7 @@ static std::vector<int64_t> random_numels(std::mt19937_64& r, int32_t chunk) {
 static void fuzz_tables() {
   std::mt19937_64 r(1);
   for (int it = 0; it < 400; ++it) {
-    const int32_t chunk = kChunks[it % 5];
+    const int32_t chunk = kChunks[it % kNChunks];
     check_table(random_numels(r, chunk), chunk, it % 4 == 0);
   }
   // edge shapes: one element, exactly one chunk, one chunk plus one, many
@@ -164,12 +165,12 @@ static void fuzz_table_sizes() {
   }
   int64_t N, K;
   std::vector<int64_t> v = {100};
-  for (int32_t c : {0, -4096, 512, 1000, 3000, 32768, 4097, INT32_MIN, INT32_MAX})
+  for (int32_t c : {0, -4096, 32, 1, 1000, 3000, 32768, 4097, 96, INT32_MIN, INT32_MAX})
     EXPECT(table_sizes(v.data(), 1, c, &N, &K, "f") == ONEBIT_EUNSUPPORTED, "chunk %d", c);
   // random sizes near the bound against a 128-bit sum
   std::mt19937_64 r(2);
   for (int it = 0; it < 20000; ++it) {
-    const int32_t chunk = kChunks[r() % 5];
+    const int32_t chunk = kChunks[r() % kNChunks];
     const int L = 1 + (int)(r() % 6);
     std::vector<int64_t> n(L);
     for (int l = 0; l < L; ++l) {
@@ -217,7 +218,7 @@ static void fuzz_scalars() {
                            kMaxChunks * 1024, kMaxChunks * 1024 + 1, kMaxChunks * 16384,
                            kMaxChunks * 16384 + 1};
   for (int it = 0; it < 200000; ++it) {
-    const int64_t chunk = kChunks[r() % 5];
+    const int64_t chunk = kChunks[r() % kNChunks];
     int64_t n;
     if (it < (int)(sizeof edges / sizeof edges[0])) n = edges[it];
     else if (r() % 2) n = (int64_t)r();
@@ -240,7 +241,8 @@ static void fuzz_scalars() {
   EXPECT(check_W(INT32_MIN, "f") == ONEBIT_EUNSUPPORTED && check_W(INT32_MAX, "f") == ONEBIT_EUNSUPPORTED,
          "check_W extremes");
   for (int32_t c = -70000; c <= 70000; ++c)
-    EXPECT(chunk_supported(c) == (c == 1024 || c == 2048 || c == 4096 || c == 8192 || c == 16384),
+    EXPECT(chunk_supported(c) == (c == 64 || c == 128 || c == 256 || c == 512 || c == 1024 ||
+                                  c == 2048 || c == 4096 || c == 8192 || c == 16384),
            "chunk_supported(%d)", c);
   // error text is kept per thread and cleared by a success
   fail(ONEBIT_EINVAL, "msg %d", 7);

@@ -51,7 +51,7 @@ def test_argument_checks(ob):
     assert lib.onebit_compress_ef(-1, 4096, None, None, None, None, None, None) == ob.ONEBIT_EINVAL
     assert lib.onebit_compress_ef(10, 1000, None, None, None, None, None, None) == \
         ob.ONEBIT_EUNSUPPORTED
-    assert lib.onebit_compress_ef(10, 512, None, None, None, None, None, None) == \
+    assert lib.onebit_compress_ef(10, 32, None, None, None, None, None, None) == \
         ob.ONEBIT_EUNSUPPORTED
     assert lib.onebit_compress_ef(10, 4096, None, P(4096), P(4096), P(4096), None, None) == \
         ob.ONEBIT_EINVAL

@@ -64,7 +64,7 @@ TABLES = [[1], [10, 20, 30], [4096 * 2 + 7, 3, 1000], [1, 3, 4095, 4097, 100, 81
 
 
 @pytest.mark.parametrize("numels", TABLES)
-@pytest.mark.parametrize("chunk", [1024, 4096])
+@pytest.mark.parametrize("chunk", [64, 256, 1024, 4096])
 @pytest.mark.parametrize("W", [1, 3])
 def test_lamb_entry_points_stay_in_bounds(numels, chunk, W):
     table = ob.LayerTable(numels, chunk)
@@ -126,8 +126,8 @@ def test_lamb_entry_points_stay_in_bounds(numels, chunk, W):
 
 @pytest.mark.parametrize("n", [1, 1000, 3 * 4096 + 5])
 @pytest.mark.parametrize("W", [1, 4])
-def test_adam_entry_points_stay_in_bounds(n, W):
-    chunk = 4096
+@pytest.mark.parametrize("chunk", [128, 4096])
+def test_adam_entry_points_stay_in_bounds(n, W, chunk):
     K = (n + chunk - 1) // chunk
     words = K * chunk // 32
     A = Arena()
@@ -159,8 +159,9 @@ def test_adam_entry_points_stay_in_bounds(n, W):
 
 @pytest.mark.parametrize("numels", TABLES)
 @pytest.mark.parametrize("nsel", [1, 3])
-def test_sparse_entry_point_stays_in_bounds(numels, nsel):
-    W, chunk = 3, 4096
+@pytest.mark.parametrize("chunk", [256, 4096])
+def test_sparse_entry_point_stays_in_bounds(numels, nsel, chunk):
+    W = 3
     table = ob.LayerTable(numels, chunk)
     N, K, L = table.N, table.K, len(numels)
     wl = Workload("bounds", numels, W=W, chunk=chunk)
@@ -193,11 +194,11 @@ def test_sparse_entry_point_stays_in_bounds(numels, nsel):
 
 @pytest.mark.parametrize("numels", TABLES)
 @pytest.mark.parametrize("W", [1, 3])
-def test_share_entry_points_stay_in_bounds(numels, W):
+@pytest.mark.parametrize("chunk", [128, 4096])
+def test_share_entry_points_stay_in_bounds(numels, W, chunk):
     """The per-GPU entry points (worker compression, a chunk range served,
     receiver statistics and update, the Adam receiver update) touch only
     their arguments, and write their packed outputs in full."""
-    chunk = 4096
     table = ob.LayerTable(numels, chunk)
     N, K, L = table.N, table.K, len(numels)
     words = K * chunk // 32
@@ -260,10 +261,11 @@ def test_share_entry_points_stay_in_bounds(numels, W):
 
 @pytest.mark.parametrize("numels", TABLES)
 @pytest.mark.parametrize("nsel", [1, 3])
-def test_sparse_share_entry_points_stay_in_bounds(numels, nsel):
+@pytest.mark.parametrize("chunk", [256, 4096])
+def test_sparse_share_entry_points_stay_in_bounds(numels, nsel, chunk):
     """The sparse stage's per-GPU entry points touch only their arguments
     and write the transmitted values and their means in full."""
-    W, chunk = 3, 4096
+    W = 3
     table = ob.LayerTable(numels, chunk)
     N, K, L = table.N, table.K, len(numels)
     wl = Workload("bounds", numels, W=W, chunk=chunk)

@@ -34,10 +34,10 @@ def _table(r, chunk):
     return sizes
 
 
-@pytest.mark.parametrize("seed", range(40))
+@pytest.mark.parametrize("seed", range(60))
 def test_random_table(seed):
     r = np.random.default_rng(1000 + seed)
-    chunk = int(r.choice([1024, 2048, 4096, 8192, 16384]))
+    chunk = int(r.choice([64, 128, 256, 512, 1024, 2048, 4096, 8192, 16384]))
     W = int(r.integers(1, 17))
     numels = _table(r, chunk)
     mode = ["lamb", "lamb", "adam", "sparse", "share"][seed % 5]

@@ -1,0 +1,181 @@
+"""Chunks of 64, 128, 256 and 512 elements on the GPU, against the oracle.
+
+A chunk shorter than 1024 elements runs on the workgroup shape of a
+1024-element chunk, one wave per chunk, with the positions past the chunk
+treated as zeros: the stride-halving norm tree of the chunk is then
+unchanged, since the extra levels add exact zeros to non-negative partial
+sums, so signs, scales and errors must match the oracle bit for bit, as for
+the longer chunks.  Every entry point family is covered: the codec, the LAMB
+warmup (plain and with the norm carried), the freeze, the compression step
+with fp32 and with packed momentum under both rho rules, the 1-bit Adam mode,
+the sparse stage, and one GPU's share equal to the fused step.  Tables are
+ragged, so chunks straddle tensors and the last chunk is partial.
+"""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("no GPU", allow_module_level=True)
+
+import communication_compressed_optimizer_amd as ob  # noqa: E402
+import oracle  # noqa: E402
+from synth.workloads import Workload  # noqa: E402
+
+from tests.harness import (DevRun, HostRun, assert_parity, compare_adam,  # noqa: E402
+                           compare_sparse, compare_state)
+from tests.test_gpu_sharded import Sharded, _assert_equals_fused  # noqa: E402
+
+SMALL = [64, 128, 256, 512]
+
+
+def _normals(n, seed, std=1.0):
+    return (np.random.default_rng(seed).standard_normal(n) * std).astype(np.float32)
+
+
+def _dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _bits(t):
+    return t.cpu().numpy().view(np.uint32)
+
+
+def _table(C):
+    """Tensors shorter than, equal to and longer than a chunk, straddling
+    chunk boundaries, ending in a partial chunk."""
+    return [1, 3, C - 1, C + 1, 100, 2 * C, 17, 5 * C + C // 2 + 9]
+
+
+@pytest.mark.parametrize("C", SMALL)
+@pytest.mark.parametrize("n_of", [lambda C: 1, lambda C: C - 1, lambda C: C,
+                                  lambda C: 7 * C + 5, lambda C: 100_003],
+                         ids=["1", "C-1", "C", "7C+5", "100003"])
+def test_codec_small_chunks(C, n_of):
+    n = n_of(C)
+    K = oracle.num_chunks(n, C)
+    inp, err = _normals(n, 11, 1e-3), _normals(n, 12, 1e-4)
+    inp[::97] = 0.0
+    d_in, d_err = _dev(inp), _dev(err)
+    d_bits = torch.full((K * C // 32,), -1, dtype=torch.int32, device="cuda")
+    d_sc = torch.full((K,), float("nan"), dtype=torch.float32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ob.onebit_compress_ef(n, C, d_in, d_err, d_bits, d_sc, status)
+    bits, scales = oracle.compress_ef(inp, err, C)
+    assert np.array_equal(_bits(d_bits), bits)
+    assert np.array_equal(_bits(d_sc), scales.view(np.uint32))
+    assert np.array_equal(_bits(d_err), err.view(np.uint32))
+    # the server's average of W = 3 packed workers, recompressed with its error
+    W = 3
+    bits_w, scales_w = [], []
+    for w in range(W):
+        b, s = oracle.compress_ef(_normals(n, 100 + w, 1e-3), np.zeros(n, np.float32), C)
+        bits_w.append(b)
+        scales_w.append(s)
+    err_s = _normals(n, 200, 1e-4)
+    d_err_s = _dev(err_s)
+    ob.onebit_average_packed(n, C, W, [_dev(b.view(np.int32)) for b in bits_w],
+                             [_dev(s) for s in scales_w], d_err_s, d_bits, d_sc, status)
+    b, s = oracle.average_packed(bits_w, scales_w, err_s, C)
+    assert np.array_equal(_bits(d_bits), b)
+    assert np.array_equal(_bits(d_sc), s.view(np.uint32))
+    assert np.array_equal(_bits(d_err_s), err_s.view(np.uint32))
+    out = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
+    ob.onebit_decompress(n, C, d_bits, d_sc, out)
+    assert np.array_equal(out.cpu().numpy(), oracle.decompress(b, s, n, C))
+    assert int(status.item()) == 0
+
+
+@pytest.mark.parametrize("C", SMALL)
+@pytest.mark.parametrize("W", [1, 4])
+def test_lamb_trajectory_small_chunks(C, W):
+    """Three warmup steps (the norm carried for W = 4), the freeze, then
+    compression steps with fp32 momentum, packed momentum and the norm-ratio
+    rho rule, GPU and oracle each on their own state."""
+    wl = Workload("small", _table(C), W=W, chunk=C, init="fresh", grad_std=0.02)
+    d, h = DevRun(wl, carry_norm=W > 1), HostRun(wl)
+    step = 0
+    for _ in range(3):
+        d.warmup_step(step)
+        h.warmup_step(step)
+        step += 1
+    assert_parity(compare_state(d, h, stage="warmup"), "after warmup")
+    d.freeze(3)
+    h.freeze(3)
+    for packed in (False, True):
+        d.compressed_step(step, packed=packed)
+        h.compressed_step(step)
+        step += 1
+        if packed:
+            d.m.copy_(d.momentum_from_packed())
+        assert_parity(compare_state(d, h), f"step {step - 1}, packed={packed}")
+    d.hp.rho_mode = h.hp.rho_mode = ob.ONEBIT_RHO_NORM_RATIO
+    d.compressed_step(step)
+    h.compressed_step(step)
+    assert_parity(compare_state(d, h), "norm-ratio rho")
+    assert int(d.status.item()) == 0
+
+
+@pytest.mark.parametrize("C", SMALL)
+def test_compressed_step_exact_small_chunks(C):
+    """From a frozen state the compression step has no order-dependent sum:
+    two steps, W = 8, every array exact."""
+    wl = Workload("small", _table(C), W=8, chunk=C, init="frozen", grad_std=1e-3)
+    d, h = DevRun(wl), HostRun(wl)
+    for step in range(2):
+        d.compressed_step(step)
+        h.compressed_step(step)
+        rep = compare_state(d, h)
+        assert_parity(rep, f"step {step}")
+        assert rep["x"]["max_abs"] == 0.0
+
+
+@pytest.mark.parametrize("C", SMALL)
+def test_adam_small_chunks(C):
+    wl = Workload("small", [9 * C + 7], W=4, chunk=C, init="fresh", grad_std=0.02)
+    d, h = DevRun(wl), HostRun(wl)
+    step = 0
+    for _ in range(2):
+        d.adam_warmup_step(step)
+        h.adam_warmup_step(step)
+        step += 1
+    for packed in (False, True):
+        d.adam_compressed_step(step, packed=packed)
+        h.adam_compressed_step(step)
+        step += 1
+        if packed:
+            d.m.copy_(d.momentum_from_packed())
+        assert_parity(compare_adam(d, h), f"step {step - 1}, packed={packed}")
+
+
+@pytest.mark.parametrize("C", SMALL)
+def test_sparse_small_chunks(C):
+    """The sparse stage with one block and with every block of the chunk
+    transmitted (nsel = 1 and nsel = C/64)."""
+    for nsel in sorted({1, C // 64}):
+        wl = Workload("small", _table(C), W=3, chunk=C, init="frozen")
+        d, h = DevRun(wl), HostRun(wl)
+        for step in range(2):
+            d.sparse_step(step, nsel)
+            h.sparse_step(step, nsel)
+            assert_parity(compare_sparse(d, h), f"nsel {nsel}, step {step}")
+        assert int(d.status.item()) == 0
+
+
+@pytest.mark.parametrize("C", SMALL)
+def test_share_small_chunks(C):
+    """One GPU's share entry points equal the fused step bit for bit (fp32
+    momentum, then packed)."""
+    wl = Workload("small", _table(C), W=3, chunk=C, init="frozen")
+    f, s = DevRun(wl), DevRun(wl)
+    sh = Sharded(s)
+    for step in range(2):
+        packed = step > 0
+        f.fill_grads(step)
+        s.fill_grads(step)
+        f.compressed_step(step, fill=False, packed=packed)
+        sh.step(packed=packed)
+        torch.cuda.synchronize()
+        _assert_equals_fused(sh, f, packed)
