@@ -172,7 +172,10 @@ void launch_chunks(int64_t n, hipStream_t st, KF k, A... args) {
 // 7-wave cap 7.44, 8-wave cap 7.89 -- the cap's spills are reloaded every
 // worker iteration, so the best cap depends on where they land; prefetching
 // the next worker, keeping beta1*m in LDS, or keeping the workers' signs in
-// LDS and summing after the loop (no spills, 3.5% slower) did not help).
+// LDS and summing after the loop (no spills, 3.5% slower) did not help; nor
+// did a persistent grid of one workgroup per CU that loads the next chunk's
+// m, g_0 and e_0 across the current chunk's server reduction: within 1%,
+// and slower at other grid sizes or with contiguous chunk ranges).
 constexpr bool kPassA_NT = true;   // streaming loads and stores
 constexpr bool kPassA_PF = false;  // next-worker prefetch
 constexpr int kPassA_WPE = 6;      // minimum waves per SIMD
