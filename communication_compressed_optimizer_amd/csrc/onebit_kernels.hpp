@@ -7,7 +7,9 @@
 // a kernel says otherwise: T = C/16); thread t owns the slots p = t + T*k
 // (k = 0..SPT-1) of its chunk, i.e. chunk elements 4p..4p+3.  The loads and
 // stores of a wave are therefore 64 consecutive float4 (1 KiB) per slot:
-// fully coalesced dwordx4 traffic.
+// fully coalesced dwordx4 traffic.  A chunk shorter than 1024 elements keeps
+// the 1024-element geometry (one wave) with the chunk in its first C/4
+// slots (struct Geo below).
 //
 // Chunk scale.  The sum of squares of a chunk is the stride-halving tree
 // t[j] += t[j+h], h = C/2, ..., 1 (zero past the last valid element), which
@@ -120,7 +122,8 @@ using Slots = SlotsN<4>;
 
 // Chunk k of an n-element buffer.  Chunk code is instantiated twice: for the
 // full chunks (TAIL = false: nk == C at compile time, no guards) and for the
-// one partial last chunk (TAIL = true).
+// one partial last chunk (TAIL = true).  Chunks shorter than the workgroup's
+// geometry (Geo::SMALL) take the guarded instantiation for every chunk.
 template <int C, bool TAIL>
 struct ChunkAt {
   int64_t k, base;
