@@ -480,6 +480,10 @@ def main():
         "cpu_baseline": cpu,
         "cpu_baseline_by_step": cpu_by_step or None,
         "cpu_baseline_by_config": cpu_by_config,
+        "readings": "the compression-stage rescale (reconstructed gradient, fresh variance, "
+                    "rho as the per-tensor maximum of the ratio, the soft thresholds) is a "
+                    "reading of the 1-bit LAMB page's prose, which prints no formula for it; "
+                    "GPU and oracle agree on that reading, not on a printed equation",
     }
     print(json.dumps(out), flush=True)
 
@@ -906,6 +910,9 @@ def bench_sparse(args, wl, ob, torch, table, hp, g, e, x, m, v, vf, c_avg, statu
                      "algorithmic_bytes": abytes},
         "runtime_copy": _ceiling(torch, stream, achieved),
         "cpu_baseline": cpu,
+        "readings": "the sparse stage is a reading of the SLAMB page's abstract (a masked "
+                    "momentum, error compensation on each worker, an element-wise rescale), "
+                    "which gives no algorithm in detail; GPU and oracle agree on that reading",
     }
     print(json.dumps(out), flush=True)
 
