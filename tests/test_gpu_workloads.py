@@ -6,6 +6,9 @@ compared for the tensors wholly inside a window).  Inputs of both sides come
 from the same seeded generator (device fill on the GPU, host fill for the
 oracle, bit-identical by construction and by test_synth_device_matches_host).
 """
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 
@@ -70,39 +73,80 @@ def covering_windows(wl, chunks=16384):
     return [(lo * C, min(N, hi * C)) for lo, hi in wins]
 
 
-@pytest.mark.timeout(900)
-def test_bert_large_whole_buffer():
-    """BERT-Large table, W = 8, one compression step, compared against the
-    oracle over the WHOLE buffer: every chunk's signs, scales and errors of
-    all eight workers and of the server, m, v_fresh, and the parameters and
-    per-tensor coefficients of every tensor (the oracle runs consecutive
-    windows so host memory stays bounded).  Under error feedback a wrong sign
-    anywhere is carried into every later step ("1-bit LAMB" page, Related
-    work), so no chunk is left to sampling."""
-    wl = WORKLOADS["bert_large"]
-    wins = covering_windows(wl)
+def whole_buffer_parity(d, wl, run_host, stage="compression", chunks=8192, threads=4):
+    """Compare the GPU state d with the oracle over the WHOLE buffer.  The
+    oracle runs covering_windows(wl, chunks), each window on its own state
+    (run_host(h) steps it), on a few threads: the oracle and the input
+    generator are C calls that release the interpreter lock, and a few
+    windows at a time keep host memory bounded.  Every chunk-local array is
+    compared element by element, and the per-tensor values on every tensor
+    (each lies wholly inside some window)."""
     C, off = wl.chunk, wl.offsets
+    wins = covering_windows(wl, chunks)
     covered = np.zeros(wl.K, bool)
     whole = np.zeros(wl.L, bool)
     for lo, hi in wins:
         covered[lo // C:-(-hi // C)] = True
         whole |= (off[:-1] >= lo) & (off[1:] <= hi)
     assert covered.all() and whole.all()
+    torch.cuda.synchronize()
+
+    def one(win):
+        lo, hi = win
+        h = HostRun(wl, lo, hi)
+        run_host(h)
+        rep = compare_state(d, h, stage=stage)
+        return lo, hi, rep, -(-hi // C) - lo // C, h.full.size
+
+    n_chunks = n_tensors = 0
+    with ThreadPoolExecutor(max(1, min(threads, os.cpu_count() or 1))) as ex:
+        for lo, hi, rep, nc, nt in ex.map(one, wins):
+            assert_parity(rep, f"window [{lo}, {hi})")
+            last = f"bits_w{wl.W - 1}"
+            if last in rep:                         # every worker sign word of the window
+                assert rep[last]["n"] == nc * C // 32
+            n_chunks += nc
+            n_tensors += nt
+    assert n_chunks >= wl.K and n_tensors >= wl.L
+    return wins
+
+
+@pytest.mark.timeout(900)
+def test_bert_large_whole_buffer():
+    """BERT-Large table, W = 8, one compression step, compared against the
+    oracle over the WHOLE buffer: every chunk's signs, scales and errors of
+    all eight workers and of the server, m, v_fresh, and the parameters and
+    per-tensor coefficients of every tensor.  Under error feedback a wrong
+    sign anywhere is carried into every later step ("1-bit LAMB" page,
+    Related work), so no chunk is left to sampling."""
+    wl = WORKLOADS["bert_large"]
     d = DevRun(wl)
     d.compressed_step(0)
     torch.cuda.synchronize()
     assert int(d.status.item()) == 0
-    n_chunks = n_tensors = 0
-    for lo, hi in wins:
-        h = HostRun(wl, lo, hi)
-        h.compressed_step(0)
-        rep = compare_state(d, h)
-        assert_parity(rep, f"window [{lo}, {hi})")
-        assert rep["bits_w7"]["n"] == (-(-hi // C) - lo // C) * C // 32
-        n_chunks += -(-hi // C) - lo // C
-        n_tensors += h.full.size
-        del h
-    assert n_chunks >= wl.K and n_tensors >= wl.L
+    whole_buffer_parity(d, wl, lambda h: h.compressed_step(0))
+
+
+@pytest.mark.timeout(900)
+def test_mixed_warmup_whole_buffer():
+    """BERT-Large table with per-tensor gradient scales, W = 8: two LAMB
+    warmup steps, the second with the parameters' squared norm carried over
+    from the first, compared against the oracle over the whole buffer: m and
+    v of every element bit for bit, and the parameters, trust ratios and
+    their running sums of every tensor within the bar (the segment sums of
+    the carried norm are indexed deep into the table here)."""
+    wl = WORKLOADS["mixed"]
+    d = DevRun(wl, carry_norm=True)
+    for step in range(2):
+        d.warmup_step(step)
+    torch.cuda.synchronize()
+    assert int(d.status.item()) == 0
+
+    def run_host(h):
+        for step in range(2):
+            h.warmup_step(step)
+
+    whole_buffer_parity(d, wl, run_host, stage="warmup")
 
 
 def test_mixed_warmup_to_compression():
@@ -135,9 +179,11 @@ def test_mixed_warmup_to_compression():
     assert int(d.status.item()) == 0
 
 
+@pytest.mark.timeout(1200)
 def test_bert_xl_step():
     """BERT-XL table (2.83e9 parameters, W = 4, about 150 GB of state): one
-    compression step, windows checked."""
+    compression step compared against the oracle over the whole buffer
+    (691,493 chunks, element indices up to 2.83e9)."""
     torch.cuda.empty_cache()
     wl = WORKLOADS["bert_xl"]
     free, _ = torch.cuda.mem_get_info()
@@ -147,12 +193,9 @@ def test_bert_xl_step():
     d = DevRun(wl, store_worker_bits=False)
     d.compressed_step(0)
     torch.cuda.synchronize()
-    for lo, hi in block_windows(wl, chunks=64):
-        h = HostRun(wl, lo, hi)
-        h.compressed_step(0)
-        rep = compare_state(d, h)
-        assert_parity(rep, f"window [{lo}, {hi})")
     assert int(d.status.item()) == 0
+    wins = whole_buffer_parity(d, wl, lambda h: h.compressed_step(0))
+    assert wins[-1][1] == wl.N > 2**31
     del d
     torch.cuda.empty_cache()
 
