@@ -107,7 +107,7 @@ struct Geo {
   static constexpr int G = SMALL ? 1024 : C;  // elements a workgroup lays out
   static constexpr int T = G / (4 * SPT);     // threads per chunk
   static constexpr int NW = T / 64;           // waves per chunk
-  static constexpr int WORDS = C / 32 > 0 ? C / 32 : 1;  // sign words per chunk
+  static constexpr int WORDS = C / 32;        // sign words per chunk
   static_assert(T >= 64 && T <= 1024, "workgroup size");
 };
 
