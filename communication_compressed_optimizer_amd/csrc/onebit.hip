@@ -28,6 +28,7 @@ struct onebit_layer_table {
   int64_t K = 0;
   int64_t S = 0;  // (chunk, tensor) segments
   int device = -1;  // the device that holds dblock
+  int cus = 0;      // its compute units (sizes the persistent pass-A grid)
   void* dblock = nullptr;
   DevTable dev{};
 };
@@ -172,14 +173,24 @@ void launch_chunks(int64_t n, hipStream_t st, KF k, A... args) {
 // 7-wave cap 7.44, 8-wave cap 7.89 -- the cap's spills are reloaded every
 // worker iteration, so the best cap depends on where they land; prefetching
 // the next worker, keeping beta1*m in LDS, or keeping the workers' signs in
-// LDS and summing after the loop (no spills, 3.5% slower) did not help; nor
-// did a persistent grid of one workgroup per CU that loads the next chunk's
-// m, g_0 and e_0 across the current chunk's server reduction: within 1%,
-// and slower at other grid sizes or with contiguous chunk ranges).
+// LDS and summing after the loop (no spills, 3.5% slower) did not help; a
+// persistent grid of one workgroup per CU that loads only the next chunk's
+// m, g_0 and e_0 across the current chunk's server reduction came within 1%,
+// and was slower at other grid sizes or with contiguous chunk ranges).
 constexpr bool kPassA_NT = true;   // streaming loads and stores
 constexpr bool kPassA_PF = false;  // next-worker prefetch
 constexpr int kPassA_WPE = 6;      // minimum waves per SIMD
 constexpr int kPassA_SPT = 4;      // float4 slots per thread (workgroup = C / (4 * SPT))
+// Chunks of 4096 elements run pass A as a persistent grid with two workers
+// and the next chunk's first three in flight (k_compressed_pass_a_ring): at
+// BERT-Large, W = 8, interleaved against one workgroup per chunk on seven
+// boxes, 0.7-4.2% faster (7.05-7.16 against 7.16-7.38 ms; the larger gains
+// on the boxes where the 30-stream pattern runs slowest), outputs
+// identical.  At 2048 it was 4% slower and at 1024 no faster, and larger
+// chunks would need more than one wave per SIMD at its register count; they
+// keep the layout above.
+template <int C>
+constexpr bool kPassA_ring = C == 4096;
 constexpr bool kPassB_NT = true;
 // LAMB warmup passes (BERT-Large, W = 8, interleaved on one box): streaming
 // accesses take pass 1 from 3.30 to 2.95 ms and pass 2 from 0.97 to 0.87 ms;
@@ -287,10 +298,23 @@ struct LaunchPassA {
   static void go(const onebit_layer_table* t, int W, const Workers& wk, float* err_s,
                  const float* m, const float* v_frozen, float* v_fresh, uint32_t* bits_s,
                  float* scales_s, const Coef& cf, const Ws& ws, int32_t* status, hipStream_t st) {
-    hipLaunchKernelGGL(
-        (k_compressed_pass_a<C, kPassA_NT, kPassA_PF, kPassA_WPE, kPassA_SPT, RN, PM>),
-        dim3((unsigned)t->K), dim3(Geo<C, kPassA_SPT>::T), 0, st, t->N / C, t->dev, W, wk, err_s, m,
-        v_frozen, v_fresh, bits_s, scales_s, ws.seg_max, ws.seg_x, ws.seg_u, cf, status);
+    const int64_t n_full = t->N / C;
+    if constexpr (kPassA_ring<C>) {
+      // one wave per SIMD: 4 / (waves per chunk) workgroups per CU, no more
+      // than there are full chunks (at least one, for a lone partial chunk)
+      int64_t G = (int64_t)t->cus * (4 / Geo<C>::NW);
+      if (G > n_full) G = n_full;
+      if (G < 1) G = 1;
+      hipLaunchKernelGGL((k_compressed_pass_a_ring<C, kPassA_NT, RN, PM>), dim3((unsigned)G),
+                         dim3(Geo<C>::T), 0, st, n_full, t->dev, W, wk, err_s, m, v_frozen,
+                         v_fresh, bits_s, scales_s, ws.seg_max, ws.seg_x, ws.seg_u, cf, status);
+    } else {
+      hipLaunchKernelGGL(
+          (k_compressed_pass_a<C, kPassA_NT, kPassA_PF, kPassA_WPE, kPassA_SPT, RN, PM>),
+          dim3((unsigned)t->K), dim3(Geo<C, kPassA_SPT>::T), 0, st, n_full, t->dev, W, wk,
+          err_s, m, v_frozen, v_fresh, bits_s, scales_s, ws.seg_max, ws.seg_x, ws.seg_u, cf,
+          status);
+    }
   }
 };
 
@@ -625,6 +649,11 @@ int onebit_layer_table_create(const int64_t* numels, int32_t L, int32_t chunk,
   int device = -1;
   if (hipError_t e = hipGetDevice(&device); e != hipSuccess)
     return fail(ONEBIT_EHIP, "%s: hipGetDevice: %s", __func__, hipGetErrorString(e));
+  int cus = 0;
+  if (hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
+      e != hipSuccess || cus < 1)
+    return fail(ONEBIT_EHIP, "%s: compute unit count: %s", __func__,
+                e != hipSuccess ? hipGetErrorString(e) : "none");
   // Set-up for onebit_lamb_compressed_step_noalloc on this device: its
   // scratch address is looked up here, outside any stream capture, since
   // every call of it takes a table made on its device.  A failure is left
@@ -650,6 +679,7 @@ int onebit_layer_table_create(const int64_t* numels, int32_t L, int32_t chunk,
   t->K = K;
   t->S = S;
   t->device = device;
+  t->cus = cus;
   using onebit_host::round256;
   const size_t b_off = round256(sizeof(int64_t) * ((size_t)L + 1));
   const size_t b_k = round256(sizeof(int32_t) * (size_t)K);

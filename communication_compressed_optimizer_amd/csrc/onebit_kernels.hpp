@@ -743,6 +743,49 @@ __device__ __forceinline__ float workers_and_server(const ChunkAt<C, TAIL> ch, i
   return s2;
 }
 
+// Pass A after the compressed allreduce, on one chunk: the reconstructed
+// gradient from the server's output (nib, s2) and beta1*m (bm), the fresh
+// variance (vf in, stored), and the chunk's statistics of the rescale from
+// v_frozen (vz): the maximum of the ratio q per (chunk, tensor) segment, or
+// (RN, the norm-ratio variant) the double sums of (sqrt(v_frozen)+eta)^2 and
+// (sqrt(v_fresh)+eta)^2.
+template <int C, bool TAIL, bool NT, int SPT, bool RN>
+__device__ __forceinline__ void rescale_chunk(const ChunkAt<C, TAIL>& ch, const DevTable& tab,
+                                              const SlotsN<SPT>& bm, const uint32_t (&nib)[SPT],
+                                              float s2, SlotsN<SPT>& vf, SlotsN<SPT>& vz,
+                                              float* __restrict__ v_fresh,
+                                              float* __restrict__ seg_max,
+                                              double* __restrict__ seg_z,
+                                              double* __restrict__ seg_f, const Coef& cf,
+                                              float* red, double* dred) {
+#pragma unroll
+  for (int a = 0; a < SPT; ++a)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float mh = signed_scale(nib, a, c, s2);
+      const float gh = (mh - bm[a][c]) / cf.a1;
+      vf[a][c] = (cf.beta2 * vf[a][c]) + (cf.a2 * (gh * gh));
+    }
+  store_chunk<C, TAIL, NT, SPT>(v_fresh, ch.base, ch.nk, vf);
+  if constexpr (RN) {
+#pragma unroll
+    for (int a = 0; a < SPT; ++a)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        vz[a][c] = __builtin_sqrtf(vz[a][c]) + cf.eta;
+        vf[a][c] = __builtin_sqrtf(vf[a][c]) + cf.eta;
+      }
+    segment_sums<C, SPT>(tab, ch.k, ch.base, ch.nk, vz, vf, dred, seg_z, seg_f);
+  } else {
+#pragma unroll
+    for (int a = 0; a < SPT; ++a)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        vz[a][c] = (__builtin_sqrtf(vz[a][c]) + cf.eta) / (__builtin_sqrtf(vf[a][c]) + cf.eta);
+    segment_max<C, SPT>(tab, ch.k, ch.base, ch.nk, vz, red, seg_max);  // vz: the ratio q
+  }
+}
+
 // 1-bit LAMB compression step, pass A: the compressed allreduce, then the
 // reconstructed gradient, the fresh variance and the per-(chunk, tensor)
 // statistic of the rescale: the maximum of the ratio q, or (RN, the
@@ -777,32 +820,8 @@ __device__ __forceinline__ void pass_a_chunk(int64_t kk, const DevTable& tab, in
     load_chunk<C, TAIL, NT, SPT>(v_fresh, base, nk, vf);
     load_chunk<C, TAIL, NT, SPT>(v_frozen, base, nk, vz);
   }
-#pragma unroll
-  for (int a = 0; a < SPT; ++a)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const float mh = signed_scale(nib, a, c, s2);
-      const float gh = (mh - bm[a][c]) / cf.a1;
-      vf[a][c] = (cf.beta2 * vf[a][c]) + (cf.a2 * (gh * gh));
-    }
-  store_chunk<C, TAIL, NT, SPT>(v_fresh, base, nk, vf);
-  if constexpr (RN) {
-#pragma unroll
-    for (int a = 0; a < SPT; ++a)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        vz[a][c] = __builtin_sqrtf(vz[a][c]) + cf.eta;
-        vf[a][c] = __builtin_sqrtf(vf[a][c]) + cf.eta;
-      }
-    segment_sums<C, SPT>(tab, ch.k, base, nk, vz, vf, dred, seg_z, seg_f);
-  } else {
-#pragma unroll
-    for (int a = 0; a < SPT; ++a)
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        vz[a][c] = (__builtin_sqrtf(vz[a][c]) + cf.eta) / (__builtin_sqrtf(vf[a][c]) + cf.eta);
-    segment_max<C, SPT>(tab, ch.k, base, nk, vz, red, seg_max);  // vz now holds the ratio q
-  }
+  rescale_chunk<C, TAIL, NT, SPT, RN>(ch, tab, bm, nib, s2, vf, vz, v_fresh, seg_max, seg_z,
+                                      seg_f, cf, red, dred);
 }
 
 
@@ -854,6 +873,172 @@ __device__ __forceinline__ void adam_allreduce_chunk(int64_t kk, int64_t n, int 
   uint32_t nib[SPT];
   workers_and_server<C, TAIL, NT, PF, SPT, PM>(ch, W, wk, err_s, m, bits_s, scales_s, cf, status,
                                                lds, parity, bm, nib, nullptr, nullptr, d0, d1);
+}
+
+// One worker's part of the compressed allreduce on full chunk k (base =
+// k*C) for the persistent pass A: the loop body of workers_and_server.
+template <int C, bool NT>
+__device__ __forceinline__ void ring_worker(int64_t k, int64_t base, int w, const Workers& wk,
+                                            const Slots& bm, Slots& g, const Slots& e, Slots& acc,
+                                            const Coef& cf, int32_t* status, float4* lds,
+                                            int& parity) {
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) g[a][c] = (bm[a][c] + (cf.a1 * g[a][c])) + e[a][c];
+  uint32_t wnib[4];
+  const float s = compress_slots<C, false>(g, C, lds, parity, wnib);
+  store_chunk<C, false, NT>(wk.e[w], base, C, g);
+  if (wk.bits[w]) store_sign_words<C>(wk.bits[w] + k * Geo<C>::WORDS, wnib);
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float sv = signed_scale(wnib, a, c, s);
+      acc[a][c] = w == 0 ? sv : acc[a][c] + sv;
+    }
+  if (threadIdx.x == 0) {
+    if (wk.scales[w]) wk.scales[w][k] = s;
+    if (!__builtin_isfinite(s)) flag(status, 1);
+  }
+}
+
+// Pass A as a persistent grid (chunks of up to 4096 elements; the library
+// uses it at 4096).  A grid of G workgroups, sized by the host to one wave
+// per SIMD, steps through the full chunks b, b + G, b + 2G, ...; block 0
+// first takes the partial last chunk through pass_a_chunk.  Each workgroup
+// keeps the memory pipe busy
+// across its own reductions: while worker w's chunk is reduced, the loads
+// of workers w+1 and w+2 are in flight (three slot buffers, rotated by
+// unrolling the worker loop by three), and across the server's reduction
+// the next chunk's momentum and its workers 0-2 are loaded, so no chunk
+// starts cold.  Per chunk the arithmetic is pass_a_chunk's, operation for
+// operation, so every output is bit for bit the same.  With PM the next
+// chunk's momentum is its previous server output (sign words and scale),
+// read before this workgroup rewrites them; no other workgroup touches that
+// chunk.
+template <int C, bool NT, bool RN, bool PM>
+__global__ void __launch_bounds__(Geo<C>::T, 1)
+k_compressed_pass_a_ring(int64_t n_full, DevTable tab, int W, Workers wk,
+                         float* __restrict__ err_s, const float* __restrict__ m,
+                         const float* __restrict__ v_frozen, float* __restrict__ v_fresh,
+                         uint32_t* __restrict__ bits_s, float* __restrict__ scales_s,
+                         float* __restrict__ seg_max, double* __restrict__ seg_z,
+                         double* __restrict__ seg_f, Coef cf, int32_t* status) {
+  static_assert(!Geo<C>::SMALL && Geo<C>::T <= 256, "one wave per SIMD needs T <= 256");
+  constexpr int T = Geo<C>::T;
+  __shared__ float4 lds[2 * T];
+  __shared__ float red[T / 64];
+  __shared__ double dred[RN ? 2 * (T / 64) : 1];
+  const int64_t has_tail = tab.K - n_full;
+  if (has_tail && blockIdx.x == 0)
+    pass_a_chunk<C, true, NT, false, 4, RN, PM>(n_full, tab, W, wk, err_s, m, v_frozen, v_fresh,
+                                                bits_s, scales_s, seg_max, seg_z, seg_f, cf,
+                                                status, lds, red, dred);
+  int64_t k = blockIdx.x;
+  if (k >= n_full) return;
+  const int64_t G = gridDim.x;
+  int parity = 0;
+
+  // the momentum of the chunk ahead: m, or its previous server output
+  Slots mn;
+  uint32_t pn[4] = {0u, 0u, 0u, 0u};
+  float sp = 0.0f;
+  // three slot buffers for the workers in flight: worker w in buffer w mod 3
+  Slots g0, e0, g1, e1, g2, e2;
+  if constexpr (PM) {
+    load_sign_nibbles<C>(bits_s + k * Geo<C>::WORDS, pn);
+    sp = scales_s[k];
+  } else {
+    load_chunk<C, false, NT>(m, k * C, C, mn);
+  }
+  load_chunk<C, false, NT>(wk.g[0], k * C, C, g0);
+  load_chunk<C, false, NT>(wk.e[0], k * C, C, e0);
+  if (W > 1) {
+    load_chunk<C, false, NT>(wk.g[1], k * C, C, g1);
+    load_chunk<C, false, NT>(wk.e[1], k * C, C, e1);
+  }
+
+  const int t = threadIdx.x;
+  const float fW = (float)W;
+  for (; k < n_full; k += G) {
+    const int64_t base = k * C;
+    const int64_t kn = k + G;
+    Slots bm, acc;
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if constexpr (PM) bm[a][c] = cf.beta1 * signed_scale(pn, a, c, sp);
+        else bm[a][c] = cf.beta1 * mn[a][c];
+      }
+    if (W > 2 && k == (int64_t)blockIdx.x) {   // later chunks have it in flight already
+      load_chunk<C, false, NT>(wk.g[2], base, C, g2);
+      load_chunk<C, false, NT>(wk.e[2], base, C, e2);
+    }
+
+    for (int w = 0; w < W; w += 3) {
+      ring_worker<C, NT>(k, base, w, wk, bm, g0, e0, acc, cf, status, lds, parity);
+      if (w + 3 < W) {
+        load_chunk<C, false, NT>(wk.g[w + 3], base, C, g0);
+        load_chunk<C, false, NT>(wk.e[w + 3], base, C, e0);
+      }
+      if (w + 1 < W) {
+        ring_worker<C, NT>(k, base, w + 1, wk, bm, g1, e1, acc, cf, status, lds, parity);
+        if (w + 4 < W) {
+          load_chunk<C, false, NT>(wk.g[w + 4], base, C, g1);
+          load_chunk<C, false, NT>(wk.e[w + 4], base, C, e1);
+        }
+      }
+      if (w + 2 < W) {
+        ring_worker<C, NT>(k, base, w + 2, wk, bm, g2, e2, acc, cf, status, lds, parity);
+        if (w + 5 < W) {
+          load_chunk<C, false, NT>(wk.g[w + 5], base, C, g2);
+          load_chunk<C, false, NT>(wk.e[w + 5], base, C, e2);
+        }
+      }
+    }
+
+    // the server's error, then the next chunk's first loads, then the
+    // variances (needed only after the server's reduction)
+    Slots y, vf, vz;
+    uint32_t nib[4];
+    load_chunk<C, false, NT>(err_s, base, C, y);
+    if (kn < n_full) {
+      if constexpr (PM) {
+        load_sign_nibbles<C>(bits_s + kn * Geo<C>::WORDS, pn);
+        sp = scales_s[kn];
+      } else {
+        load_chunk<C, false, NT>(m, kn * C, C, mn);
+      }
+      load_chunk<C, false, NT>(wk.g[0], kn * C, C, g0);
+      load_chunk<C, false, NT>(wk.e[0], kn * C, C, e0);
+      if (W > 1) {
+        load_chunk<C, false, NT>(wk.g[1], kn * C, C, g1);
+        load_chunk<C, false, NT>(wk.e[1], kn * C, C, e1);
+      }
+      if (W > 2) {
+        load_chunk<C, false, NT>(wk.g[2], kn * C, C, g2);
+        load_chunk<C, false, NT>(wk.e[2], kn * C, C, e2);
+      }
+    }
+    load_chunk<C, false, NT>(v_fresh, base, C, vf);
+    load_chunk<C, false, NT>(v_frozen, base, C, vz);
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) y[a][c] = (acc[a][c] / fW) + y[a][c];
+    const float s2 = compress_slots<C, false>(y, C, lds, parity, nib);
+    store_chunk<C, false, NT>(err_s, base, C, y);
+    store_sign_words<C>(bits_s + k * Geo<C>::WORDS, nib);
+    if (t == 0) {
+      scales_s[k] = s2;
+      if (!__builtin_isfinite(s2)) flag(status, 2);
+    }
+    const ChunkAt<C, false> ch(k, tab.N);
+    rescale_chunk<C, false, NT, 4, RN>(ch, tab, bm, nib, s2, vf, vz, v_fresh, seg_max, seg_z,
+                                       seg_f, cf, red, dred);
+  }
 }
 
 // One workgroup per chunk of an n-element buffer; block 0 takes the partial
