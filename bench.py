@@ -470,7 +470,9 @@ def main():
             "step_bytes": pm_bytes, "GBps": pm_bytes / (pm_ms * 1e-3) / 1e9,
             "note": "same step with m = NULL: the momentum is the previous server output "
                     "(bits_s, scales_s), outputs bit-identical to the fp32-momentum step"},
-        "roofline": {"bound": "hbm", "kernel": "k_compressed_pass_a<4096>",
+        "roofline": {"bound": "hbm",
+                     "kernel": "k_compressed_pass_a_ring<4096>" if C == 4096 else
+                     f"k_compressed_pass_a<{C}>",
                      "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
                      "algorithmic_bytes": abytes},

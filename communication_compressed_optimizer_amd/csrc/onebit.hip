@@ -181,16 +181,21 @@ constexpr bool kPassA_NT = true;   // streaming loads and stores
 constexpr bool kPassA_PF = false;  // next-worker prefetch
 constexpr int kPassA_WPE = 6;      // minimum waves per SIMD
 constexpr int kPassA_SPT = 4;      // float4 slots per thread (workgroup = C / (4 * SPT))
-// Chunks of 4096 elements run pass A as a persistent grid with two workers
-// and the next chunk's first three in flight (k_compressed_pass_a_ring): at
-// BERT-Large, W = 8, interleaved against one workgroup per chunk on seven
-// boxes, 0.7-4.2% faster (7.05-7.16 against 7.16-7.38 ms; the larger gains
-// on the boxes where the 30-stream pattern runs slowest), outputs
-// identical.  At 2048 it was 4% slower and at 1024 no faster, and larger
-// chunks would need more than one wave per SIMD at its register count; they
-// keep the layout above.
+// With 4096-element chunks and at least kPassA_ring_min_W workers, pass A
+// runs as a persistent grid with two workers and the next chunk's first
+// three in flight (k_compressed_pass_a_ring).  At BERT-Large, W = 8,
+// interleaved against one workgroup per chunk on seven boxes, it was
+// 0.7-4.2% faster (7.05-7.16 against 7.16-7.38 ms; the larger gains where
+// the 30-stream pattern runs slowest), outputs identical.  Over W on one
+// table (two boxes): W = 2-6 slower (by 22% at W = 2, 1-4% at W = 4-6: per
+// chunk there is too little worker traffic to hide its reductions behind),
+// W = 7 even, W = 8-16 between 4.8% faster and 2% slower, 1.1% faster on
+// average.  With 2048-element chunks it was 4% slower, with 1024 no faster,
+// and larger chunks would need more than one wave per SIMD at its register
+// count; all of those keep the layout above.
 template <int C>
 constexpr bool kPassA_ring = C == 4096;
+constexpr int kPassA_ring_min_W = 7;
 constexpr bool kPassB_NT = true;
 // LAMB warmup passes (BERT-Large, W = 8, interleaved on one box): streaming
 // accesses take pass 1 from 3.30 to 2.95 ms and pass 2 from 0.97 to 0.87 ms;
@@ -299,15 +304,17 @@ struct LaunchPassA {
                  const float* m, const float* v_frozen, float* v_fresh, uint32_t* bits_s,
                  float* scales_s, const Coef& cf, const Ws& ws, int32_t* status, hipStream_t st) {
     const int64_t n_full = t->N / C;
-    if constexpr (kPassA_ring<C>) {
+    if (kPassA_ring<C> && W >= kPassA_ring_min_W) {
       // one wave per SIMD: 4 / (waves per chunk) workgroups per CU, no more
       // than there are full chunks (at least one, for a lone partial chunk)
       int64_t G = (int64_t)t->cus * (4 / Geo<C>::NW);
       if (G > n_full) G = n_full;
       if (G < 1) G = 1;
-      hipLaunchKernelGGL((k_compressed_pass_a_ring<C, kPassA_NT, RN, PM>), dim3((unsigned)G),
-                         dim3(Geo<C>::T), 0, st, n_full, t->dev, W, wk, err_s, m, v_frozen,
-                         v_fresh, bits_s, scales_s, ws.seg_max, ws.seg_x, ws.seg_u, cf, status);
+      if constexpr (kPassA_ring<C>)
+        hipLaunchKernelGGL((k_compressed_pass_a_ring<C, kPassA_NT, RN, PM>), dim3((unsigned)G),
+                           dim3(Geo<C>::T), 0, st, n_full, t->dev, W, wk, err_s, m, v_frozen,
+                           v_fresh, bits_s, scales_s, ws.seg_max, ws.seg_x, ws.seg_u, cf,
+                           status);
     } else {
       hipLaunchKernelGGL(
           (k_compressed_pass_a<C, kPassA_NT, kPassA_PF, kPassA_WPE, kPassA_SPT, RN, PM>),

@@ -65,7 +65,7 @@ TABLES = [[1], [10, 20, 30], [4096 * 2 + 7, 3, 1000], [1, 3, 4095, 4097, 100, 81
 
 @pytest.mark.parametrize("numels", TABLES)
 @pytest.mark.parametrize("chunk", [64, 256, 1024, 4096])
-@pytest.mark.parametrize("W", [1, 3])
+@pytest.mark.parametrize("W", [1, 3, 8])
 def test_lamb_entry_points_stay_in_bounds(numels, chunk, W):
     table = ob.LayerTable(numels, chunk)
     N, K, L = table.N, table.K, len(numels)

@@ -75,7 +75,7 @@ def _bits(t):
 
 
 @pytest.mark.parametrize("packed", [False, True])
-@pytest.mark.parametrize("W", [1, 3])
+@pytest.mark.parametrize("W", [1, 3, 8])
 def test_resume_inside_compression_stage(tmp_path, packed, W):
     wl = Workload("checkpoint", TABLE, W=W, init="fresh", grad_std=0.02)
     a, h = DevRun(wl), HostRun(wl)

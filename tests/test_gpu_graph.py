@@ -39,8 +39,9 @@ def _capture(fn):
     return g
 
 
-def test_lamb_steps_replay_as_eager():
-    wl = Workload("graph", TABLE, W=4, init="fresh", grad_std=0.02)
+@pytest.mark.parametrize("W", [4, 8])
+def test_lamb_steps_replay_as_eager(W):
+    wl = Workload("graph", TABLE, W=W, init="fresh", grad_std=0.02)
     a, b = DevRun(wl), DevRun(wl)
     for r in (a, b):
         r.fill_grads(0)

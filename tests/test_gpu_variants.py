@@ -38,7 +38,7 @@ def _set(run, **kw):
 
 
 @pytest.mark.parametrize("name", sorted(VARIANTS))
-@pytest.mark.parametrize("W", [1, 4])
+@pytest.mark.parametrize("W", [1, 4, 8])
 def test_variant_trajectory(name, W):
     cfg = dict(VARIANTS[name])
     bias = cfg.pop("bias", False)

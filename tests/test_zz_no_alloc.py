@@ -52,7 +52,9 @@ def _same(a, b, packed=False):
 
 @pytest.mark.parametrize("rho_mode", [ob.ONEBIT_RHO_MAX, ob.ONEBIT_RHO_NORM_RATIO])
 def test_noalloc_equals_workspace_step(rho_mode):
-    for numels, W in ((LARGE, 3), (SMALL, 2)):          # the second call's table is smaller
+    # the first call at W = 8 (the persistent pass A), the second on a smaller
+    # table at W = 2 (one workgroup per chunk)
+    for numels, W in ((LARGE, 8), (SMALL, 2)):
         wl = Workload("noalloc", numels, W=W, init="frozen")
         a, b = DevRun(wl), DevRun(wl)
         for r in (a, b):
