@@ -471,7 +471,9 @@ def main():
             "note": "same step with m = NULL: the momentum is the previous server output "
                     "(bits_s, scales_s), outputs bit-identical to the fp32-momentum step"},
         "roofline": {"bound": "hbm",
-                     "kernel": "k_compressed_pass_a_ring<4096>" if C == 4096 else
+                     # the library's choice of pass-A kernel (persistent ring at
+                     # 4096-element chunks from seven workers up)
+                     "kernel": "k_compressed_pass_a_ring<4096>" if C == 4096 and W >= 7 else
                      f"k_compressed_pass_a<{C}>",
                      "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
