@@ -47,6 +47,15 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libonebit.s
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
 
+# The arrays come from torch, so the library must share torch's HIP runtime:
+# torch is imported first, and libonebit.so's HIP calls then bind to the
+# runtime it loaded.  Loaded the other way round, the process can end up with
+# two runtimes, and the library's sees no device.
+try:
+    import torch  # noqa: F401
+except ImportError:  # pragma: no cover - the binding's host checks need no GPU
+    pass
+
 _lib = ctypes.CDLL(LIB_PATH)
 
 _P = ctypes.c_void_p

@@ -197,6 +197,13 @@ template <int C>
 constexpr bool kPassA_ring = C == 4096;
 constexpr int kPassA_ring_min_W = 7;
 constexpr bool kPassB_NT = true;
+// Pass B at 4096-element chunks runs at most two workgroups per CU: each
+// takes 64 KiB of dynamic LDS it does not use, of the CU's 160 KiB.  Fewer
+// chunks in flight serve its five streams better (interleaved at
+// BERT-Large: 0.870 against 0.901 ms for finalize + pass B; three per CU
+// 0.899 ms, one per CU 0.983 ms; outputs identical).
+template <int C>
+constexpr unsigned kPassB_lds = C == 4096 ? 65536u : 0u;
 // LAMB warmup passes (BERT-Large, W = 8, interleaved on one box): streaming
 // accesses take pass 1 from 3.30 to 2.95 ms and pass 2 from 0.97 to 0.87 ms;
 // a 5- or 6-wave register cap on pass 1 is slower (3.07, 3.44 ms) and one on
@@ -437,7 +444,8 @@ struct LaunchPassB {
       hipLaunchKernelGGL((k_rescale_finalize<256>), dim3((unsigned)t->L), dim3(256), 0, st,
                          t->dev, (const float*)ws.seg_max, (const double*)ws.seg_x,
                          (const double*)ws.seg_u, c_avg, f_prev, ws.c_layer, c_out, cf, status);
-    hipLaunchKernelGGL((k_compressed_pass_b<C, kPassB_NT>), dim3((unsigned)t->K), dim3(Geo<C>::T), 0,
+    hipLaunchKernelGGL((k_compressed_pass_b<C, kPassB_NT>), dim3((unsigned)t->K), dim3(Geo<C>::T),
+                       kPassB_lds<C>,
                        st, t->N / C, t->dev, bits_s, scales_s, v_frozen, x, m,
                        (const float*)ws.c_layer, cf);
   }
