@@ -160,6 +160,19 @@ def test_package_refuses_to_load_without_library(tmp_path):
     assert res.returncode != 0 and "is not built" in res.stderr
 
 
+def test_torch_is_loaded_before_the_library():
+    """The binding imports torch before it loads libonebit.so, so that the
+    library's HIP calls bind to the runtime torch's tensors live in (loaded
+    the other way round a process can hold two runtimes)."""
+    import subprocess
+    import sys
+    code = ("import sys; import communication_compressed_optimizer_amd as ob; "
+            "assert 'torch' in sys.modules, 'torch not loaded'; print('ok')")
+    res = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
+                         timeout=300)
+    assert res.returncode == 0 and "ok" in res.stdout, res.stderr[-2000:]
+
+
 def test_binding_checks_tensors_before_the_library(ob):
     """Host tensors and short worker lists are rejected by the binding
     itself (a host address or a missing worker pointer would reach the
