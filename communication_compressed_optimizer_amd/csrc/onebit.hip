@@ -166,6 +166,14 @@ void launch_chunks(int64_t n, hipStream_t st, KF k, A... args) {
   if (K > 0) hipLaunchKernelGGL(k, dim3((unsigned)K), dim3(Geo<C>::T), 0, st, n / C, args...);
 }
 
+// The same with `lds` bytes of dynamic LDS per workgroup that the kernel
+// does not use: it caps the workgroups a CU holds at once (160 KiB each).
+template <int C, typename KF, typename... A>
+void launch_chunks_capped(unsigned lds, int64_t n, hipStream_t st, KF k, A... args) {
+  const int64_t K = (n + C - 1) / C;
+  if (K > 0) hipLaunchKernelGGL(k, dim3((unsigned)K), dim3(Geo<C>::T), lds, st, n / C, args...);
+}
+
 // Tuning of the compression-step kernels, measured on MI355X at the
 // BERT-Large table with W = 8 (phase 1, interleaved medians on one box:
 // plain accesses 7.76 ms, streaming 7.38 ms; with the partial chunk folded
@@ -225,8 +233,13 @@ constexpr int kAdam_SPT = 4;
 // cap changes nothing (6.38 ms), so it runs uncapped (104 VGPRs, no spills).
 constexpr bool kSparse_NT = true;
 // One GPU's share of a W-GPU step: the worker compression and the receiver
-// statistics stream like the codec kernels.
+// statistics stream like the codec kernels.  The worker compression at
+// 4096-element chunks runs at most two workgroups per CU, like pass B
+// (0.84 against 0.88 ms at N = 333.6 M, two runs on one box; the receiver
+// statistics were 21% slower so capped, and keep the full grid).
 constexpr bool kShare_NT = true;
+template <int C>
+constexpr unsigned kWorker_lds = C == 4096 ? 65536u : 0u;
 // Chunk geometry of the element-wise 1-bit Adam warmup kernel (any chunk
 // gives the same result; this one gives 256-thread workgroups).
 constexpr int kAdamWarmupChunk = 4096;
@@ -371,11 +384,11 @@ struct LaunchWorker {
                   const float* scales_m, uint32_t* bits_w, float* scales_w, const Coef& cf,
                   int32_t* status, hipStream_t st) {
     if (m)
-      launch_chunks<C>(n, st, k_worker_compress<C, kShare_NT, false>, n, g, e, m, bits_m, scales_m,
-                       bits_w, scales_w, cf, status);
+      launch_chunks_capped<C>(kWorker_lds<C>, n, st, k_worker_compress<C, kShare_NT, false>, n, g,
+                              e, m, bits_m, scales_m, bits_w, scales_w, cf, status);
     else
-      launch_chunks<C>(n, st, k_worker_compress<C, kShare_NT, true>, n, g, e, m, bits_m, scales_m,
-                       bits_w, scales_w, cf, status);
+      launch_chunks_capped<C>(kWorker_lds<C>, n, st, k_worker_compress<C, kShare_NT, true>, n, g,
+                              e, m, bits_m, scales_m, bits_w, scales_w, cf, status);
   }
 };
 
@@ -444,10 +457,8 @@ struct LaunchPassB {
       hipLaunchKernelGGL((k_rescale_finalize<256>), dim3((unsigned)t->L), dim3(256), 0, st,
                          t->dev, (const float*)ws.seg_max, (const double*)ws.seg_x,
                          (const double*)ws.seg_u, c_avg, f_prev, ws.c_layer, c_out, cf, status);
-    hipLaunchKernelGGL((k_compressed_pass_b<C, kPassB_NT>), dim3((unsigned)t->K), dim3(Geo<C>::T),
-                       kPassB_lds<C>,
-                       st, t->N / C, t->dev, bits_s, scales_s, v_frozen, x, m,
-                       (const float*)ws.c_layer, cf);
+    launch_chunks_capped<C>(kPassB_lds<C>, t->N, st, k_compressed_pass_b<C, kPassB_NT>, t->dev,
+                            bits_s, scales_s, v_frozen, x, m, (const float*)ws.c_layer, cf);
   }
 };
 
