@@ -1,8 +1,9 @@
 """Entry points on a flat buffer of more than 2^31 elements (64-bit element,
 word and chunk indexing): the codec (compress_ef, decompress,
 average_packed), the fused 1-bit Adam step and one GPU's share of it
-(worker_compress, average_packed, adam_update), and the sparse stage fused
-and shared (sparse_worker, sparse_average, sparse_update), each checked
+(worker_compress, average_packed, adam_update), the sparse stage fused
+and shared (sparse_worker, sparse_average, sparse_update), and the fused
+1-bit LAMB step at W = 7 on a table of whole tensors, each checked
 against the oracle on windows of chunks at the start, across element 2^31
 and at the ragged end.  Every value compared is chunk-local or element-wise
 (the sparse stage's per-tensor coefficient is an input), so the oracle
@@ -278,4 +279,31 @@ def test_sparse_fused_and_share_past_2_31():
                             s.status)
     s.check(refs)
     del s
+    torch.cuda.empty_cache()
+
+
+def test_lamb_step_past_2_31():
+    """The fused 1-bit LAMB step at W = 7 (the persistent pass A) on a table
+    of 2,048 tensors of 2^20 elements and a ragged last one (3*4096 + 5),
+    N > 2^31: one compression step from a frozen state, checked against the
+    oracle on the first tensor, the tensor that ends at element 2^31 and the
+    last one (whole tensors, so the parameters and coefficients too)."""
+    from synth.workloads import Workload
+    from tests.harness import DevRun, HostRun, assert_parity, compare_state
+    W = 7
+    numels = [1 << 20] * 2048 + [3 * C + 5]
+    wl = Workload("large", numels, W=W, chunk=C, init="frozen")
+    assert wl.N == N
+    need_gib(5 + 2 * W)
+    d = DevRun(wl, store_worker_bits=False)
+    d.compressed_step(0)
+    torch.cuda.synchronize()
+    assert int(d.status.item()) == 0
+    for lo, hi in ((0, 1 << 20), ((1 << 31) - (1 << 20), 1 << 31), (1 << 31, N)):
+        h = HostRun(wl, lo, hi)
+        h.compressed_step(0)
+        rep = compare_state(d, h)
+        assert rep["x"]["n"] == hi - lo             # the window's tensor is whole
+        assert_parity(rep, f"window [{lo}, {hi})")
+    del d
     torch.cuda.empty_cache()
