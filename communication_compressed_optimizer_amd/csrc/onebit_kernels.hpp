@@ -904,15 +904,15 @@ __device__ __forceinline__ void ring_worker(int64_t k, int64_t base, int w, cons
 }
 
 // Pass A as a persistent grid (chunks of up to 4096 elements; the library
-// uses it at 4096).  A grid of G workgroups, sized by the host to one wave
-// per SIMD, steps through the full chunks b, b + G, b + 2G, ...; block 0
-// first takes the partial last chunk through pass_a_chunk.  Each workgroup
-// keeps the memory pipe busy
-// across its own reductions: while worker w's chunk is reduced, the loads
-// of workers w+1 and w+2 are in flight (three slot buffers, rotated by
-// unrolling the worker loop by three), and across the server's reduction
-// the next chunk's momentum and its workers 0-2 are loaded, so no chunk
-// starts cold.  Per chunk the arithmetic is pass_a_chunk's, operation for
+// uses it at 4096 with seven or more workers).  A grid of G workgroups,
+// sized by the host to one wave per SIMD, steps through the full chunks b,
+// b + G, b + 2G, ...; block 0 first takes the partial last chunk through
+// pass_a_chunk.  Each workgroup keeps the memory pipe busy across its own
+// reductions: while worker w's chunk is reduced, the loads of workers w+1
+// and w+2 are in flight (three slot buffers, rotated by unrolling the
+// worker loop by three), and across the server's reduction the next
+// chunk's momentum and its workers 0-2 are loaded, so no chunk starts
+// cold.  Per chunk the arithmetic is pass_a_chunk's, operation for
 // operation, so every output is bit for bit the same.  With PM the next
 // chunk's momentum is its previous server output (sign words and scale),
 // read before this workgroup rewrites them; no other workgroup touches that
