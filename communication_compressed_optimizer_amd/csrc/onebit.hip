@@ -215,7 +215,11 @@ constexpr unsigned kPassB_lds = C == 4096 ? 65536u : 0u;
 // LAMB warmup passes (BERT-Large, W = 8, interleaved on one box): streaming
 // accesses take pass 1 from 3.30 to 2.95 ms and pass 2 from 0.97 to 0.87 ms;
 // a 5- or 6-wave register cap on pass 1 is slower (3.07, 3.44 ms) and one on
-// the 1-bit Adam warmup changes nothing (3.19-3.22 against 3.20 ms).
+// the 1-bit Adam warmup changes nothing (3.19-3.22 against 3.20 ms).  Pass 1
+// keeps the next gradient and then m and v in flight while it sums: the
+// carried warmup step 3.53-3.61 against 3.56-3.66 ms (two rounds, outputs
+// identical); a persistent grid of one or two workgroups per CU, or caps on
+// the workgroups per CU, did not help.
 constexpr bool kWarm_NT = true;
 // Standalone codec kernels (N = 333,563,904, W = 8, interleaved): streaming
 // accesses take compress_ef from 0.741 to 0.655 ms (77% of 8 TB/s),

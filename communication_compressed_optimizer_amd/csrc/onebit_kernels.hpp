@@ -1771,19 +1771,33 @@ __device__ __forceinline__ void warmup_pass1_chunk(int64_t k, const DevTable& ta
   const ChunkAt<C, TAIL> ch(k, tab.N);
   const int64_t base = ch.base;
   const int nk = ch.nk;
-  Slots gs;
+  // The gradients are summed in worker order with the next one in flight;
+  // m and v are loaded as soon as the last gradient has been asked for.
+  Slots gs, gn, mm, vv, u, xx;
   load_chunk<C, TAIL, NT>(wk.g[0], base, nk, gs);
+  if (W > 1) {
+    load_chunk<C, TAIL, NT>(wk.g[1], base, nk, gn);
+  } else {
+    load_chunk<C, TAIL, NT>(m, base, nk, mm);
+    load_chunk<C, TAIL, NT>(v, base, nk, vv);
+  }
   for (int w = 1; w < W; ++w) {
     Slots g;
-    load_chunk<C, TAIL, NT>(wk.g[w], base, nk, g);
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) g[a][c] = gn[a][c];
+    if (w + 1 < W) {
+      load_chunk<C, TAIL, NT>(wk.g[w + 1], base, nk, gn);
+    } else {
+      load_chunk<C, TAIL, NT>(m, base, nk, mm);
+      load_chunk<C, TAIL, NT>(v, base, nk, vv);
+    }
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
       for (int c = 0; c < 4; ++c) gs[a][c] = gs[a][c] + g[a][c];
   }
-  Slots mm, vv, u, xx;
-  load_chunk<C, TAIL, NT>(m, base, nk, mm);
-  load_chunk<C, TAIL, NT>(v, base, nk, vv);
   if constexpr (XS) {
 #pragma unroll
     for (int a = 0; a < 4; ++a)
