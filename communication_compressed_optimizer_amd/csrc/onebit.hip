@@ -166,6 +166,14 @@ void launch_chunks(int64_t n, hipStream_t st, KF k, A... args) {
   if (K > 0) hipLaunchKernelGGL(k, dim3((unsigned)K), dim3(Geo<C>::T), 0, st, n / C, args...);
 }
 
+// The same for a kernel laid out with SPT float4 slots per thread
+// (Geo<C, SPT>::T threads per chunk).
+template <int C, int SPT, typename KF, typename... A>
+void launch_chunks_slots(int64_t n, hipStream_t st, KF k, A... args) {
+  const int64_t K = (n + C - 1) / C;
+  if (K > 0) hipLaunchKernelGGL(k, dim3((unsigned)K), dim3(Geo<C, SPT>::T), 0, st, n / C, args...);
+}
+
 // The same with `lds` bytes of dynamic LDS per workgroup that the kernel
 // does not use: it caps the workgroups a CU holds at once (160 KiB each).
 template <int C, typename KF, typename... A>
@@ -219,8 +227,22 @@ constexpr unsigned kPassB_lds = C == 4096 ? 65536u : 0u;
 // keeps the next gradient and then m and v in flight while it sums: the
 // carried warmup step 3.53-3.61 against 3.56-3.66 ms (two rounds, outputs
 // identical); a persistent grid of one or two workgroups per CU, or caps on
-// the workgroups per CU, did not help.
+// the workgroups per CU, did not help.  At 4096-element chunks both passes
+// lay a chunk over 512 threads (two float4 slots each; pass 1 82 VGPRs and
+// five waves per SIMD, where four slots took 143 VGPRs and three) and pass 1
+// keeps two gradients in flight: pass 1 alone took 2.63-2.67 against
+// 2.69-2.79 ms at W = 8 and 1.74 against 1.83 ms at W = 4 (two rounds, one
+// box; m and v identical, the per-segment sums within 1e-12, their order
+// being the layout's), and the carried warmup step 3.48 / 3.59 against
+// 3.56 / 3.72 ms at W = 8 and 2.58 against 2.65 ms at W = 4 (outputs
+// identical).  One slot per thread with one, three or all gradients in
+// flight was as fast at W = 8 and slower at W = 4; two slots with one
+// gradient in flight, or four slots with two, no faster.
 constexpr bool kWarm_NT = true;
+template <int C>
+constexpr int kWarm_SPT = C == 4096 ? 2 : 4;
+template <int C>
+constexpr int kWarm_DEPTH = C == 4096 ? 2 : 1;
 // Standalone codec kernels (N = 333,563,904, W = 8, interleaved): streaming
 // accesses take compress_ef from 0.741 to 0.655 ms (77% of 8 TB/s),
 // average_packed from 0.554 to 0.535 ms and decompress from 0.247 to 0.240 ms.
@@ -247,6 +269,11 @@ constexpr unsigned kWorker_lds = C == 4096 ? 65536u : 0u;
 // Chunk geometry of the element-wise 1-bit Adam warmup kernel (any chunk
 // gives the same result; this one gives 256-thread workgroups).
 constexpr int kAdamWarmupChunk = 4096;
+// Its layout and gradients in flight, as the LAMB warmup's first pass (x, m
+// and v identical; at N = 333.6 M the step moved by 0-0.6%, 3.26-3.29 ms at
+// W = 8, on a 10 M-element buffer it was 2-4% faster).
+constexpr int kAdamWarmupSPT = 2;
+constexpr int kAdamWarmupDepth = 2;
 
 template <int C>
 struct LaunchCompress {
@@ -281,21 +308,25 @@ struct LaunchWarmup {
   static void run(const onebit_layer_table* t, int W, const Workers& wk, float* x, float* m,
                   float* v, float* c_sum, float* c_out, double* x_sq, bool x_in, const Coef& cf,
                   const Ws& ws, int32_t* status, hipStream_t st) {
+    constexpr int S = kWarm_SPT<C>;
+    constexpr int D = kWarm_DEPTH<C>;
     if (x_in)
-      launch_chunks<C>(t->N, st, k_warmup_pass1<C, kWarm_NT, 1, true>, t->dev, W, wk,
-                       (const float*)x, m, v, ws.seg_x, ws.seg_u, cf);
+      launch_chunks_slots<C, S>(t->N, st, k_warmup_pass1<C, kWarm_NT, 1, true, S, D>, t->dev, W,
+                                wk, (const float*)x, m, v, ws.seg_x, ws.seg_u, cf);
     else
-      launch_chunks<C>(t->N, st, k_warmup_pass1<C, kWarm_NT, 1, false>, t->dev, W, wk,
-                       (const float*)x, m, v, ws.seg_x, ws.seg_u, cf);
+      launch_chunks_slots<C, S>(t->N, st, k_warmup_pass1<C, kWarm_NT, 1, false, S, D>, t->dev, W,
+                                wk, (const float*)x, m, v, ws.seg_x, ws.seg_u, cf);
     hipLaunchKernelGGL(k_warmup_finalize<256>, dim3((unsigned)t->L), dim3(256), 0, st, t->dev,
                        (const double*)(x_in ? x_sq : ws.seg_x), (const double*)ws.seg_u, c_sum,
                        ws.c_layer, c_out, cf, status);
     if (x_sq)
-      launch_chunks<C>(t->N, st, k_warmup_pass2<C, kWarm_NT, true>, t->dev, (const float*)m,
-                       (const float*)v, x, (const float*)ws.c_layer, x_sq, cf);
+      launch_chunks_slots<C, S>(t->N, st, k_warmup_pass2<C, kWarm_NT, true, S>, t->dev,
+                                (const float*)m, (const float*)v, x, (const float*)ws.c_layer,
+                                x_sq, cf);
     else
-      launch_chunks<C>(t->N, st, k_warmup_pass2<C, kWarm_NT, false>, t->dev, (const float*)m,
-                       (const float*)v, x, (const float*)ws.c_layer, x_sq, cf);
+      launch_chunks_slots<C, S>(t->N, st, k_warmup_pass2<C, kWarm_NT, false, S>, t->dev,
+                                (const float*)m, (const float*)v, x, (const float*)ws.c_layer,
+                                x_sq, cf);
   }
 };
 
@@ -1209,8 +1240,9 @@ int onebit_adam_warmup_step(int64_t n, int32_t W, const float* const* grads, flo
   sp.add(v, 4 * n, true, "v");
   if (int rc = sp.check(__func__)) return rc;
   constexpr int C = kAdamWarmupChunk;
-  launch_chunks<C>(n, (hipStream_t)stream, k_adam_warmup<C>, n, (int)W, wk, x, m, v,
-                   make_coef(*hp));
+  launch_chunks_slots<C, kAdamWarmupSPT>(n, (hipStream_t)stream,
+                                         k_adam_warmup<C, 1, kAdamWarmupSPT, kAdamWarmupDepth>, n,
+                                         (int)W, wk, x, m, v, make_coef(*hp));
   return launch_status(__func__);
 }
 

@@ -1259,30 +1259,54 @@ k_adam_update(int64_t n_full, int64_t n, const uint32_t* __restrict__ bits_s,
 
 // 1-bit Adam warmup: one Adam step, element-wise in one pass (mean gradient,
 // moments, x = x - lr*(m/(sqrt(v)+eta))).
-template <int C, bool TAIL>
+template <int C, bool TAIL, int SPT, int DEPTH>
 __device__ __forceinline__ void adam_warmup_chunk(int64_t k, int64_t n, int W, const Workers& wk,
                                                   float* __restrict__ x, float* __restrict__ m,
                                                   float* __restrict__ v, const Coef& cf) {
   const ChunkAt<C, TAIL> ch(k, n);
   const int64_t base = ch.base;
   const int nk = ch.nk;
-  Slots gs;
-  load_chunk<C, TAIL, true>(wk.g[0], base, nk, gs);
-  for (int w = 1; w < W; ++w) {
-    Slots g;
-    load_chunk<C, TAIL, true>(wk.g[w], base, nk, g);
+  // gradients summed in worker order with DEPTH of them in flight, as in the
+  // LAMB warmup's first pass; m, v and x loaded once the last gradient has
+  // been asked for
+  SlotsN<SPT> gs, mm, vv, xx;
+  SlotsN<SPT> q[DEPTH];
+  load_chunk<C, TAIL, true, SPT>(wk.g[0], base, nk, gs);
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+  for (int d = 0; d < DEPTH; ++d)
+    if (1 + d < W) load_chunk<C, TAIL, true, SPT>(wk.g[1 + d], base, nk, q[d]);
+  if (W <= DEPTH) {
+    load_chunk<C, TAIL, true, SPT>(m, base, nk, mm);
+    load_chunk<C, TAIL, true, SPT>(v, base, nk, vv);
+    load_chunk<C, TAIL, true, SPT>(x, base, nk, xx);
+  }
+  for (int w = 1; w < W; ++w) {
+    SlotsN<SPT> g;
+#pragma unroll
+    for (int a = 0; a < SPT; ++a)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) g[a][c] = q[0][a][c];
+#pragma unroll
+    for (int d = 0; d + 1 < DEPTH; ++d)
+#pragma unroll
+      for (int a = 0; a < SPT; ++a)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) q[d][a][c] = q[d + 1][a][c];
+    if (w + DEPTH < W) {
+      load_chunk<C, TAIL, true, SPT>(wk.g[w + DEPTH], base, nk, q[DEPTH - 1]);
+    } else if (w + DEPTH == W) {
+      load_chunk<C, TAIL, true, SPT>(m, base, nk, mm);
+      load_chunk<C, TAIL, true, SPT>(v, base, nk, vv);
+      load_chunk<C, TAIL, true, SPT>(x, base, nk, xx);
+    }
+#pragma unroll
+    for (int a = 0; a < SPT; ++a)
 #pragma unroll
       for (int c = 0; c < 4; ++c) gs[a][c] = gs[a][c] + g[a][c];
   }
-  Slots mm, vv, xx;
-  load_chunk<C, TAIL, true>(m, base, nk, mm);
-  load_chunk<C, TAIL, true>(v, base, nk, vv);
-  load_chunk<C, TAIL, true>(x, base, nk, xx);
   const float fW = (float)W;
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < SPT; ++a)
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const float gb = gs[a][c] / fW;
@@ -1291,20 +1315,21 @@ __device__ __forceinline__ void adam_warmup_chunk(int64_t k, int64_t n, int W, c
       const float u = warmup_dir(mm[a][c], vv[a][c], xx[a][c], cf);
       xx[a][c] = xx[a][c] - (cf.lr * u);
     }
-  store_chunk<C, TAIL, true>(m, base, nk, mm);
-  store_chunk<C, TAIL, true>(v, base, nk, vv);
-  store_chunk<C, TAIL, true>(x, base, nk, xx);
+  store_chunk<C, TAIL, true, SPT>(m, base, nk, mm);
+  store_chunk<C, TAIL, true, SPT>(v, base, nk, vv);
+  store_chunk<C, TAIL, true, SPT>(x, base, nk, xx);
 }
 
-template <int C, int WPE = 1>
-__global__ void __launch_bounds__(Geo<C>::T, WPE)
+template <int C, int WPE = 1, int SPT = 4, int DEPTH = 1>
+__global__ void __launch_bounds__((Geo<C, SPT>::T), WPE)
 k_adam_warmup(int64_t n_full, int64_t n, int W, Workers wk, float* __restrict__ x,
               float* __restrict__ m, float* __restrict__ v, Coef cf) {
   const int64_t has_tail = partial_chunks<C>(n_full, n);
   if (has_tail && blockIdx.x == 0)
-    adam_warmup_chunk<C, true>(n_full, n, W, wk, x, m, v, cf);
+    adam_warmup_chunk<C, true, SPT, DEPTH>(n_full, n, W, wk, x, m, v, cf);
   else
-    adam_warmup_chunk<C, kSmall<C>>((int64_t)blockIdx.x - has_tail, n, W, wk, x, m, v, cf);
+    adam_warmup_chunk<C, kSmall<C>, SPT, DEPTH>((int64_t)blockIdx.x - has_tail, n, W, wk, x, m, v,
+                                                cf);
 }
 
 // SLAMB-style sparse compression stage, one pass per chunk.  The chunk's
@@ -1689,21 +1714,21 @@ k_rescale_finalize(DevTable tab, const float* __restrict__ seg_max, const double
 }
 
 // Per-element step size lr*c_l for the chunk's elements.
-template <int C, bool TAIL>
+template <int C, bool TAIL, int SPT = 4>
 __device__ __forceinline__ void step_sizes(const DevTable& tab, int64_t k, int64_t base,
                                            const float* __restrict__ c_layer, float lr,
-                                           Slots& st) {
-  constexpr int T = Geo<C>::T;
+                                           SlotsN<SPT>& st) {
+  constexpr int T = Geo<C, SPT>::T;
   const int l0 = tab.l0[k];
   const int l1 = tab.l1[k];
   const float s0 = lr * c_layer[l0];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < SPT; ++a)
 #pragma unroll
     for (int c = 0; c < 4; ++c) st[a][c] = s0;
   if (l0 != l1) {
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < SPT; ++a)
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int64_t gi = base + 4 * ((int)threadIdx.x + T * a) + c;
@@ -1760,8 +1785,12 @@ k_compressed_pass_b(int64_t n_full, DevTable tab, const uint32_t* __restrict__ b
 // u^2 in double.  NT: streaming accesses; WPE: minimum waves per SIMD.  XS:
 // the sums of x^2 are carried over from the previous step's pass 2 (x_sq),
 // so x is not read and only the sums of u^2 are formed (the host selects it
-// only without weight decay, where u does not depend on x).
-template <int C, bool TAIL, bool NT, bool XS>
+// only without weight decay, where u does not depend on x).  SPT: float4
+// slots per thread (the workgroup is C / (4*SPT) threads); both passes take
+// the same SPT, so that the sums of x^2 pass 2 carries are the ones pass 1
+// would form.  DEPTH: gradients in flight while the running sum takes the
+// next one.
+template <int C, bool TAIL, bool NT, bool XS, int SPT, int DEPTH>
 __device__ __forceinline__ void warmup_pass1_chunk(int64_t k, const DevTable& tab, int W,
                                                    const Workers& wk, const float* __restrict__ x,
                                                    float* __restrict__ m, float* __restrict__ v,
@@ -1771,44 +1800,53 @@ __device__ __forceinline__ void warmup_pass1_chunk(int64_t k, const DevTable& ta
   const ChunkAt<C, TAIL> ch(k, tab.N);
   const int64_t base = ch.base;
   const int nk = ch.nk;
-  // The gradients are summed in worker order with the next one in flight;
-  // m and v are loaded as soon as the last gradient has been asked for.
-  Slots gs, gn, mm, vv, u, xx;
-  load_chunk<C, TAIL, NT>(wk.g[0], base, nk, gs);
-  if (W > 1) {
-    load_chunk<C, TAIL, NT>(wk.g[1], base, nk, gn);
-  } else {
-    load_chunk<C, TAIL, NT>(m, base, nk, mm);
-    load_chunk<C, TAIL, NT>(v, base, nk, vv);
+  // The gradients are summed in worker order, gradient w + 1 .. w + DEPTH
+  // in flight (q[0] .. q[DEPTH-1]) while gradient w is added; m and v are
+  // loaded as soon as the last gradient has been asked for.
+  SlotsN<SPT> gs, mm, vv, u, xx;
+  SlotsN<SPT> q[DEPTH];
+  load_chunk<C, TAIL, NT, SPT>(wk.g[0], base, nk, gs);
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d)
+    if (1 + d < W) load_chunk<C, TAIL, NT, SPT>(wk.g[1 + d], base, nk, q[d]);
+  if (W <= DEPTH) {
+    load_chunk<C, TAIL, NT, SPT>(m, base, nk, mm);
+    load_chunk<C, TAIL, NT, SPT>(v, base, nk, vv);
   }
   for (int w = 1; w < W; ++w) {
-    Slots g;
+    SlotsN<SPT> g;
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < SPT; ++a)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) g[a][c] = gn[a][c];
-    if (w + 1 < W) {
-      load_chunk<C, TAIL, NT>(wk.g[w + 1], base, nk, gn);
-    } else {
-      load_chunk<C, TAIL, NT>(m, base, nk, mm);
-      load_chunk<C, TAIL, NT>(v, base, nk, vv);
+      for (int c = 0; c < 4; ++c) g[a][c] = q[0][a][c];
+#pragma unroll
+    for (int d = 0; d + 1 < DEPTH; ++d)
+#pragma unroll
+      for (int a = 0; a < SPT; ++a)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) q[d][a][c] = q[d + 1][a][c];
+    if (w + DEPTH < W) {
+      load_chunk<C, TAIL, NT, SPT>(wk.g[w + DEPTH], base, nk, q[DEPTH - 1]);
+    } else if (w + DEPTH == W) {
+      load_chunk<C, TAIL, NT, SPT>(m, base, nk, mm);
+      load_chunk<C, TAIL, NT, SPT>(v, base, nk, vv);
     }
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < SPT; ++a)
 #pragma unroll
       for (int c = 0; c < 4; ++c) gs[a][c] = gs[a][c] + g[a][c];
   }
   if constexpr (XS) {
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < SPT; ++a)
 #pragma unroll
       for (int c = 0; c < 4; ++c) xx[a][c] = 0.0f;  // not read: weight decay is 0 here
   } else {
-    load_chunk<C, TAIL, NT>(x, base, nk, xx);
+    load_chunk<C, TAIL, NT, SPT>(x, base, nk, xx);
   }
   const float fW = (float)W;
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < SPT; ++a)
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const float gb = gs[a][c] / fW;
@@ -1816,23 +1854,24 @@ __device__ __forceinline__ void warmup_pass1_chunk(int64_t k, const DevTable& ta
       vv[a][c] = (cf.beta2 * vv[a][c]) + (cf.a2 * (gb * gb));
       u[a][c] = warmup_dir(mm[a][c], vv[a][c], xx[a][c], cf);
     }
-  store_chunk<C, TAIL, NT>(m, base, nk, mm);
-  store_chunk<C, TAIL, NT>(v, base, nk, vv);
-  segment_sums<C, 4, !XS, true>(tab, ch.k, base, nk, xx, u, red, seg_x, seg_u);
+  store_chunk<C, TAIL, NT, SPT>(m, base, nk, mm);
+  store_chunk<C, TAIL, NT, SPT>(v, base, nk, vv);
+  segment_sums<C, SPT, !XS, true>(tab, ch.k, base, nk, xx, u, red, seg_x, seg_u);
 }
 
-template <int C, bool NT = false, int WPE = 1, bool XS = false>
-__global__ void __launch_bounds__(Geo<C>::T, WPE)
+template <int C, bool NT = false, int WPE = 1, bool XS = false, int SPT = 4, int DEPTH = 1>
+__global__ void __launch_bounds__((Geo<C, SPT>::T), WPE)
 k_warmup_pass1(int64_t n_full, DevTable tab, int W, Workers wk, const float* __restrict__ x,
                float* __restrict__ m, float* __restrict__ v, double* __restrict__ seg_x,
                double* __restrict__ seg_u, Coef cf) {
-  __shared__ double red[2 * (Geo<C>::T / 64)];
+  __shared__ double red[2 * (Geo<C, SPT>::T / 64)];
   const int64_t has_tail = tab.K - n_full;
   if (has_tail && blockIdx.x == 0)
-    warmup_pass1_chunk<C, true, NT, XS>(n_full, tab, W, wk, x, m, v, seg_x, seg_u, cf, red);
+    warmup_pass1_chunk<C, true, NT, XS, SPT, DEPTH>(n_full, tab, W, wk, x, m, v, seg_x, seg_u,
+                                                    cf, red);
   else
-    warmup_pass1_chunk<C, kSmall<C>, NT, XS>((int64_t)blockIdx.x - has_tail, tab, W, wk, x, m, v,
-                                         seg_x, seg_u, cf, red);
+    warmup_pass1_chunk<C, kSmall<C>, NT, XS, SPT, DEPTH>((int64_t)blockIdx.x - has_tail, tab, W,
+                                                         wk, x, m, v, seg_x, seg_u, cf, red);
 }
 
 // Per tensor: norms, trust ratio, clip, c_sum.
@@ -1863,9 +1902,9 @@ k_warmup_finalize(DevTable tab, const double* __restrict__ seg_x, const double* 
 
 // Warmup pass 2: x = x - (lr*c_l)*u with u recomputed from the new m, v.
 // XO: also the per-(chunk, tensor) sums of the updated x^2 into x_sq, by the
-// reduction pass 1 uses, for the next step's pass 1 to take instead of
-// reading x.
-template <int C, bool TAIL, bool NT, bool XO>
+// reduction pass 1 uses (same SPT), for the next step's pass 1 to take
+// instead of reading x.
+template <int C, bool TAIL, bool NT, bool XO, int SPT>
 __device__ __forceinline__ void warmup_pass2_chunk(int64_t k, const DevTable& tab,
                                                    const float* __restrict__ m,
                                                    const float* __restrict__ v,
@@ -1874,35 +1913,35 @@ __device__ __forceinline__ void warmup_pass2_chunk(int64_t k, const DevTable& ta
                                                    double* __restrict__ x_sq, const Coef& cf,
                                                    double* red) {
   const ChunkAt<C, TAIL> ch(k, tab.N);
-  Slots mm, vv, xx, st;
-  load_chunk<C, TAIL, NT>(m, ch.base, ch.nk, mm);
-  load_chunk<C, TAIL, NT>(v, ch.base, ch.nk, vv);
-  load_chunk<C, TAIL, NT>(x, ch.base, ch.nk, xx);
-  step_sizes<C, TAIL>(tab, ch.k, ch.base, c_layer, cf.lr, st);
+  SlotsN<SPT> mm, vv, xx, st;
+  load_chunk<C, TAIL, NT, SPT>(m, ch.base, ch.nk, mm);
+  load_chunk<C, TAIL, NT, SPT>(v, ch.base, ch.nk, vv);
+  load_chunk<C, TAIL, NT, SPT>(x, ch.base, ch.nk, xx);
+  step_sizes<C, TAIL, SPT>(tab, ch.k, ch.base, c_layer, cf.lr, st);
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < SPT; ++a)
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const float u = warmup_dir(mm[a][c], vv[a][c], xx[a][c], cf);
       xx[a][c] = xx[a][c] - (st[a][c] * u);
     }
-  store_chunk<C, TAIL, NT>(x, ch.base, ch.nk, xx);
-  if constexpr (XO) segment_sums<C, 4, true, false>(tab, ch.k, ch.base, ch.nk, xx, xx, red, x_sq,
-                                                    nullptr);
+  store_chunk<C, TAIL, NT, SPT>(x, ch.base, ch.nk, xx);
+  if constexpr (XO) segment_sums<C, SPT, true, false>(tab, ch.k, ch.base, ch.nk, xx, xx, red, x_sq,
+                                                      nullptr);
 }
 
-template <int C, bool NT = false, bool XO = false>
-__global__ void __launch_bounds__(Geo<C>::T)
+template <int C, bool NT = false, bool XO = false, int SPT = 4>
+__global__ void __launch_bounds__((Geo<C, SPT>::T))
 k_warmup_pass2(int64_t n_full, DevTable tab, const float* __restrict__ m, const float* __restrict__ v,
                float* __restrict__ x, const float* __restrict__ c_layer, double* __restrict__ x_sq,
                Coef cf) {
-  __shared__ double red[XO ? 2 * (Geo<C>::T / 64) : 1];
+  __shared__ double red[XO ? 2 * (Geo<C, SPT>::T / 64) : 1];
   const int64_t has_tail = tab.K - n_full;
   if (has_tail && blockIdx.x == 0)
-    warmup_pass2_chunk<C, true, NT, XO>(n_full, tab, m, v, x, c_layer, x_sq, cf, red);
+    warmup_pass2_chunk<C, true, NT, XO, SPT>(n_full, tab, m, v, x, c_layer, x_sq, cf, red);
   else
-    warmup_pass2_chunk<C, kSmall<C>, NT, XO>((int64_t)blockIdx.x - has_tail, tab, m, v, x, c_layer,
-                                         x_sq, cf, red);
+    warmup_pass2_chunk<C, kSmall<C>, NT, XO, SPT>((int64_t)blockIdx.x - has_tail, tab, m, v, x,
+                                                  c_layer, x_sq, cf, red);
 }
 
 // Freeze, element part: v_fresh = v, error buffers cleared.
