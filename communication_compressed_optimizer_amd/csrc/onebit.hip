@@ -43,7 +43,6 @@ using onebit_host::check_n;
 using onebit_host::check_W;
 using onebit_host::chunk_supported;
 using onebit_host::fail;
-using onebit_host::kMaxChunks;
 using onebit_host::ok;
 using onebit_host::Spans;
 
@@ -274,6 +273,27 @@ constexpr int kAdamWarmupChunk = 4096;
 // W = 8, on a 10 M-element buffer it was 2-4% faster).
 constexpr int kAdamWarmupSPT = 2;
 constexpr int kAdamWarmupDepth = 2;
+
+// The host's bound on the chunks of one launch (onebit_host::max_chunks)
+// assumes these workgroup widths: four float4 slots per thread for the
+// entry points that take n and chunk, table_slots(C) for the narrowest
+// layout a table kernel takes, so no grid reaches 2^32 work-items.
+template <int C>
+constexpr bool launch_widths_bounded() {
+  constexpr int64_t codec = onebit_host::chunk_threads(C, 4);
+  constexpr int64_t table = onebit_host::chunk_threads(C, onebit_host::table_slots(C));
+  return Geo<C>::T <= codec && Geo<C, kAdam_SPT>::T <= codec && Geo<C>::T <= table &&
+         Geo<C, kPassA_SPT>::T <= table && Geo<C, kWarm_SPT<C>>::T <= table;
+}
+static_assert(launch_widths_bounded<64>() && launch_widths_bounded<128>() &&
+                  launch_widths_bounded<256>() && launch_widths_bounded<512>() &&
+                  launch_widths_bounded<1024>() && launch_widths_bounded<2048>() &&
+                  launch_widths_bounded<4096>() && launch_widths_bounded<8192>() &&
+                  launch_widths_bounded<16384>(),
+              "a launch geometry is wider than the host's chunk bound assumes");
+static_assert(Geo<kAdamWarmupChunk, kAdamWarmupSPT>::T <=
+                  onebit_host::chunk_threads(kAdamWarmupChunk, kAdamWarmupSPT),
+              "the 1-bit Adam warmup's width");
 
 template <int C>
 struct LaunchCompress {
@@ -1222,7 +1242,7 @@ int onebit_adam_warmup_step(int64_t n, int32_t W, const float* const* grads, flo
   if (n < 0) return fail(ONEBIT_EINVAL, "%s: n < 0", __func__);
   if (int rc = check_W(W, __func__)) return rc;
   if (int rc = check_hparams(hp, __func__, false)) return rc;
-  if (int rc = check_n(n, kAdamWarmupChunk, __func__)) return rc;
+  if (int rc = check_n(n, kAdamWarmupChunk, __func__, kAdamWarmupSPT)) return rc;
   if (n == 0) return ok();
   if (!grads) return fail(ONEBIT_EINVAL, "%s: grads is NULL", __func__);
   Workers wk{};

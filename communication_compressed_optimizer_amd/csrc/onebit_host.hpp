@@ -57,15 +57,40 @@ inline size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
 
 constexpr int kMaxWorkers = ONEBIT_MAX_WORKERS;
 
-// Chunk counts beyond this are refused (launch grids are 32-bit).
+// Chunk counts beyond this are refused at any chunk size (chunk and segment
+// indices are 32-bit).
 constexpr int64_t kMaxChunks = INT32_MAX / 2;
+
+// Threads per chunk of a launch that lays `slots` float4 slots per thread,
+// one workgroup per chunk: one 64-wide wave below 1024 elements (the padded
+// geometry), else chunk / (4 * slots).
+constexpr int64_t chunk_threads(int64_t chunk, int64_t slots) {
+  return chunk < 1024 ? 64 : chunk / (4 * slots);
+}
+
+// Float4 slots per thread of the narrowest layout a kernel on a layer table
+// takes at this chunk size: two for the warmup passes at 4096, else four.
+// onebit.hip checks its launch geometries against it at compile time.
+constexpr int64_t table_slots(int64_t chunk) { return chunk == 4096 ? 2 : 4; }
+
+// Chunks one launch of that layout may cover.  A dispatch counts its grid in
+// work-items, 32 bits wide, so chunks * chunk_threads must stay below 2^32;
+// that binds only below 1024 elements (at 64: fewer than 2^32 elements).
+constexpr int64_t max_chunks(int64_t chunk, int64_t slots = 4) {
+  return (int64_t)UINT32_MAX / chunk_threads(chunk, slots) < kMaxChunks
+             ? (int64_t)UINT32_MAX / chunk_threads(chunk, slots)
+             : kMaxChunks;
+}
 
 // ceil(n / chunk) for n >= 0, chunk >= 1, without the overflow of n + chunk - 1.
 inline int64_t chunks_of(int64_t n, int64_t chunk) { return n / chunk + (n % chunk != 0); }
 
-inline int check_n(int64_t n, int64_t chunk, const char* fn) {
+// n >= 0 (EINVAL) and at most max_chunks(chunk, slots) chunks (EUNSUPPORTED).
+inline int check_n(int64_t n, int64_t chunk, const char* fn, int64_t slots = 4) {
   if (n < 0) return fail(ONEBIT_EINVAL, "%s: n < 0", fn);
-  if (chunks_of(n, chunk) > kMaxChunks) return fail(ONEBIT_EUNSUPPORTED, "%s: n too large", fn);
+  if (chunks_of(n, chunk) > max_chunks(chunk, slots))
+    return fail(ONEBIT_EUNSUPPORTED, "%s: n too large (at most %lld chunks of %lld)", fn,
+                (long long)max_chunks(chunk, slots), (long long)chunk);
   return ONEBIT_OK;
 }
 
@@ -217,9 +242,9 @@ struct HostTable {
 
 // Checks the sizes and returns N and K without building anything: EINVAL for
 // a NULL array, L < 1 or a tensor of fewer than 1 element; EUNSUPPORTED for a
-// chunk that is not a power of two in [64, 16384] or more than 2^30 - 1
-// chunks in all.  The running sum is bounded before each add, so it cannot
-// overflow.
+// chunk that is not a power of two in [64, 16384] or more than
+// max_chunks(chunk, table_slots(chunk)) chunks in all.  The running sum is
+// bounded before each add, so it cannot overflow.
 inline int table_sizes(const int64_t* numels, int32_t L, int32_t chunk, int64_t* N, int64_t* K,
                        const char* fn) {
   if (!numels) return fail(ONEBIT_EINVAL, "%s: NULL argument", fn);
@@ -227,7 +252,7 @@ inline int table_sizes(const int64_t* numels, int32_t L, int32_t chunk, int64_t*
   if (!chunk_supported(chunk))
     return fail(ONEBIT_EUNSUPPORTED, "%s: chunk %d is not a power of two in [64, 16384]", fn,
                 chunk);
-  const int64_t max_n = kMaxChunks * chunk;
+  const int64_t max_n = max_chunks(chunk, table_slots(chunk)) * chunk;
   int64_t n = 0;
   for (int32_t l = 0; l < L; ++l) {
     if (numels[l] < 1)

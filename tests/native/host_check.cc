@@ -36,6 +36,30 @@ static int g_fail = 0;
 static const int32_t kChunks[] = {64, 128, 256, 512, 1024, 2048, 4096, 8192, 16384};
 static const int kNChunks = sizeof kChunks / sizeof kChunks[0];
 
+// Reference for the size bounds, written out per chunk size: the threads of
+// one chunk's workgroup with four float4 slots per thread (the entry points
+// that take n and chunk; one 64-wide wave up to 1024 elements), and the
+// widest a table kernel launches (the warmup passes' two slots at 4096).  A
+// launch of k chunks fits when k <= 2^30 - 1 and k * threads < 2^32.
+static int64_t ref_threads(int32_t chunk, bool table) {
+  switch (chunk) {
+    case 64: case 128: case 256: case 512: case 1024: return 64;
+    case 2048: return 128;
+    case 4096: return table ? 512 : 256;
+    case 8192: return 512;
+    default: return 1024;
+  }
+}
+static bool ref_fits(i128 k, int32_t chunk, bool table) {
+  return k <= (i128)(1 << 30) - 1 && k * ref_threads(chunk, table) <= (i128)0xFFFFFFFFu;
+}
+// The largest n whose chunks fit.
+static int64_t ref_max_n(int32_t chunk, bool table) {
+  i128 k = (i128)(1 << 30) - 1;
+  while (!ref_fits(k, chunk, table)) k = (i128)0xFFFFFFFFu / ref_threads(chunk, table);
+  return (int64_t)(k * chunk);
+}
+
 // ---------------------------------------------------------------------------
 // tables
 // ---------------------------------------------------------------------------
@@ -135,16 +159,17 @@ static void fuzz_tables() {
   check_table(bert, 4096, false);
 }
 
-// table_sizes at the bounds: at most 2^30 - 1 chunks, running sums that
+// table_sizes at the bounds: at most 2^30 - 1 chunks and fewer than 2^32
+// work-items in a launch of the widest table kernel, running sums that
 // would overflow int64, non-positive sizes, NULL, L < 1, bad chunks.
 static void fuzz_table_sizes() {
   for (int32_t chunk : kChunks) {
-    const int64_t max_n = kMaxChunks * chunk;
+    const int64_t max_n = ref_max_n(chunk, true);
     int64_t N = -1, K = -1;
     std::vector<int64_t> v = {max_n};
     EXPECT(table_sizes(v.data(), 1, chunk, &N, &K, "f") == ONEBIT_OK && N == max_n &&
-               K == kMaxChunks,
-           "exact bound refused");
+               K == max_n / chunk,
+           "exact bound refused at chunk %d", chunk);
     v = {max_n + 1};
     EXPECT(table_sizes(v.data(), 1, chunk, &N, &K, "f") == ONEBIT_EUNSUPPORTED, "bound + 1");
     v = {max_n - 5, 5};
@@ -176,7 +201,7 @@ static void fuzz_table_sizes() {
     for (int l = 0; l < L; ++l) {
       switch (r() % 4) {
         case 0: n[l] = (int64_t)(r() >> 1); break;                                  // anything
-        case 1: n[l] = kMaxChunks * chunk / L + (int64_t)(r() % 64) - 32; break;   // near the bound
+        case 1: n[l] = ref_max_n(chunk, true) / L + (int64_t)(r() % 64) - 32; break;  // near the bound
         case 2: n[l] = (int64_t)(r() % 1000) - 5; break;                            // small, some < 1
         default: n[l] = INT64_MAX - (int64_t)(r() % 3); break;
       }
@@ -195,13 +220,13 @@ static void fuzz_table_sizes() {
       for (int64_t x : n) {
         if (x < 1) break;
         run += x;
-        if (run > (i128)kMaxChunks * chunk) {
+        if (run > (i128)ref_max_n(chunk, true)) {
           expect = ONEBIT_EUNSUPPORTED;
           break;
         }
       }
     } else {
-      expect = sum > (i128)kMaxChunks * chunk ? ONEBIT_EUNSUPPORTED : ONEBIT_OK;
+      expect = sum > (i128)ref_max_n(chunk, true) ? ONEBIT_EUNSUPPORTED : ONEBIT_OK;
     }
     const int rc = table_sizes(n.data(), L, chunk, &N, &K, "f");
     EXPECT(rc == expect, "random sizes: rc %d expected %d", rc, expect);
@@ -225,7 +250,8 @@ static void fuzz_scalars() {
     else n = (int64_t)(r() % ((uint64_t)kMaxChunks * 16384 + 2));
     const int rc = check_n(n, chunk, "f");
     const i128 k = n < 0 ? 0 : ((i128)n + chunk - 1) / chunk;
-    const int expect = n < 0 ? ONEBIT_EINVAL : (k > kMaxChunks ? ONEBIT_EUNSUPPORTED : ONEBIT_OK);
+    const int expect =
+        n < 0 ? ONEBIT_EINVAL : (ref_fits(k, (int32_t)chunk, false) ? ONEBIT_OK : ONEBIT_EUNSUPPORTED);
     EXPECT(rc == expect, "check_n(%lld, %lld) = %d, expected %d", (long long)n, (long long)chunk, rc,
            expect);
     if (rc == ONEBIT_OK) {
@@ -236,6 +262,19 @@ static void fuzz_scalars() {
              "Bytes(%lld, %lld)", (long long)n, (long long)chunk);
     }
   }
+  // the exact bound at every chunk size: four slots per thread, and two (the
+  // 1-bit Adam warmup's layout at 4096)
+  for (int32_t chunk : kChunks) {
+    const int64_t n = ref_max_n(chunk, false);
+    EXPECT(check_n(n, chunk, "f") == ONEBIT_OK, "check_n at the bound, chunk %d", chunk);
+    EXPECT(check_n(n + 1, chunk, "f") == ONEBIT_EUNSUPPORTED, "check_n past the bound, chunk %d",
+           chunk);
+  }
+  EXPECT(check_n(ref_max_n(4096, true), 4096, "f", 2) == ONEBIT_OK &&
+             check_n(ref_max_n(4096, true) + 1, 4096, "f", 2) == ONEBIT_EUNSUPPORTED,
+         "check_n with two slots per thread");
+  EXPECT(ref_max_n(64, false) == 67108863LL * 64 && ref_max_n(4096, false) == 16777215LL * 4096,
+         "reference bounds");
   for (int W = -3; W <= 20; ++W)
     EXPECT((check_W(W, "f") == ONEBIT_OK) == (W >= 1 && W <= 16), "check_W(%d)", W);
   EXPECT(check_W(INT32_MIN, "f") == ONEBIT_EUNSUPPORTED && check_W(INT32_MAX, "f") == ONEBIT_EUNSUPPORTED,

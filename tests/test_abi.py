@@ -69,11 +69,18 @@ def test_argument_checks(ob):
     assert lib.onebit_average_packed(10, 4096, 17, arr2, arr2, P(4096), P(4096), P(4096), None,
                                      None) == ob.ONEBIT_EUNSUPPORTED
     assert lib.onebit_decompress(5, 4096, P(4096), P(4096), P(4098), None) == ob.ONEBIT_EALIGN
-    # at most 2^30 - 1 chunks per buffer, refused before any pointer is read
+    # at most 2^30 - 1 chunks per buffer, and fewer than 2^32 work-items in
+    # the launch (below 1024 elements a chunk takes one 64-wide wave, so at
+    # chunk 64 fewer than 2^32 elements), refused before any pointer is read
     big = (1 << 30) * 1024
     assert lib.onebit_compress_ef(big, 1024, *[P(4096)] * 4, None, None) == \
         ob.ONEBIT_EUNSUPPORTED
     assert "n too large" in ob.onebit_last_error()
+    assert lib.onebit_compress_ef(1 << 32, 64, *[P(4096)] * 4, None, None) == \
+        ob.ONEBIT_EUNSUPPORTED
+    assert "at most 67108863 chunks of 64" in ob.onebit_last_error()
+    assert lib.onebit_decompress((1 << 32) - 63, 64, P(4096), P(4096), P(4096), None) == \
+        ob.ONEBIT_EUNSUPPORTED
     assert lib.onebit_average_packed(big, 1024, 2, arr2, arr2, P(4096), P(4096), P(4096), None,
                                      None) == ob.ONEBIT_EUNSUPPORTED
     assert lib.onebit_decompress(big, 1024, P(4096), P(4096), P(4096), None) == \
@@ -94,6 +101,10 @@ def test_table_checks(ob):
     # are refused before anything is allocated
     numels = (ctypes.c_int64 * 3)(1 << 62, 1 << 62, 1 << 62)
     assert lib.onebit_layer_table_create(numels, 3, 4096, ctypes.byref(out)) == \
+        ob.ONEBIT_EUNSUPPORTED
+    assert "too many chunks" in ob.onebit_last_error()
+    numels = (ctypes.c_int64 * 1)(1 << 32)
+    assert lib.onebit_layer_table_create(numels, 1, 64, ctypes.byref(out)) == \
         ob.ONEBIT_EUNSUPPORTED
     assert "too many chunks" in ob.onebit_last_error()
     numels = (ctypes.c_int64 * 2)((1 << 29) * 4096, (1 << 29) * 4096)

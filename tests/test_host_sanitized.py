@@ -8,7 +8,8 @@ byte counts, the workspace layout and the hyper-parameter domains.  It
 includes no HIP header, so tests/native/host_check.cc compiles it with g++
 and the sanitizers and fuzzes it against brute-force references (random
 ragged tables checked element by element and segment by segment, sizes at
-the 2^30 - 1 chunk bound and at int64 overflow, pointer ranges near the top
+the chunk bounds (2^30 - 1 chunks, and under 2^32 work-items per launch) and at
+int64 overflow, pointer ranges near the top
 of the address space, random hyper-parameter structs)."""
 import os
 import shutil
