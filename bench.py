@@ -137,14 +137,14 @@ def pattern_ceiling(torch, stream, wl, g, e, err_s, m, v, vf, bits_w, bits_s, ac
     fraction of its own pattern's rate."""
     import ctypes
     lib = _ceiling_lib()
-    C, N, W = wl.chunk, wl.N, wl.W
-    n = (N // C) * C                               # whole chunks only
+    N, W = wl.N, wl.W
+    n = (N // 4096) * 4096                         # the kernels' whole 4096-element chunks
     P = ctypes.c_void_p
     ga = (P * W)(*[t.data_ptr() for t in g])
     ea = (P * W)(*[t.data_ptr() for t in e])
     ba = (P * W)(*[t.data_ptr() for t in bits_w])
     tmp = torch.empty(N, dtype=torch.float32, device="cuda")
-    sink = torch.empty(N // C + 1, dtype=torch.float32, device="cuda")
+    sink = torch.empty(N // 4096 + 1, dtype=torch.float32, device="cuda")
     st = stream.cuda_stream
     pbytes = n * (12 * W + 24) + (W + 1) * n // 8
     calls = {
@@ -271,6 +271,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="bert_large")
+    ap.add_argument("--chunk", type=int, default=0,
+                    help="elements per compression chunk (0 = the workload's own, 4096); a "
+                         "power of two in [64, 16384]")
     ap.add_argument("--method", choices=("lamb", "adam", "sparse", "share"), default="lamb",
                     help="1-bit LAMB (the default), the 1-bit Adam mode, the SLAMB-style "
                          "sparse stage, or one GPU's share of a W-GPU 1-bit LAMB step, on the "
@@ -315,10 +318,13 @@ def main():
     from synth.workloads import HPARAMS, WORKLOADS
 
     wl = WORKLOADS[args.workload]
+    if args.chunk:
+        import dataclasses
+        wl = dataclasses.replace(wl, chunk=args.chunk)
     C, N, W, K, L = wl.chunk, wl.N, wl.W, wl.K, wl.L
     torch.cuda.set_device(0)
     dev = "cuda"
-    log(f"[bench] workload {wl.name}: N={N} L={L} K={K} W={W}; allocating state")
+    log(f"[bench] workload {wl.name}: N={N} L={L} K={K} W={W} chunk={C}; allocating state")
     table = ob.LayerTable(wl.numels, C)
 
     def f():
@@ -537,7 +543,7 @@ def ceiling_sweep(args, wl, ob, torch, table, hp, g, e, err_s, m, v, vf, bits_w,
                                         scales_s, hp, ws, status, stream)
 
     tmp = torch.empty(N, dtype=torch.float32, device="cuda")
-    sink = torch.empty(N // C + 1, dtype=torch.float32, device="cuda")
+    sink = torch.empty(N // 4096 + 1, dtype=torch.float32, device="cuda")
     cases = {"phase1_kernel": (phase1, phase1_bytes(wl.N, wl.K, C, W)),
              "pattern": (pattern(0, 0), pbytes)}
     for per_cu, lds in _LDS_CAPS.items():

@@ -3,6 +3,7 @@
 // arithmetic runs in the kernels of onebit_kernels.hpp.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -29,6 +30,7 @@ struct onebit_layer_table {
   int64_t S = 0;  // (chunk, tensor) segments
   int device = -1;  // the device that holds dblock
   int cus = 0;      // its compute units (sizes the persistent pass-A grid)
+  int64_t max_tseg = 0;  // segments of the tensor that has the most
   void* dblock = nullptr;
   DevTable dev{};
 };
@@ -195,7 +197,10 @@ void launch_chunks_capped(unsigned lds, int64_t n, hipStream_t st, KF k, A... ar
 constexpr bool kPassA_NT = true;   // streaming loads and stores
 constexpr bool kPassA_PF = false;  // next-worker prefetch
 constexpr int kPassA_WPE = 6;      // minimum waves per SIMD
-constexpr int kPassA_SPT = 4;      // float4 slots per thread (workgroup = C / (4 * SPT))
+// Float4 slots per thread of pass A (workgroup = C / (4 * SPT)): the chunk's
+// own layout, four from 1024 elements up.
+template <int C>
+constexpr int kPassA_SPT = kSlots<C>;
 // With 4096-element chunks and at least kPassA_ring_min_W workers, pass A
 // runs as a persistent grid with two workers and the next chunk's first
 // three in flight (k_compressed_pass_a_ring).  At BERT-Large, W = 8,
@@ -239,7 +244,7 @@ constexpr unsigned kPassB_lds = C == 4096 ? 65536u : 0u;
 // gradient in flight, or four slots with two, no faster.
 constexpr bool kWarm_NT = true;
 template <int C>
-constexpr int kWarm_SPT = C == 4096 ? 2 : 4;
+constexpr int kWarm_SPT = C == 4096 ? 2 : kSlots<C>;
 template <int C>
 constexpr int kWarm_DEPTH = C == 4096 ? 2 : 1;
 // Standalone codec kernels (N = 333,563,904, W = 8, interleaved): streaming
@@ -252,7 +257,8 @@ constexpr bool kCodec_NT = true;
 constexpr bool kAdam_NT = true;
 constexpr bool kAdam_PF = false;
 constexpr int kAdam_WPE = 6;
-constexpr int kAdam_SPT = 4;
+template <int C>
+constexpr int kAdam_SPT = kSlots<C>;
 // Sparse-stage kernel (BERT-Large, W = 8, 1 of 64 blocks, interleaved):
 // streaming accesses 6.36 ms against 6.66 ms plain; a 5- or 6-wave register
 // cap changes nothing (6.38 ms), so it runs uncapped (104 VGPRs, no spills).
@@ -274,6 +280,14 @@ constexpr int kAdamWarmupChunk = 4096;
 constexpr int kAdamWarmupSPT = 2;
 constexpr int kAdamWarmupDepth = 2;
 
+// The per-tensor finalize kernels reduce a tensor's (chunk, tensor) segments
+// with one workgroup.  A tensor of more segments than kFinalizeWideSegs (only
+// with short chunks: at 64 elements a 16M-element tensor has 262,144; the
+// BERT-Large embedding has 7,630 at 4096) gets 1024 threads with
+// kFinalizeWideU loads in flight each, else 256 threads with one.
+constexpr int64_t kFinalizeWideSegs = 16384;
+constexpr int kFinalizeWideU = 16;
+
 // The host's bound on the chunks of one launch (onebit_host::max_chunks)
 // assumes these workgroup widths: four float4 slots per thread for the
 // entry points that take n and chunk, table_slots(C) for the narrowest
@@ -282,8 +296,8 @@ template <int C>
 constexpr bool launch_widths_bounded() {
   constexpr int64_t codec = onebit_host::chunk_threads(C, 4);
   constexpr int64_t table = onebit_host::chunk_threads(C, onebit_host::table_slots(C));
-  return Geo<C>::T <= codec && Geo<C, kAdam_SPT>::T <= codec && Geo<C>::T <= table &&
-         Geo<C, kPassA_SPT>::T <= table && Geo<C, kWarm_SPT<C>>::T <= table;
+  return Geo<C>::T <= codec && Geo<C, kAdam_SPT<C>>::T <= codec && Geo<C>::T <= table &&
+         Geo<C, kPassA_SPT<C>>::T <= table && Geo<C, kWarm_SPT<C>>::T <= table;
 }
 static_assert(launch_widths_bounded<64>() && launch_widths_bounded<128>() &&
                   launch_widths_bounded<256>() && launch_widths_bounded<512>() &&
@@ -336,9 +350,14 @@ struct LaunchWarmup {
     else
       launch_chunks_slots<C, S>(t->N, st, k_warmup_pass1<C, kWarm_NT, 1, false, S, D>, t->dev, W,
                                 wk, (const float*)x, m, v, ws.seg_x, ws.seg_u, cf);
-    hipLaunchKernelGGL(k_warmup_finalize<256>, dim3((unsigned)t->L), dim3(256), 0, st, t->dev,
-                       (const double*)(x_in ? x_sq : ws.seg_x), (const double*)ws.seg_u, c_sum,
-                       ws.c_layer, c_out, cf, status);
+    if (t->max_tseg > kFinalizeWideSegs)
+      hipLaunchKernelGGL((k_warmup_finalize<1024, kFinalizeWideU>), dim3((unsigned)t->L),
+                         dim3(1024), 0, st, t->dev, (const double*)(x_in ? x_sq : ws.seg_x),
+                         (const double*)ws.seg_u, c_sum, ws.c_layer, c_out, cf, status);
+    else
+      hipLaunchKernelGGL(k_warmup_finalize<256>, dim3((unsigned)t->L), dim3(256), 0, st, t->dev,
+                         (const double*)(x_in ? x_sq : ws.seg_x), (const double*)ws.seg_u, c_sum,
+                         ws.c_layer, c_out, cf, status);
     if (x_sq)
       launch_chunks_slots<C, S>(t->N, st, k_warmup_pass2<C, kWarm_NT, true, S>, t->dev,
                                 (const float*)m, (const float*)v, x, (const float*)ws.c_layer,
@@ -392,8 +411,8 @@ struct LaunchPassA {
                            status);
     } else {
       hipLaunchKernelGGL(
-          (k_compressed_pass_a<C, kPassA_NT, kPassA_PF, kPassA_WPE, kPassA_SPT, RN, PM>),
-          dim3((unsigned)t->K), dim3(Geo<C, kPassA_SPT>::T), 0, st, n_full, t->dev, W, wk,
+          (k_compressed_pass_a<C, kPassA_NT, kPassA_PF, kPassA_WPE, kPassA_SPT<C>, RN, PM>),
+          dim3((unsigned)t->K), dim3(Geo<C, kPassA_SPT<C>>::T), 0, st, n_full, t->dev, W, wk,
           err_s, m, v_frozen, v_fresh, bits_s, scales_s, ws.seg_max, ws.seg_x, ws.seg_u, cf,
           status);
     }
@@ -409,12 +428,12 @@ struct LaunchAdam {
                   int32_t* status, hipStream_t st) {
     const int64_t K = (n + C - 1) / C;
     if (m)
-      hipLaunchKernelGGL((k_adam_allreduce<C, kAdam_NT, kAdam_PF, kAdam_WPE, kAdam_SPT>),
-                         dim3((unsigned)K), dim3(Geo<C, kAdam_SPT>::T), 0, st, n / C, n, K, W, wk,
+      hipLaunchKernelGGL((k_adam_allreduce<C, kAdam_NT, kAdam_PF, kAdam_WPE, kAdam_SPT<C>>),
+                         dim3((unsigned)K), dim3(Geo<C, kAdam_SPT<C>>::T), 0, st, n / C, n, K, W, wk,
                          err_s, (const float*)m, bits_s, scales_s, cf, status);
     else
-      hipLaunchKernelGGL((k_adam_allreduce<C, kAdam_NT, kAdam_PF, kAdam_WPE, kAdam_SPT, true>),
-                         dim3((unsigned)K), dim3(Geo<C, kAdam_SPT>::T), 0, st, n / C, n, K, W, wk,
+      hipLaunchKernelGGL((k_adam_allreduce<C, kAdam_NT, kAdam_PF, kAdam_WPE, kAdam_SPT<C>, true>),
+                         dim3((unsigned)K), dim3(Geo<C, kAdam_SPT<C>>::T), 0, st, n / C, n, K, W, wk,
                          err_s, (const float*)m, bits_s, scales_s, cf, status);
     launch_chunks<C>(n, st, k_adam_update<C, kAdam_NT>, n, (const uint32_t*)bits_s,
                      (const float*)scales_s, v_frozen, x, m, cf);
@@ -504,10 +523,21 @@ struct LaunchPassB {
                   float* x, float* m, const float* v_frozen, const float* c_avg, float* f_prev,
                   float* c_out, const Coef& cf, bool rho_norm, const Ws& ws, int32_t* status,
                   hipStream_t st) {
-    if (rho_norm)
+    const bool wide = t->max_tseg > kFinalizeWideSegs;
+    if (rho_norm && wide)
+      hipLaunchKernelGGL((k_rescale_finalize<1024, true, kFinalizeWideU>), dim3((unsigned)t->L),
+                         dim3(1024), 0, st, t->dev, (const float*)ws.seg_max,
+                         (const double*)ws.seg_x, (const double*)ws.seg_u, c_avg, f_prev,
+                         ws.c_layer, c_out, cf, status);
+    else if (rho_norm)
       hipLaunchKernelGGL((k_rescale_finalize<256, true>), dim3((unsigned)t->L), dim3(256), 0, st,
                          t->dev, (const float*)ws.seg_max, (const double*)ws.seg_x,
                          (const double*)ws.seg_u, c_avg, f_prev, ws.c_layer, c_out, cf, status);
+    else if (wide)
+      hipLaunchKernelGGL((k_rescale_finalize<1024, false, kFinalizeWideU>), dim3((unsigned)t->L),
+                         dim3(1024), 0, st, t->dev, (const float*)ws.seg_max,
+                         (const double*)ws.seg_x, (const double*)ws.seg_u, c_avg, f_prev,
+                         ws.c_layer, c_out, cf, status);
     else
       hipLaunchKernelGGL((k_rescale_finalize<256>), dim3((unsigned)t->L), dim3(256), 0, st,
                          t->dev, (const float*)ws.seg_max, (const double*)ws.seg_x,
@@ -761,6 +791,8 @@ int onebit_layer_table_create(const int64_t* numels, int32_t L, int32_t chunk,
   t->S = S;
   t->device = device;
   t->cus = cus;
+  for (int32_t l = 0; l < L; ++l)
+    t->max_tseg = std::max<int64_t>(t->max_tseg, (int64_t)lseg[l + 1] - lseg[l]);
   using onebit_host::round256;
   const size_t b_off = round256(sizeof(int64_t) * ((size_t)L + 1));
   const size_t b_k = round256(sizeof(int32_t) * (size_t)K);

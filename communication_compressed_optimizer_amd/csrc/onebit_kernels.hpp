@@ -3,13 +3,14 @@
 // pieces.
 //
 // Every kernel that touches chunks runs one workgroup per chunk of C
-// elements with T = C/(4*SPT) threads (SPT = 4 float4 slots per thread unless
-// a kernel says otherwise: T = C/16); thread t owns the slots p = t + T*k
-// (k = 0..SPT-1) of its chunk, i.e. chunk elements 4p..4p+3.  The loads and
-// stores of a wave are therefore 64 consecutive float4 (1 KiB) per slot:
-// fully coalesced dwordx4 traffic.  A chunk shorter than 1024 elements keeps
-// the 1024-element geometry (one wave) with the chunk in its first C/4
-// slots (struct Geo below).
+// elements with T = C/(4*SPT) threads (SPT = 4 float4 slots per thread from
+// 1024 elements up unless a kernel says otherwise: T = C/16); thread t owns
+// the slots p = t + T*k (k = 0..SPT-1) of its chunk, i.e. chunk elements
+// 4p..4p+3.  The loads and stores of a wave are therefore 64 consecutive
+// float4 (1 KiB) per slot: fully coalesced dwordx4 traffic.  Below 1024
+// elements a chunk takes one wave: two slots per thread at 512, one at 256,
+// and the chunks of 128 and 64 elements lie in the first 32 or 16 lanes of
+// a one-slot wave (struct Geo below).
 //
 // Chunk scale.  The sum of squares of a chunk is the stride-halving tree
 // t[j] += t[j+h], h = C/2, ..., 1 (zero past the last valid element), which
@@ -91,23 +92,29 @@ struct WorkerVals {
   float* v[kMaxWorkers];
 };
 
+// Float4 slots per thread of a chunk's own layout: four from 1024 elements
+// up (T = C/16 threads), and below that as many as keep one 64-wide wave per
+// chunk: two at 512, one at 256 and below.
+template <int C>
+constexpr int kSlots = C >= 1024 ? 4 : (C >= 512 ? 2 : 1);
+
 // C elements per chunk, SPT float4 slots per thread, T = G/(4*SPT) threads,
-// where G = max(C, 1024) is the workgroup's geometry.  A chunk shorter than
-// 1024 elements (SMALL) keeps the 1024-element geometry of one 64-wide wave
-// and lies in its first C/4 slots: every access is then guarded by the
-// chunk's length, as for a partial chunk, and the slots past it are zero.
-// The canonical tree over the padded geometry gives the chunk's own tree
-// bit for bit: its extra top levels only add +0 to sums of squares, which
-// are >= +0.
-template <int C, int SPT = 4>
+// where G = max(C, 256*SPT) is the workgroup's geometry.  A chunk that
+// fills less than one 64-wide wave (SMALL: C < 256*SPT; with its own SPT,
+// the chunks of 64 and 128 elements) keeps the geometry of one wave and lies
+// in its first C/4 slots: every access is then guarded by the chunk's
+// length, as for a partial chunk, and the slots past it are zero.  The
+// canonical tree over the padded geometry gives the chunk's own tree bit for
+// bit: its extra top levels only add +0 to sums of squares, which are >= +0.
+template <int C, int SPT = kSlots<C>>
 struct Geo {
   static_assert(C >= 64 && C <= 16384 && (C & (C - 1)) == 0, "chunk must be 2^6..2^14");
   static_assert(SPT == 1 || SPT == 2 || SPT == 4, "slots per thread");
-  static constexpr bool SMALL = C < 1024;
-  static constexpr int G = SMALL ? 1024 : C;  // elements a workgroup lays out
-  static constexpr int T = G / (4 * SPT);     // threads per chunk
-  static constexpr int NW = T / 64;           // waves per chunk
-  static constexpr int WORDS = C / 32;        // sign words per chunk
+  static constexpr bool SMALL = C < 256 * SPT;
+  static constexpr int G = SMALL ? 256 * SPT : C;  // elements a workgroup lays out
+  static constexpr int T = G / (4 * SPT);          // threads per chunk
+  static constexpr int NW = T / 64;                // waves per chunk
+  static constexpr int WORDS = C / 32;             // sign words per chunk
   static_assert(T >= 64 && T <= 1024, "workgroup size");
 };
 
@@ -119,6 +126,8 @@ constexpr bool kSmall = Geo<C>::SMALL;
 template <int S>
 using SlotsN = float[S][4];  // [slot k][component c]
 using Slots = SlotsN<4>;
+template <int C>
+using SlotsOf = SlotsN<kSlots<C>>;  // a chunk's slots in its own layout
 
 // Chunk k of an n-element buffer.  Chunk code is instantiated twice: for the
 // full chunks (TAIL = false: nk == C at compile time, no guards) and for the
@@ -133,7 +142,7 @@ struct ChunkAt {
     base = k * C;
     // a guarded chunk is the partial last chunk (n - base < C), or any
     // chunk shorter than the geometry
-    if constexpr (TAIL && Geo<C>::SMALL) nk = (int)(n - base < C ? n - base : C);
+    if constexpr (TAIL && C < 1024) nk = (int)(n - base < C ? n - base : C);
     else nk = TAIL ? (int)(n - base) : C;
   }
 };
@@ -163,7 +172,7 @@ __device__ __forceinline__ void st4(float* p, f32x4 v) {
   else *q = v;
 }
 
-template <int C, int SPT = 4>
+template <int C, int SPT = kSlots<C>>
 __device__ __forceinline__ bool slot_valid(int k, int c, int nk) {
   return 4 * ((int)threadIdx.x + Geo<C, SPT>::T * k) + c < nk;
 }
@@ -178,7 +187,7 @@ __device__ __forceinline__ P* scalar_ptr(P* p) {
   return reinterpret_cast<P*>(((uint64_t)hi << 32) | lo);
 }
 
-template <int C, bool TAIL, bool NT = false, int SPT = 4>
+template <int C, bool TAIL, bool NT = false, int SPT = kSlots<C>>
 __device__ __forceinline__ void load_chunk(const float* __restrict__ p, int64_t base, int nk,
                                            SlotsN<SPT>& o) {
   constexpr int T = Geo<C, SPT>::T;
@@ -194,6 +203,24 @@ __device__ __forceinline__ void load_chunk(const float* __restrict__ p, int64_t 
       o[k][2] = v.z;
       o[k][3] = v.w;
     }
+  } else if constexpr (C < 1024) {
+    // a chunk shorter than 1024 elements takes this path whole: each slot it
+    // fills is one 16-byte access (chunks start on a slot boundary, so only
+    // a partial last chunk has a slot that is part valid)
+#pragma unroll
+    for (int k = 0; k < SPT; ++k) {
+      const int e0 = 4 * (t + T * k);
+      if (e0 + 4 <= nk) {
+        const f32x4 v = ld4<NT>(p + (base + e0));
+        o[k][0] = v.x;
+        o[k][1] = v.y;
+        o[k][2] = v.z;
+        o[k][3] = v.w;
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) o[k][c] = e0 + c < nk ? p[base + e0 + c] : 0.0f;
+      }
+    }
   } else {
 #pragma unroll
     for (int k = 0; k < SPT; ++k)
@@ -202,7 +229,7 @@ __device__ __forceinline__ void load_chunk(const float* __restrict__ p, int64_t 
   }
 }
 
-template <int C, bool TAIL, bool NT = false, int SPT = 4>
+template <int C, bool TAIL, bool NT = false, int SPT = kSlots<C>>
 __device__ __forceinline__ void store_chunk(float* __restrict__ p, int64_t base, int nk,
                                             const SlotsN<SPT>& o) {
   constexpr int T = Geo<C, SPT>::T;
@@ -213,6 +240,18 @@ __device__ __forceinline__ void store_chunk(float* __restrict__ p, int64_t base,
       const f32x4 v = {o[k][0], o[k][1], o[k][2], o[k][3]};
       char* pk = scalar_ptr(reinterpret_cast<char*>(p + (base + (int64_t)(4 * T * k))));
       st4<NT>(reinterpret_cast<float*>(pk + 16u * threadIdx.x), v);
+    }
+  } else if constexpr (C < 1024) {
+#pragma unroll
+    for (int k = 0; k < SPT; ++k) {
+      const int e0 = 4 * (t + T * k);
+      if (e0 + 4 <= nk) {
+        st4<NT>(p + (base + e0), f32x4{o[k][0], o[k][1], o[k][2], o[k][3]});
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          if (e0 + c < nk) p[base + e0 + c] = o[k][c];
+      }
     }
   } else {
 #pragma unroll
@@ -249,7 +288,7 @@ __device__ __forceinline__ float wave_tree_sum(float v) {
 
 // lds: 2*T float4 (double-buffered between consecutive calls, so one
 // barrier per call suffices).  Returns the sum in every thread.
-template <int C, int SPT = 4>
+template <int C, int SPT = kSlots<C>>
 __device__ __forceinline__ float chunk_sumsq(const SlotsN<SPT>& z, float4* __restrict__ lds, int& parity) {
   constexpr int T = Geo<C, SPT>::T;
   constexpr int NW = Geo<C, SPT>::NW;
@@ -311,7 +350,7 @@ __device__ __forceinline__ uint32_t or_group8(uint32_t x) {
 // nib[k]: bit c = sign of element 4(t+T*k)+c.  words: the chunk's C/32 words.
 // A chunk shorter than the geometry owns only its first WORDS words; the
 // groups of lanes past them neither store nor load.
-template <int C, int SPT = 4>
+template <int C, int SPT = kSlots<C>>
 __device__ __forceinline__ void store_sign_words(uint32_t* __restrict__ words, const uint32_t (&nib)[SPT]) {
   constexpr int T = Geo<C, SPT>::T;
   const int t = threadIdx.x;
@@ -323,7 +362,7 @@ __device__ __forceinline__ void store_sign_words(uint32_t* __restrict__ words, c
   }
 }
 
-template <int C, int SPT = 4>
+template <int C, int SPT = kSlots<C>>
 __device__ __forceinline__ void load_sign_nibbles(const uint32_t* __restrict__ words, uint32_t (&nib)[SPT]) {
   constexpr int T = Geo<C, SPT>::T;
   const int t = threadIdx.x;
@@ -343,7 +382,7 @@ __device__ __forceinline__ float signed_scale(const uint32_t (&nib)[S], int k, i
 // Error-compensated 1-bit compression of z in place (z becomes the error):
 // returns the chunk scale s; nib receives the sign nibbles (0 past the last
 // valid element, whose slots are cleared first so they count as 0).
-template <int C, bool TAIL, int SPT = 4>
+template <int C, bool TAIL, int SPT = kSlots<C>>
 __device__ __forceinline__ float compress_slots(SlotsN<SPT>& z, int nk, float4* lds, int& parity,
                                                 uint32_t (&nib)[SPT]) {
   if constexpr (TAIL) {
@@ -433,7 +472,7 @@ __device__ __forceinline__ int tensor_of(const DevTable& tab, int l0, int l1, in
 
 // Per-(chunk, tensor) maximum of q over the chunk's valid elements (NaN if
 // any of them is NaN).
-template <int C, int SPT = 4>
+template <int C, int SPT = kSlots<C>>
 __device__ __forceinline__ void segment_max(const DevTable& tab, int64_t k, int64_t base, int nk,
                                             const SlotsN<SPT>& q, float* red, float* __restrict__ seg_max) {
   constexpr int T = Geo<C, SPT>::T;
@@ -463,7 +502,7 @@ __device__ __forceinline__ void segment_max(const DevTable& tab, int64_t k, int6
 // is neither read nor written).  The warmup's two passes both call this, so
 // the sum of x^2 that pass 2 carries over for the updated parameters is, bit
 // for bit, the one the next step's pass 1 would form from them.
-template <int C, int SPT = 4, bool HA = true, bool HB = true>
+template <int C, int SPT = kSlots<C>, bool HA = true, bool HB = true>
 __device__ __forceinline__ void segment_sums(const DevTable& tab, int64_t k, int64_t base, int nk,
                                              const SlotsN<SPT>& a_, const SlotsN<SPT>& b_,
                                              double* red, double* __restrict__ seg_a,
@@ -518,14 +557,14 @@ __device__ __forceinline__ void compress_ef_chunk(int64_t k, int64_t n, const fl
                                                   float4* lds) {
   int parity = 0;
   const ChunkAt<C, TAIL> ch(k, n);
-  Slots z, e;
+  SlotsOf<C> z, e;
   load_chunk<C, TAIL, NT>(in, ch.base, ch.nk, z);
   load_chunk<C, TAIL, NT>(err, ch.base, ch.nk, e);
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < kSlots<C>; ++a)
 #pragma unroll
     for (int c = 0; c < 4; ++c) z[a][c] = z[a][c] + e[a][c];
-  uint32_t nib[4];
+  uint32_t nib[kSlots<C>];
   const float s = compress_slots<C, TAIL>(z, ch.nk, lds, parity, nib);
   store_chunk<C, TAIL, NT>(err, ch.base, ch.nk, z);
   store_sign_words<C>(bits + ch.k * Geo<C>::WORDS, nib);
@@ -557,13 +596,13 @@ __device__ __forceinline__ void average_packed_chunk(int64_t k, int64_t n, int W
                                                      int32_t* status, float4* lds) {
   int parity = 0;
   const ChunkAt<C, TAIL> ch(k, n);
-  Slots acc, y;
+  SlotsOf<C> acc, y;
   for (int w = 0; w < W; ++w) {
     const float s = pin.scales[w][ch.k];
-    uint32_t nib[4];
+    uint32_t nib[kSlots<C>];
     load_sign_nibbles<C>(pin.bits[w] + ch.k * Geo<C>::WORDS, nib);
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < kSlots<C>; ++a)
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const float v = signed_scale(nib, a, c, s);
@@ -573,10 +612,10 @@ __device__ __forceinline__ void average_packed_chunk(int64_t k, int64_t n, int W
   load_chunk<C, TAIL, NT>(err_s, ch.base, ch.nk, y);
   const float fW = (float)W;
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < kSlots<C>; ++a)
 #pragma unroll
     for (int c = 0; c < 4; ++c) y[a][c] = (acc[a][c] / fW) + y[a][c];
-  uint32_t nib[4];
+  uint32_t nib[kSlots<C>];
   const float s = compress_slots<C, TAIL>(y, ch.nk, lds, parity, nib);
   store_chunk<C, TAIL, NT>(err_s, ch.base, ch.nk, y);
   store_sign_words<C>(bits_out + ch.k * Geo<C>::WORDS, nib);
@@ -606,11 +645,11 @@ __device__ __forceinline__ void decompress_chunk(int64_t k, int64_t n, const uin
                                                  float* __restrict__ out) {
   const ChunkAt<C, TAIL> ch(k, n);
   const float s = scales[ch.k];
-  uint32_t nib[4];
+  uint32_t nib[kSlots<C>];
   load_sign_nibbles<C>(bits + ch.k * Geo<C>::WORDS, nib);
-  Slots o;
+  SlotsOf<C> o;
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < kSlots<C>; ++a)
 #pragma unroll
     for (int c = 0; c < 4; ++c) o[a][c] = signed_scale(nib, a, c, s);
   store_chunk<C, TAIL, NT>(out, ch.base, ch.nk, o);
@@ -828,7 +867,7 @@ __device__ __forceinline__ void pass_a_chunk(int64_t kk, const DevTable& tab, in
 // One workgroup per chunk; when the buffer ends in a partial chunk, block 0
 // takes it (its guarded code is slower, so it starts first and overlaps the
 // full chunks instead of trailing them).
-template <int C, bool NT = false, bool PF = false, int WPE = 1, int SPT = 4, bool RN = false,
+template <int C, bool NT = false, bool PF = false, int WPE = 1, int SPT = kSlots<C>, bool RN = false,
           bool PM = false>
 __global__ void __launch_bounds__((Geo<C, SPT>::T), WPE)
 k_compressed_pass_a(int64_t n_full, DevTable tab, int W, Workers wk, float* __restrict__ err_s,
@@ -846,7 +885,7 @@ k_compressed_pass_a(int64_t n_full, DevTable tab, int W, Workers wk, float* __re
                                            scales_s, seg_max, seg_z, seg_f, cf, status, lds, red,
                                            dred);
   else
-    pass_a_chunk<C, kSmall<C>, NT, PF, SPT, RN, PM>((int64_t)blockIdx.x - has_tail, tab, W, wk, err_s, m,
+    pass_a_chunk<C, Geo<C, SPT>::SMALL, NT, PF, SPT, RN, PM>((int64_t)blockIdx.x - has_tail, tab, W, wk, err_s, m,
                                             v_frozen, v_fresh, bits_s, scales_s, seg_max, seg_z,
                                             seg_f, cf, status, lds, red, dred);
 }
@@ -879,19 +918,19 @@ __device__ __forceinline__ void adam_allreduce_chunk(int64_t kk, int64_t n, int 
 // k*C) for the persistent pass A: the loop body of workers_and_server.
 template <int C, bool NT>
 __device__ __forceinline__ void ring_worker(int64_t k, int64_t base, int w, const Workers& wk,
-                                            const Slots& bm, Slots& g, const Slots& e, Slots& acc,
+                                            const SlotsOf<C>& bm, SlotsOf<C>& g, const SlotsOf<C>& e, SlotsOf<C>& acc,
                                             const Coef& cf, int32_t* status, float4* lds,
                                             int& parity) {
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < kSlots<C>; ++a)
 #pragma unroll
     for (int c = 0; c < 4; ++c) g[a][c] = (bm[a][c] + (cf.a1 * g[a][c])) + e[a][c];
-  uint32_t wnib[4];
+  uint32_t wnib[kSlots<C>];
   const float s = compress_slots<C, false>(g, C, lds, parity, wnib);
   store_chunk<C, false, NT>(wk.e[w], base, C, g);
   if (wk.bits[w]) store_sign_words<C>(wk.bits[w] + k * Geo<C>::WORDS, wnib);
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < kSlots<C>; ++a)
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const float sv = signed_scale(wnib, a, c, s);
@@ -941,11 +980,11 @@ k_compressed_pass_a_ring(int64_t n_full, DevTable tab, int W, Workers wk,
   int parity = 0;
 
   // the momentum of the chunk ahead: m, or its previous server output
-  Slots mn;
-  uint32_t pn[4] = {0u, 0u, 0u, 0u};
+  SlotsOf<C> mn;
+  uint32_t pn[kSlots<C>] = {0u, 0u, 0u, 0u};
   float sp = 0.0f;
   // three slot buffers for the workers in flight: worker w in buffer w mod 3
-  Slots g0, e0, g1, e1, g2, e2;
+  SlotsOf<C> g0, e0, g1, e1, g2, e2;
   if constexpr (PM) {
     load_sign_nibbles<C>(bits_s + k * Geo<C>::WORDS, pn);
     sp = scales_s[k];
@@ -964,9 +1003,9 @@ k_compressed_pass_a_ring(int64_t n_full, DevTable tab, int W, Workers wk,
   for (; k < n_full; k += G) {
     const int64_t base = k * C;
     const int64_t kn = k + G;
-    Slots bm, acc;
+    SlotsOf<C> bm, acc;
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < kSlots<C>; ++a)
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         if constexpr (PM) bm[a][c] = cf.beta1 * signed_scale(pn, a, c, sp);
@@ -1001,8 +1040,8 @@ k_compressed_pass_a_ring(int64_t n_full, DevTable tab, int W, Workers wk,
 
     // the server's error, then the next chunk's first loads, then the
     // variances (needed only after the server's reduction)
-    Slots y, vf, vz;
-    uint32_t nib[4];
+    SlotsOf<C> y, vf, vz;
+    uint32_t nib[kSlots<C>];
     load_chunk<C, false, NT>(err_s, base, C, y);
     if (kn < n_full) {
       if constexpr (PM) {
@@ -1025,7 +1064,7 @@ k_compressed_pass_a_ring(int64_t n_full, DevTable tab, int W, Workers wk,
     load_chunk<C, false, NT>(v_fresh, base, C, vf);
     load_chunk<C, false, NT>(v_frozen, base, C, vz);
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < kSlots<C>; ++a)
 #pragma unroll
       for (int c = 0; c < 4; ++c) y[a][c] = (acc[a][c] / fW) + y[a][c];
     const float s2 = compress_slots<C, false>(y, C, lds, parity, nib);
@@ -1043,7 +1082,7 @@ k_compressed_pass_a_ring(int64_t n_full, DevTable tab, int W, Workers wk,
 
 // One workgroup per chunk of an n-element buffer; block 0 takes the partial
 // last chunk, if any (as in k_compressed_pass_a).
-template <int C, bool NT = false, bool PF = false, int WPE = 1, int SPT = 4, bool PM = false>
+template <int C, bool NT = false, bool PF = false, int WPE = 1, int SPT = kSlots<C>, bool PM = false>
 __global__ void __launch_bounds__((Geo<C, SPT>::T), WPE)
 k_adam_allreduce(int64_t n_full, int64_t n, int64_t K, int W, Workers wk,
                  float* __restrict__ err_s, const float* __restrict__ m,
@@ -1055,7 +1094,7 @@ k_adam_allreduce(int64_t n_full, int64_t n, int64_t K, int W, Workers wk,
     adam_allreduce_chunk<C, true, NT, PF, SPT, PM>(n_full, n, W, wk, err_s, m, bits_s, scales_s,
                                                    cf, status, lds);
   else
-    adam_allreduce_chunk<C, kSmall<C>, NT, PF, SPT, PM>((int64_t)blockIdx.x - has_tail, n, W, wk,
+    adam_allreduce_chunk<C, Geo<C, SPT>::SMALL, NT, PF, SPT, PM>((int64_t)blockIdx.x - has_tail, n, W, wk,
                                                     err_s, m, bits_s, scales_s, cf, status, lds);
 }
 
@@ -1077,19 +1116,19 @@ __device__ __forceinline__ void beta1_momentum(const ChunkAt<C, TAIL>& ch,
                                                const float* __restrict__ m,
                                                const uint32_t* __restrict__ bits_m,
                                                const float* __restrict__ scales_m, const Coef& cf,
-                                               Slots& bm) {
+                                               SlotsOf<C>& bm) {
   if constexpr (PM) {
-    uint32_t pn[4];
+    uint32_t pn[kSlots<C>];
     load_sign_nibbles<C>(bits_m + ch.k * Geo<C>::WORDS, pn);
     const float sp = scales_m[ch.k];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < kSlots<C>; ++a)
 #pragma unroll
       for (int c = 0; c < 4; ++c) bm[a][c] = cf.beta1 * signed_scale(pn, a, c, sp);
   } else {
     load_chunk<C, TAIL, NT>(m, ch.base, ch.nk, bm);
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < kSlots<C>; ++a)
 #pragma unroll
       for (int c = 0; c < 4; ++c) bm[a][c] = cf.beta1 * bm[a][c];
   }
@@ -1107,15 +1146,15 @@ __device__ __forceinline__ void worker_compress_chunk(int64_t k, int64_t n, cons
                                                       int32_t* status, float4* lds) {
   int parity = 0;
   const ChunkAt<C, TAIL> ch(k, n);
-  Slots z, gg, ee;
+  SlotsOf<C> z, gg, ee;
   beta1_momentum<C, TAIL, NT, PM>(ch, m, bits_m, scales_m, cf, z);
   load_chunk<C, TAIL, NT>(g, ch.base, ch.nk, gg);
   load_chunk<C, TAIL, NT>(e, ch.base, ch.nk, ee);
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < kSlots<C>; ++a)
 #pragma unroll
     for (int c = 0; c < 4; ++c) z[a][c] = (z[a][c] + (cf.a1 * gg[a][c])) + ee[a][c];
-  uint32_t nib[4];
+  uint32_t nib[kSlots<C>];
   const float s = compress_slots<C, TAIL>(z, ch.nk, lds, parity, nib);
   store_chunk<C, TAIL, NT>(e, ch.base, ch.nk, z);
   store_sign_words<C>(bits_w + ch.k * Geo<C>::WORDS, nib);
@@ -1160,15 +1199,15 @@ __device__ __forceinline__ void rescale_stats_chunk(int64_t kk, const DevTable& 
   const ChunkAt<C, TAIL> ch(kk, tab.N);
   const int64_t base = ch.base;
   const int nk = ch.nk;
-  uint32_t nib[4];
+  uint32_t nib[kSlots<C>];
   load_sign_nibbles<C>(bits_s + ch.k * Geo<C>::WORDS, nib);
   const float s2 = scales_s[ch.k];
-  Slots bm, vf, vz;
+  SlotsOf<C> bm, vf, vz;
   beta1_momentum<C, TAIL, NT, PM>(ch, m, bits_m, scales_m, cf, bm);
   load_chunk<C, TAIL, NT>(v_fresh, base, nk, vf);
   load_chunk<C, TAIL, NT>(v_frozen, base, nk, vz);
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < kSlots<C>; ++a)
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const float mh = signed_scale(nib, a, c, s2);
@@ -1178,7 +1217,7 @@ __device__ __forceinline__ void rescale_stats_chunk(int64_t kk, const DevTable& 
   store_chunk<C, TAIL, NT>(v_fresh, base, nk, vf);
   if constexpr (RN) {
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < kSlots<C>; ++a)
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         vz[a][c] = __builtin_sqrtf(vz[a][c]) + cf.eta;
@@ -1187,7 +1226,7 @@ __device__ __forceinline__ void rescale_stats_chunk(int64_t kk, const DevTable& 
     segment_sums<C>(tab, ch.k, base, nk, vz, vf, dred, seg_z, seg_f);
   } else {
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < kSlots<C>; ++a)
 #pragma unroll
       for (int c = 0; c < 4; ++c)
         vz[a][c] = (__builtin_sqrtf(vz[a][c]) + cf.eta) / (__builtin_sqrtf(vf[a][c]) + cf.eta);
@@ -1227,14 +1266,14 @@ __device__ __forceinline__ void adam_update_chunk(int64_t k, int64_t n,
                                                   float* __restrict__ x, float* __restrict__ m,
                                                   const Coef& cf) {
   const ChunkAt<C, TAIL> ch(k, n);
-  uint32_t nib[4];
+  uint32_t nib[kSlots<C>];
   load_sign_nibbles<C>(bits_s + ch.k * Geo<C>::WORDS, nib);
   const float s2 = scales_s[ch.k];
-  Slots xx, vz, mh;
+  SlotsOf<C> xx, vz, mh;
   load_chunk<C, TAIL, NT>(x, ch.base, ch.nk, xx);
   load_chunk<C, TAIL, NT>(v_frozen, ch.base, ch.nk, vz);
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < kSlots<C>; ++a)
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       mh[a][c] = signed_scale(nib, a, c, s2);
@@ -1320,7 +1359,7 @@ __device__ __forceinline__ void adam_warmup_chunk(int64_t k, int64_t n, int W, c
   store_chunk<C, TAIL, true, SPT>(x, base, nk, xx);
 }
 
-template <int C, int WPE = 1, int SPT = 4, int DEPTH = 1>
+template <int C, int WPE = 1, int SPT = kSlots<C>, int DEPTH = 1>
 __global__ void __launch_bounds__((Geo<C, SPT>::T), WPE)
 k_adam_warmup(int64_t n_full, int64_t n, int W, Workers wk, float* __restrict__ x,
               float* __restrict__ m, float* __restrict__ v, Coef cf) {
@@ -1328,7 +1367,7 @@ k_adam_warmup(int64_t n_full, int64_t n, int W, Workers wk, float* __restrict__ 
   if (has_tail && blockIdx.x == 0)
     adam_warmup_chunk<C, true, SPT, DEPTH>(n_full, n, W, wk, x, m, v, cf);
   else
-    adam_warmup_chunk<C, kSmall<C>, SPT, DEPTH>((int64_t)blockIdx.x - has_tail, n, W, wk, x, m, v,
+    adam_warmup_chunk<C, Geo<C, SPT>::SMALL, SPT, DEPTH>((int64_t)blockIdx.x - has_tail, n, W, wk, x, m, v,
                                                 cf);
 }
 
@@ -1358,28 +1397,28 @@ __device__ __forceinline__ void sparse_chunk(int64_t kk, const DevTable& tab, in
   const int b0 = ((sel[ch.k] % NB) + NB) % NB;
   const int64_t per = (int64_t)nsel * 64;
   // per slot: transmitted position within the chunk's values, or -1
-  int pos[4];
+  int pos[kSlots<C>];
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
+  for (int a = 0; a < kSlots<C>; ++a) {
     const int p = t + T * a;                    // float4 slot; block p/16
     const int rel = ((p / 16) - b0 + NB) % NB;
     pos[a] = ((!Geo<C>::SMALL || p < C / 4) && rel < nsel) ? rel * 64 + 4 * (p % 16) : -1;
   }
 
-  Slots bm, acc;
+  SlotsOf<C> bm, acc;
   load_chunk<C, TAIL, NT>(m, base, nk, bm);
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < kSlots<C>; ++a)
 #pragma unroll
     for (int c = 0; c < 4; ++c) bm[a][c] = cf.beta1 * bm[a][c];
 
   for (int w = 0; w < W; ++w) {
-    Slots z, e;
+    SlotsOf<C> z, e;
     load_chunk<C, TAIL, NT>(wk.g[w], base, nk, z);
     load_chunk<C, TAIL, NT>(wk.e[w], base, nk, e);
     float* vw = vals_w.v[w];
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
+    for (int a = 0; a < kSlots<C>; ++a) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         z[a][c] = (bm[a][c] + (cf.a1 * z[a][c])) + e[a][c];
@@ -1406,7 +1445,7 @@ __device__ __forceinline__ void sparse_chunk(int64_t kk, const DevTable& tab, in
   // server average, masked momentum
   const float fW = (float)W;
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < kSlots<C>; ++a)
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[a][c] = pos[a] >= 0 ? acc[a][c] / fW : 0.0f;
 
@@ -1415,7 +1454,7 @@ __device__ __forceinline__ void sparse_chunk(int64_t kk, const DevTable& tab, in
   const int l1 = tab.l1[ch.k];
   const float st0 = cf.lr * c_avg[l0];
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
+  for (int a = 0; a < kSlots<C>; ++a) {
     if (pos[a] < 0) continue;
     const int64_t e0 = base + 4 * (t + T * a);
     float xs[4], vz[4], vf[4];
@@ -1474,12 +1513,12 @@ __device__ __forceinline__ void sparse_chunk(int64_t kk, const DevTable& tab, in
 
 // Transmitted position of thread t's slots within the chunk's values, or -1.
 template <int C>
-__device__ __forceinline__ void sparse_positions(int32_t sel_k, int nsel, int (&pos)[4]) {
+__device__ __forceinline__ void sparse_positions(int32_t sel_k, int nsel, int (&pos)[kSlots<C>]) {
   constexpr int T = Geo<C>::T;
   constexpr int NB = C / 64;
   const int b0 = ((sel_k % NB) + NB) % NB;
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
+  for (int a = 0; a < kSlots<C>; ++a) {
     const int p = (int)threadIdx.x + T * a;
     const int rel = ((p / 16) - b0 + NB) % NB;
     pos[a] = ((!Geo<C>::SMALL || p < C / 4) && rel < nsel) ? rel * 64 + 4 * (p % 16) : -1;
@@ -1495,14 +1534,14 @@ __device__ __forceinline__ void sparse_worker_chunk(int64_t k, int64_t n, int ns
                                                     float* __restrict__ vals, const Coef& cf) {
   const ChunkAt<C, TAIL> ch(k, n);
   const int64_t per = (int64_t)nsel * 64;
-  int pos[4];
+  int pos[kSlots<C>];
   sparse_positions<C>(sel[ch.k], nsel, pos);
-  Slots z, gg, ee;
+  SlotsOf<C> z, gg, ee;
   load_chunk<C, TAIL, NT>(m, ch.base, ch.nk, z);
   load_chunk<C, TAIL, NT>(g, ch.base, ch.nk, gg);
   load_chunk<C, TAIL, NT>(e, ch.base, ch.nk, ee);
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
+  for (int a = 0; a < kSlots<C>; ++a) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       z[a][c] = ((cf.beta1 * z[a][c]) + (cf.a1 * gg[a][c])) + ee[a][c];
@@ -1568,14 +1607,14 @@ __device__ __forceinline__ void sparse_update_chunk(int64_t kk, const DevTable& 
   const int nk = ch.nk;
   const int t = threadIdx.x;
   const int64_t per = (int64_t)nsel * 64;
-  int pos[4];
+  int pos[kSlots<C>];
   sparse_positions<C>(sel[ch.k], nsel, pos);
   // mhat: the server's mean on the selection, 0 elsewhere.  The previous
   // momentum enters only through ghat on the selection, so m is read there
   // alone (elsewhere it is overwritten with 0 unread).
-  Slots bm, mh;
+  SlotsOf<C> bm, mh;
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
+  for (int a = 0; a < kSlots<C>; ++a) {
     if (pos[a] >= 0) {
       const f32x4 v = ld4<NT>(vals_s + ch.k * per + pos[a]);
       mh[a][0] = v.x; mh[a][1] = v.y; mh[a][2] = v.z; mh[a][3] = v.w;
@@ -1598,7 +1637,7 @@ __device__ __forceinline__ void sparse_update_chunk(int64_t kk, const DevTable& 
   const int l1 = tab.l1[ch.k];
   const float st0 = cf.lr * c_avg[l0];
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
+  for (int a = 0; a < kSlots<C>; ++a) {
     if (pos[a] < 0) continue;
     const int64_t e0 = base + 4 * (t + T * a);
     float xs[4], vz[4], vf[4];
@@ -1674,9 +1713,75 @@ k_sparse_step(int64_t n_full, DevTable tab, int W, int nsel, const int32_t* __re
                                v_frozen, v_fresh, c_avg, vals_s, cf, status);
 }
 
+// A thread's share of a tensor's reduction over its segments [lo, hi):
+// segments lo + t, lo + t + TB, ...  With U = 1 one running value; with
+// U > 1 (a tensor of very many segments: short chunks) U strided loads are
+// in flight per step, each into its own running value, and the U values are
+// then combined pairwise.  The order is fixed by (TB, U) and the segment
+// range, so the result is reproducible; the maximum does not depend on it.
+template <int TB, int U>
+__device__ __forceinline__ float thread_seg_max(const float* __restrict__ a, int lo, int hi) {
+  if constexpr (U == 1) {
+    float mx = -__builtin_inff();
+    for (int i = lo + (int)threadIdx.x; i < hi; i += TB) mx = max_nan(mx, a[i]);
+    return mx;
+  } else {
+    float r[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) r[u] = -__builtin_inff();
+    int64_t i = lo + (int64_t)threadIdx.x;
+    for (; i + (int64_t)(U - 1) * TB < hi; i += (int64_t)U * TB)
+#pragma unroll
+      for (int u = 0; u < U; ++u) r[u] = max_nan(r[u], a[i + (int64_t)u * TB]);
+    for (; i < hi; i += TB) r[0] = max_nan(r[0], a[i]);
+#pragma unroll
+    for (int h = U / 2; h >= 1; h /= 2)
+#pragma unroll
+      for (int u = 0; u < h; ++u) r[u] = max_nan(r[u], r[u + h]);
+    return r[0];
+  }
+}
+
+template <int TB, int U>
+__device__ __forceinline__ void thread_seg_sums(const double* __restrict__ a,
+                                                const double* __restrict__ b, int lo, int hi,
+                                                double& A, double& B) {
+  if constexpr (U == 1) {
+    for (int i = lo + (int)threadIdx.x; i < hi; i += TB) {
+      A += a[i];
+      B += b[i];
+    }
+  } else {
+    double ra[U], rb[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) ra[u] = rb[u] = 0.0;
+    int64_t i = lo + (int64_t)threadIdx.x;
+    for (; i + (int64_t)(U - 1) * TB < hi; i += (int64_t)U * TB)
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        ra[u] += a[i + (int64_t)u * TB];
+        rb[u] += b[i + (int64_t)u * TB];
+      }
+    for (; i < hi; i += TB) {
+      ra[0] += a[i];
+      rb[0] += b[i];
+    }
+#pragma unroll
+    for (int h = U / 2; h >= 1; h /= 2)
+#pragma unroll
+      for (int u = 0; u < h; ++u) {
+        ra[u] += ra[u + h];
+        rb[u] += rb[u + h];
+      }
+    A += ra[0];
+    B += rb[0];
+  }
+}
+
 // Per tensor: rho = max of its segments (or, RN, the ratio of the norms from
-// the segments' double sums), soft thresholds, c.
-template <int TB, bool RN = false>
+// the segments' double sums), soft thresholds, c.  One workgroup of TB
+// threads per tensor; U loads in flight per thread (thread_seg_max).
+template <int TB, bool RN = false, int U = 1>
 __global__ void __launch_bounds__(TB)
 k_rescale_finalize(DevTable tab, const float* __restrict__ seg_max, const double* __restrict__ seg_z,
                    const double* __restrict__ seg_f, const float* __restrict__ c_avg,
@@ -1690,15 +1795,11 @@ k_rescale_finalize(DevTable tab, const float* __restrict__ seg_max, const double
   float mx;
   if constexpr (RN) {
     double Z = 0.0, F = 0.0;
-    for (int i = lo + (int)threadIdx.x; i < hi; i += TB) {
-      Z += seg_z[i];
-      F += seg_f[i];
-    }
+    thread_seg_sums<TB, U>(seg_z, seg_f, lo, hi, Z, F);
     block_sum2<TB>(Z, F, dred);
     mx = (Z == 0.0 || F == 0.0) ? 1.0f : (float)(__builtin_sqrt(Z) / __builtin_sqrt(F));
   } else {
-    mx = -__builtin_inff();
-    for (int i = lo + (int)threadIdx.x; i < hi; i += TB) mx = max_nan(mx, seg_max[i]);
+    mx = thread_seg_max<TB, U>(seg_max, lo, hi);
     mx = block_max<TB>(mx, red);
   }
   if (threadIdx.x == 0) {
@@ -1714,7 +1815,7 @@ k_rescale_finalize(DevTable tab, const float* __restrict__ seg_max, const double
 }
 
 // Per-element step size lr*c_l for the chunk's elements.
-template <int C, bool TAIL, int SPT = 4>
+template <int C, bool TAIL, int SPT = kSlots<C>>
 __device__ __forceinline__ void step_sizes(const DevTable& tab, int64_t k, int64_t base,
                                            const float* __restrict__ c_layer, float lr,
                                            SlotsN<SPT>& st) {
@@ -1748,14 +1849,14 @@ __device__ __forceinline__ void pass_b_chunk(int64_t kk, const DevTable& tab,
                                              const float* __restrict__ c_layer, const Coef& cf) {
   const ChunkAt<C, TAIL> ch(kk, tab.N);
   const float s = scales_s[ch.k];
-  uint32_t nib[4];
+  uint32_t nib[kSlots<C>];
   load_sign_nibbles<C>(bits_s + ch.k * Geo<C>::WORDS, nib);
-  Slots vz, xx, mh, st;
+  SlotsOf<C> vz, xx, mh, st;
   load_chunk<C, TAIL, NT>(v_frozen, ch.base, ch.nk, vz);
   load_chunk<C, TAIL, NT>(x, ch.base, ch.nk, xx);
   step_sizes<C, TAIL>(tab, ch.k, ch.base, c_layer, cf.lr, st);
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < kSlots<C>; ++a)
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       mh[a][c] = signed_scale(nib, a, c, s);
@@ -1859,7 +1960,7 @@ __device__ __forceinline__ void warmup_pass1_chunk(int64_t k, const DevTable& ta
   segment_sums<C, SPT, !XS, true>(tab, ch.k, base, nk, xx, u, red, seg_x, seg_u);
 }
 
-template <int C, bool NT = false, int WPE = 1, bool XS = false, int SPT = 4, int DEPTH = 1>
+template <int C, bool NT = false, int WPE = 1, bool XS = false, int SPT = kSlots<C>, int DEPTH = 1>
 __global__ void __launch_bounds__((Geo<C, SPT>::T), WPE)
 k_warmup_pass1(int64_t n_full, DevTable tab, int W, Workers wk, const float* __restrict__ x,
                float* __restrict__ m, float* __restrict__ v, double* __restrict__ seg_x,
@@ -1870,12 +1971,13 @@ k_warmup_pass1(int64_t n_full, DevTable tab, int W, Workers wk, const float* __r
     warmup_pass1_chunk<C, true, NT, XS, SPT, DEPTH>(n_full, tab, W, wk, x, m, v, seg_x, seg_u,
                                                     cf, red);
   else
-    warmup_pass1_chunk<C, kSmall<C>, NT, XS, SPT, DEPTH>((int64_t)blockIdx.x - has_tail, tab, W,
+    warmup_pass1_chunk<C, Geo<C, SPT>::SMALL, NT, XS, SPT, DEPTH>((int64_t)blockIdx.x - has_tail, tab, W,
                                                          wk, x, m, v, seg_x, seg_u, cf, red);
 }
 
-// Per tensor: norms, trust ratio, clip, c_sum.
-template <int TB>
+// Per tensor: norms, trust ratio, clip, c_sum.  One workgroup of TB threads
+// per tensor; UL loads in flight per thread (thread_seg_sums).
+template <int TB, int UL = 1>
 __global__ void __launch_bounds__(TB)
 k_warmup_finalize(DevTable tab, const double* __restrict__ seg_x, const double* __restrict__ seg_u,
                   float* __restrict__ c_sum, float* __restrict__ c_layer, float* __restrict__ c_out,
@@ -1885,10 +1987,7 @@ k_warmup_finalize(DevTable tab, const double* __restrict__ seg_x, const double* 
   const int lo = tab.lseg[l];
   const int hi = tab.lseg[l + 1];
   double X = 0.0, U = 0.0;
-  for (int i = lo + (int)threadIdx.x; i < hi; i += TB) {
-    X += seg_x[i];
-    U += seg_u[i];
-  }
+  thread_seg_sums<TB, UL>(seg_x, seg_u, lo, hi, X, U);
   block_sum2<TB>(X, U, red);
   if (threadIdx.x == 0) {
     const float r = (X == 0.0 || U == 0.0) ? 1.0f : (float)(__builtin_sqrt(X) / __builtin_sqrt(U));
@@ -1930,7 +2029,7 @@ __device__ __forceinline__ void warmup_pass2_chunk(int64_t k, const DevTable& ta
                                                       nullptr);
 }
 
-template <int C, bool NT = false, bool XO = false, int SPT = 4>
+template <int C, bool NT = false, bool XO = false, int SPT = kSlots<C>>
 __global__ void __launch_bounds__((Geo<C, SPT>::T))
 k_warmup_pass2(int64_t n_full, DevTable tab, const float* __restrict__ m, const float* __restrict__ v,
                float* __restrict__ x, const float* __restrict__ c_layer, double* __restrict__ x_sq,
@@ -1940,7 +2039,7 @@ k_warmup_pass2(int64_t n_full, DevTable tab, const float* __restrict__ m, const 
   if (has_tail && blockIdx.x == 0)
     warmup_pass2_chunk<C, true, NT, XO, SPT>(n_full, tab, m, v, x, c_layer, x_sq, cf, red);
   else
-    warmup_pass2_chunk<C, kSmall<C>, NT, XO, SPT>((int64_t)blockIdx.x - has_tail, tab, m, v, x,
+    warmup_pass2_chunk<C, Geo<C, SPT>::SMALL, NT, XO, SPT>((int64_t)blockIdx.x - has_tail, tab, m, v, x,
                                                   c_layer, x_sq, cf, red);
 }
 
@@ -1951,11 +2050,11 @@ __device__ __forceinline__ void freeze_elems_chunk(int64_t k, int64_t n, int W,
                                                    float* __restrict__ v_fresh, const Workers& wk,
                                                    float* __restrict__ err_s) {
   const ChunkAt<C, TAIL> ch(k, n);
-  Slots vv, zero;
+  SlotsOf<C> vv, zero;
   load_chunk<C, TAIL>(v, ch.base, ch.nk, vv);
   store_chunk<C, TAIL>(v_fresh, ch.base, ch.nk, vv);
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < kSlots<C>; ++a)
 #pragma unroll
     for (int c = 0; c < 4; ++c) zero[a][c] = 0.0f;
   for (int w = 0; w < W; ++w) store_chunk<C, TAIL>(wk.e[w], ch.base, ch.nk, zero);

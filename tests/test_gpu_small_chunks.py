@@ -1,11 +1,14 @@
 """Chunks of 64, 128, 256 and 512 elements on the GPU, against the oracle.
 
-A chunk shorter than 1024 elements runs on the workgroup shape of a
-1024-element chunk, one wave per chunk, with the positions past the chunk
-treated as zeros: the stride-halving norm tree of the chunk is then
+A chunk shorter than 1024 elements runs one wave per chunk: two float4
+slots per lane at 512, one at 256, and the chunks of 128 and 64 elements in
+the first 32 or 16 lanes of a one-slot wave, the positions past the chunk
+treated as zeros.  The stride-halving norm tree of the chunk is then
 unchanged, since the extra levels add exact zeros to non-negative partial
 sums, so signs, scales and errors must match the oracle bit for bit, as for
-the longer chunks.  Every entry point family is covered: the codec, the LAMB
+the longer chunks.  A tensor of more than 16,384 segments (here, chunks of
+64 and 128 elements over a tensor of over a million) is finalized by the
+wide per-tensor reduction.  Every entry point family is covered: the codec, the LAMB
 warmup (plain and with the norm carried), the freeze, the compression step
 with fp32 and with packed momentum under both rho rules, the 1-bit Adam mode,
 the sparse stage, and one GPU's share equal to the fused step.  Tables are
@@ -115,6 +118,35 @@ def test_lamb_trajectory_small_chunks(C, W):
     d.compressed_step(step)
     h.compressed_step(step)
     assert_parity(compare_state(d, h), "norm-ratio rho")
+    assert int(d.status.item()) == 0
+
+
+@pytest.mark.parametrize("C", [64, 128])
+def test_many_segments_small_chunks(C):
+    """A tensor of more than 16,384 (chunk, tensor) segments takes the wide
+    per-tensor finalize (1024 threads, 16 loads in flight each) in the
+    warmup and the compression stage: two carried warmup steps, the freeze,
+    a compression step under each rho rule, against the oracle."""
+    big = 16_384 * C + 3 * C + 5
+    wl = Workload("many_segments", [5, big, 3 * C, 1_000_001], W=2, chunk=C, init="fresh",
+                  grad_std=0.02)
+    d, h = DevRun(wl, carry_norm=True), HostRun(wl)
+    off = wl.offsets
+    assert max((off[1:] - 1) // C - off[:-1] // C + 1) > 16_384    # chunks the tensor touches
+    step = 0
+    for _ in range(2):
+        d.warmup_step(step)
+        h.warmup_step(step)
+        step += 1
+    assert_parity(compare_state(d, h, stage="warmup"), "after warmup")
+    d.freeze(2)
+    h.freeze(2)
+    for rho in (ob.ONEBIT_RHO_MAX, ob.ONEBIT_RHO_NORM_RATIO):
+        d.hp.rho_mode = h.hp.rho_mode = rho
+        d.compressed_step(step)
+        h.compressed_step(step)
+        step += 1
+        assert_parity(compare_state(d, h), f"rho mode {rho}")
     assert int(d.status.item()) == 0
 
 
