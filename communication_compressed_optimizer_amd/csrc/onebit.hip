@@ -289,9 +289,10 @@ constexpr int64_t kFinalizeWideSegs = 16384;
 constexpr int kFinalizeWideU = 16;
 
 // The host's bound on the chunks of one launch (onebit_host::max_chunks)
-// assumes these workgroup widths: four float4 slots per thread for the
-// entry points that take n and chunk, table_slots(C) for the narrowest
-// layout a table kernel takes, so no grid reaches 2^32 work-items.
+// assumes these workgroup widths: one 64-wide wave below 1024 elements,
+// else C/16 threads (four float4 slots each) for the entry points that take
+// n and chunk, and C / (4 * table_slots(C)) for the widest layout a table
+// kernel takes, so no grid reaches 2^32 work-items.
 template <int C>
 constexpr bool launch_widths_bounded() {
   constexpr int64_t codec = onebit_host::chunk_threads(C, 4);

@@ -204,7 +204,8 @@ __device__ __forceinline__ void load_chunk(const float* __restrict__ p, int64_t 
       o[k][3] = v.w;
     }
   } else if constexpr (C < 1024) {
-    // a chunk shorter than 1024 elements takes this path whole: each slot it
+    // the guarded path of a chunk shorter than 1024 elements (every chunk of
+    // 64 or 128 elements, and a partial last chunk): each slot the chunk
     // fills is one 16-byte access (chunks start on a slot boundary, so only
     // a partial last chunk has a slot that is part valid)
 #pragma unroll
