@@ -405,13 +405,20 @@ def main():
             ev[2].record(st)
 
     def timed(mm):
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        """ms per step over `steps` steps with nothing between them (the step
+        time), then the two phases' mean times from HIP events recorded
+        around each phase of `steps` further steps (events between kernels
+        cost the stream a little, so they stay out of the step time)."""
         torch.cuda.synchronize()
         t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step(None, mm)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
         for i in range(args.steps):
             step(evs[i], mm)
         torch.cuda.synchronize()
-        t1 = time.perf_counter()
         p1 = [a.elapsed_time(b) for a, b, _ in evs]
         p2 = [b.elapsed_time(c) for _, b, c in evs]
         timed.p1 = sorted(p1)
