@@ -281,11 +281,13 @@ constexpr int kAdamWarmupSPT = 2;
 constexpr int kAdamWarmupDepth = 2;
 
 // The per-tensor finalize kernels reduce a tensor's (chunk, tensor) segments
-// with one workgroup.  A tensor of more segments than kFinalizeWideSegs (only
-// with short chunks: at 64 elements a 16M-element tensor has 262,144; the
-// BERT-Large embedding has 7,630 at 4096) gets 1024 threads with
-// kFinalizeWideU loads in flight each, else 256 threads with one.
-constexpr int64_t kFinalizeWideSegs = 16384;
+// with one workgroup.  When the table's largest tensor has more segments
+// than kFinalizeWideSegs (the BERT-Large embedding has 7,630 at 4096
+// elements; at 64 elements a 16M-element tensor has 262,144), every tensor
+// gets 1024 threads with up to kFinalizeWideU loads in flight each, else 256
+// threads that take their segments one at a time: 256 threads walked the
+// embedding's segments in 30 dependent loads each, 11-16 us of every step.
+constexpr int64_t kFinalizeWideSegs = 2048;
 constexpr int kFinalizeWideU = 16;
 
 // The host's bound on the chunks of one launch (onebit_host::max_chunks)

@@ -1716,10 +1716,11 @@ k_sparse_step(int64_t n_full, DevTable tab, int W, int nsel, const int32_t* __re
 
 // A thread's share of a tensor's reduction over its segments [lo, hi):
 // segments lo + t, lo + t + TB, ...  With U = 1 one running value; with
-// U > 1 (a tensor of very many segments: short chunks) U strided loads are
-// in flight per step, each into its own running value, and the U values are
-// then combined pairwise.  The order is fixed by (TB, U) and the segment
-// range, so the result is reproducible; the maximum does not depend on it.
+// U > 1 (a tensor of many segments) the segments are taken in rounds of
+// U*TB, each round's U loads per thread issued together (predicated past
+// hi) into U running values, which are then combined pairwise.  The order
+// is fixed by (TB, U) and the segment range, so the result is
+// reproducible; the maximum does not depend on it.
 template <int TB, int U>
 __device__ __forceinline__ float thread_seg_max(const float* __restrict__ a, int lo, int hi) {
   if constexpr (U == 1) {
@@ -1730,11 +1731,10 @@ __device__ __forceinline__ float thread_seg_max(const float* __restrict__ a, int
     float r[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) r[u] = -__builtin_inff();
-    int64_t i = lo + (int64_t)threadIdx.x;
-    for (; i + (int64_t)(U - 1) * TB < hi; i += (int64_t)U * TB)
+    for (int64_t i = lo + (int64_t)threadIdx.x; i < hi; i += (int64_t)U * TB)
 #pragma unroll
-      for (int u = 0; u < U; ++u) r[u] = max_nan(r[u], a[i + (int64_t)u * TB]);
-    for (; i < hi; i += TB) r[0] = max_nan(r[0], a[i]);
+      for (int u = 0; u < U; ++u)
+        if (i + (int64_t)u * TB < hi) r[u] = max_nan(r[u], a[i + (int64_t)u * TB]);
 #pragma unroll
     for (int h = U / 2; h >= 1; h /= 2)
 #pragma unroll
@@ -1756,17 +1756,13 @@ __device__ __forceinline__ void thread_seg_sums(const double* __restrict__ a,
     double ra[U], rb[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) ra[u] = rb[u] = 0.0;
-    int64_t i = lo + (int64_t)threadIdx.x;
-    for (; i + (int64_t)(U - 1) * TB < hi; i += (int64_t)U * TB)
+    for (int64_t i = lo + (int64_t)threadIdx.x; i < hi; i += (int64_t)U * TB)
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        ra[u] += a[i + (int64_t)u * TB];
-        rb[u] += b[i + (int64_t)u * TB];
-      }
-    for (; i < hi; i += TB) {
-      ra[0] += a[i];
-      rb[0] += b[i];
-    }
+      for (int u = 0; u < U; ++u)
+        if (i + (int64_t)u * TB < hi) {
+          ra[u] += a[i + (int64_t)u * TB];
+          rb[u] += b[i + (int64_t)u * TB];
+        }
 #pragma unroll
     for (int h = U / 2; h >= 1; h /= 2)
 #pragma unroll

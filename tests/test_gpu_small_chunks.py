@@ -6,9 +6,9 @@ the first 32 or 16 lanes of a one-slot wave, the positions past the chunk
 treated as zeros.  The stride-halving norm tree of the chunk is then
 unchanged, since the extra levels add exact zeros to non-negative partial
 sums, so signs, scales and errors must match the oracle bit for bit, as for
-the longer chunks.  A tensor of more than 16,384 segments (here, chunks of
-64 and 128 elements over a tensor of over a million) is finalized by the
-wide per-tensor reduction.  Every entry point family is covered: the codec, the LAMB
+the longer chunks.  A tensor of many segments (here more than 16,384:
+chunks of 64 and 128 elements over a tensor of over a million) is
+finalized by the wide per-tensor reduction in several rounds.  Every entry point family is covered: the codec, the LAMB
 warmup (plain and with the norm carried), the freeze, the compression step
 with fp32 and with packed momentum under both rho rules, the 1-bit Adam mode,
 the sparse stage, and one GPU's share equal to the fused step.  Tables are
@@ -123,10 +123,11 @@ def test_lamb_trajectory_small_chunks(C, W):
 
 @pytest.mark.parametrize("C", [64, 128])
 def test_many_segments_small_chunks(C):
-    """A tensor of more than 16,384 (chunk, tensor) segments takes the wide
-    per-tensor finalize (1024 threads, 16 loads in flight each) in the
-    warmup and the compression stage: two carried warmup steps, the freeze,
-    a compression step under each rho rule, against the oracle."""
+    """A tensor of more than 16,384 (chunk, tensor) segments: the wide
+    per-tensor finalize (1024 threads, 16 loads in flight each) takes it in
+    two rounds, in the warmup and the compression stage: two carried warmup
+    steps, the freeze, a compression step under each rho rule, against the
+    oracle."""
     big = 16_384 * C + 3 * C + 5
     wl = Workload("many_segments", [5, big, 3 * C, 1_000_001], W=2, chunk=C, init="fresh",
                   grad_std=0.02)
