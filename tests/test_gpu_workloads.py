@@ -149,6 +149,46 @@ def test_mixed_warmup_whole_buffer():
     whole_buffer_parity(d, wl, run_host, stage="warmup")
 
 
+@pytest.mark.timeout(900)
+def test_mixed_switch_whole_buffer():
+    """The Mixed configuration through the switch, over the WHOLE buffer: its
+    20 LAMB warmup steps (the parameters' squared norm carried from step to
+    step on the GPU), the freeze, then two compression steps with the
+    adaptive layerwise rescale, against the oracle on tensor-aligned windows
+    covering the buffer: every chunk's signs, scales and errors of the eight
+    workers and of the server, m and v_fresh bit for bit, and the
+    parameters, the warmup coefficients' averages, f_prev and c of every
+    tensor within the bar ("1-bit LAMB" page, Section 4 summary: the
+    warmup stage preconditions the compression stage)."""
+    wl = WORKLOADS["mixed"]
+    n_comp = 2
+    d = DevRun(wl, carry_norm=True)
+    step = 0
+    for _ in range(wl.warmup_steps):
+        d.warmup_step(step)
+        step += 1
+    d.freeze(wl.warmup_steps)
+    for _ in range(n_comp):
+        d.compressed_step(step)
+        step += 1
+    torch.cuda.synchronize()
+    assert int(d.status.item()) == 0
+
+    def run_host(h):
+        s = 0
+        for _ in range(wl.warmup_steps):
+            h.warmup_step(s)
+            s += 1
+        h.freeze(wl.warmup_steps)
+        for _ in range(n_comp):
+            h.compressed_step(s)
+            s += 1
+
+    # 22 steps of eight workers' gradients per window: the host's input
+    # generation dominates, so eight windows at a time (about 27 GB)
+    whole_buffer_parity(d, wl, run_host, threads=8)
+
+
 def test_mixed_warmup_to_compression():
     """BERT-Large table with per-tensor gradient scales: 20 LAMB warmup steps
     (the parameters' squared norm carried from step to step), freeze, 20
