@@ -113,18 +113,25 @@ def whole_buffer_parity(d, wl, run_host, stage="compression", chunks=8192, threa
 
 @pytest.mark.timeout(900)
 def test_bert_large_whole_buffer():
-    """BERT-Large table, W = 8, one compression step, compared against the
-    oracle over the WHOLE buffer: every chunk's signs, scales and errors of
-    all eight workers and of the server, m, v_fresh, and the parameters and
-    per-tensor coefficients of every tensor.  Under error feedback a wrong
-    sign anywhere is carried into every later step ("1-bit LAMB" page,
-    Related work), so no chunk is left to sampling."""
+    """BERT-Large table, W = 8, two compression steps (the second one
+    compensating the first one's errors), compared against the oracle over
+    the WHOLE buffer: every chunk's signs, scales and errors of all eight
+    workers and of the server, m, v_fresh, and the parameters and per-tensor
+    coefficients of every tensor.  Under error feedback a wrong sign anywhere
+    is carried into every later step ("1-bit LAMB" page, Related work), so
+    no chunk is left to sampling."""
     wl = WORKLOADS["bert_large"]
     d = DevRun(wl)
-    d.compressed_step(0)
+    for step in range(2):
+        d.compressed_step(step)
     torch.cuda.synchronize()
     assert int(d.status.item()) == 0
-    whole_buffer_parity(d, wl, lambda h: h.compressed_step(0))
+
+    def run_host(h):
+        for step in range(2):
+            h.compressed_step(step)
+
+    whole_buffer_parity(d, wl, run_host, threads=8)
 
 
 @pytest.mark.timeout(900)
