@@ -139,7 +139,7 @@ _F32, _WORDS, _ANY = "f32", "words", "any"
 
 
 def _chunk_ok(chunk):
-    return isinstance(chunk, int) and 64 <= chunk <= 16384 and chunk & (chunk - 1) == 0
+    return isinstance(chunk, int) and 64 <= chunk <= (1 << 24) and chunk & (chunk - 1) == 0
 
 
 def _W_ok(W):

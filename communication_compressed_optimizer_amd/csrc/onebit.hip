@@ -12,11 +12,13 @@
 #include <mutex>
 #include <new>
 #include <string>
+#include <type_traits>
 #include <vector>
 
 #include "onebit.h"
 #include "onebit_host.hpp"
 #include "onebit_kernels.hpp"
+#include "onebit_big.hpp"
 
 using namespace onebit;
 
@@ -520,35 +522,191 @@ struct LaunchSparseUpdate {
   }
 };
 
+// The per-tensor rho, soft thresholds and c of a compression step.
+void rescale_finalize(const onebit_layer_table* t, const float* c_avg, float* f_prev,
+                      float* c_out, const Coef& cf, bool rho_norm, const Ws& ws, int32_t* status,
+                      hipStream_t st) {
+  const bool wide = t->max_tseg > kFinalizeWideSegs;
+  if (rho_norm && wide)
+    hipLaunchKernelGGL((k_rescale_finalize<1024, true, kFinalizeWideU>), dim3((unsigned)t->L),
+                       dim3(1024), 0, st, t->dev, (const float*)ws.seg_max,
+                       (const double*)ws.seg_x, (const double*)ws.seg_u, c_avg, f_prev,
+                       ws.c_layer, c_out, cf, status);
+  else if (rho_norm)
+    hipLaunchKernelGGL((k_rescale_finalize<256, true>), dim3((unsigned)t->L), dim3(256), 0, st,
+                       t->dev, (const float*)ws.seg_max, (const double*)ws.seg_x,
+                       (const double*)ws.seg_u, c_avg, f_prev, ws.c_layer, c_out, cf, status);
+  else if (wide)
+    hipLaunchKernelGGL((k_rescale_finalize<1024, false, kFinalizeWideU>), dim3((unsigned)t->L),
+                       dim3(1024), 0, st, t->dev, (const float*)ws.seg_max,
+                       (const double*)ws.seg_x, (const double*)ws.seg_u, c_avg, f_prev,
+                       ws.c_layer, c_out, cf, status);
+  else
+    hipLaunchKernelGGL((k_rescale_finalize<256>), dim3((unsigned)t->L), dim3(256), 0, st,
+                       t->dev, (const float*)ws.seg_max, (const double*)ws.seg_x,
+                       (const double*)ws.seg_u, c_avg, f_prev, ws.c_layer, c_out, cf, status);
+}
+
 template <int C>
 struct LaunchPassB {
   static void run(const onebit_layer_table* t, const uint32_t* bits_s, const float* scales_s,
                   float* x, float* m, const float* v_frozen, const float* c_avg, float* f_prev,
                   float* c_out, const Coef& cf, bool rho_norm, const Ws& ws, int32_t* status,
                   hipStream_t st) {
-    const bool wide = t->max_tseg > kFinalizeWideSegs;
-    if (rho_norm && wide)
-      hipLaunchKernelGGL((k_rescale_finalize<1024, true, kFinalizeWideU>), dim3((unsigned)t->L),
-                         dim3(1024), 0, st, t->dev, (const float*)ws.seg_max,
-                         (const double*)ws.seg_x, (const double*)ws.seg_u, c_avg, f_prev,
-                         ws.c_layer, c_out, cf, status);
-    else if (rho_norm)
-      hipLaunchKernelGGL((k_rescale_finalize<256, true>), dim3((unsigned)t->L), dim3(256), 0, st,
-                         t->dev, (const float*)ws.seg_max, (const double*)ws.seg_x,
-                         (const double*)ws.seg_u, c_avg, f_prev, ws.c_layer, c_out, cf, status);
-    else if (wide)
-      hipLaunchKernelGGL((k_rescale_finalize<1024, false, kFinalizeWideU>), dim3((unsigned)t->L),
-                         dim3(1024), 0, st, t->dev, (const float*)ws.seg_max,
-                         (const double*)ws.seg_x, (const double*)ws.seg_u, c_avg, f_prev,
-                         ws.c_layer, c_out, cf, status);
-    else
-      hipLaunchKernelGGL((k_rescale_finalize<256>), dim3((unsigned)t->L), dim3(256), 0, st,
-                         t->dev, (const float*)ws.seg_max, (const double*)ws.seg_x,
-                         (const double*)ws.seg_u, c_avg, f_prev, ws.c_layer, c_out, cf, status);
+    rescale_finalize(t, c_avg, f_prev, c_out, cf, rho_norm, ws, status, st);
     launch_chunks_capped<C>(kPassB_lds<C>, t->N, st, k_compressed_pass_b<C, kPassB_NT>, t->dev,
                             bits_s, scales_s, v_frozen, x, m, (const float*)ws.c_layer, cf);
   }
 };
+
+// ---------------------------------------------------------------------------
+// Chunks longer than 16384 elements (onebit_big.hpp): one workgroup of 256
+// threads per chunk walks it in 4096-element blocks.  The 1-bit LAMB and
+// 1-bit Adam compression steps run there as their per-GPU parts in order:
+// every worker's compression, the server's average of the workers' packed
+// chunks, then the statistics and the update.  Those parts give the fused
+// step's results bit for bit; they need the workers' sign words and scales
+// kept, and (1-bit LAMB) an fp32 momentum, since the server's new output
+// would overwrite a packed momentum before the statistics read it.
+// ---------------------------------------------------------------------------
+constexpr int32_t kMaxFusedChunk = 16384;
+bool big_chunk(int32_t chunk) { return chunk > kMaxFusedChunk; }
+int big_lr(int32_t chunk) {
+  int lr = 0;
+  while ((kBlk << lr) < chunk) ++lr;
+  return lr;
+}
+static_assert(kBT <= onebit_host::chunk_threads(int64_t(kBlk) << kBigMinLog, 4),
+              "the host's chunk bound assumes 256 threads per long chunk");
+
+// The compression kernels' form by chunk length: chunks of 2^15 and 2^16
+// held in registers (8 or 16 blocks per thread group), longer ones walked
+// twice.  f is called with std::integral_constant<int, RES>.
+template <class F>
+void by_res(int lr, F&& f) {
+  if (lr == 3) f(std::integral_constant<int, 8>{});
+  else if (lr == 4) f(std::integral_constant<int, 16>{});
+  else f(std::integral_constant<int, 0>{});
+}
+
+// The launch over the n elements' chunks (nothing for n = 0).
+template <typename KF, typename... A>
+void big_launch(int64_t n, int32_t chunk, hipStream_t st, KF k, A... args) {
+  const int64_t K = onebit_host::chunks_of(n, chunk);
+  if (K > 0) hipLaunchKernelGGL(k, dim3((unsigned)K), dim3(kBT), 0, st, args...);
+}
+
+// A compression step over chunks longer than 16384 elements needs the
+// workers' sign words and scales (EUNSUPPORTED otherwise) and, with
+// need_m, the fp32 momentum.
+int check_big_step(const char* fn, int32_t chunk, int32_t W, uint32_t* const* bits_w,
+                   float* const* scales_w, const float* m, bool need_m) {
+  if (!big_chunk(chunk)) return ONEBIT_OK;
+  for (int w = 0; w < W; ++w)
+    if (!bits_w || !scales_w || !bits_w[w] || !scales_w[w])
+      return fail(ONEBIT_EUNSUPPORTED,
+                  "%s: chunks over %d elements need the workers' sign words and scales "
+                  "(bits_w, scales_w)", fn, kMaxFusedChunk);
+  if (need_m && !m)
+    return fail(ONEBIT_EUNSUPPORTED,
+                "%s: chunks over %d elements need the fp32 momentum (m = NULL is packed)", fn,
+                kMaxFusedChunk);
+  return ONEBIT_OK;
+}
+
+// The sparse stage keeps chunks of at most 16384 elements.
+int sparse_big(const char* fn, int32_t chunk) {
+  return fail(ONEBIT_EUNSUPPORTED, "%s: chunk %d: the sparse stage takes chunks of at most %d", fn,
+              chunk, kMaxFusedChunk);
+}
+
+void big_warmup(const onebit_layer_table* t, int W, const Workers& wk, float* x, float* m,
+                float* v, float* c_sum, float* c_out, double* x_sq, bool x_in, const Coef& cf,
+                const Ws& ws, int32_t* status, hipStream_t st) {
+  const int lr = big_lr(t->chunk);
+  if (x_in)
+    big_launch(t->N, t->chunk, st, k_big_warmup_pass1<kWarm_NT, true>, t->dev, lr, W, wk,
+               (const float*)x, m, v, ws.seg_x, ws.seg_u, cf);
+  else
+    big_launch(t->N, t->chunk, st, k_big_warmup_pass1<kWarm_NT, false>, t->dev, lr, W, wk,
+               (const float*)x, m, v, ws.seg_x, ws.seg_u, cf);
+  if (t->max_tseg > kFinalizeWideSegs)
+    hipLaunchKernelGGL((k_warmup_finalize<1024, kFinalizeWideU>), dim3((unsigned)t->L), dim3(1024),
+                       0, st, t->dev, (const double*)(x_in ? x_sq : ws.seg_x),
+                       (const double*)ws.seg_u, c_sum, ws.c_layer, c_out, cf, status);
+  else
+    hipLaunchKernelGGL(k_warmup_finalize<256>, dim3((unsigned)t->L), dim3(256), 0, st, t->dev,
+                       (const double*)(x_in ? x_sq : ws.seg_x), (const double*)ws.seg_u, c_sum,
+                       ws.c_layer, c_out, cf, status);
+  if (x_sq)
+    big_launch(t->N, t->chunk, st, k_big_warmup_pass2<kWarm_NT, true>, t->dev, lr,
+               (const float*)m, (const float*)v, x, (const float*)ws.c_layer, x_sq, cf);
+  else
+    big_launch(t->N, t->chunk, st, k_big_warmup_pass2<kWarm_NT, false>, t->dev, lr,
+               (const float*)m, (const float*)v, x, (const float*)ws.c_layer, x_sq, cf);
+}
+
+// Every worker's compression, then the server's average of their packed
+// chunks: the compressed allreduce of both steps (m NULL: packed momentum,
+// read from bits_s / scales_s before the server rewrites them).
+void big_allreduce(int64_t n, int32_t chunk, int W, const Workers& wk, float* err_s,
+                   const float* m, uint32_t* bits_s, float* scales_s, const Coef& cf,
+                   int32_t* status, hipStream_t st) {
+  const int lr = big_lr(chunk);
+  PackedIn pin{};
+  by_res(lr, [&](auto R) {
+    constexpr int RES = decltype(R)::value;
+    for (int w = 0; w < W; ++w) {
+      if (m)
+        big_launch(n, chunk, st, k_big_worker_compress<kShare_NT, false, RES>, n, lr, wk.g[w],
+                   wk.e[w], m, (const uint32_t*)nullptr, (const float*)nullptr, wk.bits[w],
+                   wk.scales[w], cf, status);
+      else
+        big_launch(n, chunk, st, k_big_worker_compress<kShare_NT, true, RES>, n, lr, wk.g[w],
+                   wk.e[w], m, (const uint32_t*)bits_s, (const float*)scales_s, wk.bits[w],
+                   wk.scales[w], cf, status);
+      pin.bits[w] = wk.bits[w];
+      pin.scales[w] = wk.scales[w];
+    }
+    big_launch(n, chunk, st, k_big_average_packed<kCodec_NT, RES>, n, lr, W, pin, err_s, bits_s,
+               scales_s, status);
+  });
+}
+
+void big_stats(const onebit_layer_table* t, const uint32_t* bits_s, const float* scales_s,
+               const float* m, const uint32_t* bits_m, const float* scales_m,
+               const float* v_frozen, float* v_fresh, const Coef& cf, bool rn, const Ws& ws,
+               hipStream_t st) {
+  const int lr = big_lr(t->chunk);
+#define BIG_STATS(RN, PM)                                                                        \
+  big_launch(t->N, t->chunk, st, k_big_rescale_stats<kShare_NT, RN, PM>, t->dev, lr, bits_s,     \
+             scales_s, m, bits_m, scales_m, v_frozen, v_fresh, ws.seg_max, ws.seg_x, ws.seg_u, cf)
+  if (rn && !m) BIG_STATS(true, true);
+  else if (rn) BIG_STATS(true, false);
+  else if (!m) BIG_STATS(false, true);
+  else BIG_STATS(false, false);
+#undef BIG_STATS
+}
+
+// 1-bit LAMB pass A: the allreduce, then the fresh variance and the
+// rescale statistics
+void big_pass_a(const onebit_layer_table* t, int W, const Workers& wk, float* err_s,
+                const float* m, const float* v_frozen, float* v_fresh, uint32_t* bits_s,
+                float* scales_s, const Coef& cf, bool rn, const Ws& ws, int32_t* status,
+                hipStream_t st) {
+  big_allreduce(t->N, t->chunk, W, wk, err_s, m, bits_s, scales_s, cf, status, st);
+  big_stats(t, bits_s, scales_s, m, nullptr, nullptr, v_frozen, v_fresh, cf, rn, ws, st);
+}
+
+// 1-bit LAMB pass B: the per-tensor coefficients, then the update
+void big_pass_b(const onebit_layer_table* t, const uint32_t* bits_s, const float* scales_s,
+                float* x, float* m, const float* v_frozen, const float* c_avg, float* f_prev,
+                float* c_out, const Coef& cf, bool rn, const Ws& ws, int32_t* status,
+                hipStream_t st) {
+  rescale_finalize(t, c_avg, f_prev, c_out, cf, rn, ws, status, st);
+  big_launch(t->N, t->chunk, st, k_big_pass_b<kPassB_NT>, t->dev, big_lr(t->chunk), bits_s,
+             scales_s, v_frozen, x, m, (const float*)ws.c_layer, cf);
+}
 
 // The workers' arrays of a compression step; fills wk.
 int check_workers(const char* fn, int32_t W, const float* const* grads, float* const* err_w,
@@ -657,8 +815,12 @@ int warmup_step(const char* fn, const onebit_layer_table* table, int32_t W,
   // With weight decay the direction needs x itself, so pass 1 reads it and
   // forms its norm as well (the carried value would be the same bits).
   const bool x_in = x_sq && x_sq_valid == 1 && hp->weight_decay == 0.0f;
-  by_chunk<LaunchWarmup>(table->chunk, table, (int)W, wk, x, m, v, c_sum, c_out, x_sq, x_in,
-                         make_coef(*hp), ws_view(table, ws), status, (hipStream_t)stream);
+  if (big_chunk(table->chunk))
+    big_warmup(table, (int)W, wk, x, m, v, c_sum, c_out, x_sq, x_in, make_coef(*hp),
+               ws_view(table, ws), status, (hipStream_t)stream);
+  else
+    by_chunk<LaunchWarmup>(table->chunk, table, (int)W, wk, x, m, v, c_sum, c_out, x_sq, x_in,
+                           make_coef(*hp), ws_view(table, ws), status, (hipStream_t)stream);
   return launch_status(fn);
 }
 
@@ -678,6 +840,7 @@ int compressed_step(const char* fn, const onebit_layer_table* table, int32_t W,
   if (int rc = check_phase2(fn, table, bits_s, scales_s, x, m, v_frozen, c_avg, f_prev, c_out, hp,
                             ws))
     return rc;
+  if (int rc = check_big_step(fn, table->chunk, W, bits_w, scales_w, m, true)) return rc;
   const Bytes b(table->N, table->chunk);
   const int64_t tl = 4 * (int64_t)table->L;
   Spans sp;
@@ -702,10 +865,17 @@ int compressed_step(const char* fn, const onebit_layer_table* table, int32_t W,
   const bool rn = hp->rho_mode == ONEBIT_RHO_NORM_RATIO;
   const Ws wsv = ws_view(table, ws);
   hipStream_t st = (hipStream_t)stream;
-  by_chunk<LaunchPassA>(table->chunk, table, (int)W, wk, err_s, m, v_frozen, v_fresh, bits_s,
-                        scales_s, cf, rn, wsv, status, st);
-  by_chunk<LaunchPassB>(table->chunk, table, bits_s, scales_s, x, m, v_frozen, c_avg, f_prev, c_out,
-                        cf, rn, wsv, status, st);
+  if (big_chunk(table->chunk)) {
+    big_pass_a(table, (int)W, wk, err_s, m, v_frozen, v_fresh, bits_s, scales_s, cf, rn, wsv,
+               status, st);
+    big_pass_b(table, bits_s, scales_s, x, m, v_frozen, c_avg, f_prev, c_out, cf, rn, wsv, status,
+               st);
+  } else {
+    by_chunk<LaunchPassA>(table->chunk, table, (int)W, wk, err_s, m, v_frozen, v_fresh, bits_s,
+                          scales_s, cf, rn, wsv, status, st);
+    by_chunk<LaunchPassB>(table->chunk, table, bits_s, scales_s, x, m, v_frozen, c_avg, f_prev,
+                          c_out, cf, rn, wsv, status, st);
+  }
   return launch_status(fn);
 }
 
@@ -881,7 +1051,13 @@ int onebit_compress_ef(int64_t n, int32_t chunk, const float* in, float* err, ui
   sp.add(scales, b.scales, true, "scales");
   sp.add(status, 4, true, "status");
   if (int rc = sp.check(__func__)) return rc;
-  by_chunk<LaunchCompress>(chunk, n, in, err, bits, scales, status, (hipStream_t)stream);
+  if (big_chunk(chunk))
+    by_res(big_lr(chunk), [&](auto R) {
+      big_launch(n, chunk, (hipStream_t)stream, k_big_compress_ef<kCodec_NT, decltype(R)::value>,
+                 n, big_lr(chunk), in, err, bits, scales, status);
+    });
+  else
+    by_chunk<LaunchCompress>(chunk, n, in, err, bits, scales, status, (hipStream_t)stream);
   return launch_status(__func__);
 }
 
@@ -913,8 +1089,14 @@ int onebit_average_packed(int64_t n, int32_t chunk, int32_t W, const uint32_t* c
   sp.add(scales_out, b.scales, true, "scales_out");
   sp.add(status, 4, true, "status");
   if (int rc = sp.check(__func__)) return rc;
-  by_chunk<LaunchAverage>(chunk, n, (int)W, pin, err_s, bits_out, scales_out, status,
-                          (hipStream_t)stream);
+  if (big_chunk(chunk))
+    by_res(big_lr(chunk), [&](auto R) {
+      big_launch(n, chunk, (hipStream_t)stream, k_big_average_packed<kCodec_NT, decltype(R)::value>,
+                 n, big_lr(chunk), (int)W, pin, err_s, bits_out, scales_out, status);
+    });
+  else
+    by_chunk<LaunchAverage>(chunk, n, (int)W, pin, err_s, bits_out, scales_out, status,
+                            (hipStream_t)stream);
   return launch_status(__func__);
 }
 
@@ -932,7 +1114,11 @@ int onebit_decompress(int64_t n, int32_t chunk, const uint32_t* bits, const floa
   sp.add(scales, b.scales, false, "scales");
   sp.add(out, b.elems, true, "out");
   if (int rc = sp.check(__func__)) return rc;
-  by_chunk<LaunchDecompress>(chunk, n, bits, scales, out, (hipStream_t)stream);
+  if (big_chunk(chunk))
+    big_launch(n, chunk, (hipStream_t)stream, k_big_decompress<kCodec_NT>, n, big_lr(chunk), bits,
+               scales, out);
+  else
+    by_chunk<LaunchDecompress>(chunk, n, bits, scales, out, (hipStream_t)stream);
   return launch_status(__func__);
 }
 
@@ -988,7 +1174,11 @@ int onebit_lamb_freeze(const onebit_layer_table* table, int32_t W, const float* 
   sp.add(f_prev, tl, true, "f_prev");
   if (int rc = sp.check(__func__)) return rc;
   hipStream_t st = (hipStream_t)stream;
-  by_chunk<LaunchFreeze>(table->chunk, table, (int)W, v, v_fresh, wk, err_s, st);
+  if (big_chunk(table->chunk))   // element-wise: any chunk layout gives the same result
+    launch_chunks<kBlk>(table->N, st, k_freeze_elems<kBlk>, table->N, (int)W, v, v_fresh, wk,
+                        err_s);
+  else
+    by_chunk<LaunchFreeze>(table->chunk, table, (int)W, v, v_fresh, wk, err_s, st);
   hipLaunchKernelGGL(k_freeze_tensors, dim3((unsigned)((table->L + 255) / 256)), dim3(256), 0, st,
                      (int)table->L, c_sum, den, c_avg, f_prev);
   return launch_status(__func__);
@@ -1020,9 +1210,15 @@ int onebit_lamb_compress_average(const onebit_layer_table* table, int32_t W,
   sp.add(ws, (int64_t)ws_bytes(table), true, "ws");
   sp.add(status, 4, true, "status");
   if (int rc = sp.check(__func__)) return rc;
-  by_chunk<LaunchPassA>(table->chunk, table, (int)W, wk, err_s, m, v_frozen, v_fresh, bits_s,
-                        scales_s, make_coef(*hp), hp->rho_mode == ONEBIT_RHO_NORM_RATIO,
-                        ws_view(table, ws), status, (hipStream_t)stream);
+  if (int rc = check_big_step(__func__, table->chunk, W, bits_w, scales_w, m, true)) return rc;
+  if (big_chunk(table->chunk))
+    big_pass_a(table, (int)W, wk, err_s, m, v_frozen, v_fresh, bits_s, scales_s, make_coef(*hp),
+               hp->rho_mode == ONEBIT_RHO_NORM_RATIO, ws_view(table, ws), status,
+               (hipStream_t)stream);
+  else
+    by_chunk<LaunchPassA>(table->chunk, table, (int)W, wk, err_s, m, v_frozen, v_fresh, bits_s,
+                          scales_s, make_coef(*hp), hp->rho_mode == ONEBIT_RHO_NORM_RATIO,
+                          ws_view(table, ws), status, (hipStream_t)stream);
   return launch_status(__func__);
 }
 
@@ -1048,9 +1244,14 @@ int onebit_lamb_rescale_update(const onebit_layer_table* table, const uint32_t* 
   sp.add(ws, (int64_t)ws_bytes(table), true, "ws");
   sp.add(status, 4, true, "status");
   if (int rc = sp.check(__func__)) return rc;
-  by_chunk<LaunchPassB>(table->chunk, table, bits_s, scales_s, x, m, v_frozen, c_avg, f_prev, c_out,
-                        make_coef(*hp), hp->rho_mode == ONEBIT_RHO_NORM_RATIO, ws_view(table, ws),
-                        status, (hipStream_t)stream);
+  if (big_chunk(table->chunk))
+    big_pass_b(table, bits_s, scales_s, x, m, v_frozen, c_avg, f_prev, c_out, make_coef(*hp),
+               hp->rho_mode == ONEBIT_RHO_NORM_RATIO, ws_view(table, ws), status,
+               (hipStream_t)stream);
+  else
+    by_chunk<LaunchPassB>(table->chunk, table, bits_s, scales_s, x, m, v_frozen, c_avg, f_prev,
+                          c_out, make_coef(*hp), hp->rho_mode == ONEBIT_RHO_NORM_RATIO,
+                          ws_view(table, ws), status, (hipStream_t)stream);
   return launch_status(__func__);
 }
 
@@ -1118,8 +1319,21 @@ int onebit_worker_compress(int64_t n, int32_t chunk, const float* grad, float* e
   sp.add(scales_w, b.scales, true, "scales_w");
   sp.add(status, 4, true, "status");
   if (int rc = sp.check(__func__)) return rc;
-  by_chunk<LaunchWorker>(chunk, n, grad, err_w, m, bits_m, scales_m, bits_w, scales_w,
-                         make_coef(*hp), status, (hipStream_t)stream);
+  if (big_chunk(chunk))
+    by_res(big_lr(chunk), [&](auto R) {
+      constexpr int RES = decltype(R)::value;
+      if (m)
+        big_launch(n, chunk, (hipStream_t)stream, k_big_worker_compress<kShare_NT, false, RES>, n,
+                   big_lr(chunk), grad, err_w, m, bits_m, scales_m, bits_w, scales_w,
+                   make_coef(*hp), status);
+      else
+        big_launch(n, chunk, (hipStream_t)stream, k_big_worker_compress<kShare_NT, true, RES>, n,
+                   big_lr(chunk), grad, err_w, m, bits_m, scales_m, bits_w, scales_w,
+                   make_coef(*hp), status);
+    });
+  else
+    by_chunk<LaunchWorker>(chunk, n, grad, err_w, m, bits_m, scales_m, bits_w, scales_w,
+                           make_coef(*hp), status, (hipStream_t)stream);
   return launch_status(__func__);
 }
 
@@ -1153,9 +1367,13 @@ int onebit_lamb_rescale_stats(const onebit_layer_table* table, const uint32_t* b
   sp.add(v_fresh, b.elems, true, "v_fresh");
   sp.add(ws, (int64_t)ws_bytes(table), true, "ws");
   if (int rc = sp.check(__func__)) return rc;
-  by_chunk<LaunchStats>(table->chunk, table, bits_s, scales_s, m, bits_m, scales_m, v_frozen,
-                        v_fresh, make_coef(*hp), hp->rho_mode == ONEBIT_RHO_NORM_RATIO,
-                        ws_view(table, ws), (hipStream_t)stream);
+  if (big_chunk(table->chunk))
+    big_stats(table, bits_s, scales_s, m, bits_m, scales_m, v_frozen, v_fresh, make_coef(*hp),
+              hp->rho_mode == ONEBIT_RHO_NORM_RATIO, ws_view(table, ws), (hipStream_t)stream);
+  else
+    by_chunk<LaunchStats>(table->chunk, table, bits_s, scales_s, m, bits_m, scales_m, v_frozen,
+                          v_fresh, make_coef(*hp), hp->rho_mode == ONEBIT_RHO_NORM_RATIO,
+                          ws_view(table, ws), (hipStream_t)stream);
   return launch_status(__func__);
 }
 
@@ -1180,8 +1398,12 @@ int onebit_adam_update(int64_t n, int32_t chunk, const uint32_t* bits_s, const f
   sp.add(m, b.elems, true, "m");
   sp.add(v_frozen, b.elems, false, "v_frozen");
   if (int rc = sp.check(__func__)) return rc;
-  by_chunk<LaunchAdamUpdate>(chunk, n, bits_s, scales_s, v_frozen, x, m, make_coef(*hp),
-                             (hipStream_t)stream);
+  if (big_chunk(chunk))
+    big_launch(n, chunk, (hipStream_t)stream, k_big_adam_update<kShare_NT>, n, big_lr(chunk),
+               bits_s, scales_s, v_frozen, x, m, make_coef(*hp));
+  else
+    by_chunk<LaunchAdamUpdate>(chunk, n, bits_s, scales_s, v_frozen, x, m, make_coef(*hp),
+                               (hipStream_t)stream);
   return launch_status(__func__);
 }
 
@@ -1190,6 +1412,7 @@ int onebit_sparse_worker(int64_t n, int32_t chunk, int32_t nsel, const int32_t* 
                          const onebit_hparams* hp, void* stream) {
   if (n < 0) return fail(ONEBIT_EINVAL, "%s: n < 0", __func__);
   if (!chunk_supported(chunk)) return fail(ONEBIT_EUNSUPPORTED, "%s: chunk %d", __func__, chunk);
+  if (big_chunk(chunk)) return sparse_big(__func__, chunk);
   if (int rc = check_hparams(hp, __func__, false)) return rc;
   if (nsel < 1 || nsel > chunk / 64)
     return fail(ONEBIT_EINVAL, "%s: nsel = %d outside [1, chunk/64 = %d]", __func__, nsel,
@@ -1245,6 +1468,7 @@ int onebit_sparse_update(const onebit_layer_table* table, int32_t nsel, const in
                          int32_t* status, void* stream) {
   CHECK_OPT_WORDS(status, "status");
   if (int rc = check_table(table, __func__)) return rc;
+  if (big_chunk(table->chunk)) return sparse_big(__func__, table->chunk);
   if (int rc = check_hparams(hp, __func__, false)) return rc;
   if (nsel < 1 || nsel > table->chunk / 64)
     return fail(ONEBIT_EINVAL, "%s: nsel = %d outside [1, chunk/64 = %d]", __func__, nsel,
@@ -1335,8 +1559,16 @@ int onebit_adam_compressed_step(int64_t n, int32_t chunk, int32_t W, const float
   sp.add(scales_s, b.scales, true, "scales_s");
   sp.add(status, 4, true, "status");
   if (int rc = sp.check(__func__)) return rc;
-  by_chunk<LaunchAdam>(chunk, n, (int)W, wk, err_s, m, x, v_frozen, bits_s, scales_s,
-                       make_coef(*hp), status, (hipStream_t)stream);
+  if (int rc = check_big_step(__func__, chunk, W, bits_w, scales_w, m, false)) return rc;
+  if (big_chunk(chunk)) {
+    big_allreduce(n, chunk, (int)W, wk, err_s, m, bits_s, scales_s, make_coef(*hp), status,
+                  (hipStream_t)stream);
+    big_launch(n, chunk, (hipStream_t)stream, k_big_adam_update<kAdam_NT>, n, big_lr(chunk),
+               (const uint32_t*)bits_s, (const float*)scales_s, v_frozen, x, m, make_coef(*hp));
+  } else {
+    by_chunk<LaunchAdam>(chunk, n, (int)W, wk, err_s, m, x, v_frozen, bits_s, scales_s,
+                         make_coef(*hp), status, (hipStream_t)stream);
+  }
   return launch_status(__func__);
 }
 
@@ -1348,6 +1580,7 @@ int onebit_sparse_compressed_step(const onebit_layer_table* table, int32_t W, in
                                   void* stream) {
   CHECK_OPT_WORDS(status, "status");
   if (int rc = check_table(table, __func__)) return rc;
+  if (big_chunk(table->chunk)) return sparse_big(__func__, table->chunk);
   if (int rc = check_W(W, __func__)) return rc;
   if (int rc = check_hparams(hp, __func__, false)) return rc;
   if (nsel < 1 || nsel > table->chunk / 64)

@@ -51,7 +51,8 @@ inline int ok() {
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
-inline bool chunk_supported(int32_t c) { return c >= 64 && c <= 16384 && (c & (c - 1)) == 0; }
+// Chunks of 64 .. 2^24 elements, powers of two.
+inline bool chunk_supported(int32_t c) { return c >= 64 && c <= (1 << 24) && (c & (c - 1)) == 0; }
 
 inline size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
 
@@ -63,9 +64,10 @@ constexpr int64_t kMaxChunks = INT32_MAX / 2;
 
 // Threads per chunk of a launch that lays `slots` float4 slots per thread,
 // one workgroup per chunk: one 64-wide wave below 1024 elements (the padded
-// geometry), else chunk / (4 * slots).
+// geometry), chunk / (4 * slots) up to 16384, and 256 above (a workgroup
+// that walks the chunk in 4096-element blocks).
 constexpr int64_t chunk_threads(int64_t chunk, int64_t slots) {
-  return chunk < 1024 ? 64 : chunk / (4 * slots);
+  return chunk < 1024 ? 64 : (chunk > 16384 ? 256 : chunk / (4 * slots));
 }
 
 // Float4 slots per thread of the narrowest layout a kernel on a layer table
@@ -242,7 +244,7 @@ struct HostTable {
 
 // Checks the sizes and returns N and K without building anything: EINVAL for
 // a NULL array, L < 1 or a tensor of fewer than 1 element; EUNSUPPORTED for a
-// chunk that is not a power of two in [64, 16384] or more than
+// chunk that is not a power of two in [64, 2^24] or more than
 // max_chunks(chunk, table_slots(chunk)) chunks in all.  The running sum is
 // bounded before each add, so it cannot overflow.
 inline int table_sizes(const int64_t* numels, int32_t L, int32_t chunk, int64_t* N, int64_t* K,
@@ -250,7 +252,7 @@ inline int table_sizes(const int64_t* numels, int32_t L, int32_t chunk, int64_t*
   if (!numels) return fail(ONEBIT_EINVAL, "%s: NULL argument", fn);
   if (L < 1) return fail(ONEBIT_EINVAL, "%s: L = %d < 1", fn, L);
   if (!chunk_supported(chunk))
-    return fail(ONEBIT_EUNSUPPORTED, "%s: chunk %d is not a power of two in [64, 16384]", fn,
+    return fail(ONEBIT_EUNSUPPORTED, "%s: chunk %d is not a power of two in [64, 2^24]", fn,
                 chunk);
   const int64_t max_n = max_chunks(chunk, table_slots(chunk)) * chunk;
   int64_t n = 0;

@@ -288,8 +288,10 @@ __device__ __forceinline__ float wave_tree_sum(float v) {
 }
 
 // lds: 2*T float4 (double-buffered between consecutive calls, so one
-// barrier per call suffices).  Returns the sum in every thread.
-template <int C, int SPT = kSlots<C>>
+// barrier per call suffices).  Returns the sum in every thread.  SQ =
+// false: z already holds the values to sum (the squares, or partial sums
+// of them), and the tree adds them as they are.
+template <int C, int SPT = kSlots<C>, bool SQ = true>
 __device__ __forceinline__ float chunk_sumsq(const SlotsN<SPT>& z, float4* __restrict__ lds, int& parity) {
   constexpr int T = Geo<C, SPT>::T;
   constexpr int NW = Geo<C, SPT>::NW;
@@ -298,7 +300,7 @@ __device__ __forceinline__ float chunk_sumsq(const SlotsN<SPT>& z, float4* __res
   for (int c = 0; c < 4; ++c) {
     float q[SPT];
 #pragma unroll
-    for (int k = 0; k < SPT; ++k) q[k] = z[k][c] * z[k][c];
+    for (int k = 0; k < SPT; ++k) q[k] = SQ ? z[k][c] * z[k][c] : z[k][c];
 #pragma unroll
     for (int h = SPT / 2; h >= 1; h /= 2)
 #pragma unroll

@@ -33,21 +33,24 @@ static int g_fail = 0;
     }                                                       \
   } while (0)
 
-static const int32_t kChunks[] = {64, 128, 256, 512, 1024, 2048, 4096, 8192, 16384};
+static const int32_t kChunks[] = {64,   128,   256,   512,     1024,    2048,
+                                   4096, 8192,  16384, 32768, 65536, 1 << 20, 1 << 24};
 static const int kNChunks = sizeof kChunks / sizeof kChunks[0];
 
 // Reference for the size bounds, written out per chunk size: the threads of
 // one chunk's workgroup with four float4 slots per thread (the entry points
 // that take n and chunk; one 64-wide wave up to 1024 elements), and the
-// widest a table kernel launches (the warmup passes' two slots at 4096).  A
-// launch of k chunks fits when k <= 2^30 - 1 and k * threads < 2^32.
+// widest a table kernel launches (the warmup passes' two slots at 4096);
+// chunks longer than 16384 take 256 threads that walk the chunk in blocks.
+// A launch of k chunks fits when k <= 2^30 - 1 and k * threads < 2^32.
 static int64_t ref_threads(int32_t chunk, bool table) {
   switch (chunk) {
     case 64: case 128: case 256: case 512: case 1024: return 64;
     case 2048: return 128;
     case 4096: return table ? 512 : 256;
     case 8192: return 512;
-    default: return 1024;
+    case 16384: return 1024;
+    default: return 256;
   }
 }
 static bool ref_fits(i128 k, int32_t chunk, bool table) {
@@ -137,11 +140,16 @@ static void fuzz_tables() {
   std::mt19937_64 r(1);
   for (int it = 0; it < 400; ++it) {
     const int32_t chunk = kChunks[it % kNChunks];
-    check_table(random_numels(r, chunk), chunk, it % 4 == 0);
+    check_table(random_numels(r, chunk), chunk, it % 4 == 0 && chunk <= 65536);
   }
   // edge shapes: one element, exactly one chunk, one chunk plus one, many
   // one-element tensors in one chunk, a tensor ending on every boundary
   for (int32_t chunk : kChunks) {
+    if (chunk > 65536) {
+      check_table({1}, chunk, true);
+      check_table({chunk, 1, chunk - 1, 3}, chunk, false);
+      continue;
+    }
     check_table({1}, chunk, true);
     check_table({chunk}, chunk, true);
     check_table({chunk + 1}, chunk, true);
@@ -190,7 +198,8 @@ static void fuzz_table_sizes() {
   }
   int64_t N, K;
   std::vector<int64_t> v = {100};
-  for (int32_t c : {0, -4096, 32, 1, 1000, 3000, 32768, 4097, 96, INT32_MIN, INT32_MAX})
+  for (int32_t c : {0, -4096, 32, 1, 1000, 3000, 1 << 25, 1 << 30, (1 << 24) + 64, 4097, 96,
+                    INT32_MIN, INT32_MAX})
     EXPECT(table_sizes(v.data(), 1, c, &N, &K, "f") == ONEBIT_EUNSUPPORTED, "chunk %d", c);
   // random sizes near the bound against a 128-bit sum
   std::mt19937_64 r(2);
@@ -241,13 +250,14 @@ static void fuzz_scalars() {
   std::mt19937_64 r(3);
   const int64_t edges[] = {0, 1, 4095, 4096, 4097, INT64_MAX, INT64_MAX - 1, INT64_MIN, -1,
                            kMaxChunks * 1024, kMaxChunks * 1024 + 1, kMaxChunks * 16384,
-                           kMaxChunks * 16384 + 1};
+                           kMaxChunks * 16384 + 1, kMaxChunks * (1LL << 24),
+                           kMaxChunks * (1LL << 24) + 1};
   for (int it = 0; it < 200000; ++it) {
     const int64_t chunk = kChunks[r() % kNChunks];
     int64_t n;
     if (it < (int)(sizeof edges / sizeof edges[0])) n = edges[it];
     else if (r() % 2) n = (int64_t)r();
-    else n = (int64_t)(r() % ((uint64_t)kMaxChunks * 16384 + 2));
+    else n = (int64_t)(r() % ((uint64_t)ref_max_n(chunk, false) + 2));
     const int rc = check_n(n, chunk, "f");
     const i128 k = n < 0 ? 0 : ((i128)n + chunk - 1) / chunk;
     const int expect =
@@ -273,16 +283,24 @@ static void fuzz_scalars() {
   EXPECT(check_n(ref_max_n(4096, true), 4096, "f", 2) == ONEBIT_OK &&
              check_n(ref_max_n(4096, true) + 1, 4096, "f", 2) == ONEBIT_EUNSUPPORTED,
          "check_n with two slots per thread");
-  EXPECT(ref_max_n(64, false) == 67108863LL * 64 && ref_max_n(4096, false) == 16777215LL * 4096,
+  EXPECT(ref_max_n(64, false) == 67108863LL * 64 && ref_max_n(4096, false) == 16777215LL * 4096 &&
+             ref_max_n(1 << 20, false) == 16777215LL << 20,
          "reference bounds");
   for (int W = -3; W <= 20; ++W)
     EXPECT((check_W(W, "f") == ONEBIT_OK) == (W >= 1 && W <= 16), "check_W(%d)", W);
   EXPECT(check_W(INT32_MIN, "f") == ONEBIT_EUNSUPPORTED && check_W(INT32_MAX, "f") == ONEBIT_EUNSUPPORTED,
          "check_W extremes");
-  for (int32_t c = -70000; c <= 70000; ++c)
+  // every power of two from 64 to 2^24, nothing else
+  for (int32_t c = -70000; c <= 140000; ++c)
     EXPECT(chunk_supported(c) == (c == 64 || c == 128 || c == 256 || c == 512 || c == 1024 ||
-                                  c == 2048 || c == 4096 || c == 8192 || c == 16384),
+                                  c == 2048 || c == 4096 || c == 8192 || c == 16384 ||
+                                  c == 32768 || c == 65536 || c == 131072),
            "chunk_supported(%d)", c);
+  for (int e = 17; e <= 30; ++e) {
+    EXPECT(chunk_supported(1 << e) == (e <= 24), "chunk_supported(2^%d)", e);
+    EXPECT(!chunk_supported((1 << e) + 64) && !chunk_supported((1 << e) - 64),
+           "chunk_supported(2^%d +- 64)", e);
+  }
   // error text is kept per thread and cleared by a success
   fail(ONEBIT_EINVAL, "msg %d", 7);
   EXPECT(last_error_slot() == "msg 7", "fail message");
