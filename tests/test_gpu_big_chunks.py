@@ -1,8 +1,8 @@
 """Chunks longer than 16384 elements (2^15 up to 2^24) on the GPU, against
 the oracle.
 
-Such a chunk is one workgroup of 256 threads that walks it in 4096-element
-blocks.  Its scale is the canonical stride-halving tree over the whole
+Such a chunk is one workgroup of 256 threads over its 4096-element blocks,
+held in registers at 2^15 and 2^16 and walked twice beyond.  Its scale is the canonical stride-halving tree over the whole
 chunk, formed as a pairwise tree over the blocks in bit-reversed order and
 then the tree of one block, so signs, scales and errors must equal the
 oracle's bit for bit, as for the shorter chunks; a block past the end of
@@ -13,7 +13,8 @@ for 1-bit LAMB, the fp32 momentum; the sparse stage keeps chunks of at most
 16384.  Covered: the codec (up to a chunk of 2^24), the LAMB warmup (plain
 and with the norm carried), the freeze, the compression step under both rho
 rules, the 1-bit Adam mode with fp32 and packed momentum, one GPU's share
-equal to the fused step (packed momentum included), and the refusals.
+equal to the fused step (packed momentum included), the allocation-free
+step, and the refusals.
 Tables are ragged: tensors shorter than a block, tensors straddling blocks
 and chunks, a last chunk that ends inside a block with whole blocks past it.
 """
@@ -225,3 +226,22 @@ def test_big_chunk_refusals():
     for bad in (1 << 25, 3 << 15, (1 << 24) + 64):
         with pytest.raises(ob.OnebitError):
             ob.LayerTable([100], bad)
+
+
+def test_noalloc_big_chunks():
+    """The allocation-free step at chunks of 2^15 and 2^20 equals the step
+    with a caller's workspace bit for bit, the second call on a smaller
+    table; packed momentum is refused there as in the fused step."""
+    from tests.test_zz_no_alloc import _noalloc_step, _same
+    for C, numels, W in ((1 << 15, _table(1 << 15), 4), (1 << 20, [5, 3 << 20, 7], 2)):
+        wl = Workload("big_noalloc", numels, W=W, chunk=C, init="frozen")
+        a, b = DevRun(wl), DevRun(wl)
+        for step in range(2):
+            a.compressed_step(step)
+            _noalloc_step(b, step)
+        torch.cuda.synchronize()
+        _same(a, b)
+        assert int(b.status.item()) == 0
+        with pytest.raises(ob.OnebitError) as ei:
+            _noalloc_step(b, 2, packed=True)
+        assert ei.value.code == ob.ONEBIT_EUNSUPPORTED
