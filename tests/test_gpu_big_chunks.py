@@ -245,3 +245,57 @@ def test_noalloc_big_chunks():
         with pytest.raises(ob.OnebitError) as ei:
             _noalloc_step(b, 2, packed=True)
         assert ei.value.code == ob.ONEBIT_EUNSUPPORTED
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_table_big_chunks(seed):
+    """Seeded random tables at chunks of 2^15 to 2^18 (held in registers,
+    then walked twice at lr = 5 and 6), random W and variant readings: two
+    warmup steps and three compression steps of 1-bit LAMB, or 1-bit Adam
+    with packed momentum, against the oracle."""
+    r = np.random.default_rng(5000 + seed)
+    chunk = int(r.choice([1 << 15, 1 << 16, 1 << 17, 1 << 18]))
+    W = int(r.integers(1, 9))
+    L = int(r.integers(1, 12))
+    numels = []
+    for _ in range(L):
+        kind = r.random()
+        if kind < 0.15:
+            numels.append(int(chunk * r.integers(1, 3)))
+        elif kind < 0.3:
+            numels.append(int(r.integers(1, 8)))
+        else:
+            numels.append(int(np.exp(r.uniform(0, np.log(2 * chunk)))) + 1)
+    wl = Workload("random_big", numels, W=W, chunk=chunk, init="fresh", grad_std=0.02,
+                  layer_scaled=bool(r.random() < 0.5), seed=seed)
+    d, h = DevRun(wl, carry_norm=seed % 3 == 0), HostRun(wl)
+    if seed % 4 != 3:
+        variant = dict(rho_mode=int(r.integers(0, 2)), c_avg_decay=float(r.choice([0.0, 0.8])),
+                       weight_decay=float(r.choice([0.0, 0.01])))
+        for run in (d, h):
+            for k, v in variant.items():
+                setattr(run.hp, k, v)
+        bias = bool(r.random() < 0.5)
+        for step in range(2):
+            for run in (d, h):
+                run.hp.bias_step = step + 1 if bias else 0
+                run.warmup_step(step)
+            assert_parity(compare_state(d, h, stage="warmup"), f"seed {seed} warmup {step}")
+        for run in (d, h):
+            run.hp.bias_step = 0
+            run.freeze(2)
+        for step in range(2, 5):
+            d.compressed_step(step)
+            h.compressed_step(step)
+            assert_parity(compare_state(d, h), f"seed {seed} compression {step}")
+    else:
+        for step in range(2):
+            d.adam_warmup_step(step)
+            h.adam_warmup_step(step)
+        for step in range(2, 5):
+            d.adam_compressed_step(step, packed=step > 2)
+            h.adam_compressed_step(step)
+            if step > 2:
+                d.m.copy_(d.momentum_from_packed())
+            assert_parity(compare_adam(d, h), f"seed {seed} adam {step}")
+    assert int(d.status.item()) == 0
