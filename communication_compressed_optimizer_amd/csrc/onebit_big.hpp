@@ -343,18 +343,32 @@ k_big_average_packed(int64_t n, int lr, int W, PackedIn pin, float* __restrict__
   int parity = 0;
   const BigAt ch(blockIdx.x, n, lr);
   const float fW = (float)W;
+  // The workers in groups of kGrp: a group's sign words and scales are
+  // loaded together, then added in worker order.  Holding 16 blocks leaves
+  // no registers for a group (the compiler then moves the blocks to
+  // scratch memory), so that form takes one worker at a time.
+  constexpr int kGrp = RES == 16 ? 1 : 4;
   auto zf = [&](int b, int v, Slots& y) {
     Slots acc;
-    for (int w = 0; w < W; ++w) {
-      const float s = pin.scales[w][ch.k];
-      uint32_t nib[4];
-      load_sign_nibbles<kBlk>(pin.bits[w] + ch.word0(b), nib);
+    for (int w0 = 0; w0 < W; w0 += kGrp) {
+      float sg[kGrp];
+      uint32_t nib[kGrp][4];
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+      for (int j = 0; j < kGrp; ++j)
+        if (w0 + j < W) {
+          sg[j] = pin.scales[w0 + j][ch.k];
+          load_sign_nibbles<kBlk>(pin.bits[w0 + j] + ch.word0(b), nib[j]);
+        }
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const float sv = signed_scale(nib, a, c, s);
-          acc[a][c] = w == 0 ? sv : acc[a][c] + sv;
+      for (int j = 0; j < kGrp; ++j)
+        if (w0 + j < W) {
+#pragma unroll
+          for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const float sv = signed_scale(nib[j], a, c, sg[j]);
+              acc[a][c] = w0 + j == 0 ? sv : acc[a][c] + sv;
+            }
         }
     }
     bload<NT>(err_s, ch, b, v, y);
