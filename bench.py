@@ -536,7 +536,7 @@ def main():
                      # the library's choice of pass-A kernel (persistent ring at
                      # 4096-element chunks from seven workers up)
                      "kernel": "k_compressed_pass_a_ring<4096>" if C == 4096 and W >= 7 else
-                     ("k_big_worker_compress x W, k_big_average_packed, k_big_rescale_stats"
+                     ("k_big_workers_compress, k_big_average_packed, k_big_rescale_stats"
                       if long_chunk else f"k_compressed_pass_a<{C}>"),
                      "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,

@@ -654,9 +654,23 @@ void big_allreduce(int64_t n, int32_t chunk, int W, const Workers& wk, float* er
                    int32_t* status, hipStream_t st) {
   const int lr = big_lr(chunk);
   PackedIn pin{};
+  // With the fp32 momentum, one launch for all workers (they share m
+  // through L2) unless its grid would pass 2^32 work-items.  A packed
+  // momentum is 1/32 of m's bytes: there the one launch saved nothing and
+  // made the 1-bit Adam step 3% slower (chunks of 32768, W = 8), so each
+  // worker keeps its own launch.
+  const int64_t K = onebit_host::chunks_of(n, chunk);
+  const int64_t groups = (K + 7) / 8 * 8 * W;
+  const bool one_launch = m && K > 0 && groups * kBT <= (int64_t)UINT32_MAX;
   by_res(lr, [&](auto R) {
     constexpr int RES = decltype(R)::value;
+    if (one_launch)
+      hipLaunchKernelGGL((k_big_workers_compress<kShare_NT, RES>), dim3((unsigned)groups),
+                         dim3(kBT), 0, st, n, lr, W, wk, m, cf, status);
     for (int w = 0; w < W; ++w) {
+      pin.bits[w] = wk.bits[w];
+      pin.scales[w] = wk.scales[w];
+      if (one_launch) continue;
       if (m)
         big_launch(n, chunk, st, k_big_worker_compress<kShare_NT, false, RES>, n, lr, wk.g[w],
                    wk.e[w], m, (const uint32_t*)nullptr, (const float*)nullptr, wk.bits[w],
@@ -665,8 +679,6 @@ void big_allreduce(int64_t n, int32_t chunk, int W, const Workers& wk, float* er
         big_launch(n, chunk, st, k_big_worker_compress<kShare_NT, true, RES>, n, lr, wk.g[w],
                    wk.e[w], m, (const uint32_t*)bits_s, (const float*)scales_s, wk.bits[w],
                    wk.scales[w], cf, status);
-      pin.bits[w] = wk.bits[w];
-      pin.scales[w] = wk.scales[w];
     }
     big_launch(n, chunk, st, k_big_average_packed<kCodec_NT, RES>, n, lr, W, pin, err_s, bits_s,
                scales_s, status);

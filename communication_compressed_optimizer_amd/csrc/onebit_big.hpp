@@ -306,19 +306,21 @@ __device__ __forceinline__ void big_beta1_momentum(const BigAt& ch, int b, int v
   }
 }
 
-// One worker: z = (beta1*m + a1*g) + e
-template <bool NT, bool PM, int RES>
-__global__ void __launch_bounds__(kBT, 1)
-k_big_worker_compress(int64_t n, int lr, const float* __restrict__ g, float* __restrict__ e,
-                      const float* __restrict__ m, const uint32_t* __restrict__ bits_m,
-                      const float* __restrict__ scales_m, uint32_t* __restrict__ bits_w,
-                      float* __restrict__ scales_w, Coef cf, int32_t* status) {
-  __shared__ float4 lds[2 * kBT];
+// One worker's chunk: z = (beta1*m + a1*g) + e compressed (NTM: the
+// momentum read as streaming data too).
+template <bool NT, bool NTM, bool PM, int RES>
+__device__ __forceinline__ void big_worker_chunk(const BigAt& ch, const float* __restrict__ g,
+                                                 float* __restrict__ e,
+                                                 const float* __restrict__ m,
+                                                 const uint32_t* __restrict__ bits_m,
+                                                 const float* __restrict__ scales_m,
+                                                 uint32_t* __restrict__ bits_w,
+                                                 float* __restrict__ scales_w, const Coef& cf,
+                                                 int32_t* status, float4* lds) {
   int parity = 0;
-  const BigAt ch(blockIdx.x, n, lr);
   auto zf = [&](int b, int v, Slots& z) {
     Slots gg, ee;
-    big_beta1_momentum<NT, PM>(ch, b, v, m, bits_m, scales_m, cf, z);
+    big_beta1_momentum<NTM, PM>(ch, b, v, m, bits_m, scales_m, cf, z);
     bload<NT>(g, ch, b, v, gg);
     bload<NT>(e, ch, b, v, ee);
 #pragma unroll
@@ -331,6 +333,39 @@ k_big_worker_compress(int64_t n, int lr, const float* __restrict__ g, float* __r
     scales_w[ch.k] = s;
     if (!__builtin_isfinite(s)) flag(status, 1);
   }
+}
+
+// One worker: z = (beta1*m + a1*g) + e
+template <bool NT, bool PM, int RES>
+__global__ void __launch_bounds__(kBT, 1)
+k_big_worker_compress(int64_t n, int lr, const float* __restrict__ g, float* __restrict__ e,
+                      const float* __restrict__ m, const uint32_t* __restrict__ bits_m,
+                      const float* __restrict__ scales_m, uint32_t* __restrict__ bits_w,
+                      float* __restrict__ scales_w, Coef cf, int32_t* status) {
+  __shared__ float4 lds[2 * kBT];
+  big_worker_chunk<NT, NT, PM, RES>(BigAt(blockIdx.x, n, lr), g, e, m, bits_m, scales_m, bits_w,
+                                    scales_w, cf, status, lds);
+}
+
+// All W workers in one launch (fp32 momentum), one workgroup per (chunk,
+// worker).  Workgroup g takes chunk 8*((g/8)/W) + g mod 8 for worker
+// (g/8) mod W, so the W workgroups of a chunk have the same g mod 8 (the
+// same XCD, as workgroups are dealt to the eight XCDs in turn) and lie close
+// in dispatch order: the momentum they share is then read from HBM once and
+// from that XCD's L2 by the others, and so is read with ordinary (not
+// streaming) loads.  Grid: ceil(K/8)*8*W workgroups; those past the last
+// chunk return at once.
+template <bool NT, int RES>
+__global__ void __launch_bounds__(kBT, 1)
+k_big_workers_compress(int64_t n, int lr, int W, Workers wk, const float* __restrict__ m,
+                       Coef cf, int32_t* status) {
+  __shared__ float4 lds[2 * kBT];
+  const int64_t gi = blockIdx.x, r = gi >> 3;
+  const int w = (int)(r % W);
+  const int64_t k = (r / W) * 8 + (gi & 7);
+  if (k * ((int64_t)kBlk << lr) >= n) return;
+  big_worker_chunk<NT, false, false, RES>(BigAt(k, n, lr), wk.g[w], wk.e[w], m, nullptr, nullptr,
+                                          wk.bits[w], wk.scales[w], cf, status, lds);
 }
 
 // The server: y = (mean of the W workers' +-s) + err_s, recompressed
