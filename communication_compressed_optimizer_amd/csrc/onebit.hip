@@ -589,12 +589,22 @@ void by_res(int lr, F&& f) {
   else f(std::integral_constant<int, 0>{});
 }
 
-// The launch over the n elements' chunks (nothing for n = 0).
+// The launch over the n elements' chunks (nothing for n = 0); lds bytes of
+// dynamic LDS cap the workgroups resident on a CU.
+template <typename KF, typename... A>
+void big_launch_lds(unsigned lds, int64_t n, int32_t chunk, hipStream_t st, KF k, A... args) {
+  const int64_t K = onebit_host::chunks_of(n, chunk);
+  if (K > 0) hipLaunchKernelGGL(k, dim3((unsigned)K), dim3(kBT), lds, st, args...);
+}
 template <typename KF, typename... A>
 void big_launch(int64_t n, int32_t chunk, hipStream_t st, KF k, A... args) {
-  const int64_t K = onebit_host::chunks_of(n, chunk);
-  if (K > 0) hipLaunchKernelGGL(k, dim3((unsigned)K), dim3(kBT), 0, st, args...);
+  big_launch_lds(0u, n, chunk, st, k, args...);
 }
+// The update at two workgroups per CU (63 KiB of dynamic LDS each; three
+// would need more than the CU's 160 KiB), as the update at 4096: 1.008
+// against 1.040 ms uncapped at chunks of 32768 (BERT-Large table).  The
+// statistics kernel was 17% slower so capped and keeps no cap.
+constexpr unsigned kBigUpdate_lds = 63u * 1024u;
 
 // A compression step over chunks longer than 16384 elements needs the
 // workers' sign words and scales (EUNSUPPORTED otherwise) and, with
@@ -716,8 +726,9 @@ void big_pass_b(const onebit_layer_table* t, const uint32_t* bits_s, const float
                 float* c_out, const Coef& cf, bool rn, const Ws& ws, int32_t* status,
                 hipStream_t st) {
   rescale_finalize(t, c_avg, f_prev, c_out, cf, rn, ws, status, st);
-  big_launch(t->N, t->chunk, st, k_big_pass_b<kPassB_NT>, t->dev, big_lr(t->chunk), bits_s,
-             scales_s, v_frozen, x, m, (const float*)ws.c_layer, cf);
+  big_launch_lds(kBigUpdate_lds, t->N, t->chunk, st, k_big_pass_b<kPassB_NT>, t->dev,
+                 big_lr(t->chunk), bits_s, scales_s, v_frozen, x, m, (const float*)ws.c_layer,
+                 cf);
 }
 
 // The workers' arrays of a compression step; fills wk.
