@@ -199,6 +199,13 @@ void launch_chunks_capped(unsigned lds, int64_t n, hipStream_t st, KF k, A... ar
 constexpr bool kPassA_NT = true;   // streaming loads and stores
 constexpr bool kPassA_PF = false;  // next-worker prefetch
 constexpr int kPassA_WPE = 6;      // minimum waves per SIMD
+// A table of at most 16 chunks per CU takes pass A at four waves per SIMD:
+// six leave the last of its 2.7 rounds (4096 chunks, 256 CUs) part empty.
+// Single 16M-element tensor, W = 4, three interleaved pairs on one box:
+// 0.262 against 0.269 ms per step (packed momentum 0.236 against 0.251);
+// on the BERT-XL table (W = 4) four were 2-4% slower in phase 1.
+constexpr int kPassA_WPE_small = 4;
+constexpr int64_t kPassA_small_per_cu = 16;
 // Float4 slots per thread of pass A (workgroup = C / (4 * SPT)): the chunk's
 // own layout, four from 1024 elements up.
 template <int C>
@@ -414,6 +421,12 @@ struct LaunchPassA {
                            dim3(Geo<C>::T), 0, st, n_full, t->dev, W, wk, err_s, m, v_frozen,
                            v_fresh, bits_s, scales_s, ws.seg_max, ws.seg_x, ws.seg_u, cf,
                            status);
+    } else if (t->K <= kPassA_small_per_cu * t->cus) {
+      hipLaunchKernelGGL(
+          (k_compressed_pass_a<C, kPassA_NT, kPassA_PF, kPassA_WPE_small, kPassA_SPT<C>, RN, PM>),
+          dim3((unsigned)t->K), dim3(Geo<C, kPassA_SPT<C>>::T), 0, st, n_full, t->dev, W, wk,
+          err_s, m, v_frozen, v_fresh, bits_s, scales_s, ws.seg_max, ws.seg_x, ws.seg_u, cf,
+          status);
     } else {
       hipLaunchKernelGGL(
           (k_compressed_pass_a<C, kPassA_NT, kPassA_PF, kPassA_WPE, kPassA_SPT<C>, RN, PM>),
