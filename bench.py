@@ -16,7 +16,7 @@ fp32 momentum; `packed_momentum` times the same step with the momentum kept
 as the server's packed output (bit-identical results); `roofline` is the
 dominant kernel (phase 1: compression, average, rescale statistics) timed
 with HIP events on its stream; `runtime_copy` is the runtime's own 1 GiB
-device-to-device copy timed on the same box, as a reference rate;
+device-to-device copy timed on the same machine, as a reference rate;
 `cpu_baseline` is the single-threaded CPU oracle on a bounded window of the
 same workload.  `--method adam` and
 `--method sparse` time the 1-bit Adam mode and the SLAMB-style sparse stage
@@ -85,7 +85,7 @@ def sparse_bytes(N, K, C, W, nsel):
 
 def copy_ceiling(torch, stream, nbytes=1 << 30, reps=10):
     """torch's device-to-device copy of nbytes on the same stream, timed with
-    HIP events: a reference rate of this box, reported beside the 8 TB/s
+    HIP events: a reference rate of this machine, reported beside the 8 TB/s
     peak.  Returns GB/s counting the bytes read and written."""
     a = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
     b = torch.empty_like(a)
@@ -108,7 +108,7 @@ def _ceiling(torch, stream, achieved):
     return {"copy_GBps": copy_gbps, "copy_frac_of_peak": copy_gbps / PEAK_HBM_GBPS,
             "kernel_frac_of_copy": achieved / copy_gbps,
             "note": "1 GiB device-to-device copy by the runtime (torch copy_) on the same stream "
-                    "after the timed steps, read plus written bytes; a reference rate of the box, "
+                    "after the timed steps, read plus written bytes; a reference rate of the machine, "
                     "not an upper bound (a tuned streaming copy runs faster)"}
 
 
@@ -126,7 +126,7 @@ def _ceiling_lib():
 
 def pattern_ceiling(torch, stream, wl, g, e, err_s, m, v, vf, bits_w, bits_s, achieved,
                     reps=10):
-    """The box's practical ceiling, measured in the same run on the step's own
+    """The machine's practical ceiling, measured in the same run on the step's own
     buffers by pure-traffic kernels with the step's loads, stores and launch
     shape (libonebit_ceiling.so): phase 1's exact stream set (m read; per
     worker g and e read, e and the sign words written, a workgroup barrier per
@@ -562,7 +562,7 @@ _LDS_CAPS = {1: 84 * 1024, 2: 56 * 1024, 3: 44 * 1024, 4: 36 * 1024}
 
 def ceiling_sweep(args, wl, ob, torch, table, hp, g, e, err_s, m, v, vf, bits_w, scales_w,
                   bits_s, scales_s, ws, status, stream, reps=8, rounds=3):
-    """What the phase-1 access pattern costs on this box, from committed
+    """What the phase-1 access pattern costs on this machine, from committed
     kernels only: the real phase-1 kernel, interleaved with the pure-traffic
     kernel of its stream set (libonebit_ceiling.so) uncapped and at 1-4
     workgroups per CU, then that pattern's loads alone and its stores alone,
@@ -622,7 +622,7 @@ def ceiling_sweep(args, wl, ob, torch, table, hp, g, e, err_s, m, v, vf, bits_w,
     torch.cuda.synchronize()
     times["pattern_stores_only"] = [ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]
     sbytes = n * (4 * W + 8) + (W + 1) * n // 8
-    out = {"metric": "phase-1 access pattern on this box (pure-traffic kernels)",
+    out = {"metric": "phase-1 access pattern on this machine (pure-traffic kernels)",
            "workload": f"{wl.name}: N={N}, W={W}, chunk {C}", "unit": "ms, GB/s",
            "note": "medians; *_per_cu caps the resident workgroups per CU with dynamic LDS; "
                    "loads_only/stores_only are the pattern's reads or writes alone"}

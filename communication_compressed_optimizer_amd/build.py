@@ -1,5 +1,5 @@
 """Build libonebit.so (the C-ABI library and its gfx950 kernels) in-tree,
-and libonebit_ceiling.so (pure-traffic kernels that measure the box's
+and libonebit_ceiling.so (pure-traffic kernels that measure the machine's
 practical HBM ceiling for the same access patterns; used by bench.py only).
 
 Flags that matter for results: contraction off (no fused multiply-add may

@@ -1,5 +1,5 @@
 // libonebit_ceiling.so: pure-traffic kernels that measure what the HBM of
-// the box in hand sustains for the access patterns of the optimizer's
+// the machine in hand sustains for the access patterns of the optimizer's
 // kernels, as a practical ceiling beside the 8 TB/s peak.  They are
 // measurement tools, not part of the optimizer: no entry point of
 // libonebit.so calls them.

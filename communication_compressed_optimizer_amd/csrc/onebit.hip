@@ -186,7 +186,7 @@ void launch_chunks_capped(unsigned lds, int64_t n, hipStream_t st, KF k, A... ar
 }
 
 // Tuning of the compression-step kernels, measured on MI355X at the
-// BERT-Large table with W = 8 (phase 1, interleaved medians on one box:
+// BERT-Large table with W = 8 (phase 1, interleaved medians on one machine:
 // plain accesses 7.76 ms, streaming 7.38 ms; with the partial chunk folded
 // into the grid, streaming with a 6-wave register cap 7.05 ms, uncapped 7.39,
 // 7-wave cap 7.44, 8-wave cap 7.89 -- the cap's spills are reloaded every
@@ -201,7 +201,7 @@ constexpr bool kPassA_PF = false;  // next-worker prefetch
 constexpr int kPassA_WPE = 6;      // minimum waves per SIMD
 // A table of at most 16 chunks per CU takes pass A at four waves per SIMD:
 // six leave the last of its 2.7 rounds (4096 chunks, 256 CUs) part empty.
-// Single 16M-element tensor, W = 4, three interleaved pairs on one box:
+// Single 16M-element tensor, W = 4, three interleaved pairs on one machine:
 // 0.262 against 0.269 ms per step (packed momentum 0.236 against 0.251);
 // on the BERT-XL table (W = 4) four were 2-4% slower in phase 1.
 constexpr int kPassA_WPE_small = 4;
@@ -213,10 +213,10 @@ constexpr int kPassA_SPT = kSlots<C>;
 // With 4096-element chunks and at least kPassA_ring_min_W workers, pass A
 // runs as a persistent grid with two workers and the next chunk's first
 // three in flight (k_compressed_pass_a_ring).  At BERT-Large, W = 8,
-// interleaved against one workgroup per chunk on seven boxes, it was
+// interleaved against one workgroup per chunk on seven machines, it was
 // 0.7-4.2% faster (7.05-7.16 against 7.16-7.38 ms; the larger gains where
 // the 30-stream pattern runs slowest), outputs identical.  Over W on one
-// table (two boxes): W = 2-6 slower (by 22% at W = 2, 1-4% at W = 4-6: per
+// table (two machines): W = 2-6 slower (by 22% at W = 2, 1-4% at W = 4-6: per
 // chunk there is too little worker traffic to hide its reductions behind),
 // W = 7 even, W = 8-16 between 4.8% faster and 2% slower, 1.1% faster on
 // average.  With 2048-element chunks it was 4% slower, with 1024 no faster,
@@ -233,19 +233,19 @@ constexpr bool kPassB_NT = true;
 // 0.899 ms, one per CU 0.983 ms; outputs identical).
 template <int C>
 constexpr unsigned kPassB_lds = C == 4096 ? 65536u : 0u;
-// LAMB warmup passes (BERT-Large, W = 8, interleaved on one box): streaming
+// LAMB warmup passes (BERT-Large, W = 8, interleaved on one machine): streaming
 // accesses take pass 1 from 3.30 to 2.95 ms and pass 2 from 0.97 to 0.87 ms;
 // a 5- or 6-wave register cap on pass 1 is slower (3.07, 3.44 ms) and one on
 // the 1-bit Adam warmup changes nothing (3.19-3.22 against 3.20 ms).  Pass 1
 // keeps the next gradient and then m and v in flight while it sums: the
-// carried warmup step 3.53-3.61 against 3.56-3.66 ms (two rounds, outputs
+// carried warmup step 3.53-3.61 against 3.56-3.66 ms (two series, outputs
 // identical); a persistent grid of one or two workgroups per CU, or caps on
 // the workgroups per CU, did not help.  At 4096-element chunks both passes
 // lay a chunk over 512 threads (two float4 slots each; pass 1 82 VGPRs and
 // five waves per SIMD, where four slots took 143 VGPRs and three) and pass 1
 // keeps two gradients in flight: pass 1 alone took 2.63-2.67 against
-// 2.69-2.79 ms at W = 8 and 1.74 against 1.83 ms at W = 4 (two rounds, one
-// box; m and v identical, the per-segment sums within 1e-12, their order
+// 2.69-2.79 ms at W = 8 and 1.74 against 1.83 ms at W = 4 (two series on one
+// machine; m and v identical, the per-segment sums within 1e-12, their order
 // being the layout's), and the carried warmup step 3.48 / 3.59 against
 // 3.56 / 3.72 ms at W = 8 and 2.58 against 2.65 ms at W = 4 (outputs
 // identical).  One slot per thread with one, three or all gradients in
@@ -275,7 +275,7 @@ constexpr bool kSparse_NT = true;
 // One GPU's share of a W-GPU step: the worker compression and the receiver
 // statistics stream like the codec kernels.  The worker compression at
 // 4096-element chunks runs at most two workgroups per CU, like pass B
-// (0.84 against 0.88 ms at N = 333.6 M, two runs on one box; the receiver
+// (0.84 against 0.88 ms at N = 333.6 M, two runs on one machine; the receiver
 // statistics were 21% slower so capped, and keep the full grid).
 constexpr bool kShare_NT = true;
 template <int C>
