@@ -96,6 +96,10 @@ def test_table_checks(ob):
     numels = (ctypes.c_int64 * 1)(10)
     assert lib.onebit_layer_table_create(numels, 1, 3000, ctypes.byref(out)) == \
         ob.ONEBIT_EUNSUPPORTED
+    for chunk in (1 << 25, 3 << 15, (1 << 24) + 64, 32):
+        assert lib.onebit_layer_table_create(numels, 1, chunk, ctypes.byref(out)) == \
+            ob.ONEBIT_EUNSUPPORTED
+        assert "[64, 2^24]" in ob.onebit_last_error()
     assert lib.onebit_layer_table_destroy(None) == ob.ONEBIT_OK
     # sizes whose sum would overflow int64, or that exceed 2^30 - 1 chunks,
     # are refused before anything is allocated
@@ -201,6 +205,11 @@ def test_binding_checks_tensors_before_the_library(ob):
     assert ob._Sizes(10, 3000).elems is None and ob._Sizes(-1, 4096).elems is None
     z = ob._Sizes(4097, 4096)
     assert (z.K, z.elems, z.words, z.scales) == (2, 4 * 4097, 4 * 2 * 128, 8)
+    # chunks are powers of two from 64 to 2^24
+    z = ob._Sizes(5, 1 << 24)
+    assert (z.K, z.elems, z.words, z.scales) == (1, 20, 4 * (1 << 19), 4)
+    assert ob._Sizes(5, 1 << 25).elems is None and ob._Sizes(5, 32).elems is None
+    assert ob._Sizes(5, 3 << 15).elems is None
 
 
 def test_share_entry_point_checks(ob):
